@@ -1,0 +1,104 @@
+"""Seeded input generator: determinism, storage rounding and cache layout bookkeeping."""
+
+import numpy as np
+import pytest
+
+from mlra_latent_kv_amd import inputs as I
+
+
+def test_bf16_rounding_matches_torch_rne():
+    import torch
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 3,
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 1e4, -1e4],
+                                 dtype=np.float32)])
+    ours = I.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(I.bf16_bits_to_f32(ours), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+@pytest.mark.parametrize("wname", I.WORKLOAD_ORDER)
+def test_deterministic_per_seed(wname):
+    w = I.WORKLOADS[wname]
+    a = I.make_inputs(w, seqlens=[5, 70])
+    b = I.make_inputs(w, seqlens=[5, 70])
+    c = I.make_inputs(w, seed=w.seed + 1, seqlens=[5, 70])
+    for k in ("q_nope", "q_rope", "cache", "w_uk", "w_uv"):
+        assert np.array_equal(a[k], b[k])
+        assert not np.array_equal(a[k], c[k])
+
+
+def test_shapes_and_replicated_branch_query():
+    w = I.WORKLOADS["mlra4_bf16_b32_h32_l8192"]
+    inp = I.make_inputs(w, seqlens=[3, 4])
+    assert inp["q_nope"].shape == (2, 32, 4, 128) and inp["q_nope"].dtype == np.uint16
+    assert inp["q_rope"].shape == (2, 32, 64)
+    assert inp["cache"].shape == (2, 4, 576)
+    assert inp["w_uk"].shape == (4, 32, 128, 128) and inp["w_uv"].shape == (4, 32, 128, 128)
+    for br in range(1, 4):
+        assert np.array_equal(inp["q_nope"][:, :, br], inp["q_nope"][:, :, 0])
+
+
+def test_paged_layout_bookkeeping_and_poison():
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    lens = [1, 64, 65, 130, 0]
+    p = I.make_inputs(w, seed=3, seqlens=lens, paged=True)
+    c = I.make_inputs(w, seed=3, seqlens=lens, paged=False)
+    bt, pool, pos = p["block_table"], p["cache"], p["row_pos"].reshape(-1, I.PAGE)
+    npages = [(L + 63) // 64 for L in lens]
+    assert pool.shape[0] == sum(npages)
+    used = sorted(int(x) for x in bt.reshape(-1) if x >= 0)
+    assert used == list(range(sum(npages)))          # a permutation of all pool pages
+    poison = I.f32_to_bf16_bits(np.array([1e4, -1e4], np.float32))
+    for b, L in enumerate(lens):
+        for t in range(L):
+            pg, slot = bt[b, t // 64], t % 64
+            assert pos[pg, slot] == t
+            assert np.array_equal(pool[pg, slot], c["cache"][b, t])
+        for j in range(npages[b], bt.shape[1]):
+            assert bt[b, j] == -1
+        if L % 64:
+            tail = pool[bt[b, L // 64], L % 64:]
+            assert np.array_equal(tail[:, 0], np.full(len(tail), poison[0]))
+            assert np.array_equal(tail[:, 1], np.full(len(tail), poison[1]))
+    # contiguous cache: rows past the length are poisoned and marked unused
+    assert np.array_equal(c["cache"][0, 1:, 0], np.full(c["cache"].shape[1] - 1, poison[0]))
+    assert (c["row_pos"].reshape(len(lens), -1)[0, 1:] == -1).all()
+
+
+def test_variable_lengths_in_range():
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    lens = I.draw_seqlens(w, 64, np.random.default_rng(np.random.SeedSequence(w.seed).spawn(8)[6]))
+    assert lens.min() >= 1024 and lens.max() <= 32768 and len(set(lens.tolist())) > 50
+
+
+def test_value_distribution_scale():
+    w = I.WORKLOADS["mla_bf16_b32_h128_l4096"]
+    inp = I.make_inputs(w, seqlens=[512])
+    lat = I.to_f64(inp["cache"][0, :, :512], "bf16")
+    kr = I.to_f64(inp["cache"][0, :, 512:], "bf16")
+    assert abs(lat.std() * np.sqrt(512) - 1) < 0.02
+    assert abs(kr.std() * np.sqrt(64) - 1) < 0.02
+    assert abs(I.to_f64(inp["w_uk"], "bf16").std() * np.sqrt(512) - 1) < 0.02
+
+
+def test_sharp_gain_gives_target_logit_std():
+    """Empirical logit std of the sharp variant, computed directly from the definitions of
+    the score (up-projected key plus rotary term) with random rotations ignored (they
+    preserve norms)."""
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    g = I.sharp_q_gain(w)
+    inp = I.make_inputs(w, seqlens=[256], q_gain=g, paged=False)
+    qn = I.to_f64(inp["q_nope"], "bf16")[0, :, 0]
+    qr = I.to_f64(inp["q_rope"], "bf16")[0]
+    lat = I.to_f64(inp["cache"][0, :, :512], "bf16")
+    kr = I.to_f64(inp["cache"][0, :, 512:], "bf16")
+    wk = I.to_f64(inp["w_uk"], "bf16")[0]
+    s = np.stack([(lat @ wk[h].T) @ qn[h] + kr @ qr[h] for h in range(w.heads)]) * w.softmax_scale
+    assert 1.6 < s.std() < 2.4
+
+
+def test_cache_bytes():
+    w = I.WORKLOADS["mla_bf16_b32_h128_l4096"]
+    assert I.cache_bytes(w, np.full(32, 4096)) == 32 * 4096 * 1152
