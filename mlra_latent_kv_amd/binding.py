@@ -1,0 +1,158 @@
+"""ctypes binding of libmla_decode.so: same entry points as include/mla_decode.h.
+
+Argument marshalling only.  Every step of the decode runs in the library's HIP kernels;
+there is no Python or CPU fallback.  If the shared library is missing this module raises
+on first use rather than degrading silently.
+
+Tensor arguments may be torch tensors (their ``data_ptr()`` is passed) or raw integer
+device addresses.  ``stream`` defaults to torch's current HIP stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla_decode.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "mla_decode.h")
+
+MLA_F32, MLA_BF16 = 0, 1
+PAGE_SIZE = 64
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_UNSUPPORTED",
+          4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_DTYPE", 6: "MLA_ERR_ALIGN", 7: "MLA_ERR_HIP"}
+
+
+class MlaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_int32), ("num_heads", c_int32), ("num_branches", c_int32),
+        ("d_nope", c_int32), ("d_v", c_int32), ("d_latent", c_int32), ("d_rope", c_int32),
+        ("page_size", c_int32), ("max_pages_per_seq", c_int32), ("max_seqlen", c_int32),
+        ("num_splits", c_int32), ("dtype", c_int32),
+        ("latent_stride_tok", c_int64), ("latent_stride_seq", c_int64),
+        ("rope_stride_tok", c_int64), ("rope_stride_seq", c_int64),
+        ("block_table_stride", c_int64),
+        ("softmax_scale", c_float), ("out_scale", c_float), ("rope_theta", c_float),
+    ]
+
+    def copy(self) -> "MlaParams":
+        c = MlaParams()
+        ctypes.pointer(c)[0] = self
+        return c
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_str(status)}")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m mlra_latent_kv_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(MlaParams)
+    lib.mla_workspace_size.argtypes = [P, ctypes.POINTER(c_size_t)]
+    lib.mla_num_splits.argtypes = [P, ctypes.POINTER(c_int32)]
+    dec = [P] + [c_void_p] * 10 + [c_size_t, c_void_p]
+    lib.mla_decode.argtypes = dec
+    lib.mlra_decode.argtypes = dec
+    lib.mla_rope_rotate.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_float,
+                                    c_int32, c_void_p]
+    lib.mla_status_str.argtypes = [c_int32]
+    lib.mla_status_str.restype = ctypes.c_char_p
+    for f in ("mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
+              "mla_rope_rotate"):
+        getattr(lib, f).restype = c_int32
+    _lib = lib
+    return lib
+
+
+def header_functions(header: str = HEADER) -> list:
+    """Names of the functions include/mla_decode.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ml\w+)\s*\(", text, flags=re.M)))
+
+
+def status_str(status: int) -> str:
+    try:
+        return load().mla_status_str(status).decode()
+    except Exception:  # library missing: still give a readable name
+        return STATUS.get(status, f"status {status}")
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def workspace_size(params: MlaParams) -> int:
+    n = c_size_t(0)
+    st = load().mla_workspace_size(ctypes.byref(params), ctypes.byref(n))
+    if st:
+        raise MlaError(st, "mla_workspace_size")
+    return n.value
+
+
+def num_splits(params: MlaParams) -> int:
+    n = c_int32(0)
+    st = load().mla_num_splits(ctypes.byref(params), ctypes.byref(n))
+    if st:
+        raise MlaError(st, "mla_num_splits")
+    return n.value
+
+
+def _decode(fname, params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+            workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = getattr(load(), fname)(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(latent),
+                                _ptr(rope), _ptr(seqlens), _ptr(block_table), _ptr(w_uk),
+                                _ptr(w_uv), _ptr(out), _ptr(workspace), workspace_bytes,
+                                _stream(stream))
+    if check and st:
+        raise MlaError(st, fname)
+    return st
+
+
+def mla_decode(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+               workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    return _decode("mla_decode", params, q_nope, q_rope, latent, rope, seqlens, block_table,
+                   w_uk, w_uv, out, workspace, workspace_bytes, stream, check)
+
+
+def mlra_decode(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    return _decode("mlra_decode", params, q_nope, q_rope, latent, rope, seqlens, block_table,
+                   w_uk, w_uv, out, workspace, workspace_bytes, stream, check)
+
+
+def mla_rope_rotate(x, row_stride: int, pos, n_rows: int, d_rope: int, theta: float, dtype: int,
+                    stream=None, check=True) -> int:
+    st = load().mla_rope_rotate(_ptr(x), row_stride, _ptr(pos), n_rows, d_rope, theta, dtype,
+                                _stream(stream) if n_rows else None)
+    if check and st:
+        raise MlaError(st, "mla_rope_rotate")
+    return st

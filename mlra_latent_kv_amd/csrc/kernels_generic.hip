@@ -1,0 +1,300 @@
+// Prologue (absorbed query), split combine, W_UV epilogue, rotary-key rotation, and the
+// fp32 SIMT main loop used for small fp32 shapes.  The bf16 MFMA main loop is in
+// main_bf16.hip.
+//
+// Absorption ("超越 GQA 的推理革命…MLA…", section 矩陣吸收): the key up-projection W_UK is
+// folded into the query (prologue) and the value up-projection W_UV is applied once to the
+// attention-weighted latent (epilogue), so per-token keys and values are never formed.
+#include <cmath>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace mla {
+
+constexpr int kBatchBlock = 8;  // sequences per prologue / epilogue workgroup (weight reuse)
+
+// ----------------------------------------------------------------------------- prologue
+// qcat[b,h] = [ (W_UK[br,h]^T q_nope[b,h,br])_{br} | RoPE(q_rope[b,h], L_b - 1) ] * qscale
+// qscale = softmax_scale * log2(e) so the main loop can use exp2.
+template <typename T>
+__global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
+                                                  const T* __restrict__ q_rope,
+                                                  const int32_t* __restrict__ seqlens,
+                                                  const T* __restrict__ w_uk, T* __restrict__ qcat,
+                                                  int B, int H, int NB, int dn, int dcb, int dr,
+                                                  float qscale, double theta) {
+  extern __shared__ float sq[];  // [kBatchBlock][NB][dn]
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kBatchBlock;
+  const int nb = min(kBatchBlock, B - b0);
+  const int dc = NB * dcb, row = dc + dr;
+  const int per_b = NB * dn;
+  for (int i = threadIdx.x; i < kBatchBlock * per_b; i += blockDim.x) {
+    const int j = i / per_b, rest = i % per_b;
+    sq[i] = j < nb ? to_f32(q_nope[((size_t)(b0 + j) * H + h) * per_b + rest]) : 0.0f;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < dc; c += blockDim.x) {
+    const int br = c / dcb, cc = c % dcb;
+    const T* w = w_uk + ((size_t)br * H + h) * dn * dcb + cc;
+    const float* q = sq + br * dn;
+    float acc[kBatchBlock];
+#pragma unroll
+    for (int j = 0; j < kBatchBlock; ++j) acc[j] = 0.0f;
+    for (int n = 0; n < dn; ++n) {
+      const float wv = to_f32(w[(size_t)n * dcb]);
+#pragma unroll
+      for (int j = 0; j < kBatchBlock; ++j) acc[j] = fmaf(q[j * per_b + n], wv, acc[j]);
+    }
+    for (int j = 0; j < nb; ++j)
+      qcat[((size_t)(b0 + j) * H + h) * row + c] = from_f32<T>(acc[j] * qscale);
+  }
+  const int half = dr / 2;
+  for (int i = threadIdx.x; i < nb * half; i += blockDim.x) {
+    const int j = i / half, k = i % half;
+    const int b = b0 + j;
+    const int L = seqlens[b];
+    const double ang = (double)(L > 0 ? L - 1 : 0) * pow(theta, -2.0 * k / dr);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const T* x = q_rope + ((size_t)b * H + h) * dr + 2 * k;
+    const double x0 = to_f32(x[0]), x1 = to_f32(x[1]);
+    T* o = qcat + ((size_t)b * H + h) * row + dc + 2 * k;
+    o[0] = from_f32<T>((float)(x0 * cs - x1 * sn) * qscale);
+    o[1] = from_f32<T>((float)(x0 * sn + x1 * cs) * qscale);
+  }
+}
+
+hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(p.H, (p.B + kBatchBlock - 1) / kBatchBlock);
+  const size_t lds = (size_t)kBatchBlock * p.NB * p.dn * sizeof(float);
+  const float qscale = a.softmax_scale * kLog2e;
+  if (p.dtype == MLA_BF16)
+    hipLaunchKernelGGL(k_prologue<bf16>, grid, dim3(256), lds, s, (const bf16*)a.q_nope,
+                       (const bf16*)a.q_rope, a.seqlens, (const bf16*)a.w_uk, (bf16*)a.qcat, p.B,
+                       p.H, p.NB, p.dn, p.dcb, p.dr, qscale, (double)a.rope_theta);
+  else
+    hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, s, (const float*)a.q_nope,
+                       (const float*)a.q_rope, a.seqlens, (const float*)a.w_uk, (float*)a.qcat,
+                       p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, (double)a.rope_theta);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- combine
+// Per (b, h, branch): merge the splits' (m_s, l_s, O_s) with log-sum-exp weights:
+//   M = max_s m_s,  o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Splits with no tokens carry m = -inf and are skipped (their O_s is never read).
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o,
+                                                 const float* __restrict__ part_ml,
+                                                 float* __restrict__ olat, int H, int S, int NB,
+                                                 int dcb) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int dc = NB * dcb;
+  for (int d = threadIdx.x; d < dc; d += blockDim.x) {
+    const int br = d / dcb;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s)
+      M = fmaxf(M, part_ml[((((size_t)b * S + s) * NB + br) * H + h) * 2]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < S; ++s) {
+        const float* ml = part_ml + ((((size_t)b * S + s) * NB + br) * H + h) * 2;
+        const float m = ml[0];
+        if (m == -INFINITY) continue;
+        const float w = exp2f(m - M);
+        den = fmaf(w, ml[1], den);
+        num = fmaf(w, part_o[(((size_t)b * S + s) * H + h) * dc + d], num);
+      }
+    }
+    olat[((size_t)b * H + h) * dc + d] = den > 0.0f ? num / den : 0.0f;
+  }
+}
+
+hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine, dim3(p.H, p.B), dim3(256), 0, s, a.part_o, a.part_ml, a.olat,
+                     p.H, p.splits, p.NB, p.dcb);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- epilogue
+// out[b,h,v] = out_scale * sum_br sum_c olat[b,h,br*dcb + c] * W_UV[br,h,c,v]
+template <typename T>
+__global__ __launch_bounds__(128) void k_epilogue(const float* __restrict__ olat,
+                                                  const T* __restrict__ w_uv, T* __restrict__ out,
+                                                  int B, int H, int NB, int dcb, int dv,
+                                                  float out_scale) {
+  extern __shared__ float so[];  // [kBatchBlock][dc]
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kBatchBlock;
+  const int nb = min(kBatchBlock, B - b0);
+  const int dc = NB * dcb;
+  for (int i = threadIdx.x; i < kBatchBlock * dc; i += blockDim.x) {
+    const int j = i / dc, d = i % dc;
+    so[i] = j < nb ? olat[((size_t)(b0 + j) * H + h) * dc + d] : 0.0f;
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < dv; v += blockDim.x) {
+    float acc[kBatchBlock];
+#pragma unroll
+    for (int j = 0; j < kBatchBlock; ++j) acc[j] = 0.0f;
+    for (int br = 0; br < NB; ++br) {
+      const T* w = w_uv + ((size_t)br * H + h) * dcb * dv + v;
+      const float* o = so + br * dcb;
+      for (int c = 0; c < dcb; ++c) {
+        const float wv = to_f32(w[(size_t)c * dv]);
+#pragma unroll
+        for (int j = 0; j < kBatchBlock; ++j) acc[j] = fmaf(o[j * dc + c], wv, acc[j]);
+      }
+    }
+    for (int j = 0; j < nb; ++j)
+      out[((size_t)(b0 + j) * H + h) * dv + v] = from_f32<T>(acc[j] * out_scale);
+  }
+}
+
+hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(p.H, (p.B + kBatchBlock - 1) / kBatchBlock);
+  const size_t lds = (size_t)kBatchBlock * p.dc * sizeof(float);
+  if (p.dtype == MLA_BF16)
+    hipLaunchKernelGGL(k_epilogue<bf16>, grid, dim3(128), lds, s, a.olat, (const bf16*)a.w_uv,
+                       (bf16*)a.out, p.B, p.H, p.NB, p.dcb, p.dv, a.out_scale);
+  else
+    hipLaunchKernelGGL(k_epilogue<float>, grid, dim3(128), lds, s, a.olat, (const float*)a.w_uv,
+                       (float*)a.out, p.B, p.H, p.NB, p.dcb, p.dv, a.out_scale);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- rope rotate
+// RoFormer rotation of consecutive pairs by pos * theta^(-2k/d_rope), angles in fp64.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_rotate(T* __restrict__ x, int64_t row_stride,
+                                                     const int32_t* __restrict__ pos, int64_t n,
+                                                     int dr, double theta) {
+  const int half = dr / 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n * half) return;
+  const int64_t r = i / half;
+  const int k = (int)(i % half);
+  const int p = pos[r];
+  if (p < 0) return;
+  const double ang = (double)p * pow(theta, -2.0 * k / dr);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  T* px = x + r * row_stride + 2 * k;
+  const double x0 = to_f32(px[0]), x1 = to_f32(px[1]);
+  px[0] = from_f32<T>((float)(x0 * cs - x1 * sn));
+  px[1] = from_f32<T>((float)(x0 * sn + x1 * cs));
+}
+
+hipError_t launch_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
+                              int d_rope, float theta, int dtype, hipStream_t s) {
+  const int64_t work = n_rows * (d_rope / 2);
+  const dim3 grid((unsigned)((work + 255) / 256));
+  if (dtype == MLA_BF16)
+    hipLaunchKernelGGL(k_rope_rotate<bf16>, grid, dim3(256), 0, s, (bf16*)x, row_stride, pos,
+                       n_rows, d_rope, (double)theta);
+  else
+    hipLaunchKernelGGL(k_rope_rotate<float>, grid, dim3(256), 0, s, (float*)x, row_stride, pos,
+                       n_rows, d_rope, (double)theta);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- fp32 main loop
+// Generic SIMT split-K loop for small fp32 shapes: one wave per (sequence, split, head).
+// Lane t of a 64-token tile computes that token's scores for every branch; the online
+// softmax keeps (m, l) per branch; lane d accumulates latent-space output columns.
+__global__ __launch_bounds__(64) void k_main_f32(
+    const float* __restrict__ qcat, const float* __restrict__ latent,
+    const float* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
+    int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
+    int64_t bt_stride, int paged, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
+    int S, int chunk, int NB, int dcb, int dr) {
+  __shared__ float sq[512 + 64];
+  __shared__ float sp[64 * 4];
+  const int h = blockIdx.x % H;
+  const int unit = blockIdx.x / H;
+  const int b = unit / S, s = unit % S;
+  const int lane = threadIdx.x;
+  const int dc = NB * dcb, row = dc + dr;
+  const int L = seqlens[b];
+  const int t0 = s * chunk;
+  const int t1 = min(L, t0 + chunk);
+  float* ml = part_ml + (((size_t)b * S + s) * NB) * H * 2;
+  if (t0 >= t1) {
+    if (lane < NB) {
+      ml[((size_t)lane * H + h) * 2 + 0] = -INFINITY;
+      ml[((size_t)lane * H + h) * 2 + 1] = 0.0f;
+    }
+    return;
+  }
+  for (int i = lane; i < row; i += 64) sq[i] = qcat[((size_t)b * H + h) * row + i];
+  __syncthreads();
+  auto lat_row = [&](int t) -> const float* {
+    if (paged) return latent + (int64_t)bt[(int64_t)b * bt_stride + t / 64] * lat_seq + (t % 64) * lat_tok;
+    return latent + (int64_t)b * lat_seq + (int64_t)t * lat_tok;
+  };
+  auto rope_row = [&](int t) -> const float* {
+    if (paged) return rope + (int64_t)bt[(int64_t)b * bt_stride + t / 64] * rope_seq + (t % 64) * rope_tok;
+    return rope + (int64_t)b * rope_seq + (int64_t)t * rope_tok;
+  };
+  float m[4], l[4], alpha[4];
+  for (int br = 0; br < 4; ++br) { m[br] = -INFINITY; l[br] = 0.0f; alpha[br] = 1.0f; }
+  float o[8];
+  for (int k = 0; k < 8; ++k) o[k] = 0.0f;
+  for (int tile = t0; tile < t1; tile += 64) {
+    const int t = tile + lane;
+    const bool valid = t < t1;
+    float sc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (valid) {
+      const float* lr = lat_row(t);
+      const float* rr = rope_row(t);
+      float rs = 0.0f;
+      for (int i = 0; i < dr; ++i) rs = fmaf(sq[dc + i], rr[i], rs);
+      for (int br = 0; br < NB; ++br) {
+        float acc = rs;
+        for (int c = 0; c < dcb; ++c) acc = fmaf(sq[br * dcb + c], lr[br * dcb + c], acc);
+        sc[br] = acc;
+      }
+    }
+    for (int br = 0; br < NB; ++br) {
+      const float mx = wave_max(sc[br]);
+      const float mn = fmaxf(m[br], mx);
+      alpha[br] = exp2f(m[br] - mn);
+      const float pv = valid ? exp2f(sc[br] - mn) : 0.0f;
+      l[br] = alpha[br] * l[br] + wave_sum(pv);
+      m[br] = mn;
+      sp[lane * 4 + br] = pv;
+    }
+    __syncthreads();
+    const int nt = min(64, t1 - tile);
+    for (int k = 0; k < 8; ++k) {
+      const int d = lane + 64 * k;
+      if (d >= dc) break;
+      const int br = d / dcb;
+      float acc = o[k] * alpha[br];
+      for (int j = 0; j < nt; ++j) acc = fmaf(sp[j * 4 + br], lat_row(tile + j)[d], acc);
+      o[k] = acc;
+    }
+    __syncthreads();
+  }
+  for (int k = 0; k < 8; ++k) {
+    const int d = lane + 64 * k;
+    if (d >= dc) break;
+    part_o[(((size_t)b * S + s) * H + h) * dc + d] = o[k];
+  }
+  if (lane < NB) {
+    ml[((size_t)lane * H + h) * 2 + 0] = m[lane];
+    ml[((size_t)lane * H + h) * 2 + 1] = l[lane];
+  }
+}
+
+hipError_t launch_main_f32(const Plan& p, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((size_t)p.B * p.splits * p.H));
+  hipLaunchKernelGGL(k_main_f32, grid, dim3(64), 0, s, (const float*)a.qcat,
+                     (const float*)a.latent, (const float*)a.rope, a.lat_tok, a.lat_seq,
+                     a.rope_tok, a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged,
+                     a.part_o, a.part_ml, p.H, p.splits, p.chunk, p.NB, p.dcb, p.dr);
+  return hipGetLastError();
+}
+
+}  // namespace mla

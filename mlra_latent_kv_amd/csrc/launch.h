@@ -1,0 +1,37 @@
+// Internal launch interface between the C ABI (api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "plan.h"
+
+namespace mla {
+
+struct DecodeArgs {
+  const void* q_nope;
+  const void* q_rope;
+  const void* latent;
+  const void* rope;
+  const int32_t* seqlens;
+  const int32_t* block_table;
+  const void* w_uk;
+  const void* w_uv;
+  void* out;
+  int64_t lat_tok, lat_seq, rope_tok, rope_seq, bt_stride;
+  float softmax_scale, out_scale, rope_theta;
+  // workspace regions
+  void* qcat;       // [B][H][row] storage dtype, pre-scaled by softmax_scale*log2(e)
+  float* part_o;    // [B][S][H][d_c]
+  float* part_ml;   // [B][S][NB][H][2]  (running max in log2 units, running sum)
+  float* olat;      // [B][H][d_c]
+};
+
+hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_main_f32(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
+                              int d_rope, float theta, int dtype, hipStream_t s);
+
+}  // namespace mla

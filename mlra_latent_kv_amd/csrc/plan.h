@@ -1,0 +1,50 @@
+// Host-side argument validation and launch plan for the decode step.
+// Pure C++ (no HIP): the same source is compiled into the HIP library and, on its own,
+// into a host-only test binary.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "mla_decode.h"
+
+namespace mla {
+
+constexpr int kPage = MLA_PAGE_SIZE;   // tokens per page == tokens per main-loop tile
+constexpr int kHeadGroup = 32;         // heads per workgroup of the bf16 main kernel
+constexpr int kTargetWorkgroups = 256; // one per CU of an MI355X; the split heuristic aims here
+constexpr size_t kWsAlign = 256;
+
+enum class Path { kBf16Mfma, kF32Simt };
+
+struct Plan {
+  int B, H, NB, dcb, dc, dr, dn, dv, row;
+  int dtype, elem;
+  int paged;
+  int max_seqlen;
+  int n_tiles;   // ceil(max_seqlen / 64), >= 1
+  int splits;    // sequence splits per sequence
+  int chunk;     // tokens per split, multiple of 64
+  int n_hg;      // head groups of the bf16 kernel (H / 32); 0 on the fp32 path
+  Path path;
+  // workspace layout (byte offsets)
+  size_t off_qcat, off_part_o, off_part_ml, off_olat, bytes;
+};
+
+// Validates *p (shape, dtype, support, strides) and fills *plan.  Touches no device.
+mla_status make_plan(const mla_params* p, Plan* plan);
+
+// Per-call checks on top of make_plan: required pointers, alignment, workspace size,
+// and the branch count the entry point accepts (1 for mla_decode, 4 for mlra_decode).
+mla_status check_call(const mla_params* p, const Plan& plan, int want_branches,
+                      const void* q_nope, const void* q_rope, const void* latent,
+                      const void* rope, const int32_t* seqlens, const int32_t* block_table,
+                      const void* w_uk, const void* w_uv, const void* out,
+                      const void* workspace, size_t workspace_bytes);
+
+mla_status check_rope_rotate(const void* x, int64_t row_stride, const int32_t* pos,
+                             int64_t n_rows, int32_t d_rope, float theta, int32_t dtype);
+
+const char* status_str(int32_t s);
+
+}  // namespace mla

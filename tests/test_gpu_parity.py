@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
+inputs.  Tolerance for bf16 storage with fp32 accumulation: max abs error <= 2e-2 and
+relative L2 <= 1e-2 over the whole output; the fp32 path must agree to 1e-5.
+
+Under the default value distribution the attention is close to uniform, so every bf16 case
+also runs a "sharp" variant (query scaled so logits have std ~2), and negative controls
+plant mistakes in the *oracle* to show the tolerance separates a right answer from a
+plausibly wrong one.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from mlra_latent_kv_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-5, 1e-5)}
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def oracle_out(inp, batches=None, heads=None, **over):
+    """Oracle output for ``inp``; ``over`` replaces inputs or arguments (negative controls)."""
+    dt = inp["dtype"]
+    g = lambda k, d: over.get(k, d)
+    return O.mla_decode(g("q_nope", inp["q_nope"]), g("q_rope", inp["q_rope"]), inp["cache"],
+                        g("seqlens", inp["seqlens"]), inp["w_uk"], g("w_uv", inp["w_uv"]),
+                        d_rope=inp["workload"].d_rope, scale=g("scale", inp["softmax_scale"]),
+                        out_scale=inp["out_scale"], theta=inp["rope_theta"],
+                        page_size=inp["page_size"], block_table=g("block_table", inp["block_table"]),
+                        to_f64=lambda a: I.to_f64(a, dt), batches=batches, heads=heads)
+
+
+def gpu_out(inp, num_splits=0):
+    import torch
+    from mlra_latent_kv_amd import harness as H
+    case = H.to_device(inp, num_splits=num_splits)
+    out = case.run()
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), case
+
+
+def assert_close(got, ref, dtype, what=""):
+    max_abs_tol, rel_tol = TOL[dtype]
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    rl = rel_l2(got, ref) if got.size else 0.0
+    note(f"  {what}: max_abs={err:.3e} rel_l2={rl:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= max_abs_tol and rl <= rel_tol, (what, err, rl)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    import os
+    from mlra_latent_kv_amd import binding as B
+    if not os.path.exists(B.LIB_PATH):
+        from mlra_latent_kv_amd import build
+        build.build()
+    B.load()
+
+
+# ----------------------------------------------------------------------------- RoPE write path
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_rotate_matches_oracle(dtype):
+    import torch
+    from mlra_latent_kv_amd import binding as B
+    rng = np.random.default_rng(4)
+    n, d, stride = 1000, 64, 80
+    x = rng.standard_normal((n, stride)).astype(np.float32)
+    xs = I.to_storage(x, dtype)
+    pos = rng.integers(0, 131072, n).astype(np.int32)
+    pos[:5] = [0, 1, 131071, -1, 4095]
+    t = (torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16) if dtype == "bf16"
+         else torch.from_numpy(xs)).cuda()
+    before = t.clone()
+    B.mla_rope_rotate(t, stride, torch.from_numpy(pos).cuda(), n, d, 10000.0,
+                      B.MLA_BF16 if dtype == "bf16" else B.MLA_F32)
+    torch.cuda.synchronize()
+    got = t.float().cpu().numpy().astype(np.float64)
+    src = I.to_f64(xs, dtype)
+    ref = src.copy()
+    ok = pos >= 0
+    ref[ok, :d] = O.rope(src[ok, :d], pos[ok], 10000.0)
+    assert torch.equal(t[:, d:], before[:, d:])          # columns past d_rope untouched
+    assert torch.equal(t[3], before[3])                  # pos < 0 leaves the row unchanged
+    if dtype == "f32":
+        assert np.abs(got - ref).max() < 2e-6
+    else:  # one bf16 rounding of the exact rotation
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+
+
+# ----------------------------------------------------------------------------- fp32 path
+
+def test_tiny_f32_workload_full_size():
+    w = I.WORKLOADS["tiny_mla_f32_b1_h4_l64"]
+    inp = I.make_inputs(w)
+    got, _ = gpu_out(inp)
+    assert_close(got, oracle_out(inp), "f32", w.name)
+
+
+F32_MLRA = I.Workload("mlra4_f32_small", batch=1, heads=4, branches=4, d_nope=16, d_v=16, d_cb=16,
+                      d_rope=8, dtype="f32", paged=False, seqlen=64, out_scale=0.5, seed=77)
+
+
+@pytest.mark.parametrize("w", [I.WORKLOADS["tiny_mla_f32_b1_h4_l64"], F32_MLRA], ids=lambda w: w.name)
+@pytest.mark.parametrize("paged", [False, True])
+def test_f32_ragged(w, paged):
+    inp = I.make_inputs(w, seqlens=[1, 63, 64, 65, 200, 0], paged=paged, q_gain=I.sharp_q_gain(w))
+    for splits in (0, 2):
+        got, _ = gpu_out(inp, num_splits=splits)
+        assert_close(got, oracle_out(inp), "f32", f"{w.name} paged={paged} splits={splits}")
+
+
+# ----------------------------------------------------------------------------- bf16 path
+
+BF16 = ["mla_bf16_b32_h128_l4096", "mla_bf16_paged_b64_h32_l1k-32k", "mlra4_bf16_b32_h32_l8192",
+        "mla_bf16_paged_b4_h128_l131072"]
+RAGGED = [1, 63, 64, 65, 300, 1000, 2049]
+
+
+@pytest.mark.parametrize("sharp", [False, True], ids=["default", "sharp"])
+@pytest.mark.parametrize("wname", BF16)
+def test_bf16_small_ragged(wname, sharp):
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=RAGGED, q_gain=I.sharp_q_gain(w) if sharp else 1.0)
+    got, _ = gpu_out(inp)
+    assert_close(got, oracle_out(inp), "bf16", f"{wname} sharp={sharp}")
+
+
+@pytest.mark.parametrize("wname", ["mla_bf16_b32_h128_l4096", "mlra4_bf16_b32_h32_l8192"])
+def test_split_count_invariance(wname):
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=[700, 1500, 129], q_gain=I.sharp_q_gain(w))
+    ref = oracle_out(inp)
+    outs = {}
+    for splits in (1, 2, 7, 24):
+        outs[splits], _ = gpu_out(inp, num_splits=splits)
+        assert_close(outs[splits], ref, "bf16", f"{wname} splits={splits}")
+    for s in (2, 7, 24):
+        assert rel_l2(outs[s], outs[1]) < 3e-3
+
+
+def test_paged_and_contiguous_bitwise_equal():
+    import torch
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    lens = [65, 1000, 64, 333]
+    a, _ = gpu_out(I.make_inputs(w, seed=5, seqlens=lens, paged=True), num_splits=3)
+    b, _ = gpu_out(I.make_inputs(w, seed=5, seqlens=lens, paged=False), num_splits=3)
+    assert np.array_equal(a, b)
+
+
+def test_run_to_run_bitwise_deterministic():
+    import torch
+    w = I.WORKLOADS["mlra4_bf16_b32_h32_l8192"]
+    inp = I.make_inputs(w, seqlens=[900, 31], q_gain=I.sharp_q_gain(w))
+    _, case = gpu_out(inp)
+    first = case.out.clone()
+    for _ in range(3):
+        case.run()
+        torch.cuda.synchronize()
+        assert torch.equal(case.out, first)
+
+
+def test_zero_length_sequences_write_zeros():
+    w = I.WORKLOADS["mla_bf16_b32_h128_l4096"]
+    inp = I.make_inputs(w, seqlens=[0, 130, 0])
+    got, _ = gpu_out(inp)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    assert_close(got, oracle_out(inp), "bf16", "zero-length mix")
+
+
+# ----------------------------------------------------------------------------- negative controls
+
+@pytest.mark.parametrize("wname", ["mla_bf16_paged_b64_h32_l1k-32k", "mlra4_bf16_b32_h32_l8192"])
+def test_negative_controls_fail_the_tolerance(wname):
+    """Plant each plausible mistake in the oracle; the GPU output must NOT match it."""
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=[190, 700, 1300], q_gain=I.sharp_q_gain(w))
+    got, _ = gpu_out(inp)
+    assert_close(got, oracle_out(inp), "bf16", "correct oracle")
+    controls = {
+        "uniform weights": dict(q_nope=np.zeros_like(inp["q_nope"]), q_rope=np.zeros_like(inp["q_rope"])),
+        "rope term dropped": dict(q_rope=np.zeros_like(inp["q_rope"])),
+        "scale x2": dict(scale=2 * inp["softmax_scale"]),
+        "seqlen - 1": dict(seqlens=inp["seqlens"] - 1),
+    }
+    if w.branches == 4:
+        wv = inp["w_uv"].copy()
+        wv[2] = 0
+        controls["branch 2 dropped"] = dict(w_uv=wv)
+    if inp["block_table"] is not None:
+        bt = inp["block_table"].copy()
+        bt[0, [0, 1]] = bt[0, [1, 0]]
+        controls["two pages swapped"] = dict(block_table=bt)
+    for name, over in controls.items():
+        bad = oracle_out(inp, **over)
+        rl = rel_l2(got, bad)
+        note(f"  control {name}: rel_l2 vs GPU = {rl:.3e}")
+        assert rl > TOL["bf16"][1], name
+
+
+# ----------------------------------------------------------------------------- full sizes
+
+SAMPLES = {
+    "mla_bf16_b32_h128_l4096": ([0, 17, 31], [0, 63, 127]),
+    "mla_bf16_paged_b64_h32_l1k-32k": ([0, 21, 63], [0, 31]),
+    "mlra4_bf16_b32_h32_l8192": ([0, 31], [0, 13, 31]),
+    "mla_bf16_paged_b4_h128_l131072": ([0, 3], [5, 120]),
+}
+
+
+@pytest.mark.parametrize("wname", list(SAMPLES))
+def test_full_size_sampled(wname):
+    """Each workload at full size, in the launch configuration the benchmark times, checked on
+    sampled (sequence, head) outputs that the oracle computes one by one; every output must be
+    finite."""
+    import torch
+    w = I.WORKLOADS[wname]
+    note(f"  generating {wname}")
+    inp = I.make_inputs(w)
+    got, case = gpu_out(inp)
+    del case
+    torch.cuda.empty_cache()
+    assert np.all(np.isfinite(got))
+    bs, hs = SAMPLES[wname]
+    ref = oracle_out(inp, batches=bs, heads=hs)
+    assert_close(got[np.ix_(bs, hs)], ref, "bf16", f"{wname} sampled")
