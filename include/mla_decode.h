@@ -83,8 +83,9 @@ typedef struct mla_params {
  *  - MLA_F32 (generic SIMT path): NB in {1, 4}, NB*d_latent <= 512, d_rope even <= 64,
  *    d_nope <= 256, d_v <= 256, any H >= 1.
  *  - page_size in {0, 64}.
- * Alignment: bf16 latent/rope pointers 16-byte aligned and their strides multiples of
- * 8 elements; fp32 pointers 4-byte aligned.
+ * Alignment: bf16 latent, rope, q_nope, w_uk and w_uv pointers 16-byte aligned and the
+ * cache strides multiples of 8 elements; other pointers aligned to their element size.
+ * num_splits (given or chosen) is at most 512.
  */
 
 /*
@@ -148,6 +149,25 @@ mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_ro
                        const void* latent, const void* rope, const int32_t* seqlens,
                        const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Tracing variants: identical to mla_decode / mlra_decode, and additionally record five
+ * caller-created HIP events (hipEvent_t values passed as void*) on `stream` at the stage
+ * boundaries: events[0] before the prologue, events[1] before the split-K main loop,
+ * events[2] before the combine, events[3] before the epilogue, events[4] after it.  With
+ * events == NULL they behave exactly like the plain entry points.  A failed hipEventRecord
+ * returns MLA_ERR_HIP.
+ */
+mla_status mla_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
+                            const void* latent, const void* rope, const int32_t* seqlens,
+                            const int32_t* block_table, const void* w_uk, const void* w_uv,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events);
+mla_status mlra_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
+                             const void* latent, const void* rope, const int32_t* seqlens,
+                             const int32_t* block_table, const void* w_uk, const void* w_uv,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events);
 
 /*
  * Rotate rows of a rotary-key cache in place (the write-side step that gives the decoupled

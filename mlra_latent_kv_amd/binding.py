@@ -59,6 +59,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m mlra_latent_kv_amd.build`")
+    # torch ships its own copy of the HIP runtime; load it first so that the library binds to
+    # that copy (same soname) and shares torch's device memory and streams.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(MlaParams)
     lib.mla_workspace_size.argtypes = [P, ctypes.POINTER(c_size_t)]
@@ -66,12 +69,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     dec = [P] + [c_void_p] * 10 + [c_size_t, c_void_p]
     lib.mla_decode.argtypes = dec
     lib.mlra_decode.argtypes = dec
+    lib.mla_decode_timed.argtypes = dec + [c_void_p]
+    lib.mlra_decode_timed.argtypes = dec + [c_void_p]
     lib.mla_rope_rotate.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_float,
                                     c_int32, c_void_p]
     lib.mla_status_str.argtypes = [c_int32]
     lib.mla_status_str.restype = ctypes.c_char_p
     for f in ("mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
-              "mla_rope_rotate"):
+              "mla_decode_timed", "mlra_decode_timed", "mla_rope_rotate"):
         getattr(lib, f).restype = c_int32
     _lib = lib
     return lib
@@ -125,28 +130,32 @@ def num_splits(params: MlaParams) -> int:
 
 
 def _decode(fname, params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
-            workspace, workspace_bytes=None, stream=None, check=True) -> int:
+            workspace, workspace_bytes=None, stream=None, check=True, events=None) -> int:
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    st = getattr(load(), fname)(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(latent),
-                                _ptr(rope), _ptr(seqlens), _ptr(block_table), _ptr(w_uk),
-                                _ptr(w_uv), _ptr(out), _ptr(workspace), workspace_bytes,
-                                _stream(stream))
+    args = [ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(latent), _ptr(rope),
+            _ptr(seqlens), _ptr(block_table), _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace),
+            workspace_bytes, _stream(stream)]
+    if events is not None:
+        fname += "_timed"
+        args.append(ctypes.cast(events, c_void_p))
+    st = getattr(load(), fname)(*args)
     if check and st:
         raise MlaError(st, fname)
     return st
 
 
 def mla_decode(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
-               workspace, workspace_bytes=None, stream=None, check=True) -> int:
+               workspace, workspace_bytes=None, stream=None, check=True, events=None) -> int:
+    """``events``: optional ctypes array of 5 hipEvent_t -> calls mla_decode_timed."""
     return _decode("mla_decode", params, q_nope, q_rope, latent, rope, seqlens, block_table,
-                   w_uk, w_uv, out, workspace, workspace_bytes, stream, check)
+                   w_uk, w_uv, out, workspace, workspace_bytes, stream, check, events)
 
 
 def mlra_decode(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
-                workspace, workspace_bytes=None, stream=None, check=True) -> int:
+                workspace, workspace_bytes=None, stream=None, check=True, events=None) -> int:
     return _decode("mlra_decode", params, q_nope, q_rope, latent, rope, seqlens, block_table,
-                   w_uk, w_uv, out, workspace, workspace_bytes, stream, check)
+                   w_uk, w_uv, out, workspace, workspace_bytes, stream, check, events)
 
 
 def mla_rope_rotate(x, row_stride: int, pos, n_rows: int, d_rope: int, theta: float, dtype: int,

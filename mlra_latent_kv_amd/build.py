@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["api.hip", "kernels_generic.hip", "main_bf16.hip"]
+HIP_SOURCES = ["api.hip", "kernels_generic.hip", "kernels_bf16_aux.hip", "main_bf16.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 
@@ -38,7 +38,10 @@ def _compile(src: str) -> str:
     if src.endswith(".hip"):
         # packed-fp32 instruction selection is disabled for all device code
         cmd += ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-                "-Xclang", "-packed-fp32-ops"]
+                "-Xclang", "-packed-fp32-ops",
+                # keep MFMA accumulators in VGPRs: the softmax rescales them every tile, and
+                # VALU cannot operate on AGPRs (each rescale would copy them out and back)
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -56,6 +59,10 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    und = subprocess.run(["nm", "-u", "-C", tmp], capture_output=True, text=True).stdout
+    missing = [ln.strip() for ln in und.splitlines() if "mla::" in ln]
+    if missing:
+        raise RuntimeError(f"unresolved library symbols: {missing}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

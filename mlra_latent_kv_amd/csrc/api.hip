@@ -19,7 +19,7 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
                       const void* q_rope, const void* latent, const void* rope,
                       const int32_t* seqlens, const int32_t* block_table, const void* w_uk,
                       const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, void* const* events) {
   Plan plan;
   mla_status st = make_plan(p, &plan);
   if (st != MLA_OK) return st;
@@ -49,14 +49,23 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
   a.qcat = ws + plan.off_qcat;
   a.part_o = reinterpret_cast<float*>(ws + plan.off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + plan.off_part_ml);
-  a.olat = reinterpret_cast<float*>(ws + plan.off_olat);
+  a.olat = ws + plan.off_olat;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_prologue(plan, a, s);
+  auto mark = [&](int i) {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  const bool bf = plan.path == Path::kBf16Mfma;
+  if (e == hipSuccess) e = bf ? launch_prologue_bf16(plan, a, s) : launch_prologue(plan, a, s);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
-    e = plan.path == Path::kBf16Mfma ? launch_main_bf16(plan, a, s) : launch_main_f32(plan, a, s);
+    e = bf ? launch_main_bf16(plan, a, s) : launch_main_f32(plan, a, s);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_combine(plan, a, s);
-  if (e == hipSuccess) e = launch_epilogue(plan, a, s);
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = bf ? launch_epilogue_bf16(plan, a, s) : launch_epilogue(plan, a, s);
+  if (e == hipSuccess) e = mark(4);
   return to_status(e);
 }
 
@@ -85,7 +94,7 @@ mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_rop
                       const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
                       void* workspace, size_t workspace_bytes, void* stream) {
   return run_decode(1, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
-                    workspace, workspace_bytes, stream);
+                    workspace, workspace_bytes, stream, nullptr);
 }
 
 mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_rope,
@@ -93,7 +102,25 @@ mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_ro
                        const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
                        void* workspace, size_t workspace_bytes, void* stream) {
   return run_decode(4, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
-                    workspace, workspace_bytes, stream);
+                    workspace, workspace_bytes, stream, nullptr);
+}
+
+mla_status mla_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
+                            const void* latent, const void* rope, const int32_t* seqlens,
+                            const int32_t* block_table, const void* w_uk, const void* w_uv,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events) {
+  return run_decode(1, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                    workspace, workspace_bytes, stream, events);
+}
+
+mla_status mlra_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
+                             const void* latent, const void* rope, const int32_t* seqlens,
+                             const int32_t* block_table, const void* w_uk, const void* w_uv,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events) {
+  return run_decode(4, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                    workspace, workspace_bytes, stream, events);
 }
 
 mla_status mla_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,

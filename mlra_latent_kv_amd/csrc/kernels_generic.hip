@@ -1,6 +1,6 @@
-// Prologue (absorbed query), split combine, W_UV epilogue, rotary-key rotation, and the
-// fp32 SIMT main loop used for small fp32 shapes.  The bf16 MFMA main loop is in
-// main_bf16.hip.
+// fp32 path (prologue, W_UV epilogue, SIMT main loop for small fp32 shapes), the split
+// combine shared by both paths, and the rotary-key rotation.  The bf16 path's prologue and
+// epilogue are in kernels_bf16_aux.hip, its main loop in main_bf16.hip.
 //
 // Absorption ("超越 GQA 的推理革命…MLA…", section 矩陣吸收): the key up-projection W_UK is
 // folded into the query (prologue) and the value up-projection W_UV is applied once to the
@@ -70,12 +70,7 @@ hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(p.H, (p.B + kBatchBlock - 1) / kBatchBlock);
   const size_t lds = (size_t)kBatchBlock * p.NB * p.dn * sizeof(float);
   const float qscale = a.softmax_scale * kLog2e;
-  if (p.dtype == MLA_BF16)
-    hipLaunchKernelGGL(k_prologue<bf16>, grid, dim3(256), lds, s, (const bf16*)a.q_nope,
-                       (const bf16*)a.q_rope, a.seqlens, (const bf16*)a.w_uk, (bf16*)a.qcat, p.B,
-                       p.H, p.NB, p.dn, p.dcb, p.dr, qscale, (double)a.rope_theta);
-  else
-    hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, s, (const float*)a.q_nope,
+  hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, s, (const float*)a.q_nope,
                        (const float*)a.q_rope, a.seqlens, (const float*)a.w_uk, (float*)a.qcat,
                        p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, (double)a.rope_theta);
   return hipGetLastError();
@@ -84,36 +79,66 @@ hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
 // ----------------------------------------------------------------------------- combine
 // Per (b, h, branch): merge the splits' (m_s, l_s, O_s) with log-sum-exp weights:
 //   M = max_s m_s,  o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// Splits with no tokens carry m = -inf and are skipped (their O_s is never read).
+// One workgroup handles 8 heads of one sequence: the split weights are formed once in LDS,
+// then the partial outputs stream through with 16-byte loads.  Splits with no tokens
+// carry m = -inf and weight 0 (their O_s is never read).
+constexpr int kCombHeads = 8;
+
+template <typename TO>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o,
                                                  const float* __restrict__ part_ml,
-                                                 float* __restrict__ olat, int H, int S, int NB,
+                                                 TO* __restrict__ olat, int H, int S, int NB,
                                                  int dcb) {
-  const int h = blockIdx.x, b = blockIdx.y;
+  extern __shared__ float sw[];  // [kCombHeads][NB][S]
+  const int hb = blockIdx.x, b = blockIdx.y;
+  const int h0 = hb * kCombHeads;
+  const int nh = min(kCombHeads, H - h0);
   const int dc = NB * dcb;
-  for (int d = threadIdx.x; d < dc; d += blockDim.x) {
-    const int br = d / dcb;
+  for (int t = threadIdx.x; t < nh * NB; t += blockDim.x) {
+    const int hl = t / NB, br = t % NB;
+    const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + (h0 + hl) * 2;
+    const size_t sstride = (size_t)NB * H * 2;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s)
-      M = fmaxf(M, part_ml[((((size_t)b * S + s) * NB + br) * H + h) * 2]);
-    float num = 0.0f, den = 0.0f;
-    if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s * sstride]);
+    float den = 0.0f;
+    if (M != -INFINITY)
       for (int s = 0; s < S; ++s) {
-        const float* ml = part_ml + ((((size_t)b * S + s) * NB + br) * H + h) * 2;
-        const float m = ml[0];
-        if (m == -INFINITY) continue;
-        const float w = exp2f(m - M);
-        den = fmaf(w, ml[1], den);
-        num = fmaf(w, part_o[(((size_t)b * S + s) * H + h) * dc + d], num);
+        const float m = ml[s * sstride];
+        if (m != -INFINITY) den = fmaf(exp2f(m - M), ml[s * sstride + 1], den);
       }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    float* wrow = sw + (hl * NB + br) * S;
+    for (int s = 0; s < S; ++s) {
+      const float m = ml[s * sstride];
+      wrow[s] = (m == -INFINITY) ? 0.0f : exp2f(m - M) * inv;
     }
-    olat[((size_t)b * H + h) * dc + d] = den > 0.0f ? num / den : 0.0f;
+  }
+  __syncthreads();
+  const int q4 = dc / 4;
+  for (int it = threadIdx.x; it < nh * q4; it += blockDim.x) {
+    const int hl = it / q4, d = 4 * (it % q4);
+    const float* wrow = sw + (hl * NB + d / dcb) * S;
+    const float* src = part_o + (((size_t)b * S) * H + h0 + hl) * dc + d;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < S; ++s) {
+      const float wt = wrow[s];
+      if (wt != 0.0f) acc += wt * *(const f32x4*)(src + (size_t)s * H * dc);
+    }
+    TO* dst = olat + ((size_t)b * H + h0 + hl) * dc + d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = from_f32<TO>(acc[e]);
   }
 }
 
 hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(p.H, p.B), dim3(256), 0, s, a.part_o, a.part_ml, a.olat,
-                     p.H, p.splits, p.NB, p.dcb);
+  const dim3 grid((p.H + kCombHeads - 1) / kCombHeads, p.B);
+  const size_t lds = (size_t)kCombHeads * p.NB * p.splits * sizeof(float);
+  if (p.dtype == MLA_BF16)
+    hipLaunchKernelGGL(k_combine<bf16>, grid, dim3(256), lds, s, a.part_o, a.part_ml,
+                       (bf16*)a.olat, p.H, p.splits, p.NB, p.dcb);
+  else
+    hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), lds, s, a.part_o, a.part_ml,
+                       (float*)a.olat, p.H, p.splits, p.NB, p.dcb);
   return hipGetLastError();
 }
 
@@ -155,12 +180,8 @@ __global__ __launch_bounds__(128) void k_epilogue(const float* __restrict__ olat
 hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(p.H, (p.B + kBatchBlock - 1) / kBatchBlock);
   const size_t lds = (size_t)kBatchBlock * p.dc * sizeof(float);
-  if (p.dtype == MLA_BF16)
-    hipLaunchKernelGGL(k_epilogue<bf16>, grid, dim3(128), lds, s, a.olat, (const bf16*)a.w_uv,
-                       (bf16*)a.out, p.B, p.H, p.NB, p.dcb, p.dv, a.out_scale);
-  else
-    hipLaunchKernelGGL(k_epilogue<float>, grid, dim3(128), lds, s, a.olat, (const float*)a.w_uv,
-                       (float*)a.out, p.B, p.H, p.NB, p.dcb, p.dv, a.out_scale);
+  hipLaunchKernelGGL(k_epilogue<float>, grid, dim3(128), lds, s, (const float*)a.olat,
+                     (const float*)a.w_uv, (float*)a.out, p.B, p.H, p.NB, p.dcb, p.dv, a.out_scale);
   return hipGetLastError();
 }
 

@@ -23,14 +23,16 @@ struct DecodeArgs {
   void* qcat;       // [B][H][row] storage dtype, pre-scaled by softmax_scale*log2(e)
   float* part_o;    // [B][S][H][d_c]
   float* part_ml;   // [B][S][NB][H][2]  (running max in log2 units, running sum)
-  float* olat;      // [B][H][d_c]
+  void* olat;       // [B][H][d_c], bf16 on the bf16 path (MFMA operand), fp32 otherwise
 };
 
-hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s);       // fp32 path
+hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_main_f32(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s);
-hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s);       // fp32 path
+hipError_t launch_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
                               int d_rope, float theta, int dtype, hipStream_t s);
 

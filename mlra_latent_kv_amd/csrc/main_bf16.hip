@@ -1,56 +1,95 @@
 // Split-K main loop of the absorbed MLA / MLRA-4 decode step for gfx950 (bf16 in, fp32 acc).
 //
 // Work item = (sequence b, sequence split s, group of 32 heads).  The workgroup streams the
-// split's cached rows [c_KV (512) | k_rope (64)] in 64-token tiles (one page each) through
-// LDS and, per tile:
-//   S  = q_cat . tile^T       scores of 32 heads x 64 tokens (MFMA 32x32x16 bf16)
+// split's cached rows [c_KV (512) | k_rope (64)] in 32-token tiles through a ring of LDS
+// buffers filled by direct-to-LDS buffer loads (no staging registers, rows past the end of
+// the sequence read back as zeros), and per tile computes
+//   S  = q_cat . tile^T       scores of 32 heads x 32 tokens (MFMA 32x32x16 bf16)
 //   online softmax            running max / sum per head (per branch for MLRA-4)
-//   O += P . tile[:, :512]    latent-space output (MFMA 32x32x16 bf16, operands from LDS
-//                             transpose reads)
+//   O += P . tile[:, :512]    latent-space output; the value operand is read from the
+//                             token-major tile with ds_read_b64_tr_b16
 // and finally writes its partial (m, l, O) for the combine kernel.  This is the absorbed
-// form of the yololab page (section 矩陣吸收): all heads share the one cached latent, so
-// each tile is a dense [heads x 576] . [576 x tokens] contraction and the latent also serves
-// as the value operand.  For MLRA-4 ("[ICLR 2025] MLRA…", section 2.1) the latent holds four
-// 128-wide branches with independent softmaxes; the rotary score is shared by them.
+// form of the yololab MLA page (section 矩陣吸收): all heads share the one cached latent, so
+// each tile is a dense [heads x 576] . [576 x tokens] contraction and the latent doubles as
+// the value.  For MLRA-4 ("[ICLR 2025] MLRA…", section 2.1) the latent holds four
+// 128-wide branches with independent softmaxes that share the rotary score.
 //
-// Wave w (of 4) owns latent columns [128w, 128w+128) (= branch w for MLRA-4) and rotary
-// columns [512+16w, 512+16w+16):
-//   * QK: it computes the partial score of its columns for all 32 heads x 64 tokens; the
-//     four partials meet in LDS and every wave forms the full scores of the heads.
-//   * PV: it accumulates O^T[d][h] for its 128 latent columns, reading the value operand
-//     with ds_read_b64_tr_b16 straight from the token-major tile.
+// Wave w (of 4) owns latent columns [128w, 128w+128): it computes their score contribution
+// and accumulates O^T for those columns.
+//  * MLA (one branch): the waves' partial scores (plus a quarter of the rotary columns each)
+//    meet in LDS; wave w sums them for heads 8w..8w+7, runs the softmax for those heads, and
+//    publishes bf16 probabilities and rescale factors for everyone's PV step.
+//  * MLRA-4: wave w's columns are exactly branch w; it also computes the full rotary score
+//    itself, so its branch's scores, softmax and probabilities never leave its registers.
 #include "device_common.h"
 #include "launch.h"
 
 namespace mla {
 namespace {
 
-constexpr int kT = 64;                              // tokens per tile (one page)
-constexpr int kHG = kHeadGroup;                     // heads per workgroup
-constexpr int kThreads = 256;                       // 4 waves
+constexpr int kTT = 32;                              // tokens per tile (half a page)
+constexpr int kHG = kHeadGroup;                      // heads per workgroup
+constexpr int kThreads = 256;                        // 4 waves
 constexpr int kDC = 512, kDR = 64, kRow = kDC + kDR;
-constexpr int kChunks = kRow / 8;                   // 16-byte chunks per row (72)
-constexpr int kLatChunks = kDC / 8;                 // 64
-constexpr int kLoads = kT * kChunks / kThreads;     // 16-byte loads per thread per tile (18)
-constexpr int kKPitch = kRow + 8;                   // LDS row pitch, bf16 elements (1168 B)
-constexpr int kSPitch = kT + 4;                     // LDS score row pitch, floats
+constexpr int kLatPitchB = kDC * 2 + 16;             // LDS bytes per latent row (bank skew)
+constexpr int kLatPitch = kLatPitchB / 2;            // ... in bf16 elements
+constexpr int kRopeOff = kTT * kLatPitchB;           // rotary region of a buffer
+constexpr int kBufBytes = kRopeOff + kTT * kDR * 2;  // one tile
+constexpr int kSPitch = kTT + 4;                     // fp32 partial-score row pitch
+constexpr int kPPitch = kTT + 8;                     // bf16 probability row pitch
+constexpr int kLoadsPerTile = 9;                     // buffer loads per wave per tile
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+template <int NB>
+struct Ring {
+  static constexpr int kBufs = NB == 1 ? 3 : 4;
+};
 
 template <int NB>
 struct Smem {
-  bf16 k[kT * kKPitch];                             // current tile, token-major
-  float s[NB == 1 ? 4 : 8][kHG * kSPitch];          // per-wave partial scores [h][t]
+  char ring[Ring<NB>::kBufs][kBufBytes];
+  float s[NB == 1 ? 4 * kHG * kSPitch : 4];   // MLA: per-wave partial scores [w][h][t]
+  bf16 p[NB == 1 ? kHG * kPPitch : 8];        // MLA: probabilities [h][t]
+  float alpha[kHG];                           // MLA: per-head rescale of this tile
 };
 
-__device__ __forceinline__ bf16x8 tr_pair(const bf16* p) {
-  // two 4-row transposed reads: rows r..r+3 and r+4..r+7 of the same 16 columns
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16*lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Wait until at most n tiles' worth of this wave's buffer loads are still in flight.
+__device__ __forceinline__ void wait_tiles(int n) {
+  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  if (n <= 0)
+    __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+  else if (n == 1)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerTile);      // vmcnt(9)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * kLoadsPerTile) & 15) | (((2 * kLoadsPerTile) >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also fences global
+// memory, which here would wait for every in-flight tile load (they write LDS
+// asynchronously) and drain the prefetch ring; tile arrival is tracked with explicit
+// vmcnt waits instead (wait_tiles).  The memory clobber keeps the compiler from moving
+// LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Value operand: 8 tokens of one latent column, two transposed 4-row reads `delta` rows apart.
+__device__ __forceinline__ bf16x8 tr_pair(const bf16* p, int delta_rows) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * kKPitch));
-  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + delta_rows * kLatPitch));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 template <int NB>
@@ -60,11 +99,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16(
     int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
     int S, int chunk, int n_hg, int units) {
+  constexpr int kBufs = Ring<NB>::kBufs;
   __shared__ __align__(16) Smem<NB> sm;
 
   // XCD-aware mapping: consecutive blocks go to different XCDs, so the head groups of one
   // (sequence, split) are placed 8 blocks apart -> same XCD, dispatched back to back, and
-  // their repeated reads of the same tiles can hit that XCD's L2.
+  // their reads of the same tiles can hit that XCD's L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, r = bid >> 3;
   const int hg = r % n_hg;
@@ -72,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16(
   if (unit >= units) return;
   const int b = unit / S, s = unit % S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lh = lane & 31, kg = lane >> 5;
+  const int l32 = lane & 31, kg = lane >> 5;
   const int h0 = hg * kHG;
   const int L = seqlens[b];
   const int t_begin = s * chunk;
@@ -87,157 +127,196 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16(
     }
     return;
   }
+  const int n_tiles = (t_end - t_begin + kTT - 1) / kTT;
 
-  // absorbed query of this wave's columns: A operand, lane (head lh, k-group kg)
-  bf16x8 qa[9];
-  {
-    const bf16* qrow = qcat + ((size_t)b * H + h0 + lh) * kRow + 8 * kg;
+  // Tile loads: wave w brings latent rows 8w..8w+7 (one row of 64 x 16 B per instruction)
+  // and the rotary keys of the same 8 rows (one instruction, 16-byte chunks XOR-swizzled by
+  // row so that 32 rows read at one column hit distinct banks).
+  const uint32_t lat_row_b = (uint32_t)(lat_tok * 2), rope_row_b = (uint32_t)(rope_tok * 2);
+  uint32_t voff_lat[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qa[j] = *(const bf16x8*)(qrow + 128 * w + 16 * j);
-    qa[8] = *(const bf16x8*)(qrow + kDC + 16 * w);
-  }
+  for (int j = 0; j < 8; ++j) voff_lat[j] = (8 * w + j) * lat_row_b + 16 * lane;
+  const int rrow = 8 * w + (lane >> 3);
+  const uint32_t voff_rope = rrow * rope_row_b + 16 * ((lane & 7) ^ (rrow & 7));
 
-  u32x4 stage[kLoads];
-  auto load_tile = [&](int t0) {
+  auto issue = [&](int k) {
+    const int t0 = t_begin + kTT * k;
+    const int valid = min(kTT, t_end - t0);
     const bf16* lb;
     const bf16* rb;
     if (paged) {
-      const int64_t pg = bt[(int64_t)b * bt_stride + t0 / kT];
-      lb = latent + pg * lat_seq;
-      rb = rope + pg * rope_seq;
+      const int64_t pg = bt[(int64_t)b * bt_stride + t0 / kPage];
+      lb = latent + pg * lat_seq + (int64_t)(t0 % kPage) * lat_tok;
+      rb = rope + pg * rope_seq + (int64_t)(t0 % kPage) * rope_tok;
     } else {
       lb = latent + (int64_t)b * lat_seq + (int64_t)t0 * lat_tok;
       rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
     }
+    const __amdgpu_buffer_rsrc_t rl = rsrc(lb, valid * lat_row_b);
+    const __amdgpu_buffer_rsrc_t rr = rsrc(rb, valid * rope_row_b);
+    char* buf = sm.ring[k % kBufs];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int c = tid + kThreads * j;
-      const int row = c / kChunks, col = c % kChunks;
-      const bf16* src = col < kLatChunks ? lb + row * lat_tok + col * 8
-                                         : rb + row * rope_tok + (col - kLatChunks) * 8;
-      stage[j] = t0 + row < t_end ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
-    }
+    for (int j = 0; j < 8; ++j) dma16(rl, buf + (8 * w + j) * kLatPitchB, voff_lat[j]);
+    dma16(rr, buf + kRopeOff + w * 1024, voff_rope);
   };
+
+  // absorbed query: MFMA B operand, lane (head l32, k-half kg)
+  constexpr int kQSteps = NB == 1 ? 9 : 12;
+  bf16x8 qb[kQSteps];
+  {
+    const bf16* qrow = qcat + ((size_t)b * H + h0 + l32) * kRow + 8 * kg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qb[j] = *(const bf16x8*)(qrow + 128 * w + 16 * j);
+    if (NB == 1) {
+      qb[8] = *(const bf16x8*)(qrow + kDC + 16 * w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qb[8 + j] = *(const bf16x8*)(qrow + kDC + 16 * j);
+    }
+  }
+
+  for (int k = 0; k < min(kBufs - 1, n_tiles); ++k) issue(k);
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 O[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) O[mb] = f32x16{};
 
-  // transpose-read coordinates for the PV value operand (see tr_pair)
+  // transposed-read source coordinates for the value operand
   const int g = lane >> 4, li = lane & 15;
-  const int tr_row = 8 * (g >> 1) + (li >> 2);
-  const int tr_col = 128 * w + 16 * (g & 1) + 4 * (li & 3);
+  const int v_col = 128 * w + 16 * (g & 1) + 4 * (li & 3);
+  const int v_row = NB == 1 ? 8 * kg + (li >> 2) : 4 * kg + (li >> 2);
+  constexpr int v_delta = NB == 1 ? 4 : 8;
 
-  load_tile(t_begin);
-  for (int t0 = t_begin; t0 < t_end; t0 += kT) {
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int c = tid + kThreads * j;
-      *(u32x4*)(sm.k + (c / kChunks) * kKPitch + (c % kChunks) * 8) = stage[j];
-    }
-    if (t0 + kT < t_end) load_tile(t0 + kT);  // prefetch the next tile into registers
-    __syncthreads();
+  for (int k = 0; k < n_tiles; ++k) {
+    wait_tiles(min(kBufs - 2, n_tiles - 1 - k));
+    lds_barrier();  // tile k landed for every wave; buffer of tile k-1 is free
+    if (k + kBufs - 1 < n_tiles) issue(k + kBufs - 1);
 
-    // ---- partial scores of this wave's columns: S[h][t], M = heads, N = tokens
-    f32x16 acc[2], accr[2];
+    const int t0 = t_begin + kTT * k;
+    const int valid = min(kTT, t_end - t0);
+    const char* buf = sm.ring[k % kBufs];
+    const bf16* lat = (const bf16*)buf;
+    const char* rp = buf + kRopeOff + l32 * 128;
+
+    // ---- scores S^T[t][h] (M = tokens, N = heads) over this wave's columns
+    f32x16 acc = {};
+    {
+      const bf16* arow = lat + l32 * kLatPitch + 128 * w + 8 * kg;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      acc[nb] = f32x16{};
-      accr[nb] = f32x16{};
-      const bf16* krow = sm.k + (32 * nb + lh) * kKPitch + 8 * kg;
+      for (int j = 0; j < 8; ++j)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(arow + 16 * j), qb[j], acc, 0, 0, 0);
+      if (NB == 1) {
+        const int c = 2 * w + kg;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8*)(rp + 16 * (c ^ (l32 & 7))), qb[8], acc, 0, 0, 0);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 kb = *(const bf16x8*)(krow + 128 * w + 16 * j);
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j], kb, acc[nb], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const int c = 2 * j + kg;
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *(const bf16x8*)(rp + 16 * (c ^ (l32 & 7))), qb[8 + j], acc, 0, 0, 0);
+        }
       }
-      const bf16x8 kb = *(const bf16x8*)(krow + kDC + 16 * w);
-      if (NB == 1)
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[8], kb, acc[nb], 0, 0, 0);
-      else
-        accr[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[8], kb, accr[nb], 0, 0, 0);
     }
-    // D layout: lane (token lh, half kg), item i -> head 8*(i/4) + 4*kg + i%4
+    // D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4
+
+    bf16x8 pb[2];
+    float alpha;
+    if (NB == 1) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int j = 0; j < 4; ++j)
+        *(f32x4*)(&sm.s[(w * kHG + l32) * kSPitch + 8 * j + 4 * kg]) =
+            f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+      lds_barrier();
+      // softmax of heads 8w..8w+7: lane -> head hs, tokens tq..tq+3
+      const int hs = 8 * w + (lane >> 3), tq = 4 * (lane & 7);
+      f32x4 x = *(const f32x4*)(&sm.s[(0 * kHG + hs) * kSPitch + tq]);
+#pragma unroll
+      for (int sl = 1; sl < 4; ++sl) x += *(const f32x4*)(&sm.s[(sl * kHG + hs) * kSPitch + tq]);
+      if (valid < kTT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (tq + e >= valid) x[e] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+      const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid token
+      const float a = exp2f(m_run - m_new);
+      bf16 pe[4];
+      float psum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pe[e] = (bf16)exp2f(x[e] - m_new);
+        psum += (float)pe[e];  // normalise with the rounded weights the MFMA uses
+      }
+      psum += __shfl_xor(psum, 1, 64);
+      psum += __shfl_xor(psum, 2, 64);
+      psum += __shfl_xor(psum, 4, 64);
+      l_run = a * l_run + psum;
+      m_run = m_new;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      *(bf16x4*)(&sm.p[hs * kPPitch + tq]) = bf16x4{pe[0], pe[1], pe[2], pe[3]};
+      if ((lane & 7) == 0) sm.alpha[hs] = a;
+      lds_barrier();
+      alpha = sm.alpha[l32];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) pb[s2] = *(const bf16x8*)(&sm.p[l32 * kPPitch + 16 * s2 + 8 * kg]);
+    } else {
+      if (valid < kTT) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + 4 * kg + (i & 3) >= valid) acc[i] = -INFINITY;
+      }
+      float mx = acc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      alpha = exp2f(m_run - m_new);
+      float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int h = 8 * (i >> 2) + 4 * kg + (i & 3);
-        sm.s[w][h * kSPitch + 32 * nb + lh] = acc[nb][i];
-        if (NB == 4) sm.s[4 + w][h * kSPitch + 32 * nb + lh] = accr[nb][i];
+        const bf16 e = (bf16)exp2f(acc[i] - m_new);
+        pb[i >> 3][i & 7] = e;
+        psum += (float)e;
       }
-    __syncthreads();
-
-    // ---- online softmax; lane (head lh, half kg) holds tokens 16*s4 + 8*kg + i
-    float v[4][8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int tt = 16 * s4 + 8 * kg;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        f32x4 x;
-        if (NB == 1) {
-          x = *(const f32x4*)(&sm.s[0][lh * kSPitch + tt + 4 * q]);
-#pragma unroll
-          for (int sl = 1; sl < 4; ++sl) x += *(const f32x4*)(&sm.s[sl][lh * kSPitch + tt + 4 * q]);
-        } else {
-          x = *(const f32x4*)(&sm.s[w][lh * kSPitch + tt + 4 * q]);
-#pragma unroll
-          for (int sl = 4; sl < 8; ++sl) x += *(const f32x4*)(&sm.s[sl][lh * kSPitch + tt + 4 * q]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float val = (t0 + tt + 4 * q + e < t_end) ? x[e] : -INFINITY;
-          v[s4][4 * q + e] = val;
-          mx = fmaxf(mx, val);
-        }
-      }
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = alpha * l_run + psum;
+      m_run = m_new;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid token
-    const float alpha = exp2f(m_run - m_new);
-    bf16x8 pb[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16 e = (bf16)exp2f(v[s4][i] - m_new);
-        pb[s4][i] = e;
-        psum += (float)e;  // normalise with the same rounded weights the MFMA uses
-      }
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = alpha * l_run + psum;
-    m_run = m_new;
 
     // ---- O^T[d][h] += V^T P^T over this wave's 128 latent columns
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) O[mb] *= alpha;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const bf16* vb = sm.k + (16 * s4 + tr_row) * kKPitch + tr_col;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16* vb = lat + (16 * s2 + v_row) * kLatPitch + v_col;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 va = tr_pair(vb + 32 * mb);
-        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s4], O[mb], 0, 0, 0);
-      }
+      for (int mb = 0; mb < 4; ++mb)
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_pair(vb + 32 * mb, v_delta), pb[s2], O[mb], 0, 0, 0);
     }
   }
 
-  // ---- partial outputs.  O[mb] item i: column d = 128w + 32mb + 8*(i/4) + 4*kg + i%4, head lh
-  float* po = part_o + (((size_t)b * S + s) * H + h0 + lh) * kDC + 128 * w + 4 * kg;
+  // ---- partial outputs.  O[mb] item i: column d = 128w + 32mb + 8*(i/4) + 4*kg + i%4, head l32
+  float* po = part_o + (((size_t)b * S + s) * H + h0 + l32) * kDC + 128 * w + 4 * kg;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *(f32x4*)(po + 32 * mb + 8 * q) =
           f32x4{O[mb][4 * q], O[mb][4 * q + 1], O[mb][4 * q + 2], O[mb][4 * q + 3]};
-  const int br = NB == 1 ? 0 : w;
-  if (kg == 0 && (NB == 4 || w == 0)) {
-    ml[((size_t)br * H + h0 + lh) * 2 + 0] = m_run;
-    ml[((size_t)br * H + h0 + lh) * 2 + 1] = l_run;
+  if (NB == 1) {
+    if ((lane & 7) == 0) {
+      const int hs = h0 + 8 * w + (lane >> 3);
+      ml[(size_t)hs * 2 + 0] = m_run;
+      ml[(size_t)hs * 2 + 1] = l_run;
+    }
+  } else if (kg == 0) {
+    ml[((size_t)w * H + h0 + l32) * 2 + 0] = m_run;
+    ml[((size_t)w * H + h0 + l32) * 2 + 1] = l_run;
   }
 }
 

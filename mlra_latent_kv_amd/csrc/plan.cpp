@@ -85,6 +85,7 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
   const int chunk_tiles = (int)ceil_div(q.n_tiles, splits);
   q.chunk = chunk_tiles * kPage;
   q.splits = (int)ceil_div(q.n_tiles, chunk_tiles);
+  if (q.splits > kMaxSplits) return MLA_ERR_SHAPE;
   // grid sizes and 32-bit work-item indices must fit
   if (wg_per_split * q.splits + 8LL * std::max(q.n_hg, 1) > INT32_MAX) return MLA_ERR_SHAPE;
 
@@ -97,7 +98,7 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
   q.off_part_ml = off;
   off = align_up(off + (size_t)q.B * q.splits * q.NB * q.H * 2 * sizeof(float));
   q.off_olat = off;
-  off = align_up(off + (size_t)q.B * q.H * q.dc * sizeof(float));
+  off = align_up(off + (size_t)q.B * q.H * q.dc * (q.dtype == MLA_BF16 ? 2 : 4));
   q.bytes = off;
   *plan = q;
   return MLA_OK;
@@ -121,6 +122,9 @@ mla_status check_call(const mla_params* p, const Plan& plan, int want_branches,
     return MLA_ERR_ALIGN;
   const size_t cache_align = plan.dtype == MLA_BF16 ? 16 : 4;
   if (!aligned(latent, cache_align) || !aligned(rope, cache_align)) return MLA_ERR_ALIGN;
+  // the bf16 kernels read the query and both weights with 16-byte vector loads
+  if (plan.dtype == MLA_BF16 && (!aligned(q_nope, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16)))
+    return MLA_ERR_ALIGN;
   (void)p;
   return MLA_OK;
 }

@@ -14,6 +14,7 @@ constexpr int kPage = MLA_PAGE_SIZE;   // tokens per page == tokens per main-loo
 constexpr int kHeadGroup = 32;         // heads per workgroup of the bf16 main kernel
 constexpr int kTargetWorkgroups = 256; // one per CU of an MI355X; the split heuristic aims here
 constexpr size_t kWsAlign = 256;
+constexpr int kMaxSplits = 512;        // bound on sequence splits (combine keeps weights in LDS)
 
 enum class Path { kBf16Mfma, kF32Simt };
 

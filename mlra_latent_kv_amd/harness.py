@@ -43,12 +43,13 @@ class DeviceCase:
     def rope_ptr(self) -> int:
         return self.cache.data_ptr() + self.params.d_latent * self.params.num_branches * self.cache.element_size()
 
-    def run(self, stream=None, params: Optional[B.MlaParams] = None, out=None, workspace=None):
+    def run(self, stream=None, params: Optional[B.MlaParams] = None, out=None, workspace=None,
+            events=None):
         p = self.params if params is None else params
         fn = B.mlra_decode if self.branches == 4 else B.mla_decode
         fn(p, self.q_nope, self.q_rope, self.latent_ptr, self.rope_ptr, self.seqlens,
            self.block_table, self.w_uk, self.w_uv, self.out if out is None else out,
-           self.workspace if workspace is None else workspace, stream=stream)
+           self.workspace if workspace is None else workspace, stream=stream, events=events)
         return self.out if out is None else out
 
 

@@ -25,7 +25,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     declared = B.header_functions()
     assert set(declared) == {"mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
-                             "mla_rope_rotate", "mla_status_str"}
+                             "mla_decode_timed", "mlra_decode_timed", "mla_rope_rotate",
+                             "mla_status_str"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -108,6 +109,7 @@ def test_workspace_and_alignment(lib):
     assert call(lib, p, ws_bytes=need - 1) == 4
     assert call(lib, p, latent=FAKE + 8) == 6
     assert call(lib, p, workspace=FAKE + 64) == 6
+    assert call(lib, p, w_uk=FAKE + 2) == 6     # bf16 weights need 16-byte alignment
 
 
 def test_rope_rotate_validation(lib):
@@ -140,7 +142,7 @@ def test_workspace_layout(lib, wname):
     al = lambda x: (x + 255) // 256 * 256
     Bn, H, dc = 3, w.heads, w.d_c
     exp = al(Bn * H * w.row * w.elem_bytes) + al(Bn * S * H * dc * 4) + \
-        al(Bn * S * w.branches * H * 2 * 4) + al(Bn * H * dc * 4)
+        al(Bn * S * w.branches * H * 2 * 4) + al(Bn * H * dc * w.elem_bytes)
     assert B.workspace_size(p) == exp
 
 
