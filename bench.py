@@ -9,6 +9,12 @@ would instead leave the MALL dirty and charge the step for the write-backs.  The
 time is taken with HIP events that the library records on its own stream around its
 kernels (``mla_decode_timed``), so the flush is outside the measured interval.
 
+Step time: a HIP event pair around [flush, decode] minus one around [flush] alone, both
+averaged over the K timed steps.  The event overheads cancel and the decode's kernels run
+back to back, as they would in a model.  A separate pass with ``mla_decode_timed``
+gives per-stage times and the main-loop kernel time for the roofline; its interior events
+add a few microseconds of idle gap per stage, which that pass does not report as step time.
+
 Prints ONE JSON line on stdout.  ``value`` is the latent-cache read rate in TB/s:
   sum_b L_b * (d_c + d_rope) * bytes_per_element / t_step.
 """
@@ -46,6 +52,11 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def create(self, n):
         arr = (ctypes.c_void_p * n)()
@@ -170,30 +181,51 @@ def main():
 
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")  # 512 MiB
     ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
     K, W = args.steps, args.warmup
-    events = [ev.create(5) for _ in range(K)]
 
-    def step(i, e=None):
+    def do_flush(i):
         if args.flush == "read":
             flush.sum()
         elif args.flush == "write":
             flush.fill_(float(i))
-        case.run(events=e)
 
     for i in range(W):
-        step(i)
+        do_flush(i)
+        case.run()
     torch.cuda.synchronize()
     log(f"[bench] warm-up done ({W} steps); timing {K} steps")
+
+    # pass 1: the timed region -- K x [event, flush, decode, event], then K x [event, flush, event]
+    pairs_fd = [ev.create(2) for _ in range(K)]
+    pairs_f = [ev.create(2) for _ in range(K)]
+    torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for i in range(K):
-        step(i, events[i])
+        ev.record(pairs_fd[i][0], stream)
+        do_flush(i)
+        case.run()
+        ev.record(pairs_fd[i][1], stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    for i in range(K):
+        ev.record(pairs_f[i][0], stream)
+        do_flush(i)
+        ev.record(pairs_f[i][1], stream)
+    torch.cuda.synchronize()
+    t_fd = [ev.ms(e[0], e[1]) for e in pairs_fd]
+    t_f = [ev.ms(e[0], e[1]) for e in pairs_f]
+    total = [a - statistics.mean(t_f) for a in t_fd]
 
-    total = [ev.ms(e[0], e[4]) for e in events]
-    stage = {name: [ev.ms(e[j], e[j + 1]) for e in events]
+    # pass 2: per-stage times from the library's own stage events (diagnostic, main-loop time)
+    staged = [ev.create(5) for _ in range(K)]
+    for i in range(K):
+        do_flush(i)
+        case.run(events=staged[i])
+    torch.cuda.synchronize()
+    stage = {name: [ev.ms(e[j], e[j + 1]) for e in staged]
              for j, name in enumerate(["prologue", "main", "combine", "epilogue"])}
-    for e in events:
+    for e in pairs_fd + pairs_f + staged:
         ev.destroy(e)
     ms = statistics.mean(total)
     main_ms = statistics.mean(stage["main"])
@@ -232,6 +264,7 @@ def main():
         "ms_p10_p50_p90": [round(float(np.percentile(total, q)), 5) for q in (10, 50, 90)],
         "stage_us": {k: round(1e3 * statistics.mean(v), 2) for k, v in stage.items()},
         "wall_s_timed_region": round(t_wall, 4),
+        "flush_us": round(1e3 * statistics.mean(t_f), 2),
         "roofline": {
             "kernel": "k_main_bf16" if w.dtype == "bf16" else "k_main_f32",
             "bound": "hbm",

@@ -173,7 +173,8 @@ mla_status mlra_decode_timed(const mla_params* p, const void* q_nope, const void
  * Rotate rows of a rotary-key cache in place (the write-side step that gives the decoupled
  * key its position; RoFormer rotation, cited by the interview Q&A).  Row i starts at
  * x + i*row_stride (elements, dtype) and has d_rope elements; pairs (x_{2k}, x_{2k+1})
- * are rotated by angle pos[i] * theta^(-2k/d_rope), angles computed in fp64.  Rows with
+ * are rotated by angle pos[i] * theta^(-2k/d_rope) (product and reduction mod 2*pi in fp64,
+ * sine/cosine of the reduced angle in fp32).  Rows with
  * pos[i] < 0 are left unchanged.  x: device, [n_rows] rows; pos: device int32 [n_rows].
  * d_rope even, 2..256; n_rows >= 0 (0 launches nothing).
  */

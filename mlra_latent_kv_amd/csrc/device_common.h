@@ -36,4 +36,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// RoPE frequencies theta^(-2k/d_rope) for k < d_rope/2, computed on the host in fp64 and
+// passed by value as a kernel argument (d_rope <= 256).
+struct RopeFreq {
+  double f[128];
+};
+
+// cos/sin of the rotation angle pos * f: the product and its reduction to [-pi, pi] are done
+// in fp64 (positions reach 2^26), the trigonometric functions in fp32 on the reduced angle.
+__device__ __forceinline__ void rope_cos_sin(int pos, double f, float* c, float* s) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  double a = (double)pos * f;
+  a -= kTwoPi * rint(a * (1.0 / kTwoPi));
+  sincosf((float)a, s, c);
+}
+
 }  // namespace mla

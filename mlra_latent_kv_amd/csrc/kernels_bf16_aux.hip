@@ -41,7 +41,7 @@ constexpr int kPPitch = kPCols + 8;  // LDS pitch of the W_UK block (bf16)
 __global__ __launch_bounds__(256) void k_prologue_bf16(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
     const int32_t* __restrict__ seqlens, const bf16* __restrict__ w_uk, bf16* __restrict__ qcat,
-    int B, int H, int NB, int dcb, float qscale, double theta) {
+    int B, int H, int NB, int dcb, float qscale, RopeFreq rf) {
   constexpr int dn = 128, dr = 64;
   __shared__ __align__(16) bf16 sW[dn * kPPitch];
   const int h = blockIdx.x, b0 = blockIdx.y * kRows, cb = blockIdx.z;
@@ -57,13 +57,13 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
     *(u32x4*)(sW + r * kPPitch + col) = *(const u32x4*)(wsrc + (size_t)r * dcb + col);
   }
   // A operand: q_nope rows b0 + lane%32, K-step s covers n = 16s + 8*(lane/32) .. +8
+  // rows past B are clamped to B-1: their products are computed but never stored
   const int bl = lane & 31, kg = lane >> 5;
-  const int b = b0 + bl;
+  const int b = min(b0 + bl, B - 1);
   bf16x8 qa[dn / 16];
+  const bf16* qsrc = q_nope + (((size_t)b * H + h) * NB + br) * dn + 8 * kg;
 #pragma unroll
-  for (int s = 0; s < dn / 16; ++s)
-    qa[s] = b < B ? *(const bf16x8*)(q_nope + (((size_t)b * H + h) * NB + br) * dn + 16 * s + 8 * kg)
-                  : bf16x8{};
+  for (int s = 0; s < dn / 16; ++s) qa[s] = *(const bf16x8*)(qsrc + 16 * s);
   __syncthreads();
   f32x16 acc = {};
   const bf16* tsrc = sW + tr_src_row(lane) * kPPitch + 32 * w + tr_src_col(lane);
@@ -83,14 +83,13 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
       const int bb = b0 + t / (dr / 2), k = t % (dr / 2);
       if (bb >= B) continue;
       const int L = seqlens[bb];
-      const double ang = (double)(L > 0 ? L - 1 : 0) * pow(theta, -2.0 * k / dr);
-      double sn, cs;
-      sincos(ang, &sn, &cs);
+      float cs, sn;
+      rope_cos_sin(L > 0 ? L - 1 : 0, rf.f[k], &cs, &sn);
       const bf16* x = q_rope + ((size_t)bb * H + h) * dr + 2 * k;
-      const double x0 = (float)x[0], x1 = (float)x[1];
+      const float x0 = (float)x[0], x1 = (float)x[1];
       bf16* o = qcat + ((size_t)bb * H + h) * row + dc + 2 * k;
-      o[0] = (bf16)((float)(x0 * cs - x1 * sn) * qscale);
-      o[1] = (bf16)((float)(x0 * sn + x1 * cs) * qscale);
+      o[0] = (bf16)((x0 * cs - x1 * sn) * qscale);
+      o[1] = (bf16)((x0 * sn + x1 * cs) * qscale);
     }
   }
 }
@@ -98,39 +97,43 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
 // ----------------------------------------------------------------------------- epilogue
 constexpr int kECols = 32;           // output columns per workgroup (one wave)
 constexpr int kEPitch = kECols + 8;  // LDS pitch of the W_UV block (bf16)
-constexpr int kEMaxDc = 512;
+constexpr int kDc = 512;             // total latent width on the bf16 path (MLA 512, MLRA 4x128)
 
 __global__ __launch_bounds__(64) void k_epilogue_bf16(const bf16* __restrict__ olat,
                                                       const bf16* __restrict__ w_uv,
                                                       bf16* __restrict__ out, int B, int H, int NB,
                                                       int dcb, float out_scale) {
   constexpr int dv = 128;
-  __shared__ __align__(16) bf16 sW[kEMaxDc * kEPitch];
+  __shared__ __align__(16) bf16 sW[kDc * kEPitch];
   const int h = blockIdx.x, b0 = blockIdx.y * kRows, v0 = blockIdx.z * kECols;
-  const int dc = NB * dcb;
   const int lane = threadIdx.x;
-  // W_UV rows d (branch d/dcb), columns v0..v0+31: 4 chunks of 16 B per row
-  for (int c = lane; c < dc * 4; c += 64) {
-    const int d = c >> 2, q = c & 3;
-    const int br = d / dcb, dd = d % dcb;
-    *(u32x4*)(sW + d * kEPitch + 8 * q) =
-        *(const u32x4*)(w_uv + (((size_t)br * H + h) * dcb + dd) * dv + v0 + 8 * q);
-  }
   const int bl = lane & 31, kg = lane >> 5;
-  const int b = b0 + bl;
-  const bf16* arow = olat + ((size_t)(b < B ? b : 0) * H + h) * dc + 8 * kg;
+  // rows past B are clamped to B-1: their products are computed but never stored
+  const int b = min(b0 + bl, B - 1);
+  // batch-row operand for the whole contraction first, so its latency overlaps the weights
+  bf16x8 a[kDc / 16];
+  const bf16* arow = olat + ((size_t)b * H + h) * kDc + 8 * kg;
+#pragma unroll
+  for (int s = 0; s < kDc / 16; ++s) a[s] = *(const bf16x8*)(arow + 16 * s);
+  // W_UV rows d (branch d/dcb), columns v0..v0+31: row d = 16*i + lane/4, chunk lane%4
+  const int q = lane & 3;
+#pragma unroll
+  for (int i0 = 0; i0 < kDc / 16; i0 += 8) {
+    u32x4 t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int d = 16 * (i0 + i) + (lane >> 2);
+      t[i] = *(const u32x4*)(w_uv + (((size_t)(d / dcb) * H + h) * dcb + d % dcb) * dv + v0 + 8 * q);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(u32x4*)(sW + (16 * (i0 + i) + (lane >> 2)) * kEPitch + 8 * q) = t[i];
+  }
   __syncthreads();
   f32x16 acc = {};
   const bf16* tsrc = sW + tr_src_row(lane) * kEPitch + tr_src_col(lane);
-  for (int s = 0; s < dc / 16; s += 4) {
-    bf16x8 a[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] = b < B ? *(const bf16x8*)(arow + 16 * (s + u)) : bf16x8{};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], tr8(tsrc + 16 * (s + u) * kEPitch, kEPitch),
-                                                    acc, 0, 0, 0);
-  }
+  for (int s = 0; s < kDc / 16; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], tr8(tsrc + 16 * s * kEPitch, kEPitch), acc, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int bb = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
@@ -142,9 +145,11 @@ __global__ __launch_bounds__(64) void k_epilogue_bf16(const bf16* __restrict__ o
 
 hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(p.H, (p.B + kRows - 1) / kRows, p.dc / kPCols);
+  RopeFreq rf;
+  make_rope_freq(p.dr, a.rope_theta, &rf);
   hipLaunchKernelGGL(k_prologue_bf16, grid, dim3(256), 0, s, (const bf16*)a.q_nope,
                      (const bf16*)a.q_rope, a.seqlens, (const bf16*)a.w_uk, (bf16*)a.qcat, p.B,
-                     p.H, p.NB, p.dcb, a.softmax_scale * kLog2e, (double)a.rope_theta);
+                     p.H, p.NB, p.dcb, a.softmax_scale * kLog2e, rf);
   return hipGetLastError();
 }
 

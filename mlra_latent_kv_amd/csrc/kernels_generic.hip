@@ -14,6 +14,11 @@ namespace mla {
 
 constexpr int kBatchBlock = 8;  // sequences per prologue / epilogue workgroup (weight reuse)
 
+void make_rope_freq(int d_rope, float theta, RopeFreq* out) {
+  for (int k = 0; k < 128; ++k)
+    out->f[k] = k < d_rope / 2 ? std::pow((double)theta, -2.0 * k / d_rope) : 0.0;
+}
+
 // ----------------------------------------------------------------------------- prologue
 // qcat[b,h] = [ (W_UK[br,h]^T q_nope[b,h,br])_{br} | RoPE(q_rope[b,h], L_b - 1) ] * qscale
 // qscale = softmax_scale * log2(e) so the main loop can use exp2.
@@ -23,7 +28,7 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
                                                   const int32_t* __restrict__ seqlens,
                                                   const T* __restrict__ w_uk, T* __restrict__ qcat,
                                                   int B, int H, int NB, int dn, int dcb, int dr,
-                                                  float qscale, double theta) {
+                                                  float qscale, RopeFreq rf) {
   extern __shared__ float sq[];  // [kBatchBlock][NB][dn]
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kBatchBlock;
@@ -55,14 +60,13 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
     const int j = i / half, k = i % half;
     const int b = b0 + j;
     const int L = seqlens[b];
-    const double ang = (double)(L > 0 ? L - 1 : 0) * pow(theta, -2.0 * k / dr);
-    double sn, cs;
-    sincos(ang, &sn, &cs);
+    float cs, sn;
+    rope_cos_sin(L > 0 ? L - 1 : 0, rf.f[k], &cs, &sn);
     const T* x = q_rope + ((size_t)b * H + h) * dr + 2 * k;
-    const double x0 = to_f32(x[0]), x1 = to_f32(x[1]);
+    const float x0 = to_f32(x[0]), x1 = to_f32(x[1]);
     T* o = qcat + ((size_t)b * H + h) * row + dc + 2 * k;
-    o[0] = from_f32<T>((float)(x0 * cs - x1 * sn) * qscale);
-    o[1] = from_f32<T>((float)(x0 * sn + x1 * cs) * qscale);
+    o[0] = from_f32<T>((x0 * cs - x1 * sn) * qscale);
+    o[1] = from_f32<T>((x0 * sn + x1 * cs) * qscale);
   }
 }
 
@@ -70,9 +74,11 @@ hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(p.H, (p.B + kBatchBlock - 1) / kBatchBlock);
   const size_t lds = (size_t)kBatchBlock * p.NB * p.dn * sizeof(float);
   const float qscale = a.softmax_scale * kLog2e;
+  RopeFreq rf;
+  make_rope_freq(p.dr, a.rope_theta, &rf);
   hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, s, (const float*)a.q_nope,
                        (const float*)a.q_rope, a.seqlens, (const float*)a.w_uk, (float*)a.qcat,
-                       p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, (double)a.rope_theta);
+                       p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, rf);
   return hipGetLastError();
 }
 
@@ -94,35 +100,47 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
   const int h0 = hb * kCombHeads;
   const int nh = min(kCombHeads, H - h0);
   const int dc = NB * dcb;
-  for (int t = threadIdx.x; t < nh * NB; t += blockDim.x) {
-    const int hl = t / NB, br = t % NB;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const size_t sstride = (size_t)NB * H * 2;
+  // split weights: one wave per (head, branch), lanes stride over the splits
+  for (int pr = wv; pr < nh * NB; pr += blockDim.x / 64) {
+    const int hl = pr / NB, br = pr % NB;
     const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + (h0 + hl) * 2;
-    const size_t sstride = (size_t)NB * H * 2;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s * sstride]);
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[s * sstride]);
+    M = wave_max(M);
     float den = 0.0f;
     if (M != -INFINITY)
-      for (int s = 0; s < S; ++s) {
+      for (int s = lane; s < S; s += 64) {
         const float m = ml[s * sstride];
         if (m != -INFINITY) den = fmaf(exp2f(m - M), ml[s * sstride + 1], den);
       }
+    den = wave_sum(den);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    float* wrow = sw + (hl * NB + br) * S;
-    for (int s = 0; s < S; ++s) {
+    for (int s = lane; s < S; s += 64) {
       const float m = ml[s * sstride];
-      wrow[s] = (m == -INFINITY) ? 0.0f : exp2f(m - M) * inv;
+      sw[(hl * NB + br) * S + s] = (m == -INFINITY) ? 0.0f : exp2f(m - M) * inv;
     }
   }
   __syncthreads();
   const int q4 = dc / 4;
+  const size_t pstride = (size_t)H * dc;
   for (int it = threadIdx.x; it < nh * q4; it += blockDim.x) {
     const int hl = it / q4, d = 4 * (it % q4);
     const float* wrow = sw + (hl * NB + d / dcb) * S;
     const float* src = part_o + (((size_t)b * S) * H + h0 + hl) * dc + d;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < S; ++s) {
-      const float wt = wrow[s];
-      if (wt != 0.0f) acc += wt * *(const f32x4*)(src + (size_t)s * H * dc);
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      f32x4 v[4];
+      float wt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wt[u] = s0 + u < S ? wrow[s0 + u] : 0.0f;
+        // splits with no tokens have weight 0 and never-written partials: skip the load
+        v[u] = wt[u] != 0.0f ? *(const f32x4*)(src + (size_t)(s0 + u) * pstride) : f32x4{};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += wt[u] * v[u];
     }
     TO* dst = olat + ((size_t)b * H + h0 + hl) * dc + d;
 #pragma unroll
@@ -186,11 +204,11 @@ hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------- rope rotate
-// RoFormer rotation of consecutive pairs by pos * theta^(-2k/d_rope), angles in fp64.
+// RoFormer rotation of consecutive pairs by pos * theta^(-2k/d_rope) (angle reduced in fp64).
 template <typename T>
 __global__ __launch_bounds__(256) void k_rope_rotate(T* __restrict__ x, int64_t row_stride,
                                                      const int32_t* __restrict__ pos, int64_t n,
-                                                     int dr, double theta) {
+                                                     int dr, RopeFreq rf) {
   const int half = dr / 2;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n * half) return;
@@ -198,25 +216,26 @@ __global__ __launch_bounds__(256) void k_rope_rotate(T* __restrict__ x, int64_t 
   const int k = (int)(i % half);
   const int p = pos[r];
   if (p < 0) return;
-  const double ang = (double)p * pow(theta, -2.0 * k / dr);
-  double sn, cs;
-  sincos(ang, &sn, &cs);
+  float cs, sn;
+  rope_cos_sin(p, rf.f[k], &cs, &sn);
   T* px = x + r * row_stride + 2 * k;
-  const double x0 = to_f32(px[0]), x1 = to_f32(px[1]);
-  px[0] = from_f32<T>((float)(x0 * cs - x1 * sn));
-  px[1] = from_f32<T>((float)(x0 * sn + x1 * cs));
+  const float x0 = to_f32(px[0]), x1 = to_f32(px[1]);
+  px[0] = from_f32<T>(x0 * cs - x1 * sn);
+  px[1] = from_f32<T>(x0 * sn + x1 * cs);
 }
 
 hipError_t launch_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
                               int d_rope, float theta, int dtype, hipStream_t s) {
   const int64_t work = n_rows * (d_rope / 2);
   const dim3 grid((unsigned)((work + 255) / 256));
+  RopeFreq rf;
+  make_rope_freq(d_rope, theta, &rf);
   if (dtype == MLA_BF16)
     hipLaunchKernelGGL(k_rope_rotate<bf16>, grid, dim3(256), 0, s, (bf16*)x, row_stride, pos,
-                       n_rows, d_rope, (double)theta);
+                       n_rows, d_rope, rf);
   else
     hipLaunchKernelGGL(k_rope_rotate<float>, grid, dim3(256), 0, s, (float*)x, row_stride, pos,
-                       n_rows, d_rope, (double)theta);
+                       n_rows, d_rope, rf);
   return hipGetLastError();
 }
 

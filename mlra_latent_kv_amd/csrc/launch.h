@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "plan.h"
 
 namespace mla {
@@ -25,6 +26,10 @@ struct DecodeArgs {
   float* part_ml;   // [B][S][NB][H][2]  (running max in log2 units, running sum)
   void* olat;       // [B][H][d_c], bf16 on the bf16 path (MFMA operand), fp32 otherwise
 };
+
+struct RopeFreq;
+// theta^(-2k/d_rope), k < d_rope/2, in fp64 (RoFormer frequencies)
+void make_rope_freq(int d_rope, float theta, RopeFreq* out);
 
 hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s);       // fp32 path
 hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
