@@ -14,13 +14,18 @@
 // the value.  For MLRA-4 ("[ICLR 2025] MLRA…", section 2.1) the latent holds four
 // 128-wide branches with independent softmaxes that share the rotary score.
 //
-// Wave w (of 4) owns latent columns [128w, 128w+128): it computes their score contribution
-// and accumulates O^T for those columns.
-//  * MLA (one branch): the waves' partial scores (plus a quarter of the rotary columns each)
-//    meet in LDS; wave w sums them for heads 8w..8w+7, runs the softmax for those heads, and
-//    publishes bf16 probabilities and rescale factors for everyone's PV step.
-//  * MLRA-4: wave w's columns are exactly branch w; it also computes the full rotary score
-//    itself, so its branch's scores, softmax and probabilities never leave its registers.
+// Two workgroups share a CU (LDS <= 80 KB each, <= 256 VGPRs per wave), so every SIMD has a
+// second wave to run while one waits on LDS, MFMA results or a barrier.  Each workgroup
+// double-buffers its tiles: one lands while the other is consumed.
+//
+// Wave w (of 4) accumulates O^T for latent columns [128w, 128w+128).
+//  * MLA (one branch): for the scores, wave w takes tokens 16*(w&1).. and heads 16*(w>>1)..
+//    of the tile over the full 576 columns (MFMA 16x16x32, query in registers).  Partner
+//    waves (same heads, other 16 tokens) swap per-head maxima and sums through LDS, and
+//    every wave publishes its bf16 probabilities for everyone's PV step.
+//  * MLRA-4: wave w's latent columns are exactly branch w; it computes its branch's scores
+//    plus the full rotary score itself, so the branch's softmax and probabilities never
+//    leave its registers.
 #include "device_common.h"
 #include "launch.h"
 
@@ -35,21 +40,17 @@ constexpr int kLatPitchB = kDC * 2 + 16;             // LDS bytes per latent row
 constexpr int kLatPitch = kLatPitchB / 2;            // ... in bf16 elements
 constexpr int kRopeOff = kTT * kLatPitchB;           // rotary region of a buffer
 constexpr int kBufBytes = kRopeOff + kTT * kDR * 2;  // one tile
-constexpr int kSPitch = kTT + 4;                     // fp32 partial-score row pitch
 constexpr int kPPitch = kTT + 8;                     // bf16 probability row pitch
-constexpr int kLoadsPerTile = 9;                     // buffer loads per wave per tile
 
-template <int NB>
-struct Ring {
-  static constexpr int kBufs = NB == 1 ? 3 : 4;
-};
+constexpr int kBufs = 2;                             // tile ring depth per workgroup
 
 template <int NB>
 struct Smem {
-  char ring[Ring<NB>::kBufs][kBufBytes];
-  float s[NB == 1 ? 4 * kHG * kSPitch : 4];   // MLA: per-wave partial scores [w][h][t]
+  char ring[kBufs][kBufBytes];
   bf16 p[NB == 1 ? kHG * kPPitch : 8];        // MLA: probabilities [h][t]
-  float alpha[kHG];                           // MLA: per-head rescale of this tile
+  float mx[NB == 1 ? 2 * kHG : 1];            // MLA: per-head max of each 16-token half
+  float sum[NB == 1 ? 2 * kHG : 1];           // MLA: per-head probability sum of each half
+  float alpha[NB == 1 ? kHG : 1];             // MLA: per-head rescale of this tile
 };
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -65,16 +66,10 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
-// Wait until at most n tiles' worth of this wave's buffer loads are still in flight.
-__device__ __forceinline__ void wait_tiles(int n) {
-  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-  if (n <= 0)
-    __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
-  else if (n == 1)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerTile);      // vmcnt(9)
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * kLoadsPerTile) & 15) | (((2 * kLoadsPerTile) >> 4) << 14));
-}
+// Wait for all of this wave's tile loads (with a ring of two, the next tile is issued only
+// after the current one has landed).  s_waitcnt encoding (gfx9): vmcnt(0), other counters
+// left alone.
+__device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() also fences global
 // memory, which here would wait for every in-flight tile load (they write LDS
@@ -93,13 +88,12 @@ __device__ __forceinline__ bf16x8 tr_pair(const bf16* p, int delta_rows) {
 }
 
 template <int NB>
-__global__ __launch_bounds__(kThreads, 1) void k_main_bf16(
+__global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
     int S, int chunk, int n_hg, int units) {
-  constexpr int kBufs = Ring<NB>::kBufs;
   __shared__ __align__(16) Smem<NB> sm;
 
   // XCD-aware mapping: consecutive blocks go to different XCDs, so the head groups of one
@@ -160,22 +154,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16(
     dma16(rr, buf + kRopeOff + w * 1024, voff_rope);
   };
 
-  // absorbed query: MFMA B operand, lane (head l32, k-half kg)
-  constexpr int kQSteps = NB == 1 ? 9 : 12;
+  // absorbed query as the MFMA B operand (N = heads).
+  //  MLA, 16x16x32: lane (head 16*(w>>1) + lane%16, k-group lane/16), K-step j = 32 columns.
+  //  MLRA, 32x32x16: lane (head l32, k-half kg), K-step j = 16 columns of branch w / rope.
+  constexpr int kQSteps = NB == 1 ? 18 : 12;
+  const int tb = w & 1, hb = w >> 1;          // MLA score block: token half, head half
+  const int l16 = lane & 15, g16 = lane >> 4;
   bf16x8 qb[kQSteps];
-  {
+  if (NB == 1) {
+    const bf16* qrow = qcat + ((size_t)b * H + h0 + 16 * hb + l16) * kRow + 8 * g16;
+#pragma unroll
+    for (int j = 0; j < 18; ++j) qb[j] = *(const bf16x8*)(qrow + 32 * j);
+  } else {
     const bf16* qrow = qcat + ((size_t)b * H + h0 + l32) * kRow + 8 * kg;
 #pragma unroll
     for (int j = 0; j < 8; ++j) qb[j] = *(const bf16x8*)(qrow + 128 * w + 16 * j);
-    if (NB == 1) {
-      qb[8] = *(const bf16x8*)(qrow + kDC + 16 * w);
-    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qb[8 + j] = *(const bf16x8*)(qrow + kDC + 16 * j);
-    }
+    for (int j = 0; j < 4; ++j) qb[8 + j] = *(const bf16x8*)(qrow + kDC + 16 * j);
   }
 
-  for (int k = 0; k < min(kBufs - 1, n_tiles); ++k) issue(k);
+  issue(0);
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 O[4];
@@ -189,28 +187,80 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16(
   constexpr int v_delta = NB == 1 ? 4 : 8;
 
   for (int k = 0; k < n_tiles; ++k) {
-    wait_tiles(min(kBufs - 2, n_tiles - 1 - k));
+    wait_tile();
     lds_barrier();  // tile k landed for every wave; buffer of tile k-1 is free
-    if (k + kBufs - 1 < n_tiles) issue(k + kBufs - 1);
+    if (k + 1 < n_tiles) issue(k + 1);
 
     const int t0 = t_begin + kTT * k;
     const int valid = min(kTT, t_end - t0);
     const char* buf = sm.ring[k % kBufs];
     const bf16* lat = (const bf16*)buf;
-    const char* rp = buf + kRopeOff + l32 * 128;
 
-    // ---- scores S^T[t][h] (M = tokens, N = heads) over this wave's columns
-    f32x16 acc = {};
-    {
-      const bf16* arow = lat + l32 * kLatPitch + 128 * w + 8 * kg;
+    bf16x8 pb[2];
+    float alpha;
+    if (NB == 1) {
+      // ---- scores of 16 tokens x 16 heads over all 576 columns (M = tokens, N = heads)
+      f32x4 acc = {};
+      {
+        const int t = 16 * tb + l16;
+        const bf16* arow = lat + t * kLatPitch + 8 * g16;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(arow + 16 * j), qb[j], acc, 0, 0, 0);
-      if (NB == 1) {
-        const int c = 2 * w + kg;
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8*)(rp + 16 * (c ^ (l32 & 7))), qb[8], acc, 0, 0, 0);
-      } else {
+        for (int j = 0; j < 16; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(arow + 32 * j), qb[j], acc, 0, 0, 0);
+        const char* rrow = buf + kRopeOff + t * 128;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int c = 4 * j + g16;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *(const bf16x8*)(rrow + 16 * (c ^ (t & 7))), qb[16 + j], acc, 0, 0, 0);
+        }
+      }
+      // D layout: lane (head 16*hb + l16, group g16), item e -> token 16*tb + 4*g16 + e
+      const int h = 16 * hb + l16;
+      const int tq = 16 * tb + 4 * g16;
+      if (valid < kTT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (tq + e >= valid) acc[e] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (g16 == 0) sm.mx[tb * kHG + h] = mx;
+      lds_barrier();
+      mx = fmaxf(mx, sm.mx[(tb ^ 1) * kHG + h]);  // max over the tile's 32 tokens
+      const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid token
+      const float a = exp2f(m_run - m_new);
+      bf16 pe[4];
+      float psum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pe[e] = (bf16)exp2f(acc[e] - m_new);
+        psum += (float)pe[e];  // normalise with the rounded weights the MFMA uses
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      *(bf16x4*)(&sm.p[h * kPPitch + tq]) = bf16x4{pe[0], pe[1], pe[2], pe[3]};
+      if (g16 == 0) {
+        sm.sum[tb * kHG + h] = psum;
+        if (tb == 0) sm.alpha[h] = a;
+      }
+      lds_barrier();
+      l_run = a * l_run + psum + sm.sum[(tb ^ 1) * kHG + h];
+      m_run = m_new;
+      alpha = sm.alpha[l32];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) pb[s2] = *(const bf16x8*)(&sm.p[l32 * kPPitch + 16 * s2 + 8 * kg]);
+    } else {
+      // ---- branch-w scores S^T[t][h] (M = tokens, N = heads): 128 latent + 64 rotary columns
+      f32x16 acc = {};
+      {
+        const bf16* arow = lat + l32 * kLatPitch + 128 * w + 8 * kg;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(arow + 16 * j), qb[j], acc, 0, 0, 0);
+        const char* rp = buf + kRopeOff + l32 * 128;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int c = 2 * j + kg;
@@ -218,53 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16(
               *(const bf16x8*)(rp + 16 * (c ^ (l32 & 7))), qb[8 + j], acc, 0, 0, 0);
         }
       }
-    }
-    // D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4
-
-    bf16x8 pb[2];
-    float alpha;
-    if (NB == 1) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(f32x4*)(&sm.s[(w * kHG + l32) * kSPitch + 8 * j + 4 * kg]) =
-            f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
-      lds_barrier();
-      // softmax of heads 8w..8w+7: lane -> head hs, tokens tq..tq+3
-      const int hs = 8 * w + (lane >> 3), tq = 4 * (lane & 7);
-      f32x4 x = *(const f32x4*)(&sm.s[(0 * kHG + hs) * kSPitch + tq]);
-#pragma unroll
-      for (int sl = 1; sl < 4; ++sl) x += *(const f32x4*)(&sm.s[(sl * kHG + hs) * kSPitch + tq]);
-      if (valid < kTT) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (tq + e >= valid) x[e] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-      const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid token
-      const float a = exp2f(m_run - m_new);
-      bf16 pe[4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pe[e] = (bf16)exp2f(x[e] - m_new);
-        psum += (float)pe[e];  // normalise with the rounded weights the MFMA uses
-      }
-      psum += __shfl_xor(psum, 1, 64);
-      psum += __shfl_xor(psum, 2, 64);
-      psum += __shfl_xor(psum, 4, 64);
-      l_run = a * l_run + psum;
-      m_run = m_new;
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      *(bf16x4*)(&sm.p[hs * kPPitch + tq]) = bf16x4{pe[0], pe[1], pe[2], pe[3]};
-      if ((lane & 7) == 0) sm.alpha[hs] = a;
-      lds_barrier();
-      alpha = sm.alpha[l32];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) pb[s2] = *(const bf16x8*)(&sm.p[l32 * kPPitch + 16 * s2 + 8 * kg]);
-    } else {
+      // D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4
       if (valid < kTT) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -309,8 +313,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16(
       *(f32x4*)(po + 32 * mb + 8 * q) =
           f32x4{O[mb][4 * q], O[mb][4 * q + 1], O[mb][4 * q + 2], O[mb][4 * q + 3]};
   if (NB == 1) {
-    if ((lane & 7) == 0) {
-      const int hs = h0 + 8 * w + (lane >> 3);
+    if (tb == 0 && g16 == 0) {
+      const int hs = h0 + 16 * hb + l16;
       ml[(size_t)hs * 2 + 0] = m_run;
       ml[(size_t)hs * 2 + 1] = l_run;
     }

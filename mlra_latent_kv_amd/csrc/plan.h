@@ -12,7 +12,7 @@ namespace mla {
 
 constexpr int kPage = MLA_PAGE_SIZE;   // tokens per page == tokens per main-loop tile
 constexpr int kHeadGroup = 32;         // heads per workgroup of the bf16 main kernel
-constexpr int kTargetWorkgroups = 256; // one per CU of an MI355X; the split heuristic aims here
+constexpr int kTargetWorkgroups = 512; // two per CU of an MI355X (main loop runs 2 per CU)
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxSplits = 512;        // bound on sequence splits (combine keeps weights in LDS)
 

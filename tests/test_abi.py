@@ -146,12 +146,12 @@ def test_workspace_layout(lib, wname):
     assert B.workspace_size(p) == exp
 
 
-def test_split_plan_targets_one_workgroup_per_cu(lib):
+def test_split_plan_targets_two_workgroups_per_cu(lib):
     p = params_for("mla_bf16_b32_h128_l4096", batch=32, max_seqlen=4096)
-    assert B.num_splits(p) == 2          # 32 sequences x 4 head groups x 2 splits = 256
+    assert B.num_splits(p) == 4          # 32 sequences x 4 head groups x 4 splits = 512
     p = params_for("mla_bf16_paged_b4_h128_l131072", batch=4, max_seqlen=131072,
                    max_pages_per_seq=2048, block_table_stride=2048)
-    assert B.num_splits(p) == 16
+    assert B.num_splits(p) == 32         # 4 sequences x 4 head groups x 32 splits = 512
     p.num_splits = 7
     assert B.num_splits(p) == 7
 
