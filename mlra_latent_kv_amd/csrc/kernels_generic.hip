@@ -5,6 +5,7 @@
 // Absorption ("超越 GQA 的推理革命…MLA…", section 矩陣吸收): the key up-projection W_UK is
 // folded into the query (prologue) and the value up-projection W_UV is applied once to the
 // attention-weighted latent (epilogue), so per-token keys and values are never formed.
+#include <algorithm>
 #include <cmath>
 
 #include "device_common.h"
@@ -88,23 +89,26 @@ hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
 // One workgroup handles 8 heads of one sequence: the split weights are formed once in LDS,
 // then the partial outputs stream through with 16-byte loads.  Splits with no tokens
 // carry m = -inf and weight 0 (their O_s is never read).
-constexpr int kCombHeads = 8;
+constexpr int kCombHeads = 8;    // heads per combine workgroup
+constexpr int kCombCols = 128;   // latent columns per combine workgroup (multiple of 4)
 
 template <typename TO>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o,
                                                  const float* __restrict__ part_ml,
                                                  TO* __restrict__ olat, int H, int S, int NB,
                                                  int dcb) {
-  extern __shared__ float sw[];  // [kCombHeads][NB][S]
+  extern __shared__ float sw[];  // [kCombHeads][branches in this column block][S]
   const int hb = blockIdx.x, b = blockIdx.y;
   const int h0 = hb * kCombHeads;
   const int nh = min(kCombHeads, H - h0);
   const int dc = NB * dcb;
+  const int d0 = blockIdx.z * kCombCols, d1 = min(dc, d0 + kCombCols);
+  const int br0 = d0 / dcb, nbr = (d1 - 1) / dcb - br0 + 1;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const size_t sstride = (size_t)NB * H * 2;
   // split weights: one wave per (head, branch), lanes stride over the splits
-  for (int pr = wv; pr < nh * NB; pr += blockDim.x / 64) {
-    const int hl = pr / NB, br = pr % NB;
+  for (int pr = wv; pr < nh * nbr; pr += blockDim.x / 64) {
+    const int hl = pr / nbr, br = br0 + pr % nbr;
     const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + (h0 + hl) * 2;
     float M = -INFINITY;
     for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[s * sstride]);
@@ -119,15 +123,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     for (int s = lane; s < S; s += 64) {
       const float m = ml[s * sstride];
-      sw[(hl * NB + br) * S + s] = (m == -INFINITY) ? 0.0f : exp2f(m - M) * inv;
+      sw[pr * S + s] = (m == -INFINITY) ? 0.0f : exp2f(m - M) * inv;
     }
   }
   __syncthreads();
-  const int q4 = dc / 4;
+  const int q4 = (d1 - d0) / 4;
   const size_t pstride = (size_t)H * dc;
   for (int it = threadIdx.x; it < nh * q4; it += blockDim.x) {
-    const int hl = it / q4, d = 4 * (it % q4);
-    const float* wrow = sw + (hl * NB + d / dcb) * S;
+    const int hl = it / q4, d = d0 + 4 * (it % q4);
+    const float* wrow = sw + (hl * nbr + d / dcb - br0) * S;
     const float* src = part_o + (((size_t)b * S) * H + h0 + hl) * dc + d;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < S; s0 += 4) {
@@ -149,8 +153,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
 }
 
 hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((p.H + kCombHeads - 1) / kCombHeads, p.B);
-  const size_t lds = (size_t)kCombHeads * p.NB * p.splits * sizeof(float);
+  const dim3 grid((p.H + kCombHeads - 1) / kCombHeads, p.B, (p.dc + kCombCols - 1) / kCombCols);
+  const int max_br = kCombCols / p.dcb + 2;
+  const size_t lds = (size_t)kCombHeads * std::min(p.NB, max_br) * p.splits * sizeof(float);
   if (p.dtype == MLA_BF16)
     hipLaunchKernelGGL(k_combine<bf16>, grid, dim3(256), lds, s, a.part_o, a.part_ml,
                        (bf16*)a.olat, p.H, p.splits, p.NB, p.dcb);
