@@ -17,7 +17,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["api.hip", "kernels_generic.hip", "kernels_bf16_aux.hip", "main_bf16.hip"]
+HIP_SOURCES = ["api.hip", "kernels_generic.hip", "kernels_bf16_aux.hip", "main_bf16.hip",
+               "main_bf16_wide.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 
@@ -32,16 +33,20 @@ def _flags():
     return ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+def _hip_flags():
+    # packed-fp32 instruction selection is disabled for all device code
+    return ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+            "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in VGPRs: the softmax may rescale them every tile,
+            # and VALU cannot operate on AGPRs (each rescale would copy them out and back)
+            "-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + _flags()
     if src.endswith(".hip"):
-        # packed-fp32 instruction selection is disabled for all device code
-        cmd += ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-                "-Xclang", "-packed-fp32-ops",
-                # keep MFMA accumulators in VGPRs: the softmax rescales them every tile, and
-                # VALU cannot operate on AGPRs (each rescale would copy them out and back)
-                "-mllvm", "-amdgpu-mfma-vgpr-form"]
+        cmd += _hip_flags()
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -60,7 +60,9 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
   if (e == hipSuccess) e = bf ? launch_prologue_bf16(plan, a, s) : launch_prologue(plan, a, s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
-    e = bf ? launch_main_bf16(plan, a, s) : launch_main_f32(plan, a, s);
+    e = !bf ? launch_main_f32(plan, a, s)
+        : plan.wide ? launch_main_bf16_wide(plan, a, s)
+                    : launch_main_bf16(plan, a, s);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_combine(plan, a, s);
   if (e == hipSuccess) e = mark(3);

@@ -34,6 +34,7 @@ void make_rope_freq(int d_rope, float theta, RopeFreq* out);
 hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s);       // fp32 path
 hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_main_bf16_wide(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_main_f32(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s);       // fp32 path

@@ -28,20 +28,16 @@
 //    leave its registers.
 #include "device_common.h"
 #include "launch.h"
+#include "tile_bf16.h"
 
 namespace mla {
 namespace {
 
-constexpr int kTT = 32;                              // tokens per tile (half a page)
+using namespace tile;
+
 constexpr int kHG = kHeadGroup;                      // heads per workgroup
 constexpr int kThreads = 256;                        // 4 waves
-constexpr int kDC = 512, kDR = 64, kRow = kDC + kDR;
-constexpr int kLatPitchB = kDC * 2 + 16;             // LDS bytes per latent row (bank skew)
-constexpr int kLatPitch = kLatPitchB / 2;            // ... in bf16 elements
-constexpr int kRopeOff = kTT * kLatPitchB;           // rotary region of a buffer
-constexpr int kBufBytes = kRopeOff + kTT * kDR * 2;  // one tile
 constexpr int kPPitch = kTT + 8;                     // bf16 probability row pitch
-
 constexpr int kBufs = 2;                             // tile ring depth per workgroup
 
 template <int NB>
@@ -52,40 +48,6 @@ struct Smem {
   float sum[NB == 1 ? 2 * kHG : 1];           // MLA: per-head probability sum of each half
   float alpha[NB == 1 ? kHG : 1];             // MLA: per-head rescale of this tile
 };
-
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16*lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
-}
-
-// Wait for all of this wave's tile loads (with a ring of two, the next tile is issued only
-// after the current one has landed).  s_waitcnt encoding (gfx9): vmcnt(0), other counters
-// left alone.
-__device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Workgroup barrier that orders LDS traffic only.  __syncthreads() also fences global
-// memory, which here would wait for every in-flight tile load (they write LDS
-// asynchronously) and drain the prefetch ring; tile arrival is tracked with explicit
-// vmcnt waits instead (wait_tiles).  The memory clobber keeps the compiler from moving
-// LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Value operand: 8 tokens of one latent column, two transposed 4-row reads `delta` rows apart.
-__device__ __forceinline__ bf16x8 tr_pair(const bf16* p, int delta_rows) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + delta_rows * kLatPitch));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
 
 template <int NB>
 __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
@@ -123,15 +85,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
   }
   const int n_tiles = (t_end - t_begin + kTT - 1) / kTT;
 
-  // Tile loads: wave w brings latent rows 8w..8w+7 (one row of 64 x 16 B per instruction)
-  // and the rotary keys of the same 8 rows (one instruction, 16-byte chunks XOR-swizzled by
-  // row so that 32 rows read at one column hit distinct banks).
+  // Tile loads: wave w brings latent rows 8w..8w+7 and the rotary keys of the same rows
+  // (chunk-swizzled through the per-lane source offsets).
   const uint32_t lat_row_b = (uint32_t)(lat_tok * 2), rope_row_b = (uint32_t)(rope_tok * 2);
-  uint32_t voff_lat[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) voff_lat[j] = (8 * w + j) * lat_row_b + 16 * lane;
-  const int rrow = 8 * w + (lane >> 3);
-  const uint32_t voff_rope = rrow * rope_row_b + 16 * ((lane & 7) ^ (rrow & 7));
 
   auto issue = [&](int k) {
     const int t0 = t_begin + kTT * k;
@@ -146,12 +102,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
       lb = latent + (int64_t)b * lat_seq + (int64_t)t0 * lat_tok;
       rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
     }
-    const __amdgpu_buffer_rsrc_t rl = rsrc(lb, valid * lat_row_b);
-    const __amdgpu_buffer_rsrc_t rr = rsrc(rb, valid * rope_row_b);
-    char* buf = sm.ring[k % kBufs];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(rl, buf + (8 * w + j) * kLatPitchB, voff_lat[j]);
-    dma16(rr, buf + kRopeOff + w * 1024, voff_rope);
+    issue_tile<Sw32, 4>(sm.ring[k % kBufs], w, lane, lb, rb, valid, lat_row_b, rope_row_b);
   };
 
   // absorbed query as the MFMA B operand (N = heads).
@@ -180,21 +131,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) O[mb] = f32x16{};
 
-  // transposed-read source coordinates for the value operand
+  // transposed-read sources of the value operand: rows v_row and v_row + v_delta of each
+  // 16-token half, columns 128w + 32mb + v_col (this wave's latent columns)
   const int g = lane >> 4, li = lane & 15;
-  const int v_col = 128 * w + 16 * (g & 1) + 4 * (li & 3);
+  const int v_col = 16 * (g & 1) + 4 * (li & 3);
   const int v_row = NB == 1 ? 8 * kg + (li >> 2) : 4 * kg + (li >> 2);
   constexpr int v_delta = NB == 1 ? 4 : 8;
+  uint32_t pv_off[2][2][4];  // [half][read][mb]; + 256w for the wave's column block
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        pv_off[s2][r][mb] = lat_piece<Sw32>(16 * s2 + v_row + r * v_delta, 32 * mb + v_col) + 256 * w;
 
   for (int k = 0; k < n_tiles; ++k) {
-    wait_tile();
+    wait_vmcnt<0>();  // with a ring of two, tile k+1 is issued only after tile k landed
     lds_barrier();  // tile k landed for every wave; buffer of tile k-1 is free
     if (k + 1 < n_tiles) issue(k + 1);
 
     const int t0 = t_begin + kTT * k;
     const int valid = min(kTT, t_end - t0);
     const char* buf = sm.ring[k % kBufs];
-    const bf16* lat = (const bf16*)buf;
 
     bf16x8 pb[2];
     float alpha;
@@ -202,18 +161,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
       // ---- scores of 16 tokens x 16 heads over all 576 columns (M = tokens, N = heads)
       f32x4 acc = {};
       {
+        // K-step j covers columns 32j..32j+31: chunk 4j + g16 of token t
         const int t = 16 * tb + l16;
-        const bf16* arow = lat + t * kLatPitch + 8 * g16;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(arow + 32 * j), qb[j], acc, 0, 0, 0);
-        const char* rrow = buf + kRopeOff + t * 128;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int c = 4 * j + g16;
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              *(const bf16x8*)(rrow + 16 * (c ^ (t & 7))), qb[16 + j], acc, 0, 0, 0);
-        }
+              lds_read16(buf + lat_chunk<Sw32>(t, 4 * (j & 3) + g16) + 256 * (j >> 2)), qb[j],
+              acc, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              lds_read16(buf + rope_chunk(t, 4 * j + g16)), qb[16 + j], acc, 0, 0, 0);
       }
       // D layout: lane (head 16*hb + l16, group g16), item e -> token 16*tb + 4*g16 + e
       const int h = 16 * hb + l16;
@@ -251,22 +209,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
       m_run = m_new;
       alpha = sm.alpha[l32];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) pb[s2] = *(const bf16x8*)(&sm.p[l32 * kPPitch + 16 * s2 + 8 * kg]);
+      for (int s2 = 0; s2 < 2; ++s2)
+        pb[s2] = lds_read16((const char*)&sm.p[l32 * kPPitch + 16 * s2 + 8 * kg]);
     } else {
       // ---- branch-w scores S^T[t][h] (M = tokens, N = heads): 128 latent + 64 rotary columns
       f32x16 acc = {};
       {
-        const bf16* arow = lat + l32 * kLatPitch + 128 * w + 8 * kg;
+        // K-step j covers columns 128w + 16j..: chunk 16w + 2j + kg of token l32
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(arow + 16 * j), qb[j], acc, 0, 0, 0);
-        const char* rp = buf + kRopeOff + l32 * 128;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = 2 * j + kg;
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *(const bf16x8*)(rp + 16 * (c ^ (l32 & 7))), qb[8 + j], acc, 0, 0, 0);
-        }
+              lds_read16(buf + lat_chunk<Sw32>(l32, 2 * j + kg) + 256 * w), qb[j], acc, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_read16(buf + rope_chunk(l32, 2 * j + kg)), qb[8 + j], acc, 0, 0, 0);
       }
       // D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4
       if (valid < kTT) {
@@ -296,12 +253,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) O[mb] *= alpha;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16* vb = lat + (16 * s2 + v_row) * kLatPitch + v_col;
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_pair(vb + 32 * mb, v_delta), pb[s2], O[mb], 0, 0, 0);
-    }
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_pair(buf + pv_off[s2][0][mb], buf + pv_off[s2][1][mb]), pb[s2], O[mb], 0, 0, 0);
   }
 
   // ---- partial outputs.  O[mb] item i: column d = 128w + 32mb + 8*(i/4) + 4*kg + i%4, head l32

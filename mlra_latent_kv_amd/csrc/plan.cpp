@@ -53,11 +53,13 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
       return MLA_ERR_UNSUPPORTED;
     q.path = Path::kBf16Mfma;
     q.n_hg = q.H / kHeadGroup;
+    q.wide = mla && q.H % kWideHeads == 0;
   } else {
     if ((q.NB != 1 && q.NB != 4) || q.dc > 512 || q.dr > 64 || q.dn > 256 || q.dv > 256)
       return MLA_ERR_UNSUPPORTED;
     q.path = Path::kF32Simt;
     q.n_hg = 0;
+    q.wide = 0;
   }
 
   // strides
@@ -74,10 +76,13 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
       return MLA_ERR_SHAPE;
   }
 
-  // split plan: aim for about one workgroup per CU on uniform lengths
-  const int64_t wg_per_split = q.path == Path::kBf16Mfma ? (int64_t)q.B * q.n_hg : (int64_t)q.B * q.H;
+  // split plan: enough workgroups to fill the chip on uniform lengths
+  const int64_t wg_per_split = q.path != Path::kBf16Mfma ? (int64_t)q.B * q.H
+                               : q.wide ? (int64_t)q.B * (q.H / kWideHeads)
+                                        : (int64_t)q.B * q.n_hg;
+  const int64_t target = q.wide ? kTargetWideWorkgroups : kTargetWorkgroups;
   int splits = p->num_splits;
-  if (splits == 0) splits = (int)std::max<int64_t>(1, ceil_div(kTargetWorkgroups, wg_per_split));
+  if (splits == 0) splits = (int)std::max<int64_t>(1, ceil_div(target, wg_per_split));
   if (splits > q.n_tiles) {
     if (p->num_splits) return MLA_ERR_SHAPE;
     splits = q.n_tiles;

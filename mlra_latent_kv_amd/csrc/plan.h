@@ -12,7 +12,9 @@ namespace mla {
 
 constexpr int kPage = MLA_PAGE_SIZE;   // tokens per page == tokens per main-loop tile
 constexpr int kHeadGroup = 32;         // heads per workgroup of the bf16 main kernel
-constexpr int kTargetWorkgroups = 512; // two per CU of an MI355X (main loop runs 2 per CU)
+constexpr int kTargetWorkgroups = 512; // two per CU of an MI355X (32-head kernel runs 2 per CU)
+constexpr int kWideHeads = 128;        // heads per workgroup of the wide bf16 kernel
+constexpr int kTargetWideWorkgroups = 256;  // one per CU (the wide kernel fills a CU's LDS)
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxSplits = 512;        // bound on sequence splits (combine keeps weights in LDS)
 
@@ -27,6 +29,7 @@ struct Plan {
   int splits;    // sequence splits per sequence
   int chunk;     // tokens per split, multiple of 64
   int n_hg;      // head groups of the bf16 kernel (H / 32); 0 on the fp32 path
+  int wide;      // 1: bf16 MLA with H % 128 == 0 runs the 128-heads-per-workgroup kernel
   Path path;
   // workspace layout (byte offsets)
   size_t off_qcat, off_part_o, off_part_ml, off_olat, bytes;

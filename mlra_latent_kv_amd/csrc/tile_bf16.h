@@ -1,0 +1,134 @@
+// LDS tile of cached rows shared by the bf16 main loops (gfx950).
+//
+// A tile holds 32 consecutive tokens of one sequence (half a page): the 512 latent columns
+// of each token in a 1024-byte row, then the 64 rotary-key columns of each token in a
+// 128-byte row.  Tiles arrive by direct-to-LDS buffer loads, where lane i of an instruction
+// always lands at byte 16*i of its destination, so the only freedom is which global 16-byte
+// chunk each lane fetches.  That choice implements an XOR swizzle of the chunks inside a
+// row, which keeps the reads free of LDS bank conflicts (64 banks of 4 bytes):
+//  * the score step reads one 16-byte chunk per token for 16 consecutive tokens at a time
+//    (ds_read_b128): the swizzle must be a bijection on any 16 consecutive rows;
+//  * the value step reads with ds_read_b64_tr_b16 (32 lanes of 8 bytes at a time), either
+//    4 rows x 4 chunks (32x32 MFMA operands, Sw32) or 8 rows x 2 chunks (16x16 operands,
+//    Sw16); the rows of one read must land on disjoint chunk slots.
+// Sw32: t mod 4 -> chunk bits 2-3, (t / 4) mod 4 -> bits 0-1.
+// Sw16: t mod 8 -> chunk bits 1-3, (t / 8) mod 2 -> bit 0.
+// Both repeat every 16 rows.  Rotary rows are 8 chunks and two share a 256-byte bank line;
+// rope_sw(t) = (t/2) mod 8 separates 16 consecutive rows.
+#pragma once
+
+#include "device_common.h"
+
+namespace mla {
+namespace tile {
+
+constexpr int kTT = 32;                                // tokens per tile
+constexpr int kDC = 512, kDR = 64, kRow = kDC + kDR;   // latent / rotary / cached row width
+constexpr int kLatRowB = kDC * 2;                      // bytes per latent row in LDS
+constexpr int kRopeRowB = kDR * 2;                     // bytes per rotary row in LDS
+constexpr int kRopeOff = kTT * kLatRowB;               // rotary region of a buffer
+constexpr int kBufBytes = kRopeOff + kTT * kRopeRowB;  // one tile: 36864 bytes
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+enum Swizzle { Sw32, Sw16 };
+
+template <Swizzle SW>
+__device__ __forceinline__ int lat_sw(int t) {
+  return SW == Sw32 ? (((t & 3) << 2) | ((t >> 2) & 3)) : (((t & 7) << 1) | ((t >> 3) & 1));
+}
+__device__ __forceinline__ int rope_sw(int t) { return (t >> 1) & 7; }
+
+// Byte offset in a tile buffer of latent (row t, global 16-byte chunk c), and of the 8-byte
+// piece holding element columns col..col+3 (col % 4 == 0).
+template <Swizzle SW>
+__device__ __forceinline__ uint32_t lat_chunk(int t, int c) {
+  return (uint32_t)(t * kLatRowB + 16 * (c ^ lat_sw<SW>(t)));
+}
+template <Swizzle SW>
+__device__ __forceinline__ uint32_t lat_piece(int t, int col) {
+  return lat_chunk<SW>(t, col >> 3) + 2 * (col & 7);
+}
+// Byte offset of rotary (row t, 16-byte chunk c), c < 8.
+__device__ __forceinline__ uint32_t rope_chunk(int t, int c) {
+  return (uint32_t)(kRopeOff + t * kRopeRowB + 16 * (c ^ rope_sw(t)));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16*lane.  Offsets at or past
+// the descriptor's size read back as zeros without touching memory.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Loads one wave issues per tile when NW waves share it: wave w fetches latent rows
+// (32/NW)w.. (one 1 KiB row per instruction) and, if w < 4, rotary rows 8w..8w+7 (one
+// instruction).
+template <int NW>
+__device__ __forceinline__ constexpr int issues_per_wave(bool rope_wave) {
+  return kTT / NW + (rope_wave ? 1 : 0);
+}
+
+// Issue wave w's loads of a tile whose first token row starts at lb (latent) / rb (rotary);
+// rows >= valid read as zeros.  Lane offsets are formed here (a few VALU operations per
+// load) rather than kept in registers across the loop.
+template <Swizzle SW, int NW>
+__device__ __forceinline__ void issue_tile(char* buf, int w, int lane, const bf16* lb,
+                                           const bf16* rb, int valid, uint32_t lat_row_b,
+                                           uint32_t rope_row_b) {
+  constexpr int R = kTT / NW;
+  const __amdgpu_buffer_rsrc_t rl = rsrc(lb, valid * lat_row_b);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int t = R * w + j;
+    dma16(rl, buf + t * kLatRowB, t * lat_row_b + 16 * (lane ^ lat_sw<SW>(t)));
+  }
+  if (w < 4) {
+    const __amdgpu_buffer_rsrc_t rr = rsrc(rb, valid * rope_row_b);
+    const int rt = 8 * w + (lane >> 3);
+    dma16(rr, buf + kRopeOff + w * 1024, rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
+  }
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt low bits
+// [3:0], high bits [15:14]; expcnt [6:4] and lgkmcnt [11:8] at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also fences global
+// memory, which would wait for every in-flight tile load (they write LDS asynchronously)
+// and drain the prefetch ring; tile arrival is tracked with explicit vmcnt waits instead.
+// The memory clobber keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS reads of tile (and query) data.  The pointer is a restrict parameter so that the
+// inlined access carries alias-scope information: without it the compiler's wait analysis
+// cannot tell a read of the current tile from the direct-to-LDS loads still in flight into
+// other ring buffers, and inserts a wait for all of them (vmcnt(0)) before the read, which
+// serialises the prefetch with the compute.  Arrival of the tile being read is guaranteed
+// by the explicit vmcnt wait and barrier at the top of each tile iteration.
+__device__ __forceinline__ bf16x8 lds_read16(const char* __restrict__ p) {
+  return *(const bf16x8*)p;
+}
+__device__ __forceinline__ s16x4 lds_read_tr(const char* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+
+// Value operand of an MFMA: two transposed 4-row reads (8 tokens of one column).
+__device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
+  const s16x4 a = lds_read_tr(lo);
+  const s16x4 b = lds_read_tr(hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace tile
+}  // namespace mla

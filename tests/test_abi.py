@@ -146,14 +146,21 @@ def test_workspace_layout(lib, wname):
     assert B.workspace_size(p) == exp
 
 
-def test_split_plan_targets_two_workgroups_per_cu(lib):
+def test_split_plan_fills_the_chip(lib):
+    # bf16 MLA with H % 128 == 0: one workgroup per (sequence, split, 128 heads), 256 in all
     p = params_for("mla_bf16_b32_h128_l4096", batch=32, max_seqlen=4096)
-    assert B.num_splits(p) == 4          # 32 sequences x 4 head groups x 4 splits = 512
+    assert B.num_splits(p) == 8          # 32 sequences x 8 splits = 256
     p = params_for("mla_bf16_paged_b4_h128_l131072", batch=4, max_seqlen=131072,
                    max_pages_per_seq=2048, block_table_stride=2048)
-    assert B.num_splits(p) == 32         # 4 sequences x 4 head groups x 32 splits = 512
+    assert B.num_splits(p) == 64         # 4 sequences x 64 splits = 256
     p.num_splits = 7
     assert B.num_splits(p) == 7
+    # 32-head groups (two workgroups per CU): 512 in all
+    p = params_for("mla_bf16_paged_b64_h32_l1k-32k", batch=64, max_seqlen=32768,
+                   max_pages_per_seq=512, block_table_stride=512)
+    assert B.num_splits(p) == 8          # 64 sequences x 1 head group x 8 splits = 512
+    p = params_for("mlra4_bf16_b32_h32_l8192", batch=32, max_seqlen=8192)
+    assert B.num_splits(p) == 16         # 32 sequences x 1 head group x 16 splits = 512
 
 
 def test_plan_code_under_host_sanitizers(tmp_path):

@@ -148,8 +148,13 @@ def test_split_count_invariance(wname):
     for splits in (1, 2, 7, 24):
         outs[splits], _ = gpu_out(inp, num_splits=splits)
         assert_close(outs[splits], ref, "bf16", f"{wname} splits={splits}")
+    # Different split counts differ only by rounding: the bf16 weights are rounded against a
+    # running max that depends on where the splits start, then the bf16 latent output and
+    # the bf16 result are rounded again.  Each of those three roundings moves a value by at
+    # most 2^-9 relative (about 1.1e-3 rms), so two runs differ by at most about
+    # 2 * sqrt(3) * 1.1e-3 ~ 4e-3 rms; a wrong combine or a lost split is off by O(1).
     for s in (2, 7, 24):
-        assert rel_l2(outs[s], outs[1]) < 3e-3
+        assert rel_l2(outs[s], outs[1]) < 5e-3
 
 
 def test_paged_and_contiguous_bitwise_equal():
