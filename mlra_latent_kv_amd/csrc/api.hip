@@ -47,7 +47,7 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
   a.rope_theta = p->rope_theta;
   char* ws = static_cast<char*>(workspace);
   a.qcat = ws + plan.off_qcat;
-  a.part_o = reinterpret_cast<float*>(ws + plan.off_part_o);
+  a.part_o = ws + plan.off_part_o;
   a.part_ml = reinterpret_cast<float*>(ws + plan.off_part_ml);
   a.olat = ws + plan.off_olat;
 

@@ -8,6 +8,7 @@ namespace mla {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -35,6 +36,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+
+// Reductions over lane pairs (i, i ^ 16) and (i, i ^ 32) with the gfx950 row-swap
+// instructions (one VALU op each, no LDS round trip).  With both operands holding v, the two
+// results of v_permlane16_swap are v[i & ~16] and v[i | 16] in every lane i (for
+// v_permlane32_swap, v[i & ~32] and v[i | 32]): the lane's own value and its partner's.
+// (The results are copied to scalars before the bit casts: a bit cast applied directly to an
+// element of the returned vector reads element 0 whatever the index.)
+__device__ __forceinline__ void pair16(float v, float* a, float* b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  *a = __builtin_bit_cast(float, r0);
+  *b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void pair32(float v, float* a, float* b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  *a = __builtin_bit_cast(float, r0);
+  *b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_xor16(float v) { float a, b; pair16(v, &a, &b); return fmaxf(a, b); }
+__device__ __forceinline__ float max_xor32(float v) { float a, b; pair32(v, &a, &b); return fmaxf(a, b); }
+__device__ __forceinline__ float sum_xor16(float v) { float a, b; pair16(v, &a, &b); return a + b; }
+__device__ __forceinline__ float sum_xor32(float v) { float a, b; pair32(v, &a, &b); return a + b; }
 
 // RoPE frequencies theta^(-2k/d_rope) for k < d_rope/2, computed on the host in fp64 and
 // passed by value as a kernel argument (d_rope <= 256).

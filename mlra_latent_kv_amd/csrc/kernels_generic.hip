@@ -86,14 +86,21 @@ hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
 // ----------------------------------------------------------------------------- combine
 // Per (b, h, branch): merge the splits' (m_s, l_s, O_s) with log-sum-exp weights:
 //   M = max_s m_s,  o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One workgroup handles 8 heads of one sequence: the split weights are formed once in LDS,
-// then the partial outputs stream through with 16-byte loads.  Splits with no tokens
-// carry m = -inf and weight 0 (their O_s is never read).
+// fp32 path: one workgroup handles 8 heads of one sequence; the split weights are formed
+// once in LDS, then the partial outputs stream through.  Splits with no tokens carry
+// m = -inf and weight 0 (their O_s is never read).
 constexpr int kCombHeads = 8;    // heads per combine workgroup
 constexpr int kCombCols = 128;   // latent columns per combine workgroup (multiple of 4)
 
-template <typename TO>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o,
+// Four consecutive partial values as fp32.
+__device__ __forceinline__ f32x4 load4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+  const bf16x4 v = *(const bf16x4*)p;
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+template <typename TP, typename TO>
+__global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ part_o,
                                                  const float* __restrict__ part_ml,
                                                  TO* __restrict__ olat, int H, int S, int NB,
                                                  int dcb) {
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
   for (int it = threadIdx.x; it < nh * q4; it += blockDim.x) {
     const int hl = it / q4, d = d0 + 4 * (it % q4);
     const float* wrow = sw + (hl * nbr + d / dcb - br0) * S;
-    const float* src = part_o + (((size_t)b * S) * H + h0 + hl) * dc + d;
+    const TP* src = part_o + (((size_t)b * S) * H + h0 + hl) * dc + d;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < S; s0 += 4) {
       f32x4 v[4];
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
       for (int u = 0; u < 4; ++u) {
         wt[u] = s0 + u < S ? wrow[s0 + u] : 0.0f;
         // splits with no tokens have weight 0 and never-written partials: skip the load
-        v[u] = wt[u] != 0.0f ? *(const f32x4*)(src + (size_t)(s0 + u) * pstride) : f32x4{};
+        v[u] = wt[u] != 0.0f ? load4(src + (size_t)(s0 + u) * pstride) : f32x4{};
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) acc += wt[u] * v[u];
@@ -152,16 +159,88 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
   }
 }
 
+// bf16 path (d_c = 512, branch width 128 or 512): one workgroup per (sequence, head).  The
+// split weights of the head's branches go to LDS once; wave w then takes splits w, w+4, ...
+// with each lane covering 8 consecutive latent columns (16-byte loads, four splits in
+// flight), and the four waves' sums meet in LDS.
+constexpr int kCombDc = 512;
+
+__global__ __launch_bounds__(256) void k_combine_bf16(const bf16* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      bf16* __restrict__ olat, int H, int S,
+                                                      int NB, int dcb) {
+  __shared__ float wts[4 * kMaxSplits];  // [branch][split]
+  __shared__ f32x4 red[3][2][64];        // sums of waves 1..3, [half of the 8 columns][lane]
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const size_t sstride = (size_t)NB * H * 2;
+  for (int br = wv; br < NB; br += 4) {
+    const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + h * 2;
+    float M = -INFINITY;
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[s * sstride]);
+    M = wave_max(M);
+    float den = 0.0f;
+    if (M != -INFINITY)
+      for (int s = lane; s < S; s += 64) {
+        const float m = ml[s * sstride];
+        if (m != -INFINITY) den = fmaf(exp2f(m - M), ml[s * sstride + 1], den);
+      }
+    den = wave_sum(den);
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    for (int s = lane; s < S; s += 64) {
+      const float m = ml[s * sstride];
+      wts[br * S + s] = (m == -INFINITY) ? 0.0f : exp2f(m - M) * inv;
+    }
+  }
+  __syncthreads();
+  const float* w = wts + (8 * lane / dcb) * S;
+  const bf16* src = part_o + (((size_t)b * S) * H + h) * kCombDc + 8 * lane;
+  const size_t pstride = (size_t)H * kCombDc;
+  f32x4 acc0 = {}, acc1 = {};
+  for (int s0 = wv; s0 < S; s0 += 16) {
+    bf16x8 v[4];
+    float wt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + 4 * u;
+      wt[u] = s < S ? w[s] : 0.0f;
+      // splits with no tokens have weight 0 and never-written partials: skip the load
+      v[u] = wt[u] != 0.0f ? *(const bf16x8*)(src + (size_t)s * pstride) : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc0 += wt[u] * f32x4{(float)v[u][0], (float)v[u][1], (float)v[u][2], (float)v[u][3]};
+      acc1 += wt[u] * f32x4{(float)v[u][4], (float)v[u][5], (float)v[u][6], (float)v[u][7]};
+    }
+  }
+  if (wv > 0) {
+    red[wv - 1][0][lane] = acc0;
+    red[wv - 1][1][lane] = acc1;
+  }
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      acc0 += red[k][0][lane];
+      acc1 += red[k][1][lane];
+    }
+    *(bf16x8*)(olat + ((size_t)b * H + h) * kCombDc + 8 * lane) =
+        bf16x8{(bf16)acc0[0], (bf16)acc0[1], (bf16)acc0[2], (bf16)acc0[3],
+               (bf16)acc1[0], (bf16)acc1[1], (bf16)acc1[2], (bf16)acc1[3]};
+  }
+}
+
 hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s) {
+  if (p.dtype == MLA_BF16) {
+    hipLaunchKernelGGL(k_combine_bf16, dim3(p.B * p.H), dim3(256), 0, s, (const bf16*)a.part_o,
+                       a.part_ml, (bf16*)a.olat, p.H, p.splits, p.NB, p.dcb);
+    return hipGetLastError();
+  }
   const dim3 grid((p.H + kCombHeads - 1) / kCombHeads, p.B, (p.dc + kCombCols - 1) / kCombCols);
   const int max_br = kCombCols / p.dcb + 2;
   const size_t lds = (size_t)kCombHeads * std::min(p.NB, max_br) * p.splits * sizeof(float);
-  if (p.dtype == MLA_BF16)
-    hipLaunchKernelGGL(k_combine<bf16>, grid, dim3(256), lds, s, a.part_o, a.part_ml,
-                       (bf16*)a.olat, p.H, p.splits, p.NB, p.dcb);
-  else
-    hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), lds, s, a.part_o, a.part_ml,
-                       (float*)a.olat, p.H, p.splits, p.NB, p.dcb);
+  hipLaunchKernelGGL((k_combine<float, float>), grid, dim3(256), lds, s, (const float*)a.part_o,
+                     a.part_ml, (float*)a.olat, p.H, p.splits, p.NB, p.dcb);
   return hipGetLastError();
 }
 
@@ -338,7 +417,7 @@ hipError_t launch_main_f32(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_main_f32, grid, dim3(64), 0, s, (const float*)a.qcat,
                      (const float*)a.latent, (const float*)a.rope, a.lat_tok, a.lat_seq,
                      a.rope_tok, a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged,
-                     a.part_o, a.part_ml, p.H, p.splits, p.chunk, p.NB, p.dcb, p.dr);
+                     (float*)a.part_o, a.part_ml, p.H, p.splits, p.chunk, p.NB, p.dcb, p.dr);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ struct DecodeArgs {
   float softmax_scale, out_scale, rope_theta;
   // workspace regions
   void* qcat;       // [B][H][row] storage dtype, pre-scaled by softmax_scale*log2(e)
-  float* part_o;    // [B][S][H][d_c]
+  void* part_o;     // [B][S][H][d_c], unnormalised partial latent outputs: bf16 on the bf16
+                    // path (the same rounding as the latent output), fp32 otherwise
   float* part_ml;   // [B][S][NB][H][2]  (running max in log2 units, running sum)
   void* olat;       // [B][H][d_c], bf16 on the bf16 path (MFMA operand), fp32 otherwise
 };

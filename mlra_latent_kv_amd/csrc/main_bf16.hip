@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
-    int64_t bt_stride, int paged, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
+    int64_t bt_stride, int paged, bf16* __restrict__ part_o, float* __restrict__ part_ml, int H,
     int S, int chunk, int n_hg, int units) {
   __shared__ __align__(16) Smem<NB> sm;
 
@@ -182,8 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
           if (tq + e >= valid) acc[e] = -INFINITY;
       }
       float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_xor32(max_xor16(mx));
       if (g16 == 0) sm.mx[tb * kHG + h] = mx;
       lds_barrier();
       mx = fmaxf(mx, sm.mx[(tb ^ 1) * kHG + h]);  // max over the tile's 32 tokens
@@ -196,9 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
         pe[e] = (bf16)exp2f(acc[e] - m_new);
         psum += (float)pe[e];  // normalise with the rounded weights the MFMA uses
       }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      psum = sum_xor32(sum_xor16(psum));
       *(bf16x4*)(&sm.p[h * kPPitch + tq]) = bf16x4{pe[0], pe[1], pe[2], pe[3]};
       if (g16 == 0) {
         sm.sum[tb * kHG + h] = psum;
@@ -234,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
       float mx = acc[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_xor32(mx);
       const float m_new = fmaxf(m_run, mx);
       alpha = exp2f(m_run - m_new);
       float psum = 0.0f;
@@ -244,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
         pb[i >> 3][i & 7] = e;
         psum += (float)e;
       }
-      psum += __shfl_xor(psum, 32, 64);
+      psum = sum_xor32(psum);
       l_run = alpha * l_run + psum;
       m_run = m_new;
     }
@@ -261,13 +258,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
   }
 
   // ---- partial outputs.  O[mb] item i: column d = 128w + 32mb + 8*(i/4) + 4*kg + i%4, head l32
-  float* po = part_o + (((size_t)b * S + s) * H + h0 + l32) * kDC + 128 * w + 4 * kg;
+  bf16* po = part_o + (((size_t)b * S + s) * H + h0 + l32) * kDC + 128 * w + 4 * kg;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *(f32x4*)(po + 32 * mb + 8 * q) =
-          f32x4{O[mb][4 * q], O[mb][4 * q + 1], O[mb][4 * q + 2], O[mb][4 * q + 3]};
+      *(bf16x4*)(po + 32 * mb + 8 * q) =
+          bf16x4{(bf16)O[mb][4 * q], (bf16)O[mb][4 * q + 1], (bf16)O[mb][4 * q + 2],
+                 (bf16)O[mb][4 * q + 3]};
   if (NB == 1) {
     if (tb == 0 && g16 == 0) {
       const int hs = h0 + 16 * hb + l16;
@@ -288,7 +286,7 @@ hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   auto kern = p.NB == 1 ? k_main_bf16<1> : k_main_bf16<4>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, s, (const bf16*)a.qcat,
                      (const bf16*)a.latent, (const bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok,
-                     a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged, a.part_o,
+                     a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,
                      a.part_ml, p.H, p.splits, p.chunk, p.n_hg, units);
   return hipGetLastError();
 }

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
-    int64_t bt_stride, int paged, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
+    int64_t bt_stride, int paged, bf16* __restrict__ part_o, float* __restrict__ part_ml, int H,
     int S, int chunk, int n_hq, int units) {
   // One LDS object holds both regions.  (Kept as a single struct: with separate arrays the
   // compiler's wait analysis stops telling the tile reads apart from the loads in flight
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   // kQRegSteps in registers, the rest in qlds (this wave's 16 heads are written and read by
   // this wave only).
   bf16x8 qb[kQRegSteps];
-  uint32_t qr_off = (g16 * kHeadsWG + 16 * w + l16) * 16;  // + 8 KiB per LDS K-step
+  const uint32_t qr_off = (g16 * kHeadsWG + 16 * w + l16) * 16;  // + 8 KiB per LDS K-step
   {
     const bf16* qrow = qcat + ((size_t)b * H + h0 + l16) * kRow + 8 * g16;
 #pragma unroll
@@ -163,24 +163,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     }
     lds_barrier();  // tile k landed for every wave; the buffer of tile k-1 is free
     if (k + kAhead < n_tiles) issue(k + kAhead, pg);
-    const char* buf = ring[k % kRing];
-    // The per-lane base offsets are re-declared opaque every iteration so that the compiler
-    // keeps only these 15 registers live across the loop and folds the constant parts of each
-    // address into the instructions' offset fields, instead of hoisting one register per
-    // (base + constant) pair out of the loop.
+    // Per-tile LDS base addresses, opaque to the optimiser: every read below is one of these
+    // plus a constant that goes into the instruction's offset field (otherwise the compiler
+    // hoists one register per base + constant, or picks a base above the reads and pays an
+    // add per read for the negative difference).
+    const uint32_t bufa = lds_addr(ring[k % kRing]);
+    uint32_t qa[4], ra[2], pa[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(qk_off[j]));
+    for (int j = 0; j < 4; ++j) qa[j] = opaque(bufa + qk_off[j]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(rp_off[j]));
+    for (int j = 0; j < 2; ++j) ra[j] = opaque(bufa + rp_off[j]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(pv_off[c]));
-    asm volatile("" : "+v"(qr_off));
+    for (int c = 0; c < 8; ++c) pa[c] = opaque(bufa + pv_off[c]);
+    const uint32_t qla = opaque(lds_addr(qlds) + qr_off);
 
     // ---- S^T[t][h] for tokens 16*tb.. (M) and the wave's 16 heads (N).  Tile operands
     // are read kQkAhead K-steps ahead of their MFMAs.
     auto a_tile = [&](int j, int tb) -> bf16x8 {
-      return j < 16 ? lds_read16(buf + qk_off[j & 3] + 256 * (j >> 2) + 16384 * tb)
-                    : lds_read16(buf + rp_off[j - 16] + 2048 * tb);
+      return j < 16 ? lds_read16_at(qa[j & 3] + 256 * (j >> 2) + 16384 * tb)
+                    : lds_read16_at(ra[j - 16] + 2048 * tb);
     };
     constexpr int kQkAhead = 2;
     f32x4 acc[2] = {};
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
         aq[(j + kQkAhead) % (kQkAhead + 1)][1] = a_tile(j + kQkAhead, 1);
       }
       const bf16x8 qv = j < kQRegSteps ? qb[j < kQRegSteps ? j : 0]
-                                       : lds_read16(qlds + qr_off + 8192 * (j - kQRegSteps));
+                                       : lds_read16_at(qla + 8192 * (j - kQRegSteps));
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
         acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[j % (kQkAhead + 1)][tb], qv, acc[tb],
@@ -209,8 +210,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
 
     // value operands of the first column blocks, read while the softmax runs
     auto v_tile = [&](int cb) -> bf16x8 {
-      const char* p = buf + pv_off[cb & 7] + 256 * (cb >> 3);
-      return tr_pair(p, p + 16384);
+      const uint32_t a = pa[cb & 7] + 256 * (cb >> 3);
+      return tr_pair_at(a, a + 16384);
     };
     constexpr int kPvAhead = 4;
     bf16x8 vq[kPvAhead + 1];
@@ -229,8 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     }
     float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
                      fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // every tile holds a valid token: mx finite
+    mx = max_xor32(max_xor16(mx));  // every tile holds a valid token: mx finite
     if (k == 0) {
       m_ref = mx;  // O and l are still zero
     } else if (__ballot(mx > m_ref + kLazyTau) != 0) {
@@ -253,9 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
         pb[4 * tb + e] = p;
         psum += (float)p;  // normalise with the rounded weights the MFMA uses
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run += psum;
+    l_run += sum_xor32(sum_xor16(psum));
 
     // ---- O^T[d][h] += V^T P^T over the 32 column blocks, operands kPvAhead blocks ahead
 #pragma unroll
@@ -267,9 +265,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   }
 
   // ---- partial outputs.  O[cb] item e: column 16cb + 4*g16 + e of head h0 + l16
-  float* po = part_o + (((size_t)b * S + s) * H + h0 + l16) * kDC + 4 * g16;
+  bf16* po = part_o + (((size_t)b * S + s) * H + h0 + l16) * kDC + 4 * g16;
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb) *(f32x4*)(po + 16 * cb) = O[cb];
+  for (int cb = 0; cb < 32; ++cb)
+    *(bf16x4*)(po + 16 * cb) =
+        bf16x4{(bf16)O[cb][0], (bf16)O[cb][1], (bf16)O[cb][2], (bf16)O[cb][3]};
   if (g16 == 0) {
     ml[(size_t)(h0 + l16) * 2 + 0] = m_ref;
     ml[(size_t)(h0 + l16) * 2 + 1] = l_run;
@@ -284,7 +284,7 @@ hipError_t launch_main_bf16_wide(const Plan& p, const DecodeArgs& a, hipStream_t
   const unsigned blocks = (unsigned)(((units + 7) / 8) * 8 * n_hq);
   hipLaunchKernelGGL(k_main_bf16_wide, dim3(blocks), dim3(kThreads), 0, s, (const bf16*)a.qcat,
                      (const bf16*)a.latent, (const bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok,
-                     a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged, a.part_o,
+                     a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,
                      a.part_ml, p.H, p.splits, p.chunk, n_hq, units);
   return hipGetLastError();
 }

@@ -92,14 +92,16 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
   q.splits = (int)ceil_div(q.n_tiles, chunk_tiles);
   if (q.splits > kMaxSplits) return MLA_ERR_SHAPE;
   // grid sizes and 32-bit work-item indices must fit
-  if (wg_per_split * q.splits + 8LL * std::max(q.n_hg, 1) > INT32_MAX) return MLA_ERR_SHAPE;
+  if (wg_per_split * q.splits + 8LL * std::max(q.n_hg, 1) > INT32_MAX ||
+      (int64_t)q.B * q.H > INT32_MAX)
+    return MLA_ERR_SHAPE;
 
   // workspace
   size_t off = 0;
   q.off_qcat = off;
   off = align_up(off + (size_t)q.B * q.H * q.row * q.elem);
   q.off_part_o = off;
-  off = align_up(off + (size_t)q.B * q.splits * q.H * q.dc * sizeof(float));
+  off = align_up(off + (size_t)q.B * q.splits * q.H * q.dc * (q.dtype == MLA_BF16 ? 2 : 4));
   q.off_part_ml = off;
   off = align_up(off + (size_t)q.B * q.splits * q.NB * q.H * 2 * sizeof(float));
   q.off_olat = off;

@@ -31,7 +31,7 @@ struct Plan {
   int n_hg;      // head groups of the bf16 kernel (H / 32); 0 on the fp32 path
   int wide;      // 1: bf16 MLA with H % 128 == 0 runs the 128-heads-per-workgroup kernel
   Path path;
-  // workspace layout (byte offsets)
+  // workspace layout (byte offsets); part_o holds bf16 on the bf16 path, fp32 otherwise
   size_t off_qcat, off_part_o, off_part_ml, off_olat, bytes;
 };
 

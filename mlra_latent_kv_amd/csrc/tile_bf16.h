@@ -123,6 +123,33 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
+// The same reads at a 32-bit LDS address.  Callers form one opaque base address per tile
+// and add compile-time constants, which then go into the instructions' unsigned offset field
+// instead of costing an add each.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+__device__ __forceinline__ bf16x8 lds_read16_at(const lds_char* __restrict__ p) {
+  return *(const __attribute__((address_space(3))) bf16x8*)p;
+}
+__device__ __forceinline__ bf16x8 lds_read16_at(uint32_t a) {
+  return lds_read16_at((const lds_char*)(uintptr_t)a);
+}
+__device__ __forceinline__ s16x4 lds_read_tr_at(const lds_char* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+__device__ __forceinline__ bf16x8 tr_pair_at(uint32_t lo, uint32_t hi) {
+  const s16x4 a = lds_read_tr_at((const lds_char*)(uintptr_t)lo);
+  const s16x4 b = lds_read_tr_at((const lds_char*)(uintptr_t)hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Makes v opaque to the optimiser (no hoisting of expressions built from it).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Value operand of an MFMA: two transposed 4-row reads (8 tokens of one column).
 __device__ __forceinline__ bf16x8 tr_pair(const char* lo, const char* hi) {
   const s16x4 a = lds_read_tr(lo);

@@ -141,7 +141,8 @@ def test_workspace_layout(lib, wname):
     assert 1 <= S <= (w.seqlen + 63) // 64
     al = lambda x: (x + 255) // 256 * 256
     Bn, H, dc = 3, w.heads, w.d_c
-    exp = al(Bn * H * w.row * w.elem_bytes) + al(Bn * S * H * dc * 4) + \
+    # partial outputs are stored in the element type (bf16 on the bf16 path), (m, l) in fp32
+    exp = al(Bn * H * w.row * w.elem_bytes) + al(Bn * S * H * dc * w.elem_bytes) + \
         al(Bn * S * w.branches * H * 2 * 4) + al(Bn * H * dc * w.elem_bytes)
     assert B.workspace_size(p) == exp
 
