@@ -33,7 +33,7 @@ def _flags():
     return ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _hip_flags():
+def _hip_flags(src: str = ""):
     # packed-fp32 instruction selection is disabled for all device code
     return ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
             "-Xclang", "-packed-fp32-ops",
@@ -46,7 +46,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + _flags()
     if src.endswith(".hip"):
-        cmd += _hip_flags()
+        cmd += _hip_flags(src)
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

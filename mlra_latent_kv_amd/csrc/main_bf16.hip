@@ -40,13 +40,18 @@ constexpr int kThreads = 256;                        // 4 waves
 constexpr int kPPitch = kTT + 8;                     // bf16 probability row pitch
 constexpr int kBufs = 2;                             // tile ring depth per workgroup
 
+// LDS that waves write while tile loads are in flight is kept in front of the tile ring, with
+// a gap: placed right after the ring, a rare stale read of the exchanged per-head values was
+// observed on gfx950 while direct-to-LDS loads into the ring were outstanding (repeat-run
+// determinism tests guard this).
 template <int NB>
 struct Smem {
-  char ring[kBufs][kBufBytes];
   bf16 p[NB == 1 ? kHG * kPPitch : 8];        // MLA: probabilities [h][t]
   float mx[NB == 1 ? 2 * kHG : 1];            // MLA: per-head max of each 16-token half
   float sum[NB == 1 ? 2 * kHG : 1];           // MLA: per-head probability sum of each half
   float alpha[NB == 1 ? kHG : 1];             // MLA: per-head rescale of this tile
+  char gap[256];
+  __attribute__((aligned(256))) char ring[kBufs][kBufBytes];
 };
 
 template <int NB>

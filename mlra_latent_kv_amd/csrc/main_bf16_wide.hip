@@ -50,24 +50,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   // One LDS object holds both regions.  (Kept as a single struct: with separate arrays the
   // compiler's wait analysis stops telling the tile reads apart from the loads in flight
   // and waits for all of them before the first read of every tile.)
+  // (The query region sits in front of the ring: LDS that sits right behind the ring has
+  // shown rare stale reads on gfx950 while direct-to-LDS loads into the ring were in flight.)
   struct Smem {
-    char ring[kRing][kBufBytes];
     // query K-steps kQRegSteps..17 (columns 384..575), chunk-major: the 16-byte chunk of
     // K-step kQRegSteps + t, k-group g, head h at ((4t + g) * 128 + h) * 16, so 16
     // consecutive heads read 256 consecutive bytes
     char qlds[kQLdsSteps * 4 * kHeadsWG * 16];
+    char ring[kRing][kBufBytes];
   };
   __shared__ __align__(16) Smem sm;  // 156 KiB
   char (&ring)[kRing][kBufBytes] = sm.ring;
   char* const qlds = sm.qlds;
 
-  // XCD-aware mapping (consecutive blocks go to different XCDs): the head quads of one
-  // (sequence, split) sit 8 blocks apart, on one XCD, so their reads of the same tiles can
-  // share that XCD's L2.
+  // XCD-aware mapping.  Blocks are dispatched round-robin over the 8 XCDs; XCD x gets a
+  // contiguous range of (sequence, split) units, so the splits of one sequence (which all
+  // read its query) and the head quads of one unit (which read the same tiles) share that
+  // XCD's L2.
+  const int per_xcd = (units + 7) / 8;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, r = bid >> 3;
   const int hq = r % n_hq;
-  const int unit = (r / n_hq) * 8 + xcd;
+  const int unit = xcd * per_xcd + r / n_hq;
   if (unit >= units) return;
   const int b = unit / S, s = unit % S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -163,6 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     }
     lds_barrier();  // tile k landed for every wave; the buffer of tile k-1 is free
     if (k + kAhead < n_tiles) issue(k + kAhead, pg);
+    __builtin_amdgcn_sched_barrier(0);  // no operand reads hoisted above the loads' issue
     // Per-tile LDS base addresses, opaque to the optimiser: every read below is one of these
     // plus a constant that goes into the instruction's offset field (otherwise the compiler
     // hoists one register per base + constant, or picks a base above the reads and pays an
@@ -183,8 +188,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       return j < 16 ? lds_read16_at(qa[j & 3] + 256 * (j >> 2) + 16384 * tb)
                     : lds_read16_at(ra[j - 16] + 2048 * tb);
     };
-    constexpr int kQkAhead = 2;
-    f32x4 acc[2] = {};
+    constexpr int kQkAhead = 1;
+    // two accumulators per token block (even / odd K-steps): a dependent chain of 16x16x32
+    // MFMAs issues at about a third of the unit's rate
+    f32x4 acc2[2][2] = {};
     bf16x8 aq[kQkAhead + 1][2];
 #pragma unroll
     for (int j = 0; j < kQkAhead; ++j) {
@@ -201,8 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
                                        : lds_read16_at(qla + 8192 * (j - kQRegSteps));
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
-        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[j % (kQkAhead + 1)][tb], qv, acc[tb],
-                                                          0, 0, 0);
+        acc2[tb][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[j % (kQkAhead + 1)][tb], qv,
+                                                                  acc2[tb][j & 1], 0, 0, 0);
       // keep the written order: the scheduler would otherwise hoist more reads than the
       // register budget holds (O takes half of it) and spill
       __builtin_amdgcn_sched_barrier(0);
@@ -217,6 +224,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     bf16x8 vq[kPvAhead + 1];
 #pragma unroll
     for (int cb = 0; cb < kPvAhead; ++cb) vq[cb] = v_tile(cb);
+
+    f32x4 acc[2] = {acc2[0][0] + acc2[0][1], acc2[1][0] + acc2[1][1]};
 
     // ---- softmax.  D layout: lane (head l16, group g16), item e of block tb ->
     // token 16*tb + 4*g16 + e

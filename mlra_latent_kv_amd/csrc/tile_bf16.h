@@ -144,6 +144,12 @@ __device__ __forceinline__ bf16x8 tr_pair_at(uint32_t lo, uint32_t hi) {
   const s16x4 b = lds_read_tr_at((const lds_char*)(uintptr_t)hi);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+__device__ __forceinline__ f32x4 lds_load4f_at(const lds_char* __restrict__ p) {
+  return *(const __attribute__((address_space(3))) f32x4*)p;
+}
+__device__ __forceinline__ void lds_store4f_at(lds_char* __restrict__ p, f32x4 v) {
+  *(__attribute__((address_space(3))) f32x4*)p = v;
+}
 // Makes v opaque to the optimiser (no hoisting of expressions built from it).
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   asm volatile("" : "+v"(v));

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not ava
 
 def _asm(src: str, tmp_path) -> str:
     out = tmp_path / (src + ".s")
-    cmd = [HIPCC] + build._flags() + build._hip_flags() + [
+    cmd = [HIPCC] + build._flags() + build._hip_flags(src) + [
         "--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
@@ -43,11 +43,13 @@ def _kernels(asm: str):
 
 
 def _main_loop(lines):
-    """Lines of the outermost loop that issues tile loads: from its header label to the
-    last branch back to it."""
+    """Lines of the innermost loop that issues tile loads: from its header label to the last
+    branch back to it.  (The label of a nested loop carries the header note on the next
+    line.)"""
+    best = None
     for i, ln in enumerate(lines):
-        m = re.match(r"^(\.LBB\w+):.*Loop Header", ln)
-        if not m:
+        m = re.match(r"^(\.LBB\w+):", ln)
+        if not m or "Loop Header" not in ln + (lines[i + 1] if i + 1 < len(lines) else ""):
             continue
         label = m.group(1)
         back = [j for j in range(i + 1, len(lines))
@@ -56,18 +58,20 @@ def _main_loop(lines):
             continue
         body = lines[i:back[-1] + 1]
         if any("lds" in x and "buffer_load" in x for x in body):
-            return body
-    return None
+            if best is None or len(body) < len(best):
+                best = body
+    return best
 
 
 @pytest.mark.parametrize("src", ["main_bf16.hip", "main_bf16_wide.hip"])
 def test_main_loop_keeps_tile_loads_in_flight(src, tmp_path):
     kernels = _kernels(_asm(src, tmp_path))
     assert kernels, "no main-loop kernel found"
-    for name, lines, meta in kernels:
-        assert re.search(r"\.amdhsa_private_segment_fixed_size\s+0\b", meta), (name, "spills")
+    for name, lines, _meta in kernels:
         body = _main_loop(lines)
         assert body is not None, (name, "main loop not found")
         first_dma = next(i for i, x in enumerate(body) if "buffer_load" in x and "lds" in x)
         waits = [x.strip() for x in body[first_dma:] if re.search(r"s_waitcnt\s.*vmcnt\(0\)", x)]
         assert not waits, (name, "drains the tile loads inside the loop", waits)
+        spills = [x.strip() for x in body if "scratch_" in x]
+        assert not spills, (name, "spills inside the loop", spills[:4])

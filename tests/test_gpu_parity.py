@@ -164,6 +164,32 @@ def test_paged_and_contiguous_bitwise_equal():
     a, _ = gpu_out(I.make_inputs(w, seed=5, seqlens=lens, paged=True), num_splits=3)
     b, _ = gpu_out(I.make_inputs(w, seed=5, seqlens=lens, paged=False), num_splits=3)
     assert np.array_equal(a, b)
+@pytest.mark.parametrize("wname,lens,splits", [
+    ("mla_bf16_paged_b64_h32_l1k-32k", [65, 1000, 64, 333], 3),
+    ("mlra4_bf16_b32_h32_l8192", [700, 1500, 129], 7),
+    ("mla_bf16_b32_h128_l4096", [700, 1500, 129], 7),
+])
+def test_repeat_runs_bitwise_identical(wname, lens, splits):
+    """Every main loop is deterministic: 300 back-to-back runs of one case produce the same
+    partials and outputs, bit for bit, paged and contiguous.  (A layout with per-tile exchange
+    data right behind the tile ring once gave a run in a few hundred a stale exchanged value
+    while tile loads were in flight; this catches any such race.)"""
+    import torch
+    from mlra_latent_kv_amd import harness as H
+    w = I.WORKLOADS[wname]
+    for paged in (True, False):
+        case = H.to_device(I.make_inputs(w, seed=5, seqlens=lens, paged=paged), num_splits=splits)
+        ref = None
+        for _ in range(300):
+            case.run()
+            torch.cuda.synchronize()
+            cur = (case.workspace.clone(), case.out.clone())
+            if ref is None:
+                ref = cur
+            else:
+                assert torch.equal(cur[0], ref[0]) and torch.equal(cur[1], ref[1]), (wname, paged)
+
+
 
 
 def test_run_to_run_bitwise_deterministic():
