@@ -14,6 +14,8 @@ averaged over the K timed steps.  The event overheads cancel and the decode's ke
 back to back, as they would in a model.  A separate pass with ``mla_decode_timed``
 gives per-stage times and the main-loop kernel time for the roofline; its interior events
 add a few microseconds of idle gap per stage, which that pass does not report as step time.
+The main-loop time is that pass's event interval around the main kernel minus the interval
+of an empty event pair recorded the same way (the marker overhead both contain).
 
 Prints ONE JSON line on stdout.  ``value`` is the latent-cache read rate in TB/s:
   sum_b L_b * (d_c + d_rope) * bytes_per_element / t_step.
@@ -34,8 +36,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode attn: latent-KV read TB/s (% HBM peak), query tokens/s over B×L"
 DEFAULT_WORKLOAD = "mla_bf16_b32_h128_l4096"
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_main_bf16_counters.json")
-MAIN_SRC = os.path.join(ROOT, "mlra_latent_kv_amd", "csrc", "main_bf16.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "main_loop_counters.json")
+# sources of the main-loop kernels; the counter summary is valid only for these exact texts
+MAIN_SRCS = [os.path.join(ROOT, "mlra_latent_kv_amd", "csrc", f) for f in
+             ("main_bf16.hip", "main_bf16_wide.hip", "tile_bf16.h", "device_common.h")]
 
 
 def log(*a):
@@ -79,7 +83,17 @@ class HipEvents:
 
 
 def source_sha() -> str:
-    return hashlib.sha256(open(MAIN_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in MAIN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main_kernel(w) -> str:
+    """Name of the kernel that runs the split-K main loop for workload w."""
+    if w.dtype != "bf16":
+        return "k_main_f32"
+    return "k_main_bf16_wide" if (w.branches == 1 and w.heads % 128 == 0) else "k_main_bf16"
 
 
 def counters_traffic(workload: str):
@@ -225,10 +239,20 @@ def main():
     torch.cuda.synchronize()
     stage = {name: [ev.ms(e[j], e[j + 1]) for e in staged]
              for j, name in enumerate(["prologue", "main", "combine", "epilogue"])}
-    for e in pairs_fd + pairs_f + staged:
+    # an event pair with nothing between it, recorded the same way (after the same flush):
+    # its interval is the marker overhead that each stage interval above also contains
+    empty = [ev.create(2) for _ in range(K)]
+    for i in range(K):
+        do_flush(i)
+        ev.record(empty[i][0], stream)
+        ev.record(empty[i][1], stream)
+    torch.cuda.synchronize()
+    pair_ms = statistics.mean(ev.ms(e[0], e[1]) for e in empty)
+    for e in pairs_fd + pairs_f + staged + empty:
         ev.destroy(e)
     ms = statistics.mean(total)
-    main_ms = statistics.mean(stage["main"])
+    main_ms_raw = statistics.mean(stage["main"])
+    main_ms = main_ms_raw - pair_ms
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -266,7 +290,7 @@ def main():
         "wall_s_timed_region": round(t_wall, 4),
         "flush_us": round(1e3 * statistics.mean(t_f), 2),
         "roofline": {
-            "kernel": "k_main_bf16" if w.dtype == "bf16" else "k_main_f32",
+            "kernel": main_kernel(w),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -275,6 +299,8 @@ def main():
             "algorithmic_bytes": int(cache_bytes),
             "traffic": counters_traffic(w.name),
             "main_us": round(main_ms * 1e3, 2),
+            "main_us_event_pair": round(main_ms_raw * 1e3, 2),
+            "event_pair_overhead_us": round(pair_ms * 1e3, 2),
         },
         "cpu_baseline": None,
     }
