@@ -40,10 +40,7 @@ constexpr int kThreads = 256;                        // 4 waves
 constexpr int kPPitch = kTT + 8;                     // bf16 probability row pitch
 constexpr int kBufs = 2;                             // tile ring depth per workgroup
 
-// LDS that waves write while tile loads are in flight is kept in front of the tile ring, with
-// a gap: placed right after the ring, a rare stale read of the exchanged per-head values was
-// observed on gfx950 while direct-to-LDS loads into the ring were outstanding (repeat-run
-// determinism tests guard this).
+// Exchange buffers first, then the tile ring on a 256-byte boundary.
 template <int NB>
 struct Smem {
   bf16 p[NB == 1 ? kHG * kPPitch : 8];        // MLA: probabilities [h][t]
@@ -181,11 +178,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
       // D layout: lane (head 16*hb + l16, group g16), item e -> token 16*tb + 4*g16 + e
       const int h = 16 * hb + l16;
       const int tq = 16 * tb + 4 * g16;
-      if (valid < kTT) {
+      // Masked without a branch: a uniform branch around the masking put the first read of
+      // the last MFMA's result right behind it on the taken path, without the wait states
+      // that read needs (the compiler pads straight-line code, not that path), so the max
+      // could pick up the accumulator before the last K-step landed.
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (tq + e >= valid) acc[e] = -INFINITY;
-      }
+      for (int e = 0; e < 4; ++e) acc[e] = tq + e < valid ? acc[e] : -INFINITY;
       float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
       mx = max_xor32(max_xor16(mx));
       if (g16 == 0) sm.mx[tb * kHG + h] = mx;
@@ -228,11 +226,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
               lds_read16(buf + rope_chunk(l32, 2 * j + kg)), qb[8 + j], acc, 0, 0, 0);
       }
       // D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4
-      if (valid < kTT) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (8 * (i >> 2) + 4 * kg + (i & 3) >= valid) acc[i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        acc[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? acc[i] : -INFINITY;  // no branch
       float mx = acc[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);

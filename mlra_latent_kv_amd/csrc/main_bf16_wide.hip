@@ -50,8 +50,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   // One LDS object holds both regions.  (Kept as a single struct: with separate arrays the
   // compiler's wait analysis stops telling the tile reads apart from the loads in flight
   // and waits for all of them before the first read of every tile.)
-  // (The query region sits in front of the ring: LDS that sits right behind the ring has
-  // shown rare stale reads on gfx950 while direct-to-LDS loads into the ring were in flight.)
   struct Smem {
     // query K-steps kQRegSteps..17 (columns 384..575), chunk-major: the 16-byte chunk of
     // K-step kQRegSteps + t, k-group g, head h at ((4t + g) * 128 + h) * 16, so 16
@@ -112,15 +110,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   // K-step j covers q_cat columns 32j..32j+31, the lane's 8 at 32j + 8*g16.  K-steps below
   // kQRegSteps in registers, the rest in qlds (this wave's 16 heads are written and read by
   // this wave only).
+  // On the latent K-steps (0..15) lanes of odd k-groups hold their 8 columns as [4..7, 0..3],
+  // the order in which they read the tile (see the score reads below); the contraction
+  // order inside a K-step is free as long as both operands use the same one.
+  const bool swap_half = g16 & 1;
+  auto q_perm = [&](bf16x8 v, int j) -> bf16x8 {
+    return (j < 16 && swap_half) ? __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3) : v;
+  };
   bf16x8 qb[kQRegSteps];
   const uint32_t qr_off = (g16 * kHeadsWG + 16 * w + l16) * 16;  // + 8 KiB per LDS K-step
   {
     const bf16* qrow = qcat + ((size_t)b * H + h0 + l16) * kRow + 8 * g16;
 #pragma unroll
-    for (int j = 0; j < kQRegSteps; ++j) qb[j] = *(const bf16x8*)(qrow + 32 * j);
+    for (int j = 0; j < kQRegSteps; ++j) qb[j] = q_perm(*(const bf16x8*)(qrow + 32 * j), j);
 #pragma unroll
     for (int t = 0; t < kQLdsSteps; ++t)
-      *(bf16x8*)(qlds + qr_off + 8192 * t) = *(const bf16x8*)(qrow + 32 * (kQRegSteps + t));
+      *(bf16x8*)(qlds + qr_off + 8192 * t) =
+          q_perm(*(const bf16x8*)(qrow + 32 * (kQRegSteps + t)), kQRegSteps + t);
   }
   // Tile 0 lands together with the query.  Draining the counter here also tells the
   // compiler's wait analysis that the query registers are complete, so no wait on them
@@ -131,10 +137,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
 
   // Score reads (A = tile, M = tokens): token 16*tb + l16, chunk 4j + g16.  The swizzle
   // permutes within aligned 16-chunk groups and repeats every 16 rows, so j = 4u + j'
-  // adds 256u bytes and tb adds 16 KiB.
+  // adds 256u bytes and tb adds 16 KiB.  Latent chunks are read as two 8-byte halves, odd
+  // k-groups taking the upper half first, so that the two 16-lane groups of each 32-lane
+  // half touch different halves of the same chunk slots (conflict-free; a 16-byte read of
+  // this pattern conflicts two ways).
   uint32_t qk_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) qk_off[j] = lat_chunk<Sw16>(l16, 4 * j + g16);
+  for (int j = 0; j < 4; ++j) qk_off[j] = lat_chunk<Sw16>(l16, 4 * j + g16) + (swap_half ? 8 : 0);
   uint32_t rp_off[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) rp_off[j] = rope_chunk(l16, 4 * j + g16);  // tb adds 2 KiB
@@ -185,7 +194,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     // ---- S^T[t][h] for tokens 16*tb.. (M) and the wave's 16 heads (N).  Tile operands
     // are read kQkAhead K-steps ahead of their MFMAs.
     auto a_tile = [&](int j, int tb) -> bf16x8 {
-      return j < 16 ? lds_read16_at(qa[j & 3] + 256 * (j >> 2) + 16384 * tb)
+      // the other half's address: one XOR per read (o is a multiple of 256), formed here
+      // rather than kept in four more registers
+      const uint32_t o = 256 * (j >> 2) + 16384 * tb;
+      return j < 16 ? b64_pair_at(qa[j & 3] + o, opaque(qa[j & 3] ^ 8u) + o)
                     : lds_read16_at(ra[j - 16] + 2048 * tb);
     };
     constexpr int kQkAhead = 1;

@@ -139,6 +139,18 @@ __device__ __forceinline__ bf16x8 lds_read16_at(uint32_t a) {
 __device__ __forceinline__ s16x4 lds_read_tr_at(const lds_char* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
+__device__ __forceinline__ s16x4 lds_read8_at(const lds_char* __restrict__ p) {
+  return *(const __attribute__((address_space(3))) s16x4*)p;
+}
+// 16 bytes of one chunk as two 8-byte reads, first half at a, second at b.  gfx950 serves
+// an 8-byte read in two LDS cycles without conflicts whenever every 32-lane half of the
+// wave covers 256 distinct bytes (mod 256); a 16-byte read of the score-step pattern (16
+// rows x 4 chunk columns per wave) takes eight cycles, twice the conflict-free four.
+__device__ __forceinline__ bf16x8 b64_pair_at(uint32_t a, uint32_t b) {
+  const s16x4 x = lds_read8_at((const lds_char*)(uintptr_t)a);
+  const s16x4 y = lds_read8_at((const lds_char*)(uintptr_t)b);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 __device__ __forceinline__ bf16x8 tr_pair_at(uint32_t lo, uint32_t hi) {
   const s16x4 a = lds_read_tr_at((const lds_char*)(uintptr_t)lo);
   const s16x4 b = lds_read_tr_at((const lds_char*)(uintptr_t)hi);

@@ -171,9 +171,9 @@ def test_paged_and_contiguous_bitwise_equal():
 ])
 def test_repeat_runs_bitwise_identical(wname, lens, splits):
     """Every main loop is deterministic: 300 back-to-back runs of one case produce the same
-    partials and outputs, bit for bit, paged and contiguous.  (A layout with per-tile exchange
-    data right behind the tile ring once gave a run in a few hundred a stale exchanged value
-    while tile loads were in flight; this catches any such race.)"""
+    partials and outputs, bit for bit, paged and contiguous.  (An MFMA result read too early
+    on one side of a branch once let the running max depend on timing, which changed the
+    rounding in a run in a few hundred; any such race shows up here.)"""
     import torch
     from mlra_latent_kv_amd import harness as H
     w = I.WORKLOADS[wname]
