@@ -33,13 +33,20 @@ def _flags():
     return ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Sources whose MFMAs keep the compiler's default accumulation-register (AGPR) form: the
+# 128-head main loop holds its 256-register output there for the whole loop.
+AGPR_FORM_SOURCES = {"main_bf16_wide.hip"}
+
+
 def _hip_flags(src: str = ""):
     # packed-fp32 instruction selection is disabled for all device code
-    return ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-            "-Xclang", "-packed-fp32-ops",
-            # keep MFMA accumulators in VGPRs: the softmax may rescale them every tile,
-            # and VALU cannot operate on AGPRs (each rescale would copy them out and back)
-            "-mllvm", "-amdgpu-mfma-vgpr-form"]
+    flags = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+             "-Xclang", "-packed-fp32-ops"]
+    if os.path.basename(src) not in AGPR_FORM_SOURCES:
+        # keep MFMA accumulators in VGPRs: the softmax may rescale them every tile, and
+        # VALU cannot operate on AGPRs (each rescale would copy them out and back)
+        flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return flags
 
 
 def _compile(src: str) -> str:

@@ -3,22 +3,25 @@
 //
 // Same contraction as the 32-head kernel (yololab MLA page, section 矩陣吸收: every head
 // scores the one cached latent row plus its rotary key, and the latent row is also the
-// value), organised so that each cached tile crosses HBM -> LDS once for 128 heads:
+// value), organised so that each cached tile crosses HBM -> LDS once for 128 heads and
+// every LDS byte read feeds as many MFMA operations as the register file allows:
 //
-//  * one workgroup of 8 waves per CU handles (sequence b, split s, heads 128q..128q+127);
-//    wave w owns 16 heads outright: their scores, softmax state and the full 512-column
-//    latent output O^T (32 accumulator blocks of 16 columns x 16 heads, 128 VGPRs).  No
-//    per-tile exchange between waves; two waves share each SIMD to hide each other's
-//    latencies.
+//  * one workgroup of 4 waves per CU handles (sequence b, split s, heads 128q..128q+127);
+//    wave w owns 32 heads outright: their scores, softmax state and the full 512-column
+//    latent output O^T (16 accumulator blocks of 32 columns x 32 heads, 256 registers,
+//    which one wave per SIMD can hold in the accumulation registers).  The absorbed query's
+//    first 384 columns stay in registers, the rest (latent 384..511 and the rotary part) in
+//    LDS.  No per-tile exchange between waves.
+//  * MFMA 32x32x16 throughout: a 1 KiB operand read from LDS feeds 32K multiply-adds, twice
+//    what the 16x16x32 shape gets from the same read, so LDS traffic per tile is half that of
+//    a 16-heads-per-wave layout.
 //  * tiles of 32 tokens stream through a ring of 3 LDS buffers by direct-to-LDS loads, so
 //    two tiles are in flight while one is consumed; the barrier per tile only recycles the
-//    buffer the waves finished with.  The rest of LDS holds the query's last 192 columns;
-//    the first 384 stay in registers.  (The register file is the binding budget: O alone
-//    is half of it.)
-//  * scores S^T[t][h] = tile . q_cat^T with MFMA 16x16x32 (two 16-token blocks, 18 K-steps);
-//    the probabilities go register-direct into the value product O^T += V^T P^T (token
-//    order inside the K-step permuted to match the score layout; value operand read with
-//    ds_read_b64_tr_b16 from the token-major tile).
+//    buffer the waves finished with.
+//  * scores S^T[t][h] = tile . q_cat^T (two accumulation chains over 36 K-steps of 16
+//    columns); the probabilities go register-direct into the value product
+//    O^T += V^T P^T (token order inside a K-step permuted to match the score layout; value
+//    operand read with ds_read_b64_tr_b16 from the token-major tile).
 //  * the running max of a head is raised (and O rescaled) only when a tile's max exceeds it
 //    by more than kLazyTau (log2 units); otherwise the tile's weights are taken against the
 //    stale max and stay below 2^kLazyTau, far inside fp32 / bf16 range.  m, l and O always
@@ -32,14 +35,94 @@ namespace {
 
 using namespace tile;
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kHeadsWG = 128;          // heads per workgroup, 16 per wave
+constexpr int kHeadsWG = 128;          // heads per workgroup, 32 per wave
 constexpr int kRing = 3;               // tile buffers
 constexpr int kAhead = kRing - 1;      // tiles in flight ahead of the one being consumed
 constexpr float kLazyTau = 8.0f;       // log2 headroom before the running max is raised
-constexpr int kQRegSteps = 12;         // query K-steps (32 columns each) held in registers
-constexpr int kQLdsSteps = 18 - kQRegSteps;  // the rest (latent 384..511 + rotary) in LDS
+constexpr int kQSteps = kRow / 16;     // 36 K-steps of 16 columns: 32 latent, 4 rotary
+constexpr int kQRegSteps = 24;         // query K-steps held in registers; the rest in LDS
+constexpr int kQLdsSteps = kQSteps - kQRegSteps;
+constexpr int kIssues = issues_per_wave<kWaves>(true);  // tile loads per wave per tile
+
+// Score MFMAs in VGPR form.  This file is built with MFMAs in their accumulation-register
+// form (the default), so that O, the only other MFMA result, lives in the 256 accumulation
+// registers for the whole loop; the score accumulators sit next to the softmax in VGPRs
+// through these asm forms.  The compiler pads inline asm with no wait states: the first step
+// takes a literal zero accumulator (no VALU write ahead of it), and the caller waits before
+// the first VALU read of the result (checked on the generated code by the codegen tests).
+__device__ __forceinline__ void mfma_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// o *= a for one output block, in place in the accumulation registers.  (A VALU multiply in
+// C++ makes the register allocator give O a VGPR home and copy all of it around the loop.)
+// The caller keeps the last MFMA that wrote o well ahead of this block, and the next MFMA
+// reading o well behind it.
+__device__ __forceinline__ void scale_acc(f32x16& o, float a) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = o[i];
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %16, %0\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %0, %16\n\t"
+      "v_accvgpr_read_b32 %16, %1\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %1, %16\n\t"
+      "v_accvgpr_read_b32 %16, %2\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %2, %16\n\t"
+      "v_accvgpr_read_b32 %16, %3\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %3, %16\n\t"
+      "v_accvgpr_read_b32 %16, %4\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %4, %16\n\t"
+      "v_accvgpr_read_b32 %16, %5\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %5, %16\n\t"
+      "v_accvgpr_read_b32 %16, %6\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %6, %16\n\t"
+      "v_accvgpr_read_b32 %16, %7\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %7, %16\n\t"
+      "v_accvgpr_read_b32 %16, %8\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %8, %16\n\t"
+      "v_accvgpr_read_b32 %16, %9\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %9, %16\n\t"
+      "v_accvgpr_read_b32 %16, %10\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %10, %16\n\t"
+      "v_accvgpr_read_b32 %16, %11\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %11, %16\n\t"
+      "v_accvgpr_read_b32 %16, %12\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %12, %16\n\t"
+      "v_accvgpr_read_b32 %16, %13\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %13, %16\n\t"
+      "v_accvgpr_read_b32 %16, %14\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %14, %16\n\t"
+      "v_accvgpr_read_b32 %16, %15\n\t"
+      "v_mul_f32_e32 %16, %17, %16\n\t"
+      "v_accvgpr_write_b32 %15, %16\n\t"
+      : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]), "+a"(x[6]), "+a"(x[7]), "+a"(x[8]), "+a"(x[9]), "+a"(x[10]), "+a"(x[11]), "+a"(x[12]), "+a"(x[13]), "+a"(x[14]), "+a"(x[15]),
+        "=&v"(t)
+      : "v"(a));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = x[i];
+}
 
 __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
@@ -47,14 +130,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, bf16* __restrict__ part_o, float* __restrict__ part_ml, int H,
     int S, int chunk, int n_hq, int units) {
-  // One LDS object holds both regions.  (Kept as a single struct: with separate arrays the
-  // compiler's wait analysis stops telling the tile reads apart from the loads in flight
-  // and waits for all of them before the first read of every tile.)
+  // One LDS object.  (Kept as a single struct: with separate arrays the compiler's wait
+  // analysis stops telling the tile reads apart from the loads in flight and waits for all
+  // of them before the first read of every tile.)
   struct Smem {
-    // query K-steps kQRegSteps..17 (columns 384..575), chunk-major: the 16-byte chunk of
-    // K-step kQRegSteps + t, k-group g, head h at ((4t + g) * 128 + h) * 16, so 16
-    // consecutive heads read 256 consecutive bytes
-    char qlds[kQLdsSteps * 4 * kHeadsWG * 16];
+    // query K-steps kQRegSteps.. chunk-major: the 16-byte chunk of K-step kQRegSteps + t,
+    // k-half g, head h at ((2t + g) * 128 + h) * 16, so a wave's 32 heads read 512
+    // consecutive bytes per k-half
+    char qlds[kQLdsSteps * 2 * kHeadsWG * 16];
     char ring[kRing][kBufBytes];
   };
   __shared__ __align__(16) Smem sm;  // 156 KiB
@@ -73,8 +156,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   if (unit >= units) return;
   const int b = unit / S, s = unit % S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15, g16 = lane >> 4;
-  const int h0 = hq * kHeadsWG + 16 * w;  // this wave's heads
+  const int l32 = lane & 31, kg = lane >> 5;
+  const int h0 = hq * kHeadsWG + 32 * w;  // this wave's heads
   const int L = seqlens[b];
   const int t_begin = s * chunk;
   const int t_end = min(L, t_begin + chunk);
@@ -102,31 +185,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       lb = latent + (int64_t)b * lat_seq + (int64_t)t0 * lat_tok;
       rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
     }
-    issue_tile<Sw16, kWaves>(ring[k % kRing], w, lane, lb, rb, min(kTT, t_end - t0), lat_row_b,
+    issue_tile<Sw32, kWaves>(ring[k % kRing], w, lane, lb, rb, min(kTT, t_end - t0), lat_row_b,
                              rope_row_b);
   };
 
-  // Absorbed query as the B operand of 16x16x32 (N = heads): lane (head l16, k-group g16),
-  // K-step j covers q_cat columns 32j..32j+31, the lane's 8 at 32j + 8*g16.  K-steps below
-  // kQRegSteps in registers, the rest in qlds (this wave's 16 heads are written and read by
+  // Absorbed query as the B operand of 32x32x16 (N = heads): lane (head l32, k-half kg),
+  // K-step j covers q_cat columns 16j..16j+15, the lane's 8 at 16j + 8*kg.  K-steps below
+  // kQRegSteps in registers, the rest in qlds (this wave's 32 heads are written and read by
   // this wave only).
-  // On the latent K-steps (0..15) lanes of odd k-groups hold their 8 columns as [4..7, 0..3],
-  // the order in which they read the tile (see the score reads below); the contraction
-  // order inside a K-step is free as long as both operands use the same one.
-  const bool swap_half = g16 & 1;
-  auto q_perm = [&](bf16x8 v, int j) -> bf16x8 {
-    return (j < 16 && swap_half) ? __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3) : v;
-  };
   bf16x8 qb[kQRegSteps];
-  const uint32_t qr_off = (g16 * kHeadsWG + 16 * w + l16) * 16;  // + 8 KiB per LDS K-step
+  const uint32_t qr_off = (kg * kHeadsWG + 32 * w + l32) * 16;  // + 4 KiB per LDS K-step
   {
-    const bf16* qrow = qcat + ((size_t)b * H + h0 + l16) * kRow + 8 * g16;
+    const bf16* qrow = qcat + ((size_t)b * H + h0 + l32) * kRow + 8 * kg;
 #pragma unroll
-    for (int j = 0; j < kQRegSteps; ++j) qb[j] = q_perm(*(const bf16x8*)(qrow + 32 * j), j);
+    for (int j = 0; j < kQRegSteps; ++j) qb[j] = *(const bf16x8*)(qrow + 16 * j);
 #pragma unroll
     for (int t = 0; t < kQLdsSteps; ++t)
-      *(bf16x8*)(qlds + qr_off + 8192 * t) =
-          q_perm(*(const bf16x8*)(qrow + 32 * (kQRegSteps + t)), kQRegSteps + t);
+      *(bf16x8*)(qlds + qr_off + 4096 * t) = *(const bf16x8*)(qrow + 16 * (kQRegSteps + t));
   }
   // Tile 0 lands together with the query.  Draining the counter here also tells the
   // compiler's wait analysis that the query registers are complete, so no wait on them
@@ -135,31 +210,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   wait_vmcnt<0>();
   for (int k = 1; k < kAhead && k < n_tiles; ++k) issue(k, page_of(k));
 
-  // Score reads (A = tile, M = tokens): token 16*tb + l16, chunk 4j + g16.  The swizzle
-  // permutes within aligned 16-chunk groups and repeats every 16 rows, so j = 4u + j'
-  // adds 256u bytes and tb adds 16 KiB.  Latent chunks are read as two 8-byte halves, odd
-  // k-groups taking the upper half first, so that the two 16-lane groups of each 32-lane
-  // half touch different halves of the same chunk slots (conflict-free; a 16-byte read of
-  // this pattern conflicts two ways).
-  uint32_t qk_off[4];
+  // Score reads (A = tile, M = tokens): token l32, chunk 2j + kg for latent K-step j.  The
+  // swizzle permutes within aligned 16-chunk groups and repeats every 16 rows, so
+  // j = 8u + j' adds 256u bytes.  Rotary K-step 32 + j: rotary chunk 2j + kg.
+  //
+  // The read addresses of the current tile's buffer are carried from tile to tile (advanced
+  // by one buffer, or wrapped to the first, at the end of each tile) and kept opaque to the
+  // optimiser: every read is one of them plus a constant in the instruction's offset field,
+  // and no separate per-lane offsets stay live next to them.
+  const uint32_t buf0 = lds_addr(ring[0]);
+  uint32_t qa[8], ra[4], pa[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) qk_off[j] = lat_chunk<Sw16>(l16, 4 * j + g16) + (swap_half ? 8 : 0);
-  uint32_t rp_off[2];
+  for (int j = 0; j < 8; ++j) qa[j] = buf0 + lat_chunk<Sw32>(l32, 2 * j + kg);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) rp_off[j] = rope_chunk(l16, 4 * j + g16);  // tb adds 2 KiB
-  // Value reads (A = V^T, M = 16 latent columns, K = 32 tokens): 16-lane group g16 holds
-  // tokens 4*g16..+3 and 16 + 4*g16..+3; source lane l16 addresses token row 4*g16 + l16/4
-  // (+16 for the second read), columns 4*(l16 & 3)..+3 of the block.  Column block
-  // cb = 8u + c adds 256u bytes; the second read adds 16 KiB.
-  uint32_t pv_off[8];
+  for (int j = 0; j < 4; ++j) ra[j] = buf0 + rope_chunk(l32, 2 * j + kg);
+  // Value reads (A = V^T, M = 32 latent columns, K = 16 tokens): 16-lane group G holds
+  // columns 16*(G&1)..+15 of the block and tokens 4*kg..+3 (first read) and 8 + 4*kg..+3
+  // (second read) of the K-step; source lane li addresses token row 4*kg + li/4 (+8),
+  // columns 16*(G&1) + 4*(li&3)..+3.  Column block cb = 4u + c adds 256u bytes; the second
+  // K-step adds 16 KiB.
+  const int G = lane >> 4, li = lane & 15;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) pv_off[c] = lat_piece<Sw16>(4 * g16 + (l16 >> 2), 16 * c + 4 * (l16 & 3));
+  for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      pa[rr][c] = buf0 + lat_piece<Sw32>(4 * kg + (li >> 2) + 8 * rr,
+                                         32 * c + 16 * (G & 1) + 4 * (li & 3));
+  const uint32_t qla = lds_addr(qlds) + qr_off;
 
-  const bool rope_wave = w < 4;
-  float m_ref = -INFINITY, l_run = 0.0f;  // per head l16 (the four k-groups hold the same)
-  f32x4 O[32];
+  float m_ref = -INFINITY, l_run = 0.0f;  // per head l32 (both k-halves hold the same)
+  f32x16 O[16];
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb) O[cb] = f32x4{};
+  for (int cb = 0; cb < 16; ++cb) O[cb] = f32x16{};
 
   for (int k = 0; k < n_tiles; ++k) {
     // page of the tile issued below, read before the barrier (whose lgkmcnt(0) covers it) so
@@ -169,131 +251,135 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     // this wave's loads of tile k are done once only the younger tiles' loads remain
     static_assert(kAhead == 2, "wait counts below assume two tiles in flight");
     if (k + 1 < n_tiles) {
-      if (rope_wave) wait_vmcnt<issues_per_wave<kWaves>(true)>();
-      else wait_vmcnt<issues_per_wave<kWaves>(false)>();
+      wait_vmcnt<kIssues>();
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();  // tile k landed for every wave; the buffer of tile k-1 is free
     if (k + kAhead < n_tiles) issue(k + kAhead, pg);
     __builtin_amdgcn_sched_barrier(0);  // no operand reads hoisted above the loads' issue
-    // Per-tile LDS base addresses, opaque to the optimiser: every read below is one of these
-    // plus a constant that goes into the instruction's offset field (otherwise the compiler
-    // hoists one register per base + constant, or picks a base above the reads and pays an
-    // add per read for the negative difference).
-    const uint32_t bufa = lds_addr(ring[k % kRing]);
-    uint32_t qa[4], ra[2], pa[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qa[j] = opaque(bufa + qk_off[j]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) ra[j] = opaque(bufa + rp_off[j]);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) pa[c] = opaque(bufa + pv_off[c]);
-    const uint32_t qla = opaque(lds_addr(qlds) + qr_off);
 
-    // ---- S^T[t][h] for tokens 16*tb.. (M) and the wave's 16 heads (N).  Tile operands
-    // are read kQkAhead K-steps ahead of their MFMAs.
-    auto a_tile = [&](int j, int tb) -> bf16x8 {
-      // the other half's address: one XOR per read (o is a multiple of 256), formed here
-      // rather than kept in four more registers
-      const uint32_t o = 256 * (j >> 2) + 16384 * tb;
-      return j < 16 ? b64_pair_at(qa[j & 3] + o, opaque(qa[j & 3] ^ 8u) + o)
-                    : lds_read16_at(ra[j - 16] + 2048 * tb);
+    // ---- S^T[t][h] for the tile's 32 tokens (M) and the wave's 32 heads (N)
+    auto a_tile = [&](int j) -> bf16x8 {
+      return j < 32 ? lds_read16_at(qa[j & 7] + 256 * (j >> 3)) : lds_read16_at(ra[j - 32]);
     };
-    constexpr int kQkAhead = 1;
-    // two accumulators per token block (even / odd K-steps): a dependent chain of 16x16x32
-    // MFMAs issues at about a third of the unit's rate
-    f32x4 acc2[2][2] = {};
-    bf16x8 aq[kQkAhead + 1][2];
+    // tile operands, and the query operands kept in LDS, are read kQkAhead K-steps ahead
+    constexpr int kQkAhead = 4;
+    constexpr int kQq = kQkAhead + 1;
+    f32x16 acc2[2];
+    bf16x8 aq[kQq], qq[kQq];
+    auto prefetch = [&](int j) {
+      aq[j % kQq] = a_tile(j);
+      if (j >= kQRegSteps) qq[j % kQq] = lds_read16_at(qla + 4096 * (j - kQRegSteps));
+    };
 #pragma unroll
-    for (int j = 0; j < kQkAhead; ++j) {
-      aq[j][0] = a_tile(j, 0);
-      aq[j][1] = a_tile(j, 1);
-    }
+    for (int j = 0; j < kQkAhead; ++j) prefetch(j);
 #pragma unroll
-    for (int j = 0; j < 18; ++j) {
-      if (j + kQkAhead < 18) {
-        aq[(j + kQkAhead) % (kQkAhead + 1)][0] = a_tile(j + kQkAhead, 0);
-        aq[(j + kQkAhead) % (kQkAhead + 1)][1] = a_tile(j + kQkAhead, 1);
-      }
-      const bf16x8 qv = j < kQRegSteps ? qb[j < kQRegSteps ? j : 0]
-                                       : lds_read16_at(qla + 8192 * (j - kQRegSteps));
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        acc2[tb][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[j % (kQkAhead + 1)][tb], qv,
-                                                                  acc2[tb][j & 1], 0, 0, 0);
-      // keep the written order: the scheduler would otherwise hoist more reads than the
-      // register budget holds (O takes half of it) and spill
+    for (int j = 0; j < kQSteps; ++j) {
+      if (j + kQkAhead < kQSteps) prefetch(j + kQkAhead);
+      const bf16x8 qv = j < kQRegSteps ? qb[j < kQRegSteps ? j : 0] : qq[j % kQq];
+      if (j < 2)
+        mfma_qk_first(acc2[j & 1], aq[j % kQq], qv);
+      else
+        mfma_qk(acc2[j & 1], aq[j % kQq], qv);
+      // keep the written order: the scheduler would otherwise hoist more operand reads than
+      // the VGPRs left next to the query hold
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // value operands of the first column blocks, read while the softmax runs
-    auto v_tile = [&](int cb) -> bf16x8 {
-      const uint32_t a = pa[cb & 7] + 256 * (cb >> 3);
-      return tr_pair_at(a, a + 16384);
+    // value operands of the first column blocks, read while the softmax runs; operand i is
+    // K-step i / 16 of column block i % 16
+    auto v_tile = [&](int i) -> bf16x8 {
+      const int cb = i & 15, ks = i >> 4;
+      const uint32_t o = 256 * (cb >> 2) + 16384 * ks;
+      return tr_pair_at(pa[0][cb & 3] + o, pa[1][cb & 3] + o);
     };
     constexpr int kPvAhead = 4;
     bf16x8 vq[kPvAhead + 1];
 #pragma unroll
-    for (int cb = 0; cb < kPvAhead; ++cb) vq[cb] = v_tile(cb);
+    for (int i = 0; i < kPvAhead; ++i) vq[i] = v_tile(i);
 
-    f32x4 acc[2] = {acc2[0][0] + acc2[0][1], acc2[1][0] + acc2[1][1]};
+    // 32x32x16 result -> VALU read: 12 wait states (fenced so that no read of acc2 is
+    // scheduled above the padding)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 11");
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc = acc2[0] + acc2[1];
 
-    // ---- softmax.  D layout: lane (head l16, group g16), item e of block tb ->
-    // token 16*tb + 4*g16 + e
+    // ---- softmax.  D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4.
+    // Masked without a branch (a uniform branch here would put the first read of the last
+    // MFMA's result right behind it on one path).
     const int valid = min(kTT, t_end - t_begin - kTT * k);
-    if (valid < kTT) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+    for (int i = 0; i < 16; ++i) acc[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? acc[i] : -INFINITY;
+    float mx = acc[0];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (16 * tb + 4 * g16 + e >= valid) acc[tb][e] = -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
-                     fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
-    mx = max_xor32(max_xor16(mx));  // every tile holds a valid token: mx finite
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
+    mx = max_xor32(mx);  // every tile holds a valid token: mx finite
     if (k == 0) {
       m_ref = mx;  // O and l are still zero
     } else if (__ballot(mx > m_ref + kLazyTau) != 0) {
       const float m_new = fmaxf(m_ref, mx);
       const float a = exp2f(m_ref - m_new);
+      // one block at a time through VGPRs (O lives in the accumulation registers)
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) O[cb] *= a;
+      for (int cb = 0; cb < 16; ++cb) {
+        scale_acc(O[cb], a);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       l_run *= a;
       m_ref = m_new;
     }
-    // B operand of the value product (K = 32 tokens, N = heads): lane (head l16, k-group
-    // g16) item e <-> token 4*g16 + e (e < 4) or 16 + 4*g16 + e - 4: the lane's own scores.
-    bf16x8 pb;
+    // B operand of the value product (K = 16 tokens per step, N = heads): lane (head l32,
+    // k-half kg) item e of step ks <-> token 16*ks + 8*(e/4) + 4*kg + e%4: the lane's own
+    // scores, items 8*ks + e.  The second step's weights are computed in the shadow of the
+    // first step's MFMAs.
+    bf16x8 pb[2];
     float psum = 0.0f;
+    auto weight = [&](int i) {
+      const bf16 p = (bf16)__builtin_amdgcn_exp2f(acc[i] - m_ref);
+      pb[i >> 3][i & 7] = p;
+      psum += (float)p;  // normalise with the rounded weights the MFMA uses
+    };
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16 p = (bf16)__builtin_amdgcn_exp2f(acc[tb][e] - m_ref);
-        pb[4 * tb + e] = p;
-        psum += (float)p;  // normalise with the rounded weights the MFMA uses
-      }
-    l_run += sum_xor32(sum_xor16(psum));
+    for (int i = 0; i < 8; ++i) weight(i);
 
-    // ---- O^T[d][h] += V^T P^T over the 32 column blocks, operands kPvAhead blocks ahead
+    // ---- O^T[d][h] += V^T P^T, K-step-major over the 16 column blocks, operands kPvAhead
+    // reads ahead
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      if (cb + kPvAhead < 32) vq[(cb + kPvAhead) % (kPvAhead + 1)] = v_tile(cb + kPvAhead);
-      O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vq[cb % (kPvAhead + 1)], pb, O[cb], 0, 0, 0);
+    for (int i = 0; i < 32; ++i) {
+      if (i + kPvAhead < 32) vq[(i + kPvAhead) % (kPvAhead + 1)] = v_tile(i + kPvAhead);
+      O[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i % (kPvAhead + 1)], pb[i >> 4],
+                                                         O[i & 15], 0, 0, 0);
+      if (i < 8) weight(8 + i);
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_run += sum_xor32(psum);
+
+    // next tile's buffer
+    const int32_t step = k % kRing == kRing - 1 ? -(kRing - 1) * kBufBytes : kBufBytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qa[j] = opaque(qa[j] + step);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = opaque(ra[j] + step);
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pa[rr][c] = opaque(pa[rr][c] + step);
   }
 
-  // ---- partial outputs.  O[cb] item e: column 16cb + 4*g16 + e of head h0 + l16
-  bf16* po = part_o + (((size_t)b * S + s) * H + h0 + l16) * kDC + 4 * g16;
+  // ---- partial outputs.  O[cb] item e: column 32cb + 8*(e/4) + 4*kg + e%4 of head h0 + l32
+  bf16* po = part_o + (((size_t)b * S + s) * H + h0 + l32) * kDC + 4 * kg;
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb)
-    *(bf16x4*)(po + 16 * cb) =
-        bf16x4{(bf16)O[cb][0], (bf16)O[cb][1], (bf16)O[cb][2], (bf16)O[cb][3]};
-  if (g16 == 0) {
-    ml[(size_t)(h0 + l16) * 2 + 0] = m_ref;
-    ml[(size_t)(h0 + l16) * 2 + 1] = l_run;
+  for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(bf16x4*)(po + 32 * cb + 8 * q) =
+          bf16x4{(bf16)O[cb][4 * q], (bf16)O[cb][4 * q + 1], (bf16)O[cb][4 * q + 2],
+                 (bf16)O[cb][4 * q + 3]};
+  if (kg == 0) {
+    ml[(size_t)(h0 + l32) * 2 + 0] = m_ref;
+    ml[(size_t)(h0 + l32) * 2 + 1] = l_run;
   }
 }
 

@@ -69,7 +69,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint3
 // (32/NW)w.. (one 1 KiB row per instruction) and, if w < 4, rotary rows 8w..8w+7 (one
 // instruction).
 template <int NW>
-__device__ __forceinline__ constexpr int issues_per_wave(bool rope_wave) {
+__host__ __device__ constexpr int issues_per_wave(bool rope_wave) {
   return kTT / NW + (rope_wave ? 1 : 0);
 }
 

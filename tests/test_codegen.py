@@ -89,11 +89,13 @@ _MFMA_WAIT = {"16x16": 8, "32x32": 12}
 
 
 def _regs(spec):
-    m = re.match(r"[va]\[(\d+):(\d+)\]", spec)
+    """Registers an operand names, as (file, index) pairs: VGPRs and accumulation registers
+    are separate files."""
+    m = re.match(r"([va])\[(\d+):(\d+)\]", spec)
     if m:
-        return set(range(int(m.group(1)), int(m.group(2)) + 1))
-    m = re.match(r"[va](\d+)$", spec)
-    return {int(m.group(1))} if m else set()
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", spec)
+    return {(m.group(1), int(m.group(2)))} if m else set()
 
 
 def _parse(asm: str):
