@@ -92,7 +92,7 @@ typedef struct mla_params {
  * Bytes of device workspace mla_decode / mlra_decode need for *p (written to *bytes, a
  * host pointer).  Depends only on the fields of *p.  The workspace holds the absorbed
  * queries, the per-split partial results (running max, running sum and latent-space
- * output of each sequence split) and the merged latent-space output.
+ * output of each sequence split) and, for fp32, the merged latent-space output.
  */
 mla_status mla_workspace_size(const mla_params* p, size_t* bytes);
 
@@ -154,9 +154,10 @@ mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_ro
  * Tracing variants: identical to mla_decode / mlra_decode, and additionally record five
  * caller-created HIP events (hipEvent_t values passed as void*) on `stream` at the stage
  * boundaries: events[0] before the prologue, events[1] before the split-K main loop,
- * events[2] before the combine, events[3] before the epilogue, events[4] after it.  With
- * events == NULL they behave exactly like the plain entry points.  A failed hipEventRecord
- * returns MLA_ERR_HIP.
+ * events[2] before the combine, events[3] before the epilogue, events[4] after it.  For
+ * bf16 the combine and the epilogue run as one kernel between events[2] and events[3], and
+ * events[4] follows events[3] directly.  With events == NULL they behave exactly like the
+ * plain entry points.  A failed hipEventRecord returns MLA_ERR_HIP.
  */
 mla_status mla_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
                             const void* latent, const void* rope, const int32_t* seqlens,

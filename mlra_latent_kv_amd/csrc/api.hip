@@ -5,6 +5,7 @@
 //   main loop -> per (sequence, split, head group) partial (m, l, O) over the latent cache
 //   combine   -> log-sum-exp merge of the splits into the latent-space output
 //   epilogue  -> out = out_scale * W_UV^T o_lat (summed over MLRA branches)
+// (on the bf16 path combine and epilogue are one kernel)
 // Nothing is allocated, nothing synchronises, no state is kept between calls.
 #include "launch.h"
 #include "plan.h"
@@ -64,9 +65,15 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
         : plan.wide ? launch_main_bf16_wide(plan, a, s)
                     : launch_main_bf16(plan, a, s);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = launch_combine(plan, a, s);
-  if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = bf ? launch_epilogue_bf16(plan, a, s) : launch_epilogue(plan, a, s);
+  if (bf) {
+    // one kernel: the merged latent output stays on chip (events 3 and 4 coincide)
+    if (e == hipSuccess) e = launch_combine_epilogue_bf16(plan, a, s);
+    if (e == hipSuccess) e = mark(3);
+  } else {
+    if (e == hipSuccess) e = launch_combine(plan, a, s);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = launch_epilogue(plan, a, s);
+  }
   if (e == hipSuccess) e = mark(4);
   return to_status(e);
 }

@@ -11,6 +11,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "tile_bf16.h"
 
 namespace mla {
 namespace {
@@ -94,53 +95,6 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
   }
 }
 
-// ----------------------------------------------------------------------------- epilogue
-constexpr int kECols = 32;           // output columns per workgroup (one wave)
-constexpr int kEPitch = kECols + 8;  // LDS pitch of the W_UV block (bf16)
-constexpr int kDc = 512;             // total latent width on the bf16 path (MLA 512, MLRA 4x128)
-
-__global__ __launch_bounds__(64) void k_epilogue_bf16(const bf16* __restrict__ olat,
-                                                      const bf16* __restrict__ w_uv,
-                                                      bf16* __restrict__ out, int B, int H, int NB,
-                                                      int dcb, float out_scale) {
-  constexpr int dv = 128;
-  __shared__ __align__(16) bf16 sW[kDc * kEPitch];
-  const int h = blockIdx.x, b0 = blockIdx.y * kRows, v0 = blockIdx.z * kECols;
-  const int lane = threadIdx.x;
-  const int bl = lane & 31, kg = lane >> 5;
-  // rows past B are clamped to B-1: their products are computed but never stored
-  const int b = min(b0 + bl, B - 1);
-  // batch-row operand for the whole contraction first, so its latency overlaps the weights
-  bf16x8 a[kDc / 16];
-  const bf16* arow = olat + ((size_t)b * H + h) * kDc + 8 * kg;
-#pragma unroll
-  for (int s = 0; s < kDc / 16; ++s) a[s] = *(const bf16x8*)(arow + 16 * s);
-  // W_UV rows d (branch d/dcb), columns v0..v0+31: row d = 16*i + lane/4, chunk lane%4
-  const int q = lane & 3;
-#pragma unroll
-  for (int i0 = 0; i0 < kDc / 16; i0 += 8) {
-    u32x4 t[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int d = 16 * (i0 + i) + (lane >> 2);
-      t[i] = *(const u32x4*)(w_uv + (((size_t)(d / dcb) * H + h) * dcb + d % dcb) * dv + v0 + 8 * q);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4*)(sW + (16 * (i0 + i) + (lane >> 2)) * kEPitch + 8 * q) = t[i];
-  }
-  __syncthreads();
-  f32x16 acc = {};
-  const bf16* tsrc = sW + tr_src_row(lane) * kEPitch + tr_src_col(lane);
-#pragma unroll
-  for (int s = 0; s < kDc / 16; ++s)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], tr8(tsrc + 16 * s * kEPitch, kEPitch), acc, 0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int bb = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
-    if (bb < B) out[((size_t)bb * H + h) * dv + v0 + (lane & 31)] = (bf16)(acc[i] * out_scale);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
@@ -153,10 +107,232 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(p.H, (p.B + kRows - 1) / kRows, p.dv / kECols);
-  hipLaunchKernelGGL(k_epilogue_bf16, grid, dim3(64), 0, s, (const bf16*)a.olat,
-                     (const bf16*)a.w_uv, (bf16*)a.out, p.B, p.H, p.NB, p.dcb, a.out_scale);
+// ------------------------------------------------------------------- combine + epilogue
+// out[b, h, :] = out_scale * sum_c o_lat[b, h, c] * W_UV[c / dcb][h][c % dcb][:], where
+// o_lat[b, h, c] = sum_s w_s O_s[b, h, c] is the log-sum-exp merge of the split partials
+// (w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s' with M the largest split max of the head's
+// branch) -- the split combine and the W_UV projection of the absorbed form (yololab MLA
+// page, section 矩陣吸收), with the MLRA-4 branch sum carried by the contraction over all
+// 512 latent columns ("[ICLR 2025] MLRA…", section 2.2).
+//
+// One workgroup (4 waves) per (head h, rows b0..b0+R-1), R in {4, 8, 16}:
+//  1. the W_UV rows of the head go to LDS by direct-to-LDS loads (one contiguous 32 KiB block
+//     per wave: wave w owns latent columns 128w..128w+127, exactly branch w for MLRA-4);
+//  2. meanwhile the split statistics (M, 1/L) of every (row, branch), then the weighted sum
+//     of the split partials, with all 256 threads sharing the (row, 16-byte chunk) work, into
+//     an LDS copy of the merged latent output (bf16, the MFMA operand);
+//  3. each wave multiplies its 128 latent columns by its W_UV rows (MFMA 32x32x16, rows of
+//     the workgroup as M, padded to 32), and the four partial products (K split four ways)
+//     are summed through LDS.
+namespace {
+
+constexpr int kCeDv = 128;                 // d_v of the bf16 path
+constexpr int kCeRowB = kCeDv * 2;         // bytes per W_UV row in LDS
+constexpr int kCeRedPitch = kCeDv + 4;     // fp32 pitch of the cross-wave sum
+constexpr int kCeMaxRows = 16;
+
+// physical 16-byte chunk of logical chunk c in W_UV row r: the transposed operand reads
+// cover 4 consecutive rows x 4 consecutive chunks, which this XOR spreads over all 16
+// chunk slots of a 256-byte bank line
+__device__ __forceinline__ int ce_sw(int r, int c) { return c ^ (4 * (r & 3)); }
+
+// R = 4 * NC rows per workgroup; each thread merges NC chunks of one row, 32 chunk loads in
+// flight
+template <int NC>
+__global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
+    const bf16* __restrict__ part_o, const float* __restrict__ part_ml,
+    const bf16* __restrict__ w_uv, bf16* __restrict__ out, int B, int H, int S, int NB,
+    int dcb, float out_scale) {
+  constexpr int R = 4 * NC;
+  struct Smem {
+    char wuv[4][128 * kCeRowB];       // per wave: its 128 W_UV rows, chunk-swizzled
+    char olat[kCeMaxRows][1024];      // merged latent rows, chunk c at c ^ (row % 16)
+    float stat_m[kCeMaxRows][4], stat_inv[kCeMaxRows][4];
+  };
+  __shared__ __align__(16) Smem sm;  // 145 KiB; wuv is reused for the cross-wave sum
+  const int h = blockIdx.x % H, b0 = (blockIdx.x / H) * R;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a uniform value: the W_UV buffer descriptor depends on it, and a descriptor
+  // the compiler cannot prove uniform turns every load into a per-lane loop
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // ---- 1. W_UV rows c0..c0+127 of head h: instruction i brings rows 4i..4i+3; lane l lands
+  // at physical chunk l%16 of row 4i + l/16 and so fetches logical chunk ce_sw(row, l%16)
+  {
+    const int c0 = 128 * w, br = c0 / dcb;
+    const bf16* wbase = w_uv + ((size_t)(br * H + h) * dcb + (c0 % dcb)) * kCeDv;
+    const __amdgpu_buffer_rsrc_t rs = tile::rsrc(wbase, 128 * kCeRowB);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      tile::dma16(rs, sm.wuv[w] + 1024 * i, r * kCeRowB + 16 * ce_sw(r, lane & 15));
+    }
+  }
+
+  // ---- 2a. split statistics of (row, branch): M = largest split max, 1/L.  A group of P
+  // consecutive lanes per (row, branch) takes splits s = q, q + P, ... and the group merges
+  // its (M, L) pairs with lane shuffles.
+  const size_t ml_s = (size_t)NB * H * 2;  // part_ml stride of one split
+  {
+    const int P = 256 / (R * NB);  // 4..64, a power of two
+    const int pair = tid / P, q = tid % P;
+    const int r = pair / NB, br = pair % NB, b = b0 + r;
+    float M = -INFINITY, L = 0.0f;
+    if (b < B) {
+      const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + h * 2;
+      for (int s = q; s < S; s += P) {
+        const float m = ml[s * ml_s];
+        if (m != -INFINITY) {
+          const float mn = fmaxf(M, m);
+          L = L * exp2f(M - mn) + ml[s * ml_s + 1] * exp2f(m - mn);
+          M = mn;
+        }
+      }
+    }
+    for (int o = 1; o < P; o <<= 1) {
+      const float Mo = __shfl_xor(M, o, 64), Lo = __shfl_xor(L, o, 64);
+      const float mn = fmaxf(M, Mo);
+      if (mn != -INFINITY) {
+        L = L * exp2f(M - mn) + Lo * exp2f(Mo - mn);
+        M = mn;
+      }
+    }
+    if (q == 0) {
+      sm.stat_m[r][br] = M;
+      sm.stat_inv[r][br] = L > 0.0f ? 1.0f / L : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // ---- 2b. merged latent: thread t takes R/4 consecutive chunks of one row (within one
+  // branch: R/4 <= 4 chunks, a branch is 16 or 64 chunks), several splits' loads in flight
+  {
+    const int first = tid * NC, r = first / 64, c = first % 64;
+    const int b = b0 + r, br = (8 * c) / dcb;
+    f32x4 acc[NC][2];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) acc[i][0] = acc[i][1] = f32x4{};
+    if (b < B) {
+      const float M = sm.stat_m[r][br], inv = sm.stat_inv[r][br];
+      const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + h * 2;
+      const size_t po_s = (size_t)H * 512;
+      const bf16* src = part_o + (((size_t)b * S) * H + h) * 512 + 8 * c;
+      constexpr int kU = 32 / NC;  // splits in flight
+      for (int s0 = 0; s0 < S; s0 += kU) {
+        // the batch's split maxima first, then every chunk load: no load waits on another.
+        // Splits with no tokens (and the batch's tail past S, read at split S-1) get weight 0,
+        // and their never-written partials are replaced by zeros after the load.
+        float wt[kU];
+        bf16x8 v[kU][NC];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) wt[u] = s0 + u < S ? ml[(s0 + u) * ml_s] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          wt[u] = wt[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(wt[u] - M) * inv;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int s = min(s0 + u, S - 1);
+#pragma unroll
+          for (int i = 0; i < NC; ++i) v[u][i] = *(const bf16x8*)(src + s * po_s + 8 * i);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int i = 0; i < NC; ++i)
+            if (wt[u] == 0.0f) v[u][i] = bf16x8{};
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            acc[i][0] += wt[u] * f32x4{(float)v[u][i][0], (float)v[u][i][1], (float)v[u][i][2],
+                                       (float)v[u][i][3]};
+            acc[i][1] += wt[u] * f32x4{(float)v[u][i][4], (float)v[u][i][5], (float)v[u][i][6],
+                                       (float)v[u][i][7]};
+          }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+        *(bf16x8*)(sm.olat[r] + 16 * ((c + i) ^ (r & 15))) =
+            bf16x8{(bf16)acc[i][0][0], (bf16)acc[i][0][1], (bf16)acc[i][0][2], (bf16)acc[i][0][3],
+                   (bf16)acc[i][1][0], (bf16)acc[i][1][1], (bf16)acc[i][1][2], (bf16)acc[i][1][3]};
+  }
+  tile::wait_vmcnt<0>();  // this wave's W_UV rows have landed
+  __syncthreads();        // every merged latent row is in LDS
+
+  // ---- 3. out[row][v] partial over this wave's 128 latent columns.  A operand: lane (row
+  // l32, k-half g) holds columns 128w + 16j + 8g..+7 (chunk 16w + 2j + g); rows >= R are zero.
+  // B operand (K = latent rows, N = v): lane (v, k-half g) holds W_UV rows 16j + 8g..+7 of
+  // column v, two transposed reads: source lane li of 16-lane group G addresses row
+  // 16j + 8*(G>>1) + li/4 (+4), columns 16*(G&1) + 4*(li&3)..+3 of the block.
+  bf16x8 a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int cc = 16 * w + 2 * j + g;
+    a[j] = l32 < R ? *(const bf16x8*)(sm.olat[l32 & (kCeMaxRows - 1)] + 16 * (cc ^ (l32 & 15)))
+                   : bf16x8{};
+  }
+  const int G = lane >> 4, li = lane & 15;
+  f32x16 o[4];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb) {
+    o[vb] = f32x16{};
+    const int col = 32 * vb + 16 * (G & 1) + 4 * (li & 3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r1 = 16 * j + 8 * (G >> 1) + (li >> 2), r2 = r1 + 4;
+      const char* base = sm.wuv[w];
+      const bf16x8 bv = tile::tr_pair(base + r1 * kCeRowB + 16 * ce_sw(r1, col >> 3) + 2 * (col & 7),
+                                      base + r2 * kCeRowB + 16 * ce_sw(r2, col >> 3) + 2 * (col & 7));
+      o[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], bv, o[vb], 0, 0, 0);
+    }
+  }
+
+  // ---- sum of the four K quarters.  D layout: lane (v, half g), item e -> row
+  // 8*(e/4) + 4*g + e%4, column 32*vb + v.  Only rows < R are stored.
+  __syncthreads();  // every wave is done with its W_UV rows
+  float* red = reinterpret_cast<float*>(sm.wuv);
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = 8 * (e >> 2) + 4 * g + (e & 3);
+      if (row < kCeMaxRows) red[(w * kCeMaxRows + row) * kCeRedPitch + 32 * vb + l32] = o[vb][e];
+    }
+  __syncthreads();
+  // thread t: row t / 16, columns 8*(t % 16)..+7
+  const int row = tid >> 4, v0 = 8 * (tid & 15);
+  if (row < R && b0 + row < B) {
+    bf16x8 res;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) sum += red[(ww * kCeMaxRows + row) * kCeRedPitch + v0 + i];
+      res[i] = (bf16)(sum * out_scale);
+    }
+    *(bf16x8*)(out + ((size_t)(b0 + row) * H + h) * kCeDv + v0) = res;
+  }
+}
+
+}  // namespace
+
+// rows per workgroup: 16, or 8 where 16 would leave CUs without a workgroup, or 4 for
+// batches of at most 4 (no thread idles on absent rows)
+int combine_epilogue_rows(int B, int H) {
+  if (B <= 4) return 4;
+  return (long)H * ((B + 15) / 16) >= 256 ? 16 : 8;
+}
+
+hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
+  const int R = combine_epilogue_rows(p.B, p.H);
+  const unsigned blocks = (unsigned)(p.H * ((p.B + R - 1) / R));
+  auto kern = R == 16 ? k_combine_epilogue_bf16<4>
+              : R == 8 ? k_combine_epilogue_bf16<2> : k_combine_epilogue_bf16<1>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, (const bf16*)a.part_o, a.part_ml,
+                     (const bf16*)a.w_uv, (bf16*)a.out, p.B, p.H, p.splits, p.NB, p.dcb,
+                     a.out_scale);
   return hipGetLastError();
 }
 

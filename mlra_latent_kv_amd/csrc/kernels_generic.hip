@@ -159,83 +159,8 @@ __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ part_o,
   }
 }
 
-// bf16 path (d_c = 512, branch width 128 or 512): one workgroup per (sequence, head).  The
-// split weights of the head's branches go to LDS once; wave w then takes splits w, w+4, ...
-// with each lane covering 8 consecutive latent columns (16-byte loads, four splits in
-// flight), and the four waves' sums meet in LDS.
-constexpr int kCombDc = 512;
-
-__global__ __launch_bounds__(256) void k_combine_bf16(const bf16* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml,
-                                                      bf16* __restrict__ olat, int H, int S,
-                                                      int NB, int dcb) {
-  __shared__ float wts[4 * kMaxSplits];  // [branch][split]
-  __shared__ f32x4 red[3][2][64];        // sums of waves 1..3, [half of the 8 columns][lane]
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const size_t sstride = (size_t)NB * H * 2;
-  for (int br = wv; br < NB; br += 4) {
-    const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + h * 2;
-    float M = -INFINITY;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[s * sstride]);
-    M = wave_max(M);
-    float den = 0.0f;
-    if (M != -INFINITY)
-      for (int s = lane; s < S; s += 64) {
-        const float m = ml[s * sstride];
-        if (m != -INFINITY) den = fmaf(exp2f(m - M), ml[s * sstride + 1], den);
-      }
-    den = wave_sum(den);
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    for (int s = lane; s < S; s += 64) {
-      const float m = ml[s * sstride];
-      wts[br * S + s] = (m == -INFINITY) ? 0.0f : exp2f(m - M) * inv;
-    }
-  }
-  __syncthreads();
-  const float* w = wts + (8 * lane / dcb) * S;
-  const bf16* src = part_o + (((size_t)b * S) * H + h) * kCombDc + 8 * lane;
-  const size_t pstride = (size_t)H * kCombDc;
-  f32x4 acc0 = {}, acc1 = {};
-  for (int s0 = wv; s0 < S; s0 += 16) {
-    bf16x8 v[4];
-    float wt[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + 4 * u;
-      wt[u] = s < S ? w[s] : 0.0f;
-      // splits with no tokens have weight 0 and never-written partials: skip the load
-      v[u] = wt[u] != 0.0f ? *(const bf16x8*)(src + (size_t)s * pstride) : bf16x8{};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc0 += wt[u] * f32x4{(float)v[u][0], (float)v[u][1], (float)v[u][2], (float)v[u][3]};
-      acc1 += wt[u] * f32x4{(float)v[u][4], (float)v[u][5], (float)v[u][6], (float)v[u][7]};
-    }
-  }
-  if (wv > 0) {
-    red[wv - 1][0][lane] = acc0;
-    red[wv - 1][1][lane] = acc1;
-  }
-  __syncthreads();
-  if (wv == 0) {
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      acc0 += red[k][0][lane];
-      acc1 += red[k][1][lane];
-    }
-    *(bf16x8*)(olat + ((size_t)b * H + h) * kCombDc + 8 * lane) =
-        bf16x8{(bf16)acc0[0], (bf16)acc0[1], (bf16)acc0[2], (bf16)acc0[3],
-               (bf16)acc1[0], (bf16)acc1[1], (bf16)acc1[2], (bf16)acc1[3]};
-  }
-}
-
+// fp32 path (the bf16 path merges the splits inside launch_combine_epilogue_bf16)
 hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  if (p.dtype == MLA_BF16) {
-    hipLaunchKernelGGL(k_combine_bf16, dim3(p.B * p.H), dim3(256), 0, s, (const bf16*)a.part_o,
-                       a.part_ml, (bf16*)a.olat, p.H, p.splits, p.NB, p.dcb);
-    return hipGetLastError();
-  }
   const dim3 grid((p.H + kCombHeads - 1) / kCombHeads, p.B, (p.dc + kCombCols - 1) / kCombCols);
   const int max_br = kCombCols / p.dcb + 2;
   const size_t lds = (size_t)kCombHeads * std::min(p.NB, max_br) * p.splits * sizeof(float);

@@ -25,7 +25,7 @@ struct DecodeArgs {
   void* part_o;     // [B][S][H][d_c], unnormalised partial latent outputs: bf16 on the bf16
                     // path (the same rounding as the latent output), fp32 otherwise
   float* part_ml;   // [B][S][NB][H][2]  (running max in log2 units, running sum)
-  void* olat;       // [B][H][d_c], bf16 on the bf16 path (MFMA operand), fp32 otherwise
+  void* olat;       // [B][H][d_c] fp32, fp32 path only (the bf16 path keeps it on chip)
 };
 
 struct RopeFreq;
@@ -37,9 +37,11 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
 hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_main_bf16_wide(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_main_f32(const Plan& p, const DecodeArgs& a, hipStream_t s);
-hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s);        // fp32 path
 hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s);       // fp32 path
-hipError_t launch_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
+// bf16 path: split combine and W_UV epilogue in one kernel (the latent output stays on chip)
+hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
+int combine_epilogue_rows(int B, int H);
 hipError_t launch_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
                               int d_rope, float theta, int dtype, hipStream_t s);
 

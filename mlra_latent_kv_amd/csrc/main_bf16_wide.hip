@@ -256,8 +256,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       wait_vmcnt<0>();
     }
     lds_barrier();  // tile k landed for every wave; the buffer of tile k-1 is free
-    if (k + kAhead < n_tiles) issue(k + kAhead, pg);
-    __builtin_amdgcn_sched_barrier(0);  // no operand reads hoisted above the loads' issue
 
     // ---- S^T[t][h] for the tile's 32 tokens (M) and the wave's 32 heads (N)
     auto a_tile = [&](int j) -> bf16x8 {
@@ -265,6 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     };
     // tile operands, and the query operands kept in LDS, are read kQkAhead K-steps ahead
     constexpr int kQkAhead = 4;
+    constexpr int kIssueStep = 2;
     constexpr int kQq = kQkAhead + 1;
     f32x16 acc2[2];
     bf16x8 aq[kQq], qq[kQq];
@@ -276,6 +275,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     for (int j = 0; j < kQkAhead; ++j) prefetch(j);
 #pragma unroll
     for (int j = 0; j < kQSteps; ++j) {
+      // the next tile's loads go out behind the first score MFMAs, whose execution covers
+      // the address set-up
+      if (j == kIssueStep && k + kAhead < n_tiles) issue(k + kAhead, pg);
       if (j + kQkAhead < kQSteps) prefetch(j + kQkAhead);
       const bf16x8 qv = j < kQRegSteps ? qb[j < kQRegSteps ? j : 0] : qq[j % kQq];
       if (j < 2)
@@ -307,11 +309,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     f32x16 acc = acc2[0] + acc2[1];
 
     // ---- softmax.  D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4.
-    // Masked without a branch (a uniform branch here would put the first read of the last
-    // MFMA's result right behind it on one path).
     const int valid = min(kTT, t_end - t_begin - kTT * k);
+    if (valid < kTT) {  // last tile of a ragged split; the padding above covers both paths
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? acc[i] : -INFINITY;
+      for (int i = 0; i < 16; ++i)
+        acc[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? acc[i] : -INFINITY;
+    }
     float mx = acc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);

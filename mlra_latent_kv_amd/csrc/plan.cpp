@@ -104,8 +104,8 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
   off = align_up(off + (size_t)q.B * q.splits * q.H * q.dc * (q.dtype == MLA_BF16 ? 2 : 4));
   q.off_part_ml = off;
   off = align_up(off + (size_t)q.B * q.splits * q.NB * q.H * 2 * sizeof(float));
-  q.off_olat = off;
-  off = align_up(off + (size_t)q.B * q.H * q.dc * (q.dtype == MLA_BF16 ? 2 : 4));
+  q.off_olat = off;  // merged latent output: fp32 path only (bf16 keeps it on chip)
+  if (q.dtype != MLA_BF16) off = align_up(off + (size_t)q.B * q.H * q.dc * 4);
   q.bytes = off;
   *plan = q;
   return MLA_OK;

@@ -143,7 +143,7 @@ def test_workspace_layout(lib, wname):
     Bn, H, dc = 3, w.heads, w.d_c
     # partial outputs are stored in the element type (bf16 on the bf16 path), (m, l) in fp32
     exp = al(Bn * H * w.row * w.elem_bytes) + al(Bn * S * H * dc * w.elem_bytes) + \
-        al(Bn * S * w.branches * H * 2 * 4) + al(Bn * H * dc * w.elem_bytes)
+        al(Bn * S * w.branches * H * 2 * 4) + (al(Bn * H * dc * 4) if w.elem_bytes == 4 else 0)
     assert B.workspace_size(p) == exp
 
 
