@@ -79,8 +79,9 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
     if (bb < B) qcat[((size_t)bb * H + h) * row + col] = (bf16)(acc[i] * qscale);
   }
   // rotary part of the query, rotated at position L_b - 1 (angles in fp64)
-  if (cb == 0) {
-    for (int t = tid; t < kRows * (dr / 2); t += 256) {
+  // (spread over the column-block workgroups of the head: one (row, pair) per thread)
+  {
+    for (int t = cb * 256 + tid; t < kRows * (dr / 2); t += 256 * (int)gridDim.z) {
       const int bb = b0 + t / (dr / 2), k = t % (dr / 2);
       if (bb >= B) continue;
       const int L = seqlens[bb];
@@ -170,26 +171,71 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     }
   }
 
+  // ---- 2. merged latent.  Thread t takes NC consecutive chunks of one row (within one
+  // branch: NC <= 4 chunks, a branch is 16 or 64 chunks).  The first batch of its split
+  // maxima and chunk loads goes out before the split statistics are formed, so that the two
+  // latencies overlap.  Splits with no tokens (and a batch's tail past S, read at split S-1)
+  // get weight 0, and their never-written partials are replaced by zeros after the load.
+  const size_t ml_s = (size_t)NB * H * 2;  // part_ml stride of one split
+  const size_t po_s = (size_t)H * 512;     // part_o stride of one split
+  const int first = tid * NC, mr = first / 64, mc = first % 64;
+  const int mb = b0 + mr, mbr = (8 * mc) / dcb;
+  const bool mlive = mb < B;
+  // every load is unconditional, at an in-bounds row and split (a predicated load leaves the
+  // compiler's wait analysis with a full drain at the join); masked values are replaced
+  // after the load
+  const int mbl = min(mb, B - 1);
+  const float* mml = part_ml + (((size_t)mbl * S) * NB + mbr) * H * 2 + h * 2;
+  const bf16* msrc = part_o + (((size_t)mbl * S) * H + h) * 512 + 8 * mc;
+  constexpr int kU = 32 / NC;  // splits in flight
+  float mv[kU];
+  bf16x8 v[kU][NC];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mv[u] = mml[min(s0 + u, S - 1) * ml_s];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int sidx = min(s0 + u, S - 1);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) v[u][i] = *(const bf16x8*)(msrc + sidx * po_s + 8 * i);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (!mlive || s0 + u >= S) mv[u] = -INFINITY;
+  };
   // ---- 2a. split statistics of (row, branch): M = largest split max, 1/L.  A group of P
   // consecutive lanes per (row, branch) takes splits s = q, q + P, ... and the group merges
-  // its (M, L) pairs with lane shuffles.
-  const size_t ml_s = (size_t)NB * H * 2;  // part_ml stride of one split
+  // its (M, L) pairs with lane shuffles.  The first four (m, l) pairs of a lane are loaded
+  // ahead of the merge batch (loads complete in order).
   {
     const int P = 256 / (R * NB);  // 4..64, a power of two
     const int pair = tid / P, q = tid % P;
     const int r = pair / NB, br = pair % NB, b = b0 + r;
-    float M = -INFINITY, L = 0.0f;
-    if (b < B) {
-      const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + h * 2;
-      for (int s = q; s < S; s += P) {
-        const float m = ml[s * ml_s];
-        if (m != -INFINITY) {
-          const float mn = fmaxf(M, m);
-          L = L * exp2f(M - mn) + ml[s * ml_s + 1] * exp2f(m - mn);
-          M = mn;
-        }
-      }
+    const float* ml = part_ml + (((size_t)min(b, B - 1) * S) * NB + br) * H * 2 + h * 2;
+    constexpr int kPre = 4;
+    float pm[kPre], pl[kPre];
+#pragma unroll
+    for (int it = 0; it < kPre; ++it) {
+      const int sidx = min(q + it * P, S - 1);
+      pm[it] = ml[sidx * ml_s];
+      pl[it] = ml[sidx * ml_s + 1];
     }
+    load_batch(0);
+#pragma unroll
+    for (int it = 0; it < kPre; ++it)
+      if (b >= B || q + it * P >= S) pm[it] = -INFINITY;
+    float M = -INFINITY, L = 0.0f;
+    auto merge = [&](float m, float l) {
+      if (m != -INFINITY) {
+        const float mn = fmaxf(M, m);
+        L = L * exp2f(M - mn) + l * exp2f(m - mn);
+        M = mn;
+      }
+    };
+#pragma unroll
+    for (int it = 0; it < kPre; ++it) merge(pm[it], pl[it]);
+    if (b < B)
+      for (int sidx = q + kPre * P; sidx < S; sidx += P) merge(ml[sidx * ml_s], ml[sidx * ml_s + 1]);
     for (int o = 1; o < P; o <<= 1) {
       const float Mo = __shfl_xor(M, o, 64), Lo = __shfl_xor(L, o, 64);
       const float mn = fmaxf(M, Mo);
@@ -205,58 +251,38 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   }
   __syncthreads();
 
-  // ---- 2b. merged latent: thread t takes R/4 consecutive chunks of one row (within one
-  // branch: R/4 <= 4 chunks, a branch is 16 or 64 chunks), several splits' loads in flight
+  // ---- 2b. weighted sum of the splits, batch by batch
   {
-    const int first = tid * NC, r = first / 64, c = first % 64;
-    const int b = b0 + r, br = (8 * c) / dcb;
     f32x4 acc[NC][2];
 #pragma unroll
     for (int i = 0; i < NC; ++i) acc[i][0] = acc[i][1] = f32x4{};
-    if (b < B) {
-      const float M = sm.stat_m[r][br], inv = sm.stat_inv[r][br];
-      const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + h * 2;
-      const size_t po_s = (size_t)H * 512;
-      const bf16* src = part_o + (((size_t)b * S) * H + h) * 512 + 8 * c;
-      constexpr int kU = 32 / NC;  // splits in flight
-      for (int s0 = 0; s0 < S; s0 += kU) {
-        // the batch's split maxima first, then every chunk load: no load waits on another.
-        // Splits with no tokens (and the batch's tail past S, read at split S-1) get weight 0,
-        // and their never-written partials are replaced by zeros after the load.
-        float wt[kU];
-        bf16x8 v[kU][NC];
+    const float M = sm.stat_m[mr][mbr], inv = sm.stat_inv[mr][mbr];
+    for (int s0 = 0; s0 < S; s0 += kU) {
+      if (s0 > 0) load_batch(s0);
+      float wt[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) wt[u] = s0 + u < S ? ml[(s0 + u) * ml_s] : -INFINITY;
+      for (int u = 0; u < kU; ++u)
+        wt[u] = mv[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv[u] - M) * inv;
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-          wt[u] = wt[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(wt[u] - M) * inv;
+      for (int u = 0; u < kU; ++u)
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int s = min(s0 + u, S - 1);
+        for (int i = 0; i < NC; ++i)
+          if (wt[u] == 0.0f) v[u][i] = bf16x8{};
 #pragma unroll
-          for (int i = 0; i < NC; ++i) v[u][i] = *(const bf16x8*)(src + s * po_s + 8 * i);
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          acc[i][0] += wt[u] * f32x4{(float)v[u][i][0], (float)v[u][i][1], (float)v[u][i][2],
+                                     (float)v[u][i][3]};
+          acc[i][1] += wt[u] * f32x4{(float)v[u][i][4], (float)v[u][i][5], (float)v[u][i][6],
+                                     (float)v[u][i][7]};
         }
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-#pragma unroll
-          for (int i = 0; i < NC; ++i)
-            if (wt[u] == 0.0f) v[u][i] = bf16x8{};
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-#pragma unroll
-          for (int i = 0; i < NC; ++i) {
-            acc[i][0] += wt[u] * f32x4{(float)v[u][i][0], (float)v[u][i][1], (float)v[u][i][2],
-                                       (float)v[u][i][3]};
-            acc[i][1] += wt[u] * f32x4{(float)v[u][i][4], (float)v[u][i][5], (float)v[u][i][6],
-                                       (float)v[u][i][7]};
-          }
-      }
     }
 #pragma unroll
     for (int i = 0; i < NC; ++i)
-        *(bf16x8*)(sm.olat[r] + 16 * ((c + i) ^ (r & 15))) =
-            bf16x8{(bf16)acc[i][0][0], (bf16)acc[i][0][1], (bf16)acc[i][0][2], (bf16)acc[i][0][3],
-                   (bf16)acc[i][1][0], (bf16)acc[i][1][1], (bf16)acc[i][1][2], (bf16)acc[i][1][3]};
+      *(bf16x8*)(sm.olat[mr] + 16 * ((mc + i) ^ (mr & 15))) =
+          bf16x8{(bf16)acc[i][0][0], (bf16)acc[i][0][1], (bf16)acc[i][0][2], (bf16)acc[i][0][3],
+                 (bf16)acc[i][1][0], (bf16)acc[i][1][1], (bf16)acc[i][1][2], (bf16)acc[i][1][3]};
   }
   tile::wait_vmcnt<0>();  // this wave's W_UV rows have landed
   __syncthreads();        // every merged latent row is in LDS
