@@ -157,6 +157,33 @@ def test_split_count_invariance(wname):
         assert rel_l2(outs[s], outs[1]) < 5e-3
 
 
+# Shapes that drive every variant of the fused split merge + W_UV epilogue: row blocks of 16,
+# 8 and 4 (partial last blocks included), several batches of splits per thread, split
+# statistics with more than four splits per statistics lane, and many empty splits.
+FUSED_CASES = [
+    # MLA, 20 rows -> 16-row blocks (second one partial), 71 splits (> 4 per lane of 16)
+    ("mla_bf16_b32_h128_l4096", [4500, 40, 700, 5, 64, 129, 1, 2100, 999, 333, 77, 18, 300, 250,
+                                 64, 65, 1000, 1, 30, 640], 71),
+    # MLRA-4, 120 rows -> 16-row blocks, 4 lanes per (row, branch), 18 splits
+    ("mlra4_bf16_b32_h32_l8192", [1100] + [37 + (11 * i) % 90 for i in range(119)], 18),
+    # MLA, 4 rows -> 4-row blocks, 41 splits (two batches of 32)
+    ("mla_bf16_paged_b4_h128_l131072", [2600, 64, 1, 2000], 41),
+    # MLRA-4, 3 rows -> 4-row blocks, 8 splits
+    ("mlra4_bf16_b32_h32_l8192", [900, 1, 450], 8),
+]
+
+
+@pytest.mark.parametrize("wname,lens,splits", FUSED_CASES,
+                         ids=[f"{c[0]}-B{len(c[1])}-S{c[2]}" for c in FUSED_CASES])
+def test_fused_merge_shapes(wname, lens, splits):
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=lens, q_gain=I.sharp_q_gain(w))
+    got, case = gpu_out(inp, num_splits=splits)
+    from mlra_latent_kv_amd import binding as B
+    assert B.num_splits(case.params) == splits
+    assert_close(got, oracle_out(inp), "bf16", f"{wname} B={len(lens)} splits={splits}")
+
+
 def test_paged_and_contiguous_bitwise_equal():
     import torch
     w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
