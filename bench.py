@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain copy kernel of this size (counter calibration)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -191,7 +193,6 @@ def main():
     torch.cuda.synchronize()
     lens = np.asarray(inp["seqlens"], np.int64)
     cache_bytes = I.cache_bytes(w, lens)
-    splits = B.num_splits(case.params)
 
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")  # 512 MiB
     ev = HipEvents()
@@ -222,6 +223,7 @@ def main():
         ev.record(pairs_fd[i][1], stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    plan = Hn.read_plan(case)  # the split plan the device made for these lengths
     for i in range(K):
         ev.record(pairs_f[i][0], stream)
         do_flush(i)
@@ -280,7 +282,8 @@ def main():
         "config": {"workload": w.name, "batch": int(len(lens)), "heads": w.heads,
                    "branches": w.branches, "seq_len": int(lens.max()),
                    "context_tokens": int(lens.sum()), "d_latent": w.d_c, "d_rope": w.d_rope,
-                   "paged": bool(inp["paged"]), "splits": splits,
+                   "paged": bool(inp["paged"]), "work_items": plan["items"],
+                   "pages_per_item": plan["pages"],
                    "cache_flush": args.flush},
         "pct_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBPS, 2),
         "query_tokens_per_s": round(len(lens) / (ms * 1e-3), 1),

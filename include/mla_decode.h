@@ -63,8 +63,9 @@ typedef struct mla_params {
   int32_t d_rope;             /* decoupled rotary key dim (even)                           */
   int32_t page_size;          /* 0 = contiguous cache, MLA_PAGE_SIZE = paged cache         */
   int32_t max_pages_per_seq;  /* paged: block_table columns in use, >= ceil(max_seqlen/64) */
-  int32_t max_seqlen;         /* host-side bound on every seqlens[b]; sizes the split plan */
-  int32_t num_splits;         /* sequence splits per sequence; 0 = chosen by the library   */
+  int32_t max_seqlen;         /* host-side bound on every seqlens[b]; sizes the workspace  */
+  int32_t num_splits;         /* 0 = balanced split plan (below); n > 0 = at most n splits
+                                 per sequence, each ceil(ceil(max_seqlen/64)/n) pages      */
   int32_t dtype;              /* mla_dtype of q, caches, weights and out                   */
   int64_t latent_stride_tok;  /* elements between consecutive tokens of the latent cache   */
   int64_t latent_stride_seq;  /* contiguous: elements between sequences; paged: pages      */
@@ -85,18 +86,37 @@ typedef struct mla_params {
  *  - page_size in {0, 64}.
  * Alignment: bf16 latent, rope, q_nope, w_uk and w_uv pointers 16-byte aligned and the
  * cache strides multiples of 8 elements; other pointers aligned to their element size.
- * num_splits (given or chosen) is at most 512.
+ * num_splits is at most 512 and at most ceil(max_seqlen / 64).
+ *
+ * Split plan.  The attention over each sequence is split into work items of whole 64-token
+ * pages (split-K over the sequence) whose partial results are merged afterwards.  The plan is
+ * made on the device from seqlens at the start of every call, so it follows the actual
+ * lengths: with p_b = ceil(seqlens[b] / 64) pages, every sequence is cut into
+ * ceil(p_b / c) items of c pages (the last one ragged; an empty sequence gets none).  With
+ * num_splits = 0, c is the smallest page count for which the batch's items fit the number of
+ * workgroups that fill the GPU once (256 items for bf16 MLA with H % 128 == 0, else 512 /
+ * workgroups per item); when no c does, c = max_b p_b.  With num_splits = n,
+ * c = ceil(ceil(max_seqlen / 64) / n).
+ * After a call has completed on its stream, the workspace starts with that plan (for
+ * inspection; nothing reads it after the call):
+ *   int32 hdr[4] at byte 0: { W = number of items, c, slots, item target (0 when forced) }
+ *   int32 work[slots][4] at byte 16: { b, t_begin, t_end, item } per dispatch slot of the
+ *         main kernels, b = -1 for a slot without an item; items are numbered
+ *         sequence-major, item i of sequence b covering tokens [t_begin, t_end)
+ *   int32 split_off[B + 1] at byte 16 + 16 * slots: items of sequence b are
+ *         split_off[b] .. split_off[b + 1] - 1, split_off[B] = W.
  */
 
 /*
  * Bytes of device workspace mla_decode / mlra_decode need for *p (written to *bytes, a
- * host pointer).  Depends only on the fields of *p.  The workspace holds the absorbed
- * queries, the per-split partial results (running max, running sum and latent-space
- * output of each sequence split) and, for fp32, the merged latent-space output.
+ * host pointer).  Depends only on the fields of *p.  The workspace holds the split plan, the
+ * absorbed queries, the per-item partial results (running max, running sum and latent-space
+ * output of each work item) and, for fp32, the merged latent-space output.
  */
 mla_status mla_workspace_size(const mla_params* p, size_t* bytes);
 
-/* Number of sequence splits the library will use for *p (written to *splits, host). */
+/* Most work items (splits) one sequence can be cut into for *p (written to *splits, host):
+ * n when num_splits = n > 0, else min(ceil(max_seqlen / 64), item target). */
 mla_status mla_num_splits(const mla_params* p, int32_t* splits);
 
 /*
@@ -153,10 +173,10 @@ mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_ro
 /*
  * Tracing variants: identical to mla_decode / mlra_decode, and additionally record five
  * caller-created HIP events (hipEvent_t values passed as void*) on `stream` at the stage
- * boundaries: events[0] before the prologue, events[1] before the split-K main loop,
- * events[2] before the combine, events[3] before the epilogue, events[4] after it.  For
- * bf16 the combine and the epilogue run as one kernel between events[2] and events[3], and
- * events[4] follows events[3] directly.  With events == NULL they behave exactly like the
+ * boundaries: events[0] before the prologue (whose launch also makes the split plan),
+ * events[1] before the split-K main loop, events[2] before the combine, events[3] before the
+ * epilogue, events[4] after it.  For bf16 the combine and the epilogue run as one kernel
+ * between events[2] and events[3], and events[4] follows events[3] directly.  With events == NULL they behave exactly like the
  * plain entry points.  A failed hipEventRecord returns MLA_ERR_HIP.
  */
 mla_status mla_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,

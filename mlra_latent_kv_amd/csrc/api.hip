@@ -1,8 +1,9 @@
 // extern "C" entry points of libmla_decode.so (declared in include/mla_decode.h).
 //
 // mla_decode / mlra_decode validate on the host, then enqueue on the caller's stream:
-//   prologue  -> absorbed query q_cat = [W_UK^T q_nope | RoPE(q_rope, L-1)] * scale*log2(e)
-//   main loop -> per (sequence, split, head group) partial (m, l, O) over the latent cache
+//   prologue  -> absorbed query q_cat = [W_UK^T q_nope | RoPE(q_rope, L-1)] * scale*log2(e),
+//                and (one extra workgroup) the split plan: page-aligned work items per sequence
+//   main loop -> per (work item, head group) partial (m, l, O) over the latent cache
 //   combine   -> log-sum-exp merge of the splits into the latent-space output
 //   epilogue  -> out = out_scale * W_UV^T o_lat (summed over MLRA branches)
 // (on the bf16 path combine and epilogue are one kernel)
@@ -47,6 +48,9 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
   a.out_scale = p->out_scale;
   a.rope_theta = p->rope_theta;
   char* ws = static_cast<char*>(workspace);
+  a.plan = plan_args(plan, seqlens, workspace);
+  a.work = a.plan.work;
+  a.split_off = a.plan.split_off;
   a.qcat = ws + plan.off_qcat;
   a.part_o = ws + plan.off_part_o;
   a.part_ml = reinterpret_cast<float*>(ws + plan.off_part_ml);

@@ -11,6 +11,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "plan_device.h"
 #include "tile_bf16.h"
 
 namespace mla {
@@ -42,10 +43,14 @@ constexpr int kPPitch = kPCols + 8;  // LDS pitch of the W_UK block (bf16)
 __global__ __launch_bounds__(256) void k_prologue_bf16(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
     const int32_t* __restrict__ seqlens, const bf16* __restrict__ w_uk, bf16* __restrict__ qcat,
-    int B, int H, int NB, int dcb, float qscale, RopeFreq rf) {
+    int B, int H, int NB, int dcb, float qscale, RopeFreq rf, PlanArgs plan) {
   constexpr int dn = 128, dr = 64;
   __shared__ __align__(16) bf16 sW[dn * kPPitch];
   const int h = blockIdx.x, b0 = blockIdx.y * kRows, cb = blockIdx.z;
+  if (h == H) {  // the extra column of blocks: block (H, 0, 0) makes the split plan
+    if (b0 == 0 && cb == 0) make_work_plan(plan, sW, (int)sizeof(sW));
+    return;
+  }
   const int dc = NB * dcb, row = dc + dr;
   const int br = (cb * kPCols) / dcb;          // branch of this column block
   const int c0 = (cb * kPCols) % dcb;          // first column inside the branch
@@ -99,12 +104,12 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
 }  // namespace
 
 hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(p.H, (p.B + kRows - 1) / kRows, p.dc / kPCols);
+  const dim3 grid(p.H + 1, (p.B + kRows - 1) / kRows, p.dc / kPCols);
   RopeFreq rf;
   make_rope_freq(p.dr, a.rope_theta, &rf);
   hipLaunchKernelGGL(k_prologue_bf16, grid, dim3(256), 0, s, (const bf16*)a.q_nope,
                      (const bf16*)a.q_rope, a.seqlens, (const bf16*)a.w_uk, (bf16*)a.qcat, p.B,
-                     p.H, p.NB, p.dcb, a.softmax_scale * kLog2e, rf);
+                     p.H, p.NB, p.dcb, a.softmax_scale * kLog2e, rf, a.plan);
   return hipGetLastError();
 }
 
@@ -142,8 +147,8 @@ __device__ __forceinline__ int ce_sw(int r, int c) { return c ^ (4 * (r & 3)); }
 template <int NC>
 __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     const bf16* __restrict__ part_o, const float* __restrict__ part_ml,
-    const bf16* __restrict__ w_uv, bf16* __restrict__ out, int B, int H, int S, int NB,
-    int dcb, float out_scale) {
+    const int32_t* __restrict__ split_off, const bf16* __restrict__ w_uv,
+    bf16* __restrict__ out, int B, int H, int NB, int dcb, float out_scale) {
   constexpr int R = 4 * NC;
   struct Smem {
     char wuv[4][128 * kCeRowB];       // per wave: its 128 W_UV rows, chunk-swizzled
@@ -171,37 +176,46 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     }
   }
 
-  // ---- 2. merged latent.  Thread t takes NC consecutive chunks of one row (within one
-  // branch: NC <= 4 chunks, a branch is 16 or 64 chunks).  The first batch of its split
-  // maxima and chunk loads goes out before the split statistics are formed, so that the two
-  // latencies overlap.  Splits with no tokens (and a batch's tail past S, read at split S-1)
-  // get weight 0, and their never-written partials are replaced by zeros after the load.
-  const size_t ml_s = (size_t)NB * H * 2;  // part_ml stride of one split
-  const size_t po_s = (size_t)H * 512;     // part_o stride of one split
+  // ---- 2. merged latent.  The splits of row b are its work items split_off[b] ..
+  // split_off[b + 1] - 1 (a variable number per row, none for an empty sequence).  Thread t
+  // takes NC consecutive chunks of one row (within one branch: NC <= 4 chunks, a branch is 16
+  // or 64 chunks).  The first batch of its split maxima and chunk loads goes out before the
+  // split statistics are formed, so that the two latencies overlap.  A batch's tail past the
+  // row's last split gets weight 0, and its loads (of an item that exists) are replaced by
+  // zeros.
+  const size_t ml_s = (size_t)NB * H * 2;  // part_ml stride of one work item
+  const size_t po_s = (size_t)H * 512;     // part_o stride of one work item
   const int first = tid * NC, mr = first / 64, mc = first % 64;
   const int mb = b0 + mr, mbr = (8 * mc) / dcb;
-  const bool mlive = mb < B;
-  // every load is unconditional, at an in-bounds row and split (a predicated load leaves the
+  // every load is unconditional, at a written work item (a predicated load leaves the
   // compiler's wait analysis with a full drain at the join); masked values are replaced
   // after the load
   const int mbl = min(mb, B - 1);
-  const float* mml = part_ml + (((size_t)mbl * S) * NB + mbr) * H * 2 + h * 2;
-  const bf16* msrc = part_o + (((size_t)mbl * S) * H + h) * 512 + 8 * mc;
+  const int mu0 = split_off[mbl], mn = mb < B ? split_off[mbl + 1] - mu0 : 0;
+  auto item_of = [](int u0, int n, int s) { return max(u0 + min(s, n - 1), 0); };
+  const float* mml = part_ml + (size_t)mbr * H * 2 + h * 2;
+  const bf16* msrc = part_o + (size_t)h * 512 + 8 * mc;
+  // the longest split list among the workgroup's rows bounds the (uniform) merge loop
+  int n_max = 0;
+  for (int r = 0; r < R; ++r) {
+    const int bb = min(b0 + r, B);
+    n_max = max(n_max, split_off[min(bb + 1, B)] - split_off[bb]);
+  }
   constexpr int kU = 32 / NC;  // splits in flight
   float mv[kU];
   bf16x8 v[kU][NC];
   auto load_batch = [&](int s0) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) mv[u] = mml[min(s0 + u, S - 1) * ml_s];
+    for (int u = 0; u < kU; ++u) mv[u] = mml[item_of(mu0, mn, s0 + u) * ml_s];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int sidx = min(s0 + u, S - 1);
+      const size_t it = item_of(mu0, mn, s0 + u);
 #pragma unroll
-      for (int i = 0; i < NC; ++i) v[u][i] = *(const bf16x8*)(msrc + sidx * po_s + 8 * i);
+      for (int i = 0; i < NC; ++i) v[u][i] = *(const bf16x8*)(msrc + it * po_s + 8 * i);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      if (!mlive || s0 + u >= S) mv[u] = -INFINITY;
+      if (s0 + u >= mn) mv[u] = -INFINITY;
   };
   // ---- 2a. split statistics of (row, branch): M = largest split max, 1/L.  A group of P
   // consecutive lanes per (row, branch) takes splits s = q, q + P, ... and the group merges
@@ -211,19 +225,21 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     const int P = 256 / (R * NB);  // 4..64, a power of two
     const int pair = tid / P, q = tid % P;
     const int r = pair / NB, br = pair % NB, b = b0 + r;
-    const float* ml = part_ml + (((size_t)min(b, B - 1) * S) * NB + br) * H * 2 + h * 2;
+    const int bl = min(b, B - 1);
+    const int u0 = split_off[bl], n = b < B ? split_off[bl + 1] - u0 : 0;
+    const float* ml = part_ml + (size_t)br * H * 2 + h * 2;
     constexpr int kPre = 4;
     float pm[kPre], pl[kPre];
 #pragma unroll
     for (int it = 0; it < kPre; ++it) {
-      const int sidx = min(q + it * P, S - 1);
+      const size_t sidx = item_of(u0, n, q + it * P);
       pm[it] = ml[sidx * ml_s];
       pl[it] = ml[sidx * ml_s + 1];
     }
     load_batch(0);
 #pragma unroll
     for (int it = 0; it < kPre; ++it)
-      if (b >= B || q + it * P >= S) pm[it] = -INFINITY;
+      if (q + it * P >= n) pm[it] = -INFINITY;
     float M = -INFINITY, L = 0.0f;
     auto merge = [&](float m, float l) {
       if (m != -INFINITY) {
@@ -234,8 +250,10 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     };
 #pragma unroll
     for (int it = 0; it < kPre; ++it) merge(pm[it], pl[it]);
-    if (b < B)
-      for (int sidx = q + kPre * P; sidx < S; sidx += P) merge(ml[sidx * ml_s], ml[sidx * ml_s + 1]);
+    for (int s = q + kPre * P; s < n; s += P) {
+      const size_t sidx = (size_t)(u0 + s);
+      merge(ml[sidx * ml_s], ml[sidx * ml_s + 1]);
+    }
     for (int o = 1; o < P; o <<= 1) {
       const float Mo = __shfl_xor(M, o, 64), Lo = __shfl_xor(L, o, 64);
       const float mn = fmaxf(M, Mo);
@@ -257,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
 #pragma unroll
     for (int i = 0; i < NC; ++i) acc[i][0] = acc[i][1] = f32x4{};
     const float M = sm.stat_m[mr][mbr], inv = sm.stat_inv[mr][mbr];
-    for (int s0 = 0; s0 < S; s0 += kU) {
+    for (int s0 = 0; s0 < n_max; s0 += kU) {
       if (s0 > 0) load_batch(s0);
       float wt[kU];
 #pragma unroll
@@ -357,7 +375,7 @@ hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipS
   auto kern = R == 16 ? k_combine_epilogue_bf16<4>
               : R == 8 ? k_combine_epilogue_bf16<2> : k_combine_epilogue_bf16<1>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, (const bf16*)a.part_o, a.part_ml,
-                     (const bf16*)a.w_uv, (bf16*)a.out, p.B, p.H, p.splits, p.NB, p.dcb,
+                     a.split_off, (const bf16*)a.w_uv, (bf16*)a.out, p.B, p.H, p.NB, p.dcb,
                      a.out_scale);
   return hipGetLastError();
 }

@@ -1,6 +1,6 @@
-// fp32 path (prologue, W_UV epilogue, SIMT main loop for small fp32 shapes), the split
-// combine shared by both paths, and the rotary-key rotation.  The bf16 path's prologue and
-// epilogue are in kernels_bf16_aux.hip, its main loop in main_bf16.hip.
+// fp32 path (prologue, split combine, W_UV epilogue, SIMT main loop for small fp32 shapes)
+// and the rotary-key rotation.  The bf16 path's prologue and fused combine + epilogue are in
+// kernels_bf16_aux.hip, its main loops in main_bf16.hip and main_bf16_wide.hip.
 //
 // Absorption ("超越 GQA 的推理革命…MLA…", section 矩陣吸收): the key up-projection W_UK is
 // folded into the query (prologue) and the value up-projection W_UV is applied once to the
@@ -10,6 +10,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "plan_device.h"
 
 namespace mla {
 
@@ -29,10 +30,15 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
                                                   const int32_t* __restrict__ seqlens,
                                                   const T* __restrict__ w_uk, T* __restrict__ qcat,
                                                   int B, int H, int NB, int dn, int dcb, int dr,
-                                                  float qscale, RopeFreq rf) {
-  extern __shared__ float sq[];  // [kBatchBlock][NB][dn]
+                                                  float qscale, RopeFreq rf, PlanArgs plan,
+                                                  int lds_bytes) {
+  extern __shared__ __align__(16) float sq[];  // [kBatchBlock][NB][dn]; the plan block: scratch
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kBatchBlock;
+  if (h == H) {  // the extra column of blocks: block (H, 0) makes the split plan
+    if (b0 == 0) make_work_plan(plan, sq, lds_bytes);
+    return;
+  }
   const int nb = min(kBatchBlock, B - b0);
   const int dc = NB * dcb, row = dc + dr;
   const int per_b = NB * dn;
@@ -72,14 +78,14 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
 }
 
 hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(p.H, (p.B + kBatchBlock - 1) / kBatchBlock);
-  const size_t lds = (size_t)kBatchBlock * p.NB * p.dn * sizeof(float);
+  const dim3 grid(p.H + 1, (p.B + kBatchBlock - 1) / kBatchBlock);
+  const size_t lds = std::max<size_t>((size_t)kBatchBlock * p.NB * p.dn * sizeof(float), 16384);
   const float qscale = a.softmax_scale * kLog2e;
   RopeFreq rf;
   make_rope_freq(p.dr, a.rope_theta, &rf);
   hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, s, (const float*)a.q_nope,
                        (const float*)a.q_rope, a.seqlens, (const float*)a.w_uk, (float*)a.qcat,
-                       p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, rf);
+                       p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, rf, a.plan, (int)lds);
   return hipGetLastError();
 }
 
@@ -87,8 +93,8 @@ hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
 // Per (b, h, branch): merge the splits' (m_s, l_s, O_s) with log-sum-exp weights:
 //   M = max_s m_s,  o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // fp32 path: one workgroup handles 8 heads of one sequence; the split weights are formed
-// once in LDS, then the partial outputs stream through.  Splits with no tokens carry
-// m = -inf and weight 0 (their O_s is never read).
+// once in LDS, then the partial outputs stream through.  The splits of sequence b are its
+// work items split_off[b] .. split_off[b + 1] - 1 (none for an empty sequence: zeros).
 constexpr int kCombHeads = 8;    // heads per combine workgroup
 constexpr int kCombCols = 128;   // latent columns per combine workgroup (multiple of 4)
 
@@ -102,6 +108,7 @@ __device__ __forceinline__ f32x4 load4(const bf16* p) {
 template <typename TP, typename TO>
 __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ part_o,
                                                  const float* __restrict__ part_ml,
+                                                 const int32_t* __restrict__ split_off,
                                                  TO* __restrict__ olat, int H, int S, int NB,
                                                  int dcb) {
   extern __shared__ float sw[];  // [kCombHeads][branches in this column block][S]
@@ -112,23 +119,25 @@ __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ part_o,
   const int d0 = blockIdx.z * kCombCols, d1 = min(dc, d0 + kCombCols);
   const int br0 = d0 / dcb, nbr = (d1 - 1) / dcb - br0 + 1;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the work items (splits) of sequence b: u0 .. u0 + n - 1, n <= S
+  const int u0 = split_off[b], n = split_off[b + 1] - u0;
   const size_t sstride = (size_t)NB * H * 2;
   // split weights: one wave per (head, branch), lanes stride over the splits
   for (int pr = wv; pr < nh * nbr; pr += blockDim.x / 64) {
     const int hl = pr / nbr, br = br0 + pr % nbr;
-    const float* ml = part_ml + (((size_t)b * S) * NB + br) * H * 2 + (h0 + hl) * 2;
+    const float* ml = part_ml + ((size_t)u0 * NB + br) * H * 2 + (h0 + hl) * 2;
     float M = -INFINITY;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[s * sstride]);
+    for (int s = lane; s < n; s += 64) M = fmaxf(M, ml[s * sstride]);
     M = wave_max(M);
     float den = 0.0f;
     if (M != -INFINITY)
-      for (int s = lane; s < S; s += 64) {
+      for (int s = lane; s < n; s += 64) {
         const float m = ml[s * sstride];
         if (m != -INFINITY) den = fmaf(exp2f(m - M), ml[s * sstride + 1], den);
       }
     den = wave_sum(den);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    for (int s = lane; s < S; s += 64) {
+    for (int s = lane; s < n; s += 64) {
       const float m = ml[s * sstride];
       sw[pr * S + s] = (m == -INFINITY) ? 0.0f : exp2f(m - M) * inv;
     }
@@ -139,15 +148,15 @@ __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ part_o,
   for (int it = threadIdx.x; it < nh * q4; it += blockDim.x) {
     const int hl = it / q4, d = d0 + 4 * (it % q4);
     const float* wrow = sw + (hl * nbr + d / dcb - br0) * S;
-    const TP* src = part_o + (((size_t)b * S) * H + h0 + hl) * dc + d;
+    const TP* src = part_o + ((size_t)u0 * H + h0 + hl) * dc + d;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = 0; s0 < S; s0 += 4) {
+    for (int s0 = 0; s0 < n; s0 += 4) {
       f32x4 v[4];
       float wt[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        wt[u] = s0 + u < S ? wrow[s0 + u] : 0.0f;
-        // splits with no tokens have weight 0 and never-written partials: skip the load
+        wt[u] = s0 + u < n ? wrow[s0 + u] : 0.0f;
+        // a split whose every score underflowed has weight 0: skip its load
         v[u] = wt[u] != 0.0f ? load4(src + (size_t)(s0 + u) * pstride) : f32x4{};
       }
 #pragma unroll
@@ -165,7 +174,7 @@ hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const int max_br = kCombCols / p.dcb + 2;
   const size_t lds = (size_t)kCombHeads * std::min(p.NB, max_br) * p.splits * sizeof(float);
   hipLaunchKernelGGL((k_combine<float, float>), grid, dim3(256), lds, s, (const float*)a.part_o,
-                     a.part_ml, (float*)a.olat, p.H, p.splits, p.NB, p.dcb);
+                     a.part_ml, a.split_off, (float*)a.olat, p.H, p.splits, p.NB, p.dcb);
   return hipGetLastError();
 }
 
@@ -255,27 +264,20 @@ hipError_t launch_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, i
 __global__ __launch_bounds__(64) void k_main_f32(
     const float* __restrict__ qcat, const float* __restrict__ latent,
     const float* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
-    int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
+    int64_t rope_seq, const int32_t* __restrict__ work, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
-    int S, int chunk, int NB, int dcb, int dr) {
+    int NB, int dcb, int dr) {
   __shared__ float sq[512 + 64];
   __shared__ float sp[64 * 4];
   const int h = blockIdx.x % H;
-  const int unit = blockIdx.x / H;
-  const int b = unit / S, s = unit % S;
+  const int slot = blockIdx.x / H;  // slot s runs work item s
+  const int b = work[4 * slot];
+  if (b < 0) return;
+  const int t0 = work[4 * slot + 1], t1 = work[4 * slot + 2];
+  const size_t item = (size_t)work[4 * slot + 3];
   const int lane = threadIdx.x;
   const int dc = NB * dcb, row = dc + dr;
-  const int L = seqlens[b];
-  const int t0 = s * chunk;
-  const int t1 = min(L, t0 + chunk);
-  float* ml = part_ml + (((size_t)b * S + s) * NB) * H * 2;
-  if (t0 >= t1) {
-    if (lane < NB) {
-      ml[((size_t)lane * H + h) * 2 + 0] = -INFINITY;
-      ml[((size_t)lane * H + h) * 2 + 1] = 0.0f;
-    }
-    return;
-  }
+  float* ml = part_ml + item * NB * H * 2;
   for (int i = lane; i < row; i += 64) sq[i] = qcat[((size_t)b * H + h) * row + i];
   __syncthreads();
   auto lat_row = [&](int t) -> const float* {
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(64) void k_main_f32(
   for (int k = 0; k < 8; ++k) {
     const int d = lane + 64 * k;
     if (d >= dc) break;
-    part_o[(((size_t)b * S + s) * H + h) * dc + d] = o[k];
+    part_o[(item * H + h) * dc + d] = o[k];
   }
   if (lane < NB) {
     ml[((size_t)lane * H + h) * 2 + 0] = m[lane];
@@ -338,11 +340,11 @@ __global__ __launch_bounds__(64) void k_main_f32(
 }
 
 hipError_t launch_main_f32(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)p.B * p.splits * p.H));
+  const dim3 grid((unsigned)((size_t)p.slots * p.H));
   hipLaunchKernelGGL(k_main_f32, grid, dim3(64), 0, s, (const float*)a.qcat,
                      (const float*)a.latent, (const float*)a.rope, a.lat_tok, a.lat_seq,
-                     a.rope_tok, a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged,
-                     (float*)a.part_o, a.part_ml, p.H, p.splits, p.chunk, p.NB, p.dcb, p.dr);
+                     a.rope_tok, a.rope_seq, a.work, a.block_table, a.bt_stride, p.paged,
+                     (float*)a.part_o, a.part_ml, p.H, p.NB, p.dcb, p.dr);
   return hipGetLastError();
 }
 

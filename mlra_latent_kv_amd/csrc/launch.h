@@ -5,6 +5,7 @@
 
 #include "device_common.h"
 #include "plan.h"
+#include "plan_device.h"
 
 namespace mla {
 
@@ -21,10 +22,13 @@ struct DecodeArgs {
   int64_t lat_tok, lat_seq, rope_tok, rope_seq, bt_stride;
   float softmax_scale, out_scale, rope_theta;
   // workspace regions
+  PlanArgs plan;    // split plan, written by the prologue launch
+  const int32_t* work;       // [slots][4] dispatch table: b, t_begin, t_end, item (b < 0: none)
+  const int32_t* split_off;  // [B + 1] first work item of each sequence
   void* qcat;       // [B][H][row] storage dtype, pre-scaled by softmax_scale*log2(e)
-  void* part_o;     // [B][S][H][d_c], unnormalised partial latent outputs: bf16 on the bf16
+  void* part_o;     // [item][H][d_c], unnormalised partial latent outputs: bf16 on the bf16
                     // path (the same rounding as the latent output), fp32 otherwise
-  float* part_ml;   // [B][S][NB][H][2]  (running max in log2 units, running sum)
+  float* part_ml;   // [item][NB][H][2]  (running max in log2 units, running sum)
   void* olat;       // [B][H][d_c] fp32, fp32 path only (the bf16 path keeps it on chip)
 };
 

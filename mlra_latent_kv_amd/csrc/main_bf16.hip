@@ -55,36 +55,27 @@ template <int NB>
 __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
-    int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
+    int64_t rope_seq, const int32_t* __restrict__ work, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, bf16* __restrict__ part_o, float* __restrict__ part_ml, int H,
-    int S, int chunk, int n_hg, int units) {
+    int n_hg) {
   __shared__ __align__(16) Smem<NB> sm;
 
   // XCD-aware mapping: consecutive blocks go to different XCDs, so the head groups of one
-  // (sequence, split) are placed 8 blocks apart -> same XCD, dispatched back to back, and
-  // their reads of the same tiles can hit that XCD's L2.
+  // dispatch slot (one work item) are placed 8 blocks apart -> same XCD, dispatched back to
+  // back, and their reads of the same tiles can hit that XCD's L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, r = bid >> 3;
   const int hg = r % n_hg;
-  const int unit = (r / n_hg) * 8 + xcd;
-  if (unit >= units) return;
-  const int b = unit / S, s = unit % S;
+  const int4 wi = *reinterpret_cast<const int4*>(work + 4 * ((r / n_hg) * 8 + xcd));
+  const int b = wi.x;
+  if (b < 0) return;  // slot without a work item
+  const int t_begin = wi.y, t_end = wi.z;  // page-aligned start, never empty
+  const size_t item = (size_t)wi.w;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, kg = lane >> 5;
   const int h0 = hg * kHG;
-  const int L = seqlens[b];
-  const int t_begin = s * chunk;
-  const int t_end = min(L, t_begin + chunk);
-  float* ml = part_ml + ((size_t)b * S + s) * NB * H * 2;  // [br][H][2]
+  float* ml = part_ml + item * NB * H * 2;  // [br][H][2]
 
-  if (t_begin >= t_end) {
-    if (tid < NB * kHG) {
-      const int br = tid / kHG, hh = tid % kHG;
-      ml[((size_t)br * H + h0 + hh) * 2 + 0] = -INFINITY;
-      ml[((size_t)br * H + h0 + hh) * 2 + 1] = 0.0f;
-    }
-    return;
-  }
   const int n_tiles = (t_end - t_begin + kTT - 1) / kTT;
 
   // Tile loads: wave w brings latent rows 8w..8w+7 and the rotary keys of the same rows
@@ -259,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
   }
 
   // ---- partial outputs.  O[mb] item i: column d = 128w + 32mb + 8*(i/4) + 4*kg + i%4, head l32
-  bf16* po = part_o + (((size_t)b * S + s) * H + h0 + l32) * kDC + 128 * w + 4 * kg;
+  bf16* po = part_o + (item * H + h0 + l32) * kDC + 128 * w + 4 * kg;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -282,13 +273,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
 }  // namespace
 
 hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  const int units = p.B * p.splits;
-  const unsigned blocks = (unsigned)(((units + 7) / 8) * 8 * p.n_hg);
+  const unsigned blocks = (unsigned)(p.slots * p.n_hg);
   auto kern = p.NB == 1 ? k_main_bf16<1> : k_main_bf16<4>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, s, (const bf16*)a.qcat,
                      (const bf16*)a.latent, (const bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok,
-                     a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,
-                     a.part_ml, p.H, p.splits, p.chunk, p.n_hg, units);
+                     a.rope_seq, a.work, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,
+                     a.part_ml, p.H, p.n_hg);
   return hipGetLastError();
 }
 

@@ -127,9 +127,9 @@ __device__ __forceinline__ void scale_acc(f32x16& o, float a) {
 __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
-    int64_t rope_seq, const int32_t* __restrict__ seqlens, const int32_t* __restrict__ bt,
+    int64_t rope_seq, const int32_t* __restrict__ work, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, bf16* __restrict__ part_o, float* __restrict__ part_ml, int H,
-    int S, int chunk, int n_hq, int units) {
+    int n_hq) {
   // One LDS object.  (Kept as a single struct: with separate arrays the compiler's wait
   // analysis stops telling the tile reads apart from the loads in flight and waits for all
   // of them before the first read of every tile.)
@@ -144,32 +144,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   char (&ring)[kRing][kBufBytes] = sm.ring;
   char* const qlds = sm.qlds;
 
-  // XCD-aware mapping.  Blocks are dispatched round-robin over the 8 XCDs; XCD x gets a
-  // contiguous range of (sequence, split) units, so the splits of one sequence (which all
-  // read its query) and the head quads of one unit (which read the same tiles) share that
-  // XCD's L2.
-  const int per_xcd = (units + 7) / 8;
+  // XCD-aware mapping.  Blocks are dispatched round-robin over the 8 XCDs: block 8r + x runs
+  // head quad r % n_hq of dispatch slot 8(r / n_hq) + x, and the split plan gives XCD x a
+  // contiguous range of work items, so the items of one sequence (which all read its query)
+  // and the head quads of one item (which read the same tiles) share that XCD's L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, r = bid >> 3;
   const int hq = r % n_hq;
-  const int unit = xcd * per_xcd + r / n_hq;
-  if (unit >= units) return;
-  const int b = unit / S, s = unit % S;
+  const int4 wi = *reinterpret_cast<const int4*>(work + 4 * (8 * (r / n_hq) + xcd));
+  const int b = wi.x;
+  if (b < 0) return;  // slot without a work item
+  const int t_begin = wi.y, t_end = wi.z;  // page-aligned start, never empty
+  int item = wi.w;  // index of the partial results
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, kg = lane >> 5;
   const int h0 = hq * kHeadsWG + 32 * w;  // this wave's heads
-  const int L = seqlens[b];
-  const int t_begin = s * chunk;
-  const int t_end = min(L, t_begin + chunk);
-  float* ml = part_ml + ((size_t)b * S + s) * H * 2;  // [H][2]
 
-  if (t_begin >= t_end) {
-    if (tid < kHeadsWG) {
-      ml[(size_t)(hq * kHeadsWG + tid) * 2 + 0] = -INFINITY;
-      ml[(size_t)(hq * kHeadsWG + tid) * 2 + 1] = 0.0f;
-    }
-    return;
-  }
   const int n_tiles = (t_end - t_begin + kTT - 1) / kTT;
 
   const uint32_t lat_row_b = (uint32_t)(lat_tok * 2), rope_row_b = (uint32_t)(rope_tok * 2);
@@ -372,7 +362,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   }
 
   // ---- partial outputs.  O[cb] item e: column 32cb + 8*(e/4) + 4*kg + e%4 of head h0 + l32
-  bf16* po = part_o + (((size_t)b * S + s) * H + h0 + l32) * kDC + 4 * kg;
+  // (the item index is made opaque here so that the output addresses are formed after the
+  // loop instead of being held in registers across it)
+  asm volatile("" : "+s"(item));
+  bf16* po = part_o + ((size_t)item * H + h0 + l32) * kDC + 4 * kg;
+  float* ml = part_ml + (size_t)item * H * 2;  // [H][2]
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
@@ -390,12 +384,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
 
 hipError_t launch_main_bf16_wide(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const int n_hq = p.H / kHeadsWG;
-  const int units = p.B * p.splits;
-  const unsigned blocks = (unsigned)(((units + 7) / 8) * 8 * n_hq);
+  const unsigned blocks = (unsigned)(p.slots * n_hq);
   hipLaunchKernelGGL(k_main_bf16_wide, dim3(blocks), dim3(kThreads), 0, s, (const bf16*)a.qcat,
                      (const bf16*)a.latent, (const bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok,
-                     a.rope_seq, a.seqlens, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,
-                     a.part_ml, p.H, p.splits, p.chunk, n_hq, units);
+                     a.rope_seq, a.work, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,
+                     a.part_ml, p.H, n_hq);
   return hipGetLastError();
 }
 

@@ -76,34 +76,47 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
       return MLA_ERR_SHAPE;
   }
 
-  // split plan: enough workgroups to fill the chip on uniform lengths
-  const int64_t wg_per_split = q.path != Path::kBf16Mfma ? (int64_t)q.B * q.H
-                               : q.wide ? (int64_t)q.B * (q.H / kWideHeads)
-                                        : (int64_t)q.B * q.n_hg;
-  const int64_t target = q.wide ? kTargetWideWorkgroups : kTargetWorkgroups;
-  int splits = p->num_splits;
-  if (splits == 0) splits = (int)std::max<int64_t>(1, ceil_div(target, wg_per_split));
-  if (splits > q.n_tiles) {
-    if (p->num_splits) return MLA_ERR_SHAPE;
-    splits = q.n_tiles;
+  // Split plan.  The device cuts sum_b ceil(L_b / 64) pages into work items of c whole pages
+  // each (a sequence of p_b pages gets ceil(p_b / c) items).  Automatic: c is the smallest
+  // count that keeps the items within `target` (enough workgroups to fill the chip once),
+  // one item per sequence if none does; forced: c = ceil(n_tiles / num_splits).
+  const int64_t wg_per_item = q.path != Path::kBf16Mfma ? q.H
+                              : q.wide ? q.H / kWideHeads
+                                       : q.n_hg;
+  const int64_t target_wg = q.wide ? kTargetWideWorkgroups : kTargetWorkgroups;
+  q.target = (int)std::max<int64_t>(1, ceil_div(target_wg, wg_per_item));
+  q.xcd_major = q.wide;
+  int64_t cap;
+  if (p->num_splits > 0) {
+    if (p->num_splits > q.n_tiles) return MLA_ERR_SHAPE;
+    q.forced_pages = (int)ceil_div(q.n_tiles, p->num_splits);
+    q.splits = (int)ceil_div(q.n_tiles, q.forced_pages);
+    if (q.splits > kMaxSplits) return MLA_ERR_SHAPE;
+    cap = (int64_t)q.B * q.splits;
+  } else {
+    // W <= target whenever some c meets it; otherwise one item per non-empty sequence
+    q.forced_pages = 0;
+    q.splits = std::min(q.n_tiles, q.target);
+    cap = std::max<int64_t>(q.target, q.B);
   }
-  const int chunk_tiles = (int)ceil_div(q.n_tiles, splits);
-  q.chunk = chunk_tiles * kPage;
-  q.splits = (int)ceil_div(q.n_tiles, chunk_tiles);
-  if (q.splits > kMaxSplits) return MLA_ERR_SHAPE;
   // grid sizes and 32-bit work-item indices must fit
-  if (wg_per_split * q.splits + 8LL * std::max(q.n_hg, 1) > INT32_MAX ||
+  if (cap + 8 > INT32_MAX / 4 || wg_per_item * (cap + 8) + 8LL * std::max(q.n_hg, 1) > INT32_MAX ||
       (int64_t)q.B * q.H > INT32_MAX)
     return MLA_ERR_SHAPE;
+  q.items_cap = (int)cap;
+  q.slots = (int)ceil_div(cap, 8) * 8;
 
-  // workspace
+  // workspace: plan, absorbed queries, per-item partials, fp32 merged latent
   size_t off = 0;
+  q.off_work = 16;  // after the 4-word header
+  q.off_split_off = q.off_work + (size_t)q.slots * 16;
+  off = align_up(q.off_split_off + ((size_t)q.B + 1) * 4);
   q.off_qcat = off;
   off = align_up(off + (size_t)q.B * q.H * q.row * q.elem);
   q.off_part_o = off;
-  off = align_up(off + (size_t)q.B * q.splits * q.H * q.dc * (q.dtype == MLA_BF16 ? 2 : 4));
+  off = align_up(off + (size_t)q.items_cap * q.H * q.dc * (q.dtype == MLA_BF16 ? 2 : 4));
   q.off_part_ml = off;
-  off = align_up(off + (size_t)q.B * q.splits * q.NB * q.H * 2 * sizeof(float));
+  off = align_up(off + (size_t)q.items_cap * q.NB * q.H * 2 * sizeof(float));
   q.off_olat = off;  // merged latent output: fp32 path only (bf16 keeps it on chip)
   if (q.dtype != MLA_BF16) off = align_up(off + (size_t)q.B * q.H * q.dc * 4);
   q.bytes = off;

@@ -16,7 +16,8 @@ constexpr int kTargetWorkgroups = 512; // two per CU of an MI355X (32-head kerne
 constexpr int kWideHeads = 128;        // heads per workgroup of the wide bf16 kernel
 constexpr int kTargetWideWorkgroups = 256;  // one per CU (the wide kernel fills a CU's LDS)
 constexpr size_t kWsAlign = 256;
-constexpr int kMaxSplits = 512;        // bound on sequence splits (combine keeps weights in LDS)
+constexpr int kMaxSplits = 512;        // bound on work items per sequence (the fp32 combine
+                                       // keeps one weight per item in LDS)
 
 enum class Path { kBf16Mfma, kF32Simt };
 
@@ -26,13 +27,20 @@ struct Plan {
   int paged;
   int max_seqlen;
   int n_tiles;   // ceil(max_seqlen / 64), >= 1
-  int splits;    // sequence splits per sequence
-  int chunk;     // tokens per split, multiple of 64
+  // Split plan.  The device cuts the batch into work items of whole pages (see
+  // plan_device.h); the host only bounds it.
+  int target;        // work items the automatic plan aims for (a workgroup set per CU slot)
+  int forced_pages;  // pages per work item when num_splits is given, else 0
+  int splits;        // most work items one sequence can be cut into (<= kMaxSplits)
+  int items_cap;     // most work items of one call: sizes the partials
+  int slots;         // dispatch slots of the main kernels (items_cap rounded up to 8)
+  int xcd_major;     // 1: slot 8g + x takes item x * ceil(W / 8) + g (XCD-contiguous items)
   int n_hg;      // head groups of the bf16 kernel (H / 32); 0 on the fp32 path
   int wide;      // 1: bf16 MLA with H % 128 == 0 runs the 128-heads-per-workgroup kernel
   Path path;
-  // workspace layout (byte offsets); part_o holds bf16 on the bf16 path, fp32 otherwise
-  size_t off_qcat, off_part_o, off_part_ml, off_olat, bytes;
+  // workspace layout (byte offsets); part_o holds bf16 on the bf16 path, fp32 otherwise.
+  // The plan comes first: header int32[4], work int32[slots][4], split_off int32[B + 1].
+  size_t off_work, off_split_off, off_qcat, off_part_o, off_part_ml, off_olat, bytes;
 };
 
 // Validates *p (shape, dtype, support, strides) and fills *plan.  Touches no device.

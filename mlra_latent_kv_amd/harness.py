@@ -110,3 +110,18 @@ def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None) -> Dev
         branches=w.branches,
     )
     return case
+
+
+def read_plan(case: DeviceCase) -> dict:
+    """The split plan the last call left at the start of the workspace (layout documented in
+    include/mla_decode.h): item count W, pages per item c, dispatch slots, item target (0 when
+    the split count was forced), the dispatch table [slots, 4] = (b, t_begin, t_end, item)
+    and split_off [B + 1].  Synchronises with the device."""
+    ws = case.workspace
+    hdr = ws[:16].view(torch.int32).cpu().numpy()
+    slots = int(hdr[2])
+    work = ws[16:16 + 16 * slots].view(torch.int32).cpu().numpy().reshape(slots, 4)
+    off = 16 + 16 * slots
+    split_off = ws[off:off + 4 * (case.params.batch + 1)].view(torch.int32).cpu().numpy()
+    return {"items": int(hdr[0]), "pages": int(hdr[1]), "slots": slots, "target": int(hdr[3]),
+            "work": work, "split_off": split_off}

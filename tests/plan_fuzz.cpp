@@ -41,7 +41,18 @@ int main() {
     if (st == MLA_OK) {
       ++ok;
       // invariants of an accepted plan
-      if (plan.splits < 1 || plan.chunk % 64 || (long long)plan.splits * plan.chunk < p.max_seqlen ||
+      const long long pages = p.max_seqlen > 0 ? (p.max_seqlen + 63) / 64 : 1;
+      const bool forced = p.num_splits > 0;
+      const long long per = forced ? plan.forced_pages : 0;
+      if (plan.splits < 1 || plan.splits > mla::kMaxSplits || plan.splits > pages ||
+          plan.target < 1 || plan.items_cap < 1 || plan.slots % 8 ||
+          plan.slots < plan.items_cap || plan.slots - plan.items_cap >= 8 ||
+          (forced && (per < 1 || per * plan.splits < pages || per * (plan.splits - 1) >= pages ||
+                      plan.items_cap != (long long)p.batch * plan.splits)) ||
+          (!forced && (plan.forced_pages != 0 || plan.items_cap < plan.target ||
+                       plan.items_cap < p.batch)) ||
+          plan.off_work != 16 || plan.off_split_off != 16 + 16 * (size_t)plan.slots ||
+          plan.off_qcat < plan.off_split_off + 4 * ((size_t)p.batch + 1) ||
           plan.off_part_o < plan.off_qcat || plan.off_part_ml < plan.off_part_o ||
           plan.off_olat < plan.off_part_ml || plan.bytes < plan.off_olat) {
         std::printf("bad plan at iteration %d\n", it);

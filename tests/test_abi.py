@@ -129,39 +129,62 @@ def test_status_strings(lib):
 
 
 @pytest.mark.parametrize("wname", I.WORKLOAD_ORDER)
-def test_workspace_layout(lib, wname):
+@pytest.mark.parametrize("forced", [0, 3])
+def test_workspace_layout(lib, wname, forced):
     w = I.WORKLOADS[wname]
     lens = [w.seqlen] * 3
     inp = I.make_inputs(w, seqlens=[1, 2, 3]) if w.seqlen > 5000 else I.make_inputs(w, seqlens=lens)
     p = make_params(inp)
     p.max_seqlen = w.seqlen
+    pages = (w.seqlen + 63) // 64
     if w.paged:
-        p.max_pages_per_seq = p.block_table_stride = (w.seqlen + 63) // 64
+        p.max_pages_per_seq = p.block_table_stride = pages
+    forced = min(forced, pages)
+    p.num_splits = forced
     S = B.num_splits(p)
-    assert 1 <= S <= (w.seqlen + 63) // 64
-    al = lambda x: (x + 255) // 256 * 256
+    wide = w.dtype == "bf16" and w.branches == 1 and w.heads % 128 == 0
+    wg_per_item = w.heads // 128 if wide else w.heads // 32 if w.dtype == "bf16" else w.heads
+    target = max(1, -(-(256 if wide else 512) // wg_per_item))
     Bn, H, dc = 3, w.heads, w.d_c
-    # partial outputs are stored in the element type (bf16 on the bf16 path), (m, l) in fp32
-    exp = al(Bn * H * w.row * w.elem_bytes) + al(Bn * S * H * dc * w.elem_bytes) + \
-        al(Bn * S * w.branches * H * 2 * 4) + (al(Bn * H * dc * 4) if w.elem_bytes == 4 else 0)
+    if forced:
+        assert S == -(-pages // -(-pages // forced))
+        cap = Bn * S
+    else:
+        assert S == min(pages, target)
+        cap = max(target, Bn)
+    slots = -(-cap // 8) * 8
+    al = lambda x: (x + 255) // 256 * 256
+    # plan (header, dispatch table, split offsets), queries, per-item partials (element type
+    # on the bf16 path), (m, l) in fp32, and the fp32 merged latent
+    exp = al(16 + 16 * slots + 4 * (Bn + 1)) + al(Bn * H * w.row * w.elem_bytes) + \
+        al(cap * H * dc * w.elem_bytes) + al(cap * w.branches * H * 2 * 4) + \
+        (al(Bn * H * dc * 4) if w.elem_bytes == 4 else 0)
     assert B.workspace_size(p) == exp
 
 
-def test_split_plan_fills_the_chip(lib):
-    # bf16 MLA with H % 128 == 0: one workgroup per (sequence, split, 128 heads), 256 in all
+def test_split_bounds(lib):
+    # bf16 MLA with H % 128 == 0: one workgroup per (work item, 128 heads), 256 items target
     p = params_for("mla_bf16_b32_h128_l4096", batch=32, max_seqlen=4096)
-    assert B.num_splits(p) == 8          # 32 sequences x 8 splits = 256
+    assert B.num_splits(p) == 64         # one sequence may take up to all of its 64 pages
     p = params_for("mla_bf16_paged_b4_h128_l131072", batch=4, max_seqlen=131072,
                    max_pages_per_seq=2048, block_table_stride=2048)
-    assert B.num_splits(p) == 64         # 4 sequences x 64 splits = 256
+    assert B.num_splits(p) == 256        # bounded by the item target
     p.num_splits = 7
     assert B.num_splits(p) == 7
-    # 32-head groups (two workgroups per CU): 512 in all
+    p.num_splits = 600                   # 4 pages per item: 512 items
+    assert B.num_splits(p) == 512
+    p.num_splits = 1000                  # 3 pages per item: 683 > 512 items
+    with pytest.raises(B.MlaError):
+        B.num_splits(p)
+    # 32-head groups (two workgroups per CU): 512 items target
     p = params_for("mla_bf16_paged_b64_h32_l1k-32k", batch=64, max_seqlen=32768,
                    max_pages_per_seq=512, block_table_stride=512)
-    assert B.num_splits(p) == 8          # 64 sequences x 1 head group x 8 splits = 512
+    assert B.num_splits(p) == 512
     p = params_for("mlra4_bf16_b32_h32_l8192", batch=32, max_seqlen=8192)
-    assert B.num_splits(p) == 16         # 32 sequences x 1 head group x 16 splits = 512
+    assert B.num_splits(p) == 128
+    p.num_splits = 129                   # more splits than pages
+    with pytest.raises(B.MlaError):
+        B.num_splits(p)
 
 
 def test_plan_code_under_host_sanitizers(tmp_path):

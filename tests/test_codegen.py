@@ -40,32 +40,84 @@ def _kernels(asm: str):
     out = []
     for m in re.finditer(r"^(_ZN3mla\w*k_main_bf16\w*):.*$", asm, re.M):
         name = m.group(1)
-        end = asm.index("s_endpgm", m.end())
+        end = asm.index(".Lfunc_end", m.end())
         meta = asm[asm.index(f".amdhsa_kernel {name}"):]
         meta = meta[:meta.index(".end_amdhsa_kernel")]
         out.append((name, asm[m.end():end].splitlines(), meta))
     return out
 
 
+def _blocks(lines):
+    """Labelled basic blocks (label, note, instruction lines) in text order.  Unlabelled
+    fall-through blocks (%bb.N) stay merged into the block before them."""
+    blocks = []
+    for ln in lines:
+        m = re.match(r"^\.(LBB\w+):(.*)$", ln)
+        if m:
+            blocks.append((m.group(1), m.group(2), []))
+        elif blocks:
+            ins = ln.split(";")[0].strip()
+            if ins and not ins.startswith("."):
+                blocks[-1][2].append(ins)
+    return blocks
+
+
 def _main_loop(lines):
-    """Lines of the innermost loop that issues tile loads: from its header label to the last
-    branch back to it.  (The label of a nested loop carries the header note on the next
-    line.)"""
+    """(blocks, header index, loop block indices) of the innermost loop that issues tile
+    loads.  Membership comes from the assembler's "in Loop: Header=" notes: the compiler may
+    rotate a loop so that its latch precedes the header and falls through into it."""
+    blocks = _blocks(lines)
+    loops = {}
+    for i, (label, note, _) in enumerate(blocks):
+        m = re.search(r"in Loop: Header=(BB\w+) Depth", note)
+        if "Inner Loop Header" in note:
+            loops.setdefault(label[1:], set()).add(i)
+        elif m:
+            loops.setdefault(m.group(1), set()).add(i)
     best = None
-    for i, ln in enumerate(lines):
-        m = re.match(r"^(\.LBB\w+):", ln)
-        if not m or "Loop Header" not in ln + (lines[i + 1] if i + 1 < len(lines) else ""):
+    for hdr, members in loops.items():
+        head = next((i for i in members if blocks[i][0] == "L" + hdr), None)
+        if head is None or "Inner Loop Header" not in blocks[head][1]:
             continue
-        label = m.group(1)
-        back = [j for j in range(i + 1, len(lines))
-                if re.search(r"s_(c)?branch\w*\s+" + re.escape(label) + r"\b", lines[j])]
-        if not back:
-            continue
-        body = lines[i:back[-1] + 1]
-        if any("lds" in x and "buffer_load" in x for x in body):
-            if best is None or len(body) < len(best):
-                best = body
+        if any("lds" in x and "buffer_load" in x for i in members for x in blocks[i][2]):
+            if best is None or len(members) < len(best[2]):
+                best = (blocks, head, members)
     return best
+
+
+def _drains_after_issue(blocks, head, members):
+    """vmcnt(0) waits on any path from a tile load of the loop to the next pass through the
+    loop header (a wait at the top of an iteration, before the next tile goes out, is the
+    kernel's own choice; a wait between issuing a tile and the end of the iteration would
+    drain it)."""
+    index = {b[0]: i for i, b in enumerate(blocks)}
+    starts = [(i, j + 1) for i in members for j, x in enumerate(blocks[i][2])
+              if "buffer_load" in x and "lds" in x]
+    seen, found, stack = set(), [], list(starts)
+    while stack:
+        i, j = stack.pop()
+        if (i, j) in seen:
+            continue
+        seen.add((i, j))
+        ins = blocks[i][2]
+        if j >= len(ins):  # fall through
+            if i + 1 in members and i + 1 != head:
+                stack.append((i + 1, 0))
+            continue
+        x = ins[j]
+        if re.match(r"s_waitcnt\s.*vmcnt\(0\)", x):
+            found.append((blocks[i][0], x))
+        m = re.match(r"s_(c)?branch\w*\s+\.(LBB\w+)", x)
+        if m:
+            t = index.get(m.group(2))
+            if t is not None and t in members and t != head:
+                stack.append((t, 0))
+            if not m.group(1):
+                continue  # unconditional: no fall-through
+        if x.startswith("s_endpgm"):
+            continue
+        stack.append((i, j + 1))
+    return found
 
 
 @pytest.mark.parametrize("src", ["main_bf16.hip", "main_bf16_wide.hip"])
@@ -73,13 +125,33 @@ def test_main_loop_keeps_tile_loads_in_flight(src, tmp_path):
     kernels = _kernels(_asm(src, tmp_path))
     assert kernels, "no main-loop kernel found"
     for name, lines, _meta in kernels:
-        body = _main_loop(lines)
-        assert body is not None, (name, "main loop not found")
-        first_dma = next(i for i, x in enumerate(body) if "buffer_load" in x and "lds" in x)
-        waits = [x.strip() for x in body[first_dma:] if re.search(r"s_waitcnt\s.*vmcnt\(0\)", x)]
+        loop = _main_loop(lines)
+        assert loop is not None, (name, "main loop not found")
+        blocks, head, members = loop
+        waits = _drains_after_issue(blocks, head, members)
         assert not waits, (name, "drains the tile loads inside the loop", waits)
-        spills = [x.strip() for x in body if "scratch_" in x]
+        spills = [x for i in members for x in blocks[i][2] if "scratch_" in x]
         assert not spills, (name, "spills inside the loop", spills[:4])
+
+
+def test_drain_scan_sees_a_wait_after_the_issue():
+    # rotated loop: the latch (LBB0_3) falls through into the header (LBB0_4)
+    loop = """.LBB0_2:                ;   in Loop: Header=BB0_4 Depth=1
+\tv_add_u32 v1, v1, v2
+{late}.LBB0_3:                ;   in Loop: Header=BB0_4 Depth=1
+\ts_add_i32 s4, s4, 1
+.LBB0_4:                ; =>This Inner Loop Header: Depth=1
+\ts_waitcnt vmcnt(0)
+\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds
+\ts_cbranch_scc1 .LBB0_2
+\ts_branch .LBB0_3
+.LBB0_5:
+\ts_endpgm
+"""
+    bad = _main_loop(loop.format(late="\ts_waitcnt vmcnt(0)\n").splitlines())
+    assert [w[0] for w in _drains_after_issue(*bad)] == ["LBB0_2"]
+    good = _main_loop(loop.format(late="").splitlines())  # the wait at the top only
+    assert _drains_after_issue(*good) == []
 
 
 # Wait states an instruction that reads or writes an MFMA's destination registers must stay

@@ -159,7 +159,8 @@ def test_split_count_invariance(wname):
 
 # Shapes that drive every variant of the fused split merge + W_UV epilogue: row blocks of 16,
 # 8 and 4 (partial last blocks included), several batches of splits per thread, split
-# statistics with more than four splits per statistics lane, and many empty splits.
+# statistics with more than four splits per statistics lane, and rows with one split next to
+# rows with many in the same workgroup (a variable split count per row).
 FUSED_CASES = [
     # MLA, 20 rows -> 16-row blocks (second one partial), 71 splits (> 4 per lane of 16)
     ("mla_bf16_b32_h128_l4096", [4500, 40, 700, 5, 64, 129, 1, 2100, 999, 333, 77, 18, 300, 250,
@@ -269,6 +270,75 @@ def test_negative_controls_fail_the_tolerance(wname):
         assert rl > TOL["bf16"][1], name
 
 
+# ----------------------------------------------------------------------------- split plan
+
+def check_plan(plan, w, lens, max_seqlen, forced):
+    """The device's split plan against its definition, worked out here from the lengths:
+    items of c whole pages per sequence (ceil(p_b / c) of them), c the smallest count whose
+    items fit the target (or the longest sequence's pages when none does), or fixed by the
+    forced split count; sequence-major item numbers; and the dispatch table the main kernels
+    read."""
+    cdiv = lambda a, b: -(-a // b)
+    W, c, slots, target = plan["items"], plan["pages"], plan["slots"], plan["target"]
+    pages = [cdiv(min(max(L, 0), max_seqlen), 64) for L in lens]
+    count = lambda cc: sum(cdiv(p, cc) for p in pages)
+    if forced:
+        assert target == 0 and c == cdiv(max(1, cdiv(max_seqlen, 64)), forced)
+    else:
+        maxp = max(max(pages), 1)
+        assert target >= 1
+        if count(maxp) <= target:
+            assert count(c) <= target and (c == 1 or count(c - 1) > target), (c, target)
+        else:
+            assert c == maxp
+    n = [cdiv(p, c) for p in pages]
+    so = plan["split_off"]
+    assert list(so) == list(np.concatenate([[0], np.cumsum(n)])) and W == so[-1]
+    wide = w.dtype == "bf16" and w.branches == 1 and w.heads % 128 == 0
+    per = cdiv(W, 8)
+    seen = np.zeros(W, np.int64)
+    for s_, (b, t0, t1, item) in enumerate(plan["work"]):
+        exp = s_
+        if wide:
+            x, g = s_ % 8, s_ // 8
+            exp = x * per + g if g < per else W
+        if exp >= W:
+            assert b == -1, (s_, plan["work"][s_])
+            continue
+        assert item == exp and so[b] <= item < so[b + 1], (s_, b, item)
+        j = item - so[b]
+        assert t0 == j * c * 64 and t1 == min(lens[b], t0 + c * 64) and t0 < t1
+        seen[item] += 1
+    assert np.all(seen == 1)
+
+
+PLAN_CASES = [
+    # wide MLA: empty, one-token, page-edge and long sequences; automatic and forced
+    ("mla_bf16_b32_h128_l4096", [0, 1, 64, 65, 4000, 0, 129, 3000, 77, 2048], 0),
+    ("mla_bf16_b32_h128_l4096", [0, 1, 64, 65, 4000, 0, 129, 3000, 77, 2048], 5),
+    # 32-head MLA: one long sequence among short ones takes most of the items
+    ("mla_bf16_paged_b64_h32_l1k-32k", [9000, 1, 70, 0, 300], 0),
+    # MLRA-4 with more sequences than the item target: one item per sequence
+    ("mlra4_bf16_b32_h32_l8192", [1 + (37 * i) % 200 for i in range(600)], 0),
+]
+
+
+@pytest.mark.parametrize("wname,lens,forced", PLAN_CASES,
+                         ids=[f"{c[0]}-B{len(c[1])}-F{c[2]}" for c in PLAN_CASES])
+def test_split_plan(wname, lens, forced):
+    from mlra_latent_kv_amd import harness as H
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=lens, q_gain=I.sharp_q_gain(w))
+    got, case = gpu_out(inp, num_splits=forced)
+    plan = H.read_plan(case)
+    note(f"  {wname}: {plan['items']} items of {plan['pages']} pages, target {plan['target']}")
+    check_plan(plan, w, lens, case.params.max_seqlen, forced)
+    bs = list(range(min(len(lens), 40)))
+    assert_close(got[bs], oracle_out(inp, batches=bs), "bf16", f"{wname} plan F{forced}")
+    if len(lens) > len(bs):
+        assert np.all(np.isfinite(got))
+
+
 # ----------------------------------------------------------------------------- full sizes
 
 SAMPLES = {
@@ -289,6 +359,8 @@ def test_full_size_sampled(wname):
     note(f"  generating {wname}")
     inp = I.make_inputs(w)
     got, case = gpu_out(inp)
+    from mlra_latent_kv_amd import harness as H
+    check_plan(H.read_plan(case), w, list(inp["seqlens"]), case.params.max_seqlen, 0)
     del case
     torch.cuda.empty_cache()
     assert np.all(np.isfinite(got))
