@@ -49,18 +49,26 @@ inline PlanArgs plan_args(const Plan& p, const int32_t* seqlens, void* workspace
   return a;
 }
 
-// LDS the planner needs at least: reduction scratch; more lets it keep split_off on chip
+// LDS the planner needs at least: reduction scratch; more lets it keep the clamped lengths
+// and split_off on chip
 constexpr int kPlanLdsMin = 64;
+// sequences per thread whose page counts stay in registers (the first 256 * kPlanRegs; any
+// further ones are re-read from seqlens)
+constexpr int kPlanRegs = 4;
 
 namespace plan_detail {
 
 __device__ __forceinline__ long long max64(long long x, long long y) { return x > y ? x : y; }
 __device__ __forceinline__ long long min64(long long x, long long y) { return x < y ? x : y; }
 
-// pages of sequence b (lengths outside [0, max_seqlen] are clamped)
-__device__ __forceinline__ int pages_of(const PlanArgs& a, int b) {
-  const int L = min(max(a.seqlens[b], 0), a.max_seqlen);
-  return (L + kPage - 1) / kPage;
+// length of sequence b clamped to [0, max_seqlen]
+__device__ __forceinline__ int clamped_len(const PlanArgs& a, int b) {
+  return min(max(a.seqlens[b], 0), a.max_seqlen);
+}
+__device__ __forceinline__ int pages_of_len(int L) { return (L + kPage - 1) / kPage; }
+// ceil(p / c) for 0 <= p, 1 <= c < 2^21 (32-bit unsigned division)
+__device__ __forceinline__ int items_of(int p, int c) {
+  return (int)(((unsigned)p + (unsigned)c - 1u) / (unsigned)c);
 }
 
 // sum / max over the 256 threads; red: 4 slots of LDS (reused after a barrier)
@@ -84,32 +92,50 @@ __device__ __forceinline__ long long block_max(long long v, long long* red) {
 }  // namespace plan_detail
 
 // Called by all 256 threads of one workgroup; lds: lds_bytes >= kPlanLdsMin of LDS, 8-byte
-// aligned.
+// aligned.  The plan workgroup runs beside the prologue's own workgroups, so its latency is
+// kept short: one read of seqlens, page counts in registers, a search range of a few steps.
 __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_bytes) {
   using namespace plan_detail;
   long long* red = static_cast<long long*>(lds);     // [4]
   int* wsum = reinterpret_cast<int*>(red + 4);       // [4]
-  int* so_lds = wsum + 4;                            // split_off copy, if it fits
-  const bool so_in_lds = (long long)(a.B + 1) * 4 <= lds_bytes - kPlanLdsMin;
+  int* so_lds = wsum + 4;                            // split_off copy [B + 1], if it fits
+  int* len_lds = so_lds + (a.B + 1);                 // clamped lengths [B], if they fit
+  const bool on_chip = (long long)(2 * a.B + 1) * 4 <= lds_bytes - kPlanLdsMin;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  int len[kPlanRegs];  // clamped lengths of sequences tid + 256 i
+#pragma unroll
+  for (int i = 0; i < kPlanRegs; ++i) {
+    const int b = tid + 256 * i;
+    len[i] = b < a.B ? clamped_len(a, b) : 0;
+  }
+  // f(pages of b) for every sequence this thread owns (b = tid, tid + 256, ...)
+  auto for_each = [&](auto&& f) {
+#pragma unroll
+    for (int i = 0; i < kPlanRegs; ++i) f(pages_of_len(len[i]));
+    for (int b = tid + 256 * kPlanRegs; b < a.B; b += 256) f(pages_of_len(clamped_len(a, b)));
+  };
 
   // ---- pages per item
   int c = a.forced_pages;
   if (c == 0) {
-    long long P = 0, maxp = 0;
-    for (int b = tid; b < a.B; b += 256) {
-      const int p = pages_of(a, b);
+    long long P = 0, maxp = 0, nonempty = 0;
+    for_each([&](int p) {
       P += p;
       maxp = max64(maxp, p);
-    }
+      nonempty += p > 0;
+    });
     P = block_sum(P, red);
+    nonempty = block_sum(nonempty, red);
     maxp = max64(block_max(maxp, red), 1);
-    // W(c) >= P / c, so the answer is at least ceil(P / target)
+    // W(c) = sum_b ceil(p_b / c) lies in [P / c, P / c + nonempty), so the answer is at
+    // least ceil(P / target), and c = ceil(P / (target - nonempty)) already fits
     long long lo = min64(max64((P + a.target - 1) / a.target, 1), maxp), hi = maxp;
+    if (a.target > nonempty) hi = min64(hi, max64((P + (a.target - nonempty) - 1) / (a.target - nonempty), lo));
     while (lo < hi) {  // uniform: every thread holds the same lo, hi
-      const long long mid = lo + (hi - lo) / 2;
+      const int mid = (int)(lo + (hi - lo) / 2);
       long long n = 0;
-      for (int b = tid; b < a.B; b += 256) n += (pages_of(a, b) + mid - 1) / mid;
+      for_each([&](int p) { n += items_of(p, mid); });
       n = block_sum(n, red);
       if (n <= a.target) hi = mid;
       else lo = mid + 1;
@@ -121,7 +147,13 @@ __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_byte
   int carry = 0;
   for (int base = 0; base < a.B; base += 256) {
     const int b = base + tid;
-    const int n = b < a.B ? (pages_of(a, b) + c - 1) / c : 0;
+    const int i = base / 256;
+    int L = 0;  // (a select chain: a run-time index into len[] would put it in scratch)
+#pragma unroll
+    for (int j = 0; j < kPlanRegs; ++j)
+      if (i == j) L = len[j];
+    if (i >= kPlanRegs && b < a.B) L = clamped_len(a, b);
+    const int n = items_of(pages_of_len(L), c);
     int x = n;  // inclusive scan over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -135,14 +167,17 @@ __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_byte
     for (int k = 0; k < w; ++k) off += wsum[k];
     if (b < a.B) {
       a.split_off[b] = off;
-      if (so_in_lds) so_lds[b] = off;
+      if (on_chip) {
+        so_lds[b] = off;
+        len_lds[b] = L;
+      }
     }
     carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
   }
   const int W = carry;
   if (tid == 0) {
     a.split_off[a.B] = W;
-    if (so_in_lds) so_lds[a.B] = W;
+    if (on_chip) so_lds[a.B] = W;
     a.hdr[0] = W;
     a.hdr[1] = c;
     a.hdr[2] = a.slots;
@@ -151,7 +186,7 @@ __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_byte
   __syncthreads();  // split_off complete (LDS and global) for the searches below
 
   // ---- dispatch table: the sequence of an item is the last b with split_off[b] <= item
-  const int32_t* so = so_in_lds ? so_lds : a.split_off;
+  const int32_t* so = on_chip ? so_lds : a.split_off;
   const int per = (W + 7) / 8;
   for (int s = tid; s < a.slots; s += 256) {
     int item = s;
@@ -167,7 +202,7 @@ __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_byte
         if (so[mid] <= item) lo = mid;
         else hi = mid;
       }
-      const int L = min(max(a.seqlens[lo], 0), a.max_seqlen);
+      const int L = on_chip ? len_lds[lo] : clamped_len(a, lo);
       const int t0 = (item - so[lo]) * c * kPage;
       e = make_int4(lo, t0, min(L, t0 + c * kPage), item);
     }
