@@ -249,15 +249,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
             tr_pair(buf + pv_off[s2][0][mb], buf + pv_off[s2][1][mb]), pb[s2], O[mb], 0, 0, 0);
   }
 
-  // ---- partial outputs.  O[mb] item i: column d = 128w + 32mb + 8*(i/4) + 4*kg + i%4, head l32
-  bf16* po = part_o + (item * H + h0 + l32) * kDC + 128 * w + 4 * kg;
+  // ---- partial outputs, through LDS so that every global store writes whole rows.  O[mb]
+  // item i is column d = 128w + 32mb + 8*(i/4) + 4*kg + i%4 of head l32: written straight
+  // out, each store instruction would touch 32 head rows with 16 bytes each.  The waves put
+  // the 32 x 512 block (bf16) into the now idle tile ring, then each stores 8 of its 1 KiB
+  // rows, one per instruction.
+  constexpr int kOutPitch = kDC * 2 + 16;  // LDS bytes per head row (+16: 2-way conflicts)
+  static_assert(kHG * kOutPitch <= kBufBytes, "output staging exceeds one ring buffer");
+  __syncthreads();  // every wave is done with the ring
+  char* stage = sm.ring[0];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *(bf16x4*)(po + 32 * mb + 8 * q) =
+      *(bf16x4*)(stage + l32 * kOutPitch + (128 * w + 32 * mb + 8 * q + 4 * kg) * 2) =
           bf16x4{(bf16)O[mb][4 * q], (bf16)O[mb][4 * q + 1], (bf16)O[mb][4 * q + 2],
                  (bf16)O[mb][4 * q + 3]};
+  __syncthreads();
+  bf16* po = part_o + (item * H + h0) * kDC + 8 * lane;
+#pragma unroll
+  for (int j = 0; j < kHG / 4; ++j) {
+    const int r = (kHG / 4) * w + j;
+    *(bf16x8*)(po + (size_t)r * kDC) = *(const bf16x8*)(stage + r * kOutPitch + 16 * lane);
+  }
   if (NB == 1) {
     if (tb == 0 && g16 == 0) {
       const int hs = h0 + 16 * hb + l16;

@@ -361,19 +361,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       for (int c = 0; c < 4; ++c) pa[rr][c] = opaque(pa[rr][c] + step);
   }
 
-  // ---- partial outputs.  O[cb] item e: column 32cb + 8*(e/4) + 4*kg + e%4 of head h0 + l32
-  // (the item index is made opaque here so that the output addresses are formed after the
-  // loop instead of being held in registers across it)
-  asm volatile("" : "+s"(item));
-  bf16* po = part_o + ((size_t)item * H + h0 + l32) * kDC + 4 * kg;
-  float* ml = part_ml + (size_t)item * H * 2;  // [H][2]
+  // ---- partial outputs, through LDS so that every global store writes whole rows.  O[cb]
+  // item e is column 32cb + 8*(e/4) + 4*kg + e%4 of head h0 + l32: written straight out,
+  // each store instruction would touch 32 head rows with 16 bytes each.  The wave puts its 32
+  // rows (bf16) into its own stretch of the now idle LDS, then stores one 1 KiB row per
+  // instruction.
+  constexpr int kOutPitch = kDC * 2 + 16;  // LDS bytes per head row (+16: 2-way conflicts)
+  static_assert(kWaves * 32 * kOutPitch <= sizeof(Smem), "output staging exceeds the LDS");
+  __syncthreads();  // every wave is done with the ring and its query rows
+  char* stage = reinterpret_cast<char*>(&sm) + w * 32 * kOutPitch;
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *(bf16x4*)(po + 32 * cb + 8 * q) =
+      *(bf16x4*)(stage + l32 * kOutPitch + (32 * cb + 8 * q + 4 * kg) * 2) =
           bf16x4{(bf16)O[cb][4 * q], (bf16)O[cb][4 * q + 1], (bf16)O[cb][4 * q + 2],
                  (bf16)O[cb][4 * q + 3]};
+  __syncthreads();  // (only this wave reads its rows back; the barrier orders the LDS accesses)
+  // the item index is made opaque here so that the output addresses are formed after the
+  // loop instead of being held in registers across it
+  asm volatile("" : "+s"(item));
+  bf16* po = part_o + ((size_t)item * H + h0) * kDC + 8 * lane;
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r)
+    *(bf16x8*)(po + (size_t)r * kDC) = *(const bf16x8*)(stage + r * kOutPitch + 16 * lane);
+  float* ml = part_ml + (size_t)item * H * 2;  // [H][2]
   if (kg == 0) {
     ml[(size_t)(h0 + l32) * 2 + 0] = m_ref;
     ml[(size_t)(h0 + l32) * 2 + 1] = l_run;
