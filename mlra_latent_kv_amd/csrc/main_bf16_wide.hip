@@ -156,7 +156,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   if (b < 0) return;  // slot without a work item
   const int t_begin = wi.y, t_end = wi.z;  // page-aligned start, never empty
   int item = wi.w;  // index of the partial results
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a uniform value: the LDS destinations of the tile loads (M0) depend on it,
+  // and from a value the compiler cannot prove uniform every load needs a v_readfirstlane
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, kg = lane >> 5;
   const int h0 = hq * kHeadsWG + 32 * w;  // this wave's heads
 
@@ -305,9 +308,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       for (int i = 0; i < 16; ++i)
         acc[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? acc[i] : -INFINITY;
     }
-    float mx = acc[0];
+    // row max as a tree of depth 3 (a linear chain of 15 is 15 dependent VALU steps)
+    float t5[5];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
+    for (int j = 0; j < 5; ++j) t5[j] = fmaxf(fmaxf(acc[3 * j], acc[3 * j + 1]), acc[3 * j + 2]);
+    float mx = fmaxf(fmaxf(fmaxf(t5[0], t5[1]), t5[2]), fmaxf(fmaxf(t5[3], t5[4]), acc[15]));
     mx = max_xor32(mx);  // every tile holds a valid token: mx finite
     if (k == 0) {
       m_ref = mx;  // O and l are still zero
@@ -327,15 +332,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     // k-half kg) item e of step ks <-> token 16*ks + 8*(e/4) + 4*kg + e%4: the lane's own
     // scores, items 8*ks + e.  The second step's weights are computed in the shadow of the
     // first step's MFMAs.
-    bf16x8 pb[2];
+    // Weights in packed pairs (items i, i + 1: one conversion); the row sum is taken over the
+    // rounded weights the MFMA uses, as a dot product of each pair with (1, 1).
+    uint32_t pw[2][4];
     float psum = 0.0f;
-    auto weight = [&](int i) {
-      const bf16 p = (bf16)__builtin_amdgcn_exp2f(acc[i] - m_ref);
-      pb[i >> 3][i & 7] = p;
-      psum += (float)p;  // normalise with the rounded weights the MFMA uses
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    auto weight2 = [&](int i) {
+      const bf16x2 p = __builtin_convertvector(
+          f32x2{__builtin_amdgcn_exp2f(acc[i] - m_ref), __builtin_amdgcn_exp2f(acc[i + 1] - m_ref)},
+          bf16x2);
+      pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
+      psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
     };
 #pragma unroll
-    for (int i = 0; i < 8; ++i) weight(i);
+    for (int i = 0; i < 8; i += 2) weight2(i);
+    bf16x8 pb[2];
+    pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]});
 
     // ---- O^T[d][h] += V^T P^T, K-step-major over the 16 column blocks, operands kPvAhead
     // reads ahead
@@ -344,7 +356,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       if (i + kPvAhead < 32) vq[(i + kPvAhead) % (kPvAhead + 1)] = v_tile(i + kPvAhead);
       O[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i % (kPvAhead + 1)], pb[i >> 4],
                                                          O[i & 15], 0, 0, 0);
-      if (i < 8) weight(8 + i);
+      if (i < 4) weight2(8 + 2 * i);
+      if (i == 3) pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[1][0], pw[1][1], pw[1][2], pw[1][3]});
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += sum_xor32(psum);
