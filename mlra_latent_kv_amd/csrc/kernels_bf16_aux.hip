@@ -55,6 +55,16 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
   const int c0 = (cb * kPCols) % dcb;          // first column inside the branch
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
+  // rotary part of the query, rotated at position L_b - 1 (angles in fp64), spread over the
+  // column-block workgroups of the head: with d_c = 512 (kRows * dr / 2 = 1024 = 256 *
+  // gridDim.z) every thread has at most one (row, pair) item.  Its loads go out with the
+  // weight loads, so the kernel makes one memory round trip, not two.
+  const int t_r = cb * 256 + tid;
+  const int bb_r = b0 + t_r / (dr / 2), k_r = t_r % (dr / 2);
+  const bool has_r = t_r < kRows * (dr / 2) && bb_r < B;
+  const bf16* xr = q_rope + ((size_t)min(bb_r, B - 1) * H + h) * dr + 2 * (has_r ? k_r : 0);
+  const float x0 = (float)xr[0], x1 = (float)xr[1];
+  const int L_r = seqlens[min(bb_r, B - 1)];
   const bf16* wsrc = w_uk + ((size_t)br * H + h) * dn * dcb + c0;
 #pragma unroll
   for (int j = 0; j < dn * kPCols / 8 / 256; ++j) {
@@ -82,21 +92,12 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
     const int bb = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
     if (bb < B) qcat[((size_t)bb * H + h) * row + col] = (bf16)(acc[i] * qscale);
   }
-  // rotary part of the query, rotated at position L_b - 1 (angles in fp64)
-  // (spread over the column-block workgroups of the head: one (row, pair) per thread)
-  {
-    for (int t = cb * 256 + tid; t < kRows * (dr / 2); t += 256 * (int)gridDim.z) {
-      const int bb = b0 + t / (dr / 2), k = t % (dr / 2);
-      if (bb >= B) continue;
-      const int L = seqlens[bb];
-      float cs, sn;
-      rope_cos_sin(L > 0 ? L - 1 : 0, rf.f[k], &cs, &sn);
-      const bf16* x = q_rope + ((size_t)bb * H + h) * dr + 2 * k;
-      const float x0 = (float)x[0], x1 = (float)x[1];
-      bf16* o = qcat + ((size_t)bb * H + h) * row + dc + 2 * k;
-      o[0] = (bf16)((x0 * cs - x1 * sn) * qscale);
-      o[1] = (bf16)((x0 * sn + x1 * cs) * qscale);
-    }
+  if (has_r) {
+    float cs, sn;
+    rope_cos_sin(L_r > 0 ? L_r - 1 : 0, rf.f[k_r], &cs, &sn);
+    bf16* o = qcat + ((size_t)bb_r * H + h) * row + dc + 2 * k_r;
+    o[0] = (bf16)((x0 * cs - x1 * sn) * qscale);
+    o[1] = (bf16)((x0 * sn + x1 * cs) * qscale);
   }
 }
 
@@ -104,6 +105,8 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
 
 hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(p.H + 1, (p.B + kRows - 1) / kRows, p.dc / kPCols);
+  // one rotary (row, pair) item per thread covers the query's rotary part
+  if (kRows * (p.dr / 2) > 256 * (int)grid.z) return hipErrorInvalidValue;
   RopeFreq rf;
   make_rope_freq(p.dr, a.rope_theta, &rf);
   hipLaunchKernelGGL(k_prologue_bf16, grid, dim3(256), 0, s, (const bf16*)a.q_nope,
