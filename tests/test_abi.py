@@ -198,3 +198,46 @@ def test_plan_code_under_host_sanitizers(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "accepted" in r.stdout
+
+
+def test_plan_checker_rejects_wrong_plans():
+    """The GPU tests judge the device's split plan with test_gpu_parity.check_plan; here that
+    checker is shown to reject plans with a plausible mistake (pages per item one too many or
+    one too few, a shifted item, a wrong split offset, a missed empty slot), on a plan built
+    from its definition."""
+    import numpy as np
+    from test_gpu_parity import check_plan
+    w = I.WORKLOADS["mla_bf16_b32_h128_l4096"]          # wide kernel: XCD-major slots
+    lens = [0, 1, 64, 65, 4000, 0, 129, 3000, 77, 2048]
+    target, slots, max_seqlen = 256, 256, 4000
+
+    def build(c, forced=0):
+        pages = [-(-min(L, max_seqlen) // 64) for L in lens]
+        n = [-(-p // c) for p in pages]
+        so = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+        W = int(so[-1]); per = -(-W // 8)
+        work = np.full((slots, 4), -1, np.int64)
+        work[:, 1:3] = 0
+        for s_ in range(slots):
+            x, g = s_ % 8, s_ // 8
+            item = x * per + g if g < per else W
+            if item < W:
+                b = int(np.searchsorted(so, item, side="right") - 1)
+                t0 = (item - so[b]) * c * 64
+                work[s_] = (b, t0, min(lens[b], t0 + c * 64), item)
+        return {"items": W, "pages": c, "slots": slots, "target": 0 if forced else target,
+                "work": work, "split_off": so}
+
+    good = build(1)                                      # 151 pages fit 256 items at c = 1
+    check_plan(good, w, lens, max_seqlen, 0)
+    check_plan(build(13, forced=5), w, lens, max_seqlen, 5)  # ceil(63 / 5) pages per item
+    bad = []
+    bad.append(build(2))                                 # not the smallest fitting c
+    bad.append(build(12, forced=5))                      # forced page count off by one
+    p = build(1); p["work"] = p["work"].copy(); p["work"][0, 1] += 64; bad.append(p)
+    p = build(1); p["split_off"] = p["split_off"].copy(); p["split_off"][3] += 1; bad.append(p)
+    p = build(1); p["work"] = p["work"].copy()
+    p["work"][np.where(p["work"][:, 0] < 0)[0][0]] = (0, 0, 1, 0); bad.append(p)
+    for i, p in enumerate(bad):
+        with pytest.raises(AssertionError):
+            check_plan(p, w, lens, max_seqlen, 5 if i == 1 else 0)
