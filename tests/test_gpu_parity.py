@@ -240,6 +240,32 @@ def test_zero_length_sequences_write_zeros():
     assert_close(got, oracle_out(inp), "bf16", "zero-length mix")
 
 
+@pytest.mark.parametrize("wname", ["mla_bf16_b32_h128_l4096", "mla_bf16_paged_b64_h32_l1k-32k",
+                                   "mlra4_bf16_b32_h32_l8192", "tiny_mla_f32_b1_h4_l64"])
+def test_all_sequences_empty(wname):
+    """A batch with no tokens at all: the plan has no work item (every dispatch slot idle),
+    the main loops write nothing, and the merge writes exact zeros."""
+    from mlra_latent_kv_amd import harness as H
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=[0, 0, 0])
+    got, case = gpu_out(inp)
+    plan = H.read_plan(case)
+    assert plan["items"] == 0 and np.all(plan["work"][:, 0] == -1)
+    assert list(plan["split_off"]) == [0, 0, 0, 0]
+    assert np.all(got == 0)
+
+
+@pytest.mark.parametrize("wname", ["mla_bf16_b32_h128_l4096", "mla_bf16_paged_b64_h32_l1k-32k",
+                                   "mlra4_bf16_b32_h32_l8192"])
+def test_single_token_sequences(wname):
+    """L = 1 everywhere (one ragged tile per sequence, one item each): the softmax is exactly
+    1 on the single token, checked against the oracle."""
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=[1] * 5, q_gain=I.sharp_q_gain(w))
+    got, _ = gpu_out(inp)
+    assert_close(got, oracle_out(inp), "bf16", f"{wname} L=1")
+
+
 # ----------------------------------------------------------------------------- negative controls
 
 @pytest.mark.parametrize("wname", ["mla_bf16_paged_b64_h32_l1k-32k", "mlra4_bf16_b32_h32_l8192"])
