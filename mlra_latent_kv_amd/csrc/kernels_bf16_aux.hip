@@ -123,7 +123,7 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
 // page, section 矩陣吸收), with the MLRA-4 branch sum carried by the contraction over all
 // 512 latent columns ("[ICLR 2025] MLRA…", section 2.2).
 //
-// One workgroup (4 waves) per (head h, rows b0..b0+R-1), R in {4, 8, 16}:
+// One workgroup (4 waves) per (head h, rows b0..b0+R-1), R in {2, 4, 8, 16}:
 //  1. the W_UV rows of the head go to LDS by direct-to-LDS loads (one contiguous 32 KiB block
 //     per wave: wave w owns latent columns 128w..128w+127, exactly branch w for MLRA-4);
 //  2. meanwhile the split statistics (M, 1/L) of every (row, branch), then the weighted sum
@@ -144,14 +144,15 @@ constexpr int kCeMaxRows = 16;
 // chunk slots of a 256-byte bank line
 __device__ __forceinline__ int ce_sw(int r, int c) { return c ^ (4 * (r & 3)); }
 
-// R = 4 * NC rows per workgroup; each thread merges NC chunks of one row, 32 chunk loads in
-// flight
-template <int NC>
+// R = 4 * NC / TPC rows per workgroup; each thread merges NC chunks of one row, with 32 chunk
+// loads in flight.  TPC = 2 (two-row blocks, for small batches): two adjacent threads share a
+// chunk, each taking every other split, and add their sums at the end.
+template <int NC, int TPC>
 __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     const bf16* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ split_off, const bf16* __restrict__ w_uv,
     bf16* __restrict__ out, int B, int H, int NB, int dcb, float out_scale) {
-  constexpr int R = 4 * NC;
+  constexpr int R = 4 * NC / TPC;
   struct Smem {
     char wuv[4][128 * kCeRowB];       // per wave: its 128 W_UV rows, chunk-swizzled
     char olat[kCeMaxRows][1024];      // merged latent rows, chunk c at c ^ (row % 16)
@@ -187,7 +188,8 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   // zeros.
   const size_t ml_s = (size_t)NB * H * 2;  // part_ml stride of one work item
   const size_t po_s = (size_t)H * 512;     // part_o stride of one work item
-  const int first = tid * NC, mr = first / 64, mc = first % 64;
+  const int first = (tid / TPC) * NC, mr = first / 64, mc = first % 64;
+  const int z = tid % TPC;  // which of the chunk's threads: takes splits z, z + TPC, ...
   const int mb = b0 + mr, mbr = (8 * mc) / dcb;
   // every load is unconditional, at a written work item (a predicated load leaves the
   // compiler's wait analysis with a full drain at the join); masked values are replaced
@@ -203,32 +205,35 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     const int bb = min(b0 + r, B);
     n_max = max(n_max, split_off[min(bb + 1, B)] - split_off[bb]);
   }
-  constexpr int kU = 32 / NC;  // splits in flight
+  constexpr int kU = 32 / NC;  // splits in flight per thread
   float mv[kU];
   bf16x8 v[kU][NC];
+  // batch starting at split s0 (a multiple of kU * TPC): this thread's splits s0 + TPC*u + z
   auto load_batch = [&](int s0) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) mv[u] = mml[item_of(mu0, mn, s0 + u) * ml_s];
+    for (int u = 0; u < kU; ++u) mv[u] = mml[item_of(mu0, mn, s0 + TPC * u + z) * ml_s];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const size_t it = item_of(mu0, mn, s0 + u);
+      const size_t it = item_of(mu0, mn, s0 + TPC * u + z);
 #pragma unroll
       for (int i = 0; i < NC; ++i) v[u][i] = *(const bf16x8*)(msrc + it * po_s + 8 * i);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      if (s0 + u >= mn) mv[u] = -INFINITY;
+      if (s0 + TPC * u + z >= mn) mv[u] = -INFINITY;
   };
   // ---- 2a. split statistics of (row, branch): M = largest split max, 1/L.  A group of P
   // consecutive lanes per (row, branch) takes splits s = q, q + P, ... and the group merges
-  // its (M, L) pairs with lane shuffles.  The first four (m, l) pairs of a lane are loaded
+  // its (M, L) pairs with lane shuffles (P <= 64: one wave; threads past the R * NB groups
+  // load in-bounds values and drop them).  The first four (m, l) pairs of a lane are loaded
   // ahead of the merge batch (loads complete in order).
   {
-    const int P = 256 / (R * NB);  // 4..64, a power of two
+    const int P = min(64, 256 / (R * NB));  // 4..64, a power of two
     const int pair = tid / P, q = tid % P;
-    const int r = pair / NB, br = pair % NB, b = b0 + r;
+    const bool live = pair < R * NB;
+    const int r = min(pair / NB, R - 1), br = pair % NB, b = b0 + r;
     const int bl = min(b, B - 1);
-    const int u0 = split_off[bl], n = b < B ? split_off[bl + 1] - u0 : 0;
+    const int u0 = split_off[bl], n = live && b < B ? split_off[bl + 1] - u0 : 0;
     const float* ml = part_ml + (size_t)br * H * 2 + h * 2;
     constexpr int kPre = 4;
     float pm[kPre], pl[kPre];
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
         M = mn;
       }
     }
-    if (q == 0) {
+    if (q == 0 && live) {
       sm.stat_m[r][br] = M;
       sm.stat_inv[r][br] = L > 0.0f ? 1.0f / L : 0.0f;
     }
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
 #pragma unroll
     for (int i = 0; i < NC; ++i) acc[i][0] = acc[i][1] = f32x4{};
     const float M = sm.stat_m[mr][mbr], inv = sm.stat_inv[mr][mbr];
-    for (int s0 = 0; s0 < n_max; s0 += kU) {
+    for (int s0 = 0; s0 < n_max; s0 += kU * TPC) {
       if (s0 > 0) load_batch(s0);
       float wt[kU];
 #pragma unroll
@@ -298,9 +303,19 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
                                      (float)v[u][i][7]};
         }
     }
+    if (TPC == 2) {  // the chunk's two threads are adjacent lanes: add their halves
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[i][0][e] += __shfl_xor(acc[i][0][e], 1, 64);
+          acc[i][1][e] += __shfl_xor(acc[i][1][e], 1, 64);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < NC; ++i)
-      *(bf16x8*)(sm.olat[mr] + 16 * ((mc + i) ^ (mr & 15))) =
+      if (z == 0)
+        *(bf16x8*)(sm.olat[mr] + 16 * ((mc + i) ^ (mr & 15))) =
           bf16x8{(bf16)acc[i][0][0], (bf16)acc[i][0][1], (bf16)acc[i][0][2], (bf16)acc[i][0][3],
                  (bf16)acc[i][1][0], (bf16)acc[i][1][1], (bf16)acc[i][1][2], (bf16)acc[i][1][3]};
   }
@@ -364,18 +379,20 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
 
 }  // namespace
 
-// rows per workgroup: 16, or 8 where 16 would leave CUs without a workgroup, or 4 for
-// batches of at most 4 (no thread idles on absent rows)
+// rows per workgroup: the largest of 16, 8, 4 that still gives every CU a workgroup, else 2
+// (fewer rows per workgroup read each head's W_UV more often, mostly from L2)
 int combine_epilogue_rows(int B, int H) {
-  if (B <= 4) return 4;
-  return (long)H * ((B + 15) / 16) >= 256 ? 16 : 8;
+  for (int R = 16; R > 2; R /= 2)
+    if ((long)H * ((B + R - 1) / R) >= 256) return R;
+  return 2;
 }
 
 hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const int R = combine_epilogue_rows(p.B, p.H);
   const unsigned blocks = (unsigned)(p.H * ((p.B + R - 1) / R));
-  auto kern = R == 16 ? k_combine_epilogue_bf16<4>
-              : R == 8 ? k_combine_epilogue_bf16<2> : k_combine_epilogue_bf16<1>;
+  auto kern = R == 16 ? k_combine_epilogue_bf16<4, 1>
+              : R == 8 ? k_combine_epilogue_bf16<2, 1>
+              : R == 4 ? k_combine_epilogue_bf16<1, 1> : k_combine_epilogue_bf16<1, 2>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, (const bf16*)a.part_o, a.part_ml,
                      a.split_off, (const bf16*)a.w_uv, (bf16*)a.out, p.B, p.H, p.NB, p.dcb,
                      a.out_scale);

@@ -158,18 +158,23 @@ def test_split_count_invariance(wname):
 
 
 # Shapes that drive every variant of the fused split merge + W_UV epilogue: row blocks of 16,
-# 8 and 4 (partial last blocks included), several batches of splits per thread, split
-# statistics with more than four splits per statistics lane, and rows with one split next to
-# rows with many in the same workgroup (a variable split count per row).
+# 8, 4 and 2 (partial last blocks included; the row count is the largest that still gives 256
+# workgroups), several batches of splits per thread, split statistics with more than four
+# splits per statistics lane, two threads per chunk (2-row blocks), and rows with one split
+# next to rows with many in the same workgroup (a variable split count per row).
 FUSED_CASES = [
-    # MLA, 20 rows -> 16-row blocks (second one partial), 71 splits (> 4 per lane of 16)
+    # MLA H=128, 20 rows -> 16-row blocks (second one partial), 71 splits (> 4 per lane of 16)
     ("mla_bf16_b32_h128_l4096", [4500, 40, 700, 5, 64, 129, 1, 2100, 999, 333, 77, 18, 300, 250,
                                  64, 65, 1000, 1, 30, 640], 71),
-    # MLRA-4, 120 rows -> 16-row blocks, 4 lanes per (row, branch), 18 splits
+    # MLRA-4 H=32, 120 rows -> 16-row blocks, 4 lanes per (row, branch), 18 splits
     ("mlra4_bf16_b32_h32_l8192", [1100] + [37 + (11 * i) % 90 for i in range(119)], 18),
-    # MLA, 4 rows -> 4-row blocks, 41 splits (two batches of 32)
+    # MLA H=128, 12 rows -> 8-row blocks (second partial), 40 splits (three batches of 16)
+    ("mla_bf16_b32_h128_l4096", [2500, 64, 1, 2000, 700, 33, 1500, 65, 128, 2560, 3, 900], 40),
+    # MLRA-4 H=32, 42 rows -> 4-row blocks (last partial), 9 splits
+    ("mlra4_bf16_b32_h32_l8192", [550 - 13 * i for i in range(42)], 9),
+    # MLA H=128, 4 rows -> 2-row blocks (two threads per chunk), 41 splits
     ("mla_bf16_paged_b4_h128_l131072", [2600, 64, 1, 2000], 41),
-    # MLRA-4, 3 rows -> 4-row blocks, 8 splits
+    # MLRA-4 H=32, 3 rows -> 2-row blocks (second partial), 8 splits
     ("mlra4_bf16_b32_h32_l8192", [900, 1, 450], 8),
 ]
 
