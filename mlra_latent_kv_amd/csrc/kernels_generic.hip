@@ -258,7 +258,7 @@ hipError_t launch_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, i
 }
 
 // ----------------------------------------------------------------------------- fp32 main loop
-// Generic SIMT split-K loop for small fp32 shapes: one wave per (sequence, split, head).
+// Generic SIMT split-K loop for small fp32 shapes: one wave per (work item, head).
 // Lane t of a 64-token tile computes that token's scores for every branch; the online
 // softmax keeps (m, l) per branch; lane d accumulates latent-space output columns.
 __global__ __launch_bounds__(64) void k_main_f32(

@@ -1,7 +1,8 @@
 // Split-K main loop of the absorbed MLA / MLRA-4 decode step for gfx950 (bf16 in, fp32 acc).
 //
-// Work item = (sequence b, sequence split s, group of 32 heads).  The workgroup streams the
-// split's cached rows [c_KV (512) | k_rope (64)] in 32-token tiles through a ring of LDS
+// One workgroup per (work item of the split plan: sequence b, tokens [t_begin, t_end); group
+// of 32 heads).  The workgroup streams the item's cached rows [c_KV (512) | k_rope (64)] in
+// 32-token tiles through a ring of LDS
 // buffers filled by direct-to-LDS buffer loads (no staging registers, rows past the end of
 // the sequence read back as zeros), and per tile computes
 //   S  = q_cat . tile^T       scores of 32 heads x 32 tokens (MFMA 32x32x16 bf16)

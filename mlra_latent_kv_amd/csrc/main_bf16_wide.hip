@@ -6,7 +6,8 @@
 // value), organised so that each cached tile crosses HBM -> LDS once for 128 heads and
 // every LDS byte read feeds as many MFMA operations as the register file allows:
 //
-//  * one workgroup of 4 waves per CU handles (sequence b, split s, heads 128q..128q+127);
+//  * one workgroup of 4 waves per CU handles (work item: sequence b, tokens [t_begin,
+//    t_end); heads 128q..128q+127);
 //    wave w owns 32 heads outright: their scores, softmax state and the full 512-column
 //    latent output O^T (16 accumulator blocks of 32 columns x 32 heads, 256 registers,
 //    which one wave per SIMD can hold in the accumulation registers).  The absorbed query's
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
 
     // ---- softmax.  D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4.
     const int valid = min(kTT, t_end - t_begin - kTT * k);
-    if (valid < kTT) {  // last tile of a ragged split; the padding above covers both paths
+    if (valid < kTT) {  // last tile of a ragged item; the padding above covers both paths
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         acc[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? acc[i] : -INFINITY;
