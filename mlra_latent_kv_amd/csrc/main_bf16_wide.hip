@@ -16,10 +16,10 @@
 //  * MFMA 32x32x16 throughout: a 1 KiB operand read from LDS feeds 32K multiply-adds, twice
 //    what the 16x16x32 shape gets from the same read, so LDS traffic per tile is half that of
 //    a 16-heads-per-wave layout.
-//  * tiles of 32 tokens stream through a ring of 3 LDS buffers by direct-to-LDS loads, so
-//    two tiles are in flight while one is consumed; the barrier per tile only recycles the
-//    buffer the waves finished with.
-//  * scores S^T[t][h] = tile . q_cat^T (two accumulation chains over 36 K-steps of 16
+//  * tiles of 32 tokens stream through a ring of 3 LDS buffers by direct-to-LDS loads, in a
+//    software pipeline: while tile k + 1 is scored, tile k's softmax runs between its score
+//    MFMAs, then tile k's values are summed, and tile k + 2 is in flight.
+//  * scores S^T[t][h] = tile . q_cat^T (one accumulation chain over 36 K-steps of 16
 //    columns); the probabilities go register-direct into the value product
 //    O^T += V^T P^T (token order inside a K-step permuted to match the score layout; value
 //    operand read with ds_read_b64_tr_b16 from the token-major tile).
@@ -197,21 +197,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     for (int t = 0; t < kQLdsSteps; ++t)
       *(bf16x8*)(qlds + qr_off + 4096 * t) = *(const bf16x8*)(qrow + 16 * (kQRegSteps + t));
   }
-  // Tile 0 lands together with the query.  Draining the counter here also tells the
-  // compiler's wait analysis that the query registers are complete, so no wait on them
-  // (which would also wait on younger tile loads) reaches the loop.
+  // Tile 0 lands together with the query; tile 1 goes out before the wait.  (The explicit
+  // wait also tells the compiler's wait analysis that the query registers are complete, so
+  // no wait on them, which would also wait on younger tile loads, reaches the loop.)
   issue(0, page_of(0));
-  wait_vmcnt<0>();
-  for (int k = 1; k < kAhead && k < n_tiles; ++k) issue(k, page_of(k));
+  if (n_tiles > 1) {
+    issue(1, page_of(1));
+    wait_vmcnt<kIssues>();
+  } else {
+    wait_vmcnt<0>();
+  }
 
   // Score reads (A = tile, M = tokens): token l32, chunk 2j + kg for latent K-step j.  The
   // swizzle permutes within aligned 16-chunk groups and repeats every 16 rows, so
   // j = 8u + j' adds 256u bytes.  Rotary K-step 32 + j: rotary chunk 2j + kg.
   //
-  // The read addresses of the current tile's buffer are carried from tile to tile (advanced
-  // by one buffer, or wrapped to the first, at the end of each tile) and kept opaque to the
-  // optimiser: every read is one of them plus a constant in the instruction's offset field,
-  // and no separate per-lane offsets stay live next to them.
+  // The read addresses of a tile's buffer are carried from tile to tile (advanced by one
+  // buffer, or wrapped to the first) and kept opaque to the optimiser: every read is one of
+  // them plus a constant in the instruction's offset field, and no separate per-lane offsets
+  // stay live next to them.  qa / ra follow the tile being scored, pa the tile whose values
+  // are being summed (one tile behind).
   const uint32_t buf0 = lds_addr(ring[0]);
   uint32_t qa[8], ra[4], pa[2][4];
 #pragma unroll
@@ -231,35 +236,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       pa[rr][c] = buf0 + lat_piece<Sw32>(4 * kg + (li >> 2) + 8 * rr,
                                          32 * c + 16 * (G & 1) + 4 * (li & 3));
   const uint32_t qla = lds_addr(qlds) + qr_off;
+  // buffer after the one at kt (0, 1, 2, 0, ...)
+  auto next_buf = [](int kt) -> int32_t {
+    return kt % kRing == kRing - 1 ? -(kRing - 1) * kBufBytes : kBufBytes;
+  };
 
   float m_ref = -INFINITY, l_run = 0.0f;  // per head l32 (both k-halves hold the same)
   f32x16 O[16];
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) O[cb] = f32x16{};
 
-  for (int k = 0; k < n_tiles; ++k) {
-    // page of the tile issued below, read before the barrier (whose lgkmcnt(0) covers it) so
-    // that no scalar load is in flight during the tile's LDS reads: scalar and LDS reads
-    // share one counter and a pending scalar load would force every LDS wait to zero
-    const int32_t pg = k + kAhead < n_tiles ? page_of(k + kAhead) : 0;
-    // this wave's loads of tile k are done once only the younger tiles' loads remain
-    static_assert(kAhead == 2, "wait counts below assume two tiles in flight");
-    if (k + 1 < n_tiles) {
-      wait_vmcnt<kIssues>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // tile k landed for every wave; the buffer of tile k-1 is free
-
-    // ---- S^T[t][h] for the tile's 32 tokens (M) and the wave's 32 heads (N)
+  // ---- S^T[t][h] of one tile for its 32 tokens (M) and the wave's 32 heads (N), one
+  // accumulation chain over 36 K-steps (the hardware orders dependent MFMAs itself).  Tile
+  // operands, and the query operands kept in LDS, are read kQkAhead K-steps ahead.  mid(j)
+  // runs after MFMA j: the previous tile's softmax and the next tile's loads are placed
+  // there, in the shadow of the score MFMAs.
+  constexpr int kQkAhead = 4;
+  constexpr int kQq = kQkAhead + 1;
+  auto scores = [&](f32x16& S, auto&& mid) {
     auto a_tile = [&](int j) -> bf16x8 {
       return j < 32 ? lds_read16_at(qa[j & 7] + 256 * (j >> 3)) : lds_read16_at(ra[j - 32]);
     };
-    // tile operands, and the query operands kept in LDS, are read kQkAhead K-steps ahead
-    constexpr int kQkAhead = 4;
-    constexpr int kIssueStep = 2;
-    constexpr int kQq = kQkAhead + 1;
-    f32x16 acc2[2];
     bf16x8 aq[kQq], qq[kQq];
     auto prefetch = [&](int j) {
       aq[j % kQq] = a_tile(j);
@@ -269,110 +266,163 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     for (int j = 0; j < kQkAhead; ++j) prefetch(j);
 #pragma unroll
     for (int j = 0; j < kQSteps; ++j) {
-      // the next tile's loads go out behind the first score MFMAs, whose execution covers
-      // the address set-up
-      if (j == kIssueStep && k + kAhead < n_tiles) issue(k + kAhead, pg);
       if (j + kQkAhead < kQSteps) prefetch(j + kQkAhead);
       const bf16x8 qv = j < kQRegSteps ? qb[j < kQRegSteps ? j : 0] : qq[j % kQq];
-      if (j < 2)
-        mfma_qk_first(acc2[j & 1], aq[j % kQq], qv);
+      if (j == 0)
+        mfma_qk_first(S, aq[j % kQq], qv);
       else
-        mfma_qk(acc2[j & 1], aq[j % kQq], qv);
+        mfma_qk(S, aq[j % kQq], qv);
       // keep the written order: the scheduler would otherwise hoist more operand reads than
-      // the VGPRs left next to the query hold
+      // the VGPRs left next to the query hold, or move the softmax pieces across MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      mid(j);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    // value operands of the first column blocks, read while the softmax runs; operand i is
-    // K-step i / 16 of column block i % 16
+  // ---- softmax of tile kt's scores S.  D layout: lane (head l32, half kg), item i -> token
+  // 8*(i/4) + 4*kg + i%4.  head(): row max, lazy raise of the running max (rescaling O);
+  // weight2(i): weights of items i, i + 1 in a packed pair (one conversion), the row sum
+  // taken over the rounded weights the MFMA uses as a dot product of the pair with (1, 1).
+  // B operand of the value product (K = 16 tokens per step, N = heads): lane (head l32,
+  // k-half kg) item e of step ks <-> token 16*ks + 8*(e/4) + 4*kg + e%4: the lane's own
+  // scores, items 8*ks + e.
+  uint32_t pw[2][4];
+  float psum = 0.0f;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  // raise of the running max decided in soft_head, applied to O and l by rescale() before
+  // the tile's values are added (the weights already use the raised max)
+  bool raise = false;
+  float a_raise = 1.0f;
+  auto soft_head = [&](const f32x16& S, int kt) {
+    // row max as a tree of depth 3 (a linear chain of 15 is 15 dependent VALU steps)
+    float t5[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) t5[j] = fmaxf(fmaxf(S[3 * j], S[3 * j + 1]), S[3 * j + 2]);
+    float mx = fmaxf(fmaxf(fmaxf(t5[0], t5[1]), t5[2]), fmaxf(fmaxf(t5[3], t5[4]), S[15]));
+    mx = max_xor32(mx);  // every tile holds a valid token: mx finite
+    raise = false;
+    if (kt == 0) {
+      m_ref = mx;  // O and l are still zero
+    } else if (__ballot(mx > m_ref + kLazyTau) != 0) {
+      const float m_new = fmaxf(m_ref, mx);
+      a_raise = exp2f(m_ref - m_new);
+      m_ref = m_new;
+      raise = true;
+    }
+    psum = 0.0f;
+  };
+  auto rescale = [&]() {
+    if (raise) {
+      // one block at a time through VGPRs (O lives in the accumulation registers)
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb) {
+        scale_acc(O[cb], a_raise);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run *= a_raise;
+    }
+  };
+  auto weight2 = [&](const f32x16& S, int i) {
+    const bf16x2 p = __builtin_convertvector(
+        f32x2{__builtin_amdgcn_exp2f(S[i] - m_ref), __builtin_amdgcn_exp2f(S[i + 1] - m_ref)},
+        bf16x2);
+    pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
+    psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
+  };
+
+  // ---- O^T[d][h] += V^T P^T over one tile (its buffer at pa), K-step-major over the 16
+  // column blocks, operands kPvAhead reads ahead; then pa moves on to the next buffer
+  constexpr int kPvAhead = 4;
+  auto values = [&](int kt) {
     auto v_tile = [&](int i) -> bf16x8 {
       const int cb = i & 15, ks = i >> 4;
       const uint32_t o = 256 * (cb >> 2) + 16384 * ks;
       return tr_pair_at(pa[0][cb & 3] + o, pa[1][cb & 3] + o);
     };
-    constexpr int kPvAhead = 4;
     bf16x8 vq[kPvAhead + 1];
 #pragma unroll
     for (int i = 0; i < kPvAhead; ++i) vq[i] = v_tile(i);
-
-    // 32x32x16 result -> VALU read: 12 wait states (fenced so that no read of acc2 is
-    // scheduled above the padding)
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 11");
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 acc = acc2[0] + acc2[1];
-
-    // ---- softmax.  D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4.
-    const int valid = min(kTT, t_end - t_begin - kTT * k);
-    if (valid < kTT) {  // last tile of a ragged item; the padding above covers both paths
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        acc[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? acc[i] : -INFINITY;
-    }
-    // row max as a tree of depth 3 (a linear chain of 15 is 15 dependent VALU steps)
-    float t5[5];
-#pragma unroll
-    for (int j = 0; j < 5; ++j) t5[j] = fmaxf(fmaxf(acc[3 * j], acc[3 * j + 1]), acc[3 * j + 2]);
-    float mx = fmaxf(fmaxf(fmaxf(t5[0], t5[1]), t5[2]), fmaxf(fmaxf(t5[3], t5[4]), acc[15]));
-    mx = max_xor32(mx);  // every tile holds a valid token: mx finite
-    if (k == 0) {
-      m_ref = mx;  // O and l are still zero
-    } else if (__ballot(mx > m_ref + kLazyTau) != 0) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float a = exp2f(m_ref - m_new);
-      // one block at a time through VGPRs (O lives in the accumulation registers)
-#pragma unroll
-      for (int cb = 0; cb < 16; ++cb) {
-        scale_acc(O[cb], a);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      l_run *= a;
-      m_ref = m_new;
-    }
-    // B operand of the value product (K = 16 tokens per step, N = heads): lane (head l32,
-    // k-half kg) item e of step ks <-> token 16*ks + 8*(e/4) + 4*kg + e%4: the lane's own
-    // scores, items 8*ks + e.  The second step's weights are computed in the shadow of the
-    // first step's MFMAs.
-    // Weights in packed pairs (items i, i + 1: one conversion); the row sum is taken over the
-    // rounded weights the MFMA uses, as a dot product of each pair with (1, 1).
-    uint32_t pw[2][4];
-    float psum = 0.0f;
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-    auto weight2 = [&](int i) {
-      const bf16x2 p = __builtin_convertvector(
-          f32x2{__builtin_amdgcn_exp2f(acc[i] - m_ref), __builtin_amdgcn_exp2f(acc[i + 1] - m_ref)},
-          bf16x2);
-      pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
-      psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
-    };
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) weight2(i);
-    bf16x8 pb[2];
-    pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]});
-
-    // ---- O^T[d][h] += V^T P^T, K-step-major over the 16 column blocks, operands kPvAhead
-    // reads ahead
+    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]});
+    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[1][0], pw[1][1], pw[1][2], pw[1][3]});
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (i + kPvAhead < 32) vq[(i + kPvAhead) % (kPvAhead + 1)] = v_tile(i + kPvAhead);
-      O[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i % (kPvAhead + 1)], pb[i >> 4],
+      O[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i % (kPvAhead + 1)], i < 16 ? pb0 : pb1,
                                                          O[i & 15], 0, 0, 0);
-      if (i < 4) weight2(8 + 2 * i);
-      if (i == 3) pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[1][0], pw[1][1], pw[1][2], pw[1][3]});
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += sum_xor32(psum);
-
-    // next tile's buffer
-    const int32_t step = k % kRing == kRing - 1 ? -(kRing - 1) * kBufBytes : kBufBytes;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qa[j] = opaque(qa[j] + step);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ra[j] = opaque(ra[j] + step);
+    const int32_t step = next_buf(kt);
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
       for (int c = 0; c < 4; ++c) pa[rr][c] = opaque(pa[rr][c] + step);
+  };
+  auto advance_qk = [&](int kt) {  // score reads move on from tile kt's buffer
+    const int32_t step = next_buf(kt);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qa[j] = opaque(qa[j] + step);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = opaque(ra[j] + step);
+  };
+
+  // ---- software pipeline over the tiles.  Fill: tile 0's scores.  Iteration k: the scores
+  // of tile k + 1 with tile k's softmax (and tile k + 2's loads) in the shadow of their MFMAs,
+  // then tile k's value product.  The ring holds tile k (values), tile k + 1 (scores) and
+  // tile k + 2 (in flight): one tile in flight, issued a full iteration before it is needed.
+  lds_barrier();  // tile 0 landed for every wave
+  // scores of even tiles in Sa, odd tiles in Sb (two iterations per trip, no register copies)
+  f32x16 Sa, Sb;
+  scores(Sa, [](int) {});
+  advance_qk(0);
+  auto step = [&](int k, const f32x16& S_cur, f32x16& S_next) {
+    // page of the tile issued below, read before the barrier (whose lgkmcnt(0) covers it) so
+    // that no scalar load is in flight during the tile's LDS reads: scalar and LDS reads
+    // share one counter and a pending scalar load would force every LDS wait to zero
+    const int32_t pg = k + 2 < n_tiles ? page_of(k + 2) : 0;
+    wait_vmcnt<0>();  // this wave's loads of tile k + 1, the only tile in flight, are done
+    lds_barrier();    // tile k + 1 landed for every wave; tile k - 1's buffer is free
+    scores(S_next, [&](int j) {
+      // the loads of tile k + 2 go out behind the first score MFMAs, whose execution covers
+      // the address set-up; tile k's softmax runs in the shadow of the following ones (its
+      // scores were complete a whole value product ago)
+      if (j == 1 && k + 2 < n_tiles) issue(k + 2, pg);
+      if (j == 3) soft_head(S_cur, k);
+      if (j >= 5 && j <= 19 && (j & 1)) weight2(S_cur, j - 5);
+    });
+    advance_qk(k + 1);
+    rescale();
+    values(k);
+  };
+  int k = 0;
+  for (; k + 2 < n_tiles; k += 2) {
+    step(k, Sa, Sb);
+    step(k + 1, Sb, Sa);
+  }
+  if (k + 1 < n_tiles) {
+    step(k, Sa, Sb);
+    ++k;
+  }
+  // last tile k = n_tiles - 1: its scores are complete (12 wait states after the last score
+  // MFMA: with a single tile they were written just above), rows past the item's end are
+  // masked, and there is no next tile
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 11");
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    f32x16 S = (k & 1) ? Sb : Sa;
+    const int valid = min(kTT, t_end - t_begin - kTT * k);
+    if (valid < kTT) {  // ragged last tile
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        S[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? S[i] : -INFINITY;
+    }
+    soft_head(S, k);
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) weight2(S, i);
+    rescale();
+    values(k);
   }
 
   // ---- partial outputs, through LDS so that every global store writes whole rows.  O[cb]

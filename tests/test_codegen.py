@@ -89,7 +89,9 @@ def _drains_after_issue(blocks, head, members):
     """vmcnt(0) waits on any path from a tile load of the loop to the next pass through the
     loop header (a wait at the top of an iteration, before the next tile goes out, is the
     kernel's own choice; a wait between issuing a tile and the end of the iteration would
-    drain it)."""
+    drain it).  A full wait directly followed by the tile barrier (s_waitcnt lgkmcnt(0);
+    s_barrier) is the kernel's explicit wait for a tile it must have complete (the pipelined
+    loop keeps exactly one tile in flight), not a drain of loads still ahead."""
     index = {b[0]: i for i, b in enumerate(blocks)}
     starts = [(i, j + 1) for i in members for j, x in enumerate(blocks[i][2])
               if "buffer_load" in x and "lds" in x]
@@ -105,7 +107,8 @@ def _drains_after_issue(blocks, head, members):
                 stack.append((i + 1, 0))
             continue
         x = ins[j]
-        if re.match(r"s_waitcnt\s.*vmcnt\(0\)", x):
+        if re.match(r"s_waitcnt\s.*vmcnt\(0\)", x) and not (
+                ins[j + 1:j + 3] == ["s_waitcnt lgkmcnt(0)", "s_barrier"]):
             found.append((blocks[i][0], x))
         m = re.match(r"s_(c)?branch\w*\s+\.(LBB\w+)", x)
         if m:
@@ -152,6 +155,9 @@ def test_drain_scan_sees_a_wait_after_the_issue():
     assert [w[0] for w in _drains_after_issue(*bad)] == ["LBB0_2"]
     good = _main_loop(loop.format(late="").splitlines())  # the wait at the top only
     assert _drains_after_issue(*good) == []
+    # the explicit wait for the one tile in flight, right before the tile barrier
+    barrier = "\ts_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n"
+    assert _drains_after_issue(*_main_loop(loop.format(late=barrier).splitlines())) == []
 
 
 # Wait states an instruction that reads or writes an MFMA's destination registers must stay
