@@ -281,24 +281,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   };
 
   // ---- softmax of tile kt's scores S.  D layout: lane (head l32, half kg), item i -> token
-  // 8*(i/4) + 4*kg + i%4.  head(): row max, lazy raise of the running max (rescaling O);
-  // weight2(i): weights of items i, i + 1 in a packed pair (one conversion), the row sum
-  // taken over the rounded weights the MFMA uses as a dot product of the pair with (1, 1).
+  // 8*(i/4) + 4*kg + i%4.  Each piece below fits between two score MFMAs:
+  //  * soft_max1 / soft_max2: row max as a tree of depth 3 (a linear chain of 15 is 15
+  //    dependent VALU steps), and the lazy raise of the running max, which rescale() then
+  //    applies to O and l before the tile's values are added (the weights already use it);
+  //  * weight_exp / weight_pack: the weights of items i, i + 1, then their conversion to a
+  //    packed pair (one conversion), summed over the rounded weights the MFMA uses as a dot
+  //    product of the pair with (1, 1).
   // B operand of the value product (K = 16 tokens per step, N = heads): lane (head l32,
   // k-half kg) item e of step ks <-> token 16*ks + 8*(e/4) + 4*kg + e%4: the lane's own
   // scores, items 8*ks + e.
   uint32_t pw[2][4];
   float psum = 0.0f;
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  // raise of the running max decided in soft_head, applied to O and l by rescale() before
-  // the tile's values are added (the weights already use the raised max)
   bool raise = false;
   float a_raise = 1.0f;
-  auto soft_head = [&](const f32x16& S, int kt) {
-    // row max as a tree of depth 3 (a linear chain of 15 is 15 dependent VALU steps)
-    float t5[5];
+  float t5[5];
+  auto soft_max1 = [&](const f32x16& S) {
 #pragma unroll
     for (int j = 0; j < 5; ++j) t5[j] = fmaxf(fmaxf(S[3 * j], S[3 * j + 1]), S[3 * j + 2]);
+  };
+  auto soft_max2 = [&](const f32x16& S, int kt) {
     float mx = fmaxf(fmaxf(fmaxf(t5[0], t5[1]), t5[2]), fmaxf(fmaxf(t5[3], t5[4]), S[15]));
     mx = max_xor32(mx);  // every tile holds a valid token: mx finite
     raise = false;
@@ -323,26 +326,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       l_run *= a_raise;
     }
   };
-  auto weight2 = [&](const f32x16& S, int i) {
-    const bf16x2 p = __builtin_convertvector(
-        f32x2{__builtin_amdgcn_exp2f(S[i] - m_ref), __builtin_amdgcn_exp2f(S[i + 1] - m_ref)},
-        bf16x2);
+  float e2[2];
+  auto weight_exp = [&](const f32x16& S, int i) {
+    e2[0] = __builtin_amdgcn_exp2f(S[i] - m_ref);
+    e2[1] = __builtin_amdgcn_exp2f(S[i + 1] - m_ref);
+  };
+  auto weight_pack = [&](int i) {
+    const bf16x2 p = __builtin_convertvector(f32x2{e2[0], e2[1]}, bf16x2);
     pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
     psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
   };
 
   // ---- O^T[d][h] += V^T P^T over one tile (its buffer at pa), K-step-major over the 16
   // column blocks, operands kPvAhead reads ahead; then pa moves on to the next buffer
+  // (the first kPvAhead operands are read by the caller, in the shadow of earlier work)
   constexpr int kPvAhead = 4;
+  bf16x8 vq[kPvAhead + 1];
+  auto v_tile = [&](int i) -> bf16x8 {
+    const int cb = i & 15, ks = i >> 4;
+    const uint32_t o = 256 * (cb >> 2) + 16384 * ks;
+    return tr_pair_at(pa[0][cb & 3] + o, pa[1][cb & 3] + o);
+  };
   auto values = [&](int kt) {
-    auto v_tile = [&](int i) -> bf16x8 {
-      const int cb = i & 15, ks = i >> 4;
-      const uint32_t o = 256 * (cb >> 2) + 16384 * ks;
-      return tr_pair_at(pa[0][cb & 3] + o, pa[1][cb & 3] + o);
-    };
-    bf16x8 vq[kPvAhead + 1];
-#pragma unroll
-    for (int i = 0; i < kPvAhead; ++i) vq[i] = v_tile(i);
     const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]});
     const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[1][0], pw[1][1], pw[1][2], pw[1][3]});
 #pragma unroll
@@ -386,10 +391,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     scores(S_next, [&](int j) {
       // the loads of tile k + 2 go out behind the first score MFMAs, whose execution covers
       // the address set-up; tile k's softmax runs in the shadow of the following ones (its
-      // scores were complete a whole value product ago)
+      // scores were complete a whole value product ago), one piece per MFMA
       if (j == 1 && k + 2 < n_tiles) issue(k + 2, pg);
-      if (j == 3) soft_head(S_cur, k);
-      if (j >= 5 && j <= 19 && (j & 1)) weight2(S_cur, j - 5);
+      if (j == 3) soft_max1(S_cur);
+      if (j == 4) soft_max2(S_cur, k);
+      if (j >= 5 && j <= 20) {
+        if (j & 1)
+          weight_exp(S_cur, j - 5);
+        else
+          weight_pack(j - 6);
+      }
+      // the first operands of tile k's values are read behind the last score MFMAs
+      if (j >= kQSteps - kPvAhead) vq[j - (kQSteps - kPvAhead)] = v_tile(j - (kQSteps - kPvAhead));
     });
     advance_qk(k + 1);
     rescale();
@@ -418,10 +431,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       for (int i = 0; i < 16; ++i)
         S[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? S[i] : -INFINITY;
     }
-    soft_head(S, k);
+    soft_max1(S);
+    soft_max2(S, k);
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) weight2(S, i);
+    for (int i = 0; i < 16; i += 2) {
+      weight_exp(S, i);
+      weight_pack(i);
+    }
     rescale();
+#pragma unroll
+    for (int i = 0; i < kPvAhead; ++i) vq[i] = v_tile(i);
     values(k);
   }
 
