@@ -179,34 +179,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       lb = latent + (int64_t)b * lat_seq + (int64_t)t0 * lat_tok;
       rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
     }
-    issue_tile<Sw32, kWaves>(ring[k % kRing], w, lane, lb, rb, min(kTT, t_end - t0), lat_row_b,
-                             rope_row_b);
+    // valid rows, uniform (the clamp would otherwise become a vector med3, and a buffer
+    // descriptor in vector registers costs a loop per load)
+    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(kTT, t_end - t0)));
+    issue_tile<Sw32, kWaves>(ring[k % kRing], w, lane, lb, rb, valid, lat_row_b, rope_row_b);
   };
 
   // Absorbed query as the B operand of 32x32x16 (N = heads): lane (head l32, k-half kg),
   // K-step j covers q_cat columns 16j..16j+15, the lane's 8 at 16j + 8*kg.  K-steps below
   // kQRegSteps in registers, the rest in qlds (this wave's 32 heads are written and read by
   // this wave only).
-  bf16x8 qb[kQRegSteps];
+  //
+  // Start-up order: tile 0, the query, tile 1, then one wait for all but tile 1, so that the
+  // query and the first tile share one memory latency (with the query's LDS part written
+  // before tile 0 goes out, the two latencies would add up).  Tile 1 goes out even for a
+  // one-tile item, with no valid rows (its loads return zeros without touching memory), so
+  // that the wait is the same on every path: after a branch the compiler's wait analysis
+  // assumes the worst of both sides and would make the query's LDS writes wait for tile 1.
+  // The explicit wait also tells that analysis that the query registers are complete, so no
+  // wait on them, which would also wait on younger tile loads, reaches the loop.
+  const int32_t pg0 = page_of(0), pg1 = n_tiles > 1 ? page_of(1) : pg0;
+  issue(0, pg0);
+  bf16x8 qb[kQRegSteps], qt[kQLdsSteps];
   const uint32_t qr_off = (kg * kHeadsWG + 32 * w + l32) * 16;  // + 4 KiB per LDS K-step
   {
     const bf16* qrow = qcat + ((size_t)b * H + h0 + l32) * kRow + 8 * kg;
 #pragma unroll
     for (int j = 0; j < kQRegSteps; ++j) qb[j] = *(const bf16x8*)(qrow + 16 * j);
 #pragma unroll
-    for (int t = 0; t < kQLdsSteps; ++t)
-      *(bf16x8*)(qlds + qr_off + 4096 * t) = *(const bf16x8*)(qrow + 16 * (kQRegSteps + t));
+    for (int t = 0; t < kQLdsSteps; ++t) qt[t] = *(const bf16x8*)(qrow + 16 * (kQRegSteps + t));
   }
-  // Tile 0 lands together with the query; tile 1 goes out before the wait.  (The explicit
-  // wait also tells the compiler's wait analysis that the query registers are complete, so
-  // no wait on them, which would also wait on younger tile loads, reaches the loop.)
-  issue(0, page_of(0));
-  if (n_tiles > 1) {
-    issue(1, page_of(1));
-    wait_vmcnt<kIssues>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  __builtin_amdgcn_sched_barrier(0);  // every query load ahead of tile 1 (the wait counts on it)
+  issue(1, pg1);
+  wait_vmcnt<kIssues>();
+#pragma unroll
+  for (int t = 0; t < kQLdsSteps; ++t) lds_write16(qlds + qr_off + 4096 * t, qt[t]);
 
   // Score reads (A = tile, M = tokens): token l32, chunk 2j + kg for latent K-step j.  The
   // swizzle permutes within aligned 16-chunk groups and repeats every 16 rows, so

@@ -87,7 +87,7 @@ __device__ __forceinline__ void issue_tile(char* buf, int w, int lane, const bf1
     const int t = R * w + j;
     dma16(rl, buf + t * kLatRowB, t * lat_row_b + 16 * (lane ^ lat_sw<SW>(t)));
   }
-  if (w < 4) {
+  if (NW <= 4 || w < 4) {  // (known true at compile time for up to 4 waves)
     const __amdgpu_buffer_rsrc_t rr = rsrc(rb, valid * rope_row_b);
     const int rt = 8 * w + (lane >> 3);
     dma16(rr, buf + kRopeOff + w * 1024, rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
@@ -119,6 +119,9 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ bf16x8 lds_read16(const char* __restrict__ p) {
   return *(const bf16x8*)p;
 }
+// 16-byte LDS write, with the same alias-scope information as the reads (a write the wait
+// analysis cannot tell apart from the tile loads in flight would first wait for all of them)
+__device__ __forceinline__ void lds_write16(char* __restrict__ p, bf16x8 v) { *(bf16x8*)p = v; }
 __device__ __forceinline__ s16x4 lds_read_tr(const char* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
