@@ -304,9 +304,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   bool raise = false;
   float a_raise = 1.0f;
   float t5[5];
+  // Each piece ends by passing its results through an empty volatile asm, which keeps it
+  // between the score MFMAs (themselves volatile asm) where it is written: otherwise the
+  // compiler sinks the weights past the rescale branch to their use in the value product,
+  // where they would run serially between the two products.
   auto soft_max1 = [&](const f32x16& S) {
 #pragma unroll
     for (int j = 0; j < 5; ++j) t5[j] = fmaxf(fmaxf(S[3 * j], S[3 * j + 1]), S[3 * j + 2]);
+    asm volatile("" : "+v"(t5[0]), "+v"(t5[1]), "+v"(t5[2]), "+v"(t5[3]), "+v"(t5[4]));
   };
   auto soft_max2 = [&](const f32x16& S, int kt) {
     float mx = fmaxf(fmaxf(fmaxf(t5[0], t5[1]), t5[2]), fmaxf(fmaxf(t5[3], t5[4]), S[15]));
@@ -337,11 +342,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   auto weight_exp = [&](const f32x16& S, int i) {
     e2[0] = __builtin_amdgcn_exp2f(S[i] - m_ref);
     e2[1] = __builtin_amdgcn_exp2f(S[i + 1] - m_ref);
+    asm volatile("" : "+v"(e2[0]), "+v"(e2[1]));
   };
   auto weight_pack = [&](int i) {
     const bf16x2 p = __builtin_convertvector(f32x2{e2[0], e2[1]}, bf16x2);
     pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
     psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
+    asm volatile("" : "+v"(pw[i >> 3][(i & 7) >> 1]), "+v"(psum));
   };
 
   // ---- O^T[d][h] += V^T P^T over one tile (its buffer at pa), K-step-major over the 16
