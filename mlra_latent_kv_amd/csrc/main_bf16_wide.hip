@@ -10,15 +10,15 @@
 //    t_end); heads 128q..128q+127);
 //    wave w owns 32 heads outright: their scores, softmax state and the full 512-column
 //    latent output O^T (16 accumulator blocks of 32 columns x 32 heads, 256 registers,
-//    which one wave per SIMD can hold in the accumulation registers).  The absorbed query's
-//    first 384 columns stay in registers, the rest (latent 384..511 and the rotary part) in
-//    LDS.  No per-tile exchange between waves.
+//    which one wave per SIMD can hold in the accumulation registers).  The absorbed query
+//    (576 columns of 32 heads) stays in registers for the whole loop, so the LDS holds tiles
+//    only.  No per-tile exchange between waves.
 //  * MFMA 32x32x16 throughout: a 1 KiB operand read from LDS feeds 32K multiply-adds, twice
 //    what the 16x16x32 shape gets from the same read, so LDS traffic per tile is half that of
 //    a 16-heads-per-wave layout.
-//  * tiles of 32 tokens stream through a ring of 3 LDS buffers by direct-to-LDS loads, in a
+//  * tiles of 32 tokens stream through a ring of 4 LDS buffers by direct-to-LDS loads, in a
 //    software pipeline: while tile k + 1 is scored, tile k's softmax runs between its score
-//    MFMAs, then tile k's values are summed, and tile k + 2 is in flight.
+//    MFMAs, then tile k's values are summed, and tiles k + 2 and k + 3 are in flight.
 //  * scores S^T[t][h] = tile . q_cat^T (one accumulation chain over 36 K-steps of 16
 //    columns); the probabilities go register-direct into the value product
 //    O^T += V^T P^T (token order inside a K-step permuted to match the score layout; value
@@ -39,12 +39,9 @@ using namespace tile;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kHeadsWG = 128;          // heads per workgroup, 32 per wave
-constexpr int kRing = 3;               // tile buffers
-constexpr int kAhead = kRing - 1;      // tiles in flight ahead of the one being consumed
+constexpr int kRing = 4;               // tile buffers: values, scores, two in flight
 constexpr float kLazyTau = 8.0f;       // log2 headroom before the running max is raised
 constexpr int kQSteps = kRow / 16;     // 36 K-steps of 16 columns: 32 latent, 4 rotary
-constexpr int kQRegSteps = 24;         // query K-steps held in registers; the rest in LDS
-constexpr int kQLdsSteps = kQSteps - kQRegSteps;
 constexpr int kIssues = issues_per_wave<kWaves>(true);  // tile loads per wave per tile
 
 // Score MFMAs in VGPR form.  This file is built with MFMAs in their accumulation-register
@@ -135,15 +132,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   // analysis stops telling the tile reads apart from the loads in flight and waits for all
   // of them before the first read of every tile.)
   struct Smem {
-    // query K-steps kQRegSteps.. chunk-major: the 16-byte chunk of K-step kQRegSteps + t,
-    // k-half g, head h at ((2t + g) * 128 + h) * 16, so a wave's 32 heads read 512
-    // consecutive bytes per k-half
-    char qlds[kQLdsSteps * 2 * kHeadsWG * 16];
     char ring[kRing][kBufBytes];
   };
-  __shared__ __align__(16) Smem sm;  // 156 KiB
+  __shared__ __align__(16) Smem sm;  // 144 KiB
   char (&ring)[kRing][kBufBytes] = sm.ring;
-  char* const qlds = sm.qlds;
 
   // XCD-aware mapping.  Blocks are dispatched round-robin over the 8 XCDs: block 8r + x runs
   // head quad r % n_hq of dispatch slot 8(r / n_hq) + x, and the split plan gives XCD x a
@@ -186,34 +178,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   };
 
   // Absorbed query as the B operand of 32x32x16 (N = heads): lane (head l32, k-half kg),
-  // K-step j covers q_cat columns 16j..16j+15, the lane's 8 at 16j + 8*kg.  K-steps below
-  // kQRegSteps in registers, the rest in qlds (this wave's 32 heads are written and read by
-  // this wave only).
+  // K-step j covers q_cat columns 16j..16j+15, the lane's 8 at 16j + 8*kg; all 36 K-steps
+  // in registers.
   //
-  // Start-up order: tile 0, the query, tile 1, then one wait for all but tile 1, so that the
-  // query and the first tile share one memory latency (with the query's LDS part written
-  // before tile 0 goes out, the two latencies would add up).  Tile 1 goes out even for a
-  // one-tile item, with no valid rows (its loads return zeros without touching memory), so
-  // that the wait is the same on every path: after a branch the compiler's wait analysis
-  // assumes the worst of both sides and would make the query's LDS writes wait for tile 1.
-  // The explicit wait also tells that analysis that the query registers are complete, so no
-  // wait on them, which would also wait on younger tile loads, reaches the loop.
-  const int32_t pg0 = page_of(0), pg1 = n_tiles > 1 ? page_of(1) : pg0;
+  // Start-up order: tile 0, the query, tiles 1 and 2, then one wait for all but tiles 1 and
+  // 2, so that the query and the first tile share one memory latency.  Every tile load from
+  // here on goes out unconditionally, past the item's end with no valid rows (such loads
+  // return zeros without touching memory), so that the number of loads in flight, and with
+  // it every wait count, is the same on every path.  The explicit wait also tells the
+  // compiler's wait analysis that the query registers are complete, so no wait on them,
+  // which would also wait on younger tile loads, reaches the loop.
+  // page of tile k, or 0 past the item's end (the block table row ends with the sequence)
+  auto page_or0 = [&](int k) -> int32_t { return k < n_tiles ? page_of(k) : 0; };
+  const int32_t pg0 = page_of(0), pg1 = page_or0(1), pg2 = page_or0(2);
   issue(0, pg0);
-  bf16x8 qb[kQRegSteps], qt[kQLdsSteps];
-  const uint32_t qr_off = (kg * kHeadsWG + 32 * w + l32) * 16;  // + 4 KiB per LDS K-step
+  bf16x8 qb[kQSteps];
   {
     const bf16* qrow = qcat + ((size_t)b * H + h0 + l32) * kRow + 8 * kg;
 #pragma unroll
-    for (int j = 0; j < kQRegSteps; ++j) qb[j] = *(const bf16x8*)(qrow + 16 * j);
-#pragma unroll
-    for (int t = 0; t < kQLdsSteps; ++t) qt[t] = *(const bf16x8*)(qrow + 16 * (kQRegSteps + t));
+    for (int j = 0; j < kQSteps; ++j) qb[j] = *(const bf16x8*)(qrow + 16 * j);
   }
-  __builtin_amdgcn_sched_barrier(0);  // every query load ahead of tile 1 (the wait counts on it)
+  __builtin_amdgcn_sched_barrier(0);  // every query load ahead of tiles 1, 2 (the wait counts on it)
   issue(1, pg1);
-  wait_vmcnt<kIssues>();
-#pragma unroll
-  for (int t = 0; t < kQLdsSteps; ++t) lds_write16(qlds + qr_off + 4096 * t, qt[t]);
+  issue(2, pg2);
+  wait_vmcnt<2 * kIssues>();
 
   // Score reads (A = tile, M = tokens): token l32, chunk 2j + kg for latent K-step j.  The
   // swizzle permutes within aligned 16-chunk groups and repeats every 16 rows, so
@@ -242,7 +230,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     for (int c = 0; c < 4; ++c)
       pa[rr][c] = buf0 + lat_piece<Sw32>(4 * kg + (li >> 2) + 8 * rr,
                                          32 * c + 16 * (G & 1) + 4 * (li & 3));
-  const uint32_t qla = lds_addr(qlds) + qr_off;
   // buffer after the one at kt (0, 1, 2, 0, ...)
   auto next_buf = [](int kt) -> int32_t {
     return kt % kRing == kRing - 1 ? -(kRing - 1) * kBufBytes : kBufBytes;
@@ -255,30 +242,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
 
   // ---- S^T[t][h] of one tile for its 32 tokens (M) and the wave's 32 heads (N), one
   // accumulation chain over 36 K-steps (the hardware orders dependent MFMAs itself).  Tile
-  // operands, and the query operands kept in LDS, are read kQkAhead K-steps ahead.  mid(j)
-  // runs after MFMA j: the previous tile's softmax and the next tile's loads are placed
-  // there, in the shadow of the score MFMAs.
+  // operands are read kQkAhead K-steps ahead.  mid(j) runs after MFMA j: the previous tile's
+  // softmax and the next tile's loads are placed there, in the shadow of the score MFMAs.
   constexpr int kQkAhead = 4;
   constexpr int kQq = kQkAhead + 1;
   auto scores = [&](f32x16& S, auto&& mid) {
     auto a_tile = [&](int j) -> bf16x8 {
       return j < 32 ? lds_read16_at(qa[j & 7] + 256 * (j >> 3)) : lds_read16_at(ra[j - 32]);
     };
-    bf16x8 aq[kQq], qq[kQq];
-    auto prefetch = [&](int j) {
-      aq[j % kQq] = a_tile(j);
-      if (j >= kQRegSteps) qq[j % kQq] = lds_read16_at(qla + 4096 * (j - kQRegSteps));
-    };
+    bf16x8 aq[kQq];
+    auto prefetch = [&](int j) { aq[j % kQq] = a_tile(j); };
 #pragma unroll
     for (int j = 0; j < kQkAhead; ++j) prefetch(j);
 #pragma unroll
     for (int j = 0; j < kQSteps; ++j) {
       if (j + kQkAhead < kQSteps) prefetch(j + kQkAhead);
-      const bf16x8 qv = j < kQRegSteps ? qb[j < kQRegSteps ? j : 0] : qq[j % kQq];
       if (j == 0)
-        mfma_qk_first(S, aq[j % kQq], qv);
+        mfma_qk_first(S, aq[j % kQq], qb[j]);
       else
-        mfma_qk(S, aq[j % kQq], qv);
+        mfma_qk(S, aq[j % kQq], qb[j]);
       // keep the written order: the scheduler would otherwise hoist more operand reads than
       // the VGPRs left next to the query hold, or move the softmax pieces across MFMAs
       __builtin_amdgcn_sched_barrier(0);
@@ -387,9 +369,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   };
 
   // ---- software pipeline over the tiles.  Fill: tile 0's scores.  Iteration k: the scores
-  // of tile k + 1 with tile k's softmax (and tile k + 2's loads) in the shadow of their MFMAs,
+  // of tile k + 1 with tile k's softmax (and tile k + 3's loads) in the shadow of their MFMAs,
   // then tile k's value product.  The ring holds tile k (values), tile k + 1 (scores) and
-  // tile k + 2 (in flight): one tile in flight, issued a full iteration before it is needed.
+  // tiles k + 2, k + 3 (in flight): each tile is issued two iterations before it is scored.
   lds_barrier();  // tile 0 landed for every wave
   // scores of even tiles in Sa, odd tiles in Sb (two iterations per trip, no register copies)
   f32x16 Sa, Sb;
@@ -399,14 +381,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     // page of the tile issued below, read before the barrier (whose lgkmcnt(0) covers it) so
     // that no scalar load is in flight during the tile's LDS reads: scalar and LDS reads
     // share one counter and a pending scalar load would force every LDS wait to zero
-    const int32_t pg = k + 2 < n_tiles ? page_of(k + 2) : 0;
-    wait_vmcnt<0>();  // this wave's loads of tile k + 1, the only tile in flight, are done
+    const int32_t pg = page_or0(k + 3);
+    wait_vmcnt<kIssues>();  // tile k + 1 is done; only tile k + 2's loads may be out
     lds_barrier();    // tile k + 1 landed for every wave; tile k - 1's buffer is free
     scores(S_next, [&](int j) {
-      // the loads of tile k + 2 go out behind the first score MFMAs, whose execution covers
+      // the loads of tile k + 3 (into tile k - 1's buffer) go out behind the first score
+      // MFMAs, whose execution covers
       // the address set-up; tile k's softmax runs in the shadow of the following ones (its
       // scores were complete a whole value product ago), one piece per MFMA
-      if (j == 1 && k + 2 < n_tiles) issue(k + 2, pg);
+      if (j == 1) issue(k + 3, pg);
       if (j == 3) soft_max1(S_cur);
       if (j == 4) soft_max2(S_cur, k);
       if (j >= 5 && j <= 20) {
@@ -465,7 +448,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   // instruction.
   constexpr int kOutPitch = kDC * 2 + 16;  // LDS bytes per head row (+16: 2-way conflicts)
   static_assert(kWaves * 32 * kOutPitch <= sizeof(Smem), "output staging exceeds the LDS");
-  __syncthreads();  // every wave is done with the ring and its query rows
+  wait_vmcnt<0>();  // no load into the ring is still out
+  __syncthreads();  // every wave is done with the ring
   char* stage = reinterpret_cast<char*>(&sm) + w * 32 * kOutPitch;
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb)
