@@ -161,7 +161,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   const uint32_t lat_row_b = (uint32_t)(lat_tok * 2), rope_row_b = (uint32_t)(rope_tok * 2);
   const int32_t* bt_row = bt + (paged ? (int64_t)b * bt_stride : 0);
   auto page_of = [&](int k) -> int32_t { return paged ? bt_row[(t_begin + kTT * k) / kPage] : 0; };
-  auto issue = [&](int k, int64_t pg) {
+  // part < 0: every load of wave w for tile k; else only load `part` (0 .. kIssues - 1)
+  auto issue = [&](int k, int64_t pg, int part = -1) {
     const int t0 = t_begin + kTT * k;
     const bf16 *lb, *rb;
     if (paged) {
@@ -174,7 +175,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     // valid rows, uniform (the clamp would otherwise become a vector med3, and a buffer
     // descriptor in vector registers costs a loop per load)
     const int valid = __builtin_amdgcn_readfirstlane(max(0, min(kTT, t_end - t0)));
-    issue_tile<Sw32, kWaves>(ring[k % kRing], w, lane, lb, rb, valid, lat_row_b, rope_row_b);
+    if (part < 0)
+      issue_tile<Sw32, kWaves>(ring[k % kRing], w, lane, lb, rb, valid, lat_row_b, rope_row_b);
+    else
+      issue_tile_part<Sw32, kWaves>(ring[k % kRing], w, lane, lb, rb, valid, lat_row_b,
+                                    rope_row_b, part);
   };
 
   // Absorbed query as the B operand of 32x32x16 (N = heads): lane (head l32, k-half kg),
@@ -385,11 +390,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     wait_vmcnt<kIssues>();  // tile k + 1 is done; only tile k + 2's loads may be out
     lds_barrier();    // tile k + 1 landed for every wave; tile k - 1's buffer is free
     scores(S_next, [&](int j) {
-      // the loads of tile k + 3 (into tile k - 1's buffer) go out behind the first score
-      // MFMAs, whose execution covers
-      // the address set-up; tile k's softmax runs in the shadow of the following ones (its
-      // scores were complete a whole value product ago), one piece per MFMA
-      if (j == 1) issue(k + 3, pg);
+      // the loads of tile k + 3 (into tile k - 1's buffer) go out one per gap behind score
+      // MFMAs 1..9 (issued back to back they would stall the wave for ~200 cycles; with two
+      // tiles in flight their latency has room); tile k's softmax runs in the shadow of the
+      // score MFMAs too (its scores were complete a whole value product ago), one piece per
+      // MFMA
+      if (j >= 1 && j <= kIssues) issue(k + 3, pg, j - 1);
       if (j == 3) soft_max1(S_cur);
       if (j == 4) soft_max2(S_cur, k);
       if (j >= 5 && j <= 20) {

@@ -94,6 +94,25 @@ __device__ __forceinline__ void issue_tile(char* buf, int w, int lane, const bf1
   }
 }
 
+// One of the loads of issue_tile: latent row R*w + part for part < R = kTT / NW, the rotary
+// rows for part == R.  A wave that issues a tile's loads back to back stalls on them, so a
+// caller with the latency to spare spreads them over several gaps between other work.
+template <Swizzle SW, int NW>
+__device__ __forceinline__ void issue_tile_part(char* buf, int w, int lane, const bf16* lb,
+                                                const bf16* rb, int valid, uint32_t lat_row_b,
+                                                uint32_t rope_row_b, int part) {
+  constexpr int R = kTT / NW;
+  if (part < R) {
+    const int t = R * w + part;
+    dma16(rsrc(lb, valid * lat_row_b), buf + t * kLatRowB,
+          t * lat_row_b + 16 * (lane ^ lat_sw<SW>(t)));
+  } else if (NW <= 4 || w < 4) {  // (known true at compile time for up to 4 waves)
+    const int rt = 8 * w + (lane >> 3);
+    dma16(rsrc(rb, valid * rope_row_b), buf + kRopeOff + w * 1024,
+          rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
+  }
+}
+
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt low bits
 // [3:0], high bits [15:14]; expcnt [6:4] and lgkmcnt [11:8] at their maxima).
 template <int N>
