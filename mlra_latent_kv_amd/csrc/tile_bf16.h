@@ -124,8 +124,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() also fences global
 // memory, which would wait for every in-flight tile load (they write LDS asynchronously)
 // and drain the prefetch ring; tile arrival is tracked with explicit vmcnt waits instead.
-// The memory clobber keeps the compiler from moving LDS accesses across the barrier.
+// The memory clobber keeps the compiler from moving LDS accesses across the barrier.  The
+// same lgkmcnt(0) goes first as a builtin too: the compiler's wait analysis does not look
+// into inline asm, and would otherwise still count a scalar load issued before the barrier
+// as outstanding, which forces the first LDS wait after it to lgkmcnt(0) (scalar loads
+// complete out of order), i.e. a wait for every operand read issued there.
 __device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt at their maxima
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
