@@ -17,8 +17,9 @@
 //    what the 16x16x32 shape gets from the same read, so LDS traffic per tile is half that of
 //    a 16-heads-per-wave layout.
 //  * tiles of 32 tokens stream through a ring of 4 LDS buffers by direct-to-LDS loads, in a
-//    software pipeline: while tile k + 1 is scored, tile k's softmax runs between its score
-//    MFMAs, then tile k's values are summed, and tiles k + 2 and k + 3 are in flight.
+//    software pipeline: while tile k + 1 is scored, tile k's value MFMAs alternate with its
+//    score MFMAs, tile k + 1's softmax runs between tile k's last value MFMAs, and tiles
+//    k + 2 and k + 3 are in flight.
 //  * scores S^T[t][h] = tile . q_cat^T (one accumulation chain over 36 K-steps of 16
 //    columns); the probabilities go register-direct into the value product
 //    O^T += V^T P^T (token order inside a K-step permuted to match the score layout; value
@@ -251,56 +252,66 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   // softmax and the next tile's loads are placed there, in the shadow of the score MFMAs.
   constexpr int kQkAhead = 4;
   constexpr int kQq = kQkAhead + 1;
-  auto scores = [&](f32x16& S, auto&& mid) {
+  // iteration at which K-step t's tile operand is read: kQkAhead steps ahead, or kQkNear
+  // steps ahead once the value MFMAs alternate with the score MFMAs (from gap kVStart on),
+  // where each step is two MFMA slots
+  auto read_at = [](int t, int v_start) {
+    constexpr int kQkNear = 2;
+    return t - (t >= v_start + kQkNear ? kQkNear : kQkAhead);
+  };
+  auto scores = [&](f32x16& S, int v_start, auto&& mid) {
     auto a_tile = [&](int j) -> bf16x8 {
       return j < 32 ? lds_read16_at(qa[j & 7] + 256 * (j >> 3)) : lds_read16_at(ra[j - 32]);
     };
     bf16x8 aq[kQq];
-    auto prefetch = [&](int j) { aq[j % kQq] = a_tile(j); };
 #pragma unroll
-    for (int j = 0; j < kQkAhead; ++j) prefetch(j);
+    for (int t = 0; t < kQSteps; ++t)
+      if (read_at(t, v_start) < 0) aq[t % kQq] = a_tile(t);
 #pragma unroll
     for (int j = 0; j < kQSteps; ++j) {
-      if (j + kQkAhead < kQSteps) prefetch(j + kQkAhead);
+#pragma unroll
+      for (int t = j + 1; t < kQSteps && t <= j + kQkAhead; ++t)
+        if (read_at(t, v_start) == j) aq[t % kQq] = a_tile(t);
       if (j == 0)
         mfma_qk_first(S, aq[j % kQq], qb[j]);
       else
         mfma_qk(S, aq[j % kQq], qb[j]);
       // keep the written order: the scheduler would otherwise hoist more operand reads than
-      // the VGPRs left next to the query hold, or move the softmax pieces across MFMAs
+      // the VGPRs left next to the query hold, or move the pieces in mid() across MFMAs
       __builtin_amdgcn_sched_barrier(0);
       mid(j);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- softmax of tile kt's scores S.  D layout: lane (head l32, half kg), item i -> token
-  // 8*(i/4) + 4*kg + i%4.  Each piece below fits between two score MFMAs:
+  // ---- softmax of one tile's scores S into weight set P (tiles alternate between the two
+  // sets: the value product of tile k reads set k & 1 while tile k + 1's softmax writes the
+  // other).  D layout: lane (head l32, half kg), item i -> token 8*(i/4) + 4*kg + i%4.
   //  * soft_max1 / soft_max2: row max as a tree of depth 3 (a linear chain of 15 is 15
   //    dependent VALU steps), and the lazy raise of the running max, which rescale() then
-  //    applies to O and l before the tile's values are added (the weights already use it);
+  //    applies to O and l once the previous tile's values are in (the weights already use
+  //    the raised max);
   //  * weight_exp / weight_pack: the weights of items i, i + 1, then their conversion to a
   //    packed pair (one conversion), summed over the rounded weights the MFMA uses as a dot
   //    product of the pair with (1, 1).
+  // Each piece ends by passing its results through an empty volatile asm, which keeps it in
+  // the gap between MFMAs where it is written (the compiler would otherwise sink it towards
+  // its use, past branches, where it runs serially).
   // B operand of the value product (K = 16 tokens per step, N = heads): lane (head l32,
   // k-half kg) item e of step ks <-> token 16*ks + 8*(e/4) + 4*kg + e%4: the lane's own
   // scores, items 8*ks + e.
-  uint32_t pw[2][4];
-  float psum = 0.0f;
+  uint32_t pw[2][2][4];
+  float psum[2] = {0.0f, 0.0f};
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
   bool raise = false;
   float a_raise = 1.0f;
   float t5[5];
-  // Each piece ends by passing its results through an empty volatile asm, which keeps it
-  // between the score MFMAs (themselves volatile asm) where it is written: otherwise the
-  // compiler sinks the weights past the rescale branch to their use in the value product,
-  // where they would run serially between the two products.
   auto soft_max1 = [&](const f32x16& S) {
 #pragma unroll
     for (int j = 0; j < 5; ++j) t5[j] = fmaxf(fmaxf(S[3 * j], S[3 * j + 1]), S[3 * j + 2]);
     asm volatile("" : "+v"(t5[0]), "+v"(t5[1]), "+v"(t5[2]), "+v"(t5[3]), "+v"(t5[4]));
   };
-  auto soft_max2 = [&](const f32x16& S, int kt) {
+  auto soft_max2 = [&](const f32x16& S, int kt, int P) {
     float mx = fmaxf(fmaxf(fmaxf(t5[0], t5[1]), t5[2]), fmaxf(fmaxf(t5[3], t5[4]), S[15]));
     mx = max_xor32(mx);  // every tile holds a valid token: mx finite
     raise = false;
@@ -312,10 +323,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
       m_ref = m_new;
       raise = true;
     }
-    psum = 0.0f;
+    psum[P] = 0.0f;
+    asm volatile("" : "+v"(m_ref), "+v"(psum[P]));
   };
+  // O and l to the raised max: after the previous tile's last value MFMA, before this one's
+  // first (the padding covers the accumulation-register reads after that MFMA's writes)
   auto rescale = [&]() {
     if (raise) {
+      asm volatile("s_nop 15\n\ts_nop 7");
       // one block at a time through VGPRs (O lives in the accumulation registers)
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb) {
@@ -331,11 +346,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     e2[1] = __builtin_amdgcn_exp2f(S[i + 1] - m_ref);
     asm volatile("" : "+v"(e2[0]), "+v"(e2[1]));
   };
-  auto weight_pack = [&](int i) {
+  auto weight_pack = [&](int i, int P) {
     const bf16x2 p = __builtin_convertvector(f32x2{e2[0], e2[1]}, bf16x2);
-    pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
-    psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
-    asm volatile("" : "+v"(pw[i >> 3][(i & 7) >> 1]), "+v"(psum));
+    pw[P][i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
+    psum[P] = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum[P], false);
+    asm volatile("" : "+v"(pw[P][i >> 3][(i & 7) >> 1]), "+v"(psum[P]));
+  };
+  // rows past the item's end in tile kt (only the last tile can have them) get -inf
+  auto mask_ragged = [&](f32x16& S, int kt) {
+    const int valid = min(kTT, t_end - t_begin - kTT * kt);
+    if (valid < kTT) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        S[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? S[i] : -INFINITY;
+    }
+  };
+  // softmax piece q (0 .. kSoftPieces - 1) of tile kt into set P
+  constexpr int kSoftPieces = 18;
+  auto soft_piece = [&](f32x16& S, int kt, int P, int q) {
+    if (q == 0) {
+      mask_ragged(S, kt);
+      soft_max1(S);
+    } else if (q == 1) {
+      soft_max2(S, kt, P);
+    } else if ((q & 1) == 0) {
+      weight_exp(S, q - 2);
+    } else {
+      weight_pack(q - 3, P);
+    }
   };
 
   // ---- O^T[d][h] += V^T P^T over one tile (its buffer at pa), K-step-major over the 16
@@ -348,17 +386,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     const uint32_t o = 256 * (cb >> 2) + 16384 * ks;
     return tr_pair_at(pa[0][cb & 3] + o, pa[1][cb & 3] + o);
   };
-  auto values = [&](int kt) {
-    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]});
-    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[1][0], pw[1][1], pw[1][2], pw[1][3]});
+  // value MFMA at which operand i is read: kPvAhead ahead, or kPvNear ahead for the first
+  // n_inter MFMAs (those alternating with score MFMAs, where each step is two MFMA slots);
+  // negative: read before the first value MFMA (value_pre)
+  auto vread_at = [](int i, int n_inter) {
+    constexpr int kPvNear = 2;
+    return i - (i < n_inter ? kPvNear : kPvAhead);
+  };
+  auto value_pre = [&](int g, int n_inter) {  // g = -kPvAhead .. -1
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i + kPvAhead < 32) vq[(i + kPvAhead) % (kPvAhead + 1)] = v_tile(i + kPvAhead);
-      O[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i % (kPvAhead + 1)], i < 16 ? pb0 : pb1,
-                                                         O[i & 15], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    l_run += sum_xor32(psum);
+    for (int i2 = 0; i2 < kPvAhead; ++i2)
+      if (vread_at(i2, n_inter) == g) vq[i2 % (kPvAhead + 1)] = v_tile(i2);
+  };
+  // value MFMA i of the tile with weight set P
+  auto value_mfma = [&](int i, int P, int n_inter) {
+    const int ks = i >> 4;
+    const bf16x8 pb =
+        __builtin_bit_cast(bf16x8, u32x4{pw[P][ks][0], pw[P][ks][1], pw[P][ks][2], pw[P][ks][3]});
+#pragma unroll
+    for (int i2 = i + 1; i2 < 32 && i2 <= i + kPvAhead; ++i2)
+      if (vread_at(i2, n_inter) == i) vq[i2 % (kPvAhead + 1)] = v_tile(i2);
+    O[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i % (kPvAhead + 1)], pb, O[i & 15], 0, 0, 0);
+  };
+  auto values_end = [&](int kt, int P) {
+    l_run += sum_xor32(psum[P]);
     const int32_t step = next_buf(kt);
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr)
@@ -373,79 +424,90 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     for (int j = 0; j < 4; ++j) ra[j] = opaque(ra[j] + step);
   };
 
-  // ---- software pipeline over the tiles.  Fill: tile 0's scores.  Iteration k: the scores
-  // of tile k + 1 with tile k's softmax (and tile k + 3's loads) in the shadow of their MFMAs,
-  // then tile k's value product.  The ring holds tile k (values), tile k + 1 (scores) and
-  // tiles k + 2, k + 3 (in flight): each tile is issued two iterations before it is scored.
+  // ---- software pipeline over the tiles.  Fill: tile 0's scores and softmax.  Iteration k:
+  // the score chain of tile k + 1, with tile k + 3's loads behind its first MFMAs and tile k's
+  // value MFMAs alternating with its MFMAs from gap kVStart on (so each stream's operand
+  // reads run twice as many MFMA slots ahead); then tile k's remaining value MFMAs, with tile
+  // k + 1's softmax in their gaps (its scores are complete by then); then the lazy rescale.
+  // The ring holds tile k (values), tile k + 1 (scores) and tiles k + 2, k + 3 (in flight).
+  // score gap of tile k's first value MFMA: later starts leave more tail gaps for the
+  // softmax but fewer alternating pairs (13, 17, 21, 25, 29 timed; 21 best overall)
+  constexpr int kVStart = 21;
+  constexpr int kTail = 32 - (kQSteps - kVStart);  // value MFMAs after the score chain
+  static_assert(kTail >= 1 && kVStart >= kPvAhead, "value schedule");
   lds_barrier();  // tile 0 landed for every wave
-  // scores of even tiles in Sa, odd tiles in Sb (two iterations per trip, no register copies)
-  f32x16 Sa, Sb;
-  scores(Sa, [](int) {});
+  f32x16 S;
+  scores(S, kQSteps, [](int) {});
   advance_qk(0);
-  auto step = [&](int k, const f32x16& S_cur, f32x16& S_next) {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 11");  // the last score MFMA's result, before the first VALU read of S
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < kSoftPieces; ++q) soft_piece(S, 0, 0, q);
+  auto step = [&](int k, int P) {  // P = k & 1
     // page of the tile issued below, read before the barrier (whose lgkmcnt(0) covers it) so
     // that no scalar load is in flight during the tile's LDS reads: scalar and LDS reads
     // share one counter and a pending scalar load would force every LDS wait to zero
     const int32_t pg = page_or0(k + 3);
     wait_vmcnt<kIssues>();  // tile k + 1 is done; only tile k + 2's loads may be out
     lds_barrier();    // tile k + 1 landed for every wave; tile k - 1's buffer is free
-    scores(S_next, [&](int j) {
+    scores(S, kVStart, [&](int j) {
       // the loads of tile k + 3 (into tile k - 1's buffer) go out one per gap behind score
       // MFMAs 1..9 (issued back to back they would stall the wave for ~200 cycles; with two
-      // tiles in flight their latency has room); tile k's softmax runs in the shadow of the
-      // score MFMAs too (its scores were complete a whole value product ago), one piece per
-      // MFMA
+      // tiles in flight their latency has room)
       if (j >= 1 && j <= kIssues) issue(k + 3, pg, j - 1);
-      if (j == 3) soft_max1(S_cur);
-      if (j == 4) soft_max2(S_cur, k);
-      if (j >= 5 && j <= 20) {
-        if (j & 1)
-          weight_exp(S_cur, j - 5);
-        else
-          weight_pack(j - 6);
-      }
-      // the first operands of tile k's values are read behind the last score MFMAs
-      if (j >= kQSteps - kPvAhead) vq[j - (kQSteps - kPvAhead)] = v_tile(j - (kQSteps - kPvAhead));
+      if (j >= kVStart - kPvAhead && j < kVStart) value_pre(j - kVStart, kQSteps - kVStart);
+      if (j >= kVStart) value_mfma(j - kVStart, P, kQSteps - kVStart);
     });
     advance_qk(k + 1);
-    rescale();
-    values(k);
+    // tail: tile k's last value MFMAs; tile k + 1's softmax in their gaps, from the second
+    // gap on (the first gives the last score MFMA's result its 12 wait states)
+#pragma unroll
+    for (int i = 32 - kTail; i < 32; ++i) {
+      value_mfma(i, P, kQSteps - kVStart);
+      __builtin_amdgcn_sched_barrier(0);
+      const int g = i - (32 - kTail);  // tail gap
+      if (g == 0) asm volatile("s_nop 11");
+      if (g >= 1) {
+        // spread the pieces over the remaining gaps (the surplus after the last gap)
+        const int per = (kSoftPieces + kTail - 2) / (kTail - 1 > 0 ? kTail - 1 : 1);
+        for (int q = (g - 1) * per; q < g * per && q < kSoftPieces; ++q) soft_piece(S, k + 1, 1 - P, q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      const int per = (kSoftPieces + kTail - 2) / (kTail - 1 > 0 ? kTail - 1 : 1);
+      for (int q = (kTail - 1) * per; q < kSoftPieces; ++q) soft_piece(S, k + 1, 1 - P, q);
+    }
+    values_end(k, P);
+    rescale();  // tile k + 1's raise, now that tile k's values are in
   };
   int k = 0;
   for (; k + 2 < n_tiles; k += 2) {
-    step(k, Sa, Sb);
-    step(k + 1, Sb, Sa);
+    step(k, 0);
+    step(k + 1, 1);
   }
   if (k + 1 < n_tiles) {
-    step(k, Sa, Sb);
+    step(k, 0);
     ++k;
   }
-  // last tile k = n_tiles - 1: its scores are complete (12 wait states after the last score
-  // MFMA: with a single tile they were written just above), rows past the item's end are
-  // masked, and there is no next tile
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 11");
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    f32x16 S = (k & 1) ? Sb : Sa;
-    const int valid = min(kTT, t_end - t_begin - kTT * k);
-    if (valid < kTT) {  // ragged last tile
+  // last tile k = n_tiles - 1: its softmax is done; its values alone (set k & 1, moved to
+  // set 0 so that every register index stays a compile-time constant)
+  if (k & 1) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        S[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? S[i] : -INFINITY;
-    }
-    soft_max1(S);
-    soft_max2(S, k);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      weight_exp(S, i);
-      weight_pack(i);
-    }
-    rescale();
-#pragma unroll
-    for (int i = 0; i < kPvAhead; ++i) vq[i] = v_tile(i);
-    values(k);
+      for (int e = 0; e < 4; ++e) pw[0][ks][e] = pw[1][ks][e];
+    psum[0] = psum[1];
   }
+#pragma unroll
+  for (int g = -kPvAhead; g < 0; ++g) value_pre(g, 0);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    value_mfma(i, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  values_end(k, 0);
 
   // ---- partial outputs, through LDS so that every global store writes whole rows.  O[cb]
   // item e is column 32cb + 8*(e/4) + 4*kg + e%4 of head h0 + l32: written straight out,
