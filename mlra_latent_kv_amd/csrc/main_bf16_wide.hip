@@ -341,10 +341,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     }
   };
   float e2[2];
-  auto weight_exp = [&](const f32x16& S, int i) {
-    e2[0] = __builtin_amdgcn_exp2f(S[i] - m_ref);
-    e2[1] = __builtin_amdgcn_exp2f(S[i + 1] - m_ref);
-    asm volatile("" : "+v"(e2[0]), "+v"(e2[1]));
+  auto weight_exp = [&](const f32x16& S, int i) {  // weight of item i into e2[i & 1]
+    e2[i & 1] = __builtin_amdgcn_exp2f(S[i] - m_ref);
+    asm volatile("" : "+v"(e2[i & 1]));
   };
   auto weight_pack = [&](int i, int P) {
     const bf16x2 p = __builtin_convertvector(f32x2{e2[0], e2[1]}, bf16x2);
@@ -361,18 +360,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
         S[i] = 8 * (i >> 2) + 4 * kg + (i & 3) < valid ? S[i] : -INFINITY;
     }
   };
-  // softmax piece q (0 .. kSoftPieces - 1) of tile kt into set P
-  constexpr int kSoftPieces = 18;
+  // softmax piece q (0 .. kSoftPieces - 1) of tile kt into set P: the masked first max level,
+  // the rest of the max with the raise, then per item pair p: item 2p's weight, item
+  // 2p + 1's weight, the pair's conversion and row sum
+  constexpr int kSoftPieces = 2 + 3 * 8;
   auto soft_piece = [&](f32x16& S, int kt, int P, int q) {
     if (q == 0) {
       mask_ragged(S, kt);
       soft_max1(S);
     } else if (q == 1) {
       soft_max2(S, kt, P);
-    } else if ((q & 1) == 0) {
-      weight_exp(S, q - 2);
     } else {
-      weight_pack(q - 3, P);
+      const int pair = (q - 2) / 3, part = (q - 2) % 3;
+      if (part < 2)
+        weight_exp(S, 2 * pair + part);
+      else
+        weight_pack(2 * pair, P);
     }
   };
 
@@ -433,6 +436,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   // score gap of tile k's first value MFMA: later starts leave more tail gaps for the
   // softmax but fewer alternating pairs (13, 17, 21, 25, 29 timed; 21 best overall)
   constexpr int kVStart = 21;
+  // tail gap (1 .. gaps) of softmax piece q, by cumulative issue cost (cycles, measured
+  // beside MFMAs: v_exp ~12, v_cvt_pk ~8, plain VALU ~6)
+  auto soft_gap = [](int q, int gaps) {
+    auto cost = [](int r) { return r == 0 ? 30 : r == 1 ? 50 : ((r - 2) % 3 == 2 ? 15 : 18); };
+    int before = 0, total = 0;
+    for (int r = 0; r < kSoftPieces; ++r) {
+      if (r < q) before += cost(r);
+      total += cost(r);
+    }
+    return 1 + before * gaps / total;
+  };
   constexpr int kTail = 32 - (kQSteps - kVStart);  // value MFMAs after the score chain
   static_assert(kTail >= 1 && kVStart >= kPvAhead, "value schedule");
   lds_barrier();  // tile 0 landed for every wave
@@ -461,23 +475,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     });
     advance_qk(k + 1);
     // tail: tile k's last value MFMAs; tile k + 1's softmax in their gaps, from the second
-    // gap on (the first gives the last score MFMA's result its 12 wait states)
+    // gap on (the first gives the last score MFMA's result its 12 wait states), each piece
+    // in the gap its cumulative issue cost falls in (about 30 cycles per gap, what one
+    // MFMA covers)
 #pragma unroll
     for (int i = 32 - kTail; i < 32; ++i) {
       value_mfma(i, P, kQSteps - kVStart);
       __builtin_amdgcn_sched_barrier(0);
       const int g = i - (32 - kTail);  // tail gap
       if (g == 0) asm volatile("s_nop 11");
-      if (g >= 1) {
-        // spread the pieces over the remaining gaps (the surplus after the last gap)
-        const int per = (kSoftPieces + kTail - 2) / (kTail - 1 > 0 ? kTail - 1 : 1);
-        for (int q = (g - 1) * per; q < g * per && q < kSoftPieces; ++q) soft_piece(S, k + 1, 1 - P, q);
-      }
+#pragma unroll
+      for (int q = 0; q < kSoftPieces; ++q)
+        if (soft_gap(q, kTail - 1) == g) soft_piece(S, k + 1, 1 - P, q);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    {
-      const int per = (kSoftPieces + kTail - 2) / (kTail - 1 > 0 ? kTail - 1 : 1);
-      for (int q = (kTail - 1) * per; q < kSoftPieces; ++q) soft_piece(S, k + 1, 1 - P, q);
     }
     values_end(k, P);
     rescale();  // tile k + 1's raise, now that tile k's values are in
