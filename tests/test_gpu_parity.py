@@ -139,6 +139,37 @@ def test_bf16_small_ragged(wname, sharp):
     assert_close(got, oracle_out(inp), "bf16", f"{wname} sharp={sharp}")
 
 
+def ramp_rows(inp, lo, hi):
+    """Scale every cached row at token position p by lo + (hi - lo) p / max_seqlen (latent and
+    rotary parts alike): the scores grow along each sequence, so later tiles keep exceeding
+    the running max by more than the lazy-raise headroom, and the rescale of the accumulated
+    output runs several times inside work items."""
+    row = inp["cache"].shape[-1]
+    rows = inp["cache"].reshape(-1, row)
+    pos = inp["row_pos"]
+    valid = pos >= 0
+    f = I.to_f64(rows[valid], inp["dtype"]).astype(np.float32)
+    scale = (lo + (hi - lo) * pos[valid].astype(np.float64) / max(inp["max_seqlen"], 1))
+    rows[valid] = I.to_storage(f * scale.astype(np.float32)[:, None], inp["dtype"])
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3], ids=["auto", "split1", "split3"])
+@pytest.mark.parametrize("wname", BF16[:3])
+def test_late_raises(wname, splits):
+    """Scores rising along the sequence (sharp query, rows scaled 0.1x .. 3x): the tile maxima
+    climb to ~29 log2 units and pass the 8-unit headroom of the running max at least twice
+    per head over the 4000-token sequence (counted on these inputs from the oracle's scores
+    with one work item per sequence, as split1 runs it; the automatic plan cuts these short
+    sequences into two-tile items).  A steeper ramp (0.25x .. 6x, logits to ~59 log2 units)
+    exceeds the max-abs bound on every version of the kernels alike (0.028): the absorbed
+    query is rounded to bf16, and at such logits its rounding moves the weights by percents."""
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=[4000, 2500, 700, 33], q_gain=I.sharp_q_gain(w))
+    ramp_rows(inp, 0.1, 3.0)
+    got, _ = gpu_out(inp, num_splits=splits)
+    assert_close(got, oracle_out(inp), "bf16", f"{wname} splits={splits}")
+
+
 @pytest.mark.parametrize("wname", ["mla_bf16_b32_h128_l4096", "mlra4_bf16_b32_h32_l8192"])
 def test_split_count_invariance(wname):
     w = I.WORKLOADS[wname]
