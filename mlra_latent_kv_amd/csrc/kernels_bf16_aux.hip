@@ -124,11 +124,12 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
 // 512 latent columns ("[ICLR 2025] MLRA…", section 2.2).
 //
 // One workgroup (4 waves) per (head h, rows b0..b0+R-1), R in {2, 4, 8, 16}:
-//  1. the W_UV rows of the head go to LDS by direct-to-LDS loads (one contiguous 32 KiB block
-//     per wave: wave w owns latent columns 128w..128w+127, exactly branch w for MLRA-4);
-//  2. meanwhile the split statistics (M, 1/L) of every (row, branch), then the weighted sum
-//     of the split partials, with all 256 threads sharing the (row, 16-byte chunk) work, into
-//     an LDS copy of the merged latent output (bf16, the MFMA operand);
+//  1. the split statistics (M, 1/L) of every (row, branch), then the weighted sum of the split
+//     partials, with all 256 threads sharing the (row, 16-byte chunk) work, into an LDS copy
+//     of the merged latent output (bf16, the MFMA operand);
+//  2. meanwhile the W_UV rows of the head go to LDS by direct-to-LDS loads (one contiguous
+//     32 KiB block per wave: wave w owns latent columns 128w..128w+127, exactly branch w for
+//     MLRA-4), issued once the statistics are formed, so that they stream in during the merge;
 //  3. each wave multiplies its 128 latent columns by its W_UV rows (MFMA 32x32x16, rows of
 //     the workgroup as M, padded to 32), and the four partial products (K split four ways)
 //     are summed through LDS.
@@ -167,8 +168,12 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   const int l32 = lane & 31, g = lane >> 5;
 
   // ---- 1. W_UV rows c0..c0+127 of head h: instruction i brings rows 4i..4i+3; lane l lands
-  // at physical chunk l%16 of row 4i + l/16 and so fetches logical chunk ce_sw(row, l%16)
-  {
+  // at physical chunk l%16 of row 4i + l/16 and so fetches logical chunk ce_sw(row, l%16).
+  // Issued after the split statistics (below): vector-memory loads complete in issue order,
+  // so issued first they made the statistics wait for these 128 KiB too.  Issued behind the
+  // statistics' barrier, below the branch of the statistics' rare extra loads, the wait
+  // analysis counts them exactly, and they stream in while the partials are merged.
+  auto issue_wuv = [&]() {
     const int c0 = 128 * w, br = c0 / dcb;
     const bf16* wbase = w_uv + ((size_t)(br * H + h) * dcb + (c0 % dcb)) * kCeDv;
     const __amdgpu_buffer_rsrc_t rs = tile::rsrc(wbase, 128 * kCeRowB);
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
       const int r = 4 * i + (lane >> 4);
       tile::dma16(rs, sm.wuv[w] + 1024 * i, r * kCeRowB + 16 * ce_sw(r, lane & 15));
     }
-  }
+  };
 
   // ---- 2. merged latent.  The splits of row b are its work items split_off[b] ..
   // split_off[b + 1] - 1 (a variable number per row, none for an empty sequence).  Thread t
@@ -274,7 +279,11 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
       sm.stat_inv[r][br] = L > 0.0f ? 1.0f / L : 0.0f;
     }
   }
-  __syncthreads();
+  // LDS-only barrier: __syncthreads() would first wait for every load in flight (all the
+  // partials of the first batch), and the merge below would start only once they had all
+  // arrived instead of load by load
+  tile::lds_barrier();
+  issue_wuv();
 
   // ---- 2b. weighted sum of the splits, batch by batch
   {
