@@ -13,7 +13,7 @@
 //    which one wave per SIMD can hold in the accumulation registers).  The absorbed query
 //    (576 columns of 32 heads) stays in registers for the whole loop, so the LDS holds tiles
 //    only.  No per-tile exchange between waves.
-//  * MFMA 32x32x16 throughout: a 1 KiB operand read from LDS feeds 32K multiply-adds, twice
+//  * MFMA 32x32x16 throughout: a 1 KiB operand read from LDS feeds 16K multiply-adds, twice
 //    what the 16x16x32 shape gets from the same read, so LDS traffic per tile is half that of
 //    a 16-heads-per-wave layout.
 //  * tiles of 32 tokens stream through a ring of 4 LDS buffers by direct-to-LDS loads, in a
