@@ -129,7 +129,8 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
 //     of the merged latent output (bf16, the MFMA operand);
 //  2. meanwhile the W_UV rows of the head go to LDS by direct-to-LDS loads (one contiguous
 //     32 KiB block per wave: wave w owns latent columns 128w..128w+127, exactly branch w for
-//     MLRA-4), issued once the statistics are formed, so that they stream in during the merge;
+//     MLRA-4), issued behind the first partials, half before the statistics are formed and
+//     half after, so that they stream in during the merge;
 //  3. each wave multiplies its 128 latent columns by its W_UV rows (MFMA 32x32x16, rows of
 //     the workgroup as M, padded to 32), and the four partial products (K split four ways)
 //     are summed through LDS.
@@ -169,16 +170,19 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
 
   // ---- 1. W_UV rows c0..c0+127 of head h: instruction i brings rows 4i..4i+3; lane l lands
   // at physical chunk l%16 of row 4i + l/16 and so fetches logical chunk ce_sw(row, l%16).
-  // Issued after the split statistics (below): vector-memory loads complete in issue order,
-  // so issued first they made the statistics wait for these 128 KiB too.  Issued behind the
-  // statistics' barrier, below the branch of the statistics' rare extra loads, the wait
-  // analysis counts them exactly, and they stream in while the partials are merged.
-  auto issue_wuv = [&]() {
+  // Instructions i0..i1-1.  Issued after the split statistics' loads and the first partials
+  // (below): vector-memory loads complete in issue order, so issued first they made the
+  // statistics wait for these 128 KiB too.  Half go out right after the first partials (a
+  // wave then has 60 loads out, within the 63 its load counter tracks; more would stall the
+  // issue), the other half behind the statistics' barrier, below the branch of the
+  // statistics' rare extra loads, where the wait analysis counts them exactly.  They stream
+  // in while the partials are merged.
+  auto issue_wuv = [&](int i0, int i1) {
     const int c0 = 128 * w, br = c0 / dcb;
     const bf16* wbase = w_uv + ((size_t)(br * H + h) * dcb + (c0 % dcb)) * kCeDv;
     const __amdgpu_buffer_rsrc_t rs = tile::rsrc(wbase, 128 * kCeRowB);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int r = 4 * i + (lane >> 4);
       tile::dma16(rs, sm.wuv[w] + 1024 * i, r * kCeRowB + 16 * ce_sw(r, lane & 15));
     }
@@ -249,6 +253,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
       pl[it] = ml[sidx * ml_s + 1];
     }
     load_batch(0);
+    issue_wuv(0, 16);
 #pragma unroll
     for (int it = 0; it < kPre; ++it)
       if (q + it * P >= n) pm[it] = -INFINITY;
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   // partials of the first batch), and the merge below would start only once they had all
   // arrived instead of load by load
   tile::lds_barrier();
-  issue_wuv();
+  issue_wuv(16, 32);
 
   // ---- 2b. weighted sum of the splits, batch by batch
   {
