@@ -8,6 +8,7 @@ plant mistakes in the *oracle* to show the tolerance separates a right answer fr
 plausibly wrong one.
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -219,6 +220,22 @@ def test_fused_merge_shapes(wname, lens, splits):
     from mlra_latent_kv_amd import binding as B
     assert B.num_splits(case.params) == splits
     assert_close(got, oracle_out(inp), "bf16", f"{wname} B={len(lens)} splits={splits}")
+
+
+# Head counts other than those of the named workloads: H = 256 runs the 128-head kernel with
+# two head quads per work item (the blocks of one dispatch slot 8 apart), H = 64 and 96 the
+# 32-head kernel with 2 and 3 head groups, and MLRA-4 runs at H = 64.
+OTHER_H = [("mla_bf16_b32_h128_l4096", 256), ("mla_bf16_b32_h128_l4096", 64),
+           ("mla_bf16_paged_b64_h32_l1k-32k", 96), ("mlra4_bf16_b32_h32_l8192", 64)]
+
+
+@pytest.mark.parametrize("splits", [0, 3], ids=["auto", "split3"])
+@pytest.mark.parametrize("wname,H", OTHER_H, ids=[f"{w}-H{h}" for w, h in OTHER_H])
+def test_other_head_counts(wname, H, splits):
+    w = dataclasses.replace(I.WORKLOADS[wname], heads=H, name=f"{wname}-H{H}")
+    inp = I.make_inputs(w, seqlens=[700, 1, 130], q_gain=I.sharp_q_gain(w))
+    got, _ = gpu_out(inp, num_splits=splits)
+    assert_close(got, oracle_out(inp), "bf16", f"{w.name} splits={splits}")
 
 
 def test_paged_and_contiguous_bitwise_equal():
