@@ -12,10 +12,13 @@ kernels (``mla_decode_timed``), so the flush is outside the measured interval.
 Step time: a HIP event pair around [flush, decode] minus one around [flush] alone, both
 averaged over the K timed steps.  The event overheads cancel and the decode's kernels run
 back to back, as they would in a model.  A separate pass with ``mla_decode_timed``
-gives per-stage times and the main-loop kernel time for the roofline; its interior events
-add a few microseconds of idle gap per stage, which that pass does not report as step time.
-The main-loop time is that pass's event interval around the main kernel minus the interval
-of an empty event pair recorded the same way (the marker overhead both contain).
+gives per-stage times and the main-loop kernel time for the roofline: the HIP event pair
+the library records on its stream around the main-loop launch (nothing subtracted, so the
+figure includes the launch's own dispatch gap and is an upper bound on the kernel's run
+time; the rocprofv3 kernel-trace average of the same command is committed beside it).
+
+A read-stream probe (libmla_probe.so: 16-byte loads over 2 GiB, every byte once) gives the
+practical HBM read ceiling of the device in the same run, reported next to the 8 TB/s peak.
 
 Prints ONE JSON line on stdout.  ``value`` is the latent-cache read rate in TB/s:
   sum_b L_b * (d_c + d_rope) * bytes_per_element / t_step.
@@ -34,7 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode attn: latent-KV read TB/s (% HBM peak), query tokens/s over B×L"
-DEFAULT_WORKLOAD = "mla_bf16_b32_h128_l4096"
+# the largest single-GPU workload: 64 sequences of U[1024, 32768] tokens, 1.25 GB of cache
+DEFAULT_WORKLOAD = "mla_bf16_paged_b64_h32_l1k-32k"
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "main_loop_counters.json")
 # sources of the main-loop kernels; the counter summary is valid only for these exact texts
@@ -82,6 +86,32 @@ class HipEvents:
             self.hip.hipEventDestroy(h)
 
 
+def read_probe(ev, stream, reps: int = 5, gib: int = 2):
+    """Median HBM read rate (GB/s) of the read-stream probe over a ``gib`` GiB buffer."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "mlra_latent_kv_amd", "libmla_probe.so"))
+    lib.mla_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.mla_probe_out_words.restype = ctypes.c_size_t
+    n = gib << 30
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(lib.mla_probe_out_words(), dtype=torch.int32, device="cuda")
+    e = ev.create(2)
+    ms = []
+    for i in range(reps + 1):
+        ev.record(e[0], stream)
+        if lib.mla_probe_read(buf.data_ptr(), n, out.data_ptr(), stream) != 0:
+            raise RuntimeError("mla_probe_read failed")
+        ev.record(e[1], stream)
+        torch.cuda.synchronize()
+        if i:  # the first run warms up
+            ms.append(ev.ms(e[0], e[1]))
+    ev.destroy(e)
+    del buf
+    torch.cuda.empty_cache()
+    return n / (statistics.median(ms) * 1e-3) / 1e9
+
+
 def source_sha() -> str:
     h = hashlib.sha256()
     for f in MAIN_SRCS:
@@ -112,7 +142,7 @@ def counters_traffic(workload: str):
 def cpu_baseline(inp, seconds: float):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same workload."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
     from oracle import mla_oracle as O
     from mlra_latent_kv_amd import inputs as I
     w = inp["workload"]
@@ -122,21 +152,23 @@ def cpu_baseline(inp, seconds: float):
               theta=inp["rope_theta"], page_size=inp["page_size"],
               block_table=inp["block_table"], to_f64=lambda a: I.to_f64(a, dt))
     hchunk = 8
-    done_bytes, pairs, t0 = 0.0, 0, time.perf_counter()
-    b = 0
-    while b < len(lens) and time.perf_counter() - t0 < seconds:
-        for h0 in range(0, w.heads, hchunk):
-            hs = list(range(h0, min(h0 + hchunk, w.heads)))
-            O.mla_decode(inp["q_nope"], inp["q_rope"], inp["cache"], lens, inp["w_uk"],
-                         inp["w_uv"], batches=[b], heads=hs, **kw)
-            done_bytes += float(lens[b]) * w.row * w.elem_bytes * len(hs) / w.heads
-            pairs += len(hs)
-            if time.perf_counter() - t0 >= seconds:
-                break
-        b += 1
-    el = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": done_bytes / el / 1e12, "unit": "TB/s", "cores": threads, "kind": "oracle",
+    cores = len(os.sched_getaffinity(0))
+    done_bytes, pairs = 0.0, 0
+    with threadpool_limits(limits=cores):  # BLAS threads = the cores this process may use
+        t0 = time.perf_counter()
+        b = 0
+        while b < len(lens) and time.perf_counter() - t0 < seconds:
+            for h0 in range(0, w.heads, hchunk):
+                hs = list(range(h0, min(h0 + hchunk, w.heads)))
+                O.mla_decode(inp["q_nope"], inp["q_rope"], inp["cache"], lens, inp["w_uk"],
+                             inp["w_uv"], batches=[b], heads=hs, **kw)
+                done_bytes += float(lens[b]) * w.row * w.elem_bytes * len(hs) / w.heads
+                pairs += len(hs)
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            b += 1
+        el = time.perf_counter() - t0
+    return {"value": done_bytes / el / 1e12, "unit": "TB/s", "cores": cores, "kind": "oracle",
             "sample": f"{pairs} (sequence, head) outputs of {w.name} from sequence 0 on, "
                       f"fp64 un-absorbed oracle, {el:.1f} s wall; value = their share of the "
                       f"cache bytes / wall time",
@@ -253,8 +285,9 @@ def main():
     for e in pairs_fd + pairs_f + staged + empty:
         ev.destroy(e)
     ms = statistics.mean(total)
-    main_ms_raw = statistics.mean(stage["main"])
-    main_ms = main_ms_raw - pair_ms
+    main_ms = statistics.mean(stage["main"])
+    probe_gbps = read_probe(ev, stream)
+    log(f"[bench] read-stream probe: {probe_gbps:.1f} GB/s")
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -286,6 +319,8 @@ def main():
                    "pages_per_item": plan["pages"],
                    "cache_flush": args.flush},
         "pct_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBPS, 2),
+        "read_probe_GBps": round(probe_gbps, 1),
+        "pct_read_probe": round(100 * value * 1e3 / probe_gbps, 2),
         "query_tokens_per_s": round(len(lens) / (ms * 1e-3), 1),
         "context_tokens_per_s": round(float(lens.sum()) / (ms * 1e-3), 1),
         "ms_p10_p50_p90": [round(float(np.percentile(total, q)), 5) for q in (10, 50, 90)],
@@ -302,8 +337,8 @@ def main():
             "algorithmic_bytes": int(cache_bytes),
             "traffic": counters_traffic(w.name),
             "main_us": round(main_ms * 1e3, 2),
-            "main_us_event_pair": round(main_ms_raw * 1e3, 2),
-            "event_pair_overhead_us": round(pair_ms * 1e3, 2),
+            "frac_of_read_probe": round(achieved / probe_gbps, 4),
+            "empty_event_pair_us": round(pair_ms * 1e3, 2),
         },
         "cpu_baseline": None,
     }

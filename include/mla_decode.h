@@ -21,9 +21,13 @@
  *    stream) and may be made concurrently from several host threads.
  *  - Arguments are validated on the host before anything is launched; a failed check
  *    returns a non-zero mla_status and launches nothing.  Values that live in device memory
- *    (seqlens, block_table entries) are not validated: seqlens[b] must lie in
+ *    (seqlens, block_table entries) are not validated by default: seqlens[b] must lie in
  *    [0, max_seqlen] and every block_table entry for a page a sequence uses must index an
- *    existing page; otherwise the behaviour is undefined.
+ *    existing page; otherwise the behaviour is undefined.  With MLA_FLAG_DEVICE_CHECKS set in
+ *    mla_params.flags the device checks both and records what it finds in the error word of
+ *    the workspace (see "Split plan" below).
+ *  - Device properties (the compute-unit count that sizes the split plan) are queried once
+ *    per device and cached; this is the only state the library keeps.
  *  - A kernel launch failure is reported as MLA_ERR_HIP.
  *  - No C++ exception crosses this interface.
  */
@@ -37,6 +41,10 @@
 extern "C" {
 #endif
 
+/* The HIP stream type, declared exactly as hip_runtime_api.h declares it (so this header
+ * can be included with or without the HIP headers). */
+typedef struct ihipStream_t* hipStream_t;
+
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_NULL = 1,        /* a required pointer is NULL                               */
@@ -44,14 +52,22 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 3, /* valid request this build has no kernel for (dims, page)  */
   MLA_ERR_WORKSPACE = 4,   /* workspace_bytes smaller than mla_workspace_size()        */
   MLA_ERR_DTYPE = 5,       /* unknown dtype                                            */
-  MLA_ERR_ALIGN = 6,       /* pointer or stride not aligned as the dtype requires      */
-  MLA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed               */
+  MLA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed               */
+  MLA_ERR_ALIGN = 7        /* pointer or stride not aligned as the dtype requires      */
 } mla_status;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 
 /* Page size of the paged latent cache, in tokens. */
 #define MLA_PAGE_SIZE 64
+
+/* mla_params.flags: check seqlens and the used block_table entries on the device and record
+ * violations in the workspace's error word (costs one extra pass over the block table). */
+#define MLA_FLAG_DEVICE_CHECKS 1
+
+/* Error-word bits (workspace int32 hdr[4], written by every call). */
+#define MLA_DEVERR_SEQLEN 1   /* some seqlens[b] outside [0, max_seqlen]; clamped into it   */
+#define MLA_DEVERR_BLOCK 2    /* some used block_table entry outside [0, num_pages)         */
 
 typedef struct mla_params {
   int32_t batch;              /* B >= 1 sequences, one query token each                    */
@@ -67,6 +83,9 @@ typedef struct mla_params {
   int32_t num_splits;         /* 0 = balanced split plan (below); n > 0 = at most n splits
                                  per sequence, each ceil(ceil(max_seqlen/64)/n) pages      */
   int32_t dtype;              /* mla_dtype of q, caches, weights and out                   */
+  int32_t flags;              /* 0, or MLA_FLAG_DEVICE_CHECKS                              */
+  int32_t num_pages;          /* paged: pages in the pool (bound for the device checks);
+                                 0 = not given (block ids are then not checked)            */
   int64_t latent_stride_tok;  /* elements between consecutive tokens of the latent cache   */
   int64_t latent_stride_seq;  /* contiguous: elements between sequences; paged: pages      */
   int64_t rope_stride_tok;    /* same two strides for the rotary-key cache                 */
@@ -86,37 +105,53 @@ typedef struct mla_params {
  *  - page_size in {0, 64}.
  * Alignment: bf16 latent, rope, q_nope, w_uk and w_uv pointers 16-byte aligned and the
  * cache strides multiples of 8 elements; other pointers aligned to their element size.
- * num_splits is at most 512 and at most ceil(max_seqlen / 64).
+ * num_splits is at most 512 and at most ceil(max_seqlen / 64).  flags is 0 or
+ * MLA_FLAG_DEVICE_CHECKS; num_pages >= 0.
  *
- * Split plan.  The attention over each sequence is split into work items of whole 64-token
- * pages (split-K over the sequence) whose partial results are merged afterwards.  The plan is
- * made on the device from seqlens at the start of every call, so it follows the actual
- * lengths: with p_b = ceil(seqlens[b] / 64) pages, every sequence is cut into
- * ceil(p_b / c) items of c pages (the last one ragged; an empty sequence gets none).  With
- * num_splits = 0, c is the smallest page count for which the batch's items fit the number of
- * workgroups that fill the GPU once (256 items for bf16 MLA with H % 128 == 0, else 512 /
- * workgroups per item); when no c does, c = max_b p_b.  With num_splits = n,
- * c = ceil(ceil(max_seqlen / 64) / n).
+ * Split plan.  The attention over each sequence is split into work items (split-K over the
+ * sequence) whose partial results are merged afterwards.  The plan is made on the device
+ * from seqlens at the start of every call, so it follows the actual lengths.  Its item
+ * target follows the device's compute-unit count (queried once per device, at most 256).
+ *  - Page plan (bf16 MLA with H % 128 == 0, the fp32 path, and any call with num_splits > 0):
+ *    with p_b = ceil(seqlens[b] / 64) pages, every sequence is cut into ceil(p_b / c) items
+ *    of c whole pages (the last one ragged; an empty sequence gets none), one item per
+ *    dispatch slot.  With num_splits = 0, c is the smallest page count for which the batch's
+ *    items fit the workgroups that fill the GPU once; when no c does, c = max_b p_b.  With
+ *    num_splits = n, c = ceil(ceil(max_seqlen / 64) / n).
+ *  - Stream plan (the other bf16 shapes, num_splits = 0, B <= 2895): the sequences'
+ *    32-token tiles are laid end to end (T tiles in all) and dispatch slot g of
+ *    G = min(slots filling the GPU once, T) takes tiles [floor(g T / G), floor((g+1) T / G));
+ *    an item is the part of one sequence inside one slot, so a slot may run several items.
  * After a call has completed on its stream, the workspace starts with that plan (for
  * inspection; nothing reads it after the call):
- *   int32 hdr[4] at byte 0: { W = number of items, c, slots, item target (0 when forced) }
- *   int32 work[slots][4] at byte 16: { b, t_begin, t_end, item } per dispatch slot of the
- *         main kernels, b = -1 for a slot without an item; items are numbered
- *         sequence-major, item i of sequence b covering tokens [t_begin, t_end)
- *   int32 split_off[B + 1] at byte 16 + 16 * slots: items of sequence b are
- *         split_off[b] .. split_off[b + 1] - 1, split_off[B] = W.
+ *   int32 hdr[8] at byte 0: { W = number of items, c (0 for the stream plan), slots, item
+ *         target (0 when forced), error bits (MLA_DEVERR_*; 0 without device checks), first
+ *         sequence with an error (-1: none), its first bad block-table column (-1: none),
+ *         items_cap }
+ *   int32 work[slots][4] at byte 32: { b, t_begin, t_end, item } of the first item of each
+ *         dispatch slot, b = -1 for a slot without items
+ *   int32 slot_end[slots] next: one past the last item of each slot
+ *   int32 items[items_cap][4] next: { b, t_begin, t_end, slot } of every item; items are
+ *         numbered sequence-major, item i of sequence b covering tokens [t_begin, t_end)
+ *   int32 split_off[B + 1] next: items of sequence b are split_off[b] .. split_off[b+1] - 1,
+ *         split_off[B] = W.
+ * With MLA_FLAG_DEVICE_CHECKS, a used block-table entry outside [0, num_pages) makes a plan
+ * with no items (every output zero, nothing read from the pool); out-of-range seqlens are
+ * clamped into [0, max_seqlen] as always and only reported.
  */
 
 /*
  * Bytes of device workspace mla_decode / mlra_decode need for *p (written to *bytes, a
- * host pointer).  Depends only on the fields of *p.  The workspace holds the split plan, the
+ * host pointer).  Depends only on the fields of *p (sized for devices of up to 256 compute
+ * units; needs no device).  The workspace holds the split plan, the
  * absorbed queries, the per-item partial results (running max, running sum and latent-space
  * output of each work item) and, for fp32, the merged latent-space output.
  */
 mla_status mla_workspace_size(const mla_params* p, size_t* bytes);
 
-/* Most work items (splits) one sequence can be cut into for *p (written to *splits, host):
- * n when num_splits = n > 0, else min(ceil(max_seqlen / 64), item target). */
+/* Most work items (splits) one sequence can be cut into for *p (written to *splits, host), on
+ * a device of up to 256 compute units: n when num_splits = n > 0, else the item target
+ * bounded by the sequence's pages (page plan) or tiles (stream plan). */
 mla_status mla_num_splits(const mla_params* p, int32_t* splits);
 
 /*
@@ -153,7 +188,7 @@ mla_status mla_num_splits(const mla_params* p, int32_t* splits);
 mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_rope,
                       const void* latent, const void* rope, const int32_t* seqlens,
                       const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * MLRA-4 decode step: the latent row is [c_0 | c_1 | c_2 | c_3] (4 x d_latent) and every
@@ -168,7 +203,7 @@ mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_rop
 mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_rope,
                        const void* latent, const void* rope, const int32_t* seqlens,
                        const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Tracing variants: identical to mla_decode / mlra_decode, and additionally record five
@@ -182,12 +217,12 @@ mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_ro
 mla_status mla_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
                             const void* latent, const void* rope, const int32_t* seqlens,
                             const int32_t* block_table, const void* w_uk, const void* w_uv,
-                            void* out, void* workspace, size_t workspace_bytes, void* stream,
+                            void* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                             void* const* events);
 mla_status mlra_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
                              const void* latent, const void* rope, const int32_t* seqlens,
                              const int32_t* block_table, const void* w_uk, const void* w_uv,
-                             void* out, void* workspace, size_t workspace_bytes, void* stream,
+                             void* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                              void* const* events);
 
 /*
@@ -200,7 +235,7 @@ mla_status mlra_decode_timed(const mla_params* p, const void* q_nope, const void
  * d_rope even, 2..256; n_rows >= 0 (0 launches nothing).
  */
 mla_status mla_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
-                           int32_t d_rope, float theta, int32_t dtype, void* stream);
+                           int32_t d_rope, float theta, int32_t dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_str(int32_t status);

@@ -15,11 +15,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
+PROBE_LIB = os.path.join(PKG, "libmla_probe.so")  # read-stream probe (benchmark support)
 ARCH = "gfx950"
 
 HIP_SOURCES = ["api.hip", "kernels_generic.hip", "kernels_bf16_aux.hip", "main_bf16.hip",
                "main_bf16_wide.hip"]
 CXX_SOURCES = ["plan.cpp"]
+PROBE_SOURCES = ["probe.hip"]
 
 
 def hipcc() -> str:
@@ -61,12 +63,8 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = HIP_SOURCES + CXX_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -75,9 +73,18 @@ def build(verbose: bool = False) -> str:
     missing = [ln.strip() for ln in und.splitlines() if "mla::" in ln]
     if missing:
         raise RuntimeError(f"unresolved library symbols: {missing}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = HIP_SOURCES + CXX_SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in HIP_SOURCES + CXX_SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

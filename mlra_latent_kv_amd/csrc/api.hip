@@ -8,6 +8,8 @@
 //   epilogue  -> out = out_scale * W_UV^T o_lat (summed over MLRA branches)
 // (on the bf16 path combine and epilogue are one kernel)
 // Nothing is allocated, nothing synchronises, no state is kept between calls.
+#include <atomic>
+
 #include "launch.h"
 #include "plan.h"
 
@@ -17,16 +19,47 @@ using namespace mla;
 
 mla_status to_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Compute units of the current device, queried once per device and cached (the split plan's
+// workgroup targets follow it, so a partitioned device gets a plan for its own CUs).
+constexpr int kCuCacheDevices = 64;
+std::atomic<int> g_cu_count[kCuCacheDevices];
+
+hipError_t device_cu_count(int* n_cu) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kCuCacheDevices) {
+    const int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *n_cu = v;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n < 1) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < kCuCacheDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *n_cu = n;
+  return hipSuccess;
+}
+
 mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope,
                       const void* q_rope, const void* latent, const void* rope,
                       const int32_t* seqlens, const int32_t* block_table, const void* w_uk,
                       const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
-                      void* stream, void* const* events) {
+                      hipStream_t stream, void* const* events) {
+  // validation against the plan mla_workspace_size describes (sized for kMaxCUs), then the
+  // plan for this device's compute units, which needs no more workspace
   Plan plan;
   mla_status st = make_plan(p, &plan);
   if (st != MLA_OK) return st;
   st = check_call(p, plan, want_branches, q_nope, q_rope, latent, rope, seqlens, block_table,
                   w_uk, w_uv, out, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  int n_cu = 0;
+  if (device_cu_count(&n_cu) != hipSuccess) return MLA_ERR_HIP;
+  st = make_plan(p, &plan, n_cu);
   if (st != MLA_OK) return st;
 
   DecodeArgs a;
@@ -50,18 +83,21 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
   char* ws = static_cast<char*>(workspace);
   a.plan = plan_args(plan, seqlens, workspace);
   a.work = a.plan.work;
+  a.slot_end = a.plan.slot_end;
+  a.items = a.plan.items;
   a.split_off = a.plan.split_off;
   a.qcat = ws + plan.off_qcat;
   a.part_o = ws + plan.off_part_o;
   a.part_ml = reinterpret_cast<float*>(ws + plan.off_part_ml);
   a.olat = ws + plan.off_olat;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t s = stream;
   auto mark = [&](int i) {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
   };
   hipError_t e = mark(0);
   const bool bf = plan.path == Path::kBf16Mfma;
+  if (e == hipSuccess && plan.checks) e = launch_device_checks(plan, a, s);
   if (e == hipSuccess) e = bf ? launch_prologue_bf16(plan, a, s) : launch_prologue(plan, a, s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
@@ -105,7 +141,7 @@ mla_status mla_num_splits(const mla_params* p, int32_t* splits) {
 mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_rope,
                       const void* latent, const void* rope, const int32_t* seqlens,
                       const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run_decode(1, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
                     workspace, workspace_bytes, stream, nullptr);
 }
@@ -113,7 +149,7 @@ mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_rop
 mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_rope,
                        const void* latent, const void* rope, const int32_t* seqlens,
                        const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run_decode(4, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
                     workspace, workspace_bytes, stream, nullptr);
 }
@@ -121,7 +157,7 @@ mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_ro
 mla_status mla_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
                             const void* latent, const void* rope, const int32_t* seqlens,
                             const int32_t* block_table, const void* w_uk, const void* w_uv,
-                            void* out, void* workspace, size_t workspace_bytes, void* stream,
+                            void* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                             void* const* events) {
   return run_decode(1, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
                     workspace, workspace_bytes, stream, events);
@@ -130,18 +166,18 @@ mla_status mla_decode_timed(const mla_params* p, const void* q_nope, const void*
 mla_status mlra_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,
                              const void* latent, const void* rope, const int32_t* seqlens,
                              const int32_t* block_table, const void* w_uk, const void* w_uv,
-                             void* out, void* workspace, size_t workspace_bytes, void* stream,
+                             void* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                              void* const* events) {
   return run_decode(4, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
                     workspace, workspace_bytes, stream, events);
 }
 
 mla_status mla_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
-                           int32_t d_rope, float theta, int32_t dtype, void* stream) {
+                           int32_t d_rope, float theta, int32_t dtype, hipStream_t stream) {
   const mla_status st = check_rope_rotate(x, row_stride, pos, n_rows, d_rope, theta, dtype);
   if (st != MLA_OK || n_rows == 0) return st;
   return to_status(launch_rope_rotate(x, row_stride, pos, n_rows, d_rope, theta, dtype,
-                                      static_cast<hipStream_t>(stream)));
+                                      stream));
 }
 
 const char* mla_status_str(int32_t status) { return status_str(status); }

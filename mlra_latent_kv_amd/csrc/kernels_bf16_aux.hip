@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
     int B, int H, int NB, int dcb, float qscale, RopeFreq rf, PlanArgs plan) {
   constexpr int dn = 128, dr = 64;
   __shared__ __align__(16) bf16 sW[dn * kPPitch];
+  static_assert(sizeof(sW) >= kPlanLdsBytes, "the plan's LDS bound");
   const int h = blockIdx.x, b0 = blockIdx.y * kRows, cb = blockIdx.z;
   if (h == H) {  // the extra column of blocks: block (H, 0, 0) makes the split plan
     if (b0 == 0 && cb == 0) make_work_plan(plan, sW, (int)sizeof(sW));
@@ -64,7 +65,8 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
   const bool has_r = t_r < kRows * (dr / 2) && bb_r < B;
   const bf16* xr = q_rope + ((size_t)min(bb_r, B - 1) * H + h) * dr + 2 * (has_r ? k_r : 0);
   const float x0 = (float)xr[0], x1 = (float)xr[1];
-  const int L_r = seqlens[min(bb_r, B - 1)];
+  // the length as the plan uses it, clamped to [0, max_seqlen]
+  const int L_r = min(max(seqlens[min(bb_r, B - 1)], 0), plan.max_seqlen);
   const bf16* wsrc = w_uk + ((size_t)br * H + h) * dn * dcb + c0;
 #pragma unroll
   for (int j = 0; j < dn * kPCols / 8 / 256; ++j) {

@@ -6,6 +6,7 @@
 // folded into the query (prologue) and the value up-projection W_UV is applied once to the
 // attention-weighted latent (epilogue), so per-token keys and values are never formed.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 
 #include "device_common.h"
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
   for (int i = threadIdx.x; i < nb * half; i += blockDim.x) {
     const int j = i / half, k = i % half;
     const int b = b0 + j;
-    const int L = seqlens[b];
+    const int L = min(max(seqlens[b], 0), plan.max_seqlen);  // as the plan clamps it
     float cs, sn;
     rope_cos_sin(L > 0 ? L - 1 : 0, rf.f[k], &cs, &sn);
     const T* x = q_rope + ((size_t)b * H + h) * dr + 2 * k;
@@ -86,6 +87,48 @@ hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, s, (const float*)a.q_nope,
                        (const float*)a.q_rope, a.seqlens, (const float*)a.w_uk, (float*)a.qcat,
                        p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, rf, a.plan, (int)lds);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- device checks
+// MLA_FLAG_DEVICE_CHECKS: one workgroup per sequence b checks seqlens[b] against
+// [0, max_seqlen] and, for a paged cache with a known pool size, every block-table entry of
+// the pages the (clamped) length uses against [0, num_pages).  It writes
+// dbg[b] = 4 * (first bad page index + 1, or 0) + error bits, which the split plan folds into
+// the error word.  Every read stays inside seqlens[b] and the row's used block-table entries.
+__global__ __launch_bounds__(256) void k_device_checks(const int32_t* __restrict__ seqlens,
+                                                       const int32_t* __restrict__ bt,
+                                                       int64_t bt_stride, int paged,
+                                                       int num_pages, int max_seqlen,
+                                                       int32_t* __restrict__ dbg) {
+  __shared__ int red[4];
+  const int b = blockIdx.x;
+  const int raw = seqlens[b];
+  int first = INT_MAX;
+  if (paged && num_pages > 0) {
+    const int L = min(max(raw, 0), max_seqlen);
+    const int np = (L + kPage - 1) / kPage;
+    const int32_t* row = bt + (int64_t)b * bt_stride;
+    for (int j = threadIdx.x; j < np; j += 256) {
+      const int e = row[j];
+      if (e < 0 || e >= num_pages) first = min(first, j);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = first;
+    __syncthreads();
+    first = min(min(red[0], red[1]), min(red[2], red[3]));
+  }
+  if (threadIdx.x == 0) {
+    int d = (raw < 0 || raw > max_seqlen) ? MLA_DEVERR_SEQLEN : 0;
+    if (first != INT_MAX) d |= MLA_DEVERR_BLOCK | (4 * (first + 1));
+    dbg[b] = d;
+  }
+}
+
+hipError_t launch_device_checks(const Plan& p, const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_device_checks, dim3(p.B), dim3(256), 0, s, a.seqlens, a.block_table,
+                     a.bt_stride, p.paged, p.num_pages, p.max_seqlen, const_cast<int32_t*>(a.plan.dbg));
   return hipGetLastError();
 }
 

@@ -23,7 +23,10 @@ struct DecodeArgs {
   float softmax_scale, out_scale, rope_theta;
   // workspace regions
   PlanArgs plan;    // split plan, written by the prologue launch
-  const int32_t* work;       // [slots][4] dispatch table: b, t_begin, t_end, item (b < 0: none)
+  const int32_t* work;       // [slots][4]: b, t_begin, t_end, item of the slot's first item
+                             // (b < 0: the slot has none)
+  const int32_t* slot_end;   // [slots]: one past the slot's last item
+  const int32_t* items;      // [items_cap][4]: b, t_begin, t_end, slot of every item
   const int32_t* split_off;  // [B + 1] first work item of each sequence
   void* qcat;       // [B][H][row] storage dtype, pre-scaled by softmax_scale*log2(e)
   void* part_o;     // [item][H][d_c], unnormalised partial latent outputs: bf16 on the bf16
@@ -36,6 +39,8 @@ struct RopeFreq;
 // theta^(-2k/d_rope), k < d_rope/2, in fp64 (RoFormer frequencies)
 void make_rope_freq(int d_rope, float theta, RopeFreq* out);
 
+// MLA_FLAG_DEVICE_CHECKS only: per-sequence checks of seqlens and block ids, before the plan
+hipError_t launch_device_checks(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s);       // fp32 path
 hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);

@@ -17,13 +17,14 @@ bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(pt
 
 }  // namespace
 
-mla_status make_plan(const mla_params* p, Plan* plan) {
+mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   if (!p || !plan) return MLA_ERR_NULL;
   if (p->dtype != MLA_F32 && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (p->batch < 1 || p->num_heads < 1 || p->num_branches < 1 || p->d_nope < 1 || p->d_v < 1 ||
       p->d_latent < 1 || p->d_rope < 2 || (p->d_rope & 1) || p->max_seqlen < 0 ||
-      p->num_splits < 0)
+      p->num_splits < 0 || p->num_pages < 0)
     return MLA_ERR_SHAPE;
+  if (p->flags & ~MLA_FLAG_DEVICE_CHECKS) return MLA_ERR_SHAPE;
   if (p->batch > (1 << 20) || p->num_heads > 4096 || p->max_seqlen > (1 << 26))
     return MLA_ERR_SHAPE;
   if (!std::isfinite(p->softmax_scale) || !std::isfinite(p->out_scale) ||
@@ -45,6 +46,9 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
   q.elem = p->dtype == MLA_F32 ? 4 : 2;
   q.paged = p->page_size == kPage;
   q.max_seqlen = p->max_seqlen;
+  q.n_cu = (n_cu <= 0 || n_cu > kMaxCUs) ? kMaxCUs : n_cu;
+  q.checks = (p->flags & MLA_FLAG_DEVICE_CHECKS) ? 1 : 0;
+  q.num_pages = q.paged ? p->num_pages : 0;
 
   if (p->dtype == MLA_BF16) {
     const bool mla = q.NB == 1 && q.dcb == 512;
@@ -76,15 +80,18 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
       return MLA_ERR_SHAPE;
   }
 
-  // Split plan.  The device cuts sum_b ceil(L_b / 64) pages into work items of c whole pages
-  // each (a sequence of p_b pages gets ceil(p_b / c) items).  Automatic: c is the smallest
-  // count that keeps the items within `target` (enough workgroups to fill the chip once),
-  // one item per sequence if none does; forced: c = ceil(n_tiles / num_splits).
+  // Split plan.  Page plan: the device cuts sum_b ceil(L_b / 64) pages into work items of c
+  // whole pages each (a sequence of p_b pages gets ceil(p_b / c) items), one per dispatch
+  // slot.  Automatic: c is the smallest count that keeps the items within `target` (enough
+  // workgroups to fill the chip once), one item per sequence if none does; forced:
+  // c = ceil(n_tiles / num_splits).
   const int64_t wg_per_item = q.path != Path::kBf16Mfma ? q.H
                               : q.wide ? q.H / kWideHeads
                                        : q.n_hg;
-  const int64_t target_wg = q.wide ? kTargetWideWorkgroups : kTargetWorkgroups;
+  // workgroups that fill the chip once: the wide kernel holds one per CU, the others two
+  const int64_t target_wg = q.wide ? q.n_cu : 2 * (int64_t)q.n_cu;
   q.target = (int)std::max<int64_t>(1, ceil_div(target_wg, wg_per_item));
+  q.stream = 0;
   q.xcd_major = q.wide;
   int64_t cap;
   if (p->num_splits > 0) {
@@ -108,9 +115,12 @@ mla_status make_plan(const mla_params* p, Plan* plan) {
 
   // workspace: plan, absorbed queries, per-item partials, fp32 merged latent
   size_t off = 0;
-  q.off_work = 16;  // after the 4-word header
-  q.off_split_off = q.off_work + (size_t)q.slots * 16;
-  off = align_up(q.off_split_off + ((size_t)q.B + 1) * 4);
+  q.off_work = 4 * kHdrWords;
+  q.off_slot_end = q.off_work + (size_t)q.slots * 16;
+  q.off_items = q.off_slot_end + (size_t)q.slots * 4;
+  q.off_split_off = q.off_items + (size_t)q.items_cap * 16;
+  q.off_dbg = q.off_split_off + ((size_t)q.B + 1) * 4;
+  off = align_up(q.off_dbg + (size_t)q.B * 4);
   q.off_qcat = off;
   off = align_up(off + (size_t)q.B * q.H * q.row * q.elem);
   q.off_part_o = off;
@@ -169,8 +179,8 @@ const char* status_str(int32_t s) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for these dims/layout";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace smaller than mla_workspace_size";
     case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown dtype";
-    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: pointer or stride misaligned";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: pointer or stride misaligned";
     default: return "unknown mla_status";
   }
 }

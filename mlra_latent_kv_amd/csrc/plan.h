@@ -10,14 +10,18 @@
 
 namespace mla {
 
-constexpr int kPage = MLA_PAGE_SIZE;   // tokens per page == tokens per main-loop tile
-constexpr int kHeadGroup = 32;         // heads per workgroup of the bf16 main kernel
-constexpr int kTargetWorkgroups = 512; // two per CU of an MI355X (32-head kernel runs 2 per CU)
+constexpr int kPage = MLA_PAGE_SIZE;   // tokens per page
+constexpr int kTileTokens = 32;        // tokens per main-loop tile (the stream plan's unit)
+constexpr int kHeadGroup = 32;         // heads per workgroup of the 32-head bf16 kernels
 constexpr int kWideHeads = 128;        // heads per workgroup of the wide bf16 kernel
-constexpr int kTargetWideWorkgroups = 256;  // one per CU (the wide kernel fills a CU's LDS)
+constexpr int kMaxCUs = 256;           // compute units the workspace is sized for (MI355X);
+                                       // a device reporting more is planned as if it had 256
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxSplits = 512;        // bound on work items per sequence (the fp32 combine
                                        // keeps one weight per item in LDS)
+constexpr int kHdrWords = 8;           // plan header words at the start of the workspace
+constexpr int kPlanLdsBytes = 34816;   // LDS of the bf16 prologue workgroup that makes the
+                                       // plan (the stream plan keeps 3 B + 2 words there)
 
 enum class Path { kBf16Mfma, kF32Simt };
 
@@ -27,24 +31,33 @@ struct Plan {
   int paged;
   int max_seqlen;
   int n_tiles;   // ceil(max_seqlen / 64), >= 1
-  // Split plan.  The device cuts the batch into work items of whole pages (see
-  // plan_device.h); the host only bounds it.
-  int target;        // work items the automatic plan aims for (a workgroup set per CU slot)
+  int n_cu;      // compute units the plan is made for (1 .. kMaxCUs)
+  int checks;    // MLA_FLAG_DEVICE_CHECKS given: a check kernel runs before the prologue
+  int num_pages; // pool pages for the block-id check (0: not checked)
+  // Split plan.  The device cuts the batch into work items (see plan_device.h); the host only
+  // bounds it.
+  int stream;        // 1: stream plan (equal tile ranges per slot, several items per slot);
+                     // 0: page plan (items of c whole pages, one item per slot)
+  int target;        // slots the automatic plan fills (one workgroup set per CU slot)
   int forced_pages;  // pages per work item when num_splits is given, else 0
-  int splits;        // most work items one sequence can be cut into (<= kMaxSplits)
+  int splits;        // most work items one sequence can be cut into
   int items_cap;     // most work items of one call: sizes the partials
-  int slots;         // dispatch slots of the main kernels (items_cap rounded up to 8)
-  int xcd_major;     // 1: slot 8g + x takes item x * ceil(W / 8) + g (XCD-contiguous items)
+  int slots;         // dispatch slots of the main kernels (rounded up to 8)
+  int xcd_major;     // page plan: slot 8g + x takes item x * ceil(W / 8) + g
   int n_hg;      // head groups of the bf16 kernel (H / 32); 0 on the fp32 path
   int wide;      // 1: bf16 MLA with H % 128 == 0 runs the 128-heads-per-workgroup kernel
   Path path;
   // workspace layout (byte offsets); part_o holds bf16 on the bf16 path, fp32 otherwise.
-  // The plan comes first: header int32[4], work int32[slots][4], split_off int32[B + 1].
-  size_t off_work, off_split_off, off_qcat, off_part_o, off_part_ml, off_olat, bytes;
+  // The plan comes first: header int32[8], work int32[slots][4], slot_end int32[slots],
+  // items int32[items_cap][4], split_off int32[B + 1], device-check results int32[B].
+  size_t off_work, off_slot_end, off_items, off_split_off, off_dbg;
+  size_t off_qcat, off_part_o, off_part_ml, off_olat, bytes;
 };
 
-// Validates *p (shape, dtype, support, strides) and fills *plan.  Touches no device.
-mla_status make_plan(const mla_params* p, Plan* plan);
+// Validates *p (shape, dtype, support, strides) and fills *plan for a device with n_cu
+// compute units (n_cu <= 0 or > kMaxCUs: kMaxCUs, the bound the workspace size uses).
+// Touches no device.
+mla_status make_plan(const mla_params* p, Plan* plan, int n_cu = 0);
 
 // Per-call checks on top of make_plan: required pointers, alignment, workspace size,
 // and the branch count the entry point accepts (1 for mla_decode, 4 for mlra_decode).

@@ -1,23 +1,36 @@
 // Split plan of one decode call, made on the device from seqlens by one workgroup of 256
 // threads (an extra workgroup of the prologue launch, so the plan costs no launch).
 //
-// The main loop is split over the sequence (split-K): every sequence b with L_b tokens,
-// p_b = ceil(L_b / 64) pages, is cut into n_b = ceil(p_b / c) work items of c whole pages
-// (the last one ragged), item j covering tokens [64cj, min(L_b, 64c(j + 1))).  Work items
-// are numbered sequence-major; split_off[b] is the first item of sequence b and
-// split_off[B] = W, the item count, so the combine finds a variable number of splits per
-// sequence.  Sequences with no tokens get no item.
+// The main loop is split over the sequence (split-K).  A work item is a token range
+// [t_begin, t_end) of one sequence; its partial result (running max, running sum, latent
+// output) is merged with the other items of the sequence afterwards.  Items are numbered
+// sequence-major; split_off[b] is the first item of sequence b and split_off[B] = W, the item
+// count, so the merge finds a variable number of items per sequence.  Sequences with no
+// tokens get no item.  Two plans:
 //
-// Balance: every item costs at most c pages and one workgroup set per item fills the chip
-// once when W <= target, so the automatic plan takes the smallest c with
-// sum_b ceil(p_b / c) <= target (binary search; the sum only falls as c grows), or
-// c = max_b p_b (one item per sequence) when no c meets the target.  With num_splits given,
-// c is fixed by the host.
+//  * Page plan (one item per dispatch slot).  Every sequence b with L_b tokens,
+//    p_b = ceil(L_b / 64) pages, is cut into ceil(p_b / c) items of c whole pages (the last
+//    one ragged).  Automatic: c is the smallest count with sum_b ceil(p_b / c) <= target
+//    (binary search; the sum only falls as c grows), or c = max_b p_b when no c meets it.
+//    With num_splits given, c is fixed by the host.  With xcd_major the 8 XCDs get
+//    contiguous item ranges (slot 8g + x takes item x * ceil(W / 8) + g), otherwise slot s
+//    takes item s.
 //
-// Dispatch table: the main kernels map their blocks to slots; slot s holds
-// {b, t_begin, t_end, item} of the item it runs, or b = -1 when it has none.  With
-// xcd_major the 8 XCDs get contiguous item ranges (slot 8g + x takes item x * ceil(W/8) + g),
-// otherwise slot s takes item s.
+//  * Stream plan (equal shares, several items per slot).  The sequences' 32-token tiles are
+//    laid end to end, T = sum_b ceil(L_b / 32) tiles, and slot g of G = min(target, T) takes
+//    tiles [floor(g T / G), floor((g + 1) T / G)).  Items are the pieces of a sequence
+//    between consecutive cuts, where the cuts are the sequence ends and the slot boundaries;
+//    a slot runs its items in order.  Every slot gets T / G tiles to within one, whatever the
+//    lengths, and a slot crosses at most a few sequence ends.
+//
+// Dispatch tables: work[s] = {b, t_begin, t_end, item} of the first item of slot s (b = -1
+// for a slot without items), slot_end[s] = one past its last item, and items[i] =
+// {b, t_begin, t_end, slot} for every item.
+//
+// Device checks (MLA_FLAG_DEVICE_CHECKS): a separate kernel (k_device_checks) writes one
+// result word per sequence, dbg[b] = 4 * (first bad page index + 1, or 0) + error bits; the
+// plan folds them into the error word hdr[4..6] and, when a block id was out of range, makes
+// a plan with no items, so nothing reads outside the pool and every output is zero.
 #pragma once
 
 #include "device_common.h"
@@ -27,18 +40,26 @@ namespace mla {
 
 struct PlanArgs {
   const int32_t* seqlens;
-  int32_t* hdr;        // [4]: W, pages per item c, slots, target (0 when c was forced)
-  int32_t* work;       // [slots][4]: b, t_begin, t_end, item
+  const int32_t* dbg;  // [B] device-check results (checks only), else nullptr
+  int32_t* hdr;        // [8]: W, pages per item c (0: stream plan), slots, target (0 when c
+                       // was forced), error bits, first bad sequence, its first bad page,
+                       // items_cap
+  int32_t* work;       // [slots][4]: b, t_begin, t_end, item of the slot's first item
+  int32_t* slot_end;   // [slots]: one past the slot's last item
+  int32_t* items;      // [items_cap][4]: b, t_begin, t_end, slot
   int32_t* split_off;  // [B + 1]
-  int B, max_seqlen, target, forced_pages, slots, xcd_major;
+  int B, max_seqlen, target, forced_pages, slots, xcd_major, stream, items_cap;
 };
 
 inline PlanArgs plan_args(const Plan& p, const int32_t* seqlens, void* workspace) {
   char* ws = static_cast<char*>(workspace);
   PlanArgs a;
   a.seqlens = seqlens;
+  a.dbg = p.checks ? reinterpret_cast<const int32_t*>(ws + p.off_dbg) : nullptr;
   a.hdr = reinterpret_cast<int32_t*>(ws);
   a.work = reinterpret_cast<int32_t*>(ws + p.off_work);
+  a.slot_end = reinterpret_cast<int32_t*>(ws + p.off_slot_end);
+  a.items = reinterpret_cast<int32_t*>(ws + p.off_items);
   a.split_off = reinterpret_cast<int32_t*>(ws + p.off_split_off);
   a.B = p.B;
   a.max_seqlen = p.max_seqlen;
@@ -46,13 +67,15 @@ inline PlanArgs plan_args(const Plan& p, const int32_t* seqlens, void* workspace
   a.forced_pages = p.forced_pages;
   a.slots = p.slots;
   a.xcd_major = p.xcd_major;
+  a.stream = p.stream;
+  a.items_cap = p.items_cap;
   return a;
 }
 
-// LDS the planner needs at least: reduction scratch; more lets it keep the clamped lengths
-// and split_off on chip
+// LDS the planner needs at least: reduction scratch; more lets it keep the clamped lengths,
+// split_off and the tile offsets on chip
 constexpr int kPlanLdsMin = 64;
-// sequences per thread whose page counts stay in registers (the first 256 * kPlanRegs; any
+// sequences per thread whose lengths stay in registers (the first 256 * kPlanRegs; any
 // further ones are re-read from seqlens)
 constexpr int kPlanRegs = 4;
 
@@ -66,12 +89,14 @@ __device__ __forceinline__ int clamped_len(const PlanArgs& a, int b) {
   return min(max(a.seqlens[b], 0), a.max_seqlen);
 }
 __device__ __forceinline__ int pages_of_len(int L) { return (L + kPage - 1) / kPage; }
+__device__ __forceinline__ int tiles_of_len(int L) { return (L + kTileTokens - 1) / kTileTokens; }
 // ceil(p / c) for 0 <= p, 1 <= c < 2^21 (32-bit unsigned division)
 __device__ __forceinline__ int items_of(int p, int c) {
   return (int)(((unsigned)p + (unsigned)c - 1u) / (unsigned)c);
 }
+__device__ __forceinline__ long long cdiv64(long long a, long long b) { return (a + b - 1) / b; }
 
-// sum / max over the 256 threads; red: 4 slots of LDS (reused after a barrier)
+// sum / max / min over the 256 threads; red: 4 slots of LDS (reused after a barrier)
 __device__ __forceinline__ long long block_sum(long long v, long long* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -88,72 +113,19 @@ __device__ __forceinline__ long long block_max(long long v, long long* red) {
   __syncthreads();
   return max64(max64(red[0], red[1]), max64(red[2], red[3]));
 }
+__device__ __forceinline__ long long block_min(long long v, long long* red) {
+  return -block_max(-v, red);
+}
 
-}  // namespace plan_detail
-
-// Called by all 256 threads of one workgroup; lds: lds_bytes >= kPlanLdsMin of LDS, 8-byte
-// aligned.  The plan workgroup runs beside the prologue's own workgroups, so its latency is
-// kept short: one read of seqlens, page counts in registers, a search range of a few steps.
-__device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_bytes) {
-  using namespace plan_detail;
-  long long* red = static_cast<long long*>(lds);     // [4]
-  int* wsum = reinterpret_cast<int*>(red + 4);       // [4]
-  int* so_lds = wsum + 4;                            // split_off copy [B + 1], if it fits
-  int* len_lds = so_lds + (a.B + 1);                 // clamped lengths [B], if they fit
-  const bool on_chip = (long long)(2 * a.B + 1) * 4 <= lds_bytes - kPlanLdsMin;
+// Exclusive scan of n(b) over b = 0 .. B-1 (256 sequences per pass): out(b, offset) is called
+// for every b with its offset; returns the total.  wsum: 4 ints of LDS.
+template <typename N, typename Out>
+__device__ __forceinline__ long long block_scan(int B, N&& n_of, Out&& out, int* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-
-  int len[kPlanRegs];  // clamped lengths of sequences tid + 256 i
-#pragma unroll
-  for (int i = 0; i < kPlanRegs; ++i) {
-    const int b = tid + 256 * i;
-    len[i] = b < a.B ? clamped_len(a, b) : 0;
-  }
-  // f(pages of b) for every sequence this thread owns (b = tid, tid + 256, ...)
-  auto for_each = [&](auto&& f) {
-#pragma unroll
-    for (int i = 0; i < kPlanRegs; ++i) f(pages_of_len(len[i]));
-    for (int b = tid + 256 * kPlanRegs; b < a.B; b += 256) f(pages_of_len(clamped_len(a, b)));
-  };
-
-  // ---- pages per item
-  int c = a.forced_pages;
-  if (c == 0) {
-    long long P = 0, maxp = 0, nonempty = 0;
-    for_each([&](int p) {
-      P += p;
-      maxp = max64(maxp, p);
-      nonempty += p > 0;
-    });
-    P = block_sum(P, red);
-    nonempty = block_sum(nonempty, red);
-    maxp = max64(block_max(maxp, red), 1);
-    // W(c) = sum_b ceil(p_b / c) lies in [P / c, P / c + nonempty), so the answer is at
-    // least ceil(P / target), and c = ceil(P / (target - nonempty)) already fits
-    long long lo = min64(max64((P + a.target - 1) / a.target, 1), maxp), hi = maxp;
-    if (a.target > nonempty) hi = min64(hi, max64((P + (a.target - nonempty) - 1) / (a.target - nonempty), lo));
-    while (lo < hi) {  // uniform: every thread holds the same lo, hi
-      const int mid = (int)(lo + (hi - lo) / 2);
-      long long n = 0;
-      for_each([&](int p) { n += items_of(p, mid); });
-      n = block_sum(n, red);
-      if (n <= a.target) hi = mid;
-      else lo = mid + 1;
-    }
-    c = (int)lo;
-  }
-
-  // ---- items per sequence and split_off (exclusive scan, 256 sequences per pass)
-  int carry = 0;
-  for (int base = 0; base < a.B; base += 256) {
+  long long carry = 0;
+  for (int base = 0; base < B; base += 256) {
     const int b = base + tid;
-    const int i = base / 256;
-    int L = 0;  // (a select chain: a run-time index into len[] would put it in scratch)
-#pragma unroll
-    for (int j = 0; j < kPlanRegs; ++j)
-      if (i == j) L = len[j];
-    if (i >= kPlanRegs && b < a.B) L = clamped_len(a, b);
-    const int n = items_of(pages_of_len(L), c);
+    const int n = b < B ? n_of(b, base / 256) : 0;
     int x = n;  // inclusive scan over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -163,50 +135,220 @@ __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_byte
     __syncthreads();  // the previous pass is done with wsum
     if (lane == 63) wsum[w] = x;
     __syncthreads();
-    int off = carry + x - n;
+    long long off = carry + x - n;
     for (int k = 0; k < w; ++k) off += wsum[k];
-    if (b < a.B) {
-      a.split_off[b] = off;
-      if (on_chip) {
-        so_lds[b] = off;
-        len_lds[b] = L;
-      }
-    }
-    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (b < B) out(b, off);
+    carry += (long long)wsum[0] + wsum[1] + wsum[2] + wsum[3];
   }
-  const int W = carry;
-  if (tid == 0) {
-    a.split_off[a.B] = W;
-    if (on_chip) so_lds[a.B] = W;
-    a.hdr[0] = W;
-    a.hdr[1] = c;
-    a.hdr[2] = a.slots;
-    a.hdr[3] = a.forced_pages ? 0 : a.target;
-  }
-  __syncthreads();  // split_off complete (LDS and global) for the searches below
+  return carry;
+}
 
-  // ---- dispatch table: the sequence of an item is the last b with split_off[b] <= item
-  const int32_t* so = on_chip ? so_lds : a.split_off;
-  const int per = (W + 7) / 8;
-  for (int s = tid; s < a.slots; s += 256) {
-    int item = s;
-    if (a.xcd_major) {
-      const int x = s & 7, g = s >> 3;
-      item = g < per ? x * per + g : W;
-    }
-    int4 e = make_int4(-1, 0, 0, -1);
-    if (item < W) {
-      int lo = 0, hi = a.B;  // so[lo] <= item < so[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (so[mid] <= item) lo = mid;
-        else hi = mid;
+// last index lo in [0, n) with v[lo] <= x, given v[0] <= x (v non-decreasing)
+template <typename V>
+__device__ __forceinline__ int upper_index(V&& v, int n, long long x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((long long)v(mid) <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace plan_detail
+
+// Called by all 256 threads of one workgroup; lds: lds_bytes >= kPlanLdsMin of LDS, 8-byte
+// aligned.  The plan workgroup runs beside the prologue's own workgroups, so its latency is
+// kept short: one read of seqlens, lengths in registers, a search range of a few steps.
+__device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_bytes) {
+  using namespace plan_detail;
+  long long* red = static_cast<long long*>(lds);     // [4]
+  int* wsum = reinterpret_cast<int*>(red + 4);       // [4]
+  int* so_lds = wsum + 4;                            // split_off copy [B + 1], if it fits
+  int* len_lds = so_lds + (a.B + 1);                 // clamped lengths [B], if they fit
+  int* off_lds = len_lds + a.B;                      // stream plan: tile offsets [B + 1]
+  const bool on_chip = (long long)(3 * a.B + 2) * 4 <= lds_bytes - kPlanLdsMin;
+  const int tid = threadIdx.x;
+
+  // ---- device-check results: error word, and no items at all after a bad block id
+  long long err_bits = 0, err_key = 0x7fffffffffffffffLL;
+  if (a.dbg) {
+    for (int b = tid; b < a.B; b += 256) {
+      const int d = a.dbg[b];
+      if (d & 3) {
+        err_bits |= d & 3;
+        err_key = min64(err_key, ((long long)b << 32) | (unsigned)(d >> 2));
       }
-      const int L = on_chip ? len_lds[lo] : clamped_len(a, lo);
-      const int t0 = (item - so[lo]) * c * kPage;
-      e = make_int4(lo, t0, min(L, t0 + c * kPage), item);
     }
-    *reinterpret_cast<int4*>(a.work + 4 * s) = e;
+    err_bits = block_max(err_bits & 1, red) | (block_max(err_bits & 2, red));
+    err_key = block_min(err_key, red);
+  }
+  const bool drop_all = (err_bits & MLA_DEVERR_BLOCK) != 0;
+
+  int len[kPlanRegs];  // clamped lengths of sequences tid + 256 i
+#pragma unroll
+  for (int i = 0; i < kPlanRegs; ++i) {
+    const int b = tid + 256 * i;
+    len[i] = b < a.B && !drop_all ? clamped_len(a, b) : 0;
+  }
+  // clamped length of sequence b = base + tid in scan pass i (a select chain: a run-time
+  // index into len[] would put it in scratch)
+  auto len_at = [&](int b, int i) {
+    int L = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanRegs; ++j)
+      if (i == j) L = len[j];
+    if (i >= kPlanRegs) L = drop_all ? 0 : clamped_len(a, b);
+    return L;
+  };
+
+  if (!a.stream) {
+    // ================================================================== page plan
+    // f(pages of b) for every sequence this thread owns (b = tid, tid + 256, ...)
+    auto for_each = [&](auto&& f) {
+#pragma unroll
+      for (int i = 0; i < kPlanRegs; ++i) f(pages_of_len(len[i]));
+      for (int b = tid + 256 * kPlanRegs; b < a.B; b += 256)
+        f(drop_all ? 0 : pages_of_len(clamped_len(a, b)));
+    };
+    int c = a.forced_pages;
+    if (c == 0) {
+      long long P = 0, maxp = 0, nonempty = 0;
+      for_each([&](int p) {
+        P += p;
+        maxp = max64(maxp, p);
+        nonempty += p > 0;
+      });
+      P = block_sum(P, red);
+      nonempty = block_sum(nonempty, red);
+      maxp = max64(block_max(maxp, red), 1);
+      // W(c) = sum_b ceil(p_b / c) lies in [P / c, P / c + nonempty), so the answer is at
+      // least ceil(P / target), and c = ceil(P / (target - nonempty)) already fits
+      long long lo = min64(max64((P + a.target - 1) / a.target, 1), maxp), hi = maxp;
+      if (a.target > nonempty) hi = min64(hi, max64((P + (a.target - nonempty) - 1) / (a.target - nonempty), lo));
+      while (lo < hi) {  // uniform: every thread holds the same lo, hi
+        const int mid = (int)(lo + (hi - lo) / 2);
+        long long n = 0;
+        for_each([&](int p) { n += items_of(p, mid); });
+        n = block_sum(n, red);
+        if (n <= a.target) hi = mid;
+        else lo = mid + 1;
+      }
+      c = (int)lo;
+    }
+    // items per sequence and split_off
+    const int W = (int)block_scan(
+        a.B, [&](int b, int i) { return items_of(pages_of_len(len_at(b, i)), c); },
+        [&](int b, long long off) {
+          a.split_off[b] = (int)off;
+          if (on_chip) {
+            so_lds[b] = (int)off;
+            len_lds[b] = len_at(b, b / 256);
+          }
+        },
+        wsum);
+    if (tid == 0) {
+      a.split_off[a.B] = W;
+      if (on_chip) so_lds[a.B] = W;
+      a.hdr[0] = W;
+      a.hdr[1] = c;
+      a.hdr[3] = a.forced_pages ? 0 : a.target;
+    }
+    __syncthreads();  // split_off complete (LDS and global) for the searches below
+
+    // dispatch tables: the sequence of an item is the last b with split_off[b] <= item
+    const int32_t* so = on_chip ? so_lds : a.split_off;
+    const int per = (W + 7) / 8;
+    for (int s = tid; s < a.slots; s += 256) {
+      int item = s;
+      if (a.xcd_major) {
+        const int x = s & 7, g = s >> 3;
+        item = g < per ? x * per + g : W;
+      }
+      int4 e = make_int4(-1, 0, 0, -1);
+      if (item < W) {
+        const int b = upper_index([&](int i) { return so[i]; }, a.B, item);
+        const int L = on_chip ? len_lds[b] : clamped_len(a, b);
+        const int t0 = (item - so[b]) * c * kPage;
+        e = make_int4(b, t0, min(L, t0 + c * kPage), item);
+        *reinterpret_cast<int4*>(a.items + 4 * item) = make_int4(b, e.y, e.z, s);
+      }
+      *reinterpret_cast<int4*>(a.work + 4 * s) = e;
+      a.slot_end[s] = item < W ? item + 1 : 0;
+    }
+  } else {
+    // ================================================================== stream plan
+    // (the host chooses it only when the per-sequence arrays fit in LDS: on_chip holds)
+    // tile offsets S_b (exclusive scan of the tile counts) and the total T
+    const long long T = block_scan(
+        a.B, [&](int b, int i) { return tiles_of_len(len_at(b, i)); },
+        [&](int b, long long off) {
+          off_lds[b] = (int)off;
+          len_lds[b] = len_at(b, b / 256);
+        },
+        wsum);
+    const int G = (int)min64(a.target, T);  // slots in use
+    // slot boundary p_g = floor(g T / G); #{g >= 0 : p_g <= x} = ceil((x + 1) G / T), x < T
+    auto bound = [&](long long g) { return g * T / G; };
+    auto n_upto = [&](long long x) { return cdiv64((x + 1) * G, T); };
+    __syncthreads();  // tile offsets and lengths in LDS
+    // items of sequence b (tiles [S, S + n)): one, plus the slot boundaries strictly inside
+    const int W = (int)block_scan(
+        a.B,
+        [&](int b, int) {
+          const long long S = off_lds[b];
+          const int n = tiles_of_len(len_lds[b]);
+          return n > 0 ? (int)(1 + n_upto(S + n - 1) - n_upto(S)) : 0;
+        },
+        [&](int b, long long off) {
+          a.split_off[b] = (int)off;
+          so_lds[b] = (int)off;
+        },
+        wsum);
+    if (tid == 0) {
+      a.split_off[a.B] = W;
+      so_lds[a.B] = W;
+      a.hdr[0] = W;
+      a.hdr[1] = 0;
+      a.hdr[3] = a.target;
+    }
+    __syncthreads();  // split_off complete
+    // every item, a thread per sequence walking its items in order; the item that starts at
+    // a slot boundary opens that slot
+    for (int b = tid; b < a.B; b += 256) {
+      const long long S = off_lds[b];
+      const int L = len_lds[b], n = tiles_of_len(L);
+      int item = so_lds[b];
+      long long x = S, g = n > 0 ? n_upto(S) - 1 : 0;  // slot of tile S
+      while (x < S + n) {
+        const long long nb = bound(g + 1);  // next slot boundary (T when g = G - 1)
+        const long long e = min64(S + n, nb);
+        const int t0 = (int)((x - S) * kTileTokens), t1 = min(L, (int)((e - S) * kTileTokens));
+        *reinterpret_cast<int4*>(a.items + 4 * item) = make_int4(b, t0, t1, (int)g);
+        if (x == bound(g))
+          *reinterpret_cast<int4*>(a.work + 4 * g) = make_int4(b, t0, t1, item);
+        ++item;
+        x = e;
+        if (x == nb) ++g;
+      }
+    }
+    __syncthreads();  // every slot's first item is written (global, same workgroup)
+    // slot ends: the first item of the next slot, W for the last; idle slots have none
+    for (int s = tid; s < a.slots; s += 256) {
+      if (s < G) {
+        a.slot_end[s] = s + 1 < G ? a.work[4 * (s + 1) + 3] : W;
+      } else {
+        *reinterpret_cast<int4*>(a.work + 4 * s) = make_int4(-1, 0, 0, -1);
+        a.slot_end[s] = 0;
+      }
+    }
+  }
+  if (tid == 0) {
+    a.hdr[2] = a.slots;
+    a.hdr[4] = (int)err_bits;
+    a.hdr[5] = err_bits ? (int)(err_key >> 32) : -1;
+    a.hdr[6] = err_bits ? (int)(err_key & 0xffffffff) - 1 : -1;
+    a.hdr[7] = a.items_cap;
   }
 }
 

@@ -53,7 +53,7 @@ class DeviceCase:
         return self.out if out is None else out
 
 
-def make_params(inp: dict, num_splits: int = 0) -> B.MlaParams:
+def make_params(inp: dict, num_splits: int = 0, flags: int = 0) -> B.MlaParams:
     w = inp["workload"]
     cache = inp["cache"]
     row = w.row
@@ -65,6 +65,7 @@ def make_params(inp: dict, num_splits: int = 0) -> B.MlaParams:
     p.max_seqlen = int(inp["max_seqlen"])
     p.num_splits = num_splits
     p.dtype = B.MLA_BF16 if w.dtype == "bf16" else B.MLA_F32
+    p.flags = flags
     p.latent_stride_tok = p.rope_stride_tok = row
     if inp["paged"]:
         p.page_size = PAGE
@@ -72,6 +73,7 @@ def make_params(inp: dict, num_splits: int = 0) -> B.MlaParams:
         p.max_pages_per_seq = bt.shape[1]
         p.block_table_stride = bt.shape[1]
         p.latent_stride_seq = p.rope_stride_seq = PAGE * row
+        p.num_pages = cache.shape[0]
     else:
         p.page_size = 0
         p.latent_stride_seq = p.rope_stride_seq = cache.shape[1] * row
@@ -81,7 +83,8 @@ def make_params(inp: dict, num_splits: int = 0) -> B.MlaParams:
     return p
 
 
-def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None) -> DeviceCase:
+def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None,
+              flags: int = 0) -> DeviceCase:
     w = inp["workload"]
     dt = w.dtype
     dev = torch.device(device)
@@ -92,7 +95,7 @@ def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None) -> Dev
     B.mla_rope_rotate(cache.data_ptr() + w.d_c * cache.element_size(), w.row, row_pos, n_rows,
                       w.d_rope, w.rope_theta, B.MLA_BF16 if dt == "bf16" else B.MLA_F32,
                       stream=stream)
-    params = make_params(inp, num_splits)
+    params = make_params(inp, num_splits, flags)
     ws_bytes = B.workspace_size(params)
     bt = inp["block_table"]
     case = DeviceCase(
@@ -114,14 +117,24 @@ def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None) -> Dev
 
 def read_plan(case: DeviceCase) -> dict:
     """The split plan the last call left at the start of the workspace (layout documented in
-    include/mla_decode.h): item count W, pages per item c, dispatch slots, item target (0 when
-    the split count was forced), the dispatch table [slots, 4] = (b, t_begin, t_end, item)
-    and split_off [B + 1].  Synchronises with the device."""
+    include/mla_decode.h): item count W, pages per item c (0 for the stream plan), dispatch
+    slots, item target (0 when the split count was forced), the device-check error word
+    (bits, first bad sequence, its first bad block-table column), the per-slot table
+    [slots, 4] = (b, t_begin, t_end, item) of each slot's first item, slot_end [slots], the
+    item table [W, 4] = (b, t_begin, t_end, slot) and split_off [B + 1].  Synchronises with
+    the device."""
     ws = case.workspace
-    hdr = ws[:16].view(torch.int32).cpu().numpy()
-    slots = int(hdr[2])
-    work = ws[16:16 + 16 * slots].view(torch.int32).cpu().numpy().reshape(slots, 4)
-    off = 16 + 16 * slots
+    hdr = ws[:32].view(torch.int32).cpu().numpy()
+    W, slots, cap = int(hdr[0]), int(hdr[2]), int(hdr[7])
+    off = 32
+    work = ws[off:off + 16 * slots].view(torch.int32).cpu().numpy().reshape(slots, 4)
+    off += 16 * slots
+    slot_end = ws[off:off + 4 * slots].view(torch.int32).cpu().numpy()
+    off += 4 * slots
+    items = ws[off:off + 16 * cap].view(torch.int32).cpu().numpy().reshape(cap, 4)[:W]
+    off += 16 * cap
     split_off = ws[off:off + 4 * (case.params.batch + 1)].view(torch.int32).cpu().numpy()
-    return {"items": int(hdr[0]), "pages": int(hdr[1]), "slots": slots, "target": int(hdr[3]),
-            "work": work, "split_off": split_off}
+    return {"items": W, "pages": int(hdr[1]), "slots": slots, "target": int(hdr[3]),
+            "err_bits": int(hdr[4]), "err_seq": int(hdr[5]), "err_page": int(hdr[6]),
+            "items_cap": cap, "work": work, "slot_end": slot_end, "item_table": items,
+            "split_off": split_off}

@@ -5,10 +5,10 @@ none of the attention arithmetic. Both the fp64 CPU oracle (via the tests) and
 the HIP path consume what it produces, so the two sides see identical inputs.
 
 Shapes follow the pages' description of a latent KV cache: one compressed
-latent vector per token plus one decoupled rotary key per token ("Multi-Head
-Latent Attention explained", sections on joint low-rank KV compression and on
-decoupled RoPE); MLRA splits the latent into independent branches
-("Multi-Head Low-Rank Attention" blog, section 2.1).
+latent vector per token plus one decoupled rotary key per token ("超越 GQA 的推理
+革命…MLA…", sections 鍵值聯合低秩壓縮 and 解耦旋轉位置編碼); MLRA splits the latent
+into independent branches, each with its own latent head ("[ICLR 2025] MLRA…",
+section 2.1).
 
 Storage layout of one cache row: ``[c_KV (d_c) | k_rope (d_r)]`` with
 ``d_c = branches * d_cb``.  The rope columns hold the *raw* (un-rotated) key;
@@ -137,6 +137,37 @@ def sharp_q_gain(w: Workload, target_logit_std: float = 2.0) -> float:
     return target_logit_std / sigma0
 
 
+def _streams(seed: int):
+    """The eight independent child streams of one input set, in draw order: q_nope, q_rope,
+    latent rows, raw rotary keys, W_UK, W_UV, lengths, page permutation."""
+    kids = np.random.SeedSequence(seed).spawn(8)
+    return tuple(np.random.default_rng(k) for k in kids)
+
+
+def _normal(rng, shape, fan_in, gain=1.0):
+    return rng.standard_normal(shape, dtype=np.float32) * np.float32(gain / math.sqrt(fan_in))
+
+
+def _queries(w: Workload, B: int, r_qn, r_qr, q_gain: float):
+    """q_nope [B, H, NB, d_nope] (an independent vector per head and branch: each MLRA branch
+    has its own latent head, so its absorbed query differs) and q_rope [B, H, d_rope]."""
+    qn = _normal(r_qn, (B, w.heads, w.branches, w.d_nope), w.d_nope, q_gain)
+    qr = _normal(r_qr, (B, w.heads, w.d_rope), w.d_rope, q_gain)
+    return to_storage(qn, w.dtype), to_storage(qr, w.dtype)
+
+
+def requery(inp: dict, q_gain: float) -> dict:
+    """The same input set with its queries redrawn at gain ``q_gain`` (same seed, so the
+    same standard normals times a different gain); the cache and weights are shared, not
+    copied."""
+    w = inp["workload"]
+    r = _streams(inp["seed"])
+    out = dict(inp)
+    out["q_nope"], out["q_rope"] = _queries(w, len(inp["seqlens"]), r[0], r[1], q_gain)
+    out["q_gain"] = q_gain
+    return out
+
+
 def make_inputs(
     w: Workload,
     *,
@@ -157,7 +188,7 @@ def make_inputs(
     Returns a dict of NumPy arrays in storage format (float32, or uint16 bf16
     bits) plus metadata:
 
-    * ``q_nope``  [B, H, NB, d_nope]   (one vector per head, replicated over branches)
+    * ``q_nope``  [B, H, NB, d_nope]   (an independent vector per head and branch)
     * ``q_rope``  [B, H, d_rope]       un-rotated
     * ``cache``   contiguous [B, Lmax, d_c + d_rope] or paged pool [P, 64, d_c + d_rope];
                   rope columns are the raw (un-rotated) keys
@@ -168,8 +199,7 @@ def make_inputs(
     """
     seed = w.seed if seed is None else seed
     paged = w.paged if paged is None else paged
-    kids = np.random.SeedSequence(seed).spawn(8)
-    r_qn, r_qr, r_lat, r_kr, r_wk, r_wv, r_len, r_perm = (np.random.default_rng(k) for k in kids)
+    r_qn, r_qr, r_lat, r_kr, r_wk, r_wv, r_len, r_perm = _streams(seed)
 
     if seqlens is not None:
         lens = np.asarray(seqlens, dtype=np.int32)
@@ -182,12 +212,8 @@ def make_inputs(
     row = dc + dr
     st = np.float32 if w.dtype == "f32" else np.uint16
 
-    def normal(rng, shape, fan_in, gain=1.0):
-        return rng.standard_normal(shape, dtype=np.float32) * np.float32(gain / math.sqrt(fan_in))
-
-    qn = normal(r_qn, (B, H, 1, dn), dn, q_gain)
-    q_nope = to_storage(np.broadcast_to(qn, (B, H, NB, dn)), w.dtype)
-    q_rope = to_storage(normal(r_qr, (B, H, dr), dr, q_gain), w.dtype)
+    normal = _normal
+    q_nope, q_rope = _queries(w, B, r_qn, r_qr, q_gain)
     w_uk = to_storage(normal(r_wk, (NB, H, dn, dcb), dcb), w.dtype)
     w_uv = to_storage(normal(r_wv, (NB, H, dcb, dv), dcb), w.dtype)
 
@@ -238,7 +264,8 @@ def make_inputs(
             off += npages[b]
 
     return dict(
-        workload=w, dtype=w.dtype, paged=paged, page_size=PAGE if paged else 0,
+        workload=w, seed=seed, q_gain=q_gain,
+        dtype=w.dtype, paged=paged, page_size=PAGE if paged else 0,
         q_nope=q_nope, q_rope=q_rope, cache=cache, row_pos=row_pos.reshape(-1),
         seqlens=lens, block_table=block_table, w_uk=w_uk, w_uv=w_uv,
         max_seqlen=Lmax, softmax_scale=w.softmax_scale, out_scale=w.out_scale,

@@ -36,8 +36,44 @@ int main() {
     p.softmax_scale = (float)pick({0, 1});
     p.out_scale = 0.5f;
     p.rope_theta = (float)pick({0, 10000});
+    p.flags = (int)pick({0, 1, 2});
+    p.num_pages = (int)pick({-1, 0, 100, 1 << 20});
+    const int n_cu = (int)pick({0, 1, 32, 80, 256, 304});
+    if (it & 1) {
+      // every other iteration: a valid bf16 / fp32 workload with one field perturbed, so
+      // that accepted plans are exercised as often as rejections
+      const int kind = (int)pick({0, 1, 2, 3});
+      p.batch = (int)pick({1, 3, 64, 1000, 3000});
+      p.num_heads = kind == 3 ? 4 : (int)pick({32, 64, 128, 256});
+      p.num_branches = kind == 1 ? 4 : 1;
+      p.d_nope = kind == 3 ? 16 : 128;
+      p.d_v = kind == 3 ? 16 : 128;
+      p.d_latent = kind == 1 ? 128 : kind == 3 ? 32 : 512;
+      p.d_rope = kind == 3 ? 8 : 64;
+      p.dtype = kind == 3 ? 0 : 1;
+      p.page_size = (int)pick({0, 64});
+      p.max_seqlen = (int)pick({0, 1, 65, 4096, 131072});
+      p.max_pages_per_seq = (p.max_seqlen + 63) / 64;
+      p.block_table_stride = p.max_pages_per_seq + (int)pick({0, 8});
+      p.num_splits = (int)pick({0, 0, 1, 3});
+      if (p.num_splits > (p.max_seqlen + 63) / 64) p.num_splits = 0;
+      const int row = p.num_branches * p.d_latent + p.d_rope;
+      p.latent_stride_tok = p.rope_stride_tok = row;
+      p.latent_stride_seq = p.rope_stride_seq = (long long)row * (p.page_size ? 64 : p.max_seqlen);
+      p.softmax_scale = 0.07f;
+      p.rope_theta = 10000.0f;
+      p.flags = (int)pick({0, 1});
+      p.num_pages = (int)pick({0, 100});
+      switch ((int)pick({0, 1, 2, 3, 4, 5})) {  // one perturbation (or none)
+        case 1: p.batch = (int)pick({0, (1 << 20) + 1}); break;
+        case 2: p.num_splits = (int)pick({-1, 1 << 20}); break;
+        case 3: p.flags = 4; break;
+        case 4: p.latent_stride_tok = row - 1; break;
+        default: break;
+      }
+    }
     mla::Plan plan;
-    const mla_status st = mla::make_plan(&p, &plan);
+    const mla_status st = mla::make_plan(&p, &plan, n_cu);
     if (st == MLA_OK) {
       ++ok;
       // invariants of an accepted plan
@@ -51,11 +87,24 @@ int main() {
                       plan.items_cap != (long long)p.batch * plan.splits)) ||
           (!forced && (plan.forced_pages != 0 || plan.items_cap < plan.target ||
                        plan.items_cap < p.batch)) ||
-          plan.off_work != 16 || plan.off_split_off != 16 + 16 * (size_t)plan.slots ||
-          plan.off_qcat < plan.off_split_off + 4 * ((size_t)p.batch + 1) ||
+          plan.n_cu < 1 || plan.n_cu > mla::kMaxCUs ||
+          (n_cu >= 1 && n_cu <= mla::kMaxCUs && plan.n_cu != n_cu) ||
+          plan.off_work != 4 * mla::kHdrWords ||
+          plan.off_slot_end != plan.off_work + 16 * (size_t)plan.slots ||
+          plan.off_items != plan.off_slot_end + 4 * (size_t)plan.slots ||
+          plan.off_split_off != plan.off_items + 16 * (size_t)plan.items_cap ||
+          plan.off_dbg != plan.off_split_off + 4 * ((size_t)p.batch + 1) ||
+          plan.off_qcat < plan.off_dbg + 4 * (size_t)p.batch ||
           plan.off_part_o < plan.off_qcat || plan.off_part_ml < plan.off_part_o ||
           plan.off_olat < plan.off_part_ml || plan.bytes < plan.off_olat) {
         std::printf("bad plan at iteration %d\n", it);
+        return 1;
+      }
+      // a plan for fewer compute units never needs more workspace than the bound
+      mla::Plan bound;
+      if (mla::make_plan(&p, &bound) != MLA_OK || bound.bytes < plan.bytes ||
+          bound.items_cap < plan.items_cap || bound.slots < plan.slots) {
+        std::printf("plan for %d CUs exceeds the workspace bound at iteration %d\n", n_cu, it);
         return 1;
       }
     } else {

@@ -35,11 +35,30 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name)
 
 
+def test_probe_library_exports_its_header(lib):
+    """The read-stream probe (benchmark support) exports what include/mla_probe.h declares."""
+    from mlra_latent_kv_amd import build
+    declared = B.header_functions(os.path.join(ROOT, "include", "mla_probe.h"))
+    assert set(declared) == {"mla_probe_out_words", "mla_probe_read"}
+    out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared) <= exported
+    probe = ctypes.CDLL(build.PROBE_LIB)
+    probe.mla_probe_out_words.restype = ctypes.c_size_t
+    assert probe.mla_probe_out_words() == 2048 * 4
+    probe.mla_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    assert probe.mla_probe_read(None, 16, FAKE, None) == 1       # rejected before any launch
+    assert probe.mla_probe_read(FAKE, 24, FAKE, None) == 1
+
+
 def test_params_struct_layout_matches_header():
-    # 12 int32, 5 int64, 3 float -> 48 + 40 + 12 = 100, padded to 104
-    assert ctypes.sizeof(B.MlaParams) == 104
-    assert B.MlaParams.latent_stride_tok.offset == 48
-    assert B.MlaParams.softmax_scale.offset == 88
+    # 14 int32, 5 int64, 3 float -> 56 + 40 + 12 = 108, padded to 112
+    assert ctypes.sizeof(B.MlaParams) == 112
+    assert B.MlaParams.flags.offset == 48 and B.MlaParams.num_pages.offset == 52
+    assert B.MlaParams.latent_stride_tok.offset == 56
+    assert B.MlaParams.softmax_scale.offset == 96
 
 
 def params_for(wname, **over):
@@ -72,7 +91,9 @@ def call(lib, p, fn="mla_decode", ws_bytes=1 << 40, **ptr):
     (dict(num_heads=48), 3),
     (dict(d_nope=64), 3),
     (dict(latent_stride_tok=500), 2),
-    (dict(latent_stride_tok=580), 6),
+    (dict(latent_stride_tok=580), 7),
+    (dict(flags=2), 2),
+    (dict(num_pages=-1), 2),
     (dict(softmax_scale=float("nan")), 2),
     (dict(rope_theta=0.0), 2),
     (dict(num_splits=1000), 2),
@@ -82,7 +103,7 @@ def test_invalid_params_rejected(lib, over, status):
     assert call(lib, p) == status
     n = ctypes.c_size_t(0)
     st = lib.mla_workspace_size(ctypes.byref(p), ctypes.byref(n))
-    assert st == status or (status in (1, 4, 6) and st == 0)
+    assert st == status or (status in (1, 4, 7) and st == 0)
 
 
 def test_branch_count_per_entry_point(lib):
@@ -107,9 +128,9 @@ def test_workspace_and_alignment(lib):
     p = params_for("mla_bf16_b32_h128_l4096")
     need = B.workspace_size(p)
     assert call(lib, p, ws_bytes=need - 1) == 4
-    assert call(lib, p, latent=FAKE + 8) == 6
-    assert call(lib, p, workspace=FAKE + 64) == 6
-    assert call(lib, p, w_uk=FAKE + 2) == 6     # bf16 weights need 16-byte alignment
+    assert call(lib, p, latent=FAKE + 8) == 7
+    assert call(lib, p, workspace=FAKE + 64) == 7
+    assert call(lib, p, w_uk=FAKE + 2) == 7     # bf16 weights need 16-byte alignment
 
 
 def test_rope_rotate_validation(lib):
@@ -119,7 +140,7 @@ def test_rope_rotate_validation(lib):
     assert f(FAKE, 64, FAKE, 10, 64, 1e4, 3, None) == 5
     assert f(None, 64, FAKE, 10, 64, 1e4, 1, None) == 1
     assert f(None, 64, None, 0, 64, 1e4, 1, None) == 0     # empty: nothing to do
-    assert f(FAKE + 1, 64, FAKE, 10, 64, 1e4, 1, None) == 6
+    assert f(FAKE + 1, 64, FAKE, 10, 64, 1e4, 1, None) == 7
 
 
 def test_status_strings(lib):
@@ -154,9 +175,11 @@ def test_workspace_layout(lib, wname, forced):
         cap = max(target, Bn)
     slots = -(-cap // 8) * 8
     al = lambda x: (x + 255) // 256 * 256
-    # plan (header, dispatch table, split offsets), queries, per-item partials (element type
-    # on the bf16 path), (m, l) in fp32, and the fp32 merged latent
-    exp = al(16 + 16 * slots + 4 * (Bn + 1)) + al(Bn * H * w.row * w.elem_bytes) + \
+    # plan (header, slot table, slot ends, item table, split offsets, device-check words),
+    # queries, per-item partials (element type on the bf16 path), (m, l) in fp32, and the
+    # fp32 merged latent; the workspace is sized for 256 compute units
+    exp = al(32 + 16 * slots + 4 * slots + 16 * cap + 4 * (Bn + 1) + 4 * Bn) + \
+        al(Bn * H * w.row * w.elem_bytes) + \
         al(cap * H * dc * w.elem_bytes) + al(cap * w.branches * H * 2 * 4) + \
         (al(Bn * H * dc * 4) if w.elem_bytes == 4 else 0)
     assert B.workspace_size(p) == exp
@@ -201,43 +224,37 @@ def test_plan_code_under_host_sanitizers(tmp_path):
 
 
 def test_plan_checker_rejects_wrong_plans():
-    """The GPU tests judge the device's split plan with test_gpu_parity.check_plan; here that
-    checker is shown to reject plans with a plausible mistake (pages per item one too many or
-    one too few, a shifted item, a wrong split offset, a missed empty slot), on a plan built
-    from its definition."""
+    """The GPU tests compare the device's split plan with plan_ref.expected_plan through
+    plan_ref.check_plan; here that comparison is shown to reject plans with a plausible
+    mistake (pages per item one too many, a shifted item, a wrong split offset, a missed idle
+    slot, a wrong slot end, a stream-plan item cut at the wrong tile)."""
+    import copy
     import numpy as np
-    from test_gpu_parity import check_plan
-    w = I.WORKLOADS["mla_bf16_b32_h128_l4096"]          # wide kernel: XCD-major slots
+    from plan_ref import check_plan, expected_plan
     lens = [0, 1, 64, 65, 4000, 0, 129, 3000, 77, 2048]
-    target, slots, max_seqlen = 256, 256, 4000
+    good = expected_plan(lens, 4000, 256, 256, xcd_major=True)
+    assert good["pages"] == 1 and good["items"] == 151  # 151 pages fit 256 items at c = 1
+    check_plan(copy.deepcopy(good), good)
+    forced = expected_plan(lens, 4000, 256, 80, forced=5)
+    assert forced["pages"] == 13                        # ceil(63 / 5) pages per item
+    stream = expected_plan(lens, 4000, 20, 24, stream=True)
+    check_plan(copy.deepcopy(stream), stream)
+    # stream plan: 20 slots share 297 tiles (14 or 15 each); every slot opens with an item
+    # and its items are consecutive
+    t = sum(-(-L // 32) for L in lens)
+    assert t == 297 and np.all(stream["slot_end"][:20] > stream["work"][:20, 3])
+    assert np.all(stream["work"][1:20, 3] == stream["slot_end"][:19])
 
-    def build(c, forced=0):
-        pages = [-(-min(L, max_seqlen) // 64) for L in lens]
-        n = [-(-p // c) for p in pages]
-        so = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
-        W = int(so[-1]); per = -(-W // 8)
-        work = np.full((slots, 4), -1, np.int64)
-        work[:, 1:3] = 0
-        for s_ in range(slots):
-            x, g = s_ % 8, s_ // 8
-            item = x * per + g if g < per else W
-            if item < W:
-                b = int(np.searchsorted(so, item, side="right") - 1)
-                t0 = (item - so[b]) * c * 64
-                work[s_] = (b, t0, min(lens[b], t0 + c * 64), item)
-        return {"items": W, "pages": c, "slots": slots, "target": 0 if forced else target,
-                "work": work, "split_off": so}
+    def bad_plans():
+        p = copy.deepcopy(good); p["pages"] = 2; yield p, good
+        p = copy.deepcopy(good); p["work"][0, 1] += 64; yield p, good
+        p = copy.deepcopy(good); p["split_off"][3] += 1; yield p, good
+        p = copy.deepcopy(good)
+        p["work"][np.where(p["work"][:, 0] < 0)[0][0]] = (0, 0, 1, 0); yield p, good
+        p = copy.deepcopy(good); p["slot_end"][0] += 1; yield p, good
+        p = copy.deepcopy(stream); p["item_table"][3, 2] -= 32; yield p, stream
+        p = copy.deepcopy(stream); p["slot_end"][5] = p["slot_end"][6]; yield p, stream
 
-    good = build(1)                                      # 151 pages fit 256 items at c = 1
-    check_plan(good, w, lens, max_seqlen, 0)
-    check_plan(build(13, forced=5), w, lens, max_seqlen, 5)  # ceil(63 / 5) pages per item
-    bad = []
-    bad.append(build(2))                                 # not the smallest fitting c
-    bad.append(build(12, forced=5))                      # forced page count off by one
-    p = build(1); p["work"] = p["work"].copy(); p["work"][0, 1] += 64; bad.append(p)
-    p = build(1); p["split_off"] = p["split_off"].copy(); p["split_off"][3] += 1; bad.append(p)
-    p = build(1); p["work"] = p["work"].copy()
-    p["work"][np.where(p["work"][:, 0] < 0)[0][0]] = (0, 0, 1, 0); bad.append(p)
-    for i, p in enumerate(bad):
+    for got, want in bad_plans():
         with pytest.raises(AssertionError):
-            check_plan(p, w, lens, max_seqlen, 5 if i == 1 else 0)
+            check_plan(got, want)

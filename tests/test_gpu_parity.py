@@ -1,6 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
 inputs.  Tolerance for bf16 storage with fp32 accumulation: max abs error <= 2e-2 and
-relative L2 <= 1e-2 over the whole output; the fp32 path must agree to 1e-5.
+relative L2 <= 1e-2 over the whole output, and relative L2 <= 3e-2 for every (sequence,
+head) output row on its own (so one wrong head among thousands cannot hide in the whole-
+output norm); the fp32 path must agree to 1e-5 on both.
 
 Under the default value distribution the attention is close to uniform, so every bf16 case
 also runs a "sharp" variant (query scaled so logits have std ~2), and negative controls
@@ -16,10 +18,20 @@ import pytest
 
 from oracle import mla_oracle as O
 from mlra_latent_kv_amd import inputs as I
+from plan_ref import check_plan, expected_plan
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-5, 1e-5)}
+# worst relative L2 of a single (sequence, head) row.  Each output row is a 128-element
+# vector; its error is three bf16 roundings (weights, partial outputs, result) of ~2^-9
+# each (about 2e-3 together), plus the absorbed query's rounding, which moves a peaked
+# row's weights by a few parts in a thousand per log2 unit of logit.  Measured on MI355X:
+# worst rows of 1e-3 .. 1.5e-2 under the default and sharp queries, and up to 3.4e-2 for
+# the 128-head kernel's 512 rows of the late-raise ramp (logits to 40 log2 units).  A head
+# that is 10 % wrong (a lost split, a wrong head's or branch's query, a dropped branch)
+# falls outside 5e-2.
+ROW_TOL = {"bf16": 5e-2, "f32": 1e-5}
 
 
 def note(msg):
@@ -52,13 +64,26 @@ def gpu_out(inp, num_splits=0):
     return out.float().cpu().numpy().astype(np.float64), case
 
 
+def worst_row_rel_l2(got, ref):
+    """Largest relative L2 error over the output rows (the last axis is one (b, h) output);
+    rows whose reference is exactly zero (empty sequences) must be exactly zero."""
+    g = got.reshape(-1, got.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    rn = np.linalg.norm(r, axis=1)
+    en = np.linalg.norm(g - r, axis=1)
+    zero = rn == 0
+    assert np.all(en[zero] == 0), "an empty sequence's output is not zero"
+    return float((en[~zero] / rn[~zero]).max()) if (~zero).any() else 0.0
+
+
 def assert_close(got, ref, dtype, what=""):
     max_abs_tol, rel_tol = TOL[dtype]
     err = float(np.abs(got - ref).max()) if got.size else 0.0
     rl = rel_l2(got, ref) if got.size else 0.0
-    note(f"  {what}: max_abs={err:.3e} rel_l2={rl:.3e}")
+    row = worst_row_rel_l2(got, ref) if got.size else 0.0
+    note(f"  {what}: max_abs={err:.3e} rel_l2={rl:.3e} worst_row_rel_l2={row:.3e}")
     assert np.all(np.isfinite(got))
-    assert err <= max_abs_tol and rl <= rel_tol, (what, err, rl)
+    assert err <= max_abs_tol and rl <= rel_tol and row <= ROW_TOL[dtype], (what, err, rl, row)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -169,6 +194,24 @@ def test_late_raises(wname, splits):
     ramp_rows(inp, 0.1, 3.0)
     got, _ = gpu_out(inp, num_splits=splits)
     assert_close(got, oracle_out(inp), "bf16", f"{wname} splits={splits}")
+
+
+@pytest.mark.xfail(reason="known precision limit: at logits beyond ~65 log2 units the absorbed "
+                          "query's bf16 rounding (relative 2^-9) moves the softmax weights by "
+                          "percents; max-abs error reaches 0.026-0.028 > 2e-2 on the 128-head "
+                          "and MLRA-4 kernels (0.017 on the 32-head MLA kernel)",
+                   strict=False)
+@pytest.mark.parametrize("wname", BF16[:3])
+def test_steep_ramp_known_limit(wname):
+    """Rows scaled 0.25x .. 6x along the sequence with a sharp query (|logit| up to 72-81
+    log2 units): outside the max-abs tolerance, kept in the suite as an expected failure.
+    A sweep of the ramp's top (3.0 .. 6.0) held max-abs <= 2e-2 on every kernel up to
+    |logit| ~ 60 log2 units and first exceeded it at 65-66 (32-head and MLRA-4 kernels)."""
+    w = I.WORKLOADS[wname]
+    inp = I.make_inputs(w, seqlens=[4000, 2500, 700, 33], q_gain=I.sharp_q_gain(w))
+    ramp_rows(inp, 0.25, 6.0)
+    got, _ = gpu_out(inp)
+    assert_close(got, oracle_out(inp), "bf16", f"{wname} steep ramp")
 
 
 @pytest.mark.parametrize("wname", ["mla_bf16_b32_h128_l4096", "mlra4_bf16_b32_h32_l8192"])
@@ -338,6 +381,13 @@ def test_negative_controls_fail_the_tolerance(wname):
         wv = inp["w_uv"].copy()
         wv[2] = 0
         controls["branch 2 dropped"] = dict(w_uv=wv)
+        # each branch has its own query: reading branch 0's for every branch, or two
+        # branches' queries swapped, must show
+        qn = inp["q_nope"].copy()
+        qn[:, :, [0, 1]] = qn[:, :, [1, 0]]
+        controls["branch queries 0 and 1 swapped"] = dict(q_nope=qn)
+        controls["branch 0 query for every branch"] = dict(
+            q_nope=np.repeat(inp["q_nope"][:, :, :1], 4, axis=2))
     if inp["block_table"] is not None:
         bt = inp["block_table"].copy()
         bt[0, [0, 1]] = bt[0, [1, 0]]
@@ -351,44 +401,36 @@ def test_negative_controls_fail_the_tolerance(wname):
 
 # ----------------------------------------------------------------------------- split plan
 
-def check_plan(plan, w, lens, max_seqlen, forced):
-    """The device's split plan against its definition, worked out here from the lengths:
-    items of c whole pages per sequence (ceil(p_b / c) of them), c the smallest count whose
-    items fit the target (or the longest sequence's pages when none does), or fixed by the
-    forced split count; sequence-major item numbers; and the dispatch table the main kernels
-    read."""
-    cdiv = lambda a, b: -(-a // b)
-    W, c, slots, target = plan["items"], plan["pages"], plan["slots"], plan["target"]
-    pages = [cdiv(min(max(L, 0), max_seqlen), 64) for L in lens]
-    count = lambda cc: sum(cdiv(p, cc) for p in pages)
+def n_cu():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def plan_kind(w, H=None):
+    """(stream plan?, XCD-major slots?, workgroups filling the GPU once per item target) of
+    the kernel that runs workload w with H heads."""
+    H = w.heads if H is None else H
+    cu = min(n_cu(), 256)
+    if w.dtype != "bf16":
+        return False, False, -(-2 * cu // H)
+    if w.branches == 1 and H % 128 == 0:
+        return False, True, -(-cu // (H // 128))
+    return False, False, -(-2 * cu // (H // 32))
+
+
+def device_plan_matches(case, w, lens, forced=0, H=None):
+    """The device's plan equals the plan worked out from its definition (plan_ref), for the
+    target this device's compute-unit count gives."""
+    from mlra_latent_kv_amd import harness as Hn
+    plan = Hn.read_plan(case)
+    stream, xcd, target = plan_kind(w, H)
     if forced:
-        assert target == 0 and c == cdiv(max(1, cdiv(max_seqlen, 64)), forced)
-    else:
-        maxp = max(max(pages), 1)
-        assert target >= 1
-        if count(maxp) <= target:
-            assert count(c) <= target and (c == 1 or count(c - 1) > target), (c, target)
-        else:
-            assert c == maxp
-    n = [cdiv(p, c) for p in pages]
-    so = plan["split_off"]
-    assert list(so) == list(np.concatenate([[0], np.cumsum(n)])) and W == so[-1]
-    wide = w.dtype == "bf16" and w.branches == 1 and w.heads % 128 == 0
-    per = cdiv(W, 8)
-    seen = np.zeros(W, np.int64)
-    for s_, (b, t0, t1, item) in enumerate(plan["work"]):
-        exp = s_
-        if wide:
-            x, g = s_ % 8, s_ // 8
-            exp = x * per + g if g < per else W
-        if exp >= W:
-            assert b == -1, (s_, plan["work"][s_])
-            continue
-        assert item == exp and so[b] <= item < so[b + 1], (s_, b, item)
-        j = item - so[b]
-        assert t0 == j * c * 64 and t1 == min(lens[b], t0 + c * 64) and t0 < t1
-        seen[item] += 1
-    assert np.all(seen == 1)
+        stream = False
+    want = expected_plan(lens, case.params.max_seqlen, target, plan["slots"], forced=forced,
+                         xcd_major=xcd, stream=stream)
+    check_plan(plan, want)
+    assert plan["err_bits"] == 0 and plan["err_seq"] == -1 and plan["err_page"] == -1
+    return plan
 
 
 PLAN_CASES = [
@@ -397,52 +439,135 @@ PLAN_CASES = [
     ("mla_bf16_b32_h128_l4096", [0, 1, 64, 65, 4000, 0, 129, 3000, 77, 2048], 5),
     # 32-head MLA: one long sequence among short ones takes most of the items
     ("mla_bf16_paged_b64_h32_l1k-32k", [9000, 1, 70, 0, 300], 0),
+    ("mla_bf16_paged_b64_h32_l1k-32k", [9000, 1, 70, 0, 300], 3),
     # MLRA-4 with more sequences than the item target: one item per sequence
     ("mlra4_bf16_b32_h32_l8192", [1 + (37 * i) % 200 for i in range(600)], 0),
+    # fp32 path
+    ("tiny_mla_f32_b1_h4_l64", [64, 0, 5, 130], 0),
 ]
 
 
 @pytest.mark.parametrize("wname,lens,forced", PLAN_CASES,
                          ids=[f"{c[0]}-B{len(c[1])}-F{c[2]}" for c in PLAN_CASES])
 def test_split_plan(wname, lens, forced):
-    from mlra_latent_kv_amd import harness as H
     w = I.WORKLOADS[wname]
     inp = I.make_inputs(w, seqlens=lens, q_gain=I.sharp_q_gain(w))
     got, case = gpu_out(inp, num_splits=forced)
-    plan = H.read_plan(case)
-    note(f"  {wname}: {plan['items']} items of {plan['pages']} pages, target {plan['target']}")
-    check_plan(plan, w, lens, case.params.max_seqlen, forced)
+    plan = device_plan_matches(case, w, lens, forced)
+    note(f"  {wname}: {plan['items']} items, c={plan['pages']}, target {plan['target']}")
     bs = list(range(min(len(lens), 40)))
-    assert_close(got[bs], oracle_out(inp, batches=bs), "bf16", f"{wname} plan F{forced}")
+    assert_close(got[bs], oracle_out(inp, batches=bs), w.dtype, f"{wname} plan F{forced}")
     if len(lens) > len(bs):
         assert np.all(np.isfinite(got))
 
 
+# ----------------------------------------------------------------------------- device checks
+
+def test_device_checks_clean_inputs_change_nothing():
+    """MLA_FLAG_DEVICE_CHECKS on valid inputs: error word clear, output bit-identical."""
+    import torch
+    from mlra_latent_kv_amd import binding as B
+    from mlra_latent_kv_amd import harness as Hn
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    inp = I.make_inputs(w, seqlens=[700, 64, 1, 2000], q_gain=I.sharp_q_gain(w))
+    plain = Hn.to_device(inp)
+    plain.run()
+    checked = Hn.to_device(inp, flags=B.MLA_FLAG_DEVICE_CHECKS)
+    checked.run()
+    torch.cuda.synchronize()
+    plan = Hn.read_plan(checked)
+    assert (plan["err_bits"], plan["err_seq"], plan["err_page"]) == (0, -1, -1)
+    assert torch.equal(plain.out, checked.out)
+
+
+def test_device_checks_report_out_of_range_seqlens():
+    """Lengths outside [0, max_seqlen] are reported (first offending sequence) and clamped:
+    the output equals that of the clamped lengths.  Every read stays inside the cache."""
+    import torch
+    from mlra_latent_kv_amd import binding as B
+    from mlra_latent_kv_amd import harness as Hn
+    w = I.WORKLOADS["mla_bf16_b32_h128_l4096"]
+    lens = [300, 0, 130, 77]
+    inp = I.make_inputs(w, seqlens=lens, q_gain=I.sharp_q_gain(w))  # max_seqlen = 300
+    ref = Hn.to_device(inp)
+    ref.run()
+    case = Hn.to_device(inp, flags=B.MLA_FLAG_DEVICE_CHECKS)
+    case.seqlens.copy_(torch.tensor([301, -5, 130, 77], dtype=torch.int32))
+    case.run()
+    torch.cuda.synchronize()
+    plan = Hn.read_plan(case)
+    assert (plan["err_bits"], plan["err_seq"], plan["err_page"]) == (B.MLA_DEVERR_SEQLEN, 0, -1)
+    assert torch.equal(ref.out, case.out)
+
+
+def test_device_checks_report_block_ids_beyond_the_pool():
+    """A used block-table entry outside [0, num_pages) is reported (first sequence, first
+    column) and the call runs no work item: every output is zero.  The test declares a pool
+    smaller than the real one, so every entry still lies inside the allocation."""
+    import torch
+    from mlra_latent_kv_amd import binding as B
+    from mlra_latent_kv_amd import harness as Hn
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    lens = [700, 64, 1, 2000]
+    inp = I.make_inputs(w, seqlens=lens, q_gain=I.sharp_q_gain(w))
+    case = Hn.to_device(inp, flags=B.MLA_FLAG_DEVICE_CHECKS)
+    P = case.params.num_pages
+    limit = P - 5
+    bt = inp["block_table"]
+    bad = [(b, j) for b in range(len(lens)) for j in range(-(-lens[b] // 64)) if bt[b, j] >= limit]
+    assert bad, "the seed gives no entry in the last five pages"
+    case.params.num_pages = limit
+    case.out.fill_(1.0)
+    case.run()
+    torch.cuda.synchronize()
+    plan = Hn.read_plan(case)
+    assert plan["err_bits"] == B.MLA_DEVERR_BLOCK
+    assert (plan["err_seq"], plan["err_page"]) == min(bad)
+    assert plan["items"] == 0 and np.all(plan["work"][:, 0] == -1)
+    assert bool((case.out == 0).all())
+
+
 # ----------------------------------------------------------------------------- full sizes
 
+# (sequences, heads) sampled at full size: at least one head of every wave / head group of the
+# kernel that runs the workload (32 heads per wave), the first and last sequences, and for the
+# varied lengths the longest sequence (b = 11, 31,799 tokens) and the shortest.
 SAMPLES = {
-    "mla_bf16_b32_h128_l4096": ([0, 17, 31], [0, 63, 127]),
-    "mla_bf16_paged_b64_h32_l1k-32k": ([0, 21, 63], [0, 31]),
+    "mla_bf16_b32_h128_l4096": ([0, 17, 31], [0, 40, 70, 127]),
+    "mla_bf16_paged_b64_h32_l1k-32k": ([0, 11, 21, 63], [0, 17, 31]),
     "mlra4_bf16_b32_h32_l8192": ([0, 31], [0, 13, 31]),
-    "mla_bf16_paged_b4_h128_l131072": ([0, 3], [5, 120]),
+    "mla_bf16_paged_b4_h128_l131072": ([0, 3], [5, 40, 70, 120]),
 }
 
 
 @pytest.mark.parametrize("wname", list(SAMPLES))
 def test_full_size_sampled(wname):
     """Each workload at full size, in the launch configuration the benchmark times, checked on
-    sampled (sequence, head) outputs that the oracle computes one by one; every output must be
-    finite."""
+    sampled (sequence, head) outputs that the oracle computes one by one, with the default
+    query and with a sharp one (logit std ~2, attention that depends on the query); every
+    output must be finite, and the device's plan must match its definition."""
     import torch
+    from mlra_latent_kv_amd import harness as H
     w = I.WORKLOADS[wname]
     note(f"  generating {wname}")
     inp = I.make_inputs(w)
-    got, case = gpu_out(inp)
-    from mlra_latent_kv_amd import harness as H
-    check_plan(H.read_plan(case), w, list(inp["seqlens"]), case.params.max_seqlen, 0)
+    lens = [int(x) for x in inp["seqlens"]]
+    bs, hs = SAMPLES[wname]
+    if wname == "mla_bf16_paged_b64_h32_l1k-32k":
+        assert bs[1] == int(np.argmax(lens)), "the sample must hold the longest sequence"
+        bs = bs + [int(np.argmin(lens))]
+    case = H.to_device(inp)
+    for sharp in (False, True):
+        if sharp:
+            inp = I.requery(inp, I.sharp_q_gain(w))
+            case.q_nope.copy_(H._to_dev(inp["q_nope"], w.dtype, case.q_nope.device))
+            case.q_rope.copy_(H._to_dev(inp["q_rope"], w.dtype, case.q_rope.device))
+        out = case.run()
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        device_plan_matches(case, w, lens)
+        assert np.all(np.isfinite(got))
+        ref = oracle_out(inp, batches=bs, heads=hs)
+        assert_close(got[np.ix_(bs, hs)], ref, "bf16", f"{wname} sampled sharp={sharp}")
     del case
     torch.cuda.empty_cache()
-    assert np.all(np.isfinite(got))
-    bs, hs = SAMPLES[wname]
-    ref = oracle_out(inp, batches=bs, heads=hs)
-    assert_close(got[np.ix_(bs, hs)], ref, "bf16", f"{wname} sampled")

@@ -29,15 +29,31 @@ def test_deterministic_per_seed(wname):
         assert not np.array_equal(a[k], c[k])
 
 
-def test_shapes_and_replicated_branch_query():
+def test_shapes_and_distinct_branch_queries():
+    """Every MLRA branch has its own latent head ("[ICLR 2025] MLRA…", section 2.1), so its
+    query is drawn independently of the others; the MLA query keeps its shape and values."""
     w = I.WORKLOADS["mlra4_bf16_b32_h32_l8192"]
     inp = I.make_inputs(w, seqlens=[3, 4])
     assert inp["q_nope"].shape == (2, 32, 4, 128) and inp["q_nope"].dtype == np.uint16
     assert inp["q_rope"].shape == (2, 32, 64)
     assert inp["cache"].shape == (2, 4, 576)
     assert inp["w_uk"].shape == (4, 32, 128, 128) and inp["w_uv"].shape == (4, 32, 128, 128)
+    q = I.to_f64(inp["q_nope"], "bf16")
     for br in range(1, 4):
-        assert np.array_equal(inp["q_nope"][:, :, br], inp["q_nope"][:, :, 0])
+        assert not np.array_equal(inp["q_nope"][:, :, br], inp["q_nope"][:, :, 0])
+        c = np.corrcoef(q[:, :, br].ravel(), q[:, :, 0].ravel())[0, 1]
+        assert abs(c) < 0.05, c                      # independent draws
+    m = I.make_inputs(I.WORKLOADS["mla_bf16_b32_h128_l4096"], seqlens=[3, 4])
+    assert m["q_nope"].shape == (2, 128, 1, 128)
+
+
+def test_requery_changes_only_the_queries():
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    inp = I.make_inputs(w, seqlens=[70, 5])
+    sharp = I.make_inputs(w, seqlens=[70, 5], q_gain=4.0)
+    r = I.requery(inp, 4.0)
+    assert np.array_equal(r["q_nope"], sharp["q_nope"]) and np.array_equal(r["q_rope"], sharp["q_rope"])
+    assert r["cache"] is inp["cache"] and r["w_uk"] is inp["w_uk"]
 
 
 def test_paged_layout_bookkeeping_and_poison():
