@@ -226,6 +226,27 @@ mla_status mlra_decode_timed(const mla_params* p, const void* q_nope, const void
                              void* const* events);
 
 /*
+ * Allocation-free variant of mla_decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, semantics and results as mla_decode (NB = 1), bit for bit, minus the
+ * workspace: the call uses a static device array of MLA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends (its device address is looked
+ * up once per device, on the first call made with that device current).  Nothing in it
+ * needs clearing: every call writes its plan, queries and partials before reading them.
+ * Returns MLA_ERR_WORKSPACE, before anything is launched, when mla_workspace_size(p) exceeds
+ * MLA_NOALLOC_SCRATCH_BYTES (e.g. B = 256 sequences at H = 128).  Calls no hipMalloc /
+ * hipFree or allocating routine.  All calls on one GPU share that GPU's array: two calls
+ * that overlap in time on one GPU (different streams, or different host threads without
+ * ordering) race on it; calls ordered on one stream do not.  After a call has completed,
+ * the array's start holds its split plan as described above (for inspection).
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+mla_status mla_decode_noalloc(const mla_params* p, const void* q_nope, const void* q_rope,
+                              const void* latent, const void* rope, const int32_t* seqlens,
+                              const int32_t* block_table, const void* w_uk, const void* w_uv,
+                              void* out, hipStream_t stream);
+
+/*
  * Rotate rows of a rotary-key cache in place (the write-side step that gives the decoupled
  * key its position; RoFormer rotation, cited by the interview Q&A).  Row i starts at
  * x + i*row_stride (elements, dtype) and has d_rope elements; pairs (x_{2k}, x_{2k+1})

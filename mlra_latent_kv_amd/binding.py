@@ -73,12 +73,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mlra_decode.argtypes = dec
     lib.mla_decode_timed.argtypes = dec + [c_void_p]
     lib.mlra_decode_timed.argtypes = dec + [c_void_p]
+    lib.mla_decode_noalloc.argtypes = [P] + [c_void_p] * 10
     lib.mla_rope_rotate.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_float,
                                     c_int32, c_void_p]
     lib.mla_status_str.argtypes = [c_int32]
     lib.mla_status_str.restype = ctypes.c_char_p
     for f in ("mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
-              "mla_decode_timed", "mlra_decode_timed", "mla_rope_rotate"):
+              "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc", "mla_rope_rotate"):
         getattr(lib, f).restype = c_int32
     _lib = lib
     return lib
@@ -158,6 +159,20 @@ def mlra_decode(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk
                 workspace, workspace_bytes=None, stream=None, check=True, events=None) -> int:
     return _decode("mlra_decode", params, q_nope, q_rope, latent, rope, seqlens, block_table,
                    w_uk, w_uv, out, workspace, workspace_bytes, stream, check, events)
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # MLA_NOALLOC_SCRATCH_BYTES
+
+
+def mla_decode_noalloc(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv,
+                       out, stream=None, check=True) -> int:
+    """mla_decode with the library's static scratch instead of a caller workspace."""
+    st = load().mla_decode_noalloc(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(latent),
+                                   _ptr(rope), _ptr(seqlens), _ptr(block_table), _ptr(w_uk),
+                                   _ptr(w_uv), _ptr(out), _stream(stream))
+    if check and st:
+        raise MlaError(st, "mla_decode_noalloc")
+    return st
 
 
 def mla_rope_rotate(x, row_stride: int, pos, n_rows: int, d_rope: int, theta: float, dtype: int,

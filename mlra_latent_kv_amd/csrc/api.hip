@@ -13,6 +13,13 @@
 #include "launch.h"
 #include "plan.h"
 
+// Scratch of mla_decode_noalloc: the workspace (split plan, absorbed queries, split
+// partials) in a file-scope device array, so that call allocates nothing.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code never uses this name
+// as an address (on the host it is only a stand-in symbol): the device address comes from
+// hipGetSymbolAddress, once per device (noalloc_scratch below).
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace mla;
@@ -118,6 +125,28 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
   return to_status(e);
 }
 
+// Device address of `scratch` on the current device, looked up on the first call on each
+// device (with that device current) and cached.
+std::atomic<char*> g_scratch[kCuCacheDevices];
+
+hipError_t noalloc_scratch(char** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kCuCacheDevices) return hipErrorInvalidDevice;
+  char* v = g_scratch[dev].load(std::memory_order_acquire);
+  if (!v) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    v = static_cast<char*>(a);
+    g_scratch[dev].store(v, std::memory_order_release);
+  }
+  *ptr = v;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,6 +199,26 @@ mla_status mlra_decode_timed(const mla_params* p, const void* q_nope, const void
                              void* const* events) {
   return run_decode(4, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
                     workspace, workspace_bytes, stream, events);
+}
+
+mla_status mla_decode_noalloc(const mla_params* p, const void* q_nope, const void* q_rope,
+                              const void* latent, const void* rope, const int32_t* seqlens,
+                              const int32_t* block_table, const void* w_uk, const void* w_uv,
+                              void* out, hipStream_t stream) {
+  // host checks first (no HIP call): arguments, and the call's workspace must fit the static
+  // scratch.  The pointer checks run here with a stand-in for the scratch address (aligned,
+  // never dereferenced); run_decode repeats them with the real one.
+  Plan plan;
+  mla_status st = make_plan(p, &plan);
+  if (st != MLA_OK) return st;
+  if (plan.bytes > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  st = check_call(p, plan, 1, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                  reinterpret_cast<const void*>(kWsAlign), (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  if (st != MLA_OK) return st;
+  char* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return MLA_ERR_HIP;
+  return run_decode(1, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                    ws, (size_t)MLA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 mla_status mla_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,

@@ -25,8 +25,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     declared = B.header_functions()
     assert set(declared) == {"mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
-                             "mla_decode_timed", "mlra_decode_timed", "mla_rope_rotate",
-                             "mla_status_str"}
+                             "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc",
+                             "mla_rope_rotate", "mla_status_str"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -104,6 +104,29 @@ def test_invalid_params_rejected(lib, over, status):
     n = ctypes.c_size_t(0)
     st = lib.mla_workspace_size(ctypes.byref(p), ctypes.byref(n))
     assert st == status or (status in (1, 4, 7) and st == 0)
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """mla_decode_noalloc validates like mla_decode and refuses a call whose workspace would
+    exceed its static scratch, all before any HIP call (so no GPU is needed here)."""
+    def noalloc(p, **ptr):
+        args = dict(q_nope=FAKE, q_rope=FAKE, latent=FAKE, rope=FAKE, seqlens=FAKE,
+                    block_table=FAKE, w_uk=FAKE, w_uv=FAKE, out=FAKE)
+        args.update(ptr)
+        return lib.mla_decode_noalloc(ctypes.byref(p), *args.values(), None)
+    big = params_for("mla_bf16_b32_h128_l4096", batch=256, max_seqlen=4096)
+    assert B.workspace_size(big) > B.NOALLOC_SCRATCH_BYTES
+    assert noalloc(big) == 4                                          # MLA_ERR_WORKSPACE
+    assert noalloc(params_for("mla_bf16_b32_h128_l4096"), q_nope=None) == 1
+    assert noalloc(params_for("mla_bf16_b32_h128_l4096"), w_uk=FAKE + 2) == 7
+    assert noalloc(params_for("mlra4_bf16_b32_h32_l8192")) == 3        # MLA only (NB = 1)
+    assert noalloc(params_for("mla_bf16_b32_h128_l4096", page_size=16)) == 3
+    # every named workload fits the scratch
+    for wname in I.WORKLOAD_ORDER:
+        w = I.WORKLOADS[wname]
+        p = params_for(wname, batch=w.batch, max_seqlen=w.seqlen,
+                       max_pages_per_seq=-(-w.seqlen // 64), block_table_stride=-(-w.seqlen // 64))
+        assert B.workspace_size(p) <= B.NOALLOC_SCRATCH_BYTES, wname
 
 
 def test_branch_count_per_entry_point(lib):
