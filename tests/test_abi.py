@@ -46,7 +46,7 @@ def test_probe_library_exports_its_header(lib):
     assert set(declared) <= exported
     probe = ctypes.CDLL(build.PROBE_LIB)
     probe.mla_probe_out_words.restype = ctypes.c_size_t
-    assert probe.mla_probe_out_words() == 2048 * 4
+    assert probe.mla_probe_out_words() == 512 * 4
     probe.mla_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                      ctypes.c_void_p]
     assert probe.mla_probe_read(None, 16, FAKE, None) == 1       # rejected before any launch
