@@ -108,29 +108,25 @@ typedef struct mla_params {
  * num_splits is at most 512 and at most ceil(max_seqlen / 64).  flags is 0 or
  * MLA_FLAG_DEVICE_CHECKS; num_pages >= 0.
  *
- * Split plan.  The attention over each sequence is split into work items (split-K over the
- * sequence) whose partial results are merged afterwards.  The plan is made on the device
- * from seqlens at the start of every call, so it follows the actual lengths.  Its item
- * target follows the device's compute-unit count (queried once per device, at most 256).
- *  - Page plan (bf16 MLA with H % 128 == 0, the fp32 path, and any call with num_splits > 0):
- *    with p_b = ceil(seqlens[b] / 64) pages, every sequence is cut into ceil(p_b / c) items
- *    of c whole pages (the last one ragged; an empty sequence gets none), one item per
- *    dispatch slot.  With num_splits = 0, c is the smallest page count for which the batch's
- *    items fit the workgroups that fill the GPU once; when no c does, c = max_b p_b.  With
- *    num_splits = n, c = ceil(ceil(max_seqlen / 64) / n).
- *  - Stream plan (the other bf16 shapes, num_splits = 0, B <= 2895): the sequences'
- *    32-token tiles are laid end to end (T tiles in all) and dispatch slot g of
- *    G = min(slots filling the GPU once, T) takes tiles [floor(g T / G), floor((g+1) T / G));
- *    an item is the part of one sequence inside one slot, so a slot may run several items.
+ * Split plan.  The attention over each sequence is split into work items of whole 64-token
+ * pages (split-K over the sequence) whose partial results are merged afterwards.  The plan is
+ * made on the device from seqlens at the start of every call, so it follows the actual
+ * lengths: with p_b = ceil(seqlens[b] / 64) pages, every sequence is cut into ceil(p_b / c)
+ * items of c pages (the last one ragged; an empty sequence gets none), one item per dispatch
+ * slot.  With num_splits = 0, c is the smallest page count for which the batch's items fit
+ * the workgroups that fill the GPU once (one per compute unit for bf16 MLA with
+ * H % 128 == 0, else two per compute unit divided by the workgroups per item; the device's
+ * compute-unit count is queried once per device, at most 256); when no c does,
+ * c = max_b p_b.  With num_splits = n, c = ceil(ceil(max_seqlen / 64) / n).
  * After a call has completed on its stream, the workspace starts with that plan (for
  * inspection; nothing reads it after the call):
- *   int32 hdr[8] at byte 0: { W = number of items, c (0 for the stream plan), slots, item
+ *   int32 hdr[8] at byte 0: { W = number of items, c, slots, item
  *         target (0 when forced), error bits (MLA_DEVERR_*; 0 without device checks), first
  *         sequence with an error (-1: none), its first bad block-table column (-1: none),
  *         items_cap }
- *   int32 work[slots][4] at byte 32: { b, t_begin, t_end, item } of the first item of each
- *         dispatch slot, b = -1 for a slot without items
- *   int32 slot_end[slots] next: one past the last item of each slot
+ *   int32 work[slots][4] at byte 32: { b, t_begin, t_end, item } of the item of each
+ *         dispatch slot of the main kernels, b = -1 for a slot without one
+ *   int32 slot_end[slots] next: item + 1 for each slot with an item, else 0
  *   int32 items[items_cap][4] next: { b, t_begin, t_end, slot } of every item; items are
  *         numbered sequence-major, item i of sequence b covering tokens [t_begin, t_end)
  *   int32 split_off[B + 1] next: items of sequence b are split_off[b] .. split_off[b+1] - 1,
@@ -150,8 +146,8 @@ typedef struct mla_params {
 mla_status mla_workspace_size(const mla_params* p, size_t* bytes);
 
 /* Most work items (splits) one sequence can be cut into for *p (written to *splits, host), on
- * a device of up to 256 compute units: n when num_splits = n > 0, else the item target
- * bounded by the sequence's pages (page plan) or tiles (stream plan). */
+ * a device of up to 256 compute units: n when num_splits = n > 0, else
+ * min(ceil(max_seqlen / 64), item target). */
 mla_status mla_num_splits(const mla_params* p, int32_t* splits);
 
 /*

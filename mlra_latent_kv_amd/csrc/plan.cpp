@@ -91,7 +91,6 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   // workgroups that fill the chip once: the wide kernel holds one per CU, the others two
   const int64_t target_wg = q.wide ? q.n_cu : 2 * (int64_t)q.n_cu;
   q.target = (int)std::max<int64_t>(1, ceil_div(target_wg, wg_per_item));
-  q.stream = 0;
   q.xcd_major = q.wide;
   int64_t cap;
   if (p->num_splits > 0) {

@@ -11,7 +11,6 @@
 namespace mla {
 
 constexpr int kPage = MLA_PAGE_SIZE;   // tokens per page
-constexpr int kTileTokens = 32;        // tokens per main-loop tile (the stream plan's unit)
 constexpr int kHeadGroup = 32;         // heads per workgroup of the 32-head bf16 kernels
 constexpr int kWideHeads = 128;        // heads per workgroup of the wide bf16 kernel
 constexpr int kMaxCUs = 256;           // compute units the workspace is sized for (MI355X);
@@ -20,8 +19,6 @@ constexpr size_t kWsAlign = 256;
 constexpr int kMaxSplits = 512;        // bound on work items per sequence (the fp32 combine
                                        // keeps one weight per item in LDS)
 constexpr int kHdrWords = 8;           // plan header words at the start of the workspace
-constexpr int kPlanLdsBytes = 34816;   // LDS of the bf16 prologue workgroup that makes the
-                                       // plan (the stream plan keeps 3 B + 2 words there)
 
 enum class Path { kBf16Mfma, kF32Simt };
 
@@ -34,10 +31,8 @@ struct Plan {
   int n_cu;      // compute units the plan is made for (1 .. kMaxCUs)
   int checks;    // MLA_FLAG_DEVICE_CHECKS given: a check kernel runs before the prologue
   int num_pages; // pool pages for the block-id check (0: not checked)
-  // Split plan.  The device cuts the batch into work items (see plan_device.h); the host only
-  // bounds it.
-  int stream;        // 1: stream plan (equal tile ranges per slot, several items per slot);
-                     // 0: page plan (items of c whole pages, one item per slot)
+  // Split plan.  The device cuts the batch into work items of whole pages, one per dispatch
+  // slot (see plan_device.h); the host only bounds it.
   int target;        // slots the automatic plan fills (one workgroup set per CU slot)
   int forced_pages;  // pages per work item when num_splits is given, else 0
   int splits;        // most work items one sequence can be cut into

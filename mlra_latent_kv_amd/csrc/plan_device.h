@@ -3,29 +3,22 @@
 //
 // The main loop is split over the sequence (split-K).  A work item is a token range
 // [t_begin, t_end) of one sequence; its partial result (running max, running sum, latent
-// output) is merged with the other items of the sequence afterwards.  Items are numbered
+// output) is merged with the other items of the sequence afterwards.  Every sequence b with
+// L_b tokens, p_b = ceil(L_b / 64) pages, is cut into ceil(p_b / c) items of c whole pages
+// (the last one ragged); sequences with no tokens get no item.  Items are numbered
 // sequence-major; split_off[b] is the first item of sequence b and split_off[B] = W, the item
-// count, so the merge finds a variable number of items per sequence.  Sequences with no
-// tokens get no item.  Two plans:
+// count, so the merge finds a variable number of items per sequence.
 //
-//  * Page plan (one item per dispatch slot).  Every sequence b with L_b tokens,
-//    p_b = ceil(L_b / 64) pages, is cut into ceil(p_b / c) items of c whole pages (the last
-//    one ragged).  Automatic: c is the smallest count with sum_b ceil(p_b / c) <= target
-//    (binary search; the sum only falls as c grows), or c = max_b p_b when no c meets it.
-//    With num_splits given, c is fixed by the host.  With xcd_major the 8 XCDs get
-//    contiguous item ranges (slot 8g + x takes item x * ceil(W / 8) + g), otherwise slot s
-//    takes item s.
+// Balance: every item costs at most c pages and one workgroup set per item fills the chip
+// once when W <= target, so the automatic plan takes the smallest c with
+// sum_b ceil(p_b / c) <= target (binary search; the sum only falls as c grows), or
+// c = max_b p_b (one item per sequence) when no c meets the target.  With num_splits given,
+// c is fixed by the host.
 //
-//  * Stream plan (equal shares, several items per slot).  The sequences' 32-token tiles are
-//    laid end to end, T = sum_b ceil(L_b / 32) tiles, and slot g of G = min(target, T) takes
-//    tiles [floor(g T / G), floor((g + 1) T / G)).  Items are the pieces of a sequence
-//    between consecutive cuts, where the cuts are the sequence ends and the slot boundaries;
-//    a slot runs its items in order.  Every slot gets T / G tiles to within one, whatever the
-//    lengths, and a slot crosses at most a few sequence ends.
-//
-// Dispatch tables: work[s] = {b, t_begin, t_end, item} of the first item of slot s (b = -1
-// for a slot without items), slot_end[s] = one past its last item, and items[i] =
-// {b, t_begin, t_end, slot} for every item.
+// Dispatch tables: one item per dispatch slot of the main kernels.  With xcd_major the 8 XCDs
+// get contiguous item ranges (slot 8g + x takes item x * ceil(W / 8) + g), otherwise slot s
+// takes item s.  work[s] = {b, t_begin, t_end, item} (b = -1 for a slot without an item),
+// slot_end[s] = item + 1 (0 for an idle slot), and items[i] = {b, t_begin, t_end, slot}.
 //
 // Device checks (MLA_FLAG_DEVICE_CHECKS): a separate kernel (k_device_checks) writes one
 // result word per sequence, dbg[b] = 4 * (first bad page index + 1, or 0) + error bits; the
@@ -41,14 +34,14 @@ namespace mla {
 struct PlanArgs {
   const int32_t* seqlens;
   const int32_t* dbg;  // [B] device-check results (checks only), else nullptr
-  int32_t* hdr;        // [8]: W, pages per item c (0: stream plan), slots, target (0 when c
+  int32_t* hdr;        // [8]: W, pages per item c, slots, target (0 when c
                        // was forced), error bits, first bad sequence, its first bad page,
                        // items_cap
-  int32_t* work;       // [slots][4]: b, t_begin, t_end, item of the slot's first item
-  int32_t* slot_end;   // [slots]: one past the slot's last item
+  int32_t* work;       // [slots][4]: b, t_begin, t_end, item of the slot's item
+  int32_t* slot_end;   // [slots]: one past the slot's item (0: idle slot)
   int32_t* items;      // [items_cap][4]: b, t_begin, t_end, slot
   int32_t* split_off;  // [B + 1]
-  int B, max_seqlen, target, forced_pages, slots, xcd_major, stream, items_cap;
+  int B, max_seqlen, target, forced_pages, slots, xcd_major, items_cap;
 };
 
 inline PlanArgs plan_args(const Plan& p, const int32_t* seqlens, void* workspace) {
@@ -67,13 +60,12 @@ inline PlanArgs plan_args(const Plan& p, const int32_t* seqlens, void* workspace
   a.forced_pages = p.forced_pages;
   a.slots = p.slots;
   a.xcd_major = p.xcd_major;
-  a.stream = p.stream;
   a.items_cap = p.items_cap;
   return a;
 }
 
-// LDS the planner needs at least: reduction scratch; more lets it keep the clamped lengths,
-// split_off and the tile offsets on chip
+// LDS the planner needs at least: reduction scratch; more lets it keep the clamped lengths
+// and split_off on chip
 constexpr int kPlanLdsMin = 64;
 // sequences per thread whose lengths stay in registers (the first 256 * kPlanRegs; any
 // further ones are re-read from seqlens)
@@ -89,12 +81,10 @@ __device__ __forceinline__ int clamped_len(const PlanArgs& a, int b) {
   return min(max(a.seqlens[b], 0), a.max_seqlen);
 }
 __device__ __forceinline__ int pages_of_len(int L) { return (L + kPage - 1) / kPage; }
-__device__ __forceinline__ int tiles_of_len(int L) { return (L + kTileTokens - 1) / kTileTokens; }
 // ceil(p / c) for 0 <= p, 1 <= c < 2^21 (32-bit unsigned division)
 __device__ __forceinline__ int items_of(int p, int c) {
   return (int)(((unsigned)p + (unsigned)c - 1u) / (unsigned)c);
 }
-__device__ __forceinline__ long long cdiv64(long long a, long long b) { return (a + b - 1) / b; }
 
 // sum / max / min over the 256 threads; red: 4 slots of LDS (reused after a barrier)
 __device__ __forceinline__ long long block_sum(long long v, long long* red) {
@@ -166,8 +156,7 @@ __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_byte
   int* wsum = reinterpret_cast<int*>(red + 4);       // [4]
   int* so_lds = wsum + 4;                            // split_off copy [B + 1], if it fits
   int* len_lds = so_lds + (a.B + 1);                 // clamped lengths [B], if they fit
-  int* off_lds = len_lds + a.B;                      // stream plan: tile offsets [B + 1]
-  const bool on_chip = (long long)(3 * a.B + 2) * 4 <= lds_bytes - kPlanLdsMin;
+  const bool on_chip = (long long)(2 * a.B + 1) * 4 <= lds_bytes - kPlanLdsMin;
   const int tid = threadIdx.x;
 
   // ---- device-check results: error word, and no items at all after a bad block id
@@ -202,8 +191,7 @@ __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_byte
     return L;
   };
 
-  if (!a.stream) {
-    // ================================================================== page plan
+  {
     // f(pages of b) for every sequence this thread owns (b = tid, tid + 256, ...)
     auto for_each = [&](auto&& f) {
 #pragma unroll
@@ -275,72 +263,6 @@ __device__ inline void make_work_plan(const PlanArgs& a, void* lds, int lds_byte
       }
       *reinterpret_cast<int4*>(a.work + 4 * s) = e;
       a.slot_end[s] = item < W ? item + 1 : 0;
-    }
-  } else {
-    // ================================================================== stream plan
-    // (the host chooses it only when the per-sequence arrays fit in LDS: on_chip holds)
-    // tile offsets S_b (exclusive scan of the tile counts) and the total T
-    const long long T = block_scan(
-        a.B, [&](int b, int i) { return tiles_of_len(len_at(b, i)); },
-        [&](int b, long long off) {
-          off_lds[b] = (int)off;
-          len_lds[b] = len_at(b, b / 256);
-        },
-        wsum);
-    const int G = (int)min64(a.target, T);  // slots in use
-    // slot boundary p_g = floor(g T / G); #{g >= 0 : p_g <= x} = ceil((x + 1) G / T), x < T
-    auto bound = [&](long long g) { return g * T / G; };
-    auto n_upto = [&](long long x) { return cdiv64((x + 1) * G, T); };
-    __syncthreads();  // tile offsets and lengths in LDS
-    // items of sequence b (tiles [S, S + n)): one, plus the slot boundaries strictly inside
-    const int W = (int)block_scan(
-        a.B,
-        [&](int b, int) {
-          const long long S = off_lds[b];
-          const int n = tiles_of_len(len_lds[b]);
-          return n > 0 ? (int)(1 + n_upto(S + n - 1) - n_upto(S)) : 0;
-        },
-        [&](int b, long long off) {
-          a.split_off[b] = (int)off;
-          so_lds[b] = (int)off;
-        },
-        wsum);
-    if (tid == 0) {
-      a.split_off[a.B] = W;
-      so_lds[a.B] = W;
-      a.hdr[0] = W;
-      a.hdr[1] = 0;
-      a.hdr[3] = a.target;
-    }
-    __syncthreads();  // split_off complete
-    // every item, a thread per sequence walking its items in order; the item that starts at
-    // a slot boundary opens that slot
-    for (int b = tid; b < a.B; b += 256) {
-      const long long S = off_lds[b];
-      const int L = len_lds[b], n = tiles_of_len(L);
-      int item = so_lds[b];
-      long long x = S, g = n > 0 ? n_upto(S) - 1 : 0;  // slot of tile S
-      while (x < S + n) {
-        const long long nb = bound(g + 1);  // next slot boundary (T when g = G - 1)
-        const long long e = min64(S + n, nb);
-        const int t0 = (int)((x - S) * kTileTokens), t1 = min(L, (int)((e - S) * kTileTokens));
-        *reinterpret_cast<int4*>(a.items + 4 * item) = make_int4(b, t0, t1, (int)g);
-        if (x == bound(g))
-          *reinterpret_cast<int4*>(a.work + 4 * g) = make_int4(b, t0, t1, item);
-        ++item;
-        x = e;
-        if (x == nb) ++g;
-      }
-    }
-    __syncthreads();  // every slot's first item is written (global, same workgroup)
-    // slot ends: the first item of the next slot, W for the last; idle slots have none
-    for (int s = tid; s < a.slots; s += 256) {
-      if (s < G) {
-        a.slot_end[s] = s + 1 < G ? a.work[4 * (s + 1) + 3] : W;
-      } else {
-        *reinterpret_cast<int4*>(a.work + 4 * s) = make_int4(-1, 0, 0, -1);
-        a.slot_end[s] = 0;
-      }
     }
   }
   if (tid == 0) {

@@ -250,7 +250,7 @@ def test_plan_checker_rejects_wrong_plans():
     """The GPU tests compare the device's split plan with plan_ref.expected_plan through
     plan_ref.check_plan; here that comparison is shown to reject plans with a plausible
     mistake (pages per item one too many, a shifted item, a wrong split offset, a missed idle
-    slot, a wrong slot end, a stream-plan item cut at the wrong tile)."""
+    slot, a wrong slot end, an item table entry cut short)."""
     import copy
     import numpy as np
     from plan_ref import check_plan, expected_plan
@@ -260,13 +260,8 @@ def test_plan_checker_rejects_wrong_plans():
     check_plan(copy.deepcopy(good), good)
     forced = expected_plan(lens, 4000, 256, 80, forced=5)
     assert forced["pages"] == 13                        # ceil(63 / 5) pages per item
-    stream = expected_plan(lens, 4000, 20, 24, stream=True)
-    check_plan(copy.deepcopy(stream), stream)
-    # stream plan: 20 slots share 297 tiles (14 or 15 each); every slot opens with an item
-    # and its items are consecutive
-    t = sum(-(-L // 32) for L in lens)
-    assert t == 297 and np.all(stream["slot_end"][:20] > stream["work"][:20, 3])
-    assert np.all(stream["work"][1:20, 3] == stream["slot_end"][:19])
+    # 63 pages at 5 forced splits: 13 pages per item; the 4000-token sequence gets 5 items
+    assert np.array_equal(forced["split_off"][4:6], [3, 8])
 
     def bad_plans():
         p = copy.deepcopy(good); p["pages"] = 2; yield p, good
@@ -275,8 +270,7 @@ def test_plan_checker_rejects_wrong_plans():
         p = copy.deepcopy(good)
         p["work"][np.where(p["work"][:, 0] < 0)[0][0]] = (0, 0, 1, 0); yield p, good
         p = copy.deepcopy(good); p["slot_end"][0] += 1; yield p, good
-        p = copy.deepcopy(stream); p["item_table"][3, 2] -= 32; yield p, stream
-        p = copy.deepcopy(stream); p["slot_end"][5] = p["slot_end"][6]; yield p, stream
+        p = copy.deepcopy(forced); p["item_table"][3, 2] -= 32; yield p, forced
 
     for got, want in bad_plans():
         with pytest.raises(AssertionError):

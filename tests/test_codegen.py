@@ -55,6 +55,10 @@ def _blocks(lines):
         m = re.match(r"^\.(LBB\w+):(.*)$", ln)
         if m:
             blocks.append((m.group(1), m.group(2), []))
+        elif blocks and not blocks[-1][2] and ln.strip().startswith(";"):
+            # a note continued on its own line (nested loops: "Parent Loop ..." on the label
+            # line, "This Inner Loop Header" on the next)
+            blocks[-1] = (blocks[-1][0], blocks[-1][1] + ln.strip(), blocks[-1][2])
         elif blocks:
             ins = ln.split(";")[0].strip()
             if ins and not ins.startswith("."):

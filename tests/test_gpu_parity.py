@@ -407,15 +407,15 @@ def n_cu():
 
 
 def plan_kind(w, H=None):
-    """(stream plan?, XCD-major slots?, workgroups filling the GPU once per item target) of
-    the kernel that runs workload w with H heads."""
+    """(XCD-major slots?, item target) of the kernel that runs workload w with H heads (one
+    workgroup per CU for the 128-head kernel, two for the others)."""
     H = w.heads if H is None else H
     cu = min(n_cu(), 256)
     if w.dtype != "bf16":
-        return False, False, -(-2 * cu // H)
+        return False, -(-2 * cu // H)
     if w.branches == 1 and H % 128 == 0:
-        return False, True, -(-cu // (H // 128))
-    return False, False, -(-2 * cu // (H // 32))
+        return True, -(-cu // (H // 128))
+    return False, -(-2 * cu // (H // 32))
 
 
 def device_plan_matches(case, w, lens, forced=0, H=None):
@@ -423,11 +423,9 @@ def device_plan_matches(case, w, lens, forced=0, H=None):
     target this device's compute-unit count gives."""
     from mlra_latent_kv_amd import harness as Hn
     plan = Hn.read_plan(case)
-    stream, xcd, target = plan_kind(w, H)
-    if forced:
-        stream = False
+    xcd, target = plan_kind(w, H)
     want = expected_plan(lens, case.params.max_seqlen, target, plan["slots"], forced=forced,
-                         xcd_major=xcd, stream=stream)
+                         xcd_major=xcd)
     check_plan(plan, want)
     assert plan["err_bits"] == 0 and plan["err_seq"] == -1 and plan["err_page"] == -1
     return plan
