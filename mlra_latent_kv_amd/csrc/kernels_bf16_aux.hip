@@ -56,16 +56,31 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   // rotary part of the query, rotated at position L_b - 1 (angles in fp64), spread over the
-  // column-block workgroups of the head: with d_c = 512 (kRows * dr / 2 = 1024 = 256 *
-  // gridDim.z) every thread has at most one (row, pair) item.  Its loads go out with the
-  // weight loads, so the kernel makes one memory round trip, not two.
-  const int t_r = cb * 256 + tid;
-  const int bb_r = b0 + t_r / (dr / 2), k_r = t_r % (dr / 2);
-  const bool has_r = t_r < kRows * (dr / 2) && bb_r < B;
-  const bf16* xr = q_rope + ((size_t)min(bb_r, B - 1) * H + h) * dr + 2 * (has_r ? k_r : 0);
-  const float x0 = (float)xr[0], x1 = (float)xr[1];
-  // the length as the plan uses it, clamped to [0, max_seqlen]
-  const int L_r = min(max(seqlens[min(bb_r, B - 1)], 0), plan.max_seqlen);
+  // column-block workgroups of the head: the kRows * dr / 2 = 1024 (row, pair) items take one
+  // per thread with d_c = 512 (gridDim.z = 4), up to four with d_c = 128 (gridDim.z = 1).
+  // Their loads go out with the weight loads, so the kernel makes one memory round trip.
+  constexpr int kRotPer = 4;  // most (row, pair) items per thread
+  const int n_rot = (kRows * (dr / 2) + 256 * (int)gridDim.z - 1) / (256 * (int)gridDim.z);
+  int bb_r[kRotPer], k_r[kRotPer], L_r[kRotPer];
+  bool has_r[kRotPer];
+  float x0[kRotPer], x1[kRotPer];
+#pragma unroll
+  for (int it = 0; it < kRotPer; ++it) {
+    const int t_r = (it * (int)gridDim.z + cb) * 256 + tid;
+    bb_r[it] = b0 + t_r / (dr / 2);
+    k_r[it] = t_r % (dr / 2);
+    has_r[it] = it < n_rot && t_r < kRows * (dr / 2) && bb_r[it] < B;
+    x0[it] = x1[it] = 0.0f;
+    L_r[it] = 0;
+    if (it < n_rot) {  // uniform
+      const int bc = min(bb_r[it], B - 1);
+      const bf16* xr = q_rope + ((size_t)bc * H + h) * dr + 2 * (has_r[it] ? k_r[it] : 0);
+      x0[it] = (float)xr[0];
+      x1[it] = (float)xr[1];
+      // the length as the plan uses it, clamped to [0, max_seqlen]
+      L_r[it] = min(max(seqlens[bc], 0), plan.max_seqlen);
+    }
+  }
   const bf16* wsrc = w_uk + ((size_t)br * H + h) * dn * dcb + c0;
 #pragma unroll
   for (int j = 0; j < dn * kPCols / 8 / 256; ++j) {
@@ -93,12 +108,15 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
     const int bb = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
     if (bb < B) qcat[((size_t)bb * H + h) * row + col] = (bf16)(acc[i] * qscale);
   }
-  if (has_r) {
-    float cs, sn;
-    rope_cos_sin(L_r > 0 ? L_r - 1 : 0, rf.f[k_r], &cs, &sn);
-    bf16* o = qcat + ((size_t)bb_r * H + h) * row + dc + 2 * k_r;
-    o[0] = (bf16)((x0 * cs - x1 * sn) * qscale);
-    o[1] = (bf16)((x0 * sn + x1 * cs) * qscale);
+#pragma unroll
+  for (int it = 0; it < kRotPer; ++it) {
+    if (has_r[it]) {
+      float cs, sn;
+      rope_cos_sin(L_r[it] > 0 ? L_r[it] - 1 : 0, rf.f[k_r[it]], &cs, &sn);
+      bf16* o = qcat + ((size_t)bb_r[it] * H + h) * row + dc + 2 * k_r[it];
+      o[0] = (bf16)((x0[it] * cs - x1[it] * sn) * qscale);
+      o[1] = (bf16)((x0[it] * sn + x1[it] * cs) * qscale);
+    }
   }
 }
 
@@ -106,8 +124,8 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
 
 hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(p.H + 1, (p.B + kRows - 1) / kRows, p.dc / kPCols);
-  // one rotary (row, pair) item per thread covers the query's rotary part
-  if (kRows * (p.dr / 2) > 256 * (int)grid.z) return hipErrorInvalidValue;
+  // at most four rotary (row, pair) items per thread cover the query's rotary part
+  if (kRows * (p.dr / 2) > 4 * 256 * (int)grid.z) return hipErrorInvalidValue;
   RopeFreq rf;
   make_rope_freq(p.dr, a.rope_theta, &rf);
   hipLaunchKernelGGL(k_prologue_bf16, grid, dim3(256), 0, s, (const bf16*)a.q_nope,
@@ -124,15 +142,16 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
 // page, section 矩陣吸收), with the MLRA-4 branch sum carried by the contraction over all
 // 512 latent columns ("[ICLR 2025] MLRA…", section 2.2).
 //
+// Latent width DC = 512 (MLA, MLRA-4) or 128 (one MLRA branch as a tensor-parallel shard).
 // One workgroup (4 waves) per (head h, rows b0..b0+R-1), R in {2, 4, 8, 16}:
 //  1. the split statistics (M, 1/L) of every (row, branch), then the weighted sum of the split
 //     partials, with all 256 threads sharing the (row, 16-byte chunk) work, into an LDS copy
 //     of the merged latent output (bf16, the MFMA operand);
 //  2. meanwhile the W_UV rows of the head go to LDS by direct-to-LDS loads (one contiguous
-//     32 KiB block per wave: wave w owns latent columns 128w..128w+127, exactly branch w for
+//     block per wave: wave w owns latent columns [w DC/4, (w+1) DC/4), exactly branch w for
 //     MLRA-4), issued behind the first partials, half before the statistics are formed and
 //     half after, so that they stream in during the merge;
-//  3. each wave multiplies its 128 latent columns by its W_UV rows (MFMA 32x32x16, rows of
+//  3. each wave multiplies its DC / 4 latent columns by its W_UV rows (MFMA 32x32x16, rows of
 //     the workgroup as M, padded to 32), and the four partial products (K split four ways)
 //     are summed through LDS.
 namespace {
@@ -147,21 +166,29 @@ constexpr int kCeMaxRows = 16;
 // chunk slots of a 256-byte bank line
 __device__ __forceinline__ int ce_sw(int r, int c) { return c ^ (4 * (r & 3)); }
 
-// R = 4 * NC / TPC rows per workgroup; each thread merges NC chunks of one row, with 32 chunk
-// loads in flight.  TPC = 2 (two-row blocks, for small batches): two adjacent threads share a
-// chunk, each taking every other split, and add their sums at the end.
-template <int NC, int TPC>
+// R = 256 NC / (TPC DC / 8) rows per workgroup; each thread merges NC chunks of one row, with
+// 32 chunk loads in flight.  TPC > 1 (small row blocks, for small batches): TPC adjacent
+// threads share a chunk, each taking every TPC-th split, and add their sums at the end.
+template <int NC, int TPC, int DC>
 __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     const bf16* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ split_off, const bf16* __restrict__ w_uv,
     bf16* __restrict__ out, int B, int H, int NB, int dcb, float out_scale) {
-  constexpr int R = 4 * NC / TPC;
+  constexpr int kCPR = DC / 8;                  // 16-byte chunks per latent row
+  constexpr int R = 256 * NC / (TPC * kCPR);
+  constexpr int kWRows = DC / 4;                // W_UV rows (latent columns) per wave
+  constexpr int kKS = kWRows / 16;              // MFMA K-steps per wave
+  constexpr int kWBytes = 4 * kWRows * kCeRowB;
+  constexpr int kRedBytes = 4 * kCeMaxRows * kCeRedPitch * 4;
+  static_assert(R >= 2 && R <= kCeMaxRows, "rows per workgroup");
   struct Smem {
-    char wuv[4][128 * kCeRowB];       // per wave: its 128 W_UV rows, chunk-swizzled
-    char olat[kCeMaxRows][1024];      // merged latent rows, chunk c at c ^ (row % 16)
+    // per wave: its W_UV rows, chunk-swizzled; reused for the cross-wave sum
+    char wuv[kWBytes > kRedBytes ? kWBytes : kRedBytes];
+    char olat[kCeMaxRows][2 * DC];    // merged latent rows, chunk c at c ^ (row % 16)
     float stat_m[kCeMaxRows][4], stat_inv[kCeMaxRows][4];
   };
-  __shared__ __align__(16) Smem sm;  // 145 KiB; wuv is reused for the cross-wave sum
+  __shared__ __align__(16) Smem sm;  // 145 KiB (DC = 512); wuv also holds the cross-wave sum
+  char* const wuv_w = sm.wuv + (size_t)kWRows * kCeRowB * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.x % H, b0 = (blockIdx.x / H) * R;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a uniform value: the W_UV buffer descriptor depends on it, and a descriptor
@@ -179,13 +206,13 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   // statistics' rare extra loads, where the wait analysis counts them exactly.  They stream
   // in while the partials are merged.
   auto issue_wuv = [&](int i0, int i1) {
-    const int c0 = 128 * w, br = c0 / dcb;
+    const int c0 = kWRows * w, br = c0 / dcb;
     const bf16* wbase = w_uv + ((size_t)(br * H + h) * dcb + (c0 % dcb)) * kCeDv;
-    const __amdgpu_buffer_rsrc_t rs = tile::rsrc(wbase, 128 * kCeRowB);
+    const __amdgpu_buffer_rsrc_t rs = tile::rsrc(wbase, kWRows * kCeRowB);
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
       const int r = 4 * i + (lane >> 4);
-      tile::dma16(rs, sm.wuv[w] + 1024 * i, r * kCeRowB + 16 * ce_sw(r, lane & 15));
+      tile::dma16(rs, wuv_w + 1024 * i, r * kCeRowB + 16 * ce_sw(r, lane & 15));
     }
   };
 
@@ -197,8 +224,8 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   // row's last split gets weight 0, and its loads (of an item that exists) are replaced by
   // zeros.
   const size_t ml_s = (size_t)NB * H * 2;  // part_ml stride of one work item
-  const size_t po_s = (size_t)H * 512;     // part_o stride of one work item
-  const int first = (tid / TPC) * NC, mr = first / 64, mc = first % 64;
+  const size_t po_s = (size_t)H * DC;      // part_o stride of one work item
+  const int first = (tid / TPC) * NC, mr = first / kCPR, mc = first % kCPR;
   const int z = tid % TPC;  // which of the chunk's threads: takes splits z, z + TPC, ...
   const int mb = b0 + mr, mbr = (8 * mc) / dcb;
   // every load is unconditional, at a written work item (a predicated load leaves the
@@ -208,7 +235,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   const int mu0 = split_off[mbl], mn = mb < B ? split_off[mbl + 1] - mu0 : 0;
   auto item_of = [](int u0, int n, int s) { return max(u0 + min(s, n - 1), 0); };
   const float* mml = part_ml + (size_t)mbr * H * 2 + h * 2;
-  const bf16* msrc = part_o + (size_t)h * 512 + 8 * mc;
+  const bf16* msrc = part_o + (size_t)h * DC + 8 * mc;
   // the longest split list among the workgroup's rows bounds the (uniform) merge loop
   int n_max = 0;
   for (int r = 0; r < R; ++r) {
@@ -254,7 +281,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
       pl[it] = ml[sidx * ml_s + 1];
     }
     load_batch(0);
-    issue_wuv(0, 16);
+    issue_wuv(0, kWRows / 8);
 #pragma unroll
     for (int it = 0; it < kPre; ++it)
       if (q + it * P >= n) pm[it] = -INFINITY;
@@ -289,7 +316,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   // partials of the first batch), and the merge below would start only once they had all
   // arrived instead of load by load
   tile::lds_barrier();
-  issue_wuv(16, 32);
+  issue_wuv(kWRows / 8, kWRows / 4);
 
   // ---- 2b. weighted sum of the splits, batch by batch
   {
@@ -318,15 +345,16 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
                                      (float)v[u][i][7]};
         }
     }
-    if (TPC == 2) {  // the chunk's two threads are adjacent lanes: add their halves
+    // the chunk's TPC threads are adjacent lanes: add their shares
+#pragma unroll
+    for (int o = 1; o < TPC; o <<= 1)
 #pragma unroll
       for (int i = 0; i < NC; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[i][0][e] += __shfl_xor(acc[i][0][e], 1, 64);
-          acc[i][1][e] += __shfl_xor(acc[i][1][e], 1, 64);
+          acc[i][0][e] += __shfl_xor(acc[i][0][e], o, 64);
+          acc[i][1][e] += __shfl_xor(acc[i][1][e], o, 64);
         }
-    }
 #pragma unroll
     for (int i = 0; i < NC; ++i)
       if (z == 0)
@@ -337,15 +365,15 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   tile::wait_vmcnt<0>();  // this wave's W_UV rows have landed
   __syncthreads();        // every merged latent row is in LDS
 
-  // ---- 3. out[row][v] partial over this wave's 128 latent columns.  A operand: lane (row
-  // l32, k-half g) holds columns 128w + 16j + 8g..+7 (chunk 16w + 2j + g); rows >= R are zero.
-  // B operand (K = latent rows, N = v): lane (v, k-half g) holds W_UV rows 16j + 8g..+7 of
-  // column v, two transposed reads: source lane li of 16-lane group G addresses row
+  // ---- 3. out[row][v] partial over this wave's DC / 4 latent columns.  A operand: lane (row
+  // l32, k-half g) holds columns w DC/4 + 16j + 8g..+7 (chunk w DC/32 + 2j + g); rows >= R are
+  // zero.  B operand (K = latent rows, N = v): lane (v, k-half g) holds W_UV rows 16j + 8g..+7
+  // of column v, two transposed reads: source lane li of 16-lane group G addresses row
   // 16j + 8*(G>>1) + li/4 (+4), columns 16*(G&1) + 4*(li&3)..+3 of the block.
-  bf16x8 a[8];
+  bf16x8 a[kKS];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int cc = 16 * w + 2 * j + g;
+  for (int j = 0; j < kKS; ++j) {
+    const int cc = (DC / 32) * w + 2 * j + g;
     a[j] = l32 < R ? *(const bf16x8*)(sm.olat[l32 & (kCeMaxRows - 1)] + 16 * (cc ^ (l32 & 15)))
                    : bf16x8{};
   }
@@ -356,9 +384,9 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     o[vb] = f32x16{};
     const int col = 32 * vb + 16 * (G & 1) + 4 * (li & 3);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kKS; ++j) {
       const int r1 = 16 * j + 8 * (G >> 1) + (li >> 2), r2 = r1 + 4;
-      const char* base = sm.wuv[w];
+      const char* base = wuv_w;
       const bf16x8 bv = tile::tr_pair(base + r1 * kCeRowB + 16 * ce_sw(r1, col >> 3) + 2 * (col & 7),
                                       base + r2 * kCeRowB + 16 * ce_sw(r2, col >> 3) + 2 * (col & 7));
       o[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], bv, o[vb], 0, 0, 0);
@@ -394,20 +422,28 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
 
 }  // namespace
 
-// rows per workgroup: the largest of 16, 8, 4 that still gives every CU a workgroup, else 2
-// (fewer rows per workgroup read each head's W_UV more often, mostly from L2)
-int combine_epilogue_rows(int B, int H) {
-  for (int R = 16; R > 2; R /= 2)
+// rows per workgroup: the largest of 16, 8, 4 that still gives every CU a workgroup, else the
+// smallest block (2 rows at DC = 512, 4 at DC = 128); fewer rows per workgroup read each
+// head's W_UV more often, mostly from L2
+int combine_epilogue_rows(int B, int H, int dc) {
+  const int r_min = dc == 128 ? 4 : 2;
+  for (int R = 16; R > r_min; R /= 2)
     if ((long)H * ((B + R - 1) / R) >= 256) return R;
-  return 2;
+  return r_min;
 }
 
 hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
-  const int R = combine_epilogue_rows(p.B, p.H);
+  const int R = combine_epilogue_rows(p.B, p.H, p.dc);
   const unsigned blocks = (unsigned)(p.H * ((p.B + R - 1) / R));
-  auto kern = R == 16 ? k_combine_epilogue_bf16<4, 1>
-              : R == 8 ? k_combine_epilogue_bf16<2, 1>
-              : R == 4 ? k_combine_epilogue_bf16<1, 1> : k_combine_epilogue_bf16<1, 2>;
+  // <NC, TPC, DC>: R = 256 NC / (TPC DC / 8)
+  auto kern = p.dc == 128
+                  ? (R == 16 ? k_combine_epilogue_bf16<1, 1, 128>
+                     : R == 8 ? k_combine_epilogue_bf16<1, 2, 128>
+                              : k_combine_epilogue_bf16<1, 4, 128>)
+              : R == 16 ? k_combine_epilogue_bf16<4, 1, 512>
+              : R == 8  ? k_combine_epilogue_bf16<2, 1, 512>
+              : R == 4  ? k_combine_epilogue_bf16<1, 1, 512>
+                        : k_combine_epilogue_bf16<1, 2, 512>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, (const bf16*)a.part_o, a.part_ml,
                      a.split_off, (const bf16*)a.w_uv, (bf16*)a.out, p.B, p.H, p.NB, p.dcb,
                      a.out_scale);

@@ -50,7 +50,7 @@ hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s);   
 hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s);       // fp32 path
 // bf16 path: split combine and W_UV epilogue in one kernel (the latent output stays on chip)
 hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s);
-int combine_epilogue_rows(int B, int H);
+int combine_epilogue_rows(int B, int H, int dc);
 hipError_t launch_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
                               int d_rope, float theta, int dtype, hipStream_t s);
 

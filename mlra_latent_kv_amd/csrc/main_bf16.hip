@@ -19,11 +19,13 @@
 // second wave to run while one waits on LDS, MFMA results or a barrier.  Each workgroup
 // double-buffers its tiles: one lands while the other is consumed.
 //
-// Wave w (of 4) accumulates O^T for latent columns [128w, 128w+128).
-//  * MLA (one branch): for the scores, wave w takes tokens 16*(w&1).. and heads 16*(w>>1)..
-//    of the tile over the full 576 columns (MFMA 16x16x32, query in registers).  Partner
-//    waves (same heads, other 16 tokens) swap per-head maxima and sums through LDS, and
-//    every wave publishes its bf16 probabilities for everyone's PV step.
+// Wave w (of 4) accumulates O^T for a quarter of the latent columns, [w DC/4, (w+1) DC/4).
+//  * MLA (one branch, latent width DC = 512, or 128 for one MLRA branch run on its own as a
+//    tensor-parallel shard with rows [c_b | k_rope] of 192): for the scores, wave w takes
+//    tokens 16*(w&1).. and heads 16*(w>>1).. of the tile over all DC + 64 columns (MFMA
+//    16x16x32, query in registers).  Partner waves (same heads, other 16 tokens) swap
+//    per-head maxima and sums through LDS, and every wave publishes its bf16 probabilities
+//    for everyone's PV step.
 //  * MLRA-4: wave w's latent columns are exactly branch w; it computes its branch's scores
 //    plus the full rotary score itself, so the branch's softmax and probabilities never
 //    leave its registers.
@@ -42,24 +44,28 @@ constexpr int kPPitch = kTT + 8;                     // bf16 probability row pit
 constexpr int kBufs = 2;                             // tile ring depth per workgroup
 
 // Exchange buffers first, then the tile ring on a 256-byte boundary.
-template <int NB>
+template <int NB, int DC>
 struct Smem {
   bf16 p[NB == 1 ? kHG * kPPitch : 8];        // MLA: probabilities [h][t]
   float mx[NB == 1 ? 2 * kHG : 1];            // MLA: per-head max of each 16-token half
   float sum[NB == 1 ? 2 * kHG : 1];           // MLA: per-head probability sum of each half
   float alpha[NB == 1 ? kHG : 1];             // MLA: per-head rescale of this tile
   char gap[256];
-  __attribute__((aligned(256))) char ring[kBufs][kBufBytes];
+  __attribute__((aligned(256))) char ring[kBufs][Geom<DC>::kBufBytes];
 };
 
-template <int NB>
+template <int NB, int DC>
 __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, const int32_t* __restrict__ work, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, bf16* __restrict__ part_o, float* __restrict__ part_ml, int H,
     int n_hg) {
-  __shared__ __align__(16) Smem<NB> sm;
+  static_assert(NB == 1 || DC == 512, "MLRA-4 rows hold four 128-wide branches");
+  using G = Geom<DC>;
+  constexpr int kRowW = DC + kDR;   // cached (and absorbed-query) row width
+  constexpr int kNOB = DC / 128;    // 32-column output blocks per wave
+  __shared__ __align__(16) Smem<NB, DC> sm;
 
   // XCD-aware mapping: consecutive blocks go to different XCDs, so the head groups of one
   // dispatch slot (one work item) are placed 8 blocks apart -> same XCD, dispatched back to
@@ -96,22 +102,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
       lb = latent + (int64_t)b * lat_seq + (int64_t)t0 * lat_tok;
       rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
     }
-    issue_tile<Sw32, 4>(sm.ring[k % kBufs], w, lane, lb, rb, valid, lat_row_b, rope_row_b);
+    issue_tile<Sw32, 4, DC>(sm.ring[k % kBufs], w, lane, lb, rb, valid, lat_row_b, rope_row_b);
   };
 
   // absorbed query as the MFMA B operand (N = heads).
-  //  MLA, 16x16x32: lane (head 16*(w>>1) + lane%16, k-group lane/16), K-step j = 32 columns.
+  //  MLA, 16x16x32: lane (head 16*(w>>1) + lane%16, k-group lane/16), K-step j = 32 columns
+  //  (DC / 32 latent steps, then 2 rotary ones).
   //  MLRA, 32x32x16: lane (head l32, k-half kg), K-step j = 16 columns of branch w / rope.
-  constexpr int kQSteps = NB == 1 ? 18 : 12;
+  constexpr int kLatSteps = DC / 32;
+  constexpr int kQSteps = NB == 1 ? kLatSteps + 2 : 12;
   const int tb = w & 1, hb = w >> 1;          // MLA score block: token half, head half
   const int l16 = lane & 15, g16 = lane >> 4;
   bf16x8 qb[kQSteps];
   if (NB == 1) {
-    const bf16* qrow = qcat + ((size_t)b * H + h0 + 16 * hb + l16) * kRow + 8 * g16;
+    const bf16* qrow = qcat + ((size_t)b * H + h0 + 16 * hb + l16) * kRowW + 8 * g16;
 #pragma unroll
-    for (int j = 0; j < 18; ++j) qb[j] = *(const bf16x8*)(qrow + 32 * j);
+    for (int j = 0; j < kQSteps; ++j) qb[j] = *(const bf16x8*)(qrow + 32 * j);
   } else {
-    const bf16* qrow = qcat + ((size_t)b * H + h0 + l32) * kRow + 8 * kg;
+    const bf16* qrow = qcat + ((size_t)b * H + h0 + l32) * kRowW + 8 * kg;
 #pragma unroll
     for (int j = 0; j < 8; ++j) qb[j] = *(const bf16x8*)(qrow + 128 * w + 16 * j);
 #pragma unroll
@@ -121,24 +129,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
   issue(0);
 
   float m_run = -INFINITY, l_run = 0.0f;
-  f32x16 O[4];
+  f32x16 O[kNOB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) O[mb] = f32x16{};
+  for (int mb = 0; mb < kNOB; ++mb) O[mb] = f32x16{};
 
   // transposed-read sources of the value operand: rows v_row and v_row + v_delta of each
-  // 16-token half, columns 128w + 32mb + v_col (this wave's latent columns)
+  // 16-token half, columns w DC/4 + 32mb + v_col (this wave's latent columns)
   const int g = lane >> 4, li = lane & 15;
   const int v_col = 16 * (g & 1) + 4 * (li & 3);
   const int v_row = NB == 1 ? 8 * kg + (li >> 2) : 4 * kg + (li >> 2);
   constexpr int v_delta = NB == 1 ? 4 : 8;
-  uint32_t pv_off[2][2][4];  // [half][read][mb]; + 256w for the wave's column block
+  uint32_t pv_off[2][2][kNOB];  // [half][read][mb]
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        pv_off[s2][r][mb] = lat_piece<Sw32>(16 * s2 + v_row + r * v_delta, 32 * mb + v_col) + 256 * w;
+      for (int mb = 0; mb < kNOB; ++mb)
+        pv_off[s2][r][mb] =
+            lat_piece<Sw32, DC>(16 * s2 + v_row + r * v_delta, w * (DC / 4) + 32 * mb + v_col);
 
   for (int k = 0; k < n_tiles; ++k) {
     wait_vmcnt<0>();  // with a ring of two, tile k+1 is issued only after tile k landed
@@ -158,14 +167,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
         // K-step j covers columns 32j..32j+31: chunk 4j + g16 of token t
         const int t = 16 * tb + l16;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < kLatSteps; ++j)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              lds_read16(buf + lat_chunk<Sw32>(t, 4 * (j & 3) + g16) + 256 * (j >> 2)), qb[j],
-              acc, 0, 0, 0);
+              lds_read16(buf + lat_chunk<Sw32, DC>(t, 4 * (j & 3) + g16) + 256 * (j >> 2)),
+              qb[j], acc, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              lds_read16(buf + rope_chunk(t, 4 * j + g16)), qb[16 + j], acc, 0, 0, 0);
+              lds_read16(buf + rope_chunk<DC>(t, 4 * j + g16)), qb[kLatSteps + j], acc, 0, 0, 0);
       }
       // D layout: lane (head 16*hb + l16, group g16), item e -> token 16*tb + 4*g16 + e
       const int h = 16 * hb + l16;
@@ -239,39 +248,42 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
       m_run = m_new;
     }
 
-    // ---- O^T[d][h] += V^T P^T over this wave's 128 latent columns
+    // ---- O^T[d][h] += V^T P^T over this wave's DC / 4 latent columns
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) O[mb] *= alpha;
+    for (int mb = 0; mb < kNOB; ++mb) O[mb] *= alpha;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < kNOB; ++mb)
         O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             tr_pair(buf + pv_off[s2][0][mb], buf + pv_off[s2][1][mb]), pb[s2], O[mb], 0, 0, 0);
   }
 
   // ---- partial outputs, through LDS so that every global store writes whole rows.  O[mb]
-  // item i is column d = 128w + 32mb + 8*(i/4) + 4*kg + i%4 of head l32: written straight
+  // item i is column d = w DC/4 + 32mb + 8*(i/4) + 4*kg + i%4 of head l32: written straight
   // out, each store instruction would touch 32 head rows with 16 bytes each.  The waves put
-  // the 32 x 512 block (bf16) into the now idle tile ring, then each stores 8 of its 1 KiB
-  // rows, one per instruction.
-  constexpr int kOutPitch = kDC * 2 + 16;  // LDS bytes per head row (+16: 2-way conflicts)
-  static_assert(kHG * kOutPitch <= kBufBytes, "output staging exceeds one ring buffer");
+  // the 32 x DC block (bf16) into the now idle tile ring, then each stores its 8 rows, one
+  // 1 KiB (or four 256-byte rows) per instruction.
+  constexpr int kOutPitch = DC * 2 + 16;  // LDS bytes per head row (+16: 2-way conflicts)
+  static_assert(kHG * kOutPitch <= G::kBufBytes, "output staging exceeds one ring buffer");
   __syncthreads();  // every wave is done with the ring
   char* stage = sm.ring[0];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < kNOB; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *(bf16x4*)(stage + l32 * kOutPitch + (128 * w + 32 * mb + 8 * q + 4 * kg) * 2) =
+      *(bf16x4*)(stage + l32 * kOutPitch + (w * (DC / 4) + 32 * mb + 8 * q + 4 * kg) * 2) =
           bf16x4{(bf16)O[mb][4 * q], (bf16)O[mb][4 * q + 1], (bf16)O[mb][4 * q + 2],
                  (bf16)O[mb][4 * q + 3]};
   __syncthreads();
-  bf16* po = part_o + (item * H + h0) * kDC + 8 * lane;
+  // lane -> (row r0 + lane / chunks, 16-byte chunk lane % chunks) of the wave's 8 rows
+  constexpr int kRowsPerStore = G::kRowsPerLoad;
+  const int sr = lane / G::kChunks, sc = lane % G::kChunks;
+  bf16* po = part_o + (item * H + h0) * DC + 8 * sc;
 #pragma unroll
-  for (int j = 0; j < kHG / 4; ++j) {
-    const int r = (kHG / 4) * w + j;
-    *(bf16x8*)(po + (size_t)r * kDC) = *(const bf16x8*)(stage + r * kOutPitch + 16 * lane);
+  for (int j = 0; j < kHG / 4 / kRowsPerStore; ++j) {
+    const int r = (kHG / 4) * w + j * kRowsPerStore + sr;
+    *(bf16x8*)(po + (size_t)r * DC) = *(const bf16x8*)(stage + r * kOutPitch + 16 * sc);
   }
   if (NB == 1) {
     if (tb == 0 && g16 == 0) {
@@ -289,7 +301,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
 
 hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const unsigned blocks = (unsigned)(p.slots * p.n_hg);
-  auto kern = p.NB == 1 ? k_main_bf16<1> : k_main_bf16<4>;
+  auto kern = p.NB == 4 ? k_main_bf16<4, 512> : p.dcb == 512 ? k_main_bf16<1, 512>
+                                                             : k_main_bf16<1, 128>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, s, (const bf16*)a.qcat,
                      (const bf16*)a.latent, (const bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok,
                      a.rope_seq, a.work, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,

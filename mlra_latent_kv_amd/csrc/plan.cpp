@@ -51,9 +51,12 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   q.num_pages = q.paged ? p->num_pages : 0;
 
   if (p->dtype == MLA_BF16) {
+    // MLA (latent 512), MLRA-4 (four branches of 128), and one MLRA branch on its own
+    // (latent 128: a tensor-parallel shard of MLRA-4)
     const bool mla = q.NB == 1 && q.dcb == 512;
+    const bool shard = q.NB == 1 && q.dcb == 128;
     const bool mlra = q.NB == 4 && q.dcb == 128;
-    if (!(mla || mlra) || q.dr != 64 || q.dn != 128 || q.dv != 128 || q.H % kHeadGroup)
+    if (!(mla || shard || mlra) || q.dr != 64 || q.dn != 128 || q.dv != 128 || q.H % kHeadGroup)
       return MLA_ERR_UNSUPPORTED;
     q.path = Path::kBf16Mfma;
     q.n_hg = q.H / kHeadGroup;

@@ -15,6 +15,9 @@
 // Sw16: t mod 8 -> chunk bits 1-3, (t / 8) mod 2 -> bit 0.
 // Both repeat every 16 rows.  Rotary rows are 8 chunks and two share a 256-byte bank line;
 // rope_sw(t) = (t/2) mod 8 separates 16 consecutive rows.
+// The latent width DC is 512 (MLA and MLRA-4 rows of 576) or 128 (one MLRA branch with the
+// rotary key, rows of 192); a 128-wide latent row is one 256-byte bank line of 16 chunks, and
+// the swizzle, which only permutes chunks inside aligned groups of 16, is the same.
 #pragma once
 
 #include "device_common.h"
@@ -29,6 +32,17 @@ constexpr int kRopeRowB = kDR * 2;                     // bytes per rotary row i
 constexpr int kRopeOff = kTT * kLatRowB;               // rotary region of a buffer
 constexpr int kBufBytes = kRopeOff + kTT * kRopeRowB;  // one tile: 36864 bytes
 
+// Tile geometry for latent width DC (the constants above are Geom<512>).
+template <int DC>
+struct Geom {
+  static constexpr int kLatRowB = DC * 2;                   // bytes per latent row
+  static constexpr int kRopeOff = kTT * kLatRowB;           // rotary region of a buffer
+  static constexpr int kBufBytes = kRopeOff + kTT * kRopeRowB;
+  static constexpr int kChunks = DC / 8;                    // 16-byte chunks per latent row
+  static constexpr int kRowsPerLoad = 64 / kChunks;         // latent rows per 64-lane load
+  static_assert(DC == 512 || DC == 128, "latent width");
+};
+
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -42,17 +56,18 @@ __device__ __forceinline__ int rope_sw(int t) { return (t >> 1) & 7; }
 
 // Byte offset in a tile buffer of latent (row t, global 16-byte chunk c), and of the 8-byte
 // piece holding element columns col..col+3 (col % 4 == 0).
-template <Swizzle SW>
+template <Swizzle SW, int DC = kDC>
 __device__ __forceinline__ uint32_t lat_chunk(int t, int c) {
-  return (uint32_t)(t * kLatRowB + 16 * (c ^ lat_sw<SW>(t)));
+  return (uint32_t)(t * Geom<DC>::kLatRowB + 16 * (c ^ lat_sw<SW>(t)));
 }
-template <Swizzle SW>
+template <Swizzle SW, int DC = kDC>
 __device__ __forceinline__ uint32_t lat_piece(int t, int col) {
-  return lat_chunk<SW>(t, col >> 3) + 2 * (col & 7);
+  return lat_chunk<SW, DC>(t, col >> 3) + 2 * (col & 7);
 }
 // Byte offset of rotary (row t, 16-byte chunk c), c < 8.
+template <int DC = kDC>
 __device__ __forceinline__ uint32_t rope_chunk(int t, int c) {
-  return (uint32_t)(kRopeOff + t * kRopeRowB + 16 * (c ^ rope_sw(t)));
+  return (uint32_t)(Geom<DC>::kRopeOff + t * kRopeRowB + 16 * (c ^ rope_sw(t)));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -75,32 +90,36 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, MLA_TILE_CPOL);
 }
 
-// Loads one wave issues per tile when NW waves share it: wave w fetches latent rows
-// (32/NW)w.. (one 1 KiB row per instruction) and, if w < 4, rotary rows 8w..8w+7 (one
-// instruction).
-template <int NW>
+// Loads one wave issues per tile when NW waves share it: wave w fetches its share of the
+// latent rows (one instruction brings 1 KiB: one 512-wide row, or four 128-wide rows) and, if
+// w < 4, rotary rows 8w..8w+7 (one instruction).
+template <int NW, int DC = kDC>
 __host__ __device__ constexpr int issues_per_wave(bool rope_wave) {
-  return kTT / NW + (rope_wave ? 1 : 0);
+  return kTT / Geom<DC>::kRowsPerLoad / NW + (rope_wave ? 1 : 0);
 }
 
 // Issue wave w's loads of a tile whose first token row starts at lb (latent) / rb (rotary);
 // rows >= valid read as zeros.  Lane offsets are formed here (a few VALU operations per
 // load) rather than kept in registers across the loop.
-template <Swizzle SW, int NW>
+template <Swizzle SW, int NW, int DC = kDC>
 __device__ __forceinline__ void issue_tile(char* buf, int w, int lane, const bf16* lb,
                                            const bf16* rb, int valid, uint32_t lat_row_b,
                                            uint32_t rope_row_b) {
-  constexpr int R = kTT / NW;
+  using G = Geom<DC>;
+  constexpr int R = kTT / G::kRowsPerLoad / NW;  // latent load instructions per wave
   const __amdgpu_buffer_rsrc_t rl = rsrc(lb, valid * lat_row_b);
+  // lane -> (row t0 + lane / chunks, physical chunk lane % chunks); it lands at byte 16 lane
+  // of the instruction's destination, which is exactly that row and chunk
+  const int lr = lane / G::kChunks, lc = lane % G::kChunks;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const int t = R * w + j;
-    dma16(rl, buf + t * kLatRowB, t * lat_row_b + 16 * (lane ^ lat_sw<SW>(t)));
+    const int t0 = (R * w + j) * G::kRowsPerLoad, t = t0 + lr;
+    dma16(rl, buf + t0 * G::kLatRowB, t * lat_row_b + 16 * (lc ^ lat_sw<SW>(t)));
   }
   if (NW <= 4 || w < 4) {  // (known true at compile time for up to 4 waves)
     const __amdgpu_buffer_rsrc_t rr = rsrc(rb, valid * rope_row_b);
     const int rt = 8 * w + (lane >> 3);
-    dma16(rr, buf + kRopeOff + w * 1024, rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
+    dma16(rr, buf + G::kRopeOff + w * 1024, rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
   }
 }
 

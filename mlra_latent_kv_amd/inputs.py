@@ -86,6 +86,12 @@ WORKLOADS = {
                  seed=1004),
         Workload("mla_bf16_paged_b4_h128_l131072", batch=4, heads=128, branches=1, d_nope=128,
                  d_v=128, d_cb=512, d_rope=64, dtype="bf16", paged=True, seqlen=131072, seed=1005),
+        # one branch of MLRA-4 on its own, as each GPU of a 4-way tensor-parallel group runs it:
+        # rows [c_b (128) | k_rope (64)]; out_scale 0.5 makes the four shards' outputs sum to
+        # the MLRA-4 output ("[ICLR 2025] MLRA…", sections 1 and 4)
+        Workload("mlra_shard_bf16_b32_h32_l8192", batch=32, heads=32, branches=1, d_nope=128,
+                 d_v=128, d_cb=128, d_rope=64, dtype="bf16", paged=False, seqlen=8192,
+                 out_scale=0.5, seed=1006),
     ]
 }
 WORKLOAD_ORDER = list(WORKLOADS)

@@ -152,7 +152,7 @@ def test_f32_ragged(w, paged):
 # ----------------------------------------------------------------------------- bf16 path
 
 BF16 = ["mla_bf16_b32_h128_l4096", "mla_bf16_paged_b64_h32_l1k-32k", "mlra4_bf16_b32_h32_l8192",
-        "mla_bf16_paged_b4_h128_l131072"]
+        "mla_bf16_paged_b4_h128_l131072", "mlra_shard_bf16_b32_h32_l8192"]
 RAGGED = [1, 63, 64, 65, 300, 1000, 2049]
 
 
@@ -440,6 +440,9 @@ PLAN_CASES = [
     ("mla_bf16_paged_b64_h32_l1k-32k", [9000, 1, 70, 0, 300], 3),
     # MLRA-4 with more sequences than the item target: one item per sequence
     ("mlra4_bf16_b32_h32_l8192", [1 + (37 * i) % 200 for i in range(600)], 0),
+    # one MLRA branch (latent 128), automatic and forced
+    ("mlra_shard_bf16_b32_h32_l8192", [8192, 1, 700, 0, 64, 3000], 0),
+    ("mlra_shard_bf16_b32_h32_l8192", [8192, 1, 700, 0, 64, 3000], 7),
     # fp32 path
     ("tiny_mla_f32_b1_h4_l64", [64, 0, 5, 130], 0),
 ]
@@ -457,6 +460,52 @@ def test_split_plan(wname, lens, forced):
     assert_close(got[bs], oracle_out(inp, batches=bs), w.dtype, f"{wname} plan F{forced}")
     if len(lens) > len(bs):
         assert np.all(np.isfinite(got))
+
+
+# ----------------------------------------------------------------------------- MLRA shards
+
+@pytest.mark.parametrize("sharp", [False, True], ids=["default", "sharp"])
+def test_mlra_shards_sum_to_mlra4(sharp):
+    """Tensor-parallel MLRA-4 on one GPU: each branch run on its own through mla_decode
+    (latent width 128, one branch's W_UK / W_UV / query, out_scale 0.5), reading its
+    [c_b | k_rope] columns straight out of the MLRA-4 cache rows (latent pointer offset by
+    128 b, rotary pointer by 512, row stride 576), sums to mlra_decode's output ("[ICLR 2025]
+    MLRA…", section 2.1: the output is the scaled sum of independent branch outputs; section
+    4: 4-way tensor parallelism puts one branch on each GPU)."""
+    import torch
+    from mlra_latent_kv_amd import binding as B
+    from mlra_latent_kv_amd import harness as Hn
+    w = I.WORKLOADS["mlra4_bf16_b32_h32_l8192"]
+    lens = [700, 1, 64, 2049, 130]
+    inp = I.make_inputs(w, seqlens=lens, q_gain=I.sharp_q_gain(w) if sharp else 1.0)
+    case = Hn.to_device(inp)
+    full = case.run().clone()
+    total = torch.zeros(case.out.shape, dtype=torch.float32, device=case.out.device)
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=case.out.device)
+    esz = case.cache.element_size()
+    for br in range(4):
+        p = case.params.copy()
+        p.num_branches, p.d_latent = 1, 128
+        out = torch.empty_like(case.out)
+        qn = case.q_nope[:, :, br:br + 1].contiguous()
+        B.mla_decode(p, qn, case.q_rope, case.cache.data_ptr() + 128 * br * esz,
+                     case.cache.data_ptr() + 512 * esz, case.seqlens, None,
+                     case.w_uk[br], case.w_uv[br], out, ws)
+        torch.cuda.synchronize()
+        one = out.float().cpu().numpy().astype(np.float64)
+        # each shard alone against the oracle on that branch's own rows
+        rows = inp["cache"]
+        shard = dict(inp, workload=I.WORKLOADS["mlra_shard_bf16_b32_h32_l8192"],
+                     q_nope=inp["q_nope"][:, :, br:br + 1],
+                     cache=np.concatenate([rows[..., 128 * br:128 * (br + 1)], rows[..., 512:]], -1),
+                     w_uk=inp["w_uk"][br:br + 1], w_uv=inp["w_uv"][br:br + 1])
+        assert_close(one, oracle_out(shard), "bf16", f"shard {br} sharp={sharp}")
+        total += out.float()
+    got = total.cpu().numpy().astype(np.float64)
+    assert_close(got, oracle_out(inp), "bf16", f"sum of 4 shards vs oracle sharp={sharp}")
+    # the summed shards and the one-call MLRA-4 differ only by bf16 roundings
+    ref = full.float().cpu().numpy().astype(np.float64)
+    assert rel_l2(got, ref) < 5e-3, rel_l2(got, ref)
 
 
 # ----------------------------------------------------------------------------- device checks
@@ -535,6 +584,7 @@ SAMPLES = {
     "mla_bf16_paged_b64_h32_l1k-32k": ([0, 11, 21, 63], [0, 17, 31]),
     "mlra4_bf16_b32_h32_l8192": ([0, 31], [0, 13, 31]),
     "mla_bf16_paged_b4_h128_l131072": ([0, 3], [5, 40, 70, 120]),
+    "mlra_shard_bf16_b32_h32_l8192": ([0, 31], [0, 13, 31]),
 }
 
 
