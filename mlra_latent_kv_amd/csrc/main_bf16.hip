@@ -41,7 +41,14 @@ using namespace tile;
 constexpr int kHG = kHeadGroup;                      // heads per workgroup
 constexpr int kThreads = 256;                        // 4 waves
 constexpr int kPPitch = kTT + 8;                     // bf16 probability row pitch
-constexpr int kBufs = 2;                             // tile ring depth per workgroup
+// Tile ring depth per workgroup: two 36 KB buffers for the 576-wide rows (two workgroups per
+// CU fill the LDS); the 12 KB tiles of the 192-wide rows take a deeper ring in the same room,
+// so that more of the (short) per-tile compute overlaps loads in flight.
+#ifndef MLA_NARROW_RING
+#define MLA_NARROW_RING 2
+#endif
+template <int DC>
+constexpr int ring_depth() { return DC == 512 ? 2 : MLA_NARROW_RING; }
 
 // Exchange buffers first, then the tile ring on a 256-byte boundary.
 template <int NB, int DC>
@@ -51,11 +58,11 @@ struct Smem {
   float sum[NB == 1 ? 2 * kHG : 1];           // MLA: per-head probability sum of each half
   float alpha[NB == 1 ? kHG : 1];             // MLA: per-head rescale of this tile
   char gap[256];
-  __attribute__((aligned(256))) char ring[kBufs][Geom<DC>::kBufBytes];
+  __attribute__((aligned(256))) char ring[ring_depth<DC>()][Geom<DC>::kBufBytes];
 };
 
 template <int NB, int DC>
-__global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
+__global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_main_bf16(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, const int32_t* __restrict__ work, const int32_t* __restrict__ bt,
@@ -63,6 +70,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
     int n_hg) {
   static_assert(NB == 1 || DC == 512, "MLRA-4 rows hold four 128-wide branches");
   using G = Geom<DC>;
+  constexpr int kBufs = ring_depth<DC>();
+  constexpr int kIssues = issues_per_wave<4, DC>(true);  // tile loads per wave per tile
   constexpr int kRowW = DC + kDR;   // cached (and absorbed-query) row width
   constexpr int kNOB = DC / 128;    // 32-column output blocks per wave
   __shared__ __align__(16) Smem<NB, DC> sm;
@@ -89,12 +98,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
   // (chunk-swizzled through the per-lane source offsets).
   const uint32_t lat_row_b = (uint32_t)(lat_tok * 2), rope_row_b = (uint32_t)(rope_tok * 2);
 
+  // tile k of the item into its ring buffer.  Past the item's end (k >= n_tiles) the same
+  // loads go out with an empty buffer descriptor: they return zeros without touching memory,
+  // so every wave issues the same number of loads per tile on every path and every wait below
+  // is a fixed count.
   auto issue = [&](int k) {
     const int t0 = t_begin + kTT * k;
-    const int valid = min(kTT, t_end - t0);
-    const bf16* lb;
-    const bf16* rb;
-    if (paged) {
+    const int valid = k < n_tiles ? min(kTT, t_end - t0) : 0;
+    const bf16* lb = latent;
+    const bf16* rb = rope;
+    if (valid == 0) {
+    } else if (paged) {
       const int64_t pg = bt[(int64_t)b * bt_stride + t0 / kPage];
       lb = latent + pg * lat_seq + (int64_t)(t0 % kPage) * lat_tok;
       rb = rope + pg * rope_seq + (int64_t)(t0 % kPage) * rope_tok;
@@ -102,7 +116,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
       lb = latent + (int64_t)b * lat_seq + (int64_t)t0 * lat_tok;
       rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
     }
-    issue_tile<Sw32, 4, DC>(sm.ring[k % kBufs], w, lane, lb, rb, valid, lat_row_b, rope_row_b);
+    issue_tile<Sw32, 4, DC>(sm.ring[k % kBufs], w, lane, lb, rb,
+                            __builtin_amdgcn_readfirstlane(valid), lat_row_b, rope_row_b);
   };
 
   // absorbed query as the MFMA B operand (N = heads).
@@ -126,7 +141,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
     for (int j = 0; j < 4; ++j) qb[8 + j] = *(const bf16x8*)(qrow + kDC + 16 * j);
   }
 
-  issue(0);
+  // start-up: the query, then tiles 0 .. kBufs - 2, then one wait for all but tiles 1 ..
+  // kBufs - 2.  The query's loads are older than tile 0's, so the wait completes them too,
+  // and tells the compiler's wait analysis so (it would otherwise wait for every load in
+  // flight before the first use of the query registers).
+#pragma unroll
+  for (int j = 0; j < kBufs - 1; ++j) issue(j);
+  wait_vmcnt<(kBufs - 2) * kIssues>();
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 O[kNOB];
@@ -150,9 +171,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
             lat_piece<Sw32, DC>(16 * s2 + v_row + r * v_delta, w * (DC / 4) + 32 * mb + v_col);
 
   for (int k = 0; k < n_tiles; ++k) {
-    wait_vmcnt<0>();  // with a ring of two, tile k+1 is issued only after tile k landed
-    lds_barrier();  // tile k landed for every wave; buffer of tile k-1 is free
-    if (k + 1 < n_tiles) issue(k + 1);
+    // tile k has landed (the kBufs - 2 younger tiles' loads may still be out); after the
+    // barrier it has landed for every wave, and tile k - 1's buffer is free for k + kBufs - 1
+    wait_vmcnt<(kBufs - 2) * kIssues>();
+    lds_barrier();
+    issue(k + kBufs - 1);
 
     const int t0 = t_begin + kTT * k;
     const int valid = min(kTT, t_end - t0);
@@ -266,6 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_main_bf16(
   // 1 KiB (or four 256-byte rows) per instruction.
   constexpr int kOutPitch = DC * 2 + 16;  // LDS bytes per head row (+16: 2-way conflicts)
   static_assert(kHG * kOutPitch <= G::kBufBytes, "output staging exceeds one ring buffer");
+  wait_vmcnt<0>();  // the loads past the item's last tile have landed (into other buffers)
   __syncthreads();  // every wave is done with the ring
   char* stage = sm.ring[0];
 #pragma unroll

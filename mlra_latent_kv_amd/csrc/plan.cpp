@@ -91,8 +91,12 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   const int64_t wg_per_item = q.path != Path::kBf16Mfma ? q.H
                               : q.wide ? q.H / kWideHeads
                                        : q.n_hg;
-  // workgroups that fill the chip once: the wide kernel holds one per CU, the others two
-  const int64_t target_wg = q.wide ? q.n_cu : 2 * (int64_t)q.n_cu;
+  // workgroups that fill the chip once: the wide kernel holds one per CU, the 32-head kernel
+  // on 192-wide rows kNarrowWgPerCu, the others two
+  const bool narrow = q.path == Path::kBf16Mfma && q.NB == 1 && q.dcb == 128;
+  const int64_t target_wg = q.wide ? q.n_cu
+                            : narrow ? (int64_t)kNarrowWgPerCu * q.n_cu
+                                     : 2 * (int64_t)q.n_cu;
   q.target = (int)std::max<int64_t>(1, ceil_div(target_wg, wg_per_item));
   q.xcd_major = q.wide;
   int64_t cap;

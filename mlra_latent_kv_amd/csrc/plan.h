@@ -13,6 +13,12 @@ namespace mla {
 constexpr int kPage = MLA_PAGE_SIZE;   // tokens per page
 constexpr int kHeadGroup = 32;         // heads per workgroup of the 32-head bf16 kernels
 constexpr int kWideHeads = 128;        // heads per workgroup of the wide bf16 kernel
+// workgroups per CU of the 32-head kernel on 192-wide rows (one MLRA branch): its tiles and
+// registers are small, so several workgroups share a CU and hide each other's per-tile chain
+#ifndef MLA_NARROW_OCC
+#define MLA_NARROW_OCC 4
+#endif
+constexpr int kNarrowWgPerCu = MLA_NARROW_OCC;
 constexpr int kMaxCUs = 256;           // compute units the workspace is sized for (MI355X);
                                        // a device reporting more is planned as if it had 256
 constexpr size_t kWsAlign = 256;
