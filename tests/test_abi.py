@@ -188,7 +188,8 @@ def test_workspace_layout(lib, wname, forced):
     S = B.num_splits(p)
     wide = w.dtype == "bf16" and w.branches == 1 and w.heads % 128 == 0
     wg_per_item = w.heads // 128 if wide else w.heads // 32 if w.dtype == "bf16" else w.heads
-    target = max(1, -(-(256 if wide else 512) // wg_per_item))
+    shard = w.dtype == "bf16" and w.branches == 1 and w.d_cb == 128   # four workgroups per CU
+    target = max(1, -(-(256 if wide else 1024 if shard else 512) // wg_per_item))
     Bn, H, dc = 3, w.heads, w.d_c
     if forced:
         assert S == -(-pages // -(-pages // forced))

@@ -408,14 +408,16 @@ def n_cu():
 
 def plan_kind(w, H=None):
     """(XCD-major slots?, item target) of the kernel that runs workload w with H heads (one
-    workgroup per CU for the 128-head kernel, two for the others)."""
+    workgroup per CU for the 128-head kernel, four for the 32-head kernel on one MLRA
+    branch's 192-wide rows, two for the others)."""
     H = w.heads if H is None else H
     cu = min(n_cu(), 256)
     if w.dtype != "bf16":
         return False, -(-2 * cu // H)
-    if w.branches == 1 and H % 128 == 0:
+    if w.branches == 1 and H % 128 == 0 and w.d_cb == 512:
         return True, -(-cu // (H // 128))
-    return False, -(-2 * cu // (H // 32))
+    per_cu = 4 if (w.branches == 1 and w.d_cb == 128) else 2  # one MLRA branch: four per CU
+    return False, -(-per_cu * cu // (H // 32))
 
 
 def device_plan_matches(case, w, lens, forced=0, H=None):
