@@ -30,7 +30,18 @@ and the branch outputs are summed with a scale.  Sources (page title, section):
 * RoPE follows RoFormer (cited in the interview Q&A's references): pairs
   (x_{2i}, x_{2i+1}) rotate by angle pos * theta^(-2i/d_rope).
 
+Write side (``latent_rows``, ``cache_append``): at write time each new token's
+hidden state is compressed into the joint latent by a down-projection
+("超越 GQA 的推理革命…MLA…", section "鍵值聯合低秩壓縮", 寫入時（壓縮）), and the
+position part is a separate uncompressed key that carries RoPE (same page,
+section "解耦旋轉位置編碼"); MLRA's branches are column blocks of the same
+projection ("[ICLR 2025] MLRA…", section 2.1), so the row is computed alike.
+
 Readings where the pages are silent (each is an argument, not hidden):
+  the cache stores the rotary key already rotated at its own position t;
+  a decode step appends its token at t = L_b, then L_b becomes t + 1;
+  a sequence whose new token starts a page takes the next entry of a free-page
+  list, in batch order; when the list runs out that sequence is not written;
   the softmax scale is an argument (default 1/sqrt(d_nope + d_rope));
   the cached rope key is rotated at its own position t, the query at L - 1;
   one q_nope per (head, branch) and one q_rope per head shared by branches;
@@ -202,3 +213,63 @@ def mla_decode(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, d_rope: int, scale
         out[i] = f(qn[b], qr[b], rows, w_uk, w_uv, d_rope=d_rope, scale=scale,
                    out_scale=out_scale, theta=theta, heads=heads)
     return out
+
+
+# ----------------------------------------------------------------------------- write side
+
+def latent_rows(hidden, w_dkv, w_kr, positions, theta: float = 10000.0) -> np.ndarray:
+    """Cache rows [c_KV | k_rope] of new tokens, fp64.
+
+    c_KV = h W_DKV, the joint low-rank latent made at write time ("超越 GQA 的推理革命…MLA…",
+    section "鍵值聯合低秩壓縮"); k_rope = RoPE(h W_KR, t), the separate uncompressed key that
+    carries the position (same page, section "解耦旋轉位置編碼"), rotated at the token's own
+    position t as the cache stores it.  hidden [n, d_model], w_dkv [d_model, d_c],
+    w_kr [d_model, d_r], positions [n] -> [n, d_c + d_r].
+    """
+    h = _as_f64(hidden)
+    c = h @ _as_f64(w_dkv)
+    k = rope(h @ _as_f64(w_kr), np.asarray(positions, dtype=np.int64), theta)
+    return np.concatenate([c, k], axis=-1)
+
+
+def cache_append(hidden, w_dkv, w_kr, seqlens, block_table=None, free_pages=(), *,
+                 theta: float = 10000.0, page_size: int = 0, capacity: Optional[int] = None):
+    """One decode step's cache write for a batch (fp64 rows, exact integer bookkeeping).
+
+    Sequence b's new token goes to position t = seqlens[b] and the length becomes t + 1.
+    Paged cache (page_size > 0): when t starts a page (t % page_size == 0) the sequence needs
+    a new page; the k-th such sequence in batch order takes free_pages[k] and it is entered at
+    block_table[b, t // page_size]; otherwise the row goes to the page already there.  When
+    the free list runs out, a sequence that needs a page is not written and keeps its length.
+    Contiguous cache: the row goes to cache[b, t], t < capacity.
+
+    Returns dict(rows [B, row] fp64, where [B] (page, slot) or (b, t) of each written row
+    (None if not written), seqlens [B], block_table (copy, updated), pages_used, written [B]).
+    """
+    lens = [int(x) for x in np.asarray(seqlens).reshape(-1)]
+    B = len(lens)
+    if any(t < 0 for t in lens):
+        raise ValueError("negative length")
+    rows = latent_rows(hidden, w_dkv, w_kr, lens, theta)
+    bt = None if block_table is None else np.array(block_table, dtype=np.int64, copy=True)
+    where, written, new_lens, used = [None] * B, [False] * B, list(lens), 0
+    free = [int(x) for x in free_pages]
+    for b, t in enumerate(lens):
+        if page_size:
+            j = t // page_size
+            if j >= bt.shape[1]:
+                raise ValueError("block table row full")
+            if t % page_size == 0:
+                if used == len(free):
+                    continue  # no free page left: not written
+                bt[b, j] = free[used]
+                used += 1
+            where[b] = (int(bt[b, j]), t % page_size)
+        else:
+            if capacity is not None and t >= capacity:
+                raise ValueError("contiguous cache full")
+            where[b] = (b, t)
+        written[b] = True
+        new_lens[b] = t + 1
+    return dict(rows=rows, where=where, seqlens=np.array(new_lens, dtype=np.int64),
+                block_table=bt, pages_used=used, written=np.array(written))

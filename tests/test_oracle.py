@@ -448,3 +448,179 @@ def test_planted_mistake_is_caught(monkeypatch, mistake):
     elif mistake == "softmax_unnormalised":
         monkeypatch.setattr(O, "softmax", lambda s: np.exp(s - s.max(-1, keepdims=True)))
     assert not _pins_pass()
+
+
+# ----------------------------------------------------------------------------- write-side pins
+# c_KV = h W_DKV and k_rope = RoPE(h W_KR, t) at the token's own position t ("超越 GQA 的推理
+# 革命…MLA…", sections 鍵值聯合低秩壓縮 and 解耦旋轉位置編碼); the new token goes to t = L_b.
+
+def _append_case(B=5, d_model=7, d_c=4, d_r=2, seed=11):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, d_model)), rng.standard_normal((d_model, d_c)),
+            rng.standard_normal((d_model, d_r)))
+
+
+def test_append_hand_example_page_allocation():
+    """Worked by hand, page size 64.  Lengths [64, 5, 0, 128, 63]: sequences 0, 2 and 3 start
+    a page (64, 0 and 128 are multiples of 64) and take free pages 11, 4, 9 in batch order, at
+    block-table columns 1, 0, 2; sequence 1 writes slot 5 of its page 0 and sequence 4 slot 63
+    of its page 5.  With only one free page, sequences 2 and 3 are not written."""
+    h, wd, wk = _append_case()
+    bt = np.full((5, 4), -1)
+    bt[0, 0], bt[1, 0], bt[3, 0], bt[3, 1], bt[4, 0] = 2, 0, 1, 3, 5
+    r = O.cache_append(h, wd, wk, [64, 5, 0, 128, 63], bt, [11, 4, 9], page_size=64)
+    assert r["where"] == [(11, 0), (0, 5), (4, 0), (9, 0), (5, 63)]
+    assert list(r["seqlens"]) == [65, 6, 1, 129, 64] and r["pages_used"] == 3
+    want = bt.copy()
+    want[0, 1], want[2, 0], want[3, 2] = 11, 4, 9
+    assert np.array_equal(r["block_table"], want) and np.array_equal(bt[0], [2, -1, -1, -1])
+    r = O.cache_append(h, wd, wk, [64, 5, 0, 128, 63], bt, [11], page_size=64)
+    assert r["where"] == [(11, 0), (0, 5), None, None, (5, 63)]
+    assert list(r["seqlens"]) == [65, 6, 0, 128, 64] and r["pages_used"] == 1
+    assert list(r["written"]) == [True, True, False, False, True]
+    want = bt.copy()
+    want[0, 1] = 11
+    assert np.array_equal(r["block_table"], want)
+    # contiguous: the row goes to (b, t)
+    r = O.cache_append(h[:2], wd, wk, [3, 0], capacity=8)
+    assert r["where"] == [(0, 3), (1, 0)] and list(r["seqlens"]) == [4, 1]
+    with pytest.raises(ValueError):
+        O.cache_append(h[:1], wd, wk, [8], capacity=8)
+
+
+def test_append_one_hot_hidden_selects_weight_rows():
+    """h = e_j picks row j of each down-projection; with d_r = 2 (one pair, frequency 1) the
+    rotary part is row j of W_KR turned by t radians counter-clockwise."""
+    _, wd, wk = _append_case(d_model=6)
+    for j, t in [(0, 0), (3, 1), (5, 77), (2, 4095)]:
+        row = O.latent_rows(np.eye(6)[j][None], wd, wk, [t])[0]
+        assert np.array_equal(row[:4], wd[j])
+        R = np.array([[math.cos(t), -math.sin(t)], [math.sin(t), math.cos(t)]])
+        assert np.allclose(row[4:], R @ wk[j], rtol=0, atol=1e-12)
+
+
+def test_append_brute_force_scalar():
+    """Pure-Python scalar loops (math.fsum dot products, complex-number rotation) against the
+    NumPy rows, several positions and a d_r = 8 rotary part."""
+    rng = np.random.default_rng(5)
+    n, d_model, d_c, d_r = 4, 9, 6, 8
+    h = rng.standard_normal((n, d_model))
+    wd = rng.standard_normal((d_model, d_c))
+    wk = rng.standard_normal((d_model, d_r))
+    pos = [0, 1, 63, 131071]
+    got = O.latent_rows(h, wd, wk, pos, theta=10000.0)
+    for i in range(n):
+        c = [math.fsum(h[i, k] * wd[k, j] for k in range(d_model)) for j in range(d_c)]
+        raw = [math.fsum(h[i, k] * wk[k, j] for k in range(d_model)) for j in range(d_r)]
+        rot = []
+        for p in range(d_r // 2):
+            z = complex(raw[2 * p], raw[2 * p + 1]) * cmath.exp(1j * pos[i] * 10000.0 ** (-2 * p / d_r))
+            rot += [z.real, z.imag]
+        assert np.allclose(got[i], c + rot, rtol=1e-12, atol=1e-12)
+
+
+def test_append_rows_are_linear_in_the_hidden_state():
+    h, wd, wk = _append_case(B=2, d_model=9, d_c=5, d_r=4)
+    pos = [17, 17]
+    a = O.latent_rows(h[:1] + 2.0 * h[1:], wd, wk, pos[:1])
+    b = O.latent_rows(h[:1], wd, wk, pos[:1]) + 2.0 * O.latent_rows(h[1:], wd, wk, pos[1:])
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def _append_then_decode(w, L, rng, patch=None):
+    """Decode output of a cache built by appending L tokens one step at a time into an empty,
+    shuffled paged pool (stored rotary keys turned back by their positions, since the decode
+    oracle takes raw keys), and of the same tokens' raw rows laid out contiguously."""
+    d_model = 24
+    h = rng.standard_normal((L, d_model)) / math.sqrt(d_model)
+    wd = rng.standard_normal((d_model, w.d_c)) / math.sqrt(d_model)
+    wk = rng.standard_normal((d_model, w.d_rope)) / math.sqrt(d_model)
+    pages = -(-L // 64)
+    free = list(rng.permutation(pages + 3))
+    pool = np.zeros((pages + 3, 64, w.row))
+    bt = np.full((1, pages), -1)
+    seqlen = [0]
+    for t in range(L):
+        r = O.cache_append(h[t:t + 1], wd, wk, seqlen, bt, free, page_size=64)
+        pg, slot = r["where"][0]
+        pool[pg, slot] = r["rows"][0]
+        bt, seqlen, free = r["block_table"], list(r["seqlens"]), free[r["pages_used"]:]
+    assert seqlen == [L]
+    raw_pool = pool.copy()
+    for t in range(L):  # decode takes raw keys: undo the rotation at each token's position
+        pg, slot = bt[0, t // 64], t % 64
+        raw_pool[pg, slot, w.d_c:] = O.rope(pool[pg, slot, w.d_c:], -t, w.rope_theta)
+    direct = np.concatenate([h @ wd, h @ wk], axis=1)[None]
+    qn = rng.standard_normal((1, w.heads, w.branches, w.d_nope))
+    qr = rng.standard_normal((1, w.heads, w.d_rope))
+    wuk = rng.standard_normal((w.branches, w.heads, w.d_nope, w.d_cb)) / math.sqrt(w.d_cb)
+    wuv = rng.standard_normal((w.branches, w.heads, w.d_cb, w.d_v)) / math.sqrt(w.d_cb)
+    kw = dict(d_rope=w.d_rope, scale=w.softmax_scale, out_scale=w.out_scale, theta=w.rope_theta)
+    a = O.mla_decode(qn, qr, raw_pool, [L], wuk, wuv, page_size=64, block_table=bt, **kw)
+    b = O.mla_decode(qn, qr, direct, [L], wuk, wuv, **kw)
+    return a, b
+
+
+@pytest.mark.parametrize("wname", ["tiny_mla_f32_b1_h4_l64", "mlra4_f32_like"])
+def test_append_then_decode_equals_direct_cache(wname):
+    """Appending tokens one decode step at a time (positions 0, 1, ..., pages taken from a
+    shuffled free list as each page fills) gives the cache the decode step reads: its output
+    equals that of the same tokens' rows written directly."""
+    w = (I.WORKLOADS["tiny_mla_f32_b1_h4_l64"] if wname.startswith("tiny") else
+         I.Workload("mlra4_f32_like", batch=1, heads=2, branches=4, d_nope=4, d_v=3, d_cb=4,
+                    d_rope=4, dtype="f32", paged=True, seqlen=150, out_scale=0.5))
+    a, b = _append_then_decode(w, 150, np.random.default_rng(3))
+    assert rel_l2(a, b) < 1e-12
+
+
+def _append_pins_pass():
+    checks = [test_append_hand_example_page_allocation,
+              test_append_one_hot_hidden_selects_weight_rows, test_append_brute_force_scalar,
+              lambda: test_append_then_decode_equals_direct_cache("tiny_mla_f32_b1_h4_l64")]
+    with np.errstate(all="ignore"):
+        for c in checks:
+            try:
+                c()
+            except (AssertionError, ValueError, IndexError):
+                return False
+    return True
+
+
+def test_append_pins_pass_unplanted():
+    assert _append_pins_pass()
+
+
+@pytest.mark.parametrize("mistake", ["position_plus_one", "not_rotated", "reverse_allocation",
+                                     "length_not_bumped", "kr_from_dkv_columns"])
+def test_append_planted_mistake_is_caught(monkeypatch, mistake):
+    real_rows, real_append = O.latent_rows, O.cache_append
+    if mistake == "position_plus_one":
+        monkeypatch.setattr(O, "latent_rows", lambda h, wd, wk, pos, theta=1e4: real_rows(
+            h, wd, wk, np.asarray(pos) + 1, theta))
+    elif mistake == "not_rotated":
+        monkeypatch.setattr(O, "latent_rows", lambda h, wd, wk, pos, theta=1e4: real_rows(
+            h, wd, wk, np.zeros_like(np.asarray(pos)), theta))
+    elif mistake == "kr_from_dkv_columns":
+        monkeypatch.setattr(O, "latent_rows", lambda h, wd, wk, pos, theta=1e4: real_rows(
+            h, wd, np.asarray(wd)[:, :np.asarray(wk).shape[1]], pos, theta))
+    elif mistake == "reverse_allocation":
+        def bad(h, wd, wk, lens, bt=None, free=(), **kw):
+            lens = list(lens)
+            order = list(range(len(lens)))[::-1]  # allocate to the last sequences first
+            res = real_append(np.asarray(h)[order], wd, wk, [lens[i] for i in order],
+                              None if bt is None else np.asarray(bt)[order], free, **kw)
+            inv = np.argsort(order)
+            res["rows"], res["seqlens"] = res["rows"][inv], res["seqlens"][inv]
+            res["where"] = [res["where"][i] for i in inv]
+            res["written"] = res["written"][inv]
+            if res["block_table"] is not None:
+                res["block_table"] = res["block_table"][inv]
+            return res
+        monkeypatch.setattr(O, "cache_append", bad)
+    elif mistake == "length_not_bumped":
+        def bad(*a, **kw):
+            res = real_append(*a, **kw)
+            res["seqlens"] = np.asarray(a[3])
+            return res
+        monkeypatch.setattr(O, "cache_append", bad)
+    assert not _append_pins_pass()
