@@ -239,37 +239,41 @@ def cache_append(hidden, w_dkv, w_kr, seqlens, block_table=None, free_pages=(), 
     Sequence b's new token goes to position t = seqlens[b] and the length becomes t + 1.
     Paged cache (page_size > 0): when t starts a page (t % page_size == 0) the sequence needs
     a new page; the k-th such sequence in batch order takes free_pages[k] and it is entered at
-    block_table[b, t // page_size]; otherwise the row goes to the page already there.  When
-    the free list runs out, a sequence that needs a page is not written and keeps its length.
-    Contiguous cache: the row goes to cache[b, t], t < capacity.
+    block_table[b, t // page_size]; otherwise the row goes to the page already there.
+    Contiguous cache: the row goes to cache[b, t], t < capacity.  A sequence is not written
+    and keeps its length when the free list has no k-th page for it, or when t lies outside
+    the cache (t < 0, a block-table column past the row, a missing page, t >= capacity).
+    pages_used = min(sequences needing a page, len(free_pages)).
 
     Returns dict(rows [B, row] fp64, where [B] (page, slot) or (b, t) of each written row
     (None if not written), seqlens [B], block_table (copy, updated), pages_used, written [B]).
     """
     lens = [int(x) for x in np.asarray(seqlens).reshape(-1)]
     B = len(lens)
-    if any(t < 0 for t in lens):
-        raise ValueError("negative length")
-    rows = latent_rows(hidden, w_dkv, w_kr, lens, theta)
+    rows = latent_rows(hidden, w_dkv, w_kr, [max(t, 0) for t in lens], theta)
     bt = None if block_table is None else np.array(block_table, dtype=np.int64, copy=True)
     where, written, new_lens, used = [None] * B, [False] * B, list(lens), 0
     free = [int(x) for x in free_pages]
+    # the page ranks count every sequence whose token starts a page, in batch order
     for b, t in enumerate(lens):
+        if t < 0:
+            continue  # outside the cache: not written
         if page_size:
             j = t // page_size
-            if j >= bt.shape[1]:
-                raise ValueError("block table row full")
             if t % page_size == 0:
-                if used == len(free):
-                    continue  # no free page left: not written
-                bt[b, j] = free[used]
+                k = used
                 used += 1
+                if k >= len(free) or j >= bt.shape[1]:
+                    continue  # no free page left, or the block-table row is full
+                bt[b, j] = free[k]
+            elif j >= bt.shape[1] or bt[b, j] < 0:
+                continue  # the page for position t is missing
             where[b] = (int(bt[b, j]), t % page_size)
         else:
             if capacity is not None and t >= capacity:
-                raise ValueError("contiguous cache full")
+                continue  # past the contiguous cache's rows
             where[b] = (b, t)
         written[b] = True
         new_lens[b] = t + 1
     return dict(rows=rows, where=where, seqlens=np.array(new_lens, dtype=np.int64),
-                block_table=bt, pages_used=used, written=np.array(written))
+                block_table=bt, pages_used=min(used, len(free)), written=np.array(written))

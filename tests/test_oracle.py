@@ -481,11 +481,16 @@ def test_append_hand_example_page_allocation():
     want = bt.copy()
     want[0, 1] = 11
     assert np.array_equal(r["block_table"], want)
-    # contiguous: the row goes to (b, t)
-    r = O.cache_append(h[:2], wd, wk, [3, 0], capacity=8)
-    assert r["where"] == [(0, 3), (1, 0)] and list(r["seqlens"]) == [4, 1]
-    with pytest.raises(ValueError):
-        O.cache_append(h[:1], wd, wk, [8], capacity=8)
+    # contiguous: the row goes to (b, t); a full sequence is left untouched
+    r = O.cache_append(h[:3], wd, wk, [3, 0, 8], capacity=8)
+    assert r["where"] == [(0, 3), (1, 0), None] and list(r["seqlens"]) == [4, 1, 8]
+    # a sequence whose page is missing (negative entry) or whose row is full is not written;
+    # it still counts in the page ranks when its token starts a page
+    bt2 = np.full((3, 2), -1)
+    bt2[0, 0], bt2[1, 0], bt2[1, 1] = 7, 8, 9
+    r = O.cache_append(h[:3], wd, wk, [65, 128, 64], bt2, [3, 6], page_size=64)
+    assert r["where"] == [None, None, (6, 0)] and list(r["seqlens"]) == [65, 128, 65]
+    assert r["pages_used"] == 2 and r["block_table"][2, 1] == 6
 
 
 def test_append_one_hot_hidden_selects_weight_rows():
