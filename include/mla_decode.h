@@ -254,6 +254,62 @@ mla_status mla_decode_noalloc(const mla_params* p, const void* q_nope, const voi
 mla_status mla_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int64_t n_rows,
                            int32_t d_rope, float theta, int32_t dtype, hipStream_t stream);
 
+/*
+ * Cache append: the write side of the same cache, one decode step's new token per sequence
+ * ("超越 GQA 的推理革命…MLA…", section 鍵值聯合低秩壓縮: at write time the token's key and
+ * value information is compressed into the joint low-rank latent; section 解耦旋轉位置編碼:
+ * the position part is a separate uncompressed key carrying RoPE).  For every sequence b,
+ * with t = seqlens[b] (the new token's position; the cache then holds t + 1 tokens):
+ *   c_KV   = h_b W_DKV                     (d_latent)
+ *   k_rope = RoPE(h_b W_KR, position t)    (d_rope, stored rotated, as mla_decode reads it)
+ * and the row [c_KV | k_rope] goes to position t of sequence b, after which seqlens[b] = t + 1.
+ * MLRA-4's four branches are column blocks of the same projection, so its rows (d_latent =
+ * 4 x 128) are written alike; one branch alone is d_latent = 128.
+ * Paged cache: when t is a multiple of 64 the token starts a new page.  The sequences that
+ * need one are ranked in batch order, the k-th takes free_pages[k], and it is entered at
+ * block_table[b, t / 64]; *pages_used (device) receives min(pages needed, n_free), so the
+ * caller can advance its free list.  A sequence that needs a page when the list is exhausted,
+ * or whose position lies outside the cache (t < 0, t / 64 >= max_pages_per_seq, or
+ * t >= capacity for a contiguous cache), is left untouched (no row, same length).
+ * Accumulation fp32, storage bf16 (round to nearest even); angles reduced in fp64.
+ *
+ * Arguments (device pointers unless noted):
+ *   hidden      bf16 [B, d_model], the new tokens' hidden states, 16-byte aligned
+ *   w_dkv       bf16 [d_model, d_latent] (row = input feature), 16-byte aligned
+ *   w_kr        bf16 [d_model, d_rope], 16-byte aligned
+ *   latent/rope the cache, addressed as in mla_decode with the strides below (written)
+ *   seqlens     int32 [B] (read and written); block_table int32 [B, block_table_stride]
+ *               (paged: read and written; may be NULL for a contiguous cache)
+ *   free_pages  int32 [n_free] page ids (may be NULL when n_free = 0)
+ *   pages_used  int32 [1] (written)
+ *   workspace   >= mla_append_workspace_size(p) bytes, 256-byte aligned
+ * Supported: MLA_BF16, d_latent 512 or 128, d_rope 64, d_model a multiple of 256 up to
+ * 65536, page_size 0 or 64.  Same conventions as the decode entry points (host validation,
+ * no allocation, asynchronous on stream).
+ */
+typedef struct mla_append_params {
+  int32_t batch;              /* B sequences, one new token each                           */
+  int32_t d_model;            /* hidden size of the new tokens                             */
+  int32_t d_latent;           /* latent width of a row (NB * d_cb)                         */
+  int32_t d_rope;             /* rotary key width                                          */
+  int32_t page_size;          /* 0 = contiguous cache, MLA_PAGE_SIZE = paged cache         */
+  int32_t max_pages_per_seq;  /* paged: usable block_table columns                         */
+  int32_t capacity;           /* contiguous: token rows per sequence                       */
+  int32_t dtype;              /* mla_dtype                                                 */
+  int64_t latent_stride_tok, latent_stride_seq, rope_stride_tok, rope_stride_seq;
+  int64_t block_table_stride;
+  float rope_theta;
+} mla_append_params;
+
+/* Workspace bytes mla_cache_append needs for *p (host pointer *bytes). */
+mla_status mla_append_workspace_size(const mla_append_params* p, size_t* bytes);
+
+mla_status mla_cache_append(const mla_append_params* p, const void* hidden, const void* w_dkv,
+                            const void* w_kr, void* latent, void* rope, int32_t* seqlens,
+                            int32_t* block_table, const int32_t* free_pages, int32_t n_free,
+                            int32_t* pages_used, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* mla_status_str(int32_t status);
 

@@ -45,6 +45,17 @@ class MlaParams(ctypes.Structure):
         return c
 
 
+class MlaAppendParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_int32), ("d_model", c_int32), ("d_latent", c_int32), ("d_rope", c_int32),
+        ("page_size", c_int32), ("max_pages_per_seq", c_int32), ("capacity", c_int32),
+        ("dtype", c_int32),
+        ("latent_stride_tok", c_int64), ("latent_stride_seq", c_int64),
+        ("rope_stride_tok", c_int64), ("rope_stride_seq", c_int64),
+        ("block_table_stride", c_int64), ("rope_theta", c_float),
+    ]
+
+
 class MlaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -74,12 +85,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_timed.argtypes = dec + [c_void_p]
     lib.mlra_decode_timed.argtypes = dec + [c_void_p]
     lib.mla_decode_noalloc.argtypes = [P] + [c_void_p] * 10
+    PA = ctypes.POINTER(MlaAppendParams)
+    lib.mla_append_workspace_size.argtypes = [PA, ctypes.POINTER(c_size_t)]
+    lib.mla_cache_append.argtypes = [PA] + [c_void_p] * 8 + [c_int32, c_void_p, c_void_p,
+                                                               c_size_t, c_void_p]
     lib.mla_rope_rotate.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_float,
                                     c_int32, c_void_p]
     lib.mla_status_str.argtypes = [c_int32]
     lib.mla_status_str.restype = ctypes.c_char_p
     for f in ("mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
-              "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc", "mla_rope_rotate"):
+              "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc", "mla_rope_rotate",
+              "mla_append_workspace_size", "mla_cache_append"):
         getattr(lib, f).restype = c_int32
     _lib = lib
     return lib
@@ -181,4 +197,27 @@ def mla_rope_rotate(x, row_stride: int, pos, n_rows: int, d_rope: int, theta: fl
                                 _stream(stream) if n_rows else None)
     if check and st:
         raise MlaError(st, "mla_rope_rotate")
+    return st
+
+
+def append_workspace_size(params: MlaAppendParams) -> int:
+    n = c_size_t(0)
+    st = load().mla_append_workspace_size(ctypes.byref(params), ctypes.byref(n))
+    if st:
+        raise MlaError(st, "mla_append_workspace_size")
+    return n.value
+
+
+def mla_cache_append(params, hidden, w_dkv, w_kr, latent, rope, seqlens, block_table, free_pages,
+                     n_free: int, pages_used, workspace, workspace_bytes=None, stream=None,
+                     check=True) -> int:
+    """One decode step's cache write (see include/mla_decode.h, mla_cache_append)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = load().mla_cache_append(ctypes.byref(params), _ptr(hidden), _ptr(w_dkv), _ptr(w_kr),
+                                 _ptr(latent), _ptr(rope), _ptr(seqlens), _ptr(block_table),
+                                 _ptr(free_pages), n_free, _ptr(pages_used), _ptr(workspace),
+                                 workspace_bytes, _stream(stream))
+    if check and st:
+        raise MlaError(st, "mla_cache_append")
     return st

@@ -10,6 +10,7 @@
 // Nothing is allocated, nothing synchronises, no state is kept between calls.
 #include <atomic>
 
+#include "append.h"
 #include "launch.h"
 #include "plan.h"
 
@@ -227,6 +228,48 @@ mla_status mla_rope_rotate(void* x, int64_t row_stride, const int32_t* pos, int6
   if (st != MLA_OK || n_rows == 0) return st;
   return to_status(launch_rope_rotate(x, row_stride, pos, n_rows, d_rope, theta, dtype,
                                       stream));
+}
+
+mla_status mla_append_workspace_size(const mla_append_params* p, size_t* bytes) {
+  if (!bytes) return MLA_ERR_NULL;
+  AppendPlan plan;
+  const mla_status st = make_append_plan(p, &plan);
+  if (st == MLA_OK) *bytes = plan.bytes;
+  return st;
+}
+
+mla_status mla_cache_append(const mla_append_params* p, const void* hidden, const void* w_dkv,
+                            const void* w_kr, void* latent, void* rope, int32_t* seqlens,
+                            int32_t* block_table, const int32_t* free_pages, int32_t n_free,
+                            int32_t* pages_used, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  AppendPlan plan;
+  mla_status st = make_append_plan(p, &plan);
+  if (st != MLA_OK) return st;
+  st = check_append_call(p, plan, hidden, w_dkv, w_kr, latent, rope, seqlens, block_table,
+                         free_pages, n_free, pages_used, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  AppendArgs a;
+  a.hidden = hidden;
+  a.w_dkv = w_dkv;
+  a.w_kr = w_kr;
+  a.latent = latent;
+  a.rope = rope;
+  a.seqlens = seqlens;
+  a.block_table = block_table;
+  a.free_pages = free_pages;
+  a.n_free = n_free;
+  a.lat_tok = p->latent_stride_tok;
+  a.lat_seq = p->latent_stride_seq;
+  a.rope_tok = p->rope_stride_tok;
+  a.rope_seq = p->rope_stride_seq;
+  a.bt_stride = p->block_table_stride;
+  a.rope_theta = p->rope_theta;
+  char* ws = static_cast<char*>(workspace);
+  a.ws.part = reinterpret_cast<float*>(ws + plan.off_part);
+  a.ws.rank = reinterpret_cast<int32_t*>(ws + plan.off_rank);
+  a.ws.pages_used = pages_used;
+  return to_status(launch_append(plan, a, stream));
 }
 
 const char* mla_status_str(int32_t status) { return status_str(status); }

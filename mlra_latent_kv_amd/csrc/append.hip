@@ -1,0 +1,204 @@
+// Write side of the latent cache: one decode step's new token per sequence, compressed and
+// appended ("超越 GQA 的推理革命…MLA…", section 鍵值聯合低秩壓縮: at write time the token is
+// compressed into the joint low-rank latent c_KV; section 解耦旋轉位置編碼: the position part
+// is a separate uncompressed key that carries RoPE).  For every sequence b, with t = seqlens[b]:
+//   row = [ h_b W_DKV | RoPE(h_b W_KR, t) ]      (bf16 storage, fp32 accumulation)
+// goes to cache position t (a paged cache takes a new page from the free list when t starts
+// one), and seqlens[b] becomes t + 1.
+//
+// Two launches:
+//  * k_append_proj: the projection [h] . [W_DKV | W_KR] as a split-K MFMA GEMM.  The weights
+//    are the bytes that matter (d_model x 576 bf16, 4.7 MB at d_model 4096); each workgroup
+//    takes a 256-deep K chunk of 32 batch rows x 128 output columns, stages its W block in
+//    LDS (read back transposed as the MFMA operand) and writes an fp32 partial.  One extra
+//    workgroup ranks the sequences that need a new page (an exclusive scan in batch order).
+//  * k_append_write: one wave per sequence sums the K-chunk partials of its row, rotates the
+//    rotary part at position t (angle reduced in fp64), rounds to bf16, takes its page and
+//    writes the row, then bumps its length.  Each sequence touches only its own block-table
+//    entry and length, so the launch has no races.
+#include <climits>
+
+#include "append.h"
+#include "device_common.h"
+#include "launch.h"
+#include "plan_device.h"
+#include "tile_bf16.h"
+
+namespace mla {
+namespace {
+
+constexpr int kKc = 256;       // K (d_model) per workgroup
+constexpr int kColsWG = 128;   // output columns per workgroup (32 per wave)
+constexpr int kRowsWG = 32;    // batch rows per workgroup
+constexpr int kWPitch = kColsWG + 8;  // LDS pitch of the W block (bf16)
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 8 consecutive rows (k) of one column of a row-major LDS block as an MFMA operand (lane%32 =
+// column, lane/32 = which 8-row half), from two transposed reads
+__device__ __forceinline__ bf16x8 tr8(const bf16* p, int pitch) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * pitch));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__global__ __launch_bounds__(256) void k_append_proj(const bf16* __restrict__ hidden,
+                                                     const bf16* __restrict__ w_dkv,
+                                                     const bf16* __restrict__ w_kr,
+                                                     const int32_t* __restrict__ seqlens,
+                                                     AppendWs ws, int B, int d_model, int dc,
+                                                     int page_size, int n_free) {
+  __shared__ __align__(16) bf16 sW[kKc * kWPitch];  // 68 KB
+  const int cb = blockIdx.x, kc = blockIdx.y, rb = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ncol = dc + 64;
+  if (cb == (int)gridDim.x - 1) {
+    // the extra column of workgroups: (0, 0) ranks the sequences that need a page
+    if (kc == 0 && rb == 0) {
+      int* wsum = reinterpret_cast<int*>(sW);
+      const long long total = plan_detail::block_scan(
+          B,
+          [&](int b, int) {
+            const int t = seqlens[b];
+            return page_size && t >= 0 && t % page_size == 0 ? 1 : 0;
+          },
+          [&](int b, long long off) { ws.rank[b] = (int)off; }, wsum);
+      if (tid == 0) ws.pages_used[0] = (int)(total < n_free ? total : n_free);
+    }
+    return;
+  }
+  const int c0 = cb * kColsWG;           // first output column of the workgroup
+  const int k0 = kc * kKc;
+  const int b0 = rb * kRowsWG;
+  // W block [kKc x 128] row-major into LDS: output column c < dc is W_DKV[:, c], else
+  // W_KR[:, c - dc]; columns past dc + 64 are zeros.  Thread t copies 16-byte chunks
+  // (8 columns of one k row); a chunk never straddles the W_DKV / W_KR border (dc is a
+  // multiple of 128 and 8 | 64).
+#pragma unroll 4
+  for (int i = tid; i < kKc * (kColsWG / 8); i += 256) {
+    const int r = i / (kColsWG / 8), col = (i % (kColsWG / 8)) * 8, c = c0 + col;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (c < dc)
+      v = *(const u32x4*)(w_dkv + (size_t)(k0 + r) * dc + c);
+    else if (c < ncol)
+      v = *(const u32x4*)(w_kr + (size_t)(k0 + r) * 64 + (c - dc));
+    *(u32x4*)(sW + r * kWPitch + col) = v;
+  }
+  // A operand: hidden rows b0 + lane%32 (clamped: rows past B are computed, never stored),
+  // K-step s covers k0 + 16s + 8*(lane/32) .. +8
+  const int bl = lane & 31, kg = lane >> 5;
+  const bf16* hrow = hidden + (size_t)min(b0 + bl, B - 1) * d_model + k0 + 8 * kg;
+  bf16x8 a[kKc / 16];
+#pragma unroll
+  for (int s = 0; s < kKc / 16; ++s) a[s] = *(const bf16x8*)(hrow + 16 * s);
+  __syncthreads();
+  // B operand: wave w's 32 columns; source lane of ds_read_b64_tr_b16: row 8*(lane/32) +
+  // (lane%16)/4, column 16*((lane/16)%2) + 4*(lane%4) of the 32-column block
+  const bf16* tsrc = sW + (8 * (lane >> 5) + ((lane & 15) >> 2)) * kWPitch + 32 * w +
+                     16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < kKc / 16; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], tr8(tsrc + 16 * s * kWPitch, kWPitch),
+                                                  acc, 0, 0, 0);
+  // D[i = batch row][j = column]: lane%32 = column, item i -> row 8*(i/4) + 4*(lane/32) + i%4
+  const int col = c0 + 32 * w + (lane & 31);
+  if (col < ncol) {
+    float* part = ws.part + (size_t)kc * B * ncol;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int b = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
+      if (b < B) part[(size_t)b * ncol + col] = acc[i];
+    }
+  }
+}
+
+// One wave per sequence b.  Lane l owns the row's columns l, l + 64, ...; the rotary pairs
+// (2k, 2k + 1) of the last 64 columns are lanes 2k and 2k + 1 of the last group.
+__global__ __launch_bounds__(64) void k_append_write(
+    AppendWs ws, int32_t* __restrict__ seqlens, int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ free_pages, int n_free, bf16* __restrict__ latent,
+    bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
+    int64_t rope_seq, int64_t bt_stride, int B, int dc, int n_kc, int page_size, int max_pages,
+    int capacity, RopeFreq rf) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int ncol = dc + 64;
+  const int t = seqlens[b];
+  // where the row goes; a position outside the cache's capacity, or a new page that the free
+  // list cannot supply, leaves the sequence untouched
+  int64_t slot_lat = -1, slot_rope = -1;
+  int new_page = -1;
+  if (t >= 0) {
+    if (page_size) {
+      const int j = t / page_size;
+      if (j < max_pages) {
+        int pg = -1;
+        if (t % page_size == 0) {
+          const int r = ws.rank[b];
+          if (r < n_free) pg = new_page = free_pages[r];
+        } else {
+          pg = block_table[(int64_t)b * bt_stride + j];
+        }
+        if (pg >= 0) {
+          slot_lat = (int64_t)pg * lat_seq + (int64_t)(t % page_size) * lat_tok;
+          slot_rope = (int64_t)pg * rope_seq + (int64_t)(t % page_size) * rope_tok;
+        }
+      }
+    } else if (t < capacity) {
+      slot_lat = (int64_t)b * lat_seq + (int64_t)t * lat_tok;
+      slot_rope = (int64_t)b * rope_seq + (int64_t)t * rope_tok;
+    }
+  }
+  if (slot_lat < 0) return;  // uniform: every lane read the same t, rank and table entry
+  // sum of the K-chunk partials for this row
+  const float* part = ws.part + (size_t)b * ncol;
+  const int n_grp = ncol / 64;  // 9 (d_c = 512) or 3 (d_c = 128)
+  float v[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) v[i] = 0.0f;
+  for (int kc = 0; kc < n_kc; ++kc) {
+    const float* p = part + (size_t)kc * B * ncol;
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+      if (i < n_grp) v[i] += p[64 * i + lane];
+  }
+  // latent columns
+#pragma unroll
+  for (int i = 0; i < 9; ++i)
+    if (i < n_grp - 1) latent[slot_lat + 64 * i + lane] = (bf16)v[i];
+  // rotary columns (the last group): pair k = lane / 2 turned by t theta^(-2k/64)
+  float x = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 9; ++i)
+    if (i == n_grp - 1) x = v[i];
+  const float partner = __shfl_xor(x, 1, 64);
+  float cs, sn;
+  rope_cos_sin(t, rf.f[lane >> 1], &cs, &sn);
+  const float x0 = (lane & 1) ? partner : x, x1 = (lane & 1) ? x : partner;
+  const float y = (lane & 1) ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
+  rope[slot_rope + lane] = (bf16)y;
+  if (lane == 0) {
+    if (new_page >= 0) block_table[(int64_t)b * bt_stride + t / page_size] = new_page;
+    seqlens[b] = t + 1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendPlan& p, const AppendArgs& a, hipStream_t s) {
+  const dim3 grid(p.n_cb + 1, p.n_kc, p.n_rb);
+  hipLaunchKernelGGL(k_append_proj, grid, dim3(256), 0, s, (const bf16*)a.hidden,
+                     (const bf16*)a.w_dkv, (const bf16*)a.w_kr, a.seqlens, a.ws, p.B, p.d_model,
+                     p.dc, p.page_size, a.n_free);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  RopeFreq rf;
+  make_rope_freq(64, a.rope_theta, &rf);
+  hipLaunchKernelGGL(k_append_write, dim3(p.B), dim3(64), 0, s, a.ws, a.seqlens, a.block_table,
+                     a.free_pages, a.n_free, (bf16*)a.latent, (bf16*)a.rope, a.lat_tok, a.lat_seq,
+                     a.rope_tok, a.rope_seq, a.bt_stride, p.B, p.dc, p.n_kc, p.page_size,
+                     p.max_pages, p.capacity, rf);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -177,6 +177,66 @@ mla_status check_rope_rotate(const void* x, int64_t row_stride, const int32_t* p
   return MLA_OK;
 }
 
+mla_status make_append_plan(const mla_append_params* p, AppendPlan* plan) {
+  if (!p || !plan) return MLA_ERR_NULL;
+  if (p->dtype != MLA_F32 && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (p->batch < 1 || p->batch > (1 << 20) || p->d_model < 1 || p->d_latent < 1 ||
+      p->d_rope < 2 || p->max_pages_per_seq < 0 || p->capacity < 0 ||
+      !(p->rope_theta > 0.0f) || !std::isfinite(p->rope_theta))
+    return MLA_ERR_SHAPE;
+  if (p->page_size != 0 && p->page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  // bf16, latent 512 (MLA, or MLRA-4's four 128-wide branches side by side) or 128 (one
+  // branch), rotary key 64, d_model a multiple of 256 up to 65536
+  if (p->dtype != MLA_BF16 || (p->d_latent != 512 && p->d_latent != 128) || p->d_rope != 64 ||
+      p->d_model % 256 || p->d_model > 65536)
+    return MLA_ERR_UNSUPPORTED;
+  AppendPlan q{};
+  q.B = p->batch;
+  q.d_model = p->d_model;
+  q.dc = p->d_latent;
+  q.ncol = q.dc + 64;
+  q.page_size = p->page_size;
+  q.max_pages = p->max_pages_per_seq;
+  q.capacity = p->capacity;
+  if (q.page_size ? (q.max_pages < 1 || p->block_table_stride < q.max_pages) : q.capacity < 1)
+    return MLA_ERR_SHAPE;
+  if (p->latent_stride_tok < q.dc || p->rope_stride_tok < 64 || p->latent_stride_seq < 0 ||
+      p->rope_stride_seq < 0)
+    return MLA_ERR_SHAPE;
+  q.n_cb = (int)ceil_div(q.ncol, 128);
+  q.n_kc = q.d_model / 256;
+  q.n_rb = (int)ceil_div(q.B, 32);
+  size_t off = 0;
+  q.off_part = off;
+  off = align_up(off + (size_t)q.n_kc * q.B * q.ncol * 4);
+  q.off_rank = off;
+  off = align_up(off + (size_t)q.B * 4);
+  q.bytes = off;
+  *plan = q;
+  return MLA_OK;
+}
+
+mla_status check_append_call(const mla_append_params* p, const AppendPlan& plan,
+                             const void* hidden, const void* w_dkv, const void* w_kr,
+                             const void* latent, const void* rope, const int32_t* seqlens,
+                             const int32_t* block_table, const int32_t* free_pages,
+                             int32_t n_free, const int32_t* pages_used, const void* workspace,
+                             size_t workspace_bytes) {
+  (void)p;
+  if (!hidden || !w_dkv || !w_kr || !latent || !rope || !seqlens || !pages_used || !workspace)
+    return MLA_ERR_NULL;
+  if (n_free < 0) return MLA_ERR_SHAPE;
+  if (plan.page_size && (!block_table || (n_free > 0 && !free_pages))) return MLA_ERR_NULL;
+  if (workspace_bytes < plan.bytes) return MLA_ERR_WORKSPACE;
+  // hidden rows and weight rows are read 16 bytes at a time
+  if (!aligned(hidden, 16) || !aligned(w_dkv, 16) || !aligned(w_kr, 16) ||
+      !aligned(latent, 2) || !aligned(rope, 2) || !aligned(seqlens, 4) ||
+      !aligned(pages_used, 4) || !aligned(workspace, kWsAlign) ||
+      (plan.page_size && !aligned(block_table, 4)) || (free_pages && !aligned(free_pages, 4)))
+    return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
 const char* status_str(int32_t s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

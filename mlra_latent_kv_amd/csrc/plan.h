@@ -71,6 +71,25 @@ mla_status check_call(const mla_params* p, const Plan& plan, int want_branches,
 mla_status check_rope_rotate(const void* x, int64_t row_stride, const int32_t* pos,
                              int64_t n_rows, int32_t d_rope, float theta, int32_t dtype);
 
+// Cache append (mla_cache_append): launch shape and workspace layout.
+struct AppendPlan {
+  int B, d_model, dc, ncol;   // ncol = dc + 64 output columns per row
+  int page_size, max_pages, capacity;
+  int n_cb, n_kc, n_rb;       // projection grid: column blocks of 128, K chunks of 256, row blocks of 32
+  size_t off_part, off_rank, bytes;
+};
+
+// Validates *p and fills *plan.  Touches no device.
+mla_status make_append_plan(const mla_append_params* p, AppendPlan* plan);
+
+// Per-call checks on top of make_append_plan: pointers, alignment, workspace size.
+mla_status check_append_call(const mla_append_params* p, const AppendPlan& plan,
+                             const void* hidden, const void* w_dkv, const void* w_kr,
+                             const void* latent, const void* rope, const int32_t* seqlens,
+                             const int32_t* block_table, const int32_t* free_pages,
+                             int32_t n_free, const int32_t* pages_used, const void* workspace,
+                             size_t workspace_bytes);
+
 const char* status_str(int32_t s);
 
 }  // namespace mla

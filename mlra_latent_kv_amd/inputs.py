@@ -282,3 +282,16 @@ def make_inputs(
 def cache_bytes(w: Workload, seqlens: np.ndarray) -> int:
     """Algorithmic latent-cache bytes one decode step reads: every cached row once."""
     return int(np.asarray(seqlens, dtype=np.int64).sum()) * w.row * w.elem_bytes
+
+
+# ----------------------------------------------------------------------------- write side
+
+def make_append_inputs(d_model: int, d_latent: int, batch: int, *, seed: int = 2001,
+                       d_rope: int = 64) -> dict:
+    """Seeded new-token hidden states and down-projections for a cache append: hidden
+    [B, d_model], w_dkv [d_model, d_latent], w_kr [d_model, d_rope], each N(0,1)/sqrt(d_model)
+    (fan_in = d_model), rounded to bf16 (uint16 bits)."""
+    r_h, r_d, r_k = (np.random.default_rng(k) for k in np.random.SeedSequence(seed).spawn(3))
+    return dict(hidden=to_storage(_normal(r_h, (batch, d_model), d_model), "bf16"),
+                w_dkv=to_storage(_normal(r_d, (d_model, d_latent), d_model), "bf16"),
+                w_kr=to_storage(_normal(r_k, (d_model, d_rope), d_model), "bf16"))

@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol(lib):
     declared = B.header_functions()
     assert set(declared) == {"mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
                              "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc",
-                             "mla_rope_rotate", "mla_status_str"}
+                             "mla_rope_rotate", "mla_status_str", "mla_append_workspace_size",
+                             "mla_cache_append"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -276,3 +277,61 @@ def test_plan_checker_rejects_wrong_plans():
     for got, want in bad_plans():
         with pytest.raises(AssertionError):
             check_plan(got, want)
+
+
+def append_params(**over):
+    p = B.MlaAppendParams()
+    p.batch, p.d_model, p.d_latent, p.d_rope = 64, 4096, 512, 64
+    p.page_size, p.max_pages_per_seq, p.capacity, p.dtype = 64, 512, 0, B.MLA_BF16
+    p.latent_stride_tok = p.rope_stride_tok = 576
+    p.latent_stride_seq = p.rope_stride_seq = 576 * 64
+    p.block_table_stride = 512
+    p.rope_theta = 10000.0
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_append_params_layout_and_workspace(lib):
+    # 8 int32, 5 int64, 1 float -> 32 + 40 + 4 = 76, padded to 80
+    assert ctypes.sizeof(B.MlaAppendParams) == 80
+    assert B.MlaAppendParams.latent_stride_tok.offset == 32
+    assert B.MlaAppendParams.rope_theta.offset == 72
+    # fp32 partials [d_model / 256][B][d_latent + 64], then the page ranks [B]
+    al = lambda x: (x + 255) // 256 * 256
+    assert B.append_workspace_size(append_params()) == al(16 * 64 * 576 * 4) + al(64 * 4)
+    assert B.append_workspace_size(append_params(d_latent=128, batch=3, d_model=256)) == \
+        al(1 * 3 * 192 * 4) + al(3 * 4)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(batch=0), 2), (dict(d_model=0), 2), (dict(rope_theta=0.0), 2),
+    (dict(dtype=0), 3), (dict(dtype=9), 5), (dict(d_model=1000), 3), (dict(d_latent=256), 3),
+    (dict(d_rope=32), 3), (dict(page_size=16), 3), (dict(max_pages_per_seq=0), 2),
+    (dict(block_table_stride=100), 2), (dict(page_size=0, capacity=0), 2),
+    (dict(latent_stride_tok=500), 2),
+])
+def test_append_invalid_params_rejected(lib, over, status):
+    n = ctypes.c_size_t(0)
+    assert lib.mla_append_workspace_size(ctypes.byref(append_params(**over)), ctypes.byref(n)) == status
+
+
+def test_append_call_checks(lib):
+    def call(p=None, n_free=1, ws_bytes=1 << 40, pages_used=FAKE, workspace=FAKE, **ptr):
+        args = dict(hidden=FAKE, w_dkv=FAKE, w_kr=FAKE, latent=FAKE, rope=FAKE, seqlens=FAKE,
+                    block_table=FAKE, free_pages=FAKE)
+        args.update(ptr)
+        p = p or append_params()
+        return lib.mla_cache_append(ctypes.byref(p), *args.values(), n_free, pages_used,
+                                    workspace, ws_bytes, None)
+    assert call(hidden=None) == 1
+    assert call(block_table=None) == 1
+    assert call(free_pages=None) == 1
+    # an empty free list needs no pointer, nor a contiguous cache a block table: those calls
+    # get past the pointer checks and stop at the (too small) workspace, before any launch
+    assert call(free_pages=None, n_free=0, ws_bytes=10) == 4
+    assert call(p=append_params(page_size=0, capacity=8), block_table=None, ws_bytes=10) == 4
+    assert call(n_free=-1) == 2
+    assert call(ws_bytes=10) == 4
+    assert call(w_dkv=FAKE + 8) == 7 and call(workspace=FAKE + 16) == 7
+    assert call(pages_used=None) == 1
