@@ -185,12 +185,100 @@ def _cpu_model():
     return None
 
 
+APPEND_METRIC = "MLA cache append: us per decode step (new token per sequence, paged)"
+
+
+def bench_append(args, ev, stream):
+    """One decode step's cache write for the paged variable-length batch (64 sequences, the
+    lengths of mla_bf16_paged_b64_h32_l1k-32k), d_model 4096 (32 heads x 128).  Before every
+    step the lengths and block table are restored and the caches flushed (outside the event
+    pair), so every step writes the same rows from cold caches."""
+    import numpy as np
+    import torch
+    from mlra_latent_kv_amd import binding as B
+    from mlra_latent_kv_amd import inputs as I
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    d_model, dc = 4096, w.d_c
+    kids = np.random.SeedSequence(w.seed).spawn(8)
+    lens = I.draw_seqlens(w, w.batch, np.random.default_rng(kids[6]))
+    Bn = len(lens)
+    inp = I.make_append_inputs(d_model, dc, Bn, seed=2001)
+    pages = [-(-int(L) // 64) for L in lens]
+    max_pages = -(-w.seqlen // 64) + 1
+    pool = sum(pages) + Bn + 8
+    perm = np.random.default_rng(7).permutation(pool).astype(np.int32)
+    bt = np.full((Bn, max_pages), -1, np.int32)
+    k = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[k:k + n]
+        k += n
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    cache = torch.zeros((pool, 64, dc + 64), dtype=torch.bfloat16, device="cuda")
+    sl0 = torch.tensor(lens.astype(np.int32), device="cuda")
+    bt0 = torch.tensor(bt, device="cuda")
+    sl, btd = sl0.clone(), bt0.clone()
+    free = torch.tensor(perm[k:], device="cuda")
+    used = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = B.MlaAppendParams()
+    p.batch, p.d_model, p.d_latent, p.d_rope = Bn, d_model, dc, 64
+    p.page_size, p.max_pages_per_seq, p.capacity, p.dtype = 64, max_pages, 0, B.MLA_BF16
+    p.latent_stride_tok = p.rope_stride_tok = dc + 64
+    p.latent_stride_seq = p.rope_stride_seq = 64 * (dc + 64)
+    p.block_table_stride, p.rope_theta = max_pages, 10000.0
+    ws = torch.empty(B.append_workspace_size(p), dtype=torch.uint8, device="cuda")
+    h, wd, wk = dev(inp["hidden"]), dev(inp["w_dkv"]), dev(inp["w_kr"])
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+
+    def step(events=None):
+        sl.copy_(sl0)
+        btd.copy_(bt0)
+        flush.sum()
+        if events is not None:
+            ev.record(events[0], stream)
+        B.mla_cache_append(p, h, wd, wk, cache.data_ptr(), cache.data_ptr() + dc * 2, sl, btd,
+                           free, free.numel(), used, ws, stream=stream)
+        if events is not None:
+            ev.record(events[1], stream)
+
+    for _ in range(args.warmup):
+        step()
+    pairs = [ev.create(2) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(pairs[i])
+    torch.cuda.synchronize()
+    t = [ev.ms(e[0], e[1]) for e in pairs]
+    for e in pairs:
+        ev.destroy(e)
+    us = 1e3 * statistics.mean(t)
+    need = int(sum(1 for L in lens if L % 64 == 0))
+    assert int(used.item()) == need and bool((sl == sl0 + 1).all())
+    nbytes = d_model * (dc + 64) * 2 + Bn * d_model * 2 + Bn * (dc + 64) * 2
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {
+        "metric": APPEND_METRIC, "value": round(us, 3), "unit": "us", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "append_paged_b64_dmodel4096", "batch": Bn, "d_model": d_model,
+                   "d_latent": dc, "d_rope": 64, "pages_taken": need},
+        "us_p10_p50_p90": [round(1e3 * float(np.percentile(t, q)), 3) for q in (10, 50, 90)],
+        "roofline": {"kernel": "k_append_proj + k_append_write", "bound": "hbm",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nbytes,
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--op", choices=["decode", "append"], default="decode",
+                    help="decode: the decode step (the metric); append: one step's cache write")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -218,6 +306,10 @@ def main():
         from mlra_latent_kv_amd import build
         build.build()
     B.load()
+    if args.op == "append":
+        print(json.dumps(bench_append(args, HipEvents(), torch.cuda.current_stream().cuda_stream)),
+              flush=True)
+        return
     w = I.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name}")
     inp = I.make_inputs(w)

@@ -9,13 +9,15 @@
 // Two launches:
 //  * k_append_proj: the projection [h] . [W_DKV | W_KR] as a split-K MFMA GEMM.  The weights
 //    are the bytes that matter (d_model x 576 bf16, 4.7 MB at d_model 4096); each workgroup
-//    takes a 256-deep K chunk of 32 batch rows x 128 output columns, stages its W block in
-//    LDS (read back transposed as the MFMA operand) and writes an fp32 partial.  One extra
-//    workgroup ranks the sequences that need a new page (an exclusive scan in batch order).
-//  * k_append_write: one wave per sequence sums the K-chunk partials of its row, rotates the
-//    rotary part at position t (angle reduced in fp64), rounds to bf16, takes its page and
-//    writes the row, then bumps its length.  Each sequence touches only its own block-table
-//    entry and length, so the launch has no races.
+//    takes a 256-deep K chunk of 128 output columns, stages that W block in LDS once (all of
+//    its loads in flight together; read back transposed as the MFMA operand), and writes fp32
+//    partials for every 32-row block of the batch.  One extra workgroup ranks the sequences
+//    that need a new page (an exclusive scan in batch order).
+//  * k_append_write: one workgroup per sequence: its four waves sum a quarter of the K-chunk
+//    partials each (loads of up to four chunks in flight at once), the sums meet in LDS, and
+//    the first wave rotates the rotary part at position t (angle reduced in fp64), rounds to
+//    bf16, takes its page and writes the row, then bumps the length.  Each sequence touches
+//    only its own block-table entry and length, so the launch has no races.
 #include <climits>
 
 #include "append.h"
@@ -49,12 +51,12 @@ __global__ __launch_bounds__(256) void k_append_proj(const bf16* __restrict__ hi
                                                      AppendWs ws, int B, int d_model, int dc,
                                                      int page_size, int n_free) {
   __shared__ __align__(16) bf16 sW[kKc * kWPitch];  // 68 KB
-  const int cb = blockIdx.x, kc = blockIdx.y, rb = blockIdx.z;
+  const int cb = blockIdx.x, kc = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ncol = dc + 64;
   if (cb == (int)gridDim.x - 1) {
     // the extra column of workgroups: (0, 0) ranks the sequences that need a page
-    if (kc == 0 && rb == 0) {
+    if (kc == 0) {
       int* wsum = reinterpret_cast<int*>(sW);
       const long long total = plan_detail::block_scan(
           B,
@@ -69,59 +71,74 @@ __global__ __launch_bounds__(256) void k_append_proj(const bf16* __restrict__ hi
   }
   const int c0 = cb * kColsWG;           // first output column of the workgroup
   const int k0 = kc * kKc;
-  const int b0 = rb * kRowsWG;
   // W block [kKc x 128] row-major into LDS: output column c < dc is W_DKV[:, c], else
   // W_KR[:, c - dc]; columns past dc + 64 are zeros.  Thread t copies 16-byte chunks
-  // (8 columns of one k row); a chunk never straddles the W_DKV / W_KR border (dc is a
-  // multiple of 128 and 8 | 64).
-#pragma unroll 4
-  for (int i = tid; i < kKc * (kColsWG / 8); i += 256) {
-    const int r = i / (kColsWG / 8), col = (i % (kColsWG / 8)) * 8, c = c0 + col;
-    u32x4 v = u32x4{0, 0, 0, 0};
+  // (8 columns of one k row), all 16 of its loads in flight before the first LDS store; a
+  // chunk never straddles the W_DKV / W_KR border (dc is a multiple of 128 and 8 | 64).
+  constexpr int kChunks = kKc * (kColsWG / 8) / 256;  // per thread
+  u32x4 wv[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int i = tid + 256 * j;
+    const int r = i / (kColsWG / 8), c = c0 + (i % (kColsWG / 8)) * 8;
+    wv[j] = u32x4{0, 0, 0, 0};
     if (c < dc)
-      v = *(const u32x4*)(w_dkv + (size_t)(k0 + r) * dc + c);
+      wv[j] = *(const u32x4*)(w_dkv + (size_t)(k0 + r) * dc + c);
     else if (c < ncol)
-      v = *(const u32x4*)(w_kr + (size_t)(k0 + r) * 64 + (c - dc));
-    *(u32x4*)(sW + r * kWPitch + col) = v;
+      wv[j] = *(const u32x4*)(w_kr + (size_t)(k0 + r) * 64 + (c - dc));
   }
   // A operand: hidden rows b0 + lane%32 (clamped: rows past B are computed, never stored),
   // K-step s covers k0 + 16s + 8*(lane/32) .. +8
   const int bl = lane & 31, kg = lane >> 5;
-  const bf16* hrow = hidden + (size_t)min(b0 + bl, B - 1) * d_model + k0 + 8 * kg;
   bf16x8 a[kKc / 16];
+  auto load_a = [&](int b0) {
+    const bf16* hrow = hidden + (size_t)min(b0 + bl, B - 1) * d_model + k0 + 8 * kg;
 #pragma unroll
-  for (int s = 0; s < kKc / 16; ++s) a[s] = *(const bf16x8*)(hrow + 16 * s);
+    for (int s = 0; s < kKc / 16; ++s) a[s] = *(const bf16x8*)(hrow + 16 * s);
+  };
+  load_a(0);
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int i = tid + 256 * j;
+    *(u32x4*)(sW + (i / (kColsWG / 8)) * kWPitch + (i % (kColsWG / 8)) * 8) = wv[j];
+  }
   __syncthreads();
   // B operand: wave w's 32 columns; source lane of ds_read_b64_tr_b16: row 8*(lane/32) +
   // (lane%16)/4, column 16*((lane/16)%2) + 4*(lane%4) of the 32-column block
   const bf16* tsrc = sW + (8 * (lane >> 5) + ((lane & 15) >> 2)) * kWPitch + 32 * w +
                      16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  f32x16 acc = {};
-#pragma unroll
-  for (int s = 0; s < kKc / 16; ++s)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], tr8(tsrc + 16 * s * kWPitch, kWPitch),
-                                                  acc, 0, 0, 0);
-  // D[i = batch row][j = column]: lane%32 = column, item i -> row 8*(i/4) + 4*(lane/32) + i%4
   const int col = c0 + 32 * w + (lane & 31);
-  if (col < ncol) {
-    float* part = ws.part + (size_t)kc * B * ncol;
+  float* part = ws.part + (size_t)kc * B * ncol;
+  for (int b0 = 0; b0 < B; b0 += kRowsWG) {
+    if (b0 > 0) load_a(b0);
+    f32x16 acc = {};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int b = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
-      if (b < B) part[(size_t)b * ncol + col] = acc[i];
+    for (int s = 0; s < kKc / 16; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], tr8(tsrc + 16 * s * kWPitch, kWPitch),
+                                                    acc, 0, 0, 0);
+    // D[i = batch row][j = column]: lane%32 = column, item i -> row 8*(i/4) + 4*kg + i%4
+    if (col < ncol) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
+        if (b < B) part[(size_t)b * ncol + col] = acc[i];
+      }
     }
   }
 }
 
-// One wave per sequence b.  Lane l owns the row's columns l, l + 64, ...; the rotary pairs
-// (2k, 2k + 1) of the last 64 columns are lanes 2k and 2k + 1 of the last group.
-__global__ __launch_bounds__(64) void k_append_write(
+// One workgroup (4 waves) per sequence b.  Lane l of every wave owns the row's columns l,
+// l + 64, ...; wave w sums the K-chunk partials kc = w, w + 4, ..., and the first wave adds
+// the four sums.  The rotary pairs (2k, 2k + 1) of the last 64 columns are lanes 2k and 2k + 1
+// of the last group.
+__global__ __launch_bounds__(256) void k_append_write(
     AppendWs ws, int32_t* __restrict__ seqlens, int32_t* __restrict__ block_table,
     const int32_t* __restrict__ free_pages, int n_free, bf16* __restrict__ latent,
     bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, int64_t bt_stride, int B, int dc, int n_kc, int page_size, int max_pages,
     int capacity, RopeFreq rf) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+  __shared__ float red[3][9][64];
+  const int b = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ncol = dc + 64;
   const int t = seqlens[b];
   // where the row goes; a position outside the cache's capacity, or a new page that the free
@@ -150,18 +167,36 @@ __global__ __launch_bounds__(64) void k_append_write(
     }
   }
   if (slot_lat < 0) return;  // uniform: every lane read the same t, rank and table entry
-  // sum of the K-chunk partials for this row
+  // sum of the K-chunk partials for this row: wave w takes chunks w, w + 4, ..., four at a
+  // time with all their loads in flight (a chunk past n_kc reads chunk w, weighted 0)
   const float* part = ws.part + (size_t)b * ncol;
   const int n_grp = ncol / 64;  // 9 (d_c = 512) or 3 (d_c = 128)
   float v[9];
 #pragma unroll
   for (int i = 0; i < 9; ++i) v[i] = 0.0f;
-  for (int kc = 0; kc < n_kc; ++kc) {
-    const float* p = part + (size_t)kc * B * ncol;
+  for (int kc0 = w; kc0 < n_kc; kc0 += 16) {
+    float x[4][9];
 #pragma unroll
-    for (int i = 0; i < 9; ++i)
-      if (i < n_grp) v[i] += p[64 * i + lane];
+    for (int u = 0; u < 4; ++u) {
+      const int kc = kc0 + 4 * u < n_kc ? kc0 + 4 * u : w;
+      const float* p = part + (size_t)kc * B * ncol;
+#pragma unroll
+      for (int i = 0; i < 9; ++i) x[u][i] = i < n_grp ? p[64 * i + lane] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 9; ++i)
+        if (kc0 + 4 * u < n_kc) v[i] += x[u][i];
   }
+  if (w > 0) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) red[w - 1][i][lane] = v[i];
+  }
+  __syncthreads();
+  if (w > 0) return;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) v[i] += red[0][i][lane] + red[1][i][lane] + red[2][i][lane];
   // latent columns
 #pragma unroll
   for (int i = 0; i < 9; ++i)
@@ -186,7 +221,7 @@ __global__ __launch_bounds__(64) void k_append_write(
 }  // namespace
 
 hipError_t launch_append(const AppendPlan& p, const AppendArgs& a, hipStream_t s) {
-  const dim3 grid(p.n_cb + 1, p.n_kc, p.n_rb);
+  const dim3 grid(p.n_cb + 1, p.n_kc);
   hipLaunchKernelGGL(k_append_proj, grid, dim3(256), 0, s, (const bf16*)a.hidden,
                      (const bf16*)a.w_dkv, (const bf16*)a.w_kr, a.seqlens, a.ws, p.B, p.d_model,
                      p.dc, p.page_size, a.n_free);
@@ -194,7 +229,7 @@ hipError_t launch_append(const AppendPlan& p, const AppendArgs& a, hipStream_t s
   if (e != hipSuccess) return e;
   RopeFreq rf;
   make_rope_freq(64, a.rope_theta, &rf);
-  hipLaunchKernelGGL(k_append_write, dim3(p.B), dim3(64), 0, s, a.ws, a.seqlens, a.block_table,
+  hipLaunchKernelGGL(k_append_write, dim3(p.B), dim3(256), 0, s, a.ws, a.seqlens, a.block_table,
                      a.free_pages, a.n_free, (bf16*)a.latent, (bf16*)a.rope, a.lat_tok, a.lat_seq,
                      a.rope_tok, a.rope_seq, a.bt_stride, p.B, p.dc, p.n_kc, p.page_size,
                      p.max_pages, p.capacity, rf);
