@@ -37,7 +37,20 @@ position part is a separate uncompressed key that carries RoPE (same page,
 section "解耦旋轉位置編碼"); MLRA's branches are column blocks of the same
 projection ("[ICLR 2025] MLRA…", section 2.1), so the row is computed alike.
 
+Variants of the decode step (``attend_unabsorbed`` / ``mla_decode`` keywords):
+* gated output ("[ICLR 2025] MLRA…", section 4: MLRA-4 combined with gated attention):
+  each head's output, after the scaled branch sum, is multiplied elementwise by
+  sigmoid(gate), the gate logits [B, H, d_v] being an input;
+* folded query ("超越 GQA 的推理革命…MLA…", section "矩陣吸收": the key up-projection is
+  absorbed into the query's projection): the query arrives as a latent-space vector per
+  branch, scored directly against c_KV;
+* latent output (same section, the value side): W_UV is left to the output projection it
+  can be folded into, and the step returns out_scale times the per-branch attention
+  outputs in latent space, side by side.
+
 Readings where the pages are silent (each is an argument, not hidden):
+  the gate is a logistic sigmoid of given logits, applied after out_scale and the branch
+  sum, one value per output element; a gate and a latent output are not combined;
   the cache stores the rotary key already rotated at its own position t;
   a decode step appends its token at t = L_b, then L_b becomes t + 1;
   a sequence whose new token starts a page takes the next entry of a free-page
@@ -121,21 +134,50 @@ def softmax(s: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def sigmoid(x) -> np.ndarray:
+    """Logistic function 1 / (1 + e^-x), fp64, written so that neither branch overflows."""
+    x = _as_f64(x)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
 def attend_unabsorbed(q_nope, q_rope, rows, w_uk, w_uv, *, d_rope: int, scale: float,
                       out_scale: float, theta: float, heads: Optional[Iterable[int]] = None,
-                      return_probs: bool = False):
+                      return_probs: bool = False, gate=None, q_latent=None,
+                      latent_out: bool = False, branches: Optional[int] = None,
+                      d_cb: Optional[int] = None):
     """One sequence, un-absorbed.
 
     q_nope [H, NB, d_nope], q_rope [H, d_rope] (raw), rows [L, NB*d_cb + d_rope] (rope raw),
     w_uk [NB, H, d_nope, d_cb], w_uv [NB, H, d_cb, d_v].  Returns out [len(heads), d_v]
     (and probabilities [len(heads), NB, L] if ``return_probs``).
+
+    Variants (the MLRA page's gated attention, section 4; the yololab page's folding of the
+    up-projections into the neighbouring projections, section "矩陣吸收"):
+      gate [H, d_v]: the head's output is multiplied elementwise by sigmoid(gate) after the
+        branch sum (gate logits are an input; the projection that makes them is the model's);
+      q_latent [H, NB*d_cb]: the query arrives already in latent space, W_UK having been folded
+        into the query projection offline, so the content score is q_latent_b . c_b and w_uk
+        is not used (may be None);
+      latent_out: W_UV is left to a folded output projection, so the result is the attention
+        output in latent space, out_scale * [o_0 | ... | o_{NB-1}] with o_b = sum_t p_bt c_bt,
+        [len(heads), NB*d_cb]; w_uv is not used (may be None).  Not combined with a gate (the
+        gate acts on the up-projected d_v vector).
+    ``branches`` / ``d_cb`` give NB and d_cb when neither weight is passed.
     """
-    q_nope, q_rope, rows = _as_f64(q_nope), _as_f64(q_rope), _as_f64(rows)
-    NB, H, d_nope, d_cb = w_uk.shape
-    d_v = w_uv.shape[-1]
+    q_rope, rows = _as_f64(q_rope), _as_f64(rows)
+    if w_uk is not None:
+        NB, H, d_nope, d_cb = w_uk.shape
+    elif w_uv is not None:
+        NB, H, d_cb = w_uv.shape[:3]
+    else:
+        NB, H = int(branches), q_rope.shape[0]
+    if latent_out and gate is not None:
+        raise ValueError("a gate acts on the up-projected output; latent_out has none")
+    d_out = NB * d_cb if latent_out else w_uv.shape[-1]
     heads = list(range(H)) if heads is None else list(heads)
     L = rows.shape[0]
-    out = np.zeros((len(heads), d_v), dtype=F64)
+    out = np.zeros((len(heads), d_out), dtype=F64)
     probs = np.zeros((len(heads), NB, L), dtype=F64)
     if L == 0:
         return (out, probs) if return_probs else out
@@ -144,16 +186,24 @@ def attend_unabsorbed(q_nope, q_rope, rows, w_uk, w_uv, *, d_rope: int, scale: f
     for j, h in enumerate(heads):
         q_rot = rope(q_rope[h], L - 1, theta)                                   # query at L - 1
         rope_score = k_rot @ q_rot
-        acc = np.zeros(d_v, dtype=F64)
+        acc = np.zeros(d_out, dtype=F64)
         for br in range(NB):
             c = lat[:, br * d_cb:(br + 1) * d_cb]                               # [L, d_cb]
-            K = c @ _as_f64(w_uk[br, h]).T                                      # [L, d_nope] up-projected keys
-            V = c @ _as_f64(w_uv[br, h])                                        # [L, d_v] up-projected values
-            s = scale * (K @ q_nope[h, br] + rope_score)
-            p = softmax(s)
+            if q_latent is None:
+                K = c @ _as_f64(w_uk[br, h]).T                                  # [L, d_nope] up-projected keys
+                content = K @ _as_f64(q_nope)[h, br]
+            else:
+                content = c @ _as_f64(q_latent)[h, br * d_cb:(br + 1) * d_cb]   # folded query
+            p = softmax(scale * (content + rope_score))
             probs[j, br] = p
-            acc += p @ V
+            if latent_out:
+                acc[br * d_cb:(br + 1) * d_cb] = p @ c                          # latent-space output
+            else:
+                V = c @ _as_f64(w_uv[br, h])                                    # [L, d_v] up-projected values
+                acc += p @ V
         out[j] = out_scale * acc
+        if gate is not None:
+            out[j] *= sigmoid(_as_f64(gate)[h])
     return (out, probs) if return_probs else out
 
 
@@ -192,26 +242,48 @@ def mla_decode(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, d_rope: int, scale
                out_scale: float = 1.0, theta: float = 10000.0, page_size: int = 0,
                block_table=None, to_f64: Callable = _as_f64,
                batches: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None,
-               absorbed: bool = False) -> np.ndarray:
+               absorbed: bool = False, gate=None, q_latent: bool = False,
+               latent_out: bool = False, branches: Optional[int] = None,
+               d_cb: Optional[int] = None) -> np.ndarray:
     """Decode step for a batch: out [len(batches), len(heads), d_v] in fp64.
 
     ``to_f64`` decodes stored cache rows (fp32 or bf16 bits) to float64; it is
     applied to one sequence's rows at a time.  ``batches`` / ``heads`` select
     a sample of outputs (each output is computed on its own, so a sample costs
-    only its share).
+    only its share).  ``gate`` [B, H, d_v], ``q_latent`` (then ``q_nope`` holds the folded
+    latent query [B, H, NB*d_cb] and ``w_uk`` may be None) and ``latent_out`` (then ``w_uv`` may
+    be None and the output is [.., .., NB*d_cb]) select the variants of ``attend_unabsorbed``.
     """
-    w_uk, w_uv = to_f64(w_uk), to_f64(w_uv)
+    w_uk = None if w_uk is None else to_f64(w_uk)
+    w_uv = None if w_uv is None else to_f64(w_uv)
     qn, qr = to_f64(q_nope), to_f64(q_rope)
+    g = None if gate is None else to_f64(gate)
     B, H = qn.shape[0], qn.shape[1]
     batches = list(range(B)) if batches is None else list(batches)
     heads = list(range(H)) if heads is None else list(heads)
-    f = attend_absorbed if absorbed else attend_unabsorbed
-    out = np.zeros((len(batches), len(heads), w_uv.shape[-1]), dtype=F64)
+    variant = g is not None or q_latent or latent_out
+    if absorbed and variant:
+        raise ValueError("the absorbed cross-check covers the plain decode only")
+    if w_uk is not None:
+        nb, dcb = w_uk.shape[0], w_uk.shape[3]
+    elif w_uv is not None:
+        nb, dcb = w_uv.shape[0], w_uv.shape[2]
+    else:
+        nb, dcb = int(branches), int(d_cb)
+    d_out = nb * dcb if latent_out else w_uv.shape[-1]
+    out = np.zeros((len(batches), len(heads), d_out), dtype=F64)
     for i, b in enumerate(batches):
         L = int(seqlens[b])
         rows = sequence_rows(cache, b, L, page_size, block_table, to_f64)
-        out[i] = f(qn[b], qr[b], rows, w_uk, w_uv, d_rope=d_rope, scale=scale,
-                   out_scale=out_scale, theta=theta, heads=heads)
+        if absorbed:
+            out[i] = attend_absorbed(qn[b], qr[b], rows, w_uk, w_uv, d_rope=d_rope, scale=scale,
+                                     out_scale=out_scale, theta=theta, heads=heads)
+        else:
+            out[i] = attend_unabsorbed(
+                None if q_latent else qn[b], qr[b], rows, w_uk, w_uv, d_rope=d_rope,
+                scale=scale, out_scale=out_scale, theta=theta, heads=heads,
+                gate=None if g is None else g[b], q_latent=qn[b] if q_latent else None,
+                latent_out=latent_out, branches=nb, d_cb=dcb)
     return out
 
 

@@ -629,3 +629,215 @@ def test_append_planted_mistake_is_caught(monkeypatch, mistake):
             return res
         monkeypatch.setattr(O, "cache_append", bad)
     assert not _append_pins_pass()
+
+
+# ----------------------------------------------------------------------------- variant pins
+# Gated output (the MLRA page, section 4: gated attention on MLRA-4) and the folded forms of
+# matrix absorption (the yololab page, section 矩陣吸收: W_UK folded into the query's
+# projection; W_UV left to the output projection, so the step returns latent-space output).
+
+def test_sigmoid_closed_forms_and_library():
+    from scipy.special import expit
+    assert O.sigmoid(0.0) == 0.5
+    assert abs(O.sigmoid(math.log(3.0)) - 0.75) < 1e-16
+    assert abs(O.sigmoid(-math.log(3.0)) - 0.25) < 1e-16
+    x = np.concatenate([np.linspace(-40, 40, 801), [-800.0, 800.0, -1e-300, 1e-300]])
+    with np.errstate(over="raise"):
+        got = O.sigmoid(x)
+    assert np.allclose(got, expit(x), rtol=1e-15, atol=0)
+    assert np.allclose(O.sigmoid(x) + O.sigmoid(-x), 1.0, rtol=0, atol=4.5e-16)  # two ulps of 1
+
+
+def test_hand_example_gated_mlra4():
+    """The scaled branch sum 163/120 (four width-1 branches) times sigmoid(ln 3) = 3/4, and
+    gate 0 halves it: 163/160 and 163/240."""
+    scale = 0.25
+    r = [1.0, 2.0, 3.0, 4.0]
+    qn = np.array([[[math.log(x) / scale] for x in r]])
+    qr = np.zeros((1, 2))
+    rows = np.array([[1.0, 1.0, 1.0, 1.0, 0.0, 0.0], [0.0] * 6])
+    one = np.ones((4, 1, 1, 1))
+    kw = dict(d_rope=2, scale=scale, out_scale=0.5, theta=10000.0)
+    g3 = O.attend_unabsorbed(qn, qr, rows, one, one, gate=np.array([[math.log(3.0)]]), **kw)
+    g0 = O.attend_unabsorbed(qn, qr, rows, one, one, gate=np.zeros((1, 1)), **kw)
+    assert abs(g3[0, 0] - float(Fraction(163, 160))) < 1e-15
+    assert abs(g0[0, 0] - float(Fraction(163, 240))) < 1e-15
+
+
+def _brute_gated(qn, qr, rows, w_uk, w_uv, gate, d_rope, scale, out_scale, theta):
+    """brute_force's output times 1 / (1 + e^-g), elementwise, in scalar Python."""
+    out = brute_force(qn, qr, rows, w_uk, w_uv, d_rope, scale, out_scale, theta)
+    return np.array([[o / (1.0 + math.exp(-float(g))) for o, g in zip(orow, grow)]
+                     for orow, grow in zip(out, gate)])
+
+
+@pytest.mark.parametrize("NB", [1, 4])
+def test_gate_brute_force(NB):
+    rng = np.random.default_rng(31 + NB)
+    H, dn, dcb, dr, dv, L = 3, 4, 5, 4, 6, 11
+    qn, qr = rng.standard_normal((H, NB, dn)), rng.standard_normal((H, dr))
+    rows = rng.standard_normal((L, NB * dcb + dr))
+    w_uk = rng.standard_normal((NB, H, dn, dcb))
+    w_uv = rng.standard_normal((NB, H, dcb, dv))
+    gate = 3.0 * rng.standard_normal((H, dv))
+    kw = dict(d_rope=dr, scale=0.3, out_scale=0.5 if NB == 4 else 1.0, theta=10000.0)
+    got = O.attend_unabsorbed(qn, qr, rows, w_uk, w_uv, gate=gate, **kw)
+    ref = _brute_gated(qn, qr, rows, w_uk, w_uv, gate, dr, 0.3, kw["out_scale"], 1e4)
+    assert rel_l2(got, ref) < 1e-12
+
+
+def test_gate_limits():
+    """A gate of +40 leaves the output (to 1 part in 1e17), -40 removes it."""
+    w, qn, qr, rows, wk, wv = _mlra_small()
+    kw = dict(d_rope=64, scale=w.softmax_scale, out_scale=0.5, theta=1e4, heads=[3, 17])
+    plain = O.attend_unabsorbed(qn, qr, rows, wk, wv, **kw)
+    up = O.attend_unabsorbed(qn, qr, rows, wk, wv, gate=np.full((32, 128), 40.0), **kw)
+    down = O.attend_unabsorbed(qn, qr, rows, wk, wv, gate=np.full((32, 128), -40.0), **kw)
+    assert rel_l2(up, plain) < 1e-15
+    assert np.abs(down).max() < 1e-17 * np.abs(plain).max() + 1e-300
+
+
+def _fold_query_py(qn, w_uk):
+    """q_lat[h, b*dcb + j] = sum_n q_nope[h, b, n] W_UK[b, h, n, j], as scalar sums."""
+    NB, H, dn, dcb = w_uk.shape
+    return np.array([[math.fsum(float(qn[h, b, n]) * float(w_uk[b, h, n, j]) for n in range(dn))
+                      for b in range(NB) for j in range(dcb)] for h in range(H)])
+
+
+@pytest.mark.parametrize("NB", [1, 4])
+def test_folded_query_equals_unabsorbed(NB):
+    """Folding W_UK into the query projection (q_lat = W_UK^T q_nope, here made by scalar
+    sums) and scoring q_lat . c gives the same step as the explicitly up-projected keys."""
+    rng = np.random.default_rng(41 + NB)
+    H, dn, dcb, dr, dv, L = 3, 6, 5, 4, 7, 13
+    qn, qr = rng.standard_normal((H, NB, dn)), rng.standard_normal((H, dr))
+    rows = rng.standard_normal((L, NB * dcb + dr))
+    w_uk = rng.standard_normal((NB, H, dn, dcb))
+    w_uv = rng.standard_normal((NB, H, dcb, dv))
+    kw = dict(d_rope=dr, scale=0.3, out_scale=0.5 if NB == 4 else 1.0, theta=10000.0)
+    ref = brute_force(qn, qr, rows, w_uk, w_uv, dr, 0.3, kw["out_scale"], 1e4)
+    got = O.attend_unabsorbed(None, qr, rows, None, w_uv, q_latent=_fold_query_py(qn, w_uk), **kw)
+    assert rel_l2(got, ref) < 1e-12
+
+
+def test_latent_output_single_token_and_uniform():
+    """L = 1 returns out_scale times the token's latent; with zero queries every token weighs
+    1/L and the output is out_scale times the latent mean (per branch slice)."""
+    rng = np.random.default_rng(5)
+    NB, H, dn, dcb, dr, L = 4, 2, 3, 5, 4, 9
+    rows = rng.standard_normal((L, NB * dcb + dr))
+    qn, qr = rng.standard_normal((H, NB, dn)), rng.standard_normal((H, dr))
+    w_uk = rng.standard_normal((NB, H, dn, dcb))
+    kw = dict(d_rope=dr, scale=0.7, out_scale=0.5, theta=1e4, latent_out=True, w_uv=None)
+    one = O.attend_unabsorbed(qn, qr, rows[:1], w_uk, **kw)
+    assert np.array_equal(one, np.tile(0.5 * rows[0, :NB * dcb], (H, 1)))
+    uni = O.attend_unabsorbed(np.zeros_like(qn), np.zeros_like(qr), rows, w_uk, **kw)
+    mean = np.array([math.fsum(rows[t, j] for t in range(L)) / L for j in range(NB * dcb)])
+    assert np.allclose(uni, np.tile(0.5 * mean, (H, 1)), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("NB", [1, 4])
+def test_latent_output_times_w_uv_equals_unabsorbed(NB):
+    """The latent output contracted with each branch's W_UV (scalar sums) and added over the
+    branches is the plain step's output."""
+    rng = np.random.default_rng(51 + NB)
+    H, dn, dcb, dr, dv, L = 2, 4, 6, 2, 5, 10
+    qn, qr = rng.standard_normal((H, NB, dn)), rng.standard_normal((H, dr))
+    rows = rng.standard_normal((L, NB * dcb + dr))
+    w_uk = rng.standard_normal((NB, H, dn, dcb))
+    w_uv = rng.standard_normal((NB, H, dcb, dv))
+    kw = dict(d_rope=dr, scale=0.4, out_scale=0.5 if NB == 4 else 1.0, theta=1e4)
+    lat = O.attend_unabsorbed(qn, qr, rows, w_uk, None, latent_out=True, **kw)
+    proj = np.array([[math.fsum(float(lat[h, b * dcb + j]) * float(w_uv[b, h, j, v])
+                                for b in range(NB) for j in range(dcb)) for v in range(dv)]
+                     for h in range(H)])
+    ref = brute_force(qn, qr, rows, w_uk, w_uv, dr, 0.4, kw["out_scale"], 1e4)
+    assert rel_l2(proj, ref) < 1e-12
+
+
+def test_latent_output_rejects_gate():
+    rng = np.random.default_rng(0)
+    with pytest.raises(ValueError):
+        O.attend_unabsorbed(rng.standard_normal((1, 1, 2)), np.zeros((1, 2)),
+                            rng.standard_normal((3, 6)), rng.standard_normal((1, 1, 2, 4)), None,
+                            d_rope=2, scale=1.0, out_scale=1.0, theta=1e4, latent_out=True,
+                            gate=np.zeros((1, 4)))
+
+
+def test_variant_batch_entry_matches_per_sequence():
+    """mla_decode passes the variants through per sequence (stored bf16 inputs; gate
+    [B, H, d_v], folded query [B, H, NB*d_cb], latent output)."""
+    w = I.WORKLOADS["mlra4_bf16_b32_h32_l8192"]
+    inp = I.make_inputs(w, seed=3, seqlens=[70, 1, 33])
+    f64 = lambda a: I.to_f64(a, "bf16")
+    qn, qr, wk, wv = f64(inp["q_nope"]), f64(inp["q_rope"]), f64(inp["w_uk"]), f64(inp["w_uv"])
+    gate = I.to_storage(np.random.default_rng(2).standard_normal((3, w.heads, w.d_v)), "bf16")
+    qlat = I.to_storage(np.einsum("bhkn,khnj->bhkj", qn, wk).reshape(3, w.heads, 4 * w.d_cb),
+                        "bf16")
+    kw = dict(d_rope=64, scale=w.softmax_scale, out_scale=0.5, theta=1e4, heads=[0, 31],
+              to_f64=f64)
+    args = (inp["cache"], inp["seqlens"])
+    got_g = O.mla_decode(inp["q_nope"], inp["q_rope"], *args, inp["w_uk"], inp["w_uv"],
+                         gate=gate, **kw)
+    got_q = O.mla_decode(qlat, inp["q_rope"], *args, None, inp["w_uv"], q_latent=True, **kw)
+    got_l = O.mla_decode(inp["q_nope"], inp["q_rope"], *args, inp["w_uk"], None,
+                         latent_out=True, **kw)
+    one = dict(d_rope=64, scale=w.softmax_scale, out_scale=0.5, theta=1e4, heads=[0, 31])
+    for b, L in enumerate(inp["seqlens"]):
+        rows = f64(inp["cache"][b, :L])
+        a = O.attend_unabsorbed(qn[b], qr[b], rows, wk, wv, **one)
+        assert rel_l2(got_g[b], a * O.sigmoid(f64(gate)[b, [0, 31]])) < 1e-13
+        aq = O.attend_unabsorbed(None, qr[b], rows, None, wv, q_latent=f64(qlat)[b], **one)
+        assert np.array_equal(got_q[b], aq) and rel_l2(aq, a) < 2e-2
+        lat = O.attend_unabsorbed(qn[b], qr[b], rows, wk, None, latent_out=True, **one)
+        assert np.array_equal(got_l[b], lat)
+
+
+def _variant_pins_pass():
+    checks = [test_hand_example_gated_mlra4, lambda: test_gate_brute_force(4),
+              test_latent_output_single_token_and_uniform,
+              lambda: test_folded_query_equals_unabsorbed(4),
+              lambda: test_latent_output_times_w_uv_equals_unabsorbed(4)]
+    with np.errstate(all="ignore"):
+        for c in checks:
+            try:
+                c()
+            except (AssertionError, ValueError, IndexError):
+                return False
+    return True
+
+
+def test_variant_pins_pass_unplanted():
+    assert _variant_pins_pass()
+
+
+@pytest.mark.parametrize("mistake", ["sigmoid_sign", "gate_before_scale_as_add",
+                                     "folded_query_branch0", "latent_out_branch_sum"])
+def test_variant_planted_mistake_is_caught(monkeypatch, mistake):
+    real = O.attend_unabsorbed
+    if mistake == "sigmoid_sign":
+        real_sig = O.sigmoid
+        monkeypatch.setattr(O, "sigmoid", lambda x: real_sig(-np.asarray(x)))
+    elif mistake == "gate_before_scale_as_add":
+        def bad(*a, gate=None, **kw):
+            out = real(*a, **kw)
+            return out if gate is None else out + O.sigmoid(gate)
+        monkeypatch.setattr(O, "attend_unabsorbed", bad)
+    elif mistake == "folded_query_branch0":
+        def bad(*a, q_latent=None, **kw):
+            if q_latent is not None:
+                d = q_latent.shape[1]
+                nb = kw.get("branches") or (a[4].shape[0] if a[4] is not None else 1)
+                q_latent = np.tile(q_latent[:, : d // nb], (1, nb))
+            return real(*a, q_latent=q_latent, **kw)
+        monkeypatch.setattr(O, "attend_unabsorbed", bad)
+    elif mistake == "latent_out_branch_sum":
+        def bad(*a, latent_out=False, **kw):
+            out = real(*a, latent_out=latent_out, **kw)
+            if latent_out:
+                nb = a[3].shape[0]
+                d = out.shape[1] // nb
+                out = np.tile(out.reshape(out.shape[0], nb, d).sum(1), (1, nb))
+            return out
+        monkeypatch.setattr(O, "attend_unabsorbed", bad)
+    assert not _variant_pins_pass()
