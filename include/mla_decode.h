@@ -65,6 +65,21 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
  * violations in the workspace's error word (costs one extra pass over the block table). */
 #define MLA_FLAG_DEVICE_CHECKS 1
 
+/* mla_params.flags: folded query.  W_UK has been folded offline into the query's own
+ * projection (the yololab MLA page, section 矩陣吸收: the key up-projection is absorbed into
+ * the query projection), so the q_nope argument holds the latent-space query
+ * q_lat [B, H, NB * d_latent] (branch br's part at columns br*d_latent ..), scored directly
+ * against c_KV: s_t = softmax_scale * (q_lat_br . c_{br,t} + q_r . k_t).  w_uk is not read
+ * (may be NULL) and d_nope is not used (any value >= 1). */
+#define MLA_FLAG_QUERY_LATENT 2
+
+/* mla_params.flags: latent output.  W_UV is left to the output projection it can be folded
+ * into (same section: the value up-projection moves past the attention), so out receives
+ * out_scale * [o_0 | .. | o_{NB-1}] [B, H, NB * d_latent], o_br = sum_t softmax(s_br)_t c_{br,t},
+ * the branch outputs side by side in latent space.  w_uv is not read (may be NULL) and d_v is
+ * not used (any value >= 1).  Not available with a gate. */
+#define MLA_FLAG_OUTPUT_LATENT 4
+
 /* Error-word bits (workspace int32 hdr[4], written by every call). */
 #define MLA_DEVERR_SEQLEN 1   /* some seqlens[b] outside [0, max_seqlen]; clamped into it   */
 #define MLA_DEVERR_BLOCK 2    /* some used block_table entry outside [0, num_pages)         */
@@ -83,7 +98,8 @@ typedef struct mla_params {
   int32_t num_splits;         /* 0 = balanced split plan (below); n > 0 = at most n splits
                                  per sequence, each ceil(ceil(max_seqlen/64)/n) pages      */
   int32_t dtype;              /* mla_dtype of q, caches, weights and out                   */
-  int32_t flags;              /* 0, or MLA_FLAG_DEVICE_CHECKS                              */
+  int32_t flags;              /* 0, or MLA_FLAG_DEVICE_CHECKS | MLA_FLAG_QUERY_LATENT |
+                                 MLA_FLAG_OUTPUT_LATENT, in any combination                */
   int32_t num_pages;          /* paged: pages in the pool (bound for the device checks);
                                  0 = not given (block ids are then not checked)            */
   int64_t latent_stride_tok;  /* elements between consecutive tokens of the latent cache   */
@@ -103,10 +119,11 @@ typedef struct mla_params {
  *  - MLA_F32 (generic SIMT path): NB in {1, 4}, NB*d_latent <= 512, d_rope even <= 64,
  *    d_nope <= 256, d_v <= 256, any H >= 1.
  *  - page_size in {0, 64}.
- * Alignment: bf16 latent, rope, q_nope, w_uk and w_uv pointers 16-byte aligned and the
- * cache strides multiples of 8 elements; other pointers aligned to their element size.
- * num_splits is at most 512 and at most ceil(max_seqlen / 64).  flags is 0 or
- * MLA_FLAG_DEVICE_CHECKS; num_pages >= 0.
+ * Alignment: bf16 latent, rope, q_nope, w_uk, w_uv, gate and out pointers 16-byte aligned
+ * and the cache strides multiples of 8 elements; other pointers aligned to their element size.
+ * num_splits is at most 512 and at most ceil(max_seqlen / 64).  flags holds only the
+ * MLA_FLAG_* bits above; num_pages >= 0.  With MLA_FLAG_QUERY_LATENT the d_nope rule does not
+ * apply, with MLA_FLAG_OUTPUT_LATENT the d_v rule does not.
  *
  * Split plan.  The attention over each sequence is split into work items of whole 64-token
  * pages (split-K over the sequence) whose partial results are merged afterwards.  The plan is
@@ -164,7 +181,7 @@ mla_status mla_num_splits(const mla_params* p, int32_t* splits);
  * rotated at its own position t (see mla_rope_rotate).  L = 0 writes zeros.
  *
  * Arguments (device pointers unless noted; element type = p->dtype unless noted):
- *   q_nope      [B, H, NB, d_nope] contiguous
+ *   q_nope      [B, H, NB, d_nope] contiguous ([B, H, NB*d_latent] with MLA_FLAG_QUERY_LATENT)
  *   q_rope      [B, H, d_rope] contiguous, NOT rotated (rotated here at position L-1)
  *   latent      contiguous: element (b, t, j) at latent[b*latent_stride_seq + t*latent_stride_tok + j]
  *               paged: element (b, t, j) at latent[pg*latent_stride_seq + (t%64)*latent_stride_tok + j]
@@ -173,9 +190,9 @@ mla_status mla_num_splits(const mla_params* p, int32_t* splits);
  *               (the usual fused row [c_KV | k_rope] is rope = latent + NB*d_latent)
  *   seqlens     int32 [B], 0 <= seqlens[b] <= max_seqlen
  *   block_table int32 [B, block_table_stride] when page_size = 64, else ignored (may be NULL)
- *   w_uk        [NB, H, d_nope, d_latent]   (K = w_uk[br,h] c)
- *   w_uv        [NB, H, d_latent, d_v]      (V = w_uv[br,h]^T c)
- *   out         [B, H, d_v] contiguous, written
+ *   w_uk        [NB, H, d_nope, d_latent]   (K = w_uk[br,h] c); unused with MLA_FLAG_QUERY_LATENT
+ *   w_uv        [NB, H, d_latent, d_v]      (V = w_uv[br,h]^T c); unused with MLA_FLAG_OUTPUT_LATENT
+ *   out         [B, H, d_v] contiguous, written ([B, H, NB*d_latent] with MLA_FLAG_OUTPUT_LATENT)
  *   workspace   >= mla_workspace_size(p) bytes, 256-byte aligned, contents need no
  *               initialisation and are overwritten
  *   stream      hipStream_t
@@ -200,6 +217,26 @@ mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_ro
                        const void* latent, const void* rope, const int32_t* seqlens,
                        const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Gated output: mla_decode / mlra_decode whose result is multiplied elementwise by
+ * sigmoid(gate), as gated attention does on MLRA-4 ("[ICLR 2025] MLRA…", section 4):
+ *   out[b,h,v] = (out_scale * sum_br W_UV[br,h]^T o_br)[v] * 1 / (1 + exp(-gate[b,h,v]))
+ *   gate  [B, H, d_v] contiguous, element type p->dtype, the gate logits (the projection that
+ *         makes them is the model's); bf16: 16-byte aligned.
+ * Other arguments, layouts and flags as mla_decode (gated) / mlra_decode (mlra_decode_gated).
+ * Returns MLA_ERR_NULL for a NULL gate and MLA_ERR_UNSUPPORTED with MLA_FLAG_OUTPUT_LATENT.
+ */
+mla_status mla_decode_gated(const mla_params* p, const void* q_nope, const void* q_rope,
+                            const void* latent, const void* rope, const int32_t* seqlens,
+                            const int32_t* block_table, const void* w_uk, const void* w_uv,
+                            const void* gate, void* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+mla_status mlra_decode_gated(const mla_params* p, const void* q_nope, const void* q_rope,
+                             const void* latent, const void* rope, const int32_t* seqlens,
+                             const int32_t* block_table, const void* w_uk, const void* w_uv,
+                             const void* gate, void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /*
  * Tracing variants: identical to mla_decode / mlra_decode, and additionally record five

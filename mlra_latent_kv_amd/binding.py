@@ -22,6 +22,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "mla_decode.h")
 MLA_F32, MLA_BF16 = 0, 1
 PAGE_SIZE = 64
 MLA_FLAG_DEVICE_CHECKS = 1
+MLA_FLAG_QUERY_LATENT = 2
+MLA_FLAG_OUTPUT_LATENT = 4
 MLA_DEVERR_SEQLEN, MLA_DEVERR_BLOCK = 1, 2
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_UNSUPPORTED",
           4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_DTYPE", 6: "MLA_ERR_HIP", 7: "MLA_ERR_ALIGN"}
@@ -85,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_timed.argtypes = dec + [c_void_p]
     lib.mlra_decode_timed.argtypes = dec + [c_void_p]
     lib.mla_decode_noalloc.argtypes = [P] + [c_void_p] * 10
+    lib.mla_decode_gated.argtypes = [P] + [c_void_p] * 11 + [c_size_t, c_void_p]
+    lib.mlra_decode_gated.argtypes = [P] + [c_void_p] * 11 + [c_size_t, c_void_p]
     PA = ctypes.POINTER(MlaAppendParams)
     lib.mla_append_workspace_size.argtypes = [PA, ctypes.POINTER(c_size_t)]
     lib.mla_cache_append.argtypes = [PA] + [c_void_p] * 8 + [c_int32, c_void_p, c_void_p,
@@ -95,6 +99,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_status_str.restype = ctypes.c_char_p
     for f in ("mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
               "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc", "mla_rope_rotate",
+              "mla_decode_gated", "mlra_decode_gated",
               "mla_append_workspace_size", "mla_cache_append"):
         getattr(lib, f).restype = c_int32
     _lib = lib
@@ -175,6 +180,33 @@ def mlra_decode(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk
                 workspace, workspace_bytes=None, stream=None, check=True, events=None) -> int:
     return _decode("mlra_decode", params, q_nope, q_rope, latent, rope, seqlens, block_table,
                    w_uk, w_uv, out, workspace, workspace_bytes, stream, check, events)
+
+
+def _decode_gated(fname, params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk,
+                  w_uv, gate, out, workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = getattr(load(), fname)(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(latent),
+                                _ptr(rope), _ptr(seqlens), _ptr(block_table), _ptr(w_uk),
+                                _ptr(w_uv), _ptr(gate), _ptr(out), _ptr(workspace),
+                                workspace_bytes, _stream(stream))
+    if check and st:
+        raise MlaError(st, fname)
+    return st
+
+
+def mla_decode_gated(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv,
+                     gate, out, workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    return _decode_gated("mla_decode_gated", params, q_nope, q_rope, latent, rope, seqlens,
+                         block_table, w_uk, w_uv, gate, out, workspace, workspace_bytes, stream,
+                         check)
+
+
+def mlra_decode_gated(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv,
+                      gate, out, workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    return _decode_gated("mlra_decode_gated", params, q_nope, q_rope, latent, rope, seqlens,
+                         block_table, w_uk, w_uv, gate, out, workspace, workspace_bytes, stream,
+                         check)
 
 
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # MLA_NOALLOC_SCRATCH_BYTES

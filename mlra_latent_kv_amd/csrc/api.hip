@@ -5,8 +5,11 @@
 //                and (one extra workgroup) the split plan: page-aligned work items per sequence
 //   main loop -> per (work item, head group) partial (m, l, O) over the latent cache
 //   combine   -> log-sum-exp merge of the splits into the latent-space output
-//   epilogue  -> out = out_scale * W_UV^T o_lat (summed over MLRA branches)
-// (on the bf16 path combine and epilogue are one kernel)
+//   epilogue  -> out = out_scale * W_UV^T o_lat (summed over MLRA branches), times
+//                sigmoid(gate) for the gated entry points
+// (on the bf16 path combine and epilogue are one kernel).  MLA_FLAG_QUERY_LATENT replaces
+// the prologue's W_UK product by the given latent query; MLA_FLAG_OUTPUT_LATENT writes the
+// merged latent output (times out_scale) instead of the W_UV product.
 // Nothing is allocated, nothing synchronises, no state is kept between calls.
 #include <atomic>
 
@@ -56,14 +59,15 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
                       const void* q_rope, const void* latent, const void* rope,
                       const int32_t* seqlens, const int32_t* block_table, const void* w_uk,
                       const void* w_uv, void* out, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream, void* const* events) {
+                      hipStream_t stream, void* const* events, const void* gate = nullptr,
+                      bool gated = false) {
   // validation against the plan mla_workspace_size describes (sized for kMaxCUs), then the
   // plan for this device's compute units, which needs no more workspace
   Plan plan;
   mla_status st = make_plan(p, &plan);
   if (st != MLA_OK) return st;
   st = check_call(p, plan, want_branches, q_nope, q_rope, latent, rope, seqlens, block_table,
-                  w_uk, w_uv, out, workspace, workspace_bytes);
+                  w_uk, w_uv, out, workspace, workspace_bytes, gated, gate);
   if (st != MLA_OK) return st;
   int n_cu = 0;
   if (device_cu_count(&n_cu) != hipSuccess) return MLA_ERR_HIP;
@@ -80,6 +84,7 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
   a.w_uk = w_uk;
   a.w_uv = w_uv;
   a.out = out;
+  a.gate = gated ? gate : nullptr;
   a.lat_tok = p->latent_stride_tok;
   a.lat_seq = p->latent_stride_seq;
   a.rope_tok = p->rope_stride_tok;
@@ -118,9 +123,10 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
     if (e == hipSuccess) e = launch_combine_epilogue_bf16(plan, a, s);
     if (e == hipSuccess) e = mark(3);
   } else {
+    // latent output: the combine writes out directly and there is no epilogue
     if (e == hipSuccess) e = launch_combine(plan, a, s);
     if (e == hipSuccess) e = mark(3);
-    if (e == hipSuccess) e = launch_epilogue(plan, a, s);
+    if (e == hipSuccess && !plan.latent_out) e = launch_epilogue(plan, a, s);
   }
   if (e == hipSuccess) e = mark(4);
   return to_status(e);
@@ -182,6 +188,24 @@ mla_status mlra_decode(const mla_params* p, const void* q_nope, const void* q_ro
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run_decode(4, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
                     workspace, workspace_bytes, stream, nullptr);
+}
+
+mla_status mla_decode_gated(const mla_params* p, const void* q_nope, const void* q_rope,
+                            const void* latent, const void* rope, const int32_t* seqlens,
+                            const int32_t* block_table, const void* w_uk, const void* w_uv,
+                            const void* gate, void* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return run_decode(1, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                    workspace, workspace_bytes, stream, nullptr, gate, true);
+}
+
+mla_status mlra_decode_gated(const mla_params* p, const void* q_nope, const void* q_rope,
+                             const void* latent, const void* rope, const int32_t* seqlens,
+                             const int32_t* block_table, const void* w_uk, const void* w_uv,
+                             const void* gate, void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return run_decode(4, p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                    workspace, workspace_bytes, stream, nullptr, gate, true);
 }
 
 mla_status mla_decode_timed(const mla_params* p, const void* q_nope, const void* q_rope,

@@ -39,6 +39,9 @@ constexpr int kRows = 32;  // batch rows per workgroup (MFMA M)
 constexpr int kPCols = 128;          // latent columns per workgroup
 constexpr int kPPitch = kPCols + 8;  // LDS pitch of the W_UK block (bf16)
 
+// LQ: folded query (MLA_FLAG_QUERY_LATENT): q_nope holds q_lat [B][H][dc], copied and scaled
+// instead of the W_UK product.
+template <bool LQ>
 __global__ __launch_bounds__(256) void k_prologue_bf16(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
     const int32_t* __restrict__ seqlens, const bf16* __restrict__ w_uk, bf16* __restrict__ qcat,
@@ -81,32 +84,49 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
       L_r[it] = min(max(seqlens[bc], 0), plan.max_seqlen);
     }
   }
-  const bf16* wsrc = w_uk + ((size_t)br * H + h) * dn * dcb + c0;
+  if constexpr (LQ) {
+    // 32 rows x 128 columns of q_lat, 16 per thread as two 16-byte pieces
 #pragma unroll
-  for (int j = 0; j < dn * kPCols / 8 / 256; ++j) {
-    const int c = tid + 256 * j, r = c >> 4, col = (c & 15) * 8;
-    *(u32x4*)(sW + r * kPPitch + col) = *(const u32x4*)(wsrc + (size_t)r * dcb + col);
-  }
-  // A operand: q_nope rows b0 + lane%32, K-step s covers n = 16s + 8*(lane/32) .. +8
-  // rows past B are clamped to B-1: their products are computed but never stored
-  const int bl = lane & 31, kg = lane >> 5;
-  const int b = min(b0 + bl, B - 1);
-  bf16x8 qa[dn / 16];
-  const bf16* qsrc = q_nope + (((size_t)b * H + h) * NB + br) * dn + 8 * kg;
+    for (int k = 0; k < 2; ++k) {
+      const int piece = tid + 256 * k, r = piece >> 4, col = cb * kPCols + 8 * (piece & 15);
+      const int bb = b0 + r;
+      if (bb < B) {
+        const size_t bh = (size_t)bb * H + h;
+        const bf16x8 v = *(const bf16x8*)(q_nope + bh * dc + col);
+        bf16x8 o;
 #pragma unroll
-  for (int s = 0; s < dn / 16; ++s) qa[s] = *(const bf16x8*)(qsrc + 16 * s);
-  __syncthreads();
-  f32x16 acc = {};
-  const bf16* tsrc = sW + tr_src_row(lane) * kPPitch + 32 * w + tr_src_col(lane);
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[e] * qscale);
+        *(bf16x8*)(qcat + bh * row + col) = o;
+      }
+    }
+  } else {
+    const bf16* wsrc = w_uk + ((size_t)br * H + h) * dn * dcb + c0;
 #pragma unroll
-  for (int s = 0; s < dn / 16; ++s)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], tr8(tsrc + 16 * s * kPPitch, kPPitch), acc, 0, 0, 0);
-  // D[i = batch row][j = column]: lane%32 = column, item i -> row 8*(i/4) + 4*(lane/32) + i%4
-  const int col = br * dcb + c0 + 32 * w + (lane & 31);
+    for (int j = 0; j < dn * kPCols / 8 / 256; ++j) {
+      const int c = tid + 256 * j, r = c >> 4, col = (c & 15) * 8;
+      *(u32x4*)(sW + r * kPPitch + col) = *(const u32x4*)(wsrc + (size_t)r * dcb + col);
+    }
+    // A operand: q_nope rows b0 + lane%32, K-step s covers n = 16s + 8*(lane/32) .. +8
+    // rows past B are clamped to B-1: their products are computed but never stored
+    const int bl = lane & 31, kg = lane >> 5;
+    const int b = min(b0 + bl, B - 1);
+    bf16x8 qa[dn / 16];
+    const bf16* qsrc = q_nope + (((size_t)b * H + h) * NB + br) * dn + 8 * kg;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int bb = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
-    if (bb < B) qcat[((size_t)bb * H + h) * row + col] = (bf16)(acc[i] * qscale);
+    for (int s = 0; s < dn / 16; ++s) qa[s] = *(const bf16x8*)(qsrc + 16 * s);
+    __syncthreads();
+    f32x16 acc = {};
+    const bf16* tsrc = sW + tr_src_row(lane) * kPPitch + 32 * w + tr_src_col(lane);
+#pragma unroll
+    for (int s = 0; s < dn / 16; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], tr8(tsrc + 16 * s * kPPitch, kPPitch), acc, 0, 0, 0);
+    // D[i = batch row][j = column]: lane%32 = column, item i -> row 8*(i/4) + 4*(lane/32) + i%4
+    const int col = br * dcb + c0 + 32 * w + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int bb = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
+      if (bb < B) qcat[((size_t)bb * H + h) * row + col] = (bf16)(acc[i] * qscale);
+    }
   }
 #pragma unroll
   for (int it = 0; it < kRotPer; ++it) {
@@ -128,7 +148,8 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
   if (kRows * (p.dr / 2) > 4 * 256 * (int)grid.z) return hipErrorInvalidValue;
   RopeFreq rf;
   make_rope_freq(p.dr, a.rope_theta, &rf);
-  hipLaunchKernelGGL(k_prologue_bf16, grid, dim3(256), 0, s, (const bf16*)a.q_nope,
+  hipLaunchKernelGGL(p.latent_q ? k_prologue_bf16<true> : k_prologue_bf16<false>, grid,
+                     dim3(256), 0, s, (const bf16*)a.q_nope,
                      (const bf16*)a.q_rope, a.seqlens, (const bf16*)a.w_uk, (bf16*)a.qcat, p.B,
                      p.H, p.NB, p.dcb, a.softmax_scale * kLog2e, rf, a.plan);
   return hipGetLastError();
@@ -169,11 +190,16 @@ __device__ __forceinline__ int ce_sw(int r, int c) { return c ^ (4 * (r & 3)); }
 // R = 256 NC / (TPC DC / 8) rows per workgroup; each thread merges NC chunks of one row, with
 // 32 chunk loads in flight.  TPC > 1 (small row blocks, for small batches): TPC adjacent
 // threads share a chunk, each taking every TPC-th split, and add their sums at the end.
-template <int NC, int TPC, int DC>
+//
+// LO (MLA_FLAG_OUTPUT_LATENT): the merged latent rows, times out_scale, are the output
+// [B][H][DC]; no W_UV is read and phase 3 does not run.  gate (gated entry points, else
+// null): the result is multiplied by 1 / (1 + exp(-gate)) elementwise.
+template <int NC, int TPC, int DC, bool LO>
 __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     const bf16* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ split_off, const bf16* __restrict__ w_uv,
-    bf16* __restrict__ out, int B, int H, int NB, int dcb, float out_scale) {
+    const bf16* __restrict__ gate, bf16* __restrict__ out, int B, int H, int NB, int dcb,
+    float out_scale) {
   constexpr int kCPR = DC / 8;                  // 16-byte chunks per latent row
   constexpr int R = 256 * NC / (TPC * kCPR);
   constexpr int kWRows = DC / 4;                // W_UV rows (latent columns) per wave
@@ -281,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
       pl[it] = ml[sidx * ml_s + 1];
     }
     load_batch(0);
-    issue_wuv(0, kWRows / 8);
+    if constexpr (!LO) issue_wuv(0, kWRows / 8);
 #pragma unroll
     for (int it = 0; it < kPre; ++it)
       if (q + it * P >= n) pm[it] = -INFINITY;
@@ -316,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   // partials of the first batch), and the merge below would start only once they had all
   // arrived instead of load by load
   tile::lds_barrier();
-  issue_wuv(kWRows / 8, kWRows / 4);
+  if constexpr (!LO) issue_wuv(kWRows / 8, kWRows / 4);
 
   // ---- 2b. weighted sum of the splits, batch by batch
   {
@@ -355,15 +381,37 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
           acc[i][0][e] += __shfl_xor(acc[i][0][e], o, 64);
           acc[i][1][e] += __shfl_xor(acc[i][1][e], o, 64);
         }
+    if constexpr (LO) {
+      // latent output: the merged chunks, scaled, are the result
 #pragma unroll
-    for (int i = 0; i < NC; ++i)
-      if (z == 0)
-        *(bf16x8*)(sm.olat[mr] + 16 * ((mc + i) ^ (mr & 15))) =
-          bf16x8{(bf16)acc[i][0][0], (bf16)acc[i][0][1], (bf16)acc[i][0][2], (bf16)acc[i][0][3],
-                 (bf16)acc[i][1][0], (bf16)acc[i][1][1], (bf16)acc[i][1][2], (bf16)acc[i][1][3]};
+      for (int i = 0; i < NC; ++i)
+        if (z == 0 && mb < B) {
+          bf16x8 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r[e] = (bf16)(acc[i][0][e] * out_scale);
+            r[4 + e] = (bf16)(acc[i][1][e] * out_scale);
+          }
+          *(bf16x8*)(out + ((size_t)mb * H + h) * DC + 8 * (mc + i)) = r;
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+        if (z == 0)
+          *(bf16x8*)(sm.olat[mr] + 16 * ((mc + i) ^ (mr & 15))) =
+            bf16x8{(bf16)acc[i][0][0], (bf16)acc[i][0][1], (bf16)acc[i][0][2], (bf16)acc[i][0][3],
+                   (bf16)acc[i][1][0], (bf16)acc[i][1][1], (bf16)acc[i][1][2], (bf16)acc[i][1][3]};
+    }
   }
+  if constexpr (LO) return;
   tile::wait_vmcnt<0>();  // this wave's W_UV rows have landed
   __syncthreads();        // every merged latent row is in LDS
+  // the gate logits of this thread's output piece (row tid / 16, columns 8 (tid % 16) ..),
+  // loaded now so that the products below hide their latency
+  const int orow = tid >> 4, ov0 = 8 * (tid & 15);
+  const bool ostore = orow < R && b0 + orow < B;
+  bf16x8 gv = {};
+  if (gate && ostore) gv = *(const bf16x8*)(gate + ((size_t)(b0 + orow) * H + h) * kCeDv + ov0);
 
   // ---- 3. out[row][v] partial over this wave's DC / 4 latent columns.  A operand: lane (row
   // l32, k-half g) holds columns w DC/4 + 16j + 8g..+7 (chunk w DC/32 + 2j + g); rows >= R are
@@ -406,17 +454,19 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     }
   __syncthreads();
   // thread t: row t / 16, columns 8*(t % 16)..+7
-  const int row = tid >> 4, v0 = 8 * (tid & 15);
-  if (row < R && b0 + row < B) {
+  if (ostore) {
     bf16x8 res;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float sum = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) sum += red[(ww * kCeMaxRows + row) * kCeRedPitch + v0 + i];
-      res[i] = (bf16)(sum * out_scale);
+      for (int ww = 0; ww < 4; ++ww) sum += red[(ww * kCeMaxRows + orow) * kCeRedPitch + ov0 + i];
+      sum *= out_scale;
+      // sigmoid(g) = 1 / (1 + 2^(-g log2 e))
+      if (gate) sum *= 1.0f / (1.0f + __builtin_amdgcn_exp2f(-(float)gv[i] * kLog2e));
+      res[i] = (bf16)sum;
     }
-    *(bf16x8*)(out + ((size_t)(b0 + row) * H + h) * kCeDv + v0) = res;
+    *(bf16x8*)(out + ((size_t)(b0 + orow) * H + h) * kCeDv + ov0) = res;
   }
 }
 
@@ -432,21 +482,28 @@ int combine_epilogue_rows(int B, int H, int dc) {
   return r_min;
 }
 
+namespace {
+// <NC, TPC, DC, LO>: R = 256 NC / (TPC DC / 8)
+template <bool LO>
+auto combine_epilogue_kernel(int dc, int R) {
+  return dc == 128 ? (R == 16  ? k_combine_epilogue_bf16<1, 1, 128, LO>
+                      : R == 8 ? k_combine_epilogue_bf16<1, 2, 128, LO>
+                               : k_combine_epilogue_bf16<1, 4, 128, LO>)
+         : R == 16 ? k_combine_epilogue_bf16<4, 1, 512, LO>
+         : R == 8  ? k_combine_epilogue_bf16<2, 1, 512, LO>
+         : R == 4  ? k_combine_epilogue_bf16<1, 1, 512, LO>
+                   : k_combine_epilogue_bf16<1, 2, 512, LO>;
+}
+}  // namespace
+
 hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const int R = combine_epilogue_rows(p.B, p.H, p.dc);
   const unsigned blocks = (unsigned)(p.H * ((p.B + R - 1) / R));
-  // <NC, TPC, DC>: R = 256 NC / (TPC DC / 8)
-  auto kern = p.dc == 128
-                  ? (R == 16 ? k_combine_epilogue_bf16<1, 1, 128>
-                     : R == 8 ? k_combine_epilogue_bf16<1, 2, 128>
-                              : k_combine_epilogue_bf16<1, 4, 128>)
-              : R == 16 ? k_combine_epilogue_bf16<4, 1, 512>
-              : R == 8  ? k_combine_epilogue_bf16<2, 1, 512>
-              : R == 4  ? k_combine_epilogue_bf16<1, 1, 512>
-                        : k_combine_epilogue_bf16<1, 2, 512>;
+  auto kern = p.latent_out ? combine_epilogue_kernel<true>(p.dc, R)
+                           : combine_epilogue_kernel<false>(p.dc, R);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, (const bf16*)a.part_o, a.part_ml,
-                     a.split_off, (const bf16*)a.w_uv, (bf16*)a.out, p.B, p.H, p.NB, p.dcb,
-                     a.out_scale);
+                     a.split_off, (const bf16*)a.w_uv, (const bf16*)a.gate, (bf16*)a.out, p.B,
+                     p.H, p.NB, p.dcb, a.out_scale);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
                                                   const T* __restrict__ w_uk, T* __restrict__ qcat,
                                                   int B, int H, int NB, int dn, int dcb, int dr,
                                                   float qscale, RopeFreq rf, PlanArgs plan,
-                                                  int lds_bytes) {
+                                                  int lds_bytes, int latent_q) {
   extern __shared__ __align__(16) float sq[];  // [kBatchBlock][NB][dn]; the plan block: scratch
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kBatchBlock;
@@ -42,13 +42,21 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
   }
   const int nb = min(kBatchBlock, B - b0);
   const int dc = NB * dcb, row = dc + dr;
+  if (latent_q) {
+    // folded query: q_nope holds q_lat [B][H][dc], W_UK already applied offline
+    for (int i = threadIdx.x; i < nb * dc; i += blockDim.x) {
+      const int j = i / dc, c = i % dc;
+      const size_t bh = (size_t)(b0 + j) * H + h;
+      qcat[bh * row + c] = from_f32<T>(to_f32(q_nope[bh * dc + c]) * qscale);
+    }
+  }
   const int per_b = NB * dn;
-  for (int i = threadIdx.x; i < kBatchBlock * per_b; i += blockDim.x) {
+  for (int i = threadIdx.x; !latent_q && i < kBatchBlock * per_b; i += blockDim.x) {
     const int j = i / per_b, rest = i % per_b;
     sq[i] = j < nb ? to_f32(q_nope[((size_t)(b0 + j) * H + h) * per_b + rest]) : 0.0f;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < dc; c += blockDim.x) {
+  for (int c = threadIdx.x; !latent_q && c < dc; c += blockDim.x) {
     const int br = c / dcb, cc = c % dcb;
     const T* w = w_uk + ((size_t)br * H + h) * dn * dcb + cc;
     const float* q = sq + br * dn;
@@ -80,13 +88,15 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
 
 hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(p.H + 1, (p.B + kBatchBlock - 1) / kBatchBlock);
-  const size_t lds = std::max<size_t>((size_t)kBatchBlock * p.NB * p.dn * sizeof(float), 16384);
+  const size_t lds = std::max<size_t>(
+      p.latent_q ? 0 : (size_t)kBatchBlock * p.NB * p.dn * sizeof(float), 16384);
   const float qscale = a.softmax_scale * kLog2e;
   RopeFreq rf;
   make_rope_freq(p.dr, a.rope_theta, &rf);
   hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, s, (const float*)a.q_nope,
                        (const float*)a.q_rope, a.seqlens, (const float*)a.w_uk, (float*)a.qcat,
-                       p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, rf, a.plan, (int)lds);
+                       p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, rf, a.plan, (int)lds,
+                       p.latent_q);
   return hipGetLastError();
 }
 
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ part_o,
                                                  const float* __restrict__ part_ml,
                                                  const int32_t* __restrict__ split_off,
                                                  TO* __restrict__ olat, int H, int S, int NB,
-                                                 int dcb) {
+                                                 int dcb, float scale) {
   extern __shared__ float sw[];  // [kCombHeads][branches in this column block][S]
   const int hb = blockIdx.x, b = blockIdx.y;
   const int h0 = hb * kCombHeads;
@@ -207,25 +217,29 @@ __global__ __launch_bounds__(256) void k_combine(const TP* __restrict__ part_o,
     }
     TO* dst = olat + ((size_t)b * H + h0 + hl) * dc + d;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = from_f32<TO>(acc[e]);
+    for (int e = 0; e < 4; ++e) dst[e] = from_f32<TO>(acc[e] * scale);
   }
 }
 
-// fp32 path (the bf16 path merges the splits inside launch_combine_epilogue_bf16)
+// fp32 path (the bf16 path merges the splits inside launch_combine_epilogue_bf16).  With a
+// latent output the merged rows, times out_scale, go straight to out.
 hipError_t launch_combine(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((p.H + kCombHeads - 1) / kCombHeads, p.B, (p.dc + kCombCols - 1) / kCombCols);
   const int max_br = kCombCols / p.dcb + 2;
   const size_t lds = (size_t)kCombHeads * std::min(p.NB, max_br) * p.splits * sizeof(float);
   hipLaunchKernelGGL((k_combine<float, float>), grid, dim3(256), lds, s, (const float*)a.part_o,
-                     a.part_ml, a.split_off, (float*)a.olat, p.H, p.splits, p.NB, p.dcb);
+                     a.part_ml, a.split_off, (float*)(p.latent_out ? a.out : a.olat), p.H,
+                     p.splits, p.NB, p.dcb, p.latent_out ? a.out_scale : 1.0f);
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------- epilogue
 // out[b,h,v] = out_scale * sum_br sum_c olat[b,h,br*dcb + c] * W_UV[br,h,c,v]
+//              (times 1 / (1 + exp(-gate[b,h,v])) when a gate is given)
 template <typename T>
 __global__ __launch_bounds__(128) void k_epilogue(const float* __restrict__ olat,
-                                                  const T* __restrict__ w_uv, T* __restrict__ out,
+                                                  const T* __restrict__ w_uv,
+                                                  const T* __restrict__ gate, T* __restrict__ out,
                                                   int B, int H, int NB, int dcb, int dv,
                                                   float out_scale) {
   extern __shared__ float so[];  // [kBatchBlock][dc]
@@ -251,8 +265,11 @@ __global__ __launch_bounds__(128) void k_epilogue(const float* __restrict__ olat
         for (int j = 0; j < kBatchBlock; ++j) acc[j] = fmaf(o[j * dc + c], wv, acc[j]);
       }
     }
-    for (int j = 0; j < nb; ++j)
-      out[((size_t)(b0 + j) * H + h) * dv + v] = from_f32<T>(acc[j] * out_scale);
+    for (int j = 0; j < nb; ++j) {
+      const size_t o = ((size_t)(b0 + j) * H + h) * dv + v;
+      const float g = gate ? 1.0f / (1.0f + expf(-to_f32(gate[o]))) : 1.0f;
+      out[o] = from_f32<T>(acc[j] * out_scale * g);
+    }
   }
 }
 
@@ -260,7 +277,8 @@ hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(p.H, (p.B + kBatchBlock - 1) / kBatchBlock);
   const size_t lds = (size_t)kBatchBlock * p.dc * sizeof(float);
   hipLaunchKernelGGL(k_epilogue<float>, grid, dim3(128), lds, s, (const float*)a.olat,
-                     (const float*)a.w_uv, (float*)a.out, p.B, p.H, p.NB, p.dcb, p.dv, a.out_scale);
+                     (const float*)a.w_uv, (const float*)a.gate, (float*)a.out, p.B, p.H, p.NB,
+                     p.dcb, p.dv, a.out_scale);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ struct DecodeArgs {
   const void* w_uk;
   const void* w_uv;
   void* out;
+  const void* gate;  // [B][H][d_v] gate logits of the gated entry points, else null
   int64_t lat_tok, lat_seq, rope_tok, rope_seq, bt_stride;
   float softmax_scale, out_scale, rope_theta;
   // workspace regions

@@ -24,7 +24,8 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
       p->d_latent < 1 || p->d_rope < 2 || (p->d_rope & 1) || p->max_seqlen < 0 ||
       p->num_splits < 0 || p->num_pages < 0)
     return MLA_ERR_SHAPE;
-  if (p->flags & ~MLA_FLAG_DEVICE_CHECKS) return MLA_ERR_SHAPE;
+  if (p->flags & ~(MLA_FLAG_DEVICE_CHECKS | MLA_FLAG_QUERY_LATENT | MLA_FLAG_OUTPUT_LATENT))
+    return MLA_ERR_SHAPE;
   if (p->batch > (1 << 20) || p->num_heads > 4096 || p->max_seqlen > (1 << 26))
     return MLA_ERR_SHAPE;
   if (!std::isfinite(p->softmax_scale) || !std::isfinite(p->out_scale) ||
@@ -49,6 +50,10 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   q.n_cu = (n_cu <= 0 || n_cu > kMaxCUs) ? kMaxCUs : n_cu;
   q.checks = (p->flags & MLA_FLAG_DEVICE_CHECKS) ? 1 : 0;
   q.num_pages = q.paged ? p->num_pages : 0;
+  q.latent_q = (p->flags & MLA_FLAG_QUERY_LATENT) ? 1 : 0;
+  q.latent_out = (p->flags & MLA_FLAG_OUTPUT_LATENT) ? 1 : 0;
+  // the folded forms leave out the dims of the product they skip
+  const bool dn_ok = q.latent_q || q.dn == 128, dv_ok = q.latent_out || q.dv == 128;
 
   if (p->dtype == MLA_BF16) {
     // MLA (latent 512), MLRA-4 (four branches of 128), and one MLRA branch on its own
@@ -56,13 +61,14 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
     const bool mla = q.NB == 1 && q.dcb == 512;
     const bool shard = q.NB == 1 && q.dcb == 128;
     const bool mlra = q.NB == 4 && q.dcb == 128;
-    if (!(mla || shard || mlra) || q.dr != 64 || q.dn != 128 || q.dv != 128 || q.H % kHeadGroup)
+    if (!(mla || shard || mlra) || q.dr != 64 || !dn_ok || !dv_ok || q.H % kHeadGroup)
       return MLA_ERR_UNSUPPORTED;
     q.path = Path::kBf16Mfma;
     q.n_hg = q.H / kHeadGroup;
     q.wide = mla && q.H % kWideHeads == 0;
   } else {
-    if ((q.NB != 1 && q.NB != 4) || q.dc > 512 || q.dr > 64 || q.dn > 256 || q.dv > 256)
+    if ((q.NB != 1 && q.NB != 4) || q.dc > 512 || q.dr > 64 || (!q.latent_q && q.dn > 256) ||
+        (!q.latent_out && q.dv > 256))
       return MLA_ERR_UNSUPPORTED;
     q.path = Path::kF32Simt;
     q.n_hg = 0;
@@ -144,22 +150,30 @@ mla_status check_call(const mla_params* p, const Plan& plan, int want_branches,
                       const void* q_nope, const void* q_rope, const void* latent,
                       const void* rope, const int32_t* seqlens, const int32_t* block_table,
                       const void* w_uk, const void* w_uv, const void* out,
-                      const void* workspace, size_t workspace_bytes) {
+                      const void* workspace, size_t workspace_bytes, bool gated,
+                      const void* gate) {
   if (plan.NB != want_branches) return MLA_ERR_UNSUPPORTED;
-  if (!q_nope || !q_rope || !latent || !rope || !seqlens || !w_uk || !w_uv || !out || !workspace)
+  if (gated && plan.latent_out) return MLA_ERR_UNSUPPORTED;  // the gate acts on d_v outputs
+  // the folded forms do not read the weight they replace
+  const bool need_uk = !plan.latent_q, need_uv = !plan.latent_out;
+  if (!q_nope || !q_rope || !latent || !rope || !seqlens || (need_uk && !w_uk) ||
+      (need_uv && !w_uv) || !out || !workspace || (gated && !gate))
     return MLA_ERR_NULL;
   if (plan.paged && !block_table) return MLA_ERR_NULL;
   if (workspace_bytes < plan.bytes) return MLA_ERR_WORKSPACE;
   const size_t ea = (size_t)plan.elem;
   if (!aligned(workspace, kWsAlign) || !aligned(seqlens, 4) || (plan.paged && !aligned(block_table, 4)))
     return MLA_ERR_ALIGN;
-  if (!aligned(q_nope, ea) || !aligned(q_rope, ea) || !aligned(w_uk, ea) || !aligned(w_uv, ea) ||
-      !aligned(out, ea))
+  if (!aligned(q_nope, ea) || !aligned(q_rope, ea) || (need_uk && !aligned(w_uk, ea)) ||
+      (need_uv && !aligned(w_uv, ea)) || !aligned(out, ea) || (gated && !aligned(gate, ea)))
     return MLA_ERR_ALIGN;
   const size_t cache_align = plan.dtype == MLA_BF16 ? 16 : 4;
   if (!aligned(latent, cache_align) || !aligned(rope, cache_align)) return MLA_ERR_ALIGN;
-  // the bf16 kernels read the query and both weights with 16-byte vector loads
-  if (plan.dtype == MLA_BF16 && (!aligned(q_nope, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16)))
+  // the bf16 kernels read the query, both weights and the gate, and write the output, with
+  // 16-byte vector accesses
+  if (plan.dtype == MLA_BF16 &&
+      (!aligned(q_nope, 16) || (need_uk && !aligned(w_uk, 16)) || (need_uv && !aligned(w_uv, 16)) ||
+       (gated && !aligned(gate, 16)) || !aligned(out, 16)))
     return MLA_ERR_ALIGN;
   (void)p;
   return MLA_OK;

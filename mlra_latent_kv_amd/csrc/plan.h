@@ -37,6 +37,8 @@ struct Plan {
   int n_cu;      // compute units the plan is made for (1 .. kMaxCUs)
   int checks;    // MLA_FLAG_DEVICE_CHECKS given: a check kernel runs before the prologue
   int num_pages; // pool pages for the block-id check (0: not checked)
+  int latent_q;  // MLA_FLAG_QUERY_LATENT: the query arrives folded (no W_UK product)
+  int latent_out;  // MLA_FLAG_OUTPUT_LATENT: out is the latent-space output (no W_UV)
   // Split plan.  The device cuts the batch into work items of whole pages, one per dispatch
   // slot (see plan_device.h); the host only bounds it.
   int target;        // slots the automatic plan fills (one workgroup set per CU slot)
@@ -66,7 +68,8 @@ mla_status check_call(const mla_params* p, const Plan& plan, int want_branches,
                       const void* q_nope, const void* q_rope, const void* latent,
                       const void* rope, const int32_t* seqlens, const int32_t* block_table,
                       const void* w_uk, const void* w_uv, const void* out,
-                      const void* workspace, size_t workspace_bytes);
+                      const void* workspace, size_t workspace_bytes, bool gated = false,
+                      const void* gate = nullptr);
 
 mla_status check_rope_rotate(const void* x, int64_t row_stride, const int32_t* pos,
                              int64_t n_rows, int32_t d_rope, float theta, int32_t dtype);

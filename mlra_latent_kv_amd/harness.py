@@ -5,6 +5,7 @@ the memory) and call the library.  No attention arithmetic happens here.
 
 from __future__ import annotations
 
+import copy
 import dataclasses
 from typing import Optional
 
@@ -51,6 +52,34 @@ class DeviceCase:
            self.block_table, self.w_uk, self.w_uv, self.out if out is None else out,
            self.workspace if workspace is None else workspace, stream=stream, events=events)
         return self.out if out is None else out
+
+
+def run_variant(case: "DeviceCase", *, gate=None, q_latent=None, latent_out: bool = False,
+                stream=None) -> torch.Tensor:
+    """One call of a decode variant on ``case``'s inputs: ``gate`` (device tensor [B, H, d_v])
+    selects the gated entry point, ``q_latent`` (device tensor [B, H, NB*d_cb]) passes a folded
+    query with MLA_FLAG_QUERY_LATENT (W_UK not passed), ``latent_out`` sets
+    MLA_FLAG_OUTPUT_LATENT (W_UV not passed) and returns [B, H, NB*d_cb].  Returns a new
+    output tensor."""
+    p = copy.copy(case.params)
+    if q_latent is not None:
+        p.flags |= B.MLA_FLAG_QUERY_LATENT
+    if latent_out:
+        p.flags |= B.MLA_FLAG_OUTPUT_LATENT
+    width = p.num_branches * p.d_latent if latent_out else p.d_v
+    out = torch.empty((p.batch, p.num_heads, width), dtype=case.out.dtype, device=case.out.device)
+    qn = case.q_nope if q_latent is None else q_latent
+    w_uk = None if q_latent is not None else case.w_uk
+    w_uv = None if latent_out else case.w_uv
+    args = (p, qn, case.q_rope, case.latent_ptr, case.rope_ptr, case.seqlens, case.block_table,
+            w_uk, w_uv)
+    if gate is not None:
+        fn = B.mlra_decode_gated if case.branches == 4 else B.mla_decode_gated
+        fn(*args, gate, out, case.workspace, stream=stream)
+    else:
+        fn = B.mlra_decode if case.branches == 4 else B.mla_decode
+        fn(*args, out, case.workspace, stream=stream)
+    return out
 
 
 def make_params(inp: dict, num_splits: int = 0, flags: int = 0) -> B.MlaParams:

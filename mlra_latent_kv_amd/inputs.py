@@ -286,6 +286,25 @@ def cache_bytes(w: Workload, seqlens: np.ndarray) -> int:
 
 # ----------------------------------------------------------------------------- write side
 
+def make_variant_inputs(inp: dict, *, seed: Optional[int] = None, gate_std: float = 2.0) -> dict:
+    """Seeded extra inputs of the decode step's variants, for the input set ``inp``:
+
+    * ``gate``      [B, H, d_v] gate logits, N(0, gate_std^2), so sigmoid(gate) spans most of
+                    (0, 1);
+    * ``q_latent``  [B, H, NB * d_cb] a latent-space query (the form the query takes once W_UK is
+                    folded into the query projection), N(0, 1) / sqrt(d_cb) times the input
+                    set's query gain: the spread of W_UK^T q_nope under the default draw.
+    Storage format as ``make_inputs`` (uint16 bf16 bits or float32).
+    """
+    w = inp["workload"]
+    B = len(inp["seqlens"])
+    seed = inp["seed"] + 7919 if seed is None else seed
+    r_g, r_q = (np.random.default_rng(k) for k in np.random.SeedSequence(seed).spawn(2))
+    gate = r_g.standard_normal((B, w.heads, w.d_v), dtype=np.float32) * np.float32(gate_std)
+    q_lat = _normal(r_q, (B, w.heads, w.branches * w.d_cb), w.d_cb, inp.get("q_gain", 1.0))
+    return {"gate": to_storage(gate, w.dtype), "q_latent": to_storage(q_lat, w.dtype)}
+
+
 def make_append_inputs(d_model: int, d_latent: int, batch: int, *, seed: int = 2001,
                        d_rope: int = 64) -> dict:
     """Seeded new-token hidden states and down-projections for a cache append: hidden

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == {"mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
                              "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc",
                              "mla_rope_rotate", "mla_status_str", "mla_append_workspace_size",
-                             "mla_cache_append"}
+                             "mla_cache_append", "mla_decode_gated", "mlra_decode_gated"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -93,7 +93,7 @@ def call(lib, p, fn="mla_decode", ws_bytes=1 << 40, **ptr):
     (dict(d_nope=64), 3),
     (dict(latent_stride_tok=500), 2),
     (dict(latent_stride_tok=580), 7),
-    (dict(flags=2), 2),
+    (dict(flags=8), 2),
     (dict(num_pages=-1), 2),
     (dict(softmax_scale=float("nan")), 2),
     (dict(rope_theta=0.0), 2),
@@ -155,6 +155,45 @@ def test_workspace_and_alignment(lib):
     assert call(lib, p, latent=FAKE + 8) == 7
     assert call(lib, p, workspace=FAKE + 64) == 7
     assert call(lib, p, w_uk=FAKE + 2) == 7     # bf16 weights need 16-byte alignment
+
+
+def call_gated(lib, p, fn="mla_decode_gated", ws_bytes=1 << 40, **ptr):
+    args = dict(q_nope=FAKE, q_rope=FAKE, latent=FAKE, rope=FAKE, seqlens=FAKE, block_table=FAKE,
+                w_uk=FAKE, w_uv=FAKE, gate=FAKE, out=FAKE, workspace=FAKE)
+    args.update(ptr)
+    return getattr(lib, fn)(ctypes.byref(p), *args.values(), ws_bytes, None)
+
+
+def test_folded_and_latent_flags_validation(lib):
+    """MLA_FLAG_QUERY_LATENT drops the W_UK pointer and the d_nope rule, MLA_FLAG_OUTPUT_LATENT
+    the W_UV pointer and the d_v rule; each call stops at the workspace check (MLA_ERR_WORKSPACE),
+    past the pointer and shape checks, so nothing is launched."""
+    QL, OL = B.MLA_FLAG_QUERY_LATENT, B.MLA_FLAG_OUTPUT_LATENT
+    plain = params_for("mla_bf16_b32_h128_l4096")
+    assert call(lib, plain, w_uk=None) == 1 and call(lib, plain, w_uv=None) == 1
+    assert call(lib, params_for("mla_bf16_b32_h128_l4096", flags=QL), w_uk=None, ws_bytes=1) == 4
+    assert call(lib, params_for("mla_bf16_b32_h128_l4096", flags=OL), w_uv=None, ws_bytes=1) == 4
+    both = params_for("mlra4_bf16_b32_h32_l8192", flags=QL | OL)
+    assert call(lib, both, fn="mlra_decode", w_uk=None, w_uv=None, ws_bytes=1) == 4
+    assert call(lib, params_for("mla_bf16_b32_h128_l4096", d_nope=64)) == 3
+    assert call(lib, params_for("mla_bf16_b32_h128_l4096", d_nope=64, flags=QL), ws_bytes=1) == 4
+    assert call(lib, params_for("mla_bf16_b32_h128_l4096", d_v=64)) == 3
+    assert call(lib, params_for("mla_bf16_b32_h128_l4096", d_v=64, flags=OL), ws_bytes=1) == 4
+    assert call(lib, params_for("tiny_mla_f32_b1_h4_l64", d_nope=999, flags=QL),
+                w_uk=None, ws_bytes=1) == 4
+
+
+def test_gated_entry_points_validation(lib):
+    p = params_for("mla_bf16_b32_h128_l4096")
+    assert call_gated(lib, p, ws_bytes=1) == 4                       # passes pointer checks
+    assert call_gated(lib, p, gate=None) == 1
+    assert call_gated(lib, p, gate=FAKE + 2) == 7                    # bf16 gate: 16-byte aligned
+    assert call_gated(lib, p, fn="mlra_decode_gated") == 3           # NB = 1 here
+    assert call_gated(lib, params_for("mlra4_bf16_b32_h32_l8192"), fn="mlra_decode_gated",
+                      ws_bytes=1) == 4
+    lo = params_for("mla_bf16_b32_h128_l4096", flags=B.MLA_FLAG_OUTPUT_LATENT)
+    assert call_gated(lib, lo) == 3                                  # no gate on a latent output
+    assert call(lib, p, out=FAKE + 4) == 7                           # bf16 out: 16-byte aligned
 
 
 def test_rope_rotate_validation(lib):
