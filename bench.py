@@ -279,6 +279,12 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--op", choices=["decode", "append"], default="decode",
                     help="decode: the decode step (the metric); append: one step's cache write")
+    ap.add_argument("--variant", default="none",
+                    choices=["none", "gate", "query_latent", "output_latent",
+                             "query_latent+output_latent"],
+                    help="time a decode variant (gated output, folded query, latent output); "
+                         "stage times and the main-loop roofline come from the plain call, "
+                         "whose main loop is the same kernel")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -318,6 +324,17 @@ def main():
     lens = np.asarray(inp["seqlens"], np.int64)
     cache_bytes = I.cache_bytes(w, lens)
 
+    step = case.run
+    if args.variant != "none":
+        var = I.make_variant_inputs(inp)
+        v_gate = Hn._to_dev(var["gate"], w.dtype, "cuda") if "gate" in args.variant else None
+        v_ql = (Hn._to_dev(var["q_latent"], w.dtype, "cuda") if "query_latent" in args.variant
+                else None)
+        v_lo = "output_latent" in args.variant
+
+        def step():
+            return Hn.run_variant(case, gate=v_gate, q_latent=v_ql, latent_out=v_lo)
+
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")  # 512 MiB
     ev = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
@@ -331,7 +348,7 @@ def main():
 
     for i in range(W):
         do_flush(i)
-        case.run()
+        step()
     torch.cuda.synchronize()
     log(f"[bench] warm-up done ({W} steps); timing {K} steps")
 
@@ -343,7 +360,7 @@ def main():
     for i in range(K):
         ev.record(pairs_fd[i][0], stream)
         do_flush(i)
-        case.run()
+        step()
         ev.record(pairs_fd[i][1], stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -409,7 +426,7 @@ def main():
                    "context_tokens": int(lens.sum()), "d_latent": w.d_c, "d_rope": w.d_rope,
                    "paged": bool(inp["paged"]), "work_items": plan["items"],
                    "pages_per_item": plan["pages"],
-                   "cache_flush": args.flush},
+                   "cache_flush": args.flush, "variant": args.variant},
         "pct_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBPS, 2),
         "read_probe_GBps": round(probe_gbps, 1),
         "pct_read_probe": round(100 * value * 1e3 / probe_gbps, 2),
@@ -434,7 +451,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.variant == "none":
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
