@@ -37,6 +37,10 @@ position part is a separate uncompressed key that carries RoPE (same page,
 section "解耦旋轉位置編碼"); MLRA's branches are column blocks of the same
 projection ("[ICLR 2025] MLRA…", section 2.1), so the row is computed alike.
 
+Several query tokens per step (``mla_decode(num_queries=s_q)``; the yololab page,
+section "繁榮背後的代價…", names the compute-heavy regime that several query rows against one
+cache read lead to): each new token attends causally over the cache, which already holds it.
+
 Variants of the decode step (``attend_unabsorbed`` / ``mla_decode`` keywords):
 * gated output ("[ICLR 2025] MLRA…", section 4: MLRA-4 combined with gated attention):
   each head's output, after the scaled branch sum, is multiplied elementwise by
@@ -51,6 +55,8 @@ Variants of the decode step (``attend_unabsorbed`` / ``mla_decode`` keywords):
 Readings where the pages are silent (each is an argument, not hidden):
   the gate is a logistic sigmoid of given logits, applied after out_scale and the branch
   sum, one value per output element; a gate and a latent output are not combined;
+  with s_q > 1 new tokens per step, query token i sits at L - s_q + i and sees the tokens up
+  to itself (the usual causal rule among the new tokens), its rotary query rotated there;
   the cache stores the rotary key already rotated at its own position t;
   a decode step appends its token at t = L_b, then L_b becomes t + 1;
   a sequence whose new token starts a page takes the next entry of a free-page
@@ -244,7 +250,7 @@ def mla_decode(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, d_rope: int, scale
                batches: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None,
                absorbed: bool = False, gate=None, q_latent: bool = False,
                latent_out: bool = False, branches: Optional[int] = None,
-               d_cb: Optional[int] = None) -> np.ndarray:
+               d_cb: Optional[int] = None, num_queries: int = 1) -> np.ndarray:
     """Decode step for a batch: out [len(batches), len(heads), d_v] in fp64.
 
     ``to_f64`` decodes stored cache rows (fp32 or bf16 bits) to float64; it is
@@ -253,6 +259,12 @@ def mla_decode(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, d_rope: int, scale
     only its share).  ``gate`` [B, H, d_v], ``q_latent`` (then ``q_nope`` holds the folded
     latent query [B, H, NB*d_cb] and ``w_uk`` may be None) and ``latent_out`` (then ``w_uv`` may
     be None and the output is [.., .., NB*d_cb]) select the variants of ``attend_unabsorbed``.
+
+    ``num_queries`` = s_q > 1: several new tokens per sequence are decoded in one step (the
+    cache already holds all of them).  The query rows are then [B, s_q * H, ...], row
+    i * H + h being head h of query token i, which sits at position L - s_q + i and attends
+    causally to the tokens up to and including itself: L_i = L - s_q + 1 + i of them (none
+    when L_i <= 0, giving a zero output).  ``heads`` then selects such rows.
     """
     w_uk = None if w_uk is None else to_f64(w_uk)
     w_uv = None if w_uv is None else to_f64(w_uv)
@@ -272,6 +284,28 @@ def mla_decode(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, d_rope: int, scale
         nb, dcb = int(branches), int(d_cb)
     d_out = nb * dcb if latent_out else w_uv.shape[-1]
     out = np.zeros((len(batches), len(heads), d_out), dtype=F64)
+    sq = int(num_queries)
+    if sq < 1 or H % sq:
+        raise ValueError("num_queries must be >= 1 and divide the query rows")
+    if sq > 1:
+        if absorbed:
+            raise ValueError("the absorbed cross-check covers one query token")
+        Hw = H // sq  # heads per query token (the weights' head count)
+        out = np.zeros((len(batches), len(heads), d_out), dtype=F64)
+        for i, b in enumerate(batches):
+            L = int(seqlens[b])
+            for j, r in enumerate(heads):
+                qi, h = divmod(r, Hw)
+                Li = max(0, L - sq + 1 + qi)  # causal: tokens 0 .. L - s_q + qi
+                rows = sequence_rows(cache, b, Li, page_size, block_table, to_f64)
+                out[i, j] = attend_unabsorbed(
+                    None if q_latent else qn[b, qi * Hw:(qi + 1) * Hw], qr[b, qi * Hw:(qi + 1) * Hw],
+                    rows, w_uk, w_uv, d_rope=d_rope, scale=scale, out_scale=out_scale,
+                    theta=theta, heads=[h],
+                    gate=None if g is None else g[b, qi * Hw:(qi + 1) * Hw],
+                    q_latent=qn[b, qi * Hw:(qi + 1) * Hw] if q_latent else None,
+                    latent_out=latent_out, branches=nb, d_cb=dcb)[0]
+        return out
     for i, b in enumerate(batches):
         L = int(seqlens[b])
         rows = sequence_rows(cache, b, L, page_size, block_table, to_f64)

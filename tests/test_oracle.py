@@ -841,3 +841,133 @@ def test_variant_planted_mistake_is_caught(monkeypatch, mistake):
             return out
         monkeypatch.setattr(O, "attend_unabsorbed", bad)
     assert not _variant_pins_pass()
+
+
+# ----------------------------------------------------------------------------- several query tokens
+# s_q new tokens per sequence decoded in one step (the compute-heavier regime of the yololab
+# page, section 繁榮背後的代價): token i sits at L - s_q + i and attends causally.
+
+def _brute_multi(qn, qr, rows, w_uk, w_uv, sq, d_rope, scale, out_scale, theta):
+    """Scalar loops over the whole cache with an explicit causal mask: query token i scores
+    every token t < L and drops those with t > L - s_q + i (weight exactly 0), its rotary part
+    at position L - s_q + i; softmax as 1 / sum_j exp(s_j - s_t) over the kept tokens."""
+    NB, Hw, dn, dcb = w_uk.shape
+    dv = w_uv.shape[-1]
+    L = len(rows)
+    res = []
+    for r in range(sq * Hw):
+        i, h = divmod(r, Hw)
+        pos = L - sq + i
+        kept = [t for t in range(L) if t <= pos]
+        if not kept:
+            res.append([0.0] * dv)
+            continue
+        qrot = _rotate_py(list(qr[r]), pos, theta)
+        acc = [[] for _ in range(dv)]
+        for br in range(NB):
+            scores, vals = {}, {}
+            for t in kept:
+                c = [float(v) for v in rows[t][br * dcb:(br + 1) * dcb]]
+                K = [math.fsum(float(w_uk[br, h, n, j]) * c[j] for j in range(dcb)) for n in range(dn)]
+                krot = _rotate_py([float(v) for v in rows[t][NB * dcb:NB * dcb + d_rope]], t, theta)
+                scores[t] = scale * (math.fsum(float(qn[r, br, n]) * K[n] for n in range(dn))
+                                     + math.fsum(qrot[k] * krot[k] for k in range(d_rope)))
+                vals[t] = [math.fsum(float(w_uv[br, h, j, v]) * c[j] for j in range(dcb))
+                           for v in range(dv)]
+            for t in kept:
+                p = 1.0 / math.fsum(math.exp(scores[j] - scores[t]) for j in kept)
+                for v in range(dv):
+                    acc[v].append(p * vals[t][v])
+        res.append([out_scale * math.fsum(a) for a in acc])
+    return np.array(res)
+
+
+@pytest.mark.parametrize("NB,sq,L", [(1, 2, 7), (4, 3, 6), (1, 4, 2), (1, 3, 3)])
+def test_multi_query_brute_force(NB, sq, L):
+    """Against the masked brute force, including L < s_q (the first rows see nothing) and
+    L = s_q (the first row sees one token)."""
+    rng = np.random.default_rng(61 + 10 * NB + sq)
+    Hw, dn, dcb, dr, dv = 2, 3, 4, 4, 5
+    qn = rng.standard_normal((1, sq * Hw, NB, dn))
+    qr = rng.standard_normal((1, sq * Hw, dr))
+    cache = rng.standard_normal((1, L, NB * dcb + dr))
+    w_uk = rng.standard_normal((NB, Hw, dn, dcb))
+    w_uv = rng.standard_normal((NB, Hw, dcb, dv))
+    kw = dict(d_rope=dr, scale=0.4, out_scale=0.5 if NB == 4 else 1.0, theta=1e4)
+    got = O.mla_decode(qn, qr, cache, [L], w_uk, w_uv, num_queries=sq, **kw)[0]
+    ref = _brute_multi(qn[0], qr[0], cache[0], w_uk, w_uv, sq, dr, 0.4, kw["out_scale"], 1e4)
+    assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_multi_query_hand_example():
+    """One head, width-1 latent, rope zero, W_UK = 1/3, W_UV = 1, cache values (3, -1), so
+    the keys are (1, -1/3); L = 2, s_q = 2.  Query 0 sees token 0 only and returns its value
+    3 exactly; query 1 = -3 ln3 / 4 has logits (-3 ln3 / 4, ln3 / 4), weights (1/4, 3/4) and
+    output 3/4 - 3/4 = 0."""
+    qn = np.array([[[[5.0]], [[-0.75 * math.log(3.0)]]]])  # [B=1, s_q*H=2, NB=1, d_nope=1]
+    qr = np.zeros((1, 2, 2))
+    cache = np.array([[[3.0, 0.0, 0.0], [-1.0, 0.0, 0.0]]])
+    w_uk = np.array([[[[1.0 / 3.0]]]])
+    w_uv = np.ones((1, 1, 1, 1))
+    out = O.mla_decode(qn, qr, cache, [2], w_uk, w_uv, d_rope=2, scale=1.0, num_queries=2)[0]
+    assert out[0, 0] == 3.0
+    assert abs(out[1, 0]) < 1e-15
+
+
+def test_multi_query_last_row_is_plain_decode_and_causality():
+    """The last query token's rows equal the one-token decode of the same cache; a change to
+    cache rows past L_i leaves query i's rows unchanged and changes the later ones."""
+    w = I.WORKLOADS["mlra4_bf16_b32_h32_l8192"]
+    inp = I.make_inputs(w, seed=8, seqlens=[40])
+    f64 = lambda a: I.to_f64(a, "bf16")
+    sq = 3
+    rng = np.random.default_rng(1)
+    qn = rng.standard_normal((1, sq * w.heads, 4, 128)) / math.sqrt(128)
+    qr = rng.standard_normal((1, sq * w.heads, 64)) / 8.0
+    cache = f64(inp["cache"])
+    wk, wv = f64(inp["w_uk"]), f64(inp["w_uv"])
+    kw = dict(d_rope=64, scale=w.softmax_scale, out_scale=0.5, theta=1e4)
+    heads = [0, 31, 32, 63, 64, 95]
+    multi = O.mla_decode(qn, qr, cache, [40], wk, wv, num_queries=sq, heads=heads, **kw)[0]
+    last = O.mla_decode(qn[:, 2 * 32:], qr[:, 2 * 32:], cache, [40], wk, wv, heads=[0, 31], **kw)[0]
+    assert np.array_equal(multi[4:], last)
+    changed = cache.copy()
+    changed[0, 38] += 1.0                  # L_i = 38, 39, 40: queries 1 and 2 see token 38
+    after = O.mla_decode(qn, qr, changed, [40], wk, wv, num_queries=sq, heads=heads, **kw)[0]
+    assert np.array_equal(after[:2], multi[:2])        # query 0 sees tokens 0..37
+    assert not np.allclose(after[2:], multi[2:])       # queries 1, 2 see token 38
+
+
+def _multi_pins_pass():
+    checks = [lambda: test_multi_query_brute_force(4, 3, 6), lambda: test_multi_query_brute_force(1, 4, 2),
+              test_multi_query_hand_example, test_multi_query_last_row_is_plain_decode_and_causality]
+    with np.errstate(all="ignore"):
+        for c in checks:
+            try:
+                c()
+            except (AssertionError, ValueError, IndexError):
+                return False
+    return True
+
+
+def test_multi_pins_pass_unplanted():
+    assert _multi_pins_pass()
+
+
+@pytest.mark.parametrize("mistake", ["not_causal", "query_rotated_one_late", "off_by_one_limit"])
+def test_multi_planted_mistake_is_caught(monkeypatch, mistake):
+    real_rows = O.sequence_rows
+    if mistake == "not_causal":
+        # every query token sees the whole cache (its rotary position stays L_i - 1)
+        def bad(cache, b, L, *a, **k):
+            return real_rows(cache, b, np.shape(cache)[1] if np.ndim(cache) == 3 else L, *a, **k)
+        monkeypatch.setattr(O, "sequence_rows", bad)
+    elif mistake == "query_rotated_one_late":
+        real_rope = O.rope
+        monkeypatch.setattr(O, "rope", lambda x, pos, theta=1e4: real_rope(
+            x, pos if np.ndim(pos) else pos + 1, theta))
+    elif mistake == "off_by_one_limit":
+        def bad(cache, b, L, *a, **k):
+            return real_rows(cache, b, max(0, L - 1) if L else 0, *a, **k)
+        monkeypatch.setattr(O, "sequence_rows", bad)
+    assert not _multi_pins_pass()
