@@ -119,21 +119,24 @@ def source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def main_kernel(w) -> str:
-    """Name of the kernel that runs the split-K main loop for workload w."""
+def main_kernel(w, num_queries: int = 1) -> str:
+    """Name of the kernel that runs the split-K main loop for workload w (its query rows are
+    num_queries tokens x heads)."""
     if w.dtype != "bf16":
         return "k_main_f32"
-    return "k_main_bf16_wide" if (w.branches == 1 and w.heads % 128 == 0) else "k_main_bf16"
+    rows = num_queries * w.heads
+    return "k_main_bf16_wide" if (w.branches == 1 and w.d_cb == 512 and rows % 128 == 0) \
+        else "k_main_bf16"
 
 
-def counters_traffic(workload: str):
+def counters_traffic(workload: str, num_queries: int = 1):
     """HBM bytes per main-kernel launch from the committed rocprofv3 counter summary, if it was
     taken on the current main-loop source; else None."""
     try:
         s = json.load(open(PMC_SUMMARY))
     except (OSError, ValueError):
         return None
-    ent = s.get(workload)
+    ent = s.get(workload if num_queries == 1 else f"{workload}@q{num_queries}")
     if not ent or ent.get("source_sha") != source_sha():
         return None
     return ent.get("hbm_bytes_per_launch")
@@ -285,6 +288,8 @@ def main():
                     help="time a decode variant (gated output, folded query, latent output); "
                          "stage times and the main-loop roofline come from the plain call, "
                          "whose main loop is the same kernel")
+    ap.add_argument("--num-queries", type=int, default=1,
+                    help="query tokens per sequence decoded in one step (causal among them)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -318,7 +323,7 @@ def main():
         return
     w = I.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name}")
-    inp = I.make_inputs(w)
+    inp = I.make_inputs(w, num_queries=args.num_queries)
     case = Hn.to_device(inp, num_splits=args.num_splits)
     torch.cuda.synchronize()
     lens = np.asarray(inp["seqlens"], np.int64)
@@ -426,32 +431,33 @@ def main():
                    "context_tokens": int(lens.sum()), "d_latent": w.d_c, "d_rope": w.d_rope,
                    "paged": bool(inp["paged"]), "work_items": plan["items"],
                    "pages_per_item": plan["pages"],
-                   "cache_flush": args.flush, "variant": args.variant},
+                   "cache_flush": args.flush, "variant": args.variant,
+                   "query_tokens_per_seq": args.num_queries},
         "pct_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBPS, 2),
         "read_probe_GBps": round(probe_gbps, 1),
         "pct_read_probe": round(100 * value * 1e3 / probe_gbps, 2),
-        "query_tokens_per_s": round(len(lens) / (ms * 1e-3), 1),
+        "query_tokens_per_s": round(args.num_queries * len(lens) / (ms * 1e-3), 1),
         "context_tokens_per_s": round(float(lens.sum()) / (ms * 1e-3), 1),
         "ms_p10_p50_p90": [round(float(np.percentile(total, q)), 5) for q in (10, 50, 90)],
         "stage_us": {k: round(1e3 * statistics.mean(v), 2) for k, v in stage.items()},
         "wall_s_timed_region": round(t_wall, 4),
         "flush_us": round(1e3 * statistics.mean(t_f), 2),
         "roofline": {
-            "kernel": main_kernel(w),
+            "kernel": main_kernel(w, args.num_queries),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes": int(cache_bytes),
-            "traffic": counters_traffic(w.name),
+            "traffic": counters_traffic(w.name, args.num_queries),
             "main_us": round(main_ms * 1e3, 2),
             "frac_of_read_probe": round(achieved / probe_gbps, 4),
             "empty_event_pair_us": round(pair_ms * 1e3, 2),
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and args.variant == "none":
+    if not args.no_cpu_baseline and args.variant == "none" and args.num_queries == 1:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -102,6 +102,9 @@ typedef struct mla_params {
                                  MLA_FLAG_OUTPUT_LATENT, in any combination                */
   int32_t num_pages;          /* paged: pages in the pool (bound for the device checks);
                                  0 = not given (block ids are then not checked)            */
+  int32_t num_queries;        /* s_q new tokens per sequence decoded in this step (0 or 1:
+                                 one); see "Several query tokens" below                    */
+  int32_t reserved;           /* 0                                                         */
   int64_t latent_stride_tok;  /* elements between consecutive tokens of the latent cache   */
   int64_t latent_stride_seq;  /* contiguous: elements between sequences; paged: pages      */
   int64_t rope_stride_tok;    /* same two strides for the rotary-key cache                 */
@@ -122,7 +125,9 @@ typedef struct mla_params {
  * Alignment: bf16 latent, rope, q_nope, w_uk, w_uv, gate and out pointers 16-byte aligned
  * and the cache strides multiples of 8 elements; other pointers aligned to their element size.
  * num_splits is at most 512 and at most ceil(max_seqlen / 64).  flags holds only the
- * MLA_FLAG_* bits above; num_pages >= 0.  With MLA_FLAG_QUERY_LATENT the d_nope rule does not
+ * MLA_FLAG_* bits above; num_pages >= 0; 0 <= num_queries <= 16 (s_q * H must meet the
+ * head rule, and every 32-head group must belong to one query token: H % 32 == 0 on bf16);
+ * reserved == 0.  With MLA_FLAG_QUERY_LATENT the d_nope rule does not
  * apply, with MLA_FLAG_OUTPUT_LATENT the d_v rule does not.
  *
  * Split plan.  The attention over each sequence is split into work items of whole 64-token
@@ -151,6 +156,19 @@ typedef struct mla_params {
  * With MLA_FLAG_DEVICE_CHECKS, a used block-table entry outside [0, num_pages) makes a plan
  * with no items (every output zero, nothing read from the pool); out-of-range seqlens are
  * clamped into [0, max_seqlen] as always and only reported.
+ */
+
+/*
+ * Several query tokens (num_queries = s_q > 1): the step decodes s_q new tokens of every
+ * sequence at once, all of them already in the cache (seqlens[b] = L counts them).  Token i
+ * (0 .. s_q - 1) sits at position L - s_q + i, its rotary query is rotated there, and it
+ * attends causally to the L_i = L - s_q + 1 + i tokens up to and including itself (a row
+ * with L_i <= 0 is zero).  The query-side and output arrays gain a token axis before the
+ * head axis: q_nope [B, s_q, H, NB, d_nope] (or [B, s_q, H, NB*d_latent] folded), q_rope
+ * [B, s_q, H, d_rope], gate and out [B, s_q, H, ...]; the weights keep their H heads.  Every
+ * (token, head) pair is one row of the split plan's work, so the workspace grows with s_q.
+ * (The yololab MLA page, section 繁榮背後的代價: several query rows per cache read move the
+ * step from memory-bound towards compute-bound.)
  */
 
 /*

@@ -35,6 +35,7 @@ class MlaParams(ctypes.Structure):
         ("d_nope", c_int32), ("d_v", c_int32), ("d_latent", c_int32), ("d_rope", c_int32),
         ("page_size", c_int32), ("max_pages_per_seq", c_int32), ("max_seqlen", c_int32),
         ("num_splits", c_int32), ("dtype", c_int32), ("flags", c_int32), ("num_pages", c_int32),
+        ("num_queries", c_int32), ("reserved", c_int32),
         ("latent_stride_tok", c_int64), ("latent_stride_seq", c_int64),
         ("rope_stride_tok", c_int64), ("rope_stride_seq", c_int64),
         ("block_table_stride", c_int64),

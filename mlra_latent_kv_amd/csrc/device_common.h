@@ -73,6 +73,13 @@ struct RopeFreq {
 
 // cos/sin of the rotation angle pos * f: the product and its reduction to [-pi, pi] are done
 // in fp64 (positions reach 2^26), the trigonometric functions in fp32 on the reduced angle.
+// Tokens query token qi of s_q sees in sequence b: the causal limit L - s_q + 1 + qi, with L =
+// seqlens[b] clamped to [0, max_seqlen] as the split plan clamps it (s_q = 1: L).
+__device__ __forceinline__ int causal_limit(const int32_t* seqlens, int b, int max_seqlen, int sq,
+                                            int qi) {
+  return min(max(seqlens[b], 0), max_seqlen) - sq + 1 + qi;
+}
+
 __device__ __forceinline__ void rope_cos_sin(int pos, double f, float* c, float* s) {
   constexpr double kTwoPi = 6.283185307179586476925286766559;
   double a = (double)pos * f;

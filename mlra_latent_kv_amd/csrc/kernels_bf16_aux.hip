@@ -45,7 +45,7 @@ template <bool LQ>
 __global__ __launch_bounds__(256) void k_prologue_bf16(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
     const int32_t* __restrict__ seqlens, const bf16* __restrict__ w_uk, bf16* __restrict__ qcat,
-    int B, int H, int NB, int dcb, float qscale, RopeFreq rf, PlanArgs plan) {
+    int B, int H, int NB, int dcb, float qscale, RopeFreq rf, PlanArgs plan, int Hw, int sq) {
   constexpr int dn = 128, dr = 64;
   __shared__ __align__(16) bf16 sW[dn * kPPitch];
   const int h = blockIdx.x, b0 = blockIdx.y * kRows, cb = blockIdx.z;
@@ -54,6 +54,9 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
     return;
   }
   const int dc = NB * dcb, row = dc + dr;
+  // query row h = token qi x Hw + weight head hw (s_q > 1 tokens per sequence: token qi sits
+  // at L - s_q + qi)
+  const int hw = h % Hw, qi = h / Hw;
   const int br = (cb * kPCols) / dcb;          // branch of this column block
   const int c0 = (cb * kPCols) % dcb;          // first column inside the branch
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -80,8 +83,8 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
       const bf16* xr = q_rope + ((size_t)bc * H + h) * dr + 2 * (has_r[it] ? k_r[it] : 0);
       x0[it] = (float)xr[0];
       x1[it] = (float)xr[1];
-      // the length as the plan uses it, clamped to [0, max_seqlen]
-      L_r[it] = min(max(seqlens[bc], 0), plan.max_seqlen);
+      // position of the query token: L - s_q + qi, L as the plan clamps it
+      L_r[it] = causal_limit(seqlens, bc, plan.max_seqlen, sq, qi) - 1;
     }
   }
   if constexpr (LQ) {
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
       }
     }
   } else {
-    const bf16* wsrc = w_uk + ((size_t)br * H + h) * dn * dcb + c0;
+    const bf16* wsrc = w_uk + ((size_t)br * Hw + hw) * dn * dcb + c0;
 #pragma unroll
     for (int j = 0; j < dn * kPCols / 8 / 256; ++j) {
       const int c = tid + 256 * j, r = c >> 4, col = (c & 15) * 8;
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
   for (int it = 0; it < kRotPer; ++it) {
     if (has_r[it]) {
       float cs, sn;
-      rope_cos_sin(L_r[it] > 0 ? L_r[it] - 1 : 0, rf.f[k_r[it]], &cs, &sn);
+      rope_cos_sin(max(L_r[it], 0), rf.f[k_r[it]], &cs, &sn);
       bf16* o = qcat + ((size_t)bb_r[it] * H + h) * row + dc + 2 * k_r[it];
       o[0] = (bf16)((x0[it] * cs - x1[it] * sn) * qscale);
       o[1] = (bf16)((x0[it] * sn + x1[it] * cs) * qscale);
@@ -151,7 +154,7 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
   hipLaunchKernelGGL(p.latent_q ? k_prologue_bf16<true> : k_prologue_bf16<false>, grid,
                      dim3(256), 0, s, (const bf16*)a.q_nope,
                      (const bf16*)a.q_rope, a.seqlens, (const bf16*)a.w_uk, (bf16*)a.qcat, p.B,
-                     p.H, p.NB, p.dcb, a.softmax_scale * kLog2e, rf, a.plan);
+                     p.H, p.NB, p.dcb, a.softmax_scale * kLog2e, rf, a.plan, p.Hw, p.sq);
   return hipGetLastError();
 }
 
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
     const bf16* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ split_off, const bf16* __restrict__ w_uv,
     const bf16* __restrict__ gate, bf16* __restrict__ out, int B, int H, int NB, int dcb,
-    float out_scale) {
+    float out_scale, int Hw) {
   constexpr int kCPR = DC / 8;                  // 16-byte chunks per latent row
   constexpr int R = 256 * NC / (TPC * kCPR);
   constexpr int kWRows = DC / 4;                // W_UV rows (latent columns) per wave
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void k_combine_epilogue_bf16(
   // in while the partials are merged.
   auto issue_wuv = [&](int i0, int i1) {
     const int c0 = kWRows * w, br = c0 / dcb;
-    const bf16* wbase = w_uv + ((size_t)(br * H + h) * dcb + (c0 % dcb)) * kCeDv;
+    const bf16* wbase = w_uv + ((size_t)(br * Hw + h % Hw) * dcb + (c0 % dcb)) * kCeDv;
     const __amdgpu_buffer_rsrc_t rs = tile::rsrc(wbase, kWRows * kCeRowB);
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
@@ -503,7 +506,7 @@ hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipS
                            : combine_epilogue_kernel<false>(p.dc, R);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, (const bf16*)a.part_o, a.part_ml,
                      a.split_off, (const bf16*)a.w_uv, (const bf16*)a.gate, (bf16*)a.out, p.B,
-                     p.H, p.NB, p.dcb, a.out_scale);
+                     p.H, p.NB, p.dcb, a.out_scale, p.Hw);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
                                                   const T* __restrict__ w_uk, T* __restrict__ qcat,
                                                   int B, int H, int NB, int dn, int dcb, int dr,
                                                   float qscale, RopeFreq rf, PlanArgs plan,
-                                                  int lds_bytes, int latent_q) {
+                                                  int lds_bytes, int latent_q, int Hw, int nq) {
   extern __shared__ __align__(16) float sq[];  // [kBatchBlock][NB][dn]; the plan block: scratch
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kBatchBlock;
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
   }
   const int nb = min(kBatchBlock, B - b0);
   const int dc = NB * dcb, row = dc + dr;
+  const int hw = h % Hw, qi = h / Hw;  // query row = token qi x Hw + weight head hw
   if (latent_q) {
     // folded query: q_nope holds q_lat [B][H][dc], W_UK already applied offline
     for (int i = threadIdx.x; i < nb * dc; i += blockDim.x) {
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
   __syncthreads();
   for (int c = threadIdx.x; !latent_q && c < dc; c += blockDim.x) {
     const int br = c / dcb, cc = c % dcb;
-    const T* w = w_uk + ((size_t)br * H + h) * dn * dcb + cc;
+    const T* w = w_uk + ((size_t)br * Hw + hw) * dn * dcb + cc;
     const float* q = sq + br * dn;
     float acc[kBatchBlock];
 #pragma unroll
@@ -75,9 +76,9 @@ __global__ __launch_bounds__(256) void k_prologue(const T* __restrict__ q_nope,
   for (int i = threadIdx.x; i < nb * half; i += blockDim.x) {
     const int j = i / half, k = i % half;
     const int b = b0 + j;
-    const int L = min(max(seqlens[b], 0), plan.max_seqlen);  // as the plan clamps it
+    const int pos = causal_limit(seqlens, b, plan.max_seqlen, nq, qi) - 1;  // L - s_q + qi
     float cs, sn;
-    rope_cos_sin(L > 0 ? L - 1 : 0, rf.f[k], &cs, &sn);
+    rope_cos_sin(max(pos, 0), rf.f[k], &cs, &sn);
     const T* x = q_rope + ((size_t)b * H + h) * dr + 2 * k;
     const float x0 = to_f32(x[0]), x1 = to_f32(x[1]);
     T* o = qcat + ((size_t)b * H + h) * row + dc + 2 * k;
@@ -96,7 +97,7 @@ hipError_t launch_prologue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, s, (const float*)a.q_nope,
                        (const float*)a.q_rope, a.seqlens, (const float*)a.w_uk, (float*)a.qcat,
                        p.B, p.H, p.NB, p.dn, p.dcb, p.dr, qscale, rf, a.plan, (int)lds,
-                       p.latent_q);
+                       p.latent_q, p.Hw, p.sq);
   return hipGetLastError();
 }
 
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(128) void k_epilogue(const float* __restrict__ olat
                                                   const T* __restrict__ w_uv,
                                                   const T* __restrict__ gate, T* __restrict__ out,
                                                   int B, int H, int NB, int dcb, int dv,
-                                                  float out_scale) {
+                                                  float out_scale, int Hw) {
   extern __shared__ float so[];  // [kBatchBlock][dc]
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kBatchBlock;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(128) void k_epilogue(const float* __restrict__ olat
 #pragma unroll
     for (int j = 0; j < kBatchBlock; ++j) acc[j] = 0.0f;
     for (int br = 0; br < NB; ++br) {
-      const T* w = w_uv + ((size_t)br * H + h) * dcb * dv + v;
+      const T* w = w_uv + ((size_t)br * Hw + h % Hw) * dcb * dv + v;
       const float* o = so + br * dcb;
       for (int c = 0; c < dcb; ++c) {
         const float wv = to_f32(w[(size_t)c * dv]);
@@ -278,7 +279,7 @@ hipError_t launch_epilogue(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const size_t lds = (size_t)kBatchBlock * p.dc * sizeof(float);
   hipLaunchKernelGGL(k_epilogue<float>, grid, dim3(128), lds, s, (const float*)a.olat,
                      (const float*)a.w_uv, (const float*)a.gate, (float*)a.out, p.B, p.H, p.NB,
-                     p.dcb, p.dv, a.out_scale);
+                     p.dcb, p.dv, a.out_scale, p.Hw);
   return hipGetLastError();
 }
 
@@ -327,14 +328,17 @@ __global__ __launch_bounds__(64) void k_main_f32(
     const float* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, const int32_t* __restrict__ work, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
-    int NB, int dcb, int dr) {
+    int NB, int dcb, int dr, const int32_t* __restrict__ seqlens, int max_seqlen, int nq,
+    int Hw) {
   __shared__ float sq[512 + 64];
   __shared__ float sp[64 * 4];
   const int h = blockIdx.x % H;
   const int slot = blockIdx.x / H;  // slot s runs work item s
   const int b = work[4 * slot];
   if (b < 0) return;
-  const int t0 = work[4 * slot + 1], t1 = work[4 * slot + 2];
+  // tokens [t0, t1) of the item, cut at this row's causal limit (s_q > 1 query tokens)
+  const int t0 = work[4 * slot + 1];
+  const int t1 = min(work[4 * slot + 2], causal_limit(seqlens, b, max_seqlen, nq, h / Hw));
   const size_t item = (size_t)work[4 * slot + 3];
   const int lane = threadIdx.x;
   const int dc = NB * dcb, row = dc + dr;
@@ -405,7 +409,8 @@ hipError_t launch_main_f32(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_main_f32, grid, dim3(64), 0, s, (const float*)a.qcat,
                      (const float*)a.latent, (const float*)a.rope, a.lat_tok, a.lat_seq,
                      a.rope_tok, a.rope_seq, a.work, a.block_table, a.bt_stride, p.paged,
-                     (float*)a.part_o, a.part_ml, p.H, p.NB, p.dcb, p.dr);
+                     (float*)a.part_o, a.part_ml, p.H, p.NB, p.dcb, p.dr, a.seqlens,
+                     p.max_seqlen, p.sq, p.Hw);
   return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, const int32_t* __restrict__ work, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, bf16* __restrict__ part_o, float* __restrict__ part_ml, int H,
-    int n_hg) {
+    int n_hg, const int32_t* __restrict__ seqlens, int max_seqlen, int sq, int Hw) {
   static_assert(NB == 1 || DC == 512, "MLRA-4 rows hold four 128-wide branches");
   using G = Geom<DC>;
   constexpr int kBufs = ring_depth<DC>();
@@ -91,6 +91,9 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
   const int l32 = lane & 31, kg = lane >> 5;
   const int h0 = hg * kHG;
   float* ml = part_ml + item * NB * H * 2;  // [br][H][2]
+  // the tokens this head group's query token sees (s_q > 1 query tokens: token h0 / Hw is
+  // causal), within the item: scores past t_lim are masked; the tiles still load to t_end
+  const int t_lim = sq > 1 ? min(t_end, causal_limit(seqlens, b, max_seqlen, sq, h0 / Hw)) : t_end;
 
   const int n_tiles = (t_end - t_begin + kTT - 1) / kTT;
 
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
     issue(k + kBufs - 1);
 
     const int t0 = t_begin + kTT * k;
-    const int valid = min(kTT, t_end - t0);
+    const int valid = min(kTT, t_lim - t0);  // <= 0: every score of the tile masked
     const char* buf = sm.ring[k % kBufs];
 
     bf16x8 pb[2];
@@ -213,13 +216,16 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
       if (g16 == 0) sm.mx[tb * kHG + h] = mx;
       lds_barrier();
       mx = fmaxf(mx, sm.mx[(tb ^ 1) * kHG + h]);  // max over the tile's 32 tokens
-      const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid token
-      const float a = exp2f(m_run - m_new);
+      // -inf only while every token so far is masked (a query token that sees none of this
+      // item's tokens yet); the weights are then taken against 0 and come out 0
+      const float m_new = fmaxf(m_run, mx);
+      const float m_off = m_new == -INFINITY ? 0.0f : m_new;
+      const float a = exp2f(m_run - m_off);
       bf16 pe[4];
       float psum = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pe[e] = (bf16)exp2f(acc[e] - m_new);
+        pe[e] = (bf16)exp2f(acc[e] - m_off);
         psum += (float)pe[e];  // normalise with the rounded weights the MFMA uses
       }
       psum = sum_xor32(sum_xor16(psum));
@@ -258,11 +264,12 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
       mx = max_xor32(mx);
       const float m_new = fmaxf(m_run, mx);
-      alpha = exp2f(m_run - m_new);
+      const float m_off = m_new == -INFINITY ? 0.0f : m_new;  // every token so far masked
+      alpha = exp2f(m_run - m_off);
       float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bf16 e = (bf16)exp2f(acc[i] - m_new);
+        const bf16 e = (bf16)exp2f(acc[i] - m_off);
         pb[i >> 3][i & 7] = e;
         psum += (float)e;
       }
@@ -330,7 +337,7 @@ hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, s, (const bf16*)a.qcat,
                      (const bf16*)a.latent, (const bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok,
                      a.rope_seq, a.work, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,
-                     a.part_ml, p.H, p.n_hg);
+                     a.part_ml, p.H, p.n_hg, a.seqlens, p.max_seqlen, p.sq, p.Hw);
   return hipGetLastError();
 }
 

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, const int32_t* __restrict__ work, const int32_t* __restrict__ bt,
     int64_t bt_stride, int paged, bf16* __restrict__ part_o, float* __restrict__ part_ml, int H,
-    int n_hq) {
+    int n_hq, const int32_t* __restrict__ seqlens, int max_seqlen, int sq, int Hw) {
   // One LDS object.  (Kept as a single struct: with separate arrays the compiler's wait
   // analysis stops telling the tile reads apart from the loads in flight and waits for all
   // of them before the first read of every tile.)
@@ -158,6 +158,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   const int h0 = hq * kHeadsWG + 32 * w;  // this wave's heads
 
   const int n_tiles = (t_end - t_begin + kTT - 1) / kTT;
+  // the tokens this wave's query token sees (s_q > 1 query tokens: token h0 / Hw is causal):
+  // scores past t_lim are masked; the tiles still load to t_end for the other waves
+  const int t_lim = sq > 1 ? min(t_end, causal_limit(seqlens, b, max_seqlen, sq, h0 / Hw)) : t_end;
 
   const uint32_t lat_row_b = (uint32_t)(lat_tok * 2), rope_row_b = (uint32_t)(rope_tok * 2);
   const int32_t* bt_row = bt + (paged ? (int64_t)b * bt_stride : 0);
@@ -316,7 +319,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     mx = max_xor32(mx);  // every tile holds a valid token: mx finite
     raise = false;
     if (kt == 0) {
-      m_ref = mx;  // O and l are still zero
+      // O and l are still zero.  mx = -inf: the wave's query token sees none of the item's
+      // tokens (s_q > 1), and never will in it; its weights are then taken against 0
+      m_ref = mx == -INFINITY ? 0.0f : mx;
     } else if (__ballot(mx > m_ref + kLazyTau) != 0) {
       const float m_new = fmaxf(m_ref, mx);
       a_raise = exp2f(m_ref - m_new);
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   };
   // rows past the item's end in tile kt (only the last tile can have them) get -inf
   auto mask_ragged = [&](f32x16& S, int kt) {
-    const int valid = min(kTT, t_end - t_begin - kTT * kt);
+    const int valid = min(kTT, t_lim - t_begin - kTT * kt);  // <= 0: all masked
     if (valid < kTT) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -546,7 +551,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     *(bf16x8*)(po + (size_t)r * kDC) = *(const bf16x8*)(stage + r * kOutPitch + 16 * lane);
   float* ml = part_ml + (size_t)item * H * 2;  // [H][2]
   if (kg == 0) {
-    ml[(size_t)(h0 + l32) * 2 + 0] = m_ref;
+    // a head that saw no token (l = 0) reports max -inf, which the merge skips
+    ml[(size_t)(h0 + l32) * 2 + 0] = l_run > 0.0f ? m_ref : -INFINITY;
     ml[(size_t)(h0 + l32) * 2 + 1] = l_run;
   }
 }
@@ -559,7 +565,7 @@ hipError_t launch_main_bf16_wide(const Plan& p, const DecodeArgs& a, hipStream_t
   hipLaunchKernelGGL(k_main_bf16_wide, dim3(blocks), dim3(kThreads), 0, s, (const bf16*)a.qcat,
                      (const bf16*)a.latent, (const bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok,
                      a.rope_seq, a.work, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,
-                     a.part_ml, p.H, n_hq);
+                     a.part_ml, p.H, n_hq, a.seqlens, p.max_seqlen, p.sq, p.Hw);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   if (p->dtype != MLA_F32 && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (p->batch < 1 || p->num_heads < 1 || p->num_branches < 1 || p->d_nope < 1 || p->d_v < 1 ||
       p->d_latent < 1 || p->d_rope < 2 || (p->d_rope & 1) || p->max_seqlen < 0 ||
-      p->num_splits < 0 || p->num_pages < 0)
+      p->num_splits < 0 || p->num_pages < 0 || p->num_queries < 0 || p->num_queries > 16 ||
+      p->reserved != 0)
     return MLA_ERR_SHAPE;
   if (p->flags & ~(MLA_FLAG_DEVICE_CHECKS | MLA_FLAG_QUERY_LATENT | MLA_FLAG_OUTPUT_LATENT))
     return MLA_ERR_SHAPE;
@@ -35,7 +36,9 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
 
   Plan q{};
   q.B = p->batch;
-  q.H = p->num_heads;
+  q.sq = p->num_queries > 1 ? p->num_queries : 1;
+  q.Hw = p->num_heads;
+  q.H = q.sq * q.Hw;  // query rows: every (token, head) pair
   q.NB = p->num_branches;
   q.dcb = p->d_latent;
   q.dc = q.NB * q.dcb;
@@ -61,7 +64,8 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
     const bool mla = q.NB == 1 && q.dcb == 512;
     const bool shard = q.NB == 1 && q.dcb == 128;
     const bool mlra = q.NB == 4 && q.dcb == 128;
-    if (!(mla || shard || mlra) || q.dr != 64 || !dn_ok || !dv_ok || q.H % kHeadGroup)
+    // every 32-head group (and, with 128-row quads, every wave) within one query token
+    if (!(mla || shard || mlra) || q.dr != 64 || !dn_ok || !dv_ok || q.Hw % kHeadGroup)
       return MLA_ERR_UNSUPPORTED;
     q.path = Path::kBf16Mfma;
     q.n_hg = q.H / kHeadGroup;

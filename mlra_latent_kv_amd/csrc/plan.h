@@ -29,7 +29,9 @@ constexpr int kHdrWords = 8;           // plan header words at the start of the 
 enum class Path { kBf16Mfma, kF32Simt };
 
 struct Plan {
+  // H: query rows per sequence, s_q tokens x Hw heads (token-major); Hw: heads of the weights
   int B, H, NB, dcb, dc, dr, dn, dv, row;
+  int sq, Hw;
   int dtype, elem;
   int paged;
   int max_seqlen;

@@ -5,7 +5,6 @@ the memory) and call the library.  No attention arithmetic happens here.
 
 from __future__ import annotations
 
-import copy
 import dataclasses
 from typing import Optional
 
@@ -61,13 +60,14 @@ def run_variant(case: "DeviceCase", *, gate=None, q_latent=None, latent_out: boo
     query with MLA_FLAG_QUERY_LATENT (W_UK not passed), ``latent_out`` sets
     MLA_FLAG_OUTPUT_LATENT (W_UV not passed) and returns [B, H, NB*d_cb].  Returns a new
     output tensor."""
-    p = copy.copy(case.params)
+    p = case.params.copy()
     if q_latent is not None:
         p.flags |= B.MLA_FLAG_QUERY_LATENT
     if latent_out:
         p.flags |= B.MLA_FLAG_OUTPUT_LATENT
     width = p.num_branches * p.d_latent if latent_out else p.d_v
-    out = torch.empty((p.batch, p.num_heads, width), dtype=case.out.dtype, device=case.out.device)
+    rows = max(p.num_queries, 1) * p.num_heads
+    out = torch.empty((p.batch, rows, width), dtype=case.out.dtype, device=case.out.device)
     qn = case.q_nope if q_latent is None else q_latent
     w_uk = None if q_latent is not None else case.w_uk
     w_uv = None if latent_out else case.w_uv
@@ -95,6 +95,7 @@ def make_params(inp: dict, num_splits: int = 0, flags: int = 0) -> B.MlaParams:
     p.num_splits = num_splits
     p.dtype = B.MLA_BF16 if w.dtype == "bf16" else B.MLA_F32
     p.flags = flags
+    p.num_queries = int(inp.get("num_queries", 1))
     p.latent_stride_tok = p.rope_stride_tok = row
     if inp["paged"]:
         p.page_size = PAGE
@@ -136,7 +137,7 @@ def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None,
         block_table=None if bt is None else torch.from_numpy(bt).to(dev),
         w_uk=_to_dev(inp["w_uk"], dt, dev),
         w_uv=_to_dev(inp["w_uv"], dt, dev),
-        out=torch.empty((len(inp["seqlens"]), w.heads, w.d_v),
+        out=torch.empty((len(inp["seqlens"]), int(inp.get("num_queries", 1)) * w.heads, w.d_v),
                         dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=dev),
         workspace=torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev),
         branches=w.branches,

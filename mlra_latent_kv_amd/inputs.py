@@ -154,11 +154,13 @@ def _normal(rng, shape, fan_in, gain=1.0):
     return rng.standard_normal(shape, dtype=np.float32) * np.float32(gain / math.sqrt(fan_in))
 
 
-def _queries(w: Workload, B: int, r_qn, r_qr, q_gain: float):
-    """q_nope [B, H, NB, d_nope] (an independent vector per head and branch: each MLRA branch
-    has its own latent head, so its absorbed query differs) and q_rope [B, H, d_rope]."""
-    qn = _normal(r_qn, (B, w.heads, w.branches, w.d_nope), w.d_nope, q_gain)
-    qr = _normal(r_qr, (B, w.heads, w.d_rope), w.d_rope, q_gain)
+def _queries(w: Workload, B: int, r_qn, r_qr, q_gain: float, num_queries: int = 1):
+    """q_nope [B, s_q * H, NB, d_nope] (an independent vector per query token, head and
+    branch: each MLRA branch has its own latent head, so its absorbed query differs) and
+    q_rope [B, s_q * H, d_rope]; s_q = num_queries new tokens per sequence, token-major."""
+    rows = num_queries * w.heads
+    qn = _normal(r_qn, (B, rows, w.branches, w.d_nope), w.d_nope, q_gain)
+    qr = _normal(r_qr, (B, rows, w.d_rope), w.d_rope, q_gain)
     return to_storage(qn, w.dtype), to_storage(qr, w.dtype)
 
 
@@ -169,7 +171,8 @@ def requery(inp: dict, q_gain: float) -> dict:
     w = inp["workload"]
     r = _streams(inp["seed"])
     out = dict(inp)
-    out["q_nope"], out["q_rope"] = _queries(w, len(inp["seqlens"]), r[0], r[1], q_gain)
+    out["q_nope"], out["q_rope"] = _queries(w, len(inp["seqlens"]), r[0], r[1], q_gain,
+                                            inp.get("num_queries", 1))
     out["q_gain"] = q_gain
     return out
 
@@ -185,8 +188,12 @@ def make_inputs(
     poison: float = 1.0e4,
     shuffle_pages: bool = True,
     max_seqlen: Optional[int] = None,
+    num_queries: int = 1,
 ) -> dict:
     """Draw one seeded input set for workload ``w``.
+
+    ``num_queries`` = s_q new tokens per sequence decoded in one step: the queries get
+    s_q * H rows (token-major); everything else is unchanged.
 
     Overrides (``batch``, ``seqlens``, ``paged``, ``q_gain``) give the small and
     "sharp" parity cases at a workload's exact feature dimensions.
@@ -219,7 +226,7 @@ def make_inputs(
     st = np.float32 if w.dtype == "f32" else np.uint16
 
     normal = _normal
-    q_nope, q_rope = _queries(w, B, r_qn, r_qr, q_gain)
+    q_nope, q_rope = _queries(w, B, r_qn, r_qr, q_gain, num_queries)
     w_uk = to_storage(normal(r_wk, (NB, H, dn, dcb), dcb), w.dtype)
     w_uv = to_storage(normal(r_wv, (NB, H, dcb, dv), dcb), w.dtype)
 
@@ -270,7 +277,7 @@ def make_inputs(
             off += npages[b]
 
     return dict(
-        workload=w, seed=seed, q_gain=q_gain,
+        workload=w, seed=seed, q_gain=q_gain, num_queries=num_queries,
         dtype=w.dtype, paged=paged, page_size=PAGE if paged else 0,
         q_nope=q_nope, q_rope=q_rope, cache=cache, row_pos=row_pos.reshape(-1),
         seqlens=lens, block_table=block_table, w_uk=w_uk, w_uv=w_uv,
@@ -300,8 +307,9 @@ def make_variant_inputs(inp: dict, *, seed: Optional[int] = None, gate_std: floa
     B = len(inp["seqlens"])
     seed = inp["seed"] + 7919 if seed is None else seed
     r_g, r_q = (np.random.default_rng(k) for k in np.random.SeedSequence(seed).spawn(2))
-    gate = r_g.standard_normal((B, w.heads, w.d_v), dtype=np.float32) * np.float32(gate_std)
-    q_lat = _normal(r_q, (B, w.heads, w.branches * w.d_cb), w.d_cb, inp.get("q_gain", 1.0))
+    rows = inp.get("num_queries", 1) * w.heads
+    gate = r_g.standard_normal((B, rows, w.d_v), dtype=np.float32) * np.float32(gate_std)
+    q_lat = _normal(r_q, (B, rows, w.branches * w.d_cb), w.d_cb, inp.get("q_gain", 1.0))
     return {"gate": to_storage(gate, w.dtype), "q_latent": to_storage(q_lat, w.dtype)}
 
 

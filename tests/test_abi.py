@@ -54,12 +54,27 @@ def test_probe_library_exports_its_header(lib):
     assert probe.mla_probe_read(FAKE, 24, FAKE, None) == 1
 
 
-def test_params_struct_layout_matches_header():
-    # 14 int32, 5 int64, 3 float -> 56 + 40 + 12 = 108, padded to 112
-    assert ctypes.sizeof(B.MlaParams) == 112
+def test_params_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror has the size and field offsets the C compiler gives the header's
+    struct (a small C program prints them)."""
+    # 16 int32, 5 int64, 3 float -> 64 + 40 + 12 = 116, padded to 120
+    assert ctypes.sizeof(B.MlaParams) == 120
     assert B.MlaParams.flags.offset == 48 and B.MlaParams.num_pages.offset == 52
-    assert B.MlaParams.latent_stride_tok.offset == 56
-    assert B.MlaParams.softmax_scale.offset == 96
+    assert B.MlaParams.num_queries.offset == 56 and B.MlaParams.latent_stride_tok.offset == 64
+    assert B.MlaParams.softmax_scale.offset == 104
+    names = [f[0] for f in B.MlaParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mla_decode.h"\n'
+                   "int main(void) {\n"
+                   '  printf("%zu\\n", sizeof(mla_params));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(mla_params, {n}));\n' for n in names)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got == [ctypes.sizeof(B.MlaParams)] + [getattr(B.MlaParams, n).offset for n in names]
 
 
 def params_for(wname, **over):
@@ -98,6 +113,9 @@ def call(lib, p, fn="mla_decode", ws_bytes=1 << 40, **ptr):
     (dict(softmax_scale=float("nan")), 2),
     (dict(rope_theta=0.0), 2),
     (dict(num_splits=1000), 2),
+    (dict(num_queries=17), 2),
+    (dict(num_queries=-1), 2),
+    (dict(reserved=1), 2),
 ])
 def test_invalid_params_rejected(lib, over, status):
     p = params_for("mla_bf16_b32_h128_l4096", **over)
@@ -181,6 +199,21 @@ def test_folded_and_latent_flags_validation(lib):
     assert call(lib, params_for("mla_bf16_b32_h128_l4096", d_v=64, flags=OL), ws_bytes=1) == 4
     assert call(lib, params_for("tiny_mla_f32_b1_h4_l64", d_nope=999, flags=QL),
                 w_uk=None, ws_bytes=1) == 4
+
+
+def test_several_query_tokens_validation(lib):
+    """num_queries = s_q multiplies the query rows: accepted on every kernel family (the call
+    stops at the workspace check), with a workspace that grows with s_q; a head count whose
+    32-head groups would straddle two tokens is refused on bf16."""
+    p1 = params_for("mla_bf16_paged_b64_h32_l1k-32k")
+    p4 = params_for("mla_bf16_paged_b64_h32_l1k-32k", num_queries=4)
+    assert call(lib, p4, ws_bytes=1) == 4
+    assert B.workspace_size(p4) > B.workspace_size(p1)
+    assert call(lib, params_for("mlra4_bf16_b32_h32_l8192", num_queries=3), fn="mlra_decode",
+                ws_bytes=1) == 4
+    assert call(lib, params_for("tiny_mla_f32_b1_h4_l64", num_queries=16), ws_bytes=1) == 4
+    assert call(lib, params_for("mla_bf16_paged_b64_h32_l1k-32k", num_heads=16,
+                                num_queries=2)) == 3
 
 
 def test_gated_entry_points_validation(lib):
