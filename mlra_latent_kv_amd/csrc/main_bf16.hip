@@ -47,6 +47,19 @@ constexpr int kPPitch = kTT + 8;                     // bf16 probability row pit
 #ifndef MLA_NARROW_RING
 #define MLA_NARROW_RING 2
 #endif
+// Lazy softmax rescale: a head's running max is raised (and O, l rescaled) only when a tile's
+// max exceeds it by more than this many log2 units; otherwise the tile's weights are taken
+// against the stale max and stay below 2^kLazyTau (0: raise on every increase).
+#ifndef MLA_NARROW_LAZY
+#define MLA_NARROW_LAZY 8
+#endif
+constexpr float kLazyTau = MLA_NARROW_LAZY;
+// MLA path: weights taken speculatively against the running max before the halves' maxima
+// are exchanged (one LDS barrier per tile instead of two); a tile that raises some head's
+// max redoes its weights (0: always exchange the maxima first).
+#ifndef MLA_NARROW_SPEC
+#define MLA_NARROW_SPEC 1
+#endif
 template <int DC>
 constexpr int ring_depth() { return DC == 512 ? 2 : MLA_NARROW_RING; }
 
@@ -57,6 +70,7 @@ struct Smem {
   float mx[NB == 1 ? 2 * kHG : 1];            // MLA: per-head max of each 16-token half
   float sum[NB == 1 ? 2 * kHG : 1];           // MLA: per-head probability sum of each half
   float alpha[NB == 1 ? kHG : 1];             // MLA: per-head rescale of this tile
+  float mrun[NB == 1 ? kHG : 1];              // MLA: per-head running max (published)
   char gap[256];
   __attribute__((aligned(256))) char ring[ring_depth<DC>()][Geom<DC>::kBufBytes];
 };
@@ -153,6 +167,8 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
   wait_vmcnt<(kBufs - 2) * kIssues>();
 
   float m_run = -INFINITY, l_run = 0.0f;
+  if (NB == 1 && tb == 0 && g16 == 0) sm.mrun[16 * hb + l16] = -INFINITY;  // (ordered by the
+                                                                           // first tile's barrier)
   f32x16 O[kNOB];
 #pragma unroll
   for (int mb = 0; mb < kNOB; ++mb) O[mb] = f32x16{};
@@ -213,22 +229,64 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
       for (int e = 0; e < 4; ++e) acc[e] = tq + e < valid ? acc[e] : -INFINITY;
       float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
       mx = max_xor32(max_xor16(mx));
+      // weights of this wave's 16 tokens against m_ref, and their sum (normalised with the
+      // rounded weights the MFMA uses); -inf max only while every token so far is masked (a
+      // query token that sees none of this item's tokens yet): taken against 0, they are 0
+      bf16 pe[4];
+      float psum;
+      auto weights = [&](float m_ref) {
+        const float m_off = m_ref == -INFINITY ? 0.0f : m_ref;
+        psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pe[e] = (bf16)exp2f(acc[e] - m_off);
+          psum += (float)pe[e];
+        }
+        psum = sum_xor32(sum_xor16(psum));
+      };
+#if MLA_NARROW_SPEC
+      // speculative: against the running max, right unless some head's tile max passes it by
+      // more than kLazyTau.  Every wave then checks all 32 heads (its value-layout head l32)
+      // from the published maxima, so the (rare) redo is taken by the whole workgroup.
+      weights(m_run);
+      *(bf16x4*)(&sm.p[h * kPPitch + tq]) = bf16x4{pe[0], pe[1], pe[2], pe[3]};
+      if (g16 == 0) {
+        sm.mx[tb * kHG + h] = mx;
+        sm.sum[tb * kHG + h] = psum;
+      }
+      lds_barrier();
+      const bool raise_l = fmaxf(sm.mx[l32], sm.mx[kHG + l32]) > sm.mrun[l32] + kLazyTau;
+      if (__builtin_amdgcn_ballot_w64(raise_l)) {
+        mx = fmaxf(mx, sm.mx[(tb ^ 1) * kHG + h]);  // max over the tile's 32 tokens
+        const bool raise_h = mx > m_run + kLazyTau;  // the first tile with a token raises
+        const float m_new = raise_h ? mx : m_run;
+        const float a = raise_h ? exp2f(m_run - m_new) : 1.0f;
+        weights(m_new);
+        lds_barrier();  // every wave has read the speculative tile's maxima
+        *(bf16x4*)(&sm.p[h * kPPitch + tq]) = bf16x4{pe[0], pe[1], pe[2], pe[3]};
+        if (g16 == 0) {
+          sm.sum[tb * kHG + h] = psum;
+          if (tb == 0) {
+            sm.alpha[h] = a;
+            sm.mrun[h] = m_new;
+          }
+        }
+        lds_barrier();
+        l_run = a * l_run + psum + sm.sum[(tb ^ 1) * kHG + h];
+        m_run = m_new;
+        alpha = sm.alpha[l32];
+      } else {
+        l_run += psum + sm.sum[(tb ^ 1) * kHG + h];
+        alpha = 1.0f;
+      }
+#else
       if (g16 == 0) sm.mx[tb * kHG + h] = mx;
       lds_barrier();
       mx = fmaxf(mx, sm.mx[(tb ^ 1) * kHG + h]);  // max over the tile's 32 tokens
-      // -inf only while every token so far is masked (a query token that sees none of this
-      // item's tokens yet); the weights are then taken against 0 and come out 0
-      const float m_new = fmaxf(m_run, mx);
-      const float m_off = m_new == -INFINITY ? 0.0f : m_new;
-      const float a = exp2f(m_run - m_off);
-      bf16 pe[4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pe[e] = (bf16)exp2f(acc[e] - m_off);
-        psum += (float)pe[e];  // normalise with the rounded weights the MFMA uses
-      }
-      psum = sum_xor32(sum_xor16(psum));
+      const bool raise_h = mx > m_run + kLazyTau;  // lazy raise; the first tile raises
+      const float m_new = raise_h ? mx : m_run;
+      const float a = raise_h ? exp2f(m_run - m_new) : 1.0f;
+      weights(m_new);
       *(bf16x4*)(&sm.p[h * kPPitch + tq]) = bf16x4{pe[0], pe[1], pe[2], pe[3]};
       if (g16 == 0) {
         sm.sum[tb * kHG + h] = psum;
@@ -238,6 +296,7 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
       l_run = a * l_run + psum + sm.sum[(tb ^ 1) * kHG + h];
       m_run = m_new;
       alpha = sm.alpha[l32];
+#endif
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
         pb[s2] = lds_read16((const char*)&sm.p[l32 * kPPitch + 16 * s2 + 8 * kg]);
@@ -263,9 +322,10 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc[i]);
       mx = max_xor32(mx);
-      const float m_new = fmaxf(m_run, mx);
+      const bool raise_h = mx > m_run + kLazyTau;  // lazy raise, as above
+      const float m_new = raise_h ? mx : m_run;
       const float m_off = m_new == -INFINITY ? 0.0f : m_new;  // every token so far masked
-      alpha = exp2f(m_run - m_off);
+      alpha = raise_h ? exp2f(m_run - m_new) : 1.0f;
       float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -279,8 +339,10 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
     }
 
     // ---- O^T[d][h] += V^T P^T over this wave's DC / 4 latent columns
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // some head of the wave raised
 #pragma unroll
-    for (int mb = 0; mb < kNOB; ++mb) O[mb] *= alpha;
+      for (int mb = 0; mb < kNOB; ++mb) O[mb] *= alpha;
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
