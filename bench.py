@@ -290,6 +290,9 @@ def main():
                          "whose main loop is the same kernel")
     ap.add_argument("--num-queries", type=int, default=1,
                     help="query tokens per sequence decoded in one step (causal among them)")
+    ap.add_argument("--latent", choices=["bf16", "fp8"], default="bf16",
+                    help="latent cache format: bf16, or OCP FP8 E4M3 codes with a per-tensor "
+                         "scale (the rotary key stays bf16; compute stays bf16/fp32)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -323,11 +326,12 @@ def main():
         return
     w = I.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name}")
-    inp = I.make_inputs(w, num_queries=args.num_queries)
+    lf = "fp8" if args.latent == "fp8" else ""
+    inp = I.make_inputs(w, num_queries=args.num_queries, latent_format=lf)
     case = Hn.to_device(inp, num_splits=args.num_splits)
     torch.cuda.synchronize()
     lens = np.asarray(inp["seqlens"], np.int64)
-    cache_bytes = I.cache_bytes(w, lens)
+    cache_bytes = I.cache_bytes(w, lens, lf)
 
     step = case.run
     if args.variant != "none":
@@ -432,7 +436,8 @@ def main():
                    "paged": bool(inp["paged"]), "work_items": plan["items"],
                    "pages_per_item": plan["pages"],
                    "cache_flush": args.flush, "variant": args.variant,
-                   "query_tokens_per_seq": args.num_queries},
+                   "query_tokens_per_seq": args.num_queries,
+                   "latent_cache": "fp8_e4m3" if lf else w.dtype},
         "pct_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBPS, 2),
         "read_probe_GBps": round(probe_gbps, 1),
         "pct_read_probe": round(100 * value * 1e3 / probe_gbps, 2),
@@ -443,21 +448,21 @@ def main():
         "wall_s_timed_region": round(t_wall, 4),
         "flush_us": round(1e3 * statistics.mean(t_f), 2),
         "roofline": {
-            "kernel": main_kernel(w, args.num_queries),
+            "kernel": "k_main_bf16" if lf else main_kernel(w, args.num_queries),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes": int(cache_bytes),
-            "traffic": counters_traffic(w.name, args.num_queries),
+            "traffic": None if lf else counters_traffic(w.name, args.num_queries),
             "main_us": round(main_ms * 1e3, 2),
             "frac_of_read_probe": round(achieved / probe_gbps, 4),
             "empty_event_pair_us": round(pair_ms * 1e3, 2),
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and args.variant == "none" and args.num_queries == 1:
+    if not args.no_cpu_baseline and args.variant == "none" and args.num_queries == 1 and not lf:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -80,6 +80,15 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
  * not used (any value >= 1).  Not available with a gate. */
 #define MLA_FLAG_OUTPUT_LATENT 4
 
+/* mla_params.latent_format: the latent part of the cache (not the rotary key) is stored as
+ * OCP FP8 E4M3 codes ("e4m3fn": 4 exponent bits with bias 7, 3 mantissa bits, no infinity)
+ * with one per-tensor scale, latent_scale; the element strides of the latent cache then count
+ * bytes.  The rotary key, the queries, the weights and the output stay in dtype, which must
+ * be MLA_BF16.  The kernels widen the codes to bf16 exactly (E4M3 fits in bf16) and fold the
+ * scale into the absorbed query and the output scale; arithmetic is as for a bf16 cache.
+ * (Quantised latent caches: the yunthe MLA page, section 一.) */
+#define MLA_LATENT_FP8 1
+
 /* Error-word bits (workspace int32 hdr[4], written by every call). */
 #define MLA_DEVERR_SEQLEN 1   /* some seqlens[b] outside [0, max_seqlen]; clamped into it   */
 #define MLA_DEVERR_BLOCK 2    /* some used block_table entry outside [0, num_pages)         */
@@ -104,7 +113,8 @@ typedef struct mla_params {
                                  0 = not given (block ids are then not checked)            */
   int32_t num_queries;        /* s_q new tokens per sequence decoded in this step (0 or 1:
                                  one); see "Several query tokens" below                    */
-  int32_t reserved;           /* 0                                                         */
+  int32_t latent_format;      /* 0: the latent cache holds dtype elements; MLA_LATENT_FP8:
+                                 OCP FP8 E4M3 codes (see latent_scale)                     */
   int64_t latent_stride_tok;  /* elements between consecutive tokens of the latent cache   */
   int64_t latent_stride_seq;  /* contiguous: elements between sequences; paged: pages      */
   int64_t rope_stride_tok;    /* same two strides for the rotary-key cache                 */
@@ -113,6 +123,8 @@ typedef struct mla_params {
   float softmax_scale;        /* score scale, usually 1/sqrt(d_nope + d_rope)              */
   float out_scale;            /* scale on the (branch-summed) output: 1 MLA, 0.5 MLRA-4    */
   float rope_theta;           /* RoPE base, e.g. 10000                                     */
+  float latent_scale;         /* MLA_LATENT_FP8: latent value = decoded code * latent_scale
+                                 (finite, > 0); otherwise unused                           */
 } mla_params;
 
 /*
@@ -127,7 +139,8 @@ typedef struct mla_params {
  * num_splits is at most 512 and at most ceil(max_seqlen / 64).  flags holds only the
  * MLA_FLAG_* bits above; num_pages >= 0; 0 <= num_queries <= 16 (s_q * H must meet the
  * head rule, and every 32-head group must belong to one query token: H % 32 == 0 on bf16);
- * reserved == 0.  With MLA_FLAG_QUERY_LATENT the d_nope rule does not
+ * latent_format is 0 or MLA_LATENT_FP8 (bf16 only; latent pointer and strides then 16-byte
+ * aligned in bytes).  With MLA_FLAG_QUERY_LATENT the d_nope rule does not
  * apply, with MLA_FLAG_OUTPUT_LATENT the d_v rule does not.
  *
  * Split plan.  The attention over each sequence is split into work items of whole 64-token

@@ -24,6 +24,7 @@ PAGE_SIZE = 64
 MLA_FLAG_DEVICE_CHECKS = 1
 MLA_FLAG_QUERY_LATENT = 2
 MLA_FLAG_OUTPUT_LATENT = 4
+MLA_LATENT_FP8 = 1
 MLA_DEVERR_SEQLEN, MLA_DEVERR_BLOCK = 1, 2
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_UNSUPPORTED",
           4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_DTYPE", 6: "MLA_ERR_HIP", 7: "MLA_ERR_ALIGN"}
@@ -35,11 +36,12 @@ class MlaParams(ctypes.Structure):
         ("d_nope", c_int32), ("d_v", c_int32), ("d_latent", c_int32), ("d_rope", c_int32),
         ("page_size", c_int32), ("max_pages_per_seq", c_int32), ("max_seqlen", c_int32),
         ("num_splits", c_int32), ("dtype", c_int32), ("flags", c_int32), ("num_pages", c_int32),
-        ("num_queries", c_int32), ("reserved", c_int32),
+        ("num_queries", c_int32), ("latent_format", c_int32),
         ("latent_stride_tok", c_int64), ("latent_stride_seq", c_int64),
         ("rope_stride_tok", c_int64), ("rope_stride_seq", c_int64),
         ("block_table_stride", c_int64),
         ("softmax_scale", c_float), ("out_scale", c_float), ("rope_theta", c_float),
+        ("latent_scale", c_float),
     ]
 
     def copy(self) -> "MlaParams":

@@ -93,6 +93,7 @@ mla_status run_decode(int want_branches, const mla_params* p, const void* q_nope
   a.softmax_scale = p->softmax_scale;
   a.out_scale = p->out_scale;
   a.rope_theta = p->rope_theta;
+  a.latent_scale = plan.f8 ? p->latent_scale : 1.0f;
   char* ws = static_cast<char*>(workspace);
   a.plan = plan_args(plan, seqlens, workspace);
   a.work = a.plan.work;

@@ -45,7 +45,8 @@ template <bool LQ>
 __global__ __launch_bounds__(256) void k_prologue_bf16(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
     const int32_t* __restrict__ seqlens, const bf16* __restrict__ w_uk, bf16* __restrict__ qcat,
-    int B, int H, int NB, int dcb, float qscale, RopeFreq rf, PlanArgs plan, int Hw, int sq) {
+    int B, int H, int NB, int dcb, float qscale, float qscale_lat, RopeFreq rf, PlanArgs plan,
+    int Hw, int sq) {
   constexpr int dn = 128, dr = 64;
   __shared__ __align__(16) bf16 sW[dn * kPPitch];
   const int h = blockIdx.x, b0 = blockIdx.y * kRows, cb = blockIdx.z;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
         const bf16x8 v = *(const bf16x8*)(q_nope + bh * dc + col);
         bf16x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[e] * qscale);
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[e] * qscale_lat);
         *(bf16x8*)(qcat + bh * row + col) = o;
       }
     }
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void k_prologue_bf16(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int bb = b0 + 8 * (i >> 2) + 4 * kg + (i & 3);
-      if (bb < B) qcat[((size_t)bb * H + h) * row + col] = (bf16)(acc[i] * qscale);
+      if (bb < B) qcat[((size_t)bb * H + h) * row + col] = (bf16)(acc[i] * qscale_lat);
     }
   }
 #pragma unroll
@@ -154,7 +155,8 @@ hipError_t launch_prologue_bf16(const Plan& p, const DecodeArgs& a, hipStream_t 
   hipLaunchKernelGGL(p.latent_q ? k_prologue_bf16<true> : k_prologue_bf16<false>, grid,
                      dim3(256), 0, s, (const bf16*)a.q_nope,
                      (const bf16*)a.q_rope, a.seqlens, (const bf16*)a.w_uk, (bf16*)a.qcat, p.B,
-                     p.H, p.NB, p.dcb, a.softmax_scale * kLog2e, rf, a.plan, p.Hw, p.sq);
+                     p.H, p.NB, p.dcb, a.softmax_scale * kLog2e,
+                     a.softmax_scale * kLog2e * a.latent_scale, rf, a.plan, p.Hw, p.sq);
   return hipGetLastError();
 }
 
@@ -506,7 +508,7 @@ hipError_t launch_combine_epilogue_bf16(const Plan& p, const DecodeArgs& a, hipS
                            : combine_epilogue_kernel<false>(p.dc, R);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, (const bf16*)a.part_o, a.part_ml,
                      a.split_off, (const bf16*)a.w_uv, (const bf16*)a.gate, (bf16*)a.out, p.B,
-                     p.H, p.NB, p.dcb, a.out_scale, p.Hw);
+                     p.H, p.NB, p.dcb, a.out_scale * a.latent_scale, p.Hw);
   return hipGetLastError();
 }
 

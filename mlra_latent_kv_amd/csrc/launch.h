@@ -22,6 +22,7 @@ struct DecodeArgs {
   const void* gate;  // [B][H][d_v] gate logits of the gated entry points, else null
   int64_t lat_tok, lat_seq, rope_tok, rope_seq, bt_stride;
   float softmax_scale, out_scale, rope_theta;
+  float latent_scale;  // value of one latent unit: the fp8 latent's scale, else 1
   // workspace regions
   PlanArgs plan;    // split plan, written by the prologue launch
   const int32_t* work;       // [slots][4]: b, t_begin, t_end, item of the slot's first item

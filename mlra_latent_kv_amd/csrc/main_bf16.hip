@@ -63,8 +63,21 @@ constexpr float kLazyTau = MLA_NARROW_LAZY;
 template <int DC>
 constexpr int ring_depth() { return DC == 512 ? 2 : MLA_NARROW_RING; }
 
-// Exchange buffers first, then the tile ring on a 256-byte boundary.
-template <int NB, int DC>
+// 8-byte LDS read of staged codes, through a restrict pointer like every other tile read (so
+// that the wait analysis does not take it for a read of the loads in flight)
+__device__ __forceinline__ uint2 lds_read8u(const char* __restrict__ p) {
+  return *reinterpret_cast<const uint2*>(p);
+}
+
+// fp8 latent (F8): a tile arrives as E4M3 latent rows (DC bytes each, unswizzled) followed by
+// the bf16 rotary rows (swizzled as in the widened tile) in one of two staging slots, and is
+// widened once per workgroup into the single bf16 tile buffer the compute reads.
+template <int DC>
+constexpr int stage_bytes() { return kTT * DC + kTT * kRopeRowB; }
+
+// Exchange buffers first, then the tile ring on a 256-byte boundary (F8: one widened tile,
+// then the two staging slots).
+template <int NB, int DC, bool F8>
 struct Smem {
   bf16 p[NB == 1 ? kHG * kPPitch : 8];        // MLA: probabilities [h][t]
   float mx[NB == 1 ? 2 * kHG : 1];            // MLA: per-head max of each 16-token half
@@ -72,10 +85,11 @@ struct Smem {
   float alpha[NB == 1 ? kHG : 1];             // MLA: per-head rescale of this tile
   float mrun[NB == 1 ? kHG : 1];              // MLA: per-head running max (published)
   char gap[256];
-  __attribute__((aligned(256))) char ring[ring_depth<DC>()][Geom<DC>::kBufBytes];
+  __attribute__((aligned(256))) char ring[F8 ? 1 : ring_depth<DC>()][Geom<DC>::kBufBytes];
+  __attribute__((aligned(256))) char stage[F8 ? 2 : 1][F8 ? stage_bytes<DC>() : 16];
 };
 
-template <int NB, int DC>
+template <int NB, int DC, bool F8>
 __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_main_bf16(
     const bf16* __restrict__ qcat, const bf16* __restrict__ latent,
     const bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
@@ -84,11 +98,13 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
     int n_hg, const int32_t* __restrict__ seqlens, int max_seqlen, int sq, int Hw) {
   static_assert(NB == 1 || DC == 512, "MLRA-4 rows hold four 128-wide branches");
   using G = Geom<DC>;
-  constexpr int kBufs = ring_depth<DC>();
+  // tiles in flight + compute: the bf16 ring, or (F8) the two staging slots
+  constexpr int kBufs = F8 ? 2 : ring_depth<DC>();
   constexpr int kIssues = issues_per_wave<4, DC>(true);  // tile loads per wave per tile
+  static_assert(!F8 || kBufs == 2, "the fp8 path waits for each tile with vmcnt(0)");
   constexpr int kRowW = DC + kDR;   // cached (and absorbed-query) row width
   constexpr int kNOB = DC / 128;    // 32-column output blocks per wave
-  __shared__ __align__(16) Smem<NB, DC> sm;
+  __shared__ __align__(16) Smem<NB, DC, F8> sm;
 
   // XCD-aware mapping: consecutive blocks go to different XCDs, so the head groups of one
   // dispatch slot (one work item) are placed 8 blocks apart -> same XCD, dispatched back to
@@ -113,7 +129,7 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
 
   // Tile loads: wave w brings latent rows 8w..8w+7 and the rotary keys of the same rows
   // (chunk-swizzled through the per-lane source offsets).
-  const uint32_t lat_row_b = (uint32_t)(lat_tok * 2), rope_row_b = (uint32_t)(rope_tok * 2);
+  const uint32_t lat_row_b = (uint32_t)(lat_tok * (F8 ? 1 : 2)), rope_row_b = (uint32_t)(rope_tok * 2);
 
   // tile k of the item into its ring buffer.  Past the item's end (k >= n_tiles) the same
   // loads go out with an empty buffer descriptor: they return zeros without touching memory,
@@ -122,19 +138,62 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
   auto issue = [&](int k) {
     const int t0 = t_begin + kTT * k;
     const int valid = k < n_tiles ? min(kTT, t_end - t0) : 0;
-    const bf16* lb = latent;
+    // latent element size: 2 bytes, or 1 for E4M3 codes (lat_tok / lat_seq count elements)
+    constexpr int kLe = F8 ? 1 : 2;
+    const char* lb = reinterpret_cast<const char*>(latent);
     const bf16* rb = rope;
     if (valid == 0) {
     } else if (paged) {
       const int64_t pg = bt[(int64_t)b * bt_stride + t0 / kPage];
-      lb = latent + pg * lat_seq + (int64_t)(t0 % kPage) * lat_tok;
+      lb += kLe * (pg * lat_seq + (int64_t)(t0 % kPage) * lat_tok);
       rb = rope + pg * rope_seq + (int64_t)(t0 % kPage) * rope_tok;
     } else {
-      lb = latent + (int64_t)b * lat_seq + (int64_t)t0 * lat_tok;
+      lb += kLe * ((int64_t)b * lat_seq + (int64_t)t0 * lat_tok);
       rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
     }
-    issue_tile<Sw32, 4, DC>(sm.ring[k % kBufs], w, lane, lb, rb,
-                            __builtin_amdgcn_readfirstlane(valid), lat_row_b, rope_row_b);
+    const int vu = __builtin_amdgcn_readfirstlane(valid);
+    if constexpr (F8) {
+      // E4M3 latent rows, row-major in the slot (one instruction = 1 KiB = 1024 / DC rows),
+      // then the bf16 rotary rows 8w .. 8w + 7 swizzled as in the widened tile
+      char* slot = sm.stage[k % kBufs];
+      constexpr int kRowsPerLd = 1024 / DC, kCpr = DC / 16, kLd = kTT / kRowsPerLd / 4;
+      const __amdgpu_buffer_rsrc_t rl = rsrc(lb, vu * lat_row_b);
+#pragma unroll
+      for (int j = 0; j < kLd; ++j) {
+        const int r0 = (kLd * w + j) * kRowsPerLd, t = r0 + lane / kCpr;
+        dma16(rl, slot + r0 * DC, t * lat_row_b + 16 * (lane % kCpr));
+      }
+      const __amdgpu_buffer_rsrc_t rr = rsrc(rb, vu * rope_row_b);
+      const int rt = 8 * w + (lane >> 3);
+      dma16(rr, slot + kTT * DC + w * 1024, rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
+    } else {
+      issue_tile<Sw32, 4, DC>(sm.ring[k % kBufs], w, lane, reinterpret_cast<const bf16*>(lb), rb,
+                              vu, lat_row_b, rope_row_b);
+    }
+  };
+  // F8: widen the staged tile k (slot k % 2) into the bf16 tile buffer: every 8 E4M3 codes of
+  // a latent row become one 16-byte chunk at its swizzled place (exact: E4M3 fits in bf16),
+  // and the rotary rows are copied as they are (already in the buffer's layout)
+  auto widen = [&](int k) {
+    const char* slot = sm.stage[k % kBufs];
+    char* dst = sm.ring[0];
+    constexpr int kPieces = DC / 8;  // 8-code pieces per row
+#pragma unroll
+    for (int i = 0; i < kTT * kPieces / kThreads; ++i) {
+      const int u = tid + kThreads * i, row = u / kPieces, c = u % kPieces;
+      const uint2 v = lds_read8u(slot + row * DC + 8 * c);
+      const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, false);
+      const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, true);
+      const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, false);
+      const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, true);
+      lds_write16(dst + lat_chunk<Sw32, DC>(row, c),
+                  bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]});
+    }
+#pragma unroll
+    for (int i = 0; i < kTT * kRopeRowB / 16 / kThreads; ++i) {
+      const int u = tid + kThreads * i;
+      lds_write16(dst + G::kRopeOff + 16 * u, lds_read16(slot + kTT * DC + 16 * u));
+    }
   };
 
   // absorbed query as the MFMA B operand (N = heads).
@@ -194,11 +253,16 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
     // barrier it has landed for every wave, and tile k - 1's buffer is free for k + kBufs - 1
     wait_vmcnt<(kBufs - 2) * kIssues>();
     lds_barrier();
+    // F8: slot k -> the bf16 buffer (every wave is done with tile k - 1), before the next
+    // tile's loads go out: read after them, the staged codes would be waited on together
+    // with those loads (the wait analysis cannot tell the two slots apart)
+    if constexpr (F8) widen(k);
     issue(k + kBufs - 1);
+    if constexpr (F8) lds_barrier();  // the widened tile is complete
 
     const int t0 = t_begin + kTT * k;
     const int valid = min(kTT, t_lim - t0);  // <= 0: every score of the tile masked
-    const char* buf = sm.ring[k % kBufs];
+    const char* buf = sm.ring[F8 ? 0 : k % kBufs];
 
     bf16x8 pb[2];
     float alpha;
@@ -394,8 +458,10 @@ __global__ __launch_bounds__(kThreads, DC == 512 ? 2 : kNarrowWgPerCu) void k_ma
 
 hipError_t launch_main_bf16(const Plan& p, const DecodeArgs& a, hipStream_t s) {
   const unsigned blocks = (unsigned)(p.slots * p.n_hg);
-  auto kern = p.NB == 4 ? k_main_bf16<4, 512> : p.dcb == 512 ? k_main_bf16<1, 512>
-                                                             : k_main_bf16<1, 128>;
+  auto kern = p.f8 ? (p.NB == 4 ? k_main_bf16<4, 512, true> : p.dcb == 512 ? k_main_bf16<1, 512, true>
+                                                                           : k_main_bf16<1, 128, true>)
+                   : (p.NB == 4 ? k_main_bf16<4, 512, false> : p.dcb == 512 ? k_main_bf16<1, 512, false>
+                                                                            : k_main_bf16<1, 128, false>);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, s, (const bf16*)a.qcat,
                      (const bf16*)a.latent, (const bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok,
                      a.rope_seq, a.work, a.block_table, a.bt_stride, p.paged, (bf16*)a.part_o,

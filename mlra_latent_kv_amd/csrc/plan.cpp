@@ -22,9 +22,12 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   if (p->dtype != MLA_F32 && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (p->batch < 1 || p->num_heads < 1 || p->num_branches < 1 || p->d_nope < 1 || p->d_v < 1 ||
       p->d_latent < 1 || p->d_rope < 2 || (p->d_rope & 1) || p->max_seqlen < 0 ||
-      p->num_splits < 0 || p->num_pages < 0 || p->num_queries < 0 || p->num_queries > 16 ||
-      p->reserved != 0)
+      p->num_splits < 0 || p->num_pages < 0 || p->num_queries < 0 || p->num_queries > 16)
     return MLA_ERR_SHAPE;
+  if (p->latent_format != 0 && p->latent_format != MLA_LATENT_FP8) return MLA_ERR_DTYPE;
+  if (p->latent_format == MLA_LATENT_FP8 &&
+      (p->dtype != MLA_BF16 || !std::isfinite(p->latent_scale) || !(p->latent_scale > 0.0f)))
+    return p->dtype != MLA_BF16 ? MLA_ERR_UNSUPPORTED : MLA_ERR_SHAPE;
   if (p->flags & ~(MLA_FLAG_DEVICE_CHECKS | MLA_FLAG_QUERY_LATENT | MLA_FLAG_OUTPUT_LATENT))
     return MLA_ERR_SHAPE;
   if (p->batch > (1 << 20) || p->num_heads > 4096 || p->max_seqlen > (1 << 26))
@@ -55,6 +58,7 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   q.num_pages = q.paged ? p->num_pages : 0;
   q.latent_q = (p->flags & MLA_FLAG_QUERY_LATENT) ? 1 : 0;
   q.latent_out = (p->flags & MLA_FLAG_OUTPUT_LATENT) ? 1 : 0;
+  q.f8 = p->latent_format == MLA_LATENT_FP8 ? 1 : 0;
   // the folded forms leave out the dims of the product they skip
   const bool dn_ok = q.latent_q || q.dn == 128, dv_ok = q.latent_out || q.dv == 128;
 
@@ -69,7 +73,8 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
       return MLA_ERR_UNSUPPORTED;
     q.path = Path::kBf16Mfma;
     q.n_hg = q.H / kHeadGroup;
-    q.wide = mla && q.H % kWideHeads == 0;
+    // (an fp8 latent runs on the 32-head kernel, which widens each tile once in LDS)
+    q.wide = mla && q.H % kWideHeads == 0 && !q.f8;
   } else {
     if ((q.NB != 1 && q.NB != 4) || q.dc > 512 || q.dr > 64 || (!q.latent_q && q.dn > 256) ||
         (!q.latent_out && q.dv > 256))
@@ -83,8 +88,10 @@ mla_status make_plan(const mla_params* p, Plan* plan, int n_cu) {
   if (p->latent_stride_tok < q.dc || p->rope_stride_tok < q.dr || p->latent_stride_seq < 0 ||
       p->rope_stride_seq < 0)
     return MLA_ERR_SHAPE;
+  // 16-byte rows: 8 bf16 elements, or 16 fp8 codes for an fp8 latent
   if (p->dtype == MLA_BF16 &&
-      ((p->latent_stride_tok | p->latent_stride_seq | p->rope_stride_tok | p->rope_stride_seq) % 8))
+      ((p->latent_stride_tok | p->latent_stride_seq) % (q.f8 ? 16 : 8) ||
+       (p->rope_stride_tok | p->rope_stride_seq) % 8))
     return MLA_ERR_ALIGN;
   q.n_tiles = (int)std::max<int64_t>(1, ceil_div(q.max_seqlen, kPage));
   if (q.paged) {

@@ -41,6 +41,7 @@ struct Plan {
   int num_pages; // pool pages for the block-id check (0: not checked)
   int latent_q;  // MLA_FLAG_QUERY_LATENT: the query arrives folded (no W_UK product)
   int latent_out;  // MLA_FLAG_OUTPUT_LATENT: out is the latent-space output (no W_UV)
+  int f8;          // MLA_LATENT_FP8: the latent cache holds E4M3 codes (scale latent_scale)
   // Split plan.  The device cuts the batch into work items of whole pages, one per dispatch
   // slot (see plan_device.h); the host only bounds it.
   int target;        // slots the automatic plan fills (one workgroup set per CU slot)

@@ -34,10 +34,11 @@ class DeviceCase:
     out: torch.Tensor
     workspace: torch.Tensor
     branches: int
+    latent8: Optional[torch.Tensor] = None  # fp8 latent codes (MLA_LATENT_FP8), else None
 
     @property
     def latent_ptr(self) -> int:
-        return self.cache.data_ptr()
+        return self.cache.data_ptr() if self.latent8 is None else self.latent8.data_ptr()
 
     @property
     def rope_ptr(self) -> int:
@@ -110,6 +111,13 @@ def make_params(inp: dict, num_splits: int = 0, flags: int = 0) -> B.MlaParams:
     p.softmax_scale = inp["softmax_scale"]
     p.out_scale = inp["out_scale"]
     p.rope_theta = inp["rope_theta"]
+    if inp.get("latent_format") == "fp8":
+        # E4M3 codes in their own [rows, d_c] array: the latent strides count bytes
+        p.latent_format = B.MLA_LATENT_FP8
+        p.latent_scale = inp["latent_scale"]
+        lat_rows = inp["latent8"].shape[-2]  # tokens per sequence (contiguous) or per page
+        p.latent_stride_tok = w.d_c
+        p.latent_stride_seq = lat_rows * w.d_c
     return p
 
 
@@ -141,6 +149,8 @@ def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None,
                         dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=dev),
         workspace=torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev),
         branches=w.branches,
+        latent8=(torch.from_numpy(np.ascontiguousarray(inp["latent8"])).to(dev)
+                 if inp.get("latent_format") == "fp8" else None),
     )
     return case
 

@@ -110,6 +110,34 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+E4M3_MAX = 448.0  # largest finite OCP FP8 E4M3 ("e4m3fn") value
+
+
+def e4m3_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal, 2^-6 * m / 8; code 0x7f / 0xff is NaN; no infinities)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e, m = (b >> 3) & 15, b & 7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def f64_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest OCP FP8 E4M3 value (ties to the even code), saturating at
+    +-448; returns uint8 codes.  Inputs must be finite."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    # the code grid below 2^-6 is subnormal with spacing 2^-9; above, 3 mantissa bits
+    e = np.floor(np.log2(np.maximum(a, np.ldexp(1.0, -6))))
+    step = np.ldexp(1.0, (e - 3).astype(np.int64))
+    q = np.round(a / step) * step  # np.round: half to even on the grid index
+    grid = e4m3_bits_to_f64(np.arange(0x7f, dtype=np.uint8))  # 0 .. 448, increasing
+    idx = np.searchsorted(grid, q)
+    assert np.all(grid[np.minimum(idx, 0x7e)] == q), "rounded value off the E4M3 grid"
+    return (idx.astype(np.uint8) | np.where(x < 0, 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
 def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     x = np.asarray(x, dtype=np.float32)
     return x.copy() if dtype == "f32" else f32_to_bf16_bits(x)
@@ -189,11 +217,18 @@ def make_inputs(
     shuffle_pages: bool = True,
     max_seqlen: Optional[int] = None,
     num_queries: int = 1,
+    latent_format: str = "",
 ) -> dict:
     """Draw one seeded input set for workload ``w``.
 
     ``num_queries`` = s_q new tokens per sequence decoded in one step: the queries get
     s_q * H rows (token-major); everything else is unchanged.
+
+    ``latent_format="fp8"`` (bf16 workloads): the latent part of the cache is also stored as
+    OCP FP8 E4M3 codes ``latent8`` (the cache's row layout with d_c bytes per row) with one
+    per-tensor scale ``latent_scale`` = max |latent| / 448 over the stored rows, so that
+    latent = decode(latent8) * latent_scale; unused rows hold the NaN code.  The rotary
+    columns stay in ``cache`` (bf16).  ``oracle_cache`` gives the values the cache holds.
 
     Overrides (``batch``, ``seqlens``, ``paged``, ``q_gain``) give the small and
     "sharp" parity cases at a workload's exact feature dimensions.
@@ -276,7 +311,21 @@ def make_inputs(
                 row_pos[pg, :n] = np.arange(j * PAGE, j * PAGE + n, dtype=np.int32)
             off += npages[b]
 
+    extra = {}
+    if latent_format == "fp8":
+        if w.dtype != "bf16":
+            raise ValueError("an fp8 latent goes with the bf16 workloads")
+        lat = to_f64(cache[..., :dc], w.dtype).reshape(-1, dc)
+        used = row_pos.reshape(-1) >= 0
+        amax = float(np.abs(lat[used]).max()) if used.any() else 1.0
+        scale = np.float32(amax / E4M3_MAX if amax > 0 else 1.0)
+        codes = np.full(lat.shape, 0x7F, dtype=np.uint8)  # NaN code on unused rows
+        codes[used] = f64_to_e4m3_bits(lat[used] / np.float64(scale))
+        extra = dict(latent8=codes.reshape(cache.shape[:-1] + (dc,)), latent_scale=float(scale))
+    elif latent_format:
+        raise ValueError(f"unknown latent format {latent_format!r}")
     return dict(
+        **extra, latent_format=latent_format,
         workload=w, seed=seed, q_gain=q_gain, num_queries=num_queries,
         dtype=w.dtype, paged=paged, page_size=PAGE if paged else 0,
         q_nope=q_nope, q_rope=q_rope, cache=cache, row_pos=row_pos.reshape(-1),
@@ -286,9 +335,23 @@ def make_inputs(
     )
 
 
-def cache_bytes(w: Workload, seqlens: np.ndarray) -> int:
-    """Algorithmic latent-cache bytes one decode step reads: every cached row once."""
-    return int(np.asarray(seqlens, dtype=np.int64).sum()) * w.row * w.elem_bytes
+def oracle_cache(inp: dict) -> np.ndarray:
+    """The values the input set's cache holds, as float64 rows [latent | raw rotary key]: the
+    stored bf16 / fp32 rows, or, with an fp8 latent, its decoded codes times the scale next
+    to the stored rotary columns."""
+    w = inp["workload"]
+    c = to_f64(inp["cache"], w.dtype)
+    if inp.get("latent_format") == "fp8":
+        c = c.copy()
+        c[..., :w.d_c] = e4m3_bits_to_f64(inp["latent8"]) * np.float64(inp["latent_scale"])
+    return c
+
+
+def cache_bytes(w: Workload, seqlens: np.ndarray, latent_format: str = "") -> int:
+    """Algorithmic latent-cache bytes one decode step reads: every cached row once (with an
+    fp8 latent, 1 byte per latent element next to the bf16 rotary key)."""
+    per = w.d_c + w.d_rope * w.elem_bytes if latent_format == "fp8" else w.row * w.elem_bytes
+    return int(np.asarray(seqlens, dtype=np.int64).sum()) * per
 
 
 # ----------------------------------------------------------------------------- write side

@@ -115,7 +115,9 @@ def call(lib, p, fn="mla_decode", ws_bytes=1 << 40, **ptr):
     (dict(num_splits=1000), 2),
     (dict(num_queries=17), 2),
     (dict(num_queries=-1), 2),
-    (dict(reserved=1), 2),
+    (dict(latent_format=2), 5),
+    (dict(latent_format=1, latent_scale=0.0), 2),
+    (dict(latent_format=1, latent_scale=float("inf")), 2),
 ])
 def test_invalid_params_rejected(lib, over, status):
     p = params_for("mla_bf16_b32_h128_l4096", **over)
@@ -199,6 +201,26 @@ def test_folded_and_latent_flags_validation(lib):
     assert call(lib, params_for("mla_bf16_b32_h128_l4096", d_v=64, flags=OL), ws_bytes=1) == 4
     assert call(lib, params_for("tiny_mla_f32_b1_h4_l64", d_nope=999, flags=QL),
                 w_uk=None, ws_bytes=1) == 4
+
+
+def test_fp8_latent_validation(lib):
+    """MLA_LATENT_FP8: bf16 only, a finite positive scale, latent strides counted in bytes and
+    16-byte aligned; the call passes validation up to the workspace check."""
+    F8 = B.MLA_LATENT_FP8
+    p = params_for("mla_bf16_paged_b64_h32_l1k-32k", latent_format=F8, latent_scale=0.01,
+                   latent_stride_tok=512, latent_stride_seq=512 * 64)
+    assert call(lib, p, ws_bytes=1) == 4
+    assert call(lib, params_for("mlra4_bf16_b32_h32_l8192", latent_format=F8, latent_scale=0.5,
+                                latent_stride_tok=512, latent_stride_seq=512 * 8192),
+                fn="mlra_decode", ws_bytes=1) == 4
+    # 128 heads with an fp8 latent run on the 32-head kernel: accepted
+    assert call(lib, params_for("mla_bf16_b32_h128_l4096", latent_format=F8, latent_scale=1.0,
+                                latent_stride_tok=512, latent_stride_seq=512 * 4096),
+                ws_bytes=1) == 4
+    bad = p.copy()
+    bad.latent_stride_tok = 520  # 8 codes past a 16-byte boundary
+    assert call(lib, bad) == 7
+    assert call(lib, params_for("tiny_mla_f32_b1_h4_l64", latent_format=F8, latent_scale=1.0)) == 3
 
 
 def test_several_query_tokens_validation(lib):

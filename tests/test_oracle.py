@@ -971,3 +971,44 @@ def test_multi_planted_mistake_is_caught(monkeypatch, mistake):
             return real_rows(cache, b, max(0, L - 1) if L else 0, *a, **k)
         monkeypatch.setattr(O, "sequence_rows", bad)
     assert not _multi_pins_pass()
+
+
+# ----------------------------------------------------------------------------- fp8 latent storage
+# OCP FP8 E4M3 ("e4m3fn"): the storage format of an fp8 latent cache.  The decode feeds the
+# oracle the exact cached values; pinned here against the format's closed forms and a brute
+# force over its grid.
+
+def test_e4m3_decode_closed_forms():
+    d = I.e4m3_bits_to_f64
+    cases = {0x00: 0.0, 0x38: 1.0, 0x7e: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+             0x07: 7 * 2.0 ** -9, 0xc0: -2.0, 0x3c: 1.5, 0x46: 3.5, 0xfe: -448.0}
+    for code, val in cases.items():
+        assert d(np.array([code], np.uint8))[0] == val, hex(code)
+    assert np.isnan(d(np.array([0x7f, 0xff], np.uint8))).all()
+    neg0 = d(np.array([0x80], np.uint8))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) < 0
+    v = d(np.arange(0x7f, dtype=np.uint8))
+    assert np.all(np.diff(v) > 0)        # codes 0 .. 0x7e increase strictly
+    assert len(set(v.tolist())) == 127
+
+
+def test_e4m3_encode_is_nearest_with_ties_to_even():
+    grid = I.e4m3_bits_to_f64(np.arange(0x7f, dtype=np.uint8))
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(3000) * 30, rng.standard_normal(1000) * 0.01,
+                        (grid[:-1] + grid[1:]) / 2, -(grid[:-1] + grid[1:]) / 2,
+                        [500.0, -1e6, 0.0]])
+    got = I.e4m3_bits_to_f64(I.f64_to_e4m3_bits(x))
+    for xi, gi in zip(x, got):
+        a = min(abs(xi), 448.0)
+        dist = np.abs(grid - a)
+        best = np.flatnonzero(dist == dist.min())
+        k = best[0] if len(best) == 1 else best[best % 2 == 0][0]  # tie: the even code
+        assert abs(gi) == grid[k] and (gi == 0 or math.copysign(1.0, gi) == math.copysign(1.0, xi)), (xi, gi)
+
+
+def test_e4m3_round_trip_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7f, 0xff)], np.uint8)
+    v = I.e4m3_bits_to_f64(codes)
+    assert np.array_equal(I.e4m3_bits_to_f64(I.f64_to_e4m3_bits(v)), v)
+    assert I.e4m3_bits_to_f64(I.f64_to_e4m3_bits(np.array([1e9, -1e9])) ).tolist() == [448.0, -448.0]
