@@ -1,7 +1,8 @@
 /*
  * mla_decode.h - C ABI of the MI355X (gfx950) MLA / MLRA-4 latent-KV decode library.
  *
- * One decode step (one query token per sequence) of Multi-head Latent Attention over a
+ * One decode step (one new token per sequence, or a few: num_queries) of Multi-head Latent
+ * Attention over a
  * cache that holds, per token, only the compressed joint latent c_KV and a decoupled
  * rotary key ("超越 GQA 的推理革命…MLA…", sections 鍵值聯合低秩壓縮 and 解耦旋轉位置編碼).
  * The step is computed with matrix absorption (same page, section 矩陣吸收): W_UK is folded
@@ -16,9 +17,9 @@
  *  - Pointers named as device pointers must be device memory of the current HIP device;
  *    host pointers are read only during the call.
  *  - The caller owns every buffer, including out and workspace.  The library never
- *    allocates or frees memory, never synchronises the stream, and keeps no mutable
- *    global state; calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- *    stream) and may be made concurrently from several host threads.
+ *    allocates or frees memory and never synchronises the stream; calls are asynchronous
+ *    on `stream` (a hipStream_t; NULL = the default stream) and may be made concurrently from
+ *    several host threads (mla_decode_noalloc: see its note on overlapping calls).
  *  - Arguments are validated on the host before anything is launched; a failed check
  *    returns a non-zero mla_status and launches nothing.  Values that live in device memory
  *    (seqlens, block_table entries) are not validated by default: seqlens[b] must lie in
@@ -27,7 +28,8 @@
  *    mla_params.flags the device checks both and records what it finds in the error word of
  *    the workspace (see "Split plan" below).
  *  - Device properties (the compute-unit count that sizes the split plan) are queried once
- *    per device and cached; this is the only state the library keeps.
+ *    per device and cached; with mla_decode_noalloc's static scratch array and its cached
+ *    device address this is the only state the library keeps.
  *  - A kernel launch failure is reported as MLA_ERR_HIP.
  *  - No C++ exception crosses this interface.
  */
@@ -129,7 +131,8 @@ typedef struct mla_params {
 
 /*
  * Supported shapes in this build (anything else returns MLA_ERR_UNSUPPORTED):
- *  - MLA_BF16, NB = 1: d_latent = 512, d_rope = 64, d_nope = 128, d_v = 128, H % 32 == 0.
+ *  - MLA_BF16, NB = 1: d_latent = 512 (MLA) or 128 (one MLRA branch on its own, a
+ *    tensor-parallel shard of MLRA-4), d_rope = 64, d_nope = 128, d_v = 128, H % 32 == 0.
  *  - MLA_BF16, NB = 4: d_latent = 128, d_rope = 64, d_nope = 128, d_v = 128, H % 32 == 0.
  *  - MLA_F32 (generic SIMT path): NB in {1, 4}, NB*d_latent <= 512, d_rope even <= 64,
  *    d_nope <= 256, d_v <= 256, any H >= 1.
@@ -149,10 +152,11 @@ typedef struct mla_params {
  * lengths: with p_b = ceil(seqlens[b] / 64) pages, every sequence is cut into ceil(p_b / c)
  * items of c pages (the last one ragged; an empty sequence gets none), one item per dispatch
  * slot.  With num_splits = 0, c is the smallest page count for which the batch's items fit
- * the workgroups that fill the GPU once (one per compute unit for bf16 MLA with
- * H % 128 == 0, else two per compute unit divided by the workgroups per item; the device's
- * compute-unit count is queried once per device, at most 256); when no c does,
- * c = max_b p_b.  With num_splits = n, c = ceil(ceil(max_seqlen / 64) / n).
+ * the workgroups that fill the GPU once (one per compute unit for bf16 MLA whose query rows,
+ * s_q * H, are a multiple of 128 with a bf16 latent; four per compute unit for d_latent = 128
+ * with NB = 1; else two; divided by the workgroups per item, which is the query rows / 128 or
+ * / 32 on bf16 and the query rows on fp32; the device's compute-unit count is queried once
+ * per device, at most 256); when no c does, c = max_b p_b.  With num_splits = n, c = ceil(ceil(max_seqlen / 64) / n).
  * After a call has completed on its stream, the workspace starts with that plan (for
  * inspection; nothing reads it after the call):
  *   int32 hdr[8] at byte 0: { W = number of items, c, slots, item
