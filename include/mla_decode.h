@@ -371,6 +371,12 @@ typedef struct mla_append_params {
   int64_t latent_stride_tok, latent_stride_seq, rope_stride_tok, rope_stride_seq;
   int64_t block_table_stride;
   float rope_theta;
+  int32_t latent_format;      /* 0: latent rows in dtype; MLA_LATENT_FP8: the latent part is
+                                 written as OCP FP8 E4M3 codes of value / latent_scale
+                                 (nearest, ties to even, saturating at +-448; strides then
+                                 count bytes), for a cache mla_decode reads with the same
+                                 latent_format and latent_scale                            */
+  float latent_scale;         /* MLA_LATENT_FP8: finite, > 0                               */
 } mla_append_params;
 
 /* Workspace bytes mla_cache_append needs for *p (host pointer *bytes). */

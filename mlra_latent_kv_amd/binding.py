@@ -58,6 +58,7 @@ class MlaAppendParams(ctypes.Structure):
         ("latent_stride_tok", c_int64), ("latent_stride_seq", c_int64),
         ("rope_stride_tok", c_int64), ("rope_stride_seq", c_int64),
         ("block_table_stride", c_int64), ("rope_theta", c_float),
+        ("latent_format", c_int32), ("latent_scale", c_float),
     ]
 
 

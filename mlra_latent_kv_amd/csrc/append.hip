@@ -16,7 +16,8 @@
 //  * k_append_write: one workgroup per sequence: its four waves sum a quarter of the K-chunk
 //    partials each (loads of up to four chunks in flight at once), the sums meet in LDS, and
 //    the first wave rotates the rotary part at position t (angle reduced in fp64), rounds to
-//    bf16, takes its page and writes the row, then bumps the length.  Each sequence touches
+//    bf16 (the latent part of an fp8 cache: encodes it as E4M3 codes of value / scale), takes
+//    its page and writes the row, then bumps the length.  Each sequence touches
 //    only its own block-table entry and length, so the launch has no races.
 #include <climits>
 
@@ -131,12 +132,28 @@ __global__ __launch_bounds__(256) void k_append_proj(const bf16* __restrict__ hi
 // l + 64, ...; wave w sums the K-chunk partials kc = w, w + 4, ..., and the first wave adds
 // the four sums.  The rotary pairs (2k, 2k + 1) of the last 64 columns are lanes 2k and 2k + 1
 // of the last group.
+// OCP FP8 E4M3 code of x (nearest, ties to the even code, saturating at +-448; x finite):
+// below 2^-6 the grid is subnormal with step 2^-9, above it 3 mantissa bits, rounded on the
+// fp32 bit pattern
+__device__ __forceinline__ uint8_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a < 448.0f)) return (uint8_t)(sign | 0x7eu);
+  if (a < 0.015625f) return (uint8_t)(sign | (uint32_t)rintf(a * 512.0f));  // 0 .. 8
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t r = (u + 0x7ffffu + ((u >> 20) & 1u)) >> 20;  // exponent and 3 mantissa bits
+  const uint32_t code = r - ((127u - 7u) << 3);                // rebias 127 -> 7
+  return (uint8_t)(sign | (code > 0x7eu ? 0x7eu : code));
+}
+
+// F8: the latent part is written as E4M3 codes of value / latent_scale (latent counts bytes)
+template <bool F8>
 __global__ __launch_bounds__(256) void k_append_write(
     AppendWs ws, int32_t* __restrict__ seqlens, int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ free_pages, int n_free, bf16* __restrict__ latent,
+    const int32_t* __restrict__ free_pages, int n_free, void* __restrict__ latent,
     bf16* __restrict__ rope, int64_t lat_tok, int64_t lat_seq, int64_t rope_tok,
     int64_t rope_seq, int64_t bt_stride, int B, int dc, int n_kc, int page_size, int max_pages,
-    int capacity, RopeFreq rf) {
+    int capacity, RopeFreq rf, float latent_scale) {
   __shared__ float red[3][9][64];
   const int b = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ncol = dc + 64;
@@ -200,7 +217,12 @@ __global__ __launch_bounds__(256) void k_append_write(
   // latent columns
 #pragma unroll
   for (int i = 0; i < 9; ++i)
-    if (i < n_grp - 1) latent[slot_lat + 64 * i + lane] = (bf16)v[i];
+    if (i < n_grp - 1) {
+      if constexpr (F8)
+        static_cast<uint8_t*>(latent)[slot_lat + 64 * i + lane] = e4m3_code(v[i] / latent_scale);
+      else
+        static_cast<bf16*>(latent)[slot_lat + 64 * i + lane] = (bf16)v[i];
+    }
   // rotary columns (the last group): pair k = lane / 2 turned by t theta^(-2k/64)
   float x = 0.0f;
 #pragma unroll
@@ -229,10 +251,10 @@ hipError_t launch_append(const AppendPlan& p, const AppendArgs& a, hipStream_t s
   if (e != hipSuccess) return e;
   RopeFreq rf;
   make_rope_freq(64, a.rope_theta, &rf);
-  hipLaunchKernelGGL(k_append_write, dim3(p.B), dim3(256), 0, s, a.ws, a.seqlens, a.block_table,
-                     a.free_pages, a.n_free, (bf16*)a.latent, (bf16*)a.rope, a.lat_tok, a.lat_seq,
-                     a.rope_tok, a.rope_seq, a.bt_stride, p.B, p.dc, p.n_kc, p.page_size,
-                     p.max_pages, p.capacity, rf);
+  hipLaunchKernelGGL(p.f8 ? k_append_write<true> : k_append_write<false>, dim3(p.B), dim3(256),
+                     0, s, a.ws, a.seqlens, a.block_table, a.free_pages, a.n_free, a.latent,
+                     (bf16*)a.rope, a.lat_tok, a.lat_seq, a.rope_tok, a.rope_seq, a.bt_stride, p.B,
+                     p.dc, p.n_kc, p.page_size, p.max_pages, p.capacity, rf, p.latent_scale);
   return hipGetLastError();
 }
 

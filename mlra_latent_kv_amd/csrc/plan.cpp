@@ -210,6 +210,10 @@ mla_status make_append_plan(const mla_append_params* p, AppendPlan* plan) {
       !(p->rope_theta > 0.0f) || !std::isfinite(p->rope_theta))
     return MLA_ERR_SHAPE;
   if (p->page_size != 0 && p->page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (p->latent_format != 0 && p->latent_format != MLA_LATENT_FP8) return MLA_ERR_DTYPE;
+  if (p->latent_format == MLA_LATENT_FP8 &&
+      (!std::isfinite(p->latent_scale) || !(p->latent_scale > 0.0f)))
+    return MLA_ERR_SHAPE;
   // bf16, latent 512 (MLA, or MLRA-4's four 128-wide branches side by side) or 128 (one
   // branch), rotary key 64, d_model a multiple of 256 up to 65536
   if (p->dtype != MLA_BF16 || (p->d_latent != 512 && p->d_latent != 128) || p->d_rope != 64 ||
@@ -223,6 +227,8 @@ mla_status make_append_plan(const mla_append_params* p, AppendPlan* plan) {
   q.page_size = p->page_size;
   q.max_pages = p->max_pages_per_seq;
   q.capacity = p->capacity;
+  q.f8 = p->latent_format == MLA_LATENT_FP8 ? 1 : 0;
+  q.latent_scale = q.f8 ? p->latent_scale : 1.0f;
   if (q.page_size ? (q.max_pages < 1 || p->block_table_stride < q.max_pages) : q.capacity < 1)
     return MLA_ERR_SHAPE;
   if (p->latent_stride_tok < q.dc || p->rope_stride_tok < 64 || p->latent_stride_seq < 0 ||
@@ -255,7 +261,7 @@ mla_status check_append_call(const mla_append_params* p, const AppendPlan& plan,
   if (workspace_bytes < plan.bytes) return MLA_ERR_WORKSPACE;
   // hidden rows and weight rows are read 16 bytes at a time
   if (!aligned(hidden, 16) || !aligned(w_dkv, 16) || !aligned(w_kr, 16) ||
-      !aligned(latent, 2) || !aligned(rope, 2) || !aligned(seqlens, 4) ||
+      !aligned(latent, plan.f8 ? 1 : 2) || !aligned(rope, 2) || !aligned(seqlens, 4) ||
       !aligned(pages_used, 4) || !aligned(workspace, kWsAlign) ||
       (plan.page_size && !aligned(block_table, 4)) || (free_pages && !aligned(free_pages, 4)))
     return MLA_ERR_ALIGN;

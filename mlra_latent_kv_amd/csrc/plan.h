@@ -81,6 +81,8 @@ mla_status check_rope_rotate(const void* x, int64_t row_stride, const int32_t* p
 struct AppendPlan {
   int B, d_model, dc, ncol;   // ncol = dc + 64 output columns per row
   int page_size, max_pages, capacity;
+  int f8;                     // MLA_LATENT_FP8: latent written as E4M3 codes of value / latent_scale
+  float latent_scale;
   int n_cb, n_kc, n_rb;       // projection grid: column blocks of 128, K chunks of 256, row blocks of 32
   size_t off_part, off_rank, bytes;
 };

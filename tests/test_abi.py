@@ -388,9 +388,10 @@ def append_params(**over):
 
 def test_append_params_layout_and_workspace(lib):
     # 8 int32, 5 int64, 1 float -> 32 + 40 + 4 = 76, padded to 80
-    assert ctypes.sizeof(B.MlaAppendParams) == 80
+    assert ctypes.sizeof(B.MlaAppendParams) == 88
     assert B.MlaAppendParams.latent_stride_tok.offset == 32
     assert B.MlaAppendParams.rope_theta.offset == 72
+    assert B.MlaAppendParams.latent_format.offset == 76 and B.MlaAppendParams.latent_scale.offset == 80
     # fp32 partials [d_model / 256][B][d_latent + 64], then the page ranks [B]
     al = lambda x: (x + 255) // 256 * 256
     assert B.append_workspace_size(append_params()) == al(16 * 64 * 576 * 4) + al(64 * 4)
@@ -404,6 +405,8 @@ def test_append_params_layout_and_workspace(lib):
     (dict(d_rope=32), 3), (dict(page_size=16), 3), (dict(max_pages_per_seq=0), 2),
     (dict(block_table_stride=100), 2), (dict(page_size=0, capacity=0), 2),
     (dict(latent_stride_tok=500), 2),
+    (dict(latent_format=2), 5), (dict(latent_format=1, latent_scale=0.0), 2),
+    (dict(latent_format=1, latent_scale=float("nan")), 2),
 ])
 def test_append_invalid_params_rejected(lib, over, status):
     n = ctypes.c_size_t(0)

@@ -213,3 +213,157 @@ def test_append_steps_then_decode(wname):
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     note(f"  {wname}: append x{steps} then decode: max_abs={err:.3e} rel_l2={rel:.3e}")
     assert err <= 2e-2 and rel <= 1e-2
+
+
+# ----------------------------------------------------------------------------- fp8 latent
+# A cache whose latent part is OCP FP8 E4M3 codes (MLA_LATENT_FP8): the append encodes each
+# latent element as the nearest code of value / scale (ties to even, saturating).  The GPU row
+# is accumulated in fp32, so at a rounding tie its code may be the neighbour of the code of
+# the fp64 value; every code must be one of the two codes around the exact value, and almost
+# all must be the nearest.
+
+def _run_append_fp8(inp, seqlens, lat8, rope16, block_table, free, paged, dc, scale):
+    import torch
+    from mlra_latent_kv_amd import binding as Bd
+    B, d_model = inp["hidden"].shape
+    l8 = torch.from_numpy(np.ascontiguousarray(lat8)).cuda()
+    r = _dev(rope16)
+    sl = torch.tensor(np.asarray(seqlens, np.int32), device="cuda")
+    bt = None if block_table is None else torch.tensor(np.asarray(block_table, np.int32), device="cuda")
+    fr = torch.tensor(np.asarray(free, np.int32) if len(free) else np.zeros(1, np.int32), device="cuda")
+    used = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    rows = 64 if paged else lat8.shape[1]
+    p = _params(B, d_model, dc, dc + 64, paged, max_pages=0 if bt is None else bt.shape[1],
+                capacity=0 if paged else lat8.shape[1], bt_stride=0 if bt is None else bt.shape[1])
+    p.latent_stride_tok, p.latent_stride_seq = dc, dc * rows
+    p.rope_stride_tok, p.rope_stride_seq = 64, 64 * rows
+    p.latent_format, p.latent_scale = Bd.MLA_LATENT_FP8, scale
+    ws = torch.empty(Bd.append_workspace_size(p), dtype=torch.uint8, device="cuda")
+    Bd.mla_cache_append(p, _dev(inp["hidden"]), _dev(inp["w_dkv"]), _dev(inp["w_kr"]),
+                        l8.data_ptr(), r.data_ptr(), sl, bt, fr, len(free), used, ws)
+    torch.cuda.synchronize()
+    return (l8.cpu().numpy(), r.view(torch.int16).cpu().numpy().view(np.uint16), sl.cpu().numpy(),
+            None if bt is None else bt.cpu().numpy(), int(used.item()))
+
+
+def _check_codes(got_codes, exact, scale, what):
+    grid = I.e4m3_bits_to_f64(np.arange(0x7f, dtype=np.uint8))
+    want = I.f64_to_e4m3_bits(exact / scale)
+    got_v = I.e4m3_bits_to_f64(got_codes)
+    want_v = I.e4m3_bits_to_f64(want)
+    a = np.minimum(np.abs(exact / scale), 448.0)
+    lo = grid[np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 0x7e)]
+    hi = grid[np.clip(np.searchsorted(grid, a, side="left"), 0, 0x7e)]
+    mag = np.abs(got_v)
+    assert np.all((mag == lo) | (mag == hi)), (what, "a code outside the two around the value")
+    assert np.all((got_v == 0) | (np.sign(got_v) == np.sign(exact))), (what, "sign")
+    frac = float(np.mean(got_v == want_v))
+    note(f"  {what}: {got_codes.size} codes, nearest code in {100 * frac:.3f} %")
+    assert frac > 0.99
+
+
+@pytest.mark.parametrize("paged", [True, False], ids=["paged", "contiguous"])
+def test_append_fp8_latent_matches_oracle(paged):
+    rng = np.random.default_rng(21)
+    dc = 512
+    lens = [0, 5, 64, 63, 128, 1, 191, 33] * 2
+    B = len(lens)
+    inp = I.make_append_inputs(4096, dc, B, seed=31)
+    scale = 0.01
+    if paged:
+        max_pages, P = 4, 60
+        perm = rng.permutation(P)
+        bt = np.full((B, max_pages), -1, np.int64)
+        k = 0
+        for b, L in enumerate(lens):
+            for j in range(-(-L // 64)):
+                bt[b, j] = perm[k]
+                k += 1
+        free, rows_shape = list(perm[k:]), (P, 64)
+    else:
+        bt, free, rows_shape = None, [], (B, 200)
+    lat8 = rng.integers(0, 0x7e, size=rows_shape + (dc,), dtype=np.uint8)
+    rope16 = I.to_storage(rng.standard_normal(rows_shape + (64,)).astype(np.float32), "bf16")
+    got8, got_r, got_len, got_bt, got_used = _run_append_fp8(inp, lens, lat8, rope16, bt, free,
+                                                             paged, dc, scale)
+    ref = O.cache_append(I.to_f64(inp["hidden"], "bf16"), I.to_f64(inp["w_dkv"], "bf16"),
+                         I.to_f64(inp["w_kr"], "bf16"), lens, bt, free, theta=10000.0,
+                         page_size=64 if paged else 0, capacity=None if paged else rows_shape[1])
+    assert np.array_equal(got_len, ref["seqlens"]) and got_used == ref["pages_used"]
+    if paged:
+        assert np.array_equal(got_bt, ref["block_table"])
+    touched = np.zeros(rows_shape, bool)
+    codes, exact = [], []
+    for b, wh in enumerate(ref["where"]):
+        if wh is None:
+            continue
+        touched[wh] = True
+        codes.append(got8[wh])
+        exact.append(ref["rows"][b][:dc])
+        r = ref["rows"][b][dc:]
+        g = I.to_f64(got_r[wh], "bf16")
+        assert np.all(np.abs(g - r) <= 2.0 ** -8 * np.abs(r) + 1e-6 * np.abs(r).max())
+    _check_codes(np.stack(codes), np.stack(exact), scale, f"fp8 append {'paged' if paged else 'contiguous'}")
+    assert np.array_equal(got8[~touched], lat8[~touched]) and np.array_equal(got_r[~touched], rope16[~touched])
+
+
+def test_append_fp8_steps_then_decode():
+    """150 decode steps appended into an fp8-latent pool on the GPU, then the GPU decode of
+    that cache; against the oracle's append of the same tokens, its latent encoded with the
+    same scale by the host encoder, and its decode on the decoded values."""
+    import torch
+    from mlra_latent_kv_amd import binding as Bd
+    from mlra_latent_kv_amd import harness as Hn
+    w = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+    B, steps, d_model, dc = 3, 150, 512, 512
+    scale = 0.005
+    rng = np.random.default_rng(9)
+    pool_pages = 12
+    free = list(rng.permutation(pool_pages))
+    lat8 = torch.zeros((pool_pages, 64, dc), dtype=torch.uint8, device="cuda")
+    rope = torch.zeros((pool_pages, 64, 64), dtype=torch.bfloat16, device="cuda")
+    bt = torch.full((B, 4), -1, dtype=torch.int32, device="cuda")
+    sl = torch.zeros(B, dtype=torch.int32, device="cuda")
+    fr = torch.tensor(np.asarray(free, np.int32), device="cuda")
+    used = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = _params(B, d_model, dc, dc + 64, True, max_pages=4, bt_stride=4)
+    p.latent_stride_tok, p.latent_stride_seq = dc, dc * 64
+    p.rope_stride_tok, p.rope_stride_seq = 64, 64 * 64
+    p.latent_format, p.latent_scale = Bd.MLA_LATENT_FP8, scale
+    ws = torch.empty(Bd.append_workspace_size(p), dtype=torch.uint8, device="cuda")
+    hs = [I.make_append_inputs(d_model, dc, B, seed=300 + s) for s in range(steps)]
+    wdk, wkr = _dev(hs[0]["w_dkv"]), _dev(hs[0]["w_kr"])
+    head = 0
+    for s in range(steps):
+        Bd.mla_cache_append(p, _dev(hs[s]["hidden"]), wdk, wkr, lat8.data_ptr(), rope.data_ptr(),
+                            sl, bt, fr[head:], len(free) - head, used, ws)
+        head += int(used.item())
+    dec = I.make_inputs(w, seqlens=[steps] * B, q_gain=I.sharp_q_gain(w))
+    dp = Hn.make_params(dec)
+    dp.page_size, dp.max_pages_per_seq, dp.block_table_stride = 64, 4, 4
+    dp.latent_stride_tok, dp.latent_stride_seq = dc, dc * 64
+    dp.rope_stride_tok, dp.rope_stride_seq = 64, 64 * 64
+    dp.num_pages = pool_pages
+    dp.latent_format, dp.latent_scale = Bd.MLA_LATENT_FP8, scale
+    out = torch.empty((B, w.heads, w.d_v), dtype=torch.bfloat16, device="cuda")
+    dws = torch.empty(Bd.workspace_size(dp), dtype=torch.uint8, device="cuda")
+    Bd.mla_decode(dp, _dev(dec["q_nope"]), _dev(dec["q_rope"]), lat8.data_ptr(), rope.data_ptr(),
+                  sl, bt, _dev(dec["w_uk"]), _dev(dec["w_uv"]), out, dws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    f64 = lambda a: I.to_f64(a, "bf16")
+    raw = np.zeros((B, steps, dc + 64))
+    for s in range(steps):
+        r = O.cache_append(f64(hs[s]["hidden"]), f64(hs[0]["w_dkv"]), f64(hs[0]["w_kr"]),
+                           [s] * B, capacity=steps)
+        rows = r["rows"]
+        rows[:, :dc] = I.e4m3_bits_to_f64(I.f64_to_e4m3_bits(rows[:, :dc] / scale)) * scale
+        rows[:, dc:] = O.rope(rows[:, dc:], -s, w.rope_theta)  # back to the raw key
+        raw[:, s] = rows
+    ref = O.mla_decode(dec["q_nope"], dec["q_rope"], raw, [steps] * B, dec["w_uk"], dec["w_uv"],
+                       d_rope=64, scale=w.softmax_scale, out_scale=w.out_scale,
+                       theta=w.rope_theta, to_f64=lambda a: f64(a) if a.dtype == np.uint16 else a)
+    err = float(np.abs(got - ref).max())
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    note(f"  fp8 append x{steps} then decode: max_abs={err:.3e} rel_l2={rel:.3e}")
+    assert err <= 2e-2 and rel <= 1e-2
