@@ -15,7 +15,9 @@ back to back, as they would in a model.  A separate pass with ``mla_decode_timed
 gives per-stage times and the main-loop kernel time for the roofline: the HIP event pair
 the library records on its stream around the main-loop launch (nothing subtracted, so the
 figure includes the launch's own dispatch gap and is an upper bound on the kernel's run
-time; the rocprofv3 kernel-trace average of the same command is committed beside it).
+time).  The rocprofv3 kernel-trace average of the same kernel, from the committed summary
+taken on the current main-loop sources, is reported beside it with the fraction it gives
+(``trace_avg_us``, ``frac_trace``; null when the summary is stale).
 
 A read-stream probe (libmla_probe.so: 16-byte loads over 2 GiB, every byte once) gives the
 practical HBM read ceiling of the device in the same run, reported next to the 8 TB/s peak.
@@ -129,9 +131,10 @@ def main_kernel(w, num_queries: int = 1) -> str:
         else "k_main_bf16"
 
 
-def counters_traffic(workload: str, num_queries: int = 1):
-    """HBM bytes per main-kernel launch from the committed rocprofv3 counter summary, if it was
-    taken on the current main-loop source; else None."""
+def counters_entry(workload: str, num_queries: int = 1):
+    """The committed rocprofv3 summary of the main kernel for this workload (HBM bytes per
+    launch, kernel-trace average), if it was taken on the current main-loop source; else
+    None."""
     try:
         s = json.load(open(PMC_SUMMARY))
     except (OSError, ValueError):
@@ -139,7 +142,13 @@ def counters_traffic(workload: str, num_queries: int = 1):
     ent = s.get(workload if num_queries == 1 else f"{workload}@q{num_queries}")
     if not ent or ent.get("source_sha") != source_sha():
         return None
-    return ent.get("hbm_bytes_per_launch")
+    return ent
+
+
+def counters_traffic(workload: str, num_queries: int = 1):
+    """HBM bytes per main-kernel launch from the committed counter summary, else None."""
+    ent = counters_entry(workload, num_queries)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(inp, seconds: float):
@@ -416,6 +425,8 @@ def main():
         log(f"[bench] calibration copy kernel: {n} bytes read, {n} bytes written")
 
     value = cache_bytes / (ms * 1e-3) / 1e12
+    ent = None if lf or args.variant != "none" else counters_entry(w.name, args.num_queries)
+    trace_us = None if ent is None else ent.get("trace_avg_us")
     achieved = cache_bytes / (main_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -457,6 +468,11 @@ def main():
             "algorithmic_bytes": int(cache_bytes),
             "traffic": None if lf else counters_traffic(w.name, args.num_queries),
             "main_us": round(main_ms * 1e3, 2),
+            # the same kernel's rocprofv3 trace average from the committed summary (taken on
+            # these main-loop sources), and the fraction it gives; null when stale
+            "trace_avg_us": trace_us,
+            "frac_trace": None if trace_us is None else round(
+                cache_bytes / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "frac_of_read_probe": round(achieved / probe_gbps, 4),
             "empty_event_pair_us": round(pair_ms * 1e3, 2),
         },
