@@ -121,17 +121,23 @@ def source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def main_kernel(w, num_queries: int = 1) -> str:
+def main_kernel(w, num_queries: int = 1, fp8: bool = False) -> str:
     """Name of the kernel that runs the split-K main loop for workload w (its query rows are
-    num_queries tokens x heads)."""
+    num_queries tokens x heads; an fp8 latent always runs on the 32-head kernel)."""
     if w.dtype != "bf16":
         return "k_main_f32"
     rows = num_queries * w.heads
-    return "k_main_bf16_wide" if (w.branches == 1 and w.d_cb == 512 and rows % 128 == 0) \
-        else "k_main_bf16"
+    wide = w.branches == 1 and w.d_cb == 512 and rows % 128 == 0 and not fp8
+    return "k_main_bf16_wide" if wide else "k_main_bf16"
 
 
-def counters_entry(workload: str, num_queries: int = 1):
+def counters_key(workload: str, num_queries: int = 1, fp8: bool = False) -> str:
+    """Key of a run in the committed counter summary: the workload name, then @qN for N query
+    tokens per sequence and @fp8 for an fp8 latent cache."""
+    return workload + (f"@q{num_queries}" if num_queries != 1 else "") + ("@fp8" if fp8 else "")
+
+
+def counters_entry(workload: str, num_queries: int = 1, fp8: bool = False):
     """The committed rocprofv3 summary of the main kernel for this workload (HBM bytes per
     launch, kernel-trace average), if it was taken on the current main-loop source; else
     None."""
@@ -139,15 +145,15 @@ def counters_entry(workload: str, num_queries: int = 1):
         s = json.load(open(PMC_SUMMARY))
     except (OSError, ValueError):
         return None
-    ent = s.get(workload if num_queries == 1 else f"{workload}@q{num_queries}")
+    ent = s.get(counters_key(workload, num_queries, fp8))
     if not ent or ent.get("source_sha") != source_sha():
         return None
     return ent
 
 
-def counters_traffic(workload: str, num_queries: int = 1):
+def counters_traffic(workload: str, num_queries: int = 1, fp8: bool = False):
     """HBM bytes per main-kernel launch from the committed counter summary, else None."""
-    ent = counters_entry(workload, num_queries)
+    ent = counters_entry(workload, num_queries, fp8)
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
@@ -425,7 +431,7 @@ def main():
         log(f"[bench] calibration copy kernel: {n} bytes read, {n} bytes written")
 
     value = cache_bytes / (ms * 1e-3) / 1e12
-    ent = None if lf or args.variant != "none" else counters_entry(w.name, args.num_queries)
+    ent = None if args.variant != "none" else counters_entry(w.name, args.num_queries, bool(lf))
     trace_us = None if ent is None else ent.get("trace_avg_us")
     achieved = cache_bytes / (main_ms * 1e-3) / 1e9
     line = {
@@ -459,14 +465,15 @@ def main():
         "wall_s_timed_region": round(t_wall, 4),
         "flush_us": round(1e3 * statistics.mean(t_f), 2),
         "roofline": {
-            "kernel": "k_main_bf16" if lf else main_kernel(w, args.num_queries),
+            "kernel": main_kernel(w, args.num_queries, bool(lf)),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes": int(cache_bytes),
-            "traffic": None if lf else counters_traffic(w.name, args.num_queries),
+            "traffic": (None if args.variant != "none"
+                        else counters_traffic(w.name, args.num_queries, bool(lf))),
             "main_us": round(main_ms * 1e3, 2),
             # the same kernel's rocprofv3 trace average from the committed summary (taken on
             # these main-loop sources), and the fraction it gives; null when stale
