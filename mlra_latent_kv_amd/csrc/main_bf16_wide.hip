@@ -19,7 +19,10 @@
 //  * tiles of 32 tokens stream through a ring of 4 LDS buffers by direct-to-LDS loads, in a
 //    software pipeline: while tile k + 1 is scored, tile k's value MFMAs alternate with its
 //    score MFMAs, tile k + 1's softmax runs between tile k's last value MFMAs, and tiles
-//    k + 2 and k + 3 are in flight.
+//    k + 2 and k + 3 are in flight.  The value MFMAs form one stream across tile
+//    boundaries: tile k's first four run around the barrier that admits tile k + 1 (their
+//    operands were read behind tile k - 1's last value MFMAs), so the matrix cores stay busy
+//    through the barrier and the latency of tile k + 1's first score-operand reads.
 //  * scores S^T[t][h] = tile . q_cat^T (one accumulation chain over 36 K-steps of 16
 //    columns); the probabilities go register-direct into the value product
 //    O^T += V^T P^T (token order inside a K-step permuted to match the score layout; value
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     constexpr int kQkNear = 2;
     return t - (t >= v_start + kQkNear ? kQkNear : kQkAhead);
   };
-  auto scores = [&](f32x16& S, int v_start, auto&& mid) {
+  auto scores = [&](f32x16& S, int v_start, auto&& pre, auto&& mid) {
     auto a_tile = [&](int j) -> bf16x8 {
       return j < 32 ? lds_read16_at(qa[j & 7] + 256 * (j >> 3)) : lds_read16_at(ra[j - 32]);
     };
@@ -270,6 +273,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
 #pragma unroll
     for (int t = 0; t < kQSteps; ++t)
       if (read_at(t, v_start) < 0) aq[t % kQq] = a_tile(t);
+    __builtin_amdgcn_sched_barrier(0);
+    pre();  // work that covers the first operand reads' latency
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kQSteps; ++j) {
 #pragma unroll
@@ -385,44 +391,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
   };
 
   // ---- O^T[d][h] += V^T P^T over one tile (its buffer at pa), K-step-major over the 16
-  // column blocks, operands kPvAhead reads ahead; then pa moves on to the next buffer
-  // (the first kPvAhead operands are read by the caller, in the shadow of earlier work)
-  constexpr int kPvAhead = 4;
-  bf16x8 vq[kPvAhead + 1];
-  auto v_tile = [&](int i) -> bf16x8 {
+  // column blocks.  The value MFMAs of consecutive tiles form one stream that never stops
+  // at a tile boundary: tile k's first kFront MFMAs run around the barrier that admits tile
+  // k + 1 (two before it, two behind the first score-operand reads of tile k + 1, whose
+  // latency they cover), the next ones alternate with tile k + 1's score MFMAs, the rest
+  // hold tile k + 1's softmax in their gaps.  Operand i of a tile goes to register slot
+  // i % 4 and is read right after the value MFMA vsched(i) (a slot is refilled only after
+  // the MFMA that used it has issued): two value MFMAs ahead while they alternate with
+  // score MFMAs (each step is two MFMA slots), four ahead elsewhere, and the first kFront
+  // operands of the next tile behind the last four MFMAs of this one.
+  constexpr int kFront = 4;       // value MFMAs of tile k around the barrier of iteration k
+  constexpr int kFrontPre = 2;    // ... of which issued before it
+  bf16x8 vq[4];
+  // operand i of the tile whose buffer is at base pa (+ buffer offset off)
+  auto v_tile = [&](int i, int32_t off) -> bf16x8 {
     const int cb = i & 15, ks = i >> 4;
     const uint32_t o = 256 * (cb >> 2) + 16384 * ks;
-    return tr_pair_at(pa[0][cb & 3] + o, pa[1][cb & 3] + o);
+    return tr_pair_at(pa[0][cb & 3] + off + o, pa[1][cb & 3] + off + o);
   };
-  // value MFMA at which operand i is read: kPvAhead ahead, or kPvNear ahead for the first
-  // n_inter MFMAs (those alternating with score MFMAs, where each step is two MFMA slots);
-  // negative: read before the first value MFMA (value_pre)
-  auto vread_at = [](int i, int n_inter) {
-    constexpr int kPvNear = 2;
-    return i - (i < n_inter ? kPvNear : kPvAhead);
+  auto vsched = [](int i, int n_alt) {  // value MFMA after which operand i is read
+    return i < kFront ? -1 : i < kFront + n_alt ? i - 2 : i - 4;
   };
-  auto value_pre = [&](int g, int n_inter) {  // g = -kPvAhead .. -1
-#pragma unroll
-    for (int i2 = 0; i2 < kPvAhead; ++i2)
-      if (vread_at(i2, n_inter) == g) vq[i2 % (kPvAhead + 1)] = v_tile(i2);
-  };
-  // value MFMA i of the tile with weight set P
-  auto value_mfma = [&](int i, int P, int n_inter) {
+  // value MFMA i of tile kt with weight set P; n_alt MFMAs from kFront on alternate with score
+  // MFMAs; next: the stream continues with a tile after this one (its first operands are read
+  // here, after pa has moved on to its buffer)
+  auto value_mfma = [&](int i, int P, int kt, int n_alt, bool next) {
     const int ks = i >> 4;
     const bf16x8 pb =
         __builtin_bit_cast(bf16x8, u32x4{pw[P][ks][0], pw[P][ks][1], pw[P][ks][2], pw[P][ks][3]});
+    O[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i & 3], pb, O[i & 15], 0, 0, 0);
 #pragma unroll
-    for (int i2 = i + 1; i2 < 32 && i2 <= i + kPvAhead; ++i2)
-      if (vread_at(i2, n_inter) == i) vq[i2 % (kPvAhead + 1)] = v_tile(i2);
-    O[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i % (kPvAhead + 1)], pb, O[i & 15], 0, 0, 0);
-  };
-  auto values_end = [&](int kt, int P) {
-    l_run += sum_xor32(psum[P]);
-    const int32_t step = next_buf(kt);
+    for (int i2 = i + 1; i2 < 32 && i2 <= i + 4; ++i2)
+      if (vsched(i2, n_alt) == i) vq[i2 & 3] = v_tile(i2, 0);
+    if (i == 27) {  // every operand of this tile is read: move on to the next buffer
+      const int32_t step = next_buf(kt);
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
+      for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pa[rr][c] = opaque(pa[rr][c] + step);
+        for (int c = 0; c < 4; ++c) pa[rr][c] = opaque(pa[rr][c] + step);
+    }
+    if (next && i >= 32 - kFront) vq[(i + kFront) & 3] = v_tile(i + kFront - 32, 0);
   };
   auto advance_qk = [&](int kt) {  // score reads move on from tile kt's buffer
     const int32_t step = next_buf(kt);
@@ -432,15 +440,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     for (int j = 0; j < 4; ++j) ra[j] = opaque(ra[j] + step);
   };
 
-  // ---- software pipeline over the tiles.  Fill: tile 0's scores and softmax.  Iteration k:
-  // the score chain of tile k + 1, with tile k + 3's loads behind its first MFMAs and tile k's
-  // value MFMAs alternating with its MFMAs from gap kVStart on (so each stream's operand
-  // reads run twice as many MFMA slots ahead); then tile k's remaining value MFMAs, with tile
+  // ---- software pipeline over the tiles.  Fill: tile 0's scores and softmax, and the first
+  // operands of its values.  Iteration k: tile k's first value MFMAs around the barrier, the
+  // score chain of tile k + 1 with tile k + 3's loads behind its first MFMAs and tile k's
+  // value MFMAs alternating with its MFMAs from gap kVStart on (so each stream's operand reads
+  // run twice as many MFMA slots ahead); then tile k's remaining value MFMAs, with tile
   // k + 1's softmax in their gaps (its scores are complete by then); then the lazy rescale.
   // The ring holds tile k (values), tile k + 1 (scores) and tiles k + 2, k + 3 (in flight).
-  // score gap of tile k's first value MFMA: later starts leave more tail gaps for the
-  // softmax but fewer alternating pairs (13, 17, 21, 25, 29 timed; 21 best overall)
-  constexpr int kVStart = 21;
+  // score gap of the first alternating value MFMA: later starts leave more tail gaps for the
+  // softmax but fewer alternating pairs
+  constexpr int kVStart = 25;
+  constexpr int kAlt = kQSteps - kVStart;  // value MFMAs alternating with score MFMAs
   // tail gap (1 .. gaps) of softmax piece q, by cumulative issue cost (cycles, measured
   // beside MFMAs: v_exp ~12, v_cvt_pk ~8, plain VALU ~6)
   auto soft_gap = [](int q, int gaps) {
@@ -452,32 +462,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     }
     return 1 + before * gaps / total;
   };
-  constexpr int kTail = 32 - (kQSteps - kVStart);  // value MFMAs after the score chain
-  static_assert(kTail >= 1 && kVStart >= kPvAhead, "value schedule");
+  constexpr int kTail = 32 - kFront - kAlt;  // value MFMAs after the score chain
+  static_assert(kTail >= 8 && kVStart >= 2 * kIssues, "value schedule");
   lds_barrier();  // tile 0 landed for every wave
   f32x16 S;
-  scores(S, kQSteps, [](int) {});
+  scores(S, kQSteps, [] {}, [](int) {});
   advance_qk(0);
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 11");  // the last score MFMA's result, before the first VALU read of S
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 0; q < kSoftPieces; ++q) soft_piece(S, 0, 0, q);
+#pragma unroll
+  for (int i = 0; i < kFront; ++i) vq[i] = v_tile(i, 0);
   auto step = [&](int k, int P) {  // P = k & 1
+#pragma unroll
+    for (int i = 0; i < kFrontPre; ++i) {
+      value_mfma(i, P, k, kAlt, true);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // page of the tile issued below, read before the barrier (whose lgkmcnt(0) covers it) so
     // that no scalar load is in flight during the tile's LDS reads: scalar and LDS reads
     // share one counter and a pending scalar load would force every LDS wait to zero
     const int32_t pg = page_or0(k + 3);
     wait_vmcnt<kIssues>();  // tile k + 1 is done; only tile k + 2's loads may be out
     lds_barrier();    // tile k + 1 landed for every wave; tile k - 1's buffer is free
-    scores(S, kVStart, [&](int j) {
-      // the loads of tile k + 3 (into tile k - 1's buffer) go out one per gap behind score
-      // MFMAs 1..9 (issued back to back they would stall the wave for ~200 cycles; with two
-      // tiles in flight their latency has room)
-      if (j >= 1 && j <= kIssues) issue(k + 3, pg, j - 1);
-      if (j >= kVStart - kPvAhead && j < kVStart) value_pre(j - kVStart, kQSteps - kVStart);
-      if (j >= kVStart) value_mfma(j - kVStart, P, kQSteps - kVStart);
-    });
+    scores(
+        S, kVStart,
+        [&] {
+#pragma unroll
+          for (int i = kFrontPre; i < kFront; ++i) {
+            value_mfma(i, P, k, kAlt, true);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        },
+        [&](int j) {
+          // the loads of tile k + 3 (into tile k - 1's buffer) go out one per gap behind
+          // score MFMAs 1..9 (issued back to back they would stall the wave for ~200 cycles;
+          // with two tiles in flight their latency has room)
+          if (j >= 1 && j <= kIssues) issue(k + 3, pg, j - 1);
+          if (j >= kVStart) value_mfma(j - kVStart + kFront, P, k, kAlt, true);
+        });
     advance_qk(k + 1);
     // tail: tile k's last value MFMAs; tile k + 1's softmax in their gaps, from the second
     // gap on (the first gives the last score MFMA's result its 12 wait states), each piece
@@ -485,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     // MFMA covers)
 #pragma unroll
     for (int i = 32 - kTail; i < 32; ++i) {
-      value_mfma(i, P, kQSteps - kVStart);
+      value_mfma(i, P, k, kAlt, true);
       __builtin_amdgcn_sched_barrier(0);
       const int g = i - (32 - kTail);  // tail gap
       if (g == 0) asm volatile("s_nop 11");
@@ -494,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
         if (soft_gap(q, kTail - 1) == g) soft_piece(S, k + 1, 1 - P, q);
       __builtin_amdgcn_sched_barrier(0);
     }
-    values_end(k, P);
+    l_run += sum_xor32(psum[P]);
     rescale();  // tile k + 1's raise, now that tile k's values are in
   };
   int k = 0;
@@ -506,8 +531,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     step(k, 0);
     ++k;
   }
-  // last tile k = n_tiles - 1: its softmax is done; its values alone (set k & 1, moved to
-  // set 0 so that every register index stays a compile-time constant)
+  // last tile k = n_tiles - 1: its softmax is done and its first operands are read; its
+  // values alone (set k & 1, moved to set 0 so that every register index stays a
+  // compile-time constant), operands read four MFMAs ahead
   if (k & 1) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -516,13 +542,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_main_bf16_wide(
     psum[0] = psum[1];
   }
 #pragma unroll
-  for (int g = -kPvAhead; g < 0; ++g) value_pre(g, 0);
-#pragma unroll
   for (int i = 0; i < 32; ++i) {
-    value_mfma(i, 0, 0);
+    value_mfma(i, 0, k, 0, false);
     __builtin_amdgcn_sched_barrier(0);
   }
-  values_end(k, 0);
+  l_run += sum_xor32(psum[0]);
 
   // ---- partial outputs, through LDS so that every global store writes whole rows.  O[cb]
   // item e is column 32cb + 8*(e/4) + 4*kg + e%4 of head h0 + l32: written straight out,
