@@ -43,9 +43,12 @@ METRIC = "MLA decode attn: latent-KV read TB/s (% HBM peak), query tokens/s over
 DEFAULT_WORKLOAD = "mla_bf16_paged_b64_h32_l1k-32k"
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "main_loop_counters.json")
-# sources of the main-loop kernels; the counter summary is valid only for these exact texts
-MAIN_SRCS = [os.path.join(ROOT, "mlra_latent_kv_amd", "csrc", f) for f in
-             ("main_bf16.hip", "main_bf16_wide.hip", "tile_bf16.h", "device_common.h")]
+# sources of each main-loop kernel; a kernel's committed counters are valid only for these
+# exact texts
+KERNEL_SRCS = {
+    "k_main_bf16": ("main_bf16.hip", "tile_bf16.h", "device_common.h"),
+    "k_main_bf16_wide": ("main_bf16_wide.hip", "tile_bf16.h", "device_common.h"),
+}
 
 
 def log(*a):
@@ -114,10 +117,11 @@ def read_probe(ev, stream, reps: int = 5, gib: int = 2):
     return n / (statistics.median(ms) * 1e-3) / 1e9
 
 
-def source_sha() -> str:
+def source_sha(kernel: str) -> str:
+    """Hash of the sources the main-loop kernel is built from."""
     h = hashlib.sha256()
-    for f in MAIN_SRCS:
-        h.update(open(f, "rb").read())
+    for f in KERNEL_SRCS[kernel]:
+        h.update(open(os.path.join(ROOT, "mlra_latent_kv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -139,14 +143,25 @@ def counters_key(workload: str, num_queries: int = 1, fp8: bool = False) -> str:
 
 def counters_entry(workload: str, num_queries: int = 1, fp8: bool = False):
     """The committed rocprofv3 summary of the main kernel for this workload (HBM bytes per
-    launch, kernel-trace average), if it was taken on the current main-loop source; else
+    launch, kernel-trace average), if it was taken on that kernel's current sources; else
     None."""
     try:
         s = json.load(open(PMC_SUMMARY))
     except (OSError, ValueError):
         return None
     ent = s.get(counters_key(workload, num_queries, fp8))
-    if not ent or ent.get("source_sha") != source_sha():
+    if not ent:
+        return None
+    kern = ent.get("kernel")
+    if kern not in KERNEL_SRCS or ent.get("source_sha") != source_sha(kern):
+        return None
+    w = None
+    try:
+        from mlra_latent_kv_amd import inputs as I
+        w = I.WORKLOADS[workload]
+    except (ImportError, KeyError):
+        return None
+    if kern != main_kernel(w, num_queries, fp8):
         return None
     return ent
 
