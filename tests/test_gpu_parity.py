@@ -196,17 +196,24 @@ def test_late_raises(wname, splits):
     assert_close(got, oracle_out(inp), "bf16", f"{wname} splits={splits}")
 
 
-@pytest.mark.xfail(reason="known precision limit: at logits beyond ~65 log2 units the absorbed "
-                          "query's bf16 rounding (relative 2^-9) moves the softmax weights by "
-                          "percents; max-abs error reaches 0.026-0.028 > 2e-2 on the 128-head "
-                          "and MLRA-4 kernels (0.017 on the 32-head MLA kernel)",
-                   strict=False)
-@pytest.mark.parametrize("wname", BF16[:3])
+_STEEP_XFAIL = pytest.mark.xfail(
+    reason="known precision limit: at logits beyond ~65 log2 units the absorbed query's bf16 "
+           "rounding (relative 2^-9) moves the softmax weights by percents; max-abs error "
+           "reaches 0.026-0.028 > 2e-2 on the 128-head and MLRA-4 kernels",
+    strict=False)
+
+
+@pytest.mark.parametrize("wname", [
+    pytest.param(BF16[0], marks=_STEEP_XFAIL),
+    BF16[1],  # the 32-head MLA kernel stays inside the bound here (max-abs ~0.017)
+    pytest.param(BF16[2], marks=_STEEP_XFAIL),
+])
 def test_steep_ramp_known_limit(wname):
     """Rows scaled 0.25x .. 6x along the sequence with a sharp query (|logit| up to 72-81
-    log2 units): outside the max-abs tolerance, kept in the suite as an expected failure.
-    A sweep of the ramp's top (3.0 .. 6.0) held max-abs <= 2e-2 on every kernel up to
-    |logit| ~ 60 log2 units and first exceeded it at 65-66 (32-head and MLRA-4 kernels)."""
+    log2 units): outside the max-abs tolerance on the 128-head and MLRA-4 kernels, kept in the
+    suite as expected failures; the 32-head MLA kernel's case is an ordinary test.  A sweep of
+    the ramp's top (3.0 .. 6.0) held max-abs <= 2e-2 on every kernel up to |logit| ~ 60 log2
+    units."""
     w = I.WORKLOADS[wname]
     inp = I.make_inputs(w, seqlens=[4000, 2500, 700, 33], q_gain=I.sharp_q_gain(w))
     ramp_rows(inp, 0.25, 6.0)
