@@ -40,6 +40,8 @@ projection ("[ICLR 2025] MLRA…", section 2.1), so the row is computed alike.
 Several query tokens per step (``mla_decode(num_queries=s_q)``; the yololab page,
 section "繁榮背後的代價…", names the compute-heavy regime that several query rows against one
 cache read lead to): each new token attends causally over the cache, which already holds it.
+``mla_prefill`` computes the same definition for many new tokens at once (the un-absorbed
+prefill: keys and values up-projected once per head, all query tokens scored against them).
 
 Variants of the decode step (``attend_unabsorbed`` / ``mla_decode`` keywords):
 * gated output ("[ICLR 2025] MLRA…", section 4: MLRA-4 combined with gated attention):
@@ -318,6 +320,62 @@ def mla_decode(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, d_rope: int, scale
                 scale=scale, out_scale=out_scale, theta=theta, heads=heads,
                 gate=None if g is None else g[b], q_latent=qn[b] if q_latent else None,
                 latent_out=latent_out, branches=nb, d_cb=dcb)
+    return out
+
+
+def mla_prefill(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, num_queries: int, d_rope: int,
+                scale: float, out_scale: float = 1.0, theta: float = 10000.0, page_size: int = 0,
+                block_table=None, to_f64: Callable = _as_f64,
+                batches: Optional[Iterable[int]] = None,
+                heads: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Prefill: the s_q newest tokens of each sequence attend causally over its cache, computed
+    the un-absorbed way for all of a head's query tokens at once (MLA, one latent branch).
+
+    The yololab page (section "繁榮背後的代價…") names the regime in which many query rows
+    meet one cache read; the interview Q&A ("MLA … 是什么", 核心机制 step 3) gives the
+    un-absorbed step itself: the cached latents are up-projected to full keys K = c W_UK^T and
+    values V = c W_UV once per head, and every query row is scored against them.  Same
+    definition, inputs and layouts as ``mla_decode(num_queries=s_q)``: query rows
+    [B, s_q * H, ...] with row i * H + h = head h of query token i, which sits at position
+    L - s_q + i (rotary part rotated there) and sees tokens 0 .. L - s_q + i; a row that sees no
+    token is zero.  Returns [len(batches), len(rows), d_v]; ``heads`` selects query rows.
+    """
+    W_UK, W_UV = to_f64(w_uk), to_f64(w_uv)
+    if W_UK.shape[0] != 1:
+        raise ValueError("the prefill covers one latent branch (MLA)")
+    _, Hw, d_nope, d_c = W_UK.shape
+    d_v = W_UV.shape[-1]
+    qn, qr = to_f64(q_nope), to_f64(q_rope)
+    B, R = qn.shape[0], qn.shape[1]
+    sq = int(num_queries)
+    if sq < 1 or R != sq * Hw:
+        raise ValueError("query rows must be s_q times the weights' heads")
+    batches = list(range(B)) if batches is None else list(batches)
+    sel = list(range(R)) if heads is None else list(heads)
+    out = np.zeros((len(batches), len(sel), d_v), dtype=F64)
+    for i, b in enumerate(batches):
+        L = int(seqlens[b])
+        rows = sequence_rows(cache, b, L, page_size, block_table, to_f64)   # [L, d_c + d_rope]
+        if L == 0:
+            continue
+        lat = rows[:, :d_c]
+        k_rot = rope(rows[:, d_c:d_c + d_rope], np.arange(L), theta)         # keys at position t
+        pos = L - sq + np.arange(sq)                                           # query positions
+        mask = np.arange(L)[None, :] > pos[:, None]                            # [s_q, L] future
+        seen = pos >= 0                                                        # sees >= 1 token
+        for h in sorted({r % Hw for r in sel}):
+            K = lat @ W_UK[0, h].T                                             # [L, d_nope]
+            V = lat @ W_UV[0, h]                                               # [L, d_v]
+            q_n = qn[b, h::Hw, 0]                                              # [s_q, d_nope]
+            q_r = rope(qr[b, h::Hw], pos, theta)                               # [s_q, d_rope]
+            S = scale * (q_n @ K.T + q_r @ k_rot.T)                            # [s_q, L]
+            S[mask] = -np.inf
+            O = np.zeros((sq, d_v), dtype=F64)
+            if seen.any():
+                O[seen] = softmax(S[seen]) @ V
+            for j, r in enumerate(sel):
+                if r % Hw == h:
+                    out[i, j] = out_scale * O[r // Hw]
     return out
 
 

@@ -1012,3 +1012,117 @@ def test_e4m3_round_trip_and_saturation():
     v = I.e4m3_bits_to_f64(codes)
     assert np.array_equal(I.e4m3_bits_to_f64(I.f64_to_e4m3_bits(v)), v)
     assert I.e4m3_bits_to_f64(I.f64_to_e4m3_bits(np.array([1e9, -1e9])) ).tolist() == [448.0, -448.0]
+
+
+# ----------------------------------------------------------------------------- prefill
+# The s_q newest tokens of each sequence attend causally over the cache, up-projected once per
+# head (the interview Q&A's 核心机制 step 3, in the many-query regime of the yololab page's
+# 繁榮背後的代價 section).  O.mla_prefill computes all query tokens of a head at once; it is
+# pinned against the scalar masked brute force, the per-row decode oracle (itself pinned
+# above), an exact first-token form and causality.
+
+def _prefill_case(sq, L, Hw=2, dn=3, dc=4, dr=4, dv=5, seed=0):
+    rng = np.random.default_rng(seed + 100 * sq + L)
+    qn = rng.standard_normal((1, sq * Hw, 1, dn))
+    qr = rng.standard_normal((1, sq * Hw, dr))
+    cache = rng.standard_normal((1, max(L, 1), dc + dr))
+    w_uk = rng.standard_normal((1, Hw, dn, dc))
+    w_uv = rng.standard_normal((1, Hw, dc, dv))
+    return qn, qr, cache, w_uk, w_uv
+
+
+@pytest.mark.parametrize("sq,L", [(2, 7), (4, 2), (3, 3), (5, 9), (1, 4)])
+def test_prefill_brute_force(sq, L):
+    """Against the scalar masked brute force, with L < s_q (early rows see nothing), L = s_q
+    (the first row sees one token) and s_q = 1 (a plain decode)."""
+    qn, qr, cache, w_uk, w_uv = _prefill_case(sq, L)
+    got = O.mla_prefill(qn, qr, cache, [L], w_uk, w_uv, num_queries=sq, d_rope=4, scale=0.4,
+                        out_scale=0.7, theta=1e4)[0]
+    ref = _brute_multi(qn[0], qr[0], cache[0, :L], w_uk, w_uv, sq, 4, 0.4, 0.7, 1e4)
+    assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_prefill_equals_per_row_decode_paged():
+    """Workload dimensions (128 heads, latent 512, rope 64, bf16 values, paged, shuffled), two
+    sequences of different lengths, a sample of query rows: equal to the per-row multi-query
+    decode oracle to fp64 rounding."""
+    w = I.WORKLOADS["mla_bf16_paged_b4_h128_l131072"]
+    sq = 6
+    inp = I.make_inputs(w, seed=3, seqlens=[70, 9])
+    f64 = lambda a: I.to_f64(a, "bf16")
+    rng = np.random.default_rng(2)
+    qn = rng.standard_normal((2, sq * w.heads, 1, 128)) / math.sqrt(128)
+    qr = rng.standard_normal((2, sq * w.heads, 64)) / 8.0
+    kw = dict(d_rope=64, scale=w.softmax_scale, out_scale=1.0, theta=1e4,
+              page_size=inp["page_size"], block_table=inp["block_table"], to_f64=f64)
+    rows = [0, 127, 128 + 5, 3 * 128 + 64, 5 * 128 + 127]
+    a = O.mla_prefill(qn, qr, inp["cache"], inp["seqlens"], inp["w_uk"], inp["w_uv"],
+                      num_queries=sq, heads=rows, **kw)
+    b = O.mla_decode(qn, qr, inp["cache"], inp["seqlens"], inp["w_uk"], inp["w_uv"],
+                     num_queries=sq, heads=rows, **kw)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(b).max()
+
+
+def test_prefill_first_token_is_its_value():
+    """L = s_q: query token 0 sees token 0 alone, its weight is exactly 1, and its output is
+    out_scale * c_0 W_UV for every head."""
+    sq = L = 4
+    qn, qr, cache, w_uk, w_uv = _prefill_case(sq, L, Hw=3)
+    out = O.mla_prefill(qn, qr, cache, [L], w_uk, w_uv, num_queries=sq, d_rope=4, scale=0.9,
+                        out_scale=0.5, theta=1e4)[0]
+    for h in range(3):
+        exp = 0.5 * cache[0, 0, :4] @ w_uv[0, h]
+        assert np.abs(out[h] - exp).max() <= 1e-14 * max(1.0, np.abs(exp).max())
+
+
+def test_prefill_causality():
+    """A change to cache row t changes exactly the query rows at positions >= t."""
+    sq, L = 5, 8
+    qn, qr, cache, w_uk, w_uv = _prefill_case(sq, L)
+    kw = dict(num_queries=sq, d_rope=4, scale=0.4, theta=1e4)
+    base = O.mla_prefill(qn, qr, cache, [L], w_uk, w_uv, **kw)[0]
+    t = 5                                  # positions of the query tokens: 3 .. 7
+    changed = cache.copy()
+    changed[0, t] += 1.0
+    after = O.mla_prefill(qn, qr, changed, [L], w_uk, w_uv, **kw)[0]
+    for r in range(sq * 2):
+        pos = L - sq + r // 2
+        if pos < t:
+            assert np.array_equal(after[r], base[r])
+        else:
+            assert not np.allclose(after[r], base[r])
+
+
+def _prefill_pins_pass():
+    checks = [lambda: test_prefill_brute_force(2, 7), lambda: test_prefill_brute_force(4, 2),
+              test_prefill_first_token_is_its_value, test_prefill_causality]
+    with np.errstate(all="ignore"):
+        for c in checks:
+            try:
+                c()
+            except (AssertionError, ValueError, IndexError):
+                return False
+    return True
+
+
+def test_prefill_pins_pass_unplanted():
+    assert _prefill_pins_pass()
+
+
+@pytest.mark.parametrize("mistake,old,new", [
+    ("not_causal", "np.arange(L)[None, :] > pos[:, None]", "np.zeros((sq, L), dtype=bool)"),
+    ("mask_off_by_one", "np.arange(L)[None, :] > pos[:, None]", "np.arange(L)[None, :] >= pos[:, None]"),
+    ("queries_at_last_position", "q_r = rope(qr[b, h::Hw], pos, theta)",
+     "q_r = rope(qr[b, h::Hw], np.full(sq, L - 1), theta)"),
+    ("values_from_keys", "V = lat @ W_UV[0, h]", "V = (lat @ W_UK[0, h].T)[:, :1] * np.ones((1, d_v))"),
+])
+def test_prefill_planted_mistake_is_caught(monkeypatch, mistake, old, new):
+    """Each mistake is planted in a copy of the oracle's prefill, on the CPU."""
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(O.mla_prefill))
+    assert old in src
+    ns = dict(vars(O))
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(O, "mla_prefill", ns["mla_prefill"])
+    assert not _prefill_pins_pass()
