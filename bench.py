@@ -304,14 +304,145 @@ def bench_append(args, ev, stream):
     }
 
 
+PREFILL_METRIC = "MLA prefill (un-absorbed): TFLOP/s (% of the 2.5 PF bf16 MFMA peak)"
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def prefill_flops(w, lens, sq):
+    """Algorithmic work of one prefill call: the up-projection of every cached latent to its
+    per-head key and value (2 * 512 * 256 per token and head) and the causal attention, 2 *
+    (192 + 128) per visible (query, key) pair and head."""
+    import numpy as np
+    proj = 2.0 * float(np.sum(lens)) * w.d_c * (w.d_nope + w.d_v) * w.heads
+    pairs = 0.0
+    for L in lens:
+        vis = np.clip(int(L) - sq + 1 + np.arange(sq), 0, int(L))
+        pairs += float(vis.sum())
+    attn = 2.0 * pairs * (w.d_nope + w.d_rope + w.d_v) * w.heads
+    return proj, attn
+
+
+def cpu_baseline_prefill(inp, seconds: float):
+    """The fp64 oracle's prefill (as it stands) on a bounded sample: whole heads of sequence 0,
+    one at a time, until the time budget is spent; value = their share of the algorithmic
+    work / wall time."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import mla_oracle as O
+    from mlra_latent_kv_amd import inputs as I
+    w, sq = inp["workload"], inp["num_queries"]
+    lens = np.asarray(inp["seqlens"])
+    proj, attn = prefill_flops(w, lens[:1], sq)
+    per_head = (proj + attn) / w.heads
+    cores = len(os.sched_getaffinity(0))
+    done, heads = 0.0, 0
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for h in range(w.heads):
+            rows = [i * w.heads + h for i in range(sq)]
+            O.mla_prefill(inp["q_nope"], inp["q_rope"], inp["cache"], inp["seqlens"], inp["w_uk"],
+                          inp["w_uv"], num_queries=sq, d_rope=w.d_rope, scale=inp["softmax_scale"],
+                          out_scale=inp["out_scale"], theta=inp["rope_theta"],
+                          page_size=inp["page_size"], block_table=inp["block_table"],
+                          to_f64=lambda a: I.to_f64(a, w.dtype), batches=[0], heads=rows)
+            done += per_head
+            heads += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        el = time.perf_counter() - t0
+    return {"value": done / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} whole heads of sequence 0 of {w.name} ({sq} query tokens each), "
+                      f"fp64 un-absorbed oracle, {el:.1f} s wall; value = their share of the "
+                      f"algorithmic work / wall time",
+            "seconds": round(el, 2), "cpu": _cpu_model()}
+
+
+def bench_prefill(args, ev, stream):
+    """One prefill call per step on a prefill workload (every token of the sequence new),
+    caches flushed before every step, outside the event pair (as for the decode)."""
+    import numpy as np
+    import torch
+    from mlra_latent_kv_amd import harness as Hn
+    from mlra_latent_kv_amd import inputs as I
+    name = args.workload if args.workload in I.PREFILL_WORKLOADS else "prefill_bf16_b1_h128_l4096"
+    w = I.PREFILL_WORKLOADS[name]
+    sq = args.num_queries if args.num_queries > 1 else w.seqlen
+    log(f"[bench] generating {w.name} (s_q = {sq})")
+    inp = I.make_inputs(w, num_queries=sq)
+    case = Hn.to_device(inp, prefill=True)
+    torch.cuda.synchronize()
+    lens = np.asarray(inp["seqlens"], np.int64)
+    proj, attn = prefill_flops(w, lens, sq)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        flush.sum()
+        Hn.run_prefill(case)
+    torch.cuda.synchronize()
+    log(f"[bench] warm-up done ({W} steps); timing {K} steps")
+    pf = [ev.create(2) for _ in range(K)]
+    pp = [ev.create(2) for _ in range(K)]
+    st = [ev.create(3) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(K):
+        ev.record(pf[i][0], stream)
+        flush.sum()
+        Hn.run_prefill(case)
+        ev.record(pf[i][1], stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    for i in range(K):
+        ev.record(pp[i][0], stream)
+        flush.sum()
+        ev.record(pp[i][1], stream)
+    for i in range(K):
+        flush.sum()
+        Hn.run_prefill(case, events=st[i])
+    torch.cuda.synchronize()
+    t_f = statistics.mean(ev.ms(a, b) for a, b in pp)
+    total = [ev.ms(a, b) - t_f for a, b in pf]
+    kv_ms = statistics.mean(ev.ms(e[0], e[1]) for e in st)
+    at_ms = statistics.mean(ev.ms(e[1], e[2]) for e in st)
+    for e in pf + pp + st:
+        ev.destroy(e)
+    ms = statistics.mean(total)
+    value = (proj + attn) / (ms * 1e-3) / 1e12
+    at_tf = attn / (at_ms * 1e-3) / 1e12
+    line = {
+        "metric": PREFILL_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": int(len(lens)), "heads": w.heads,
+                   "seq_len": int(lens.max()), "query_tokens_per_seq": sq,
+                   "d_latent": w.d_c, "d_rope": w.d_rope, "paged": bool(inp["paged"])},
+        "pct_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
+        "query_tokens_per_s": round(sq * len(lens) / (ms * 1e-3), 1),
+        "algorithmic_tflop": {"projection": round(proj / 1e12, 4), "attention": round(attn / 1e12, 4)},
+        "stage_us": {"projection": round(1e3 * kv_ms, 2), "attention": round(1e3 * at_ms, 2)},
+        "ms_p10_p50_p90": [round(float(np.percentile(total, q)), 4) for q in (10, 50, 90)],
+        "wall_s_timed_region": round(t_wall, 4),
+        "roofline": {"kernel": "k_prefill_attn", "bound": "mfma", "achieved": round(at_tf, 1),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(at_tf / MFMA_PEAK_TFLOPS, 4), "algorithmic_flops": attn,
+                     "traffic": None, "main_us": round(1e3 * at_ms, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--op", choices=["decode", "append"], default="decode",
-                    help="decode: the decode step (the metric); append: one step's cache write")
+    ap.add_argument("--op", choices=["decode", "append", "prefill"], default="decode",
+                    help="decode: the decode step (the metric); append: one step's cache write; "
+                         "prefill: the un-absorbed many-query step on a prefill workload")
     ap.add_argument("--variant", default="none",
                     choices=["none", "gate", "query_latent", "output_latent",
                              "query_latent+output_latent"],
@@ -352,6 +483,10 @@ def main():
     B.load()
     if args.op == "append":
         print(json.dumps(bench_append(args, HipEvents(), torch.cuda.current_stream().cuda_stream)),
+              flush=True)
+        return
+    if args.op == "prefill":
+        print(json.dumps(bench_prefill(args, HipEvents(), torch.cuda.current_stream().cuda_stream)),
               flush=True)
         return
     w = I.WORKLOADS[args.workload]

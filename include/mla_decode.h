@@ -388,6 +388,47 @@ mla_status mla_cache_append(const mla_append_params* p, const void* hidden, cons
                             int32_t* pages_used, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/*
+ * Prefill: many new tokens per sequence in one step, computed un-absorbed.  With s_q query
+ * tokens against L cached ones the absorbed form scores every query over the 576-wide
+ * latent row and sums the 512-wide latent (1088 multiply-adds per query, key and head);
+ * up-projecting the cached latents once per head to keys and values costs 192 + 128 per pair
+ * after that, the better trade once s_q reaches the hundreds (the interview Q&A "MLA … 是什么",
+ * section 核心机制 step 3: the latent is up-projected with W_K_up / W_V_up at inference; the
+ * yololab MLA page, section 繁榮背後的代價, on the compute-heavy regime).
+ *
+ * Same definition, arguments and layouts as mla_decode with p->num_queries = s_q ("Several
+ * query tokens" above), s_q >= 1 and not bounded by 16 here: for each sequence b with L =
+ * seqlens[b], query token i at position P = L - s_q + i and head h,
+ *   K_t    = W_UK[h] c_t                       (d_nope)   V_t = W_UV[h]^T c_t   (d_v)
+ *   s_t    = softmax_scale * (q_nope[b,i,h] . K_t + RoPE(q_rope[b,i,h], P) . k_t),  t <= P
+ *   out[b,i,h] = out_scale * sum_{t <= P} softmax(s)_t V_t    (zero when P < 0)
+ *   q_nope [B, s_q, H, 1, 128], q_rope [B, s_q, H, 64], out [B, s_q, H, 128], caches, seqlens,
+ *   block_table and weights exactly as mla_decode (w_uk [1, H, 128, 512], w_uv [1, H, 512, 128]).
+ * Supported: MLA_BF16, num_branches 1, d_latent 512, d_rope 64, d_nope 128, d_v 128, any
+ * H in [1, 4096], batch <= 65535, page_size 0 or 64, flags 0, latent_format 0 (otherwise
+ * MLA_ERR_UNSUPPORTED).  num_splits is not used.  Pointers of q_nope, q_rope, latent, rope,
+ * w_uk, w_uv and out 16-byte aligned, cache strides multiples of 8 elements (MLA_ERR_ALIGN).
+ * The workspace (>= mla_prefill_workspace_size bytes, 256-byte aligned, no initialisation)
+ * receives the up-projected keys and values, [B, H, L_pad, 128] bf16 each, L_pad =
+ * max_seqlen rounded up to a multiple of 128.  Two kernels run on `stream`: the up-projection
+ * (a GEMM of the cached latents against W_UK and W_UV) and a causal flash-attention pass.
+ */
+mla_status mla_prefill_workspace_size(const mla_params* p, size_t* bytes);
+mla_status mla_prefill(const mla_params* p, const void* q_nope, const void* q_rope,
+                       const void* latent, const void* rope, const int32_t* seqlens,
+                       const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* Tracing variant of mla_prefill: also records three caller-created HIP events (hipEvent_t
+ * values passed as void*) on `stream`: events[0] before the up-projection, events[1] between
+ * it and the attention, events[2] after the attention.  A failed hipEventRecord returns
+ * MLA_ERR_HIP. */
+mla_status mla_prefill_timed(const mla_params* p, const void* q_nope, const void* q_rope,
+                             const void* latent, const void* rope, const int32_t* seqlens,
+                             const int32_t* block_table, const void* w_uk, const void* w_uv,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, void* const* events);
+
 /* Static, human-readable name of a status code. */
 const char* mla_status_str(int32_t status);
 

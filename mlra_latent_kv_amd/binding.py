@@ -99,12 +99,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                                c_size_t, c_void_p]
     lib.mla_rope_rotate.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_float,
                                     c_int32, c_void_p]
+    lib.mla_prefill_workspace_size.argtypes = [P, ctypes.POINTER(c_size_t)]
+    lib.mla_prefill.argtypes = dec
+    lib.mla_prefill_timed.argtypes = dec + [c_void_p]
     lib.mla_status_str.argtypes = [c_int32]
     lib.mla_status_str.restype = ctypes.c_char_p
     for f in ("mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
               "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc", "mla_rope_rotate",
               "mla_decode_gated", "mlra_decode_gated",
-              "mla_append_workspace_size", "mla_cache_append"):
+              "mla_append_workspace_size", "mla_cache_append", "mla_prefill_workspace_size",
+              "mla_prefill", "mla_prefill_timed"):
         getattr(lib, f).restype = c_int32
     _lib = lib
     return lib
@@ -211,6 +215,22 @@ def mlra_decode_gated(params, q_nope, q_rope, latent, rope, seqlens, block_table
     return _decode_gated("mlra_decode_gated", params, q_nope, q_rope, latent, rope, seqlens,
                          block_table, w_uk, w_uv, gate, out, workspace, workspace_bytes, stream,
                          check)
+
+
+def prefill_workspace_size(params: MlaParams) -> int:
+    n = c_size_t(0)
+    st = load().mla_prefill_workspace_size(ctypes.byref(params), ctypes.byref(n))
+    if st:
+        raise MlaError(st, "mla_prefill_workspace_size")
+    return n.value
+
+
+def mla_prefill(params, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                workspace, workspace_bytes=None, stream=None, check=True, events=None) -> int:
+    """The un-absorbed many-query step (see include/mla_decode.h, mla_prefill); ``events``:
+    optional ctypes array of 3 hipEvent_t -> calls mla_prefill_timed."""
+    return _decode("mla_prefill", params, q_nope, q_rope, latent, rope, seqlens, block_table,
+                   w_uk, w_uv, out, workspace, workspace_bytes, stream, check, events)
 
 
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # MLA_NOALLOC_SCRATCH_BYTES

@@ -19,7 +19,7 @@ PROBE_LIB = os.path.join(PKG, "libmla_probe.so")  # read-stream probe (benchmark
 ARCH = "gfx950"
 
 HIP_SOURCES = ["api.hip", "kernels_generic.hip", "kernels_bf16_aux.hip", "main_bf16.hip",
-               "main_bf16_wide.hip", "append.hip"]
+               "main_bf16_wide.hip", "append.hip", "prefill.hip"]
 CXX_SOURCES = ["plan.cpp"]
 PROBE_SOURCES = ["probe.hip"]
 

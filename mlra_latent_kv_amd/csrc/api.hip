@@ -297,6 +297,67 @@ mla_status mla_cache_append(const mla_append_params* p, const void* hidden, cons
   return to_status(launch_append(plan, a, stream));
 }
 
+mla_status mla_prefill_workspace_size(const mla_params* p, size_t* bytes) {
+  if (!bytes) return MLA_ERR_NULL;
+  PrefillPlan plan;
+  const mla_status st = make_prefill_plan(p, &plan);
+  if (st == MLA_OK) *bytes = plan.bytes;
+  return st;
+}
+
+namespace {
+mla_status run_prefill(const mla_params* p, const void* q_nope, const void* q_rope,
+                       const void* latent, const void* rope, const int32_t* seqlens,
+                       const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       void* const* events) {
+  PrefillPlan plan;
+  mla_status st = make_prefill_plan(p, &plan);
+  if (st != MLA_OK) return st;
+  st = check_prefill_call(plan, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv,
+                          out, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  PrefillArgs a;
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.latent = latent;
+  a.rope = rope;
+  a.seqlens = seqlens;
+  a.block_table = block_table;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.lat_tok = p->latent_stride_tok;
+  a.lat_seq = p->latent_stride_seq;
+  a.rope_tok = p->rope_stride_tok;
+  a.rope_seq = p->rope_stride_seq;
+  a.bt_stride = p->block_table_stride;
+  a.softmax_scale = p->softmax_scale;
+  a.out_scale = p->out_scale;
+  a.rope_theta = p->rope_theta;
+  a.kbuf = static_cast<char*>(workspace) + plan.off_k;
+  a.vbuf = static_cast<char*>(workspace) + plan.off_v;
+  return to_status(launch_prefill(plan, a, stream, events));
+}
+}  // namespace
+
+mla_status mla_prefill(const mla_params* p, const void* q_nope, const void* q_rope,
+                       const void* latent, const void* rope, const int32_t* seqlens,
+                       const int32_t* block_table, const void* w_uk, const void* w_uv, void* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_prefill(p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                     workspace, workspace_bytes, stream, nullptr);
+}
+
+mla_status mla_prefill_timed(const mla_params* p, const void* q_nope, const void* q_rope,
+                             const void* latent, const void* rope, const int32_t* seqlens,
+                             const int32_t* block_table, const void* w_uk, const void* w_uv,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, void* const* events) {
+  return run_prefill(p, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv, out,
+                     workspace, workspace_bytes, stream, events);
+}
+
 const char* mla_status_str(int32_t status) { return status_str(status); }
 
 }  // extern "C"

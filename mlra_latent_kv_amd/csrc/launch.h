@@ -37,6 +37,27 @@ struct DecodeArgs {
   void* olat;       // [B][H][d_c] fp32, fp32 path only (the bf16 path keeps it on chip)
 };
 
+// mla_prefill: the un-absorbed many-query step (prefill.hip)
+struct PrefillArgs {
+  const void* q_nope;   // [B][s_q][H][128]
+  const void* q_rope;   // [B][s_q][H][64], not rotated
+  const void* latent;
+  const void* rope;
+  const int32_t* seqlens;
+  const int32_t* block_table;
+  const void* w_uk;     // [H][128][512]
+  const void* w_uv;     // [H][512][128]
+  void* out;            // [B][s_q][H][128]
+  int64_t lat_tok, lat_seq, rope_tok, rope_seq, bt_stride;
+  float softmax_scale, out_scale, rope_theta;
+  void* kbuf;           // workspace: up-projected keys [B][H][L_pad][128]
+  void* vbuf;           // workspace: up-projected values [B][H][L_pad][128]
+};
+// events (tracing, else null): three hipEvent_t recorded before the projection, between the
+// two kernels and after the attention
+hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_t s,
+                          void* const* events);
+
 struct RopeFreq;
 // theta^(-2k/d_rope), k < d_rope/2, in fp64 (RoFormer frequencies)
 void make_rope_freq(int d_rope, float theta, RopeFreq* out);

@@ -190,6 +190,70 @@ mla_status check_call(const mla_params* p, const Plan& plan, int want_branches,
   return MLA_OK;
 }
 
+mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
+  if (!p || !plan) return MLA_ERR_NULL;
+  if (p->dtype != MLA_F32 && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (p->latent_format != 0 && p->latent_format != MLA_LATENT_FP8) return MLA_ERR_DTYPE;
+  if (p->batch < 1 || p->num_heads < 1 || p->num_branches < 1 || p->d_nope < 1 || p->d_v < 1 ||
+      p->d_latent < 1 || p->d_rope < 2 || (p->d_rope & 1) || p->max_seqlen < 0 ||
+      p->num_queries < 0 || p->num_pages < 0)
+    return MLA_ERR_SHAPE;
+  if (p->flags & ~(MLA_FLAG_DEVICE_CHECKS | MLA_FLAG_QUERY_LATENT | MLA_FLAG_OUTPUT_LATENT))
+    return MLA_ERR_SHAPE;
+  // grid dimensions (sequences, heads) and 32-bit token indices
+  if (p->batch > 65535 || p->num_heads > 4096 || p->max_seqlen > (1 << 24) ||
+      p->num_queries > (1 << 24))
+    return MLA_ERR_SHAPE;
+  if (!std::isfinite(p->softmax_scale) || !std::isfinite(p->out_scale) ||
+      !(p->rope_theta > 0.0f) || !std::isfinite(p->rope_theta))
+    return MLA_ERR_SHAPE;
+  if (p->page_size != 0 && p->page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  // MLA with the bf16 decode dims; no folded or gated forms, no fp8 latent, no device checks
+  if (p->dtype != MLA_BF16 || p->num_branches != 1 || p->d_latent != 512 || p->d_rope != 64 ||
+      p->d_nope != 128 || p->d_v != 128 || p->flags != 0 || p->latent_format != 0)
+    return MLA_ERR_UNSUPPORTED;
+  if (p->latent_stride_tok < 512 || p->rope_stride_tok < 64 || p->latent_stride_seq < 0 ||
+      p->rope_stride_seq < 0)
+    return MLA_ERR_SHAPE;
+  if ((p->latent_stride_tok | p->latent_stride_seq | p->rope_stride_tok | p->rope_stride_seq) % 8)
+    return MLA_ERR_ALIGN;
+  if (p->page_size == kPage && (p->max_pages_per_seq < ceil_div(p->max_seqlen, kPage) ||
+                                p->block_table_stride < p->max_pages_per_seq))
+    return MLA_ERR_SHAPE;
+  PrefillPlan q{};
+  q.B = p->batch;
+  q.H = p->num_heads;
+  q.sq = p->num_queries > 1 ? p->num_queries : 1;
+  q.paged = p->page_size == kPage;
+  q.max_seqlen = p->max_seqlen;
+  q.L_pad = (int)(ceil_div(std::max(p->max_seqlen, 1), 128) * 128);
+  // attention grid: (sequence, head, block of 128 query tokens) in one dimension
+  if ((int64_t)q.B * q.H * ceil_div(q.sq, 128) > INT32_MAX) return MLA_ERR_SHAPE;
+  const size_t kv = (size_t)q.B * q.H * q.L_pad * 128 * 2;
+  q.off_k = 0;
+  q.off_v = align_up(kv);
+  q.bytes = q.off_v + align_up(kv);
+  *plan = q;
+  return MLA_OK;
+}
+
+mla_status check_prefill_call(const PrefillPlan& plan, const void* q_nope, const void* q_rope,
+                              const void* latent, const void* rope, const int32_t* seqlens,
+                              const int32_t* block_table, const void* w_uk, const void* w_uv,
+                              const void* out, const void* workspace, size_t workspace_bytes) {
+  if (!q_nope || !q_rope || !latent || !rope || !seqlens || !w_uk || !w_uv || !out || !workspace)
+    return MLA_ERR_NULL;
+  if (plan.paged && !block_table) return MLA_ERR_NULL;
+  if (workspace_bytes < plan.bytes) return MLA_ERR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign) || !aligned(seqlens, 4) || (plan.paged && !aligned(block_table, 4)))
+    return MLA_ERR_ALIGN;
+  // 16-byte vector reads of queries, cache rows and weights, 8-byte output stores
+  if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(latent, 16) || !aligned(rope, 16) ||
+      !aligned(w_uk, 16) || !aligned(w_uv, 16) || !aligned(out, 16))
+    return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
 mla_status check_rope_rotate(const void* x, int64_t row_stride, const int32_t* pos,
                              int64_t n_rows, int32_t d_rope, float theta, int32_t dtype) {
   if (dtype != MLA_F32 && dtype != MLA_BF16) return MLA_ERR_DTYPE;

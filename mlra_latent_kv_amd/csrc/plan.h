@@ -98,6 +98,25 @@ mla_status check_append_call(const mla_append_params* p, const AppendPlan& plan,
                              int32_t n_free, const int32_t* pages_used, const void* workspace,
                              size_t workspace_bytes);
 
+// Prefill (mla_prefill): the un-absorbed many-query step.  The workspace holds the keys and
+// values up-projected from the latent, [B][H][L_pad][128] bf16 each.
+struct PrefillPlan {
+  int B, H, sq;       // sequences, weight heads, query tokens per sequence (rows s_q x H)
+  int paged, max_seqlen;
+  int L_pad;          // key rows per (sequence, head) in the workspace: max_seqlen rounded up
+                      // to the projection's 128-token blocks
+  size_t off_k, off_v, bytes;
+};
+
+// Validates *p for the prefill and fills *plan.  Touches no device.
+mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan);
+
+// Per-call checks on top of make_prefill_plan: pointers, alignment, workspace size.
+mla_status check_prefill_call(const PrefillPlan& plan, const void* q_nope, const void* q_rope,
+                              const void* latent, const void* rope, const int32_t* seqlens,
+                              const int32_t* block_table, const void* w_uk, const void* w_uv,
+                              const void* out, const void* workspace, size_t workspace_bytes);
+
 const char* status_str(int32_t s);
 
 }  // namespace mla

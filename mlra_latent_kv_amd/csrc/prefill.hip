@@ -1,0 +1,403 @@
+// Un-absorbed prefill of MLA on gfx950 (bf16 in, fp32 accumulation).
+//
+// Many new tokens per sequence attend causally over the cache at once.  With that many query
+// rows the absorbed form (every query scored over the 576-wide latent row, the 512-wide
+// latent summed) costs 1088 multiply-adds per (query, key, head); the un-absorbed form
+// up-projects the cached latents once per head to keys K = c W_UK^T (128) and values
+// V = c W_UV (128) and then costs 192 + 128 per pair (the interview Q&A "MLA … 是什么",
+// 核心机制 step 3, and the compute-heavy regime the yololab MLA page names in
+// 繁榮背後的代價).  Two launches:
+//
+//  * k_prefill_kv: K and V of every (sequence, head, token) into the workspace,
+//    [B][H][L_pad][128] each, as one MFMA GEMM [tokens x 512] . [512 x 256] per head;
+//  * k_prefill_attn: per (sequence, head, block of 128 query tokens), a flash-attention
+//    pass over the key tokens up to the block's last position: scores over the 128 key
+//    columns plus the cached rotary key (64), online softmax, values summed in registers.
+//
+// Query token i of a sequence of L tokens sits at position L - s_q + i, its rotary query is
+// rotated there, and it sees the tokens up to and including itself; a token that sees none
+// writes zeros.  Layouts as the multi-token decode: q_nope [B, s_q, H, 128], q_rope
+// [B, s_q, H, 64], out [B, s_q, H, 128].
+#include "device_common.h"
+#include "launch.h"
+#include "tile_bf16.h"
+
+namespace mla {
+namespace {
+
+using namespace tile;
+
+constexpr int kPfDc = 512, kPfDn = 128, kPfDv = 128, kPfDr = 64;
+
+// ----------------------------------------------------------------------------- K and V
+// One workgroup (4 waves) per (sequence b, block of 128 tokens, head h).  Wave w computes
+// tokens 64 (w & 1) .. +63 (two 32-row M blocks) of part w >> 1 (0: K, 1: V), all 128
+// output columns (four 32-column N blocks), MFMA 32x32x16 over the 512 latent columns in
+// eight chunks of 64.  Each chunk stages, by direct-to-LDS loads, the 128 latent rows
+// (128 bytes each), W_UK[h]'s 128 rows (its columns of the chunk) and W_UV[h]'s 64 rows of
+// the chunk (256 bytes each); double-buffered.
+constexpr int kKvTok = 128, kKvChunk = 64, kKvChunks = kPfDc / kKvChunk;
+constexpr int kKvABytes = kKvTok * kKvChunk * 2;     // 16 KiB
+constexpr int kKvBkBytes = kPfDn * kKvChunk * 2;     // 16 KiB
+constexpr int kKvBvBytes = kKvChunk * kPfDv * 2;     // 16 KiB
+constexpr int kKvStage = kKvABytes + kKvBkBytes + kKvBvBytes;
+constexpr int kKvIssues = 12;                        // loads per wave per chunk (48 per stage)
+
+// 128-byte rows (8 chunks, two rows per 256-byte bank line): chunk c of row r sits at
+// c ^ ((r / 2) mod 8), so 16 consecutive rows read at one chunk hit 16 distinct slots
+__device__ __forceinline__ uint32_t row128(int r, int c) {
+  return (uint32_t)(r * 128 + 16 * (c ^ ((r >> 1) & 7)));
+}
+
+__global__ __launch_bounds__(256, 1) void k_prefill_kv(
+    const bf16* __restrict__ latent, int64_t lat_tok, int64_t lat_seq,
+    const int32_t* __restrict__ bt, int64_t bt_stride, int paged,
+    const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ w_uk,
+    const bf16* __restrict__ w_uv, bf16* __restrict__ kout, bf16* __restrict__ vout, int H,
+    int L_pad) {
+  struct Smem {
+    char st[2][kKvStage];
+  };
+  __shared__ __align__(16) Smem sm;  // 96 KiB, reused for the output tile
+  const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, kg = lane >> 5;
+  const int L = min(max(seqlens[b], 0), max_seqlen);
+  const int t0 = tb * kKvTok;
+  const uint32_t lat_row_b = (uint32_t)(lat_tok * 2);
+  const char* wk = reinterpret_cast<const char*>(w_uk + (size_t)h * kPfDn * kPfDc);
+  const char* wv = reinterpret_cast<const char*>(w_uv + (size_t)h * kPfDc * kPfDv);
+
+  // wave w issues loads 12w .. 12w + 11 of a stage: 0..15 latent rows 8i.., 16..31 W_UK rows
+  // 8(i - 16).., 32..47 W_UV rows 4(i - 32).. (one KiB each); rows past the sequence read as
+  // zeros (the descriptor ends at its last token)
+  auto issue = [&](int q) {
+    char* s = sm.st[q & 1];
+#pragma unroll
+    for (int u = 0; u < kKvIssues; ++u) {
+      const int i = kKvIssues * w + u;  // uniform
+      if (i < 16) {
+        const int r0 = 8 * i, t = t0 + r0;  // 8 rows of one page
+        const int valid = max(0, min(8, L - t));
+        const bf16* base;
+        if (paged) {
+          const int tt = min(t, max(L - 1, 0));
+          const int64_t pg = valid > 0 ? bt[(int64_t)b * bt_stride + tt / kPage] : 0;
+          base = latent + pg * lat_seq + (int64_t)(tt % kPage) * lat_tok;
+        } else {
+          base = latent + (int64_t)b * lat_seq + (int64_t)t * lat_tok;
+        }
+        const int vu = __builtin_amdgcn_readfirstlane(valid);
+        const int r = lane >> 3, c = lane & 7;
+        dma16(rsrc(base, vu * lat_row_b), s + r0 * 128,
+              r * lat_row_b + q * 128 + 16 * (c ^ (((r0 + r) >> 1) & 7)));
+      } else if (i < 32) {
+        const int r0 = 8 * (i - 16), r = r0 + (lane >> 3), c = lane & 7;
+        dma16(rsrc(wk, kPfDn * kPfDc * 2), s + kKvABytes + r0 * 128,
+              r * (kPfDc * 2) + q * 128 + 16 * (c ^ ((r >> 1) & 7)));
+      } else {
+        const int r0 = 4 * (i - 32), r = r0 + (lane >> 4), c = lane & 15;
+        dma16(rsrc(wv, kPfDc * kPfDv * 2), s + kKvABytes + kKvBkBytes + r0 * 256,
+              (q * kKvChunk + r) * (kPfDv * 2) + 16 * (c ^ lat_sw<Sw32>(r)));
+      }
+    }
+  };
+
+  const int mh = w & 1, part = w >> 1;
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
+  const int G = lane >> 4, li = lane & 15;
+
+  issue(0);
+  for (int q = 0; q < kKvChunks; ++q) {
+    if (q + 1 < kKvChunks) {
+      issue(q + 1);
+      wait_vmcnt<kKvIssues>();  // chunk q has landed for this wave
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // ... and for every wave
+    const char* s = sm.st[q & 1];
+#pragma unroll
+    for (int j = 0; j < kKvChunk / 16; ++j) {
+      bf16x8 a[2], bo[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int r = 64 * mh + 32 * mb + l32;
+        a[mb] = lds_read16(s + row128(r, 2 * j + kg));
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if (part == 0) {  // W_UK rows n: 8 consecutive latent columns of row n
+          bo[nb] = lds_read16(s + kKvABytes + row128(32 * nb + l32, 2 * j + kg));
+        } else {          // W_UV rows c: column v, 8 consecutive rows, two transposed reads
+          const int col = 32 * nb + 16 * (G & 1) + 4 * (li & 3);
+          const int r1 = 16 * j + 8 * (G >> 1) + (li >> 2);
+          const char* bv = s + kKvABytes + kKvBkBytes;
+          bo[nb] = tr_pair(bv + lat_piece<Sw32, 128>(r1, col), bv + lat_piece<Sw32, 128>(r1 + 4, col));
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bo[nb], acc[mb][nb], 0, 0, 0);
+    }
+    lds_barrier();  // every wave is done with this stage before it is refilled
+  }
+
+  // ---- output: the 128 x 256 tile (K | V) through LDS, then whole 256-byte rows.  D layout:
+  // lane (column l32 of N block nb, half kg), item i -> token 8 (i / 4) + 4 kg + i % 4 of the
+  // M block.
+  constexpr int kOutPitch = 2 * 2 * kPfDv + 16;  // bytes per token row: K | V, padded
+  static_assert(kKvTok * kOutPitch <= sizeof(Smem), "output tile exceeds the LDS");
+  char* o = reinterpret_cast<char*>(&sm);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = 64 * mh + 32 * mb + 8 * (i >> 2) + 4 * kg + (i & 3);
+        *(bf16*)(o + t * kOutPitch + 2 * (kPfDv * part + 32 * nb + l32)) = (bf16)acc[mb][nb][i];
+      }
+  __syncthreads();
+  // thread tid: 16 bytes of each of rows tid / 32 + 8 k (k = 0 .. 15), part (tid / 16) & 1
+  const size_t head_off = ((size_t)b * H + h) * L_pad;
+  const int pc = tid & 15, pp = (tid >> 4) & 1, pr = tid >> 5;
+  bf16* dst = pp == 0 ? kout : vout;
+#pragma unroll 4
+  for (int k = 0; k < kKvTok / 8; ++k) {
+    const int r = pr + 8 * k;
+    *(bf16x8*)(dst + (head_off + t0 + r) * kPfDv + 8 * pc) =
+        *(const bf16x8*)(o + r * kOutPitch + 2 * (kPfDv * pp + 8 * pc));
+  }
+}
+
+// ----------------------------------------------------------------------------- attention
+// One workgroup (4 waves) per (sequence b, head h, block of 128 query tokens); wave w holds
+// query tokens i0 + 32w .. +31 (MFMA N = rows).  Key tiles of 32 tokens stream through a
+// ring of three LDS buffers: the K rows (128 columns, from the workspace) with the cached
+// rotary keys (64 columns, already rotated at their own positions) in the 192-wide tile
+// layout of the one-branch decode, and the V rows (128 columns) after them.  Per tile and
+// wave: S^T = K . Q^T (12 K-steps), causal mask, online softmax with a lazy max (raised only
+// past kLazyTau log2 units), O^T += V^T P^T (8 MFMAs, the value operand read transposed).
+constexpr int kAtRows = 128;
+constexpr int kAtRing = 3;
+constexpr float kAtLazy = 8.0f;
+using GK = Geom<128>;                                  // K tile: 32 x 256 B + 32 x 128 B
+constexpr int kAtVOff = GK::kBufBytes;                 // V tile after it: 32 x 256 B
+constexpr int kAtBuf = GK::kBufBytes + kTT * 256;      // 20 KiB
+constexpr int kAtIssues = issues_per_wave<4, 128>(true) + 2;  // K rows, rope rows, V rows
+
+__global__ __launch_bounds__(256, 2) void k_prefill_attn(
+    const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
+    const bf16* __restrict__ rope, int64_t rope_tok, int64_t rope_seq,
+    const int32_t* __restrict__ bt, int64_t bt_stride, int paged,
+    const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ kbuf,
+    const bf16* __restrict__ vbuf, bf16* __restrict__ out, int B, int H, int sq, int L_pad,
+    float qscale, float out_scale, RopeFreq rf) {
+  struct Smem {
+    char ring[kAtRing][kAtBuf];
+  };
+  __shared__ __align__(16) Smem sm;  // 60 KiB
+  // heaviest query blocks first; the blocks of one (b, h) land on one XCD when B H % 8 == 0
+  const int n_qb = (sq + kAtRows - 1) / kAtRows;
+  const int bh = blockIdx.x % (B * H);
+  const int qb = n_qb - 1 - (int)(blockIdx.x / (B * H));
+  const int b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, kg = lane >> 5;
+  const int L = min(max(seqlens[b], 0), max_seqlen);
+  const int i0 = qb * kAtRows;
+  const int iw = i0 + 32 * w;                 // this wave's first query token
+  const int ir = iw + l32;                    // this lane's query token (row)
+  const int pos = L - sq + ir;                // its position (< 0: sees nothing)
+  const int pos_w = L - sq + iw + 31;         // the wave's last position
+  const int pos_g = min(L - sq + i0 + kAtRows - 1, L - 1);  // the workgroup's last position
+  const int n_tiles = pos_g >= 0 ? pos_g / kTT + 1 : 0;
+
+  const bf16* kb = kbuf + ((size_t)b * H + h) * L_pad * kPfDn;
+  const bf16* vb = vbuf + ((size_t)b * H + h) * L_pad * kPfDv;
+  const uint32_t rope_row_b = (uint32_t)(rope_tok * 2);
+  // tile k into its ring buffer; past n_tiles the loads go out with no valid row (zeros, no
+  // memory touched) so that every wave issues the same count and every wait is fixed
+  auto issue = [&](int k) {
+    char* buf = sm.ring[k % kAtRing];
+    const int t0 = kTT * k;
+    const int valid = __builtin_amdgcn_readfirstlane(k < n_tiles ? max(0, min(kTT, L - t0)) : 0);
+    const bf16* rb;
+    if (paged) {
+      const int64_t pg = valid > 0 ? bt[(int64_t)b * bt_stride + t0 / kPage] : 0;
+      rb = rope + pg * rope_seq + (int64_t)(t0 % kPage) * rope_tok;
+    } else {
+      rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
+    }
+    issue_tile<Sw32, 4, 128>(buf, w, lane, kb + (size_t)t0 * kPfDn, rb, valid, 256, rope_row_b);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vb + (size_t)t0 * kPfDv, valid * 256);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r0 = 4 * (2 * w + u), r = r0 + (lane >> 4), c = lane & 15;
+      dma16(rv, buf + kAtVOff + r0 * 256, r * 256 + 16 * (c ^ lat_sw<Sw32>(r)));
+    }
+  };
+
+  // query as the B operand (K = 192 columns, N = 32 rows): lane (row l32, half kg), K-step j
+  // holds columns 16 j + 8 kg .. +7; the rotary steps 8 .. 11 rotated at the row's position;
+  // scaled by softmax_scale * log2(e).  Rows past s_q load row s_q - 1 and are not stored.
+  bf16x8 qb8[12];
+  {
+    const int irc = min(ir, sq - 1);
+    const size_t row = ((size_t)b * sq + irc) * H + h;
+    const bf16* qn = q_nope + row * kPfDn + 8 * kg;
+    const bf16* qr = q_rope + row * kPfDr + 8 * kg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8 v = *(const bf16x8*)(qn + 16 * j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb8[j][e] = (bf16)((float)v[e] * qscale);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 v = *(const bf16x8*)(qr + 16 * j);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int k = (16 * j + 8 * kg + e) >> 1;  // rotation pair
+        float cs, sn;
+        rope_cos_sin(max(pos, 0), rf.f[k], &cs, &sn);
+        const float x0 = (float)v[e], x1 = (float)v[e + 1];
+        qb8[8 + j][e] = (bf16)((x0 * cs - x1 * sn) * qscale);
+        qb8[8 + j][e + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
+      }
+    }
+  }
+
+  const int G = lane >> 4, li = lane & 15;
+  float m_ref = -INFINITY, l_run = 0.0f;
+  f32x16 O[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) O[cb] = f32x16{};
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+#pragma unroll
+  for (int j = 0; j < kAtRing - 1; ++j) issue(j);
+  for (int k = 0; k < n_tiles; ++k) {
+    wait_vmcnt<(kAtRing - 2) * kAtIssues>();  // tile k has landed for this wave
+    lds_barrier();                            // ... for every wave; tile k - 1's buffer is free
+    issue(k + kAtRing - 1);
+    const int t0 = kTT * k;
+    if (t0 > pos_w) continue;  // every row of the wave is before this tile (uniform)
+    const char* buf = sm.ring[k % kAtRing];
+
+    // scores S^T[t][row] over 8 key steps and 4 rotary steps
+    f32x16 S = f32x16{};
+#pragma unroll
+    for (int j = 0; j < 12; ++j) {
+      const bf16x8 a = j < 8 ? lds_read16(buf + lat_chunk<Sw32, 128>(l32, 2 * j + kg))
+                             : lds_read16(buf + rope_chunk<128>(l32, 2 * (j - 8) + kg));
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb8[j], S, 0, 0, 0);
+    }
+    // causal mask: token t0 + 8 (i / 4) + 4 kg + i % 4 is seen by rows at positions >= it
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + 8 * (i >> 2) + 4 * kg + (i & 3);
+      S[i] = t <= pos ? S[i] : -INFINITY;
+    }
+    float mx = S[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[i]);
+    mx = max_xor32(mx);
+    // lazy raise of the running max; the first tile a row sees sets it
+    const bool raise = mx > m_ref + kAtLazy || (m_ref == -INFINITY && mx != -INFINITY);
+    float alpha = 1.0f;
+    if (raise) {
+      const float m_new = fmaxf(m_ref, mx);
+      alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - m_new);
+      m_ref = m_new;
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) O[cb] *= alpha;
+      l_run *= alpha;
+    }
+    // weights against m_ref (0 while the row has seen nothing): bf16 pairs in the value
+    // operand's token order, summed as the MFMA uses them
+    const float m_off = m_ref == -INFINITY ? 0.0f : m_ref;
+    uint32_t pw[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const bf16x2 p = __builtin_convertvector(
+          f32x2{__builtin_amdgcn_exp2f(S[i] - m_off), __builtin_amdgcn_exp2f(S[i + 1] - m_off)},
+          bf16x2);
+      pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
+      psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
+    }
+    l_run += sum_xor32(psum);
+    // O^T[d][row] += V^T P^T: value operand rows (tokens) 4 kg + li / 4 (+ 8) of each
+    // 16-token step, columns 32 cb + 16 (G & 1) + 4 (li & 3)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]});
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int col = 32 * cb + 16 * (G & 1) + 4 * (li & 3);
+        const int r = 16 * ks + 4 * kg + (li >> 2);
+        const bf16x8 va = tr_pair(buf + kAtVOff + lat_piece<Sw32, 128>(r, col),
+                                  buf + kAtVOff + lat_piece<Sw32, 128>(r + 8, col));
+        O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, O[cb], 0, 0, 0);
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no tile load is still in flight when the workgroup ends
+
+  // out[row][d] = out_scale * O / l; O^T item e of block cb: column 32 cb + 8 (e / 4) +
+  // 4 kg + e % 4 of row l32
+  if (ir < sq) {
+    const float inv = l_run > 0.0f ? out_scale / l_run : 0.0f;
+    bf16* orow = out + (((size_t)b * sq + ir) * H + h) * kPfDv;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(bf16x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
+            bf16x4{(bf16)(O[cb][4 * q] * inv), (bf16)(O[cb][4 * q + 1] * inv),
+                   (bf16)(O[cb][4 * q + 2] * inv), (bf16)(O[cb][4 * q + 3] * inv)};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_t s,
+                          void* const* events) {
+  auto mark = [&](int i) {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_prefill_kv, dim3(p.L_pad / kKvTok, p.H, p.B), dim3(256), 0, s,
+                     (const bf16*)a.latent, a.lat_tok, a.lat_seq, a.block_table, a.bt_stride,
+                     p.paged, a.seqlens, p.max_seqlen, (const bf16*)a.w_uk, (const bf16*)a.w_uv,
+                     (bf16*)a.kbuf, (bf16*)a.vbuf, p.H, p.L_pad);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = mark(1);
+  if (e != hipSuccess) return e;
+  RopeFreq rf;
+  make_rope_freq(kPfDr, a.rope_theta, &rf);
+  const int n_qb = (p.sq + kAtRows - 1) / kAtRows;
+  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)((int64_t)p.B * p.H * n_qb)), dim3(256), 0, s,
+                     (const bf16*)a.q_nope, (const bf16*)a.q_rope, (const bf16*)a.rope,
+                     a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
+                     p.max_seqlen, (const bf16*)a.kbuf, (const bf16*)a.vbuf, (bf16*)a.out, p.B,
+                     p.H, p.sq, p.L_pad, a.softmax_scale * kLog2e, a.out_scale, rf);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = mark(2);
+  return e;
+}
+
+}  // namespace mla

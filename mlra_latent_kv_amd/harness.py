@@ -122,7 +122,7 @@ def make_params(inp: dict, num_splits: int = 0, flags: int = 0) -> B.MlaParams:
 
 
 def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None,
-              flags: int = 0) -> DeviceCase:
+              flags: int = 0, prefill: bool = False) -> DeviceCase:
     w = inp["workload"]
     dt = w.dtype
     dev = torch.device(device)
@@ -134,7 +134,8 @@ def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None,
                       w.d_rope, w.rope_theta, B.MLA_BF16 if dt == "bf16" else B.MLA_F32,
                       stream=stream)
     params = make_params(inp, num_splits, flags)
-    ws_bytes = B.workspace_size(params)
+    # prefill=True: the workspace of mla_prefill (up-projected keys and values)
+    ws_bytes = B.prefill_workspace_size(params) if prefill else B.workspace_size(params)
     bt = inp["block_table"]
     case = DeviceCase(
         params=params,
@@ -153,6 +154,16 @@ def to_device(inp: dict, device="cuda", num_splits: int = 0, stream=None,
                  if inp.get("latent_format") == "fp8" else None),
     )
     return case
+
+
+def run_prefill(case: DeviceCase, stream=None, out=None, events=None) -> torch.Tensor:
+    """mla_prefill on a case made with ``to_device(.., prefill=True)``: the case's queries are
+    its s_q tokens per sequence; returns out [B, s_q * H, d_v]."""
+    o = case.out if out is None else out
+    B.mla_prefill(case.params, case.q_nope, case.q_rope, case.latent_ptr, case.rope_ptr,
+                  case.seqlens, case.block_table, case.w_uk, case.w_uv, o, case.workspace,
+                  stream=stream, events=events)
+    return o
 
 
 def read_plan(case: DeviceCase) -> dict:

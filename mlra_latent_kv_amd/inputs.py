@@ -96,6 +96,19 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Prefill workloads (mla_prefill): every token of the sequence is new, s_q = seqlen query tokens
+# per sequence attend causally over the cache that holds them (the many-query regime of the
+# yololab MLA page, section 繁榮背後的代價), with the decode workloads' feature dims.
+PREFILL_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("prefill_bf16_b1_h128_l4096", batch=1, heads=128, branches=1, d_nope=128,
+                 d_v=128, d_cb=512, d_rope=64, dtype="bf16", paged=False, seqlen=4096, seed=1007),
+        Workload("prefill_bf16_paged_b4_h32_l4096", batch=4, heads=32, branches=1, d_nope=128,
+                 d_v=128, d_cb=512, d_rope=64, dtype="bf16", paged=True, seqlen=4096, seed=1008),
+    ]
+}
+
 
 # ----------------------------------------------------------------------------- storage formats
 

@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == {"mla_workspace_size", "mla_num_splits", "mla_decode", "mlra_decode",
                              "mla_decode_timed", "mlra_decode_timed", "mla_decode_noalloc",
                              "mla_rope_rotate", "mla_status_str", "mla_append_workspace_size",
-                             "mla_cache_append", "mla_decode_gated", "mlra_decode_gated"}
+                             "mla_cache_append", "mla_decode_gated", "mlra_decode_gated",
+                             "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_timed"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -432,3 +433,31 @@ def test_append_call_checks(lib):
     assert call(ws_bytes=10) == 4
     assert call(w_dkv=FAKE + 8) == 7 and call(workspace=FAKE + 16) == 7
     assert call(pages_used=None) == 1
+
+
+# ----------------------------------------------------------------------------- prefill
+def test_prefill_workspace_size_and_validation(lib):
+    """mla_prefill's host checks: every call below fails validation before anything is
+    launched (the pointers are never dereferenced)."""
+    p = params_for("mla_bf16_b32_h128_l4096", num_queries=300, max_seqlen=300)
+    # keys and values, [B, H, L_pad, 128] bf16 each, L_pad = 300 rounded up to 384
+    assert B.prefill_workspace_size(p) == 2 * 2 * 128 * 384 * 128 * 2
+    p1 = params_for("mla_bf16_b32_h128_l4096", num_queries=1, max_seqlen=1)
+    assert B.prefill_workspace_size(p1) == 2 * 2 * 128 * 128 * 128 * 2
+    ws = B.prefill_workspace_size(p)
+    assert call(lib, p, fn="mla_prefill", ws_bytes=ws - 1) == 4        # MLA_ERR_WORKSPACE
+    assert call(lib, p, fn="mla_prefill", q_nope=None) == 1            # MLA_ERR_NULL
+    assert call(lib, p, fn="mla_prefill", w_uv=None) == 1
+    assert call(lib, p, fn="mla_prefill", q_rope=FAKE + 8) == 7        # MLA_ERR_ALIGN
+    assert call(lib, p, fn="mla_prefill", out=FAKE + 2) == 7
+    assert call(lib, p, fn="mla_prefill", workspace=FAKE + 16) == 7
+    for over, status in [(dict(num_branches=4, d_latent=128), 3),     # MLA only
+                         (dict(d_latent=128), 3), (dict(d_nope=64), 3),
+                         (dict(flags=B.MLA_FLAG_QUERY_LATENT), 3),
+                         (dict(dtype=B.MLA_F32), 3), (dict(dtype=9), 5),
+                         (dict(page_size=16), 3), (dict(num_queries=-1), 2),
+                         (dict(batch=70000), 2), (dict(latent_stride_tok=580), 7)]:
+        q = params_for("mla_bf16_b32_h128_l4096", **{**dict(num_queries=300, max_seqlen=300), **over})
+        assert call(lib, q, fn="mla_prefill") == status, over
+    paged = params_for("mla_bf16_paged_b64_h32_l1k-32k", num_queries=5)
+    assert call(lib, paged, fn="mla_prefill", block_table=None) == 1

@@ -1,0 +1,123 @@
+"""GPU prefill (mla_prefill: many new tokens per sequence, un-absorbed) against the fp64
+oracle's prefill, which computes the same causal definition as the multi-token decode (token
+i at position L - s_q + i sees tokens 0 .. L - s_q + i).  Cases cover contiguous and paged
+caches, lengths that are not multiples of the 32-token key tiles, the 64-token pages or the
+128-token query and projection blocks, L < s_q (rows that see nothing are exactly zero), the
+default and the sharp query distributions, agreement with the absorbed decode path at small
+s_q, and the full-size prefill workload on sampled rows.  Bounds as for the decode (max-abs
+2e-2, rel-L2 1e-2, worst per-row rel-L2 5e-2).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from mlra_latent_kv_amd import inputs as I
+from test_gpu_parity import assert_close, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    import os
+    from mlra_latent_kv_amd import binding as B
+    if not os.path.exists(B.LIB_PATH):
+        from mlra_latent_kv_amd import build
+        build.build()
+    B.load()
+
+
+def oracle_prefill(inp, batches=None, heads=None):
+    w = inp["workload"]
+    return O.mla_prefill(inp["q_nope"], inp["q_rope"], inp["cache"], inp["seqlens"], inp["w_uk"],
+                         inp["w_uv"], num_queries=inp["num_queries"], d_rope=w.d_rope,
+                         scale=inp["softmax_scale"], out_scale=inp["out_scale"],
+                         theta=inp["rope_theta"], page_size=inp["page_size"],
+                         block_table=inp["block_table"], to_f64=lambda a: I.to_f64(a, w.dtype),
+                         batches=batches, heads=heads)
+
+
+def gpu_prefill(inp):
+    import torch
+    from mlra_latent_kv_amd import harness as H
+    case = H.to_device(inp, prefill=True)
+    out = H.run_prefill(case)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), case
+
+
+H128 = I.WORKLOADS["mla_bf16_b32_h128_l4096"]
+H32P = I.WORKLOADS["mla_bf16_paged_b64_h32_l1k-32k"]
+PREFILL = I.PREFILL_WORKLOADS["prefill_bf16_b1_h128_l4096"]
+
+CASES = [
+    # (id, workload, s_q, lengths)
+    ("h128_contig_sq200", H128, 200, [300, 129]),
+    ("h32_paged_sq130", H32P, 130, [700, 64, 1, 130, 257]),
+    ("h32_paged_sq1", H32P, 1, [700, 64, 1, 33]),
+    ("h128_contig_sq33_tails", H128, 33, [33, 95, 161]),
+    ("h32_paged_sq257", H32P, 257, [257, 300, 2]),
+]
+
+
+@pytest.mark.parametrize("cid,w,sq,lens", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(cid, w, sq, lens):
+    for sharp in (False, True):
+        inp = I.make_inputs(w, seed=5, seqlens=lens, num_queries=sq,
+                            q_gain=I.sharp_q_gain(w) if sharp else 1.0)
+        got, _ = gpu_prefill(inp)
+        ref = oracle_prefill(inp)
+        assert got.shape == ref.shape == (len(lens), sq * w.heads, w.d_v)
+        for b, L in enumerate(lens):
+            dead = max(0, sq - L)  # query tokens before the sequence's first token
+            assert not got[b, : dead * w.heads].any(), "a token that sees nothing is not zero"
+        assert_close(got, ref, "bf16", f"{cid} sharp={sharp}")
+
+
+@pytest.mark.parametrize("sq", [1, 4, 16])
+def test_prefill_agrees_with_absorbed_decode(sq):
+    """The un-absorbed prefill and the absorbed multi-token decode compute one definition; on
+    the same inputs they agree to within the rounding of their different bf16 operands."""
+    import torch
+    from mlra_latent_kv_amd import harness as H
+    inp = I.make_inputs(H32P, seed=12, seqlens=[640, 70, 17], num_queries=sq,
+                        q_gain=I.sharp_q_gain(H32P))
+    pre, _ = gpu_prefill(inp)
+    case = H.to_device(inp)
+    dec = case.run()
+    torch.cuda.synchronize()
+    dec = dec.float().cpu().numpy().astype(np.float64)
+    assert_close(pre, dec, "bf16", f"prefill vs absorbed decode s_q={sq}")
+    assert_close(pre, oracle_prefill(inp), "bf16", f"prefill vs oracle s_q={sq}")
+
+
+def test_prefill_empty_sequences_write_zeros():
+    inp = I.make_inputs(H128, seed=3, seqlens=[0, 0], num_queries=40, max_seqlen=64)
+    got, _ = gpu_prefill(inp)
+    assert not got.any()
+
+
+def test_prefill_full_size_sampled():
+    """The prefill workload (one sequence of 4096 new tokens, 128 heads) at full size, sharp
+    queries, on sampled rows: the first and last token, tokens at the 32-, 64- and 128-token
+    block edges, for heads of every 32-head quarter."""
+    w = PREFILL
+    inp = I.make_inputs(w, num_queries=w.seqlen, q_gain=I.sharp_q_gain(w))
+    got, _ = gpu_prefill(inp)
+    tokens = [0, 1, 31, 32, 63, 64, 127, 128, 2047, 2048, 4000, 4095]
+    heads = [0, 45, 77, 127]
+    rows = [i * w.heads + h for i in tokens for h in heads]
+    ref = oracle_prefill(inp, heads=rows)
+    note(f"  sampled {len(rows)} rows")
+    assert_close(got[:, rows], ref, "bf16", "prefill full size sampled")
+
+
+def test_prefill_rejects_unsupported():
+    from mlra_latent_kv_amd import binding as B
+    from mlra_latent_kv_amd import harness as H
+    inp = I.make_inputs(I.WORKLOADS["mlra4_bf16_b32_h32_l8192"], seed=1, seqlens=[10],
+                        num_queries=4)
+    p = H.make_params(inp)
+    with pytest.raises(B.MlaError, match="UNSUPPORTED"):
+        B.prefill_workspace_size(p)
