@@ -104,7 +104,7 @@ struct PrefillPlan {
   int B, H, sq;       // sequences, weight heads, query tokens per sequence (rows s_q x H)
   int paged, max_seqlen;
   int L_pad;          // key rows per (sequence, head) in the workspace: max_seqlen rounded up
-                      // to the projection's 128-token blocks
+                      // to the projection's 256-token blocks
   size_t off_k, off_v, bytes;
 };
 

@@ -30,18 +30,20 @@ using namespace tile;
 constexpr int kPfDc = 512, kPfDn = 128, kPfDv = 128, kPfDr = 64;
 
 // ----------------------------------------------------------------------------- K and V
-// One workgroup (4 waves) per (sequence b, block of 128 tokens, head h).  Wave w computes
-// tokens 64 (w & 1) .. +63 (two 32-row M blocks) of part w >> 1 (0: K, 1: V), all 128
-// output columns (four 32-column N blocks), MFMA 32x32x16 over the 512 latent columns in
-// eight chunks of 64.  Each chunk stages, by direct-to-LDS loads, the 128 latent rows
-// (128 bytes each), W_UK[h]'s 128 rows (its columns of the chunk) and W_UV[h]'s 64 rows of
-// the chunk (256 bytes each); double-buffered.
-constexpr int kKvTok = 128, kKvChunk = 64, kKvChunks = kPfDc / kKvChunk;
-constexpr int kKvABytes = kKvTok * kKvChunk * 2;     // 16 KiB
+// One workgroup (8 waves, two per SIMD) per (sequence b, block of 256 tokens, head h).  Wave w
+// computes tokens 64 (w & 3) .. +63 (two 32-row M blocks) of part w >> 2 (0: K, 1: V), all
+// 128 output columns (four 32-column N blocks), MFMA 32x32x16 over the 512 latent columns in
+// eight chunks of 64.  Each chunk stages, by direct-to-LDS loads, the 256 latent rows (128
+// bytes of each), W_UK[h]'s 128 rows (their columns of the chunk) and W_UV[h]'s 64 rows of the
+// chunk (256 bytes each); double-buffered, so one chunk's 64 MFMAs per SIMD cover the next
+// one's loads.
+constexpr int kKvTok = 256, kKvChunk = 64, kKvChunks = kPfDc / kKvChunk, kKvWaves = 8;
+constexpr int kKvABytes = kKvTok * kKvChunk * 2;     // 32 KiB
 constexpr int kKvBkBytes = kPfDn * kKvChunk * 2;     // 16 KiB
 constexpr int kKvBvBytes = kKvChunk * kPfDv * 2;     // 16 KiB
 constexpr int kKvStage = kKvABytes + kKvBkBytes + kKvBvBytes;
-constexpr int kKvIssues = 12;                        // loads per wave per chunk (48 per stage)
+constexpr int kKvLoads = kKvStage / 1024;            // 1 KiB loads per stage: 64
+constexpr int kKvIssues = kKvLoads / kKvWaves;       // per wave: 8
 
 // 128-byte rows (8 chunks, two rows per 256-byte bank line): chunk c of row r sits at
 // c ^ ((r / 2) mod 8), so 16 consecutive rows read at one chunk hit 16 distinct slots
@@ -49,7 +51,7 @@ __device__ __forceinline__ uint32_t row128(int r, int c) {
   return (uint32_t)(r * 128 + 16 * (c ^ ((r >> 1) & 7)));
 }
 
-__global__ __launch_bounds__(256, 1) void k_prefill_kv(
+__global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     const bf16* __restrict__ latent, int64_t lat_tok, int64_t lat_seq,
     const int32_t* __restrict__ bt, int64_t bt_stride, int paged,
     const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ w_uk,
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_kv(
   struct Smem {
     char st[2][kKvStage];
   };
-  __shared__ __align__(16) Smem sm;  // 96 KiB, reused for the output tile
+  __shared__ __align__(16) Smem sm;  // 128 KiB, reused for the output tile
   const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -69,15 +71,15 @@ __global__ __launch_bounds__(256, 1) void k_prefill_kv(
   const char* wk = reinterpret_cast<const char*>(w_uk + (size_t)h * kPfDn * kPfDc);
   const char* wv = reinterpret_cast<const char*>(w_uv + (size_t)h * kPfDc * kPfDv);
 
-  // wave w issues loads 12w .. 12w + 11 of a stage: 0..15 latent rows 8i.., 16..31 W_UK rows
-  // 8(i - 16).., 32..47 W_UV rows 4(i - 32).. (one KiB each); rows past the sequence read as
+  // wave w issues loads 8w .. 8w + 7 of a stage: 0..31 latent rows 8i.., 32..47 W_UK rows
+  // 8(i - 32).., 48..63 W_UV rows 4(i - 48).. (one KiB each); rows past the sequence read as
   // zeros (the descriptor ends at its last token)
   auto issue = [&](int q) {
     char* s = sm.st[q & 1];
 #pragma unroll
     for (int u = 0; u < kKvIssues; ++u) {
       const int i = kKvIssues * w + u;  // uniform
-      if (i < 16) {
+      if (i < 32) {
         const int r0 = 8 * i, t = t0 + r0;  // 8 rows of one page
         const int valid = max(0, min(8, L - t));
         const bf16* base;
@@ -92,19 +94,19 @@ __global__ __launch_bounds__(256, 1) void k_prefill_kv(
         const int r = lane >> 3, c = lane & 7;
         dma16(rsrc(base, vu * lat_row_b), s + r0 * 128,
               r * lat_row_b + q * 128 + 16 * (c ^ (((r0 + r) >> 1) & 7)));
-      } else if (i < 32) {
-        const int r0 = 8 * (i - 16), r = r0 + (lane >> 3), c = lane & 7;
+      } else if (i < 48) {
+        const int r0 = 8 * (i - 32), r = r0 + (lane >> 3), c = lane & 7;
         dma16(rsrc(wk, kPfDn * kPfDc * 2), s + kKvABytes + r0 * 128,
               r * (kPfDc * 2) + q * 128 + 16 * (c ^ ((r >> 1) & 7)));
       } else {
-        const int r0 = 4 * (i - 32), r = r0 + (lane >> 4), c = lane & 15;
+        const int r0 = 4 * (i - 48), r = r0 + (lane >> 4), c = lane & 15;
         dma16(rsrc(wv, kPfDc * kPfDv * 2), s + kKvABytes + kKvBkBytes + r0 * 256,
               (q * kKvChunk + r) * (kPfDv * 2) + 16 * (c ^ lat_sw<Sw32>(r)));
       }
     }
   };
 
-  const int mh = w & 1, part = w >> 1;
+  const int mq = w & 3, part = w >> 2;
   f32x16 acc[2][4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_kv(
       bf16x8 a[2], bo[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int r = 64 * mh + 32 * mb + l32;
+        const int r = 64 * mq + 32 * mb + l32;
         a[mb] = lds_read16(s + row128(r, 2 * j + kg));
       }
 #pragma unroll
@@ -150,31 +152,36 @@ __global__ __launch_bounds__(256, 1) void k_prefill_kv(
     lds_barrier();  // every wave is done with this stage before it is refilled
   }
 
-  // ---- output: the 128 x 256 tile (K | V) through LDS, then whole 256-byte rows.  D layout:
-  // lane (column l32 of N block nb, half kg), item i -> token 8 (i / 4) + 4 kg + i % 4 of the
-  // M block.
-  constexpr int kOutPitch = 2 * 2 * kPfDv + 16;  // bytes per token row: K | V, padded
+  // ---- output: each part's 256 x 128 tile through LDS in turn, then whole 256-byte rows.
+  // D layout: lane (column l32 of N block nb, half kg), item i -> token 8 (i / 4) + 4 kg +
+  // i % 4 of the M block.
+  constexpr int kOutPitch = 2 * kPfDv + 16;  // bytes per token row, padded
   static_assert(kKvTok * kOutPitch <= sizeof(Smem), "output tile exceeds the LDS");
   char* o = reinterpret_cast<char*>(&sm);
+  const size_t head_off = ((size_t)b * H + h) * L_pad + t0;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int pt = 0; pt < 2; ++pt) {
+    if (part == pt) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = 64 * mh + 32 * mb + 8 * (i >> 2) + 4 * kg + (i & 3);
-        *(bf16*)(o + t * kOutPitch + 2 * (kPfDv * part + 32 * nb + l32)) = (bf16)acc[mb][nb][i];
-      }
-  __syncthreads();
-  // thread tid: 16 bytes of each of rows tid / 32 + 8 k (k = 0 .. 15), part (tid / 16) & 1
-  const size_t head_off = ((size_t)b * H + h) * L_pad;
-  const int pc = tid & 15, pp = (tid >> 4) & 1, pr = tid >> 5;
-  bf16* dst = pp == 0 ? kout : vout;
-#pragma unroll 4
-  for (int k = 0; k < kKvTok / 8; ++k) {
-    const int r = pr + 8 * k;
-    *(bf16x8*)(dst + (head_off + t0 + r) * kPfDv + 8 * pc) =
-        *(const bf16x8*)(o + r * kOutPitch + 2 * (kPfDv * pp + 8 * pc));
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int t = 64 * mq + 32 * mb + 8 * (i >> 2) + 4 * kg + (i & 3);
+            *(bf16*)(o + t * kOutPitch + 2 * (32 * nb + l32)) = (bf16)acc[mb][nb][i];
+          }
+    }
+    __syncthreads();
+    // thread tid: 16-byte piece tid % 16 of rows tid / 16 + 32 k (k = 0 .. 7)
+    bf16* dst = (pt == 0 ? kout : vout) + head_off * kPfDv;
+    const int pc = tid & 15, pr = tid >> 4;
+#pragma unroll
+    for (int k = 0; k < kKvTok / 32; ++k) {
+      const int r = pr + 32 * k;
+      *(bf16x8*)(dst + (size_t)r * kPfDv + 8 * pc) = *(const bf16x8*)(o + r * kOutPitch + 16 * pc);
+    }
+    __syncthreads();
   }
 }
 
@@ -205,10 +212,17 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(
     char ring[kAtRing][kAtBuf];
   };
   __shared__ __align__(16) Smem sm;  // 60 KiB
-  // heaviest query blocks first; the blocks of one (b, h) land on one XCD when B H % 8 == 0
+  // XCD-aware order.  Blocks go round-robin over the 8 XCDs, so block 8r + x is the r-th one
+  // XCD x runs.  Each XCD takes whole (b, h) pairs in turn, all query blocks of one pair
+  // back to back, heaviest (latest) first: the blocks of a pair read the same key and value
+  // tiles in the same order, and with two pairs in flight per XCD (64 workgroup slots) their
+  // 2 MiB each of K and V (at 4096 tokens) stay in that XCD's L2 instead of being fetched
+  // from HBM once per query block.
   const int n_qb = (sq + kAtRows - 1) / kAtRows;
-  const int bh = blockIdx.x % (B * H);
-  const int qb = n_qb - 1 - (int)(blockIdx.x / (B * H));
+  const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
+  const int bh = (r / n_qb) * 8 + x;
+  if (bh >= B * H) return;  // padding of the grid to whole groups of eight pairs
+  const int qb = n_qb - 1 - r % n_qb;
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -302,11 +316,14 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(
                              : lds_read16(buf + rope_chunk<128>(l32, 2 * (j - 8) + kg));
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb8[j], S, 0, 0, 0);
     }
-    // causal mask: token t0 + 8 (i / 4) + 4 kg + i % 4 is seen by rows at positions >= it
+    // causal mask: token t0 + 8 (i / 4) + 4 kg + i % 4 is seen by rows at positions >= it;
+    // only tiles that reach past the wave's first position need it (a uniform branch)
+    if (t0 + kTT - 1 > L - sq + iw) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = t0 + 8 * (i >> 2) + 4 * kg + (i & 3);
-      S[i] = t <= pos ? S[i] : -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int t = t0 + 8 * (i >> 2) + 4 * kg + (i & 3);
+        S[i] = t <= pos ? S[i] : -INFINITY;
+      }
     }
     float mx = S[0];
 #pragma unroll
@@ -380,7 +397,7 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_prefill_kv, dim3(p.L_pad / kKvTok, p.H, p.B), dim3(256), 0, s,
+  hipLaunchKernelGGL(k_prefill_kv, dim3(p.L_pad / kKvTok, p.H, p.B), dim3(64 * kKvWaves), 0, s,
                      (const bf16*)a.latent, a.lat_tok, a.lat_seq, a.block_table, a.bt_stride,
                      p.paged, a.seqlens, p.max_seqlen, (const bf16*)a.w_uk, (const bf16*)a.w_uv,
                      (bf16*)a.kbuf, (bf16*)a.vbuf, p.H, p.L_pad);
@@ -390,7 +407,8 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   RopeFreq rf;
   make_rope_freq(kPfDr, a.rope_theta, &rf);
   const int n_qb = (p.sq + kAtRows - 1) / kAtRows;
-  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)((int64_t)p.B * p.H * n_qb)), dim3(256), 0, s,
+  const int64_t groups = ((int64_t)p.B * p.H + 7) / 8;  // pairs (b, h) in groups of eight
+  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_qb)), dim3(256), 0, s,
                      (const bf16*)a.q_nope, (const bf16*)a.q_rope, (const bf16*)a.rope,
                      a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
                      p.max_seqlen, (const bf16*)a.kbuf, (const bf16*)a.vbuf, (bf16*)a.out, p.B,
