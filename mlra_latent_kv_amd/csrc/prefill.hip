@@ -10,7 +10,7 @@
 //
 //  * k_prefill_kv: K and V of every (sequence, head, token) into the workspace,
 //    [B][H][L_pad][128] each, as one MFMA GEMM [tokens x 512] . [512 x 256] per head;
-//  * k_prefill_attn: per (sequence, head, block of 128 query tokens), a flash-attention
+//  * k_prefill_attn: per (sequence, head, block of 256 query tokens), a flash-attention
 //    pass over the key tokens up to the block's last position: scores over the 128 key
 //    columns plus the cached rotary key (64), online softmax, values summed in registers.
 //
@@ -186,22 +186,26 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
 }
 
 // ----------------------------------------------------------------------------- attention
-// One workgroup (4 waves) per (sequence b, head h, block of 128 query tokens); wave w holds
-// query tokens i0 + 32w .. +31 (MFMA N = rows).  Key tiles of 32 tokens stream through a
-// ring of three LDS buffers: the K rows (128 columns, from the workspace) with the cached
+// One workgroup (8 waves, two per SIMD) per (sequence b, head h, block of 256 query tokens);
+// wave w holds query tokens i0 + 32w .. +31 (MFMA N = rows).  Each key tile crosses into LDS
+// once for all 256 rows (with 128-row blocks the blocks of one head fetched every tile twice
+// as often, mostly from beyond L2).  Key tiles of 32 tokens stream through a
+// ring of four LDS buffers: the K rows (128 columns, from the workspace) with the cached
 // rotary keys (64 columns, already rotated at their own positions) in the 192-wide tile
 // layout of the one-branch decode, and the V rows (128 columns) after them.  Per tile and
 // wave: S^T = K . Q^T (12 K-steps), causal mask, online softmax with a lazy max (raised only
 // past kLazyTau log2 units), O^T += V^T P^T (8 MFMAs, the value operand read transposed).
-constexpr int kAtRows = 128;
-constexpr int kAtRing = 3;
+constexpr int kAtWaves = 8;
+constexpr int kAtRows = 32 * kAtWaves;
+constexpr int kAtRing = 4;
 constexpr float kAtLazy = 8.0f;
 using GK = Geom<128>;                                  // K tile: 32 x 256 B + 32 x 128 B
 constexpr int kAtVOff = GK::kBufBytes;                 // V tile after it: 32 x 256 B
 constexpr int kAtBuf = GK::kBufBytes + kTT * 256;      // 20 KiB
-constexpr int kAtIssues = issues_per_wave<4, 128>(true) + 2;  // K rows, rope rows, V rows
+// loads per wave and tile: one of K rows, one of V rows, and for waves 0-3 one of rotary rows
+constexpr int kAtIssuesLo = 3, kAtIssuesHi = 2;
 
-__global__ __launch_bounds__(256, 2) void k_prefill_attn(
+__global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
     const bf16* __restrict__ rope, int64_t rope_tok, int64_t rope_seq,
     const int32_t* __restrict__ bt, int64_t bt_stride, int paged,
@@ -211,13 +215,11 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(
   struct Smem {
     char ring[kAtRing][kAtBuf];
   };
-  __shared__ __align__(16) Smem sm;  // 60 KiB
+  __shared__ __align__(16) Smem sm;  // 80 KiB
   // XCD-aware order.  Blocks go round-robin over the 8 XCDs, so block 8r + x is the r-th one
   // XCD x runs.  Each XCD takes whole (b, h) pairs in turn, all query blocks of one pair
   // back to back, heaviest (latest) first: the blocks of a pair read the same key and value
-  // tiles in the same order, and with two pairs in flight per XCD (64 workgroup slots) their
-  // 2 MiB each of K and V (at 4096 tokens) stay in that XCD's L2 instead of being fetched
-  // from HBM once per query block.
+  // tiles in the same order, and started together they find most tiles in that XCD's L2.
   const int n_qb = (sq + kAtRows - 1) / kAtRows;
   const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
   const int bh = (r / n_qb) * 8 + x;
@@ -252,13 +254,25 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(
     } else {
       rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
     }
-    issue_tile<Sw32, 4, 128>(buf, w, lane, kb + (size_t)t0 * kPfDn, rb, valid, 256, rope_row_b);
-    const __amdgpu_buffer_rsrc_t rv = rsrc(vb + (size_t)t0 * kPfDv, valid * 256);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r0 = 4 * (2 * w + u), r = r0 + (lane >> 4), c = lane & 15;
-      dma16(rv, buf + kAtVOff + r0 * 256, r * 256 + 16 * (c ^ lat_sw<Sw32>(r)));
+    // wave w: K rows 4w .. 4w + 3 and V rows 4w .. 4w + 3 (lane -> row 4w + lane / 16, physical
+    // chunk lane % 16, which fetches logical chunk (lane % 16) ^ swizzle(row)), and for w < 4
+    // the rotary rows 8w .. 8w + 7
+    const int r = 4 * w + (lane >> 4), c = lane & 15;
+    const uint32_t off = r * 256 + 16 * (c ^ lat_sw<Sw32>(r));
+    dma16(rsrc(kb + (size_t)t0 * kPfDn, valid * 256), buf + 4 * w * 256, off);
+    dma16(rsrc(vb + (size_t)t0 * kPfDv, valid * 256), buf + kAtVOff + 4 * w * 256, off);
+    if (w < 4) {
+      const int rt = 8 * w + (lane >> 3);
+      dma16(rsrc(rb, valid * rope_row_b), buf + GK::kRopeOff + w * 1024,
+            rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
     }
+  };
+  // tile k has landed for this wave: only the kAtRing - 2 younger tiles' loads may be out
+  auto wait_tile = [&]() {
+    if (w < 4)
+      wait_vmcnt<(kAtRing - 2) * kAtIssuesLo>();
+    else
+      wait_vmcnt<(kAtRing - 2) * kAtIssuesHi>();
   };
 
   // query as the B operand (K = 192 columns, N = 32 rows): lane (row l32, half kg), K-step j
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_attn(
 #pragma unroll
   for (int j = 0; j < kAtRing - 1; ++j) issue(j);
   for (int k = 0; k < n_tiles; ++k) {
-    wait_vmcnt<(kAtRing - 2) * kAtIssues>();  // tile k has landed for this wave
+    wait_tile();
     lds_barrier();                            // ... for every wave; tile k - 1's buffer is free
     issue(k + kAtRing - 1);
     const int t0 = kTT * k;
@@ -408,7 +422,7 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   make_rope_freq(kPfDr, a.rope_theta, &rf);
   const int n_qb = (p.sq + kAtRows - 1) / kAtRows;
   const int64_t groups = ((int64_t)p.B * p.H + 7) / 8;  // pairs (b, h) in groups of eight
-  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_qb)), dim3(256), 0, s,
+  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_qb)), dim3(64 * kAtWaves), 0, s,
                      (const bf16*)a.q_nope, (const bf16*)a.q_rope, (const bf16*)a.rope,
                      a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
                      p.max_seqlen, (const bf16*)a.kbuf, (const bf16*)a.vbuf, (bf16*)a.out, p.B,

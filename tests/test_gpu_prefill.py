@@ -2,7 +2,7 @@
 oracle's prefill, which computes the same causal definition as the multi-token decode (token
 i at position L - s_q + i sees tokens 0 .. L - s_q + i).  Cases cover contiguous and paged
 caches, lengths that are not multiples of the 32-token key tiles, the 64-token pages or the
-128-token query and projection blocks, L < s_q (rows that see nothing are exactly zero), the
+256-token query and projection blocks, L < s_q (rows that see nothing are exactly zero), the
 default and the sharp query distributions, agreement with the absorbed decode path at small
 s_q, and the full-size prefill workload on sampled rows.  Bounds as for the decode (max-abs
 2e-2, rel-L2 1e-2, worst per-row rel-L2 5e-2).
@@ -101,11 +101,11 @@ def test_prefill_empty_sequences_write_zeros():
 def test_prefill_full_size_sampled():
     """The prefill workload (one sequence of 4096 new tokens, 128 heads) at full size, sharp
     queries, on sampled rows: the first and last token, tokens at the 32-, 64- and 128-token
-    block edges, for heads of every 32-head quarter."""
+    block edges (256-token query blocks), for heads of every 32-head quarter."""
     w = PREFILL
     inp = I.make_inputs(w, num_queries=w.seqlen, q_gain=I.sharp_q_gain(w))
     got, _ = gpu_prefill(inp)
-    tokens = [0, 1, 31, 32, 63, 64, 127, 128, 2047, 2048, 4000, 4095]
+    tokens = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 2047, 2048, 4000, 4095]
     heads = [0, 45, 77, 127]
     rows = [i * w.heads + h for i in tokens for h in heads]
     ref = oracle_prefill(inp, heads=rows)
