@@ -227,8 +227,9 @@ mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
   q.paged = p->page_size == kPage;
   q.max_seqlen = p->max_seqlen;
   q.L_pad = (int)(ceil_div(std::max(p->max_seqlen, 1), 256) * 256);
-  // attention grid: (sequence, head, block of 128 query tokens) in one dimension
-  if ((ceil_div((int64_t)q.B * q.H, 8) * 8) * ceil_div(q.sq, 256) > INT32_MAX) return MLA_ERR_SHAPE;
+  // attention grid, one dimension: (sequence, head, pair of 256-token query blocks)
+  if ((ceil_div((int64_t)q.B * q.H, 8) * 8) * ceil_div(ceil_div(q.sq, 256), 2) > INT32_MAX)
+    return MLA_ERR_SHAPE;
   const size_t kv = (size_t)q.B * q.H * q.L_pad * 128 * 2;
   q.off_k = 0;
   q.off_v = align_up(kv);

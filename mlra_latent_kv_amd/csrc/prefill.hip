@@ -216,189 +216,201 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     char ring[kAtRing][kAtBuf];
   };
   __shared__ __align__(16) Smem sm;  // 80 KiB
-  // XCD-aware order.  Blocks go round-robin over the 8 XCDs, so block 8r + x is the r-th one
-  // XCD x runs.  Each XCD takes whole (b, h) pairs in turn, all query blocks of one pair
-  // back to back, heaviest (latest) first: the blocks of a pair read the same key and value
-  // tiles in the same order, and started together they find most tiles in that XCD's L2.
+  // Causal balance: a workgroup takes query blocks n_qb - 1 - j and j of one (b, h), the
+  // heavy one first, so every workgroup scans about n_qb + 1 blocks' worth of key tiles
+  // (a lone middle block when n_qb is odd).  XCD-aware order: blocks go round-robin over the
+  // 8 XCDs, so block 8r + x is the r-th one XCD x runs; each XCD takes whole (b, h) in turn,
+  // all workgroups of one back to back: they read the same key and value tiles in the same
+  // order, and started together they find most tiles in that XCD's L2.
   const int n_qb = (sq + kAtRows - 1) / kAtRows;
+  const int n_wg = (n_qb + 1) / 2;
   const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
-  const int bh = (r / n_qb) * 8 + x;
+  const int bh = (r / n_wg) * 8 + x;
   if (bh >= B * H) return;  // padding of the grid to whole groups of eight pairs
-  const int qb = n_qb - 1 - r % n_qb;
+  const int jb = r % n_wg;
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, kg = lane >> 5;
   const int L = min(max(seqlens[b], 0), max_seqlen);
-  const int i0 = qb * kAtRows;
-  const int iw = i0 + 32 * w;                 // this wave's first query token
-  const int ir = iw + l32;                    // this lane's query token (row)
-  const int pos = L - sq + ir;                // its position (< 0: sees nothing)
-  const int pos_w = L - sq + iw + 31;         // the wave's last position
-  const int pos_g = min(L - sq + i0 + kAtRows - 1, L - 1);  // the workgroup's last position
-  const int n_tiles = pos_g >= 0 ? pos_g / kTT + 1 : 0;
-
   const bf16* kb = kbuf + ((size_t)b * H + h) * L_pad * kPfDn;
   const bf16* vb = vbuf + ((size_t)b * H + h) * L_pad * kPfDv;
   const uint32_t rope_row_b = (uint32_t)(rope_tok * 2);
-  // tile k into its ring buffer; past n_tiles the loads go out with no valid row (zeros, no
-  // memory touched) so that every wave issues the same count and every wait is fixed
-  auto issue = [&](int k) {
-    char* buf = sm.ring[k % kAtRing];
-    const int t0 = kTT * k;
-    const int valid = __builtin_amdgcn_readfirstlane(k < n_tiles ? max(0, min(kTT, L - t0)) : 0);
-    const bf16* rb;
-    if (paged) {
-      const int64_t pg = valid > 0 ? bt[(int64_t)b * bt_stride + t0 / kPage] : 0;
-      rb = rope + pg * rope_seq + (int64_t)(t0 % kPage) * rope_tok;
-    } else {
-      rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
-    }
-    // wave w: K rows 4w .. 4w + 3 and V rows 4w .. 4w + 3 (lane -> row 4w + lane / 16, physical
-    // chunk lane % 16, which fetches logical chunk (lane % 16) ^ swizzle(row)), and for w < 4
-    // the rotary rows 8w .. 8w + 7
-    const int r = 4 * w + (lane >> 4), c = lane & 15;
-    const uint32_t off = r * 256 + 16 * (c ^ lat_sw<Sw32>(r));
-    dma16(rsrc(kb + (size_t)t0 * kPfDn, valid * 256), buf + 4 * w * 256, off);
-    dma16(rsrc(vb + (size_t)t0 * kPfDv, valid * 256), buf + kAtVOff + 4 * w * 256, off);
-    if (w < 4) {
-      const int rt = 8 * w + (lane >> 3);
-      dma16(rsrc(rb, valid * rope_row_b), buf + GK::kRopeOff + w * 1024,
-            rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
-    }
-  };
-  // tile k has landed for this wave: only the kAtRing - 2 younger tiles' loads may be out
-  auto wait_tile = [&]() {
-    if (w < 4)
-      wait_vmcnt<(kAtRing - 2) * kAtIssuesLo>();
-    else
-      wait_vmcnt<(kAtRing - 2) * kAtIssuesHi>();
-  };
-
-  // query as the B operand (K = 192 columns, N = 32 rows): lane (row l32, half kg), K-step j
-  // holds columns 16 j + 8 kg .. +7; the rotary steps 8 .. 11 rotated at the row's position;
-  // scaled by softmax_scale * log2(e).  Rows past s_q load row s_q - 1 and are not stored.
-  bf16x8 qb8[12];
-  {
-    const int irc = min(ir, sq - 1);
-    const size_t row = ((size_t)b * sq + irc) * H + h;
-    const bf16* qn = q_nope + row * kPfDn + 8 * kg;
-    const bf16* qr = q_rope + row * kPfDr + 8 * kg;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8 v = *(const bf16x8*)(qn + 16 * j);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qb8[j][e] = (bf16)((float)v[e] * qscale);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 v = *(const bf16x8*)(qr + 16 * j);
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int k = (16 * j + 8 * kg + e) >> 1;  // rotation pair
-        float cs, sn;
-        rope_cos_sin(max(pos, 0), rf.f[k], &cs, &sn);
-        const float x0 = (float)v[e], x1 = (float)v[e + 1];
-        qb8[8 + j][e] = (bf16)((x0 * cs - x1 * sn) * qscale);
-        qb8[8 + j][e + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
-      }
-    }
-  }
-
   const int G = lane >> 4, li = lane & 15;
-  float m_ref = -INFINITY, l_run = 0.0f;
-  f32x16 O[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) O[cb] = f32x16{};
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-#pragma unroll
-  for (int j = 0; j < kAtRing - 1; ++j) issue(j);
-  for (int k = 0; k < n_tiles; ++k) {
-    wait_tile();
-    lds_barrier();                            // ... for every wave; tile k - 1's buffer is free
-    issue(k + kAtRing - 1);
-    const int t0 = kTT * k;
-    if (t0 > pos_w) continue;  // every row of the wave is before this tile (uniform)
-    const char* buf = sm.ring[k % kAtRing];
+  for (int pass = 0; pass < 2; ++pass) {
+    const int qb = pass == 0 ? n_qb - 1 - jb : jb;
+    if (pass == 1 && qb == n_qb - 1 - jb) break;  // the lone middle block
+    const int i0 = qb * kAtRows;
+    const int iw = i0 + 32 * w;                 // this wave's first query token
+    const int ir = iw + l32;                    // this lane's query token (row)
+    const int pos = L - sq + ir;                // its position (< 0: sees nothing)
+    const int pos_w = L - sq + iw + 31;         // the wave's last position
+    const int pos_g = min(L - sq + i0 + kAtRows - 1, L - 1);  // the block's last position
+    const int n_tiles = pos_g >= 0 ? pos_g / kTT + 1 : 0;
 
-    // scores S^T[t][row] over 8 key steps and 4 rotary steps
-    f32x16 S = f32x16{};
+    // tile k into its ring buffer; past n_tiles the loads go out with no valid row (zeros, no
+    // memory touched) so that every wave issues the same count and every wait is fixed
+    auto issue = [&](int k) {
+      char* buf = sm.ring[k % kAtRing];
+      const int t0 = kTT * k;
+      const int valid = __builtin_amdgcn_readfirstlane(k < n_tiles ? max(0, min(kTT, L - t0)) : 0);
+      const bf16* rb;
+      if (paged) {
+        const int64_t pg = valid > 0 ? bt[(int64_t)b * bt_stride + t0 / kPage] : 0;
+        rb = rope + pg * rope_seq + (int64_t)(t0 % kPage) * rope_tok;
+      } else {
+        rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
+      }
+      // wave w: K rows 4w .. 4w + 3 and V rows 4w .. 4w + 3 (lane -> row 4w + lane / 16, physical
+      // chunk lane % 16, which fetches logical chunk (lane % 16) ^ swizzle(row)), and for w < 4
+      // the rotary rows 8w .. 8w + 7
+      const int r = 4 * w + (lane >> 4), c = lane & 15;
+      const uint32_t off = r * 256 + 16 * (c ^ lat_sw<Sw32>(r));
+      dma16(rsrc(kb + (size_t)t0 * kPfDn, valid * 256), buf + 4 * w * 256, off);
+      dma16(rsrc(vb + (size_t)t0 * kPfDv, valid * 256), buf + kAtVOff + 4 * w * 256, off);
+      if (w < 4) {
+        const int rt = 8 * w + (lane >> 3);
+        dma16(rsrc(rb, valid * rope_row_b), buf + GK::kRopeOff + w * 1024,
+              rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
+      }
+    };
+    // tile k has landed for this wave: only the kAtRing - 2 younger tiles' loads may be out
+    auto wait_tile = [&]() {
+      if (w < 4)
+        wait_vmcnt<(kAtRing - 2) * kAtIssuesLo>();
+      else
+        wait_vmcnt<(kAtRing - 2) * kAtIssuesHi>();
+    };
+
+    // query as the B operand (K = 192 columns, N = 32 rows): lane (row l32, half kg), K-step j
+    // holds columns 16 j + 8 kg .. +7; the rotary steps 8 .. 11 rotated at the row's position;
+    // scaled by softmax_scale * log2(e).  Rows past s_q load row s_q - 1 and are not stored.
+    bf16x8 qb8[12];
+    {
+      const int irc = min(ir, sq - 1);
+      const size_t row = ((size_t)b * sq + irc) * H + h;
+      const bf16* qn = q_nope + row * kPfDn + 8 * kg;
+      const bf16* qr = q_rope + row * kPfDr + 8 * kg;
 #pragma unroll
-    for (int j = 0; j < 12; ++j) {
-      const bf16x8 a = j < 8 ? lds_read16(buf + lat_chunk<Sw32, 128>(l32, 2 * j + kg))
-                             : lds_read16(buf + rope_chunk<128>(l32, 2 * (j - 8) + kg));
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb8[j], S, 0, 0, 0);
-    }
-    // causal mask: token t0 + 8 (i / 4) + 4 kg + i % 4 is seen by rows at positions >= it;
-    // only tiles that reach past the wave's first position need it (a uniform branch)
-    if (t0 + kTT - 1 > L - sq + iw) {
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 v = *(const bf16x8*)(qn + 16 * j);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = t0 + 8 * (i >> 2) + 4 * kg + (i & 3);
-        S[i] = t <= pos ? S[i] : -INFINITY;
+        for (int e = 0; e < 8; ++e) qb8[j][e] = (bf16)((float)v[e] * qscale);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 v = *(const bf16x8*)(qr + 16 * j);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int k = (16 * j + 8 * kg + e) >> 1;  // rotation pair
+          float cs, sn;
+          rope_cos_sin(max(pos, 0), rf.f[k], &cs, &sn);
+          const float x0 = (float)v[e], x1 = (float)v[e + 1];
+          qb8[8 + j][e] = (bf16)((x0 * cs - x1 * sn) * qscale);
+          qb8[8 + j][e + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
+        }
       }
     }
-    float mx = S[0];
+
+    float m_ref = -INFINITY, l_run = 0.0f;
+    f32x16 O[4];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[i]);
-    mx = max_xor32(mx);
-    // lazy raise of the running max; the first tile a row sees sets it
-    const bool raise = mx > m_ref + kAtLazy || (m_ref == -INFINITY && mx != -INFINITY);
-    float alpha = 1.0f;
-    if (raise) {
-      const float m_new = fmaxf(m_ref, mx);
-      alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - m_new);
-      m_ref = m_new;
-    }
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    for (int cb = 0; cb < 4; ++cb) O[cb] = f32x16{};
+
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) O[cb] *= alpha;
-      l_run *= alpha;
-    }
-    // weights against m_ref (0 while the row has seen nothing): bf16 pairs in the value
-    // operand's token order, summed as the MFMA uses them
-    const float m_off = m_ref == -INFINITY ? 0.0f : m_ref;
-    uint32_t pw[2][4];
-    float psum = 0.0f;
+    for (int j = 0; j < kAtRing - 1; ++j) issue(j);
+    for (int k = 0; k < n_tiles; ++k) {
+      wait_tile();
+      lds_barrier();                            // ... for every wave; tile k - 1's buffer is free
+      issue(k + kAtRing - 1);
+      const int t0 = kTT * k;
+      if (t0 > pos_w) continue;  // every row of the wave is before this tile (uniform)
+      const char* buf = sm.ring[k % kAtRing];
+
+      // scores S^T[t][row] over 8 key steps and 4 rotary steps
+      f32x16 S = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const bf16x2 p = __builtin_convertvector(
-          f32x2{__builtin_amdgcn_exp2f(S[i] - m_off), __builtin_amdgcn_exp2f(S[i + 1] - m_off)},
-          bf16x2);
-      pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
-      psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
-    }
-    l_run += sum_xor32(psum);
-    // O^T[d][row] += V^T P^T: value operand rows (tokens) 4 kg + li / 4 (+ 8) of each
-    // 16-token step, columns 32 cb + 16 (G & 1) + 4 (li & 3)
+      for (int j = 0; j < 12; ++j) {
+        const bf16x8 a = j < 8 ? lds_read16(buf + lat_chunk<Sw32, 128>(l32, 2 * j + kg))
+                               : lds_read16(buf + rope_chunk<128>(l32, 2 * (j - 8) + kg));
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb8[j], S, 0, 0, 0);
+      }
+      // causal mask: token t0 + 8 (i / 4) + 4 kg + i % 4 is seen by rows at positions >= it;
+      // only tiles that reach past the wave's first position need it (a uniform branch)
+      if (t0 + kTT - 1 > L - sq + iw) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]});
+        for (int i = 0; i < 16; ++i) {
+          const int t = t0 + 8 * (i >> 2) + 4 * kg + (i & 3);
+          S[i] = t <= pos ? S[i] : -INFINITY;
+        }
+      }
+      float mx = S[0];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int col = 32 * cb + 16 * (G & 1) + 4 * (li & 3);
-        const int r = 16 * ks + 4 * kg + (li >> 2);
-        const bf16x8 va = tr_pair(buf + kAtVOff + lat_piece<Sw32, 128>(r, col),
-                                  buf + kAtVOff + lat_piece<Sw32, 128>(r + 8, col));
-        O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, O[cb], 0, 0, 0);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[i]);
+      mx = max_xor32(mx);
+      // lazy raise of the running max; the first tile a row sees sets it
+      const bool raise = mx > m_ref + kAtLazy || (m_ref == -INFINITY && mx != -INFINITY);
+      float alpha = 1.0f;
+      if (raise) {
+        const float m_new = fmaxf(m_ref, mx);
+        alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - m_new);
+        m_ref = m_new;
+      }
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) O[cb] *= alpha;
+        l_run *= alpha;
+      }
+      // weights against m_ref (0 while the row has seen nothing): bf16 pairs in the value
+      // operand's token order, summed as the MFMA uses them
+      const float m_off = m_ref == -INFINITY ? 0.0f : m_ref;
+      uint32_t pw[2][4];
+      float psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const bf16x2 p = __builtin_convertvector(
+            f32x2{__builtin_amdgcn_exp2f(S[i] - m_off), __builtin_amdgcn_exp2f(S[i + 1] - m_off)},
+            bf16x2);
+        pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
+      }
+      l_run += sum_xor32(psum);
+      // O^T[d][row] += V^T P^T: value operand rows (tokens) 4 kg + li / 4 (+ 8) of each
+      // 16-token step, columns 32 cb + 16 (G & 1) + 4 (li & 3)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pb =
+            __builtin_bit_cast(bf16x8, u32x4{pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]});
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const int col = 32 * cb + 16 * (G & 1) + 4 * (li & 3);
+          const int r = 16 * ks + 4 * kg + (li >> 2);
+          const bf16x8 va = tr_pair(buf + kAtVOff + lat_piece<Sw32, 128>(r, col),
+                                    buf + kAtVOff + lat_piece<Sw32, 128>(r + 8, col));
+          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, O[cb], 0, 0, 0);
+        }
       }
     }
-  }
-  wait_vmcnt<0>();  // no tile load is still in flight when the workgroup ends
+    // no tile load is still in flight when the block ends (the ring refills for the next one,
+    // or the workgroup ends), and every wave is done reading the ring
+    wait_vmcnt<0>();
+    lds_barrier();
 
-  // out[row][d] = out_scale * O / l; O^T item e of block cb: column 32 cb + 8 (e / 4) +
-  // 4 kg + e % 4 of row l32
-  if (ir < sq) {
-    const float inv = l_run > 0.0f ? out_scale / l_run : 0.0f;
-    bf16* orow = out + (((size_t)b * sq + ir) * H + h) * kPfDv;
+    // out[row][d] = out_scale * O / l; O^T item e of block cb: column 32 cb + 8 (e / 4) +
+    // 4 kg + e % 4 of row l32
+    if (ir < sq) {
+      const float inv = l_run > 0.0f ? out_scale / l_run : 0.0f;
+      bf16* orow = out + (((size_t)b * sq + ir) * H + h) * kPfDv;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(bf16x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
-            bf16x4{(bf16)(O[cb][4 * q] * inv), (bf16)(O[cb][4 * q + 1] * inv),
-                   (bf16)(O[cb][4 * q + 2] * inv), (bf16)(O[cb][4 * q + 3] * inv)};
+        for (int q = 0; q < 4; ++q)
+          *(bf16x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
+              bf16x4{(bf16)(O[cb][4 * q] * inv), (bf16)(O[cb][4 * q + 1] * inv),
+                     (bf16)(O[cb][4 * q + 2] * inv), (bf16)(O[cb][4 * q + 3] * inv)};
+    }
   }
 }
 
@@ -420,9 +432,9 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   if (e != hipSuccess) return e;
   RopeFreq rf;
   make_rope_freq(kPfDr, a.rope_theta, &rf);
-  const int n_qb = (p.sq + kAtRows - 1) / kAtRows;
+  const int n_wg = ((p.sq + kAtRows - 1) / kAtRows + 1) / 2;  // workgroups per (b, h)
   const int64_t groups = ((int64_t)p.B * p.H + 7) / 8;  // pairs (b, h) in groups of eight
-  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_qb)), dim3(64 * kAtWaves), 0, s,
+  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_wg)), dim3(64 * kAtWaves), 0, s,
                      (const bf16*)a.q_nope, (const bf16*)a.q_rope, (const bf16*)a.rope,
                      a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
                      p.max_seqlen, (const bf16*)a.kbuf, (const bf16*)a.vbuf, (bf16*)a.out, p.B,
