@@ -410,9 +410,11 @@ mla_status mla_cache_append(const mla_append_params* p, const void* hidden, cons
  * MLA_ERR_UNSUPPORTED).  num_splits is not used.  Pointers of q_nope, q_rope, latent, rope,
  * w_uk, w_uv and out 16-byte aligned, cache strides multiples of 8 elements (MLA_ERR_ALIGN).
  * The workspace (>= mla_prefill_workspace_size bytes, 256-byte aligned, no initialisation)
- * receives the up-projected keys and values, [B, H, L_pad, 128] bf16 each, L_pad =
- * max_seqlen rounded up to a multiple of 256.  Two kernels run on `stream`: the up-projection
- * (a GEMM of the cached latents against W_UK and W_UV) and a causal flash-attention pass.
+ * receives the up-projected keys and values (B x H x L_pad x 128 bf16 each, L_pad =
+ * max_seqlen rounded up to a multiple of 256) and a copy of the rotary keys (B x L_pad x 64
+ * bf16), in an internal tiled order.  Two kernels run on `stream`: the up-projection (a GEMM
+ * of the cached latents against W_UK and W_UV, which also copies the rotary keys) and a
+ * causal flash-attention pass.
  */
 mla_status mla_prefill_workspace_size(const mla_params* p, size_t* bytes);
 mla_status mla_prefill(const mla_params* p, const void* q_nope, const void* q_rope,

@@ -336,6 +336,7 @@ mla_status run_prefill(const mla_params* p, const void* q_nope, const void* q_ro
   a.out_scale = p->out_scale;
   a.rope_theta = p->rope_theta;
   a.kbuf = static_cast<char*>(workspace) + plan.off_k;
+  a.rbuf = static_cast<char*>(workspace) + plan.off_r;
   a.vbuf = static_cast<char*>(workspace) + plan.off_v;
   return to_status(launch_prefill(plan, a, stream, events));
 }

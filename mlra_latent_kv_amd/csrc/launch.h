@@ -50,8 +50,9 @@ struct PrefillArgs {
   void* out;            // [B][s_q][H][128]
   int64_t lat_tok, lat_seq, rope_tok, rope_seq, bt_stride;
   float softmax_scale, out_scale, rope_theta;
-  void* kbuf;           // workspace: up-projected keys [B][H][L_pad][128]
-  void* vbuf;           // workspace: up-projected values [B][H][L_pad][128]
+  void* kbuf;           // workspace: up-projected keys, operand blocks [B][H][L_pad / 32][8 KiB]
+  void* rbuf;           // workspace: rotary keys, operand blocks [B][L_pad / 32][4 KiB]
+  void* vbuf;           // workspace: up-projected values, operand blocks [B][H][L_pad / 32][8 KiB]
 };
 // events (tracing, else null): three hipEvent_t recorded before the projection, between the
 // two kernels and after the attention

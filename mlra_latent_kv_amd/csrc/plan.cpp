@@ -231,8 +231,10 @@ mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
   if ((ceil_div((int64_t)q.B * q.H, 8) * 8) * ceil_div(ceil_div(q.sq, 256), 2) > INT32_MAX)
     return MLA_ERR_SHAPE;
   const size_t kv = (size_t)q.B * q.H * q.L_pad * 128 * 2;
+  const size_t r = (size_t)q.B * q.L_pad * 64 * 2;
   q.off_k = 0;
-  q.off_v = align_up(kv);
+  q.off_r = align_up(kv);
+  q.off_v = q.off_r + align_up(r);
   q.bytes = q.off_v + align_up(kv);
   *plan = q;
   return MLA_OK;

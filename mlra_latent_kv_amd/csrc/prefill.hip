@@ -18,6 +18,8 @@
 // rotated there, and it sees the tokens up to and including itself; a token that sees none
 // writes zeros.  Layouts as the multi-token decode: q_nope [B, s_q, H, 128], q_rope
 // [B, s_q, H, 64], out [B, s_q, H, 128].
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "tile_bf16.h"
@@ -28,6 +30,15 @@ namespace {
 using namespace tile;
 
 constexpr int kPfDc = 512, kPfDn = 128, kPfDv = 128, kPfDr = 64;
+
+// Workspace layout: operand blocks.  Each 32-token tile of keys, values and rotary keys is
+// stored as the MFMA operands the attention feeds, 1 KiB per block, lane i's 8 bf16 at
+// 16 i, so the attention loads whole tiles as contiguous KiBs and reads them lane-linearly.
+//   keys [B][H][tiles][8 steps j][64]:      lane (t = i % 32, g = i / 32) holds K[t][16 j + 8 g ..]
+//   rotary [B][tiles][4 steps m][64]:      rope[t][16 m + 8 g ..] (as cached: already rotated)
+//   values [B][H][tiles][2 ks][4 cb][64]:  V[16 ks + 4 g + e % 4 + 8 (e / 4)][32 cb + t],
+//                                          e = 0..7 (the score layout's token order)
+constexpr int kTileK = kTT * kPfDn * 2, kTileR = kTT * kPfDr * 2, kTileV = kTT * kPfDv * 2;
 
 // ----------------------------------------------------------------------------- K and V
 // One workgroup (8 waves, two per SIMD) per (sequence b, block of 256 tokens, head h).  Wave w
@@ -53,10 +64,11 @@ __device__ __forceinline__ uint32_t row128(int r, int c) {
 
 __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     const bf16* __restrict__ latent, int64_t lat_tok, int64_t lat_seq,
+    const bf16* __restrict__ rope, int64_t rope_tok, int64_t rope_seq,
     const int32_t* __restrict__ bt, int64_t bt_stride, int paged,
     const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ w_uk,
-    const bf16* __restrict__ w_uv, bf16* __restrict__ kout, bf16* __restrict__ vout, int H,
-    int L_pad) {
+    const bf16* __restrict__ w_uv, bf16* __restrict__ kout, bf16* __restrict__ rout,
+    bf16* __restrict__ vout, int H, int L_pad) {
   struct Smem {
     char st[2][kKvStage];
   };
@@ -106,6 +118,26 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     }
   };
 
+  // the first head's workgroups also copy the block's rotary keys into the workspace as
+  // operand blocks: thread tid, pieces tid + 512 u = (tile, step m, lane i) in order; zeros
+  // past the sequence
+  if (h == 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = tid + 512 * u;
+      const int tl = pc >> 8, m = (pc >> 6) & 3, i = pc & 63;
+      const int t = t0 + kTT * tl + (i & 31);
+      bf16x8 v = bf16x8{};
+      if (t < L) {
+        const bf16* row = paged ? rope + (int64_t)bt[(int64_t)b * bt_stride + t / kPage] * rope_seq +
+                                      (int64_t)(t % kPage) * rope_tok
+                                : rope + (int64_t)b * rope_seq + (int64_t)t * rope_tok;
+        v = *(const bf16x8*)(row + 16 * m + 8 * (i >> 5));
+      }
+      *(bf16x8*)(rout + ((size_t)b * L_pad + t0) * kPfDr + 8 * (size_t)pc) = v;
+    }
+  }
+
   const int mq = w & 3, part = w >> 2;
   f32x16 acc[2][4];
 #pragma unroll
@@ -152,15 +184,18 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     lds_barrier();  // every wave is done with this stage before it is refilled
   }
 
-  // ---- output: each part's 256 x 128 tile through LDS in turn, then whole 256-byte rows.
-  // D layout: lane (column l32 of N block nb, half kg), item i -> token 8 (i / 4) + 4 kg +
-  // i % 4 of the M block.
-  constexpr int kOutPitch = 2 * kPfDv + 16;  // bytes per token row, padded
-  static_assert(kKvTok * kOutPitch <= sizeof(Smem), "output tile exceeds the LDS");
+  // ---- output: each part's 256 x 128 tile through LDS in turn, then whole operand blocks
+  // (1 KiB of contiguous workspace per wave and store).  D layout: lane (column l32 of N
+  // block nb, half kg), item i -> token 8 (i / 4) + 4 kg + i % 4 of the M block.  Row pitches:
+  // 272 bytes for the keys (16 rows at one 16-byte column hit 16 distinct bank slots), 320
+  // for the values (the transposed reads' 4 rows x 64 bytes per half-wave are distinct).
+  constexpr int kPitchK = 2 * kPfDn + 16, kPitchV = 2 * kPfDv + 64;
+  static_assert(kKvTok * kPitchV <= sizeof(Smem), "output tile exceeds the LDS");
   char* o = reinterpret_cast<char*>(&sm);
-  const size_t head_off = ((size_t)b * H + h) * L_pad + t0;
+  const size_t head_tok = ((size_t)b * H + h) * L_pad + t0;  // first token of the block
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
+    const int pitch = pt == 0 ? kPitchK : kPitchV;
     if (part == pt) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -169,53 +204,66 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int t = 64 * mq + 32 * mb + 8 * (i >> 2) + 4 * kg + (i & 3);
-            *(bf16*)(o + t * kOutPitch + 2 * (32 * nb + l32)) = (bf16)acc[mb][nb][i];
+            *(bf16*)(o + t * pitch + 2 * (32 * nb + l32)) = (bf16)acc[mb][nb][i];
           }
     }
     __syncthreads();
-    // thread tid: 16-byte piece tid % 16 of rows tid / 16 + 32 k (k = 0 .. 7)
-    bf16* dst = (pt == 0 ? kout : vout) + head_off * kPfDv;
-    const int pc = tid & 15, pr = tid >> 4;
+    // 8 tiles x 8 blocks: wave w writes blocks 8 w .. 8 w + 7 (tile w), lane by lane
+    bf16* dst = (pt == 0 ? kout : vout) + head_tok * kPfDv + (size_t)w * (kTT * kPfDv);
+    const char* ot = o + kTT * w * pitch;  // the wave's tile
 #pragma unroll
-    for (int k = 0; k < kKvTok / 32; ++k) {
-      const int r = pr + 32 * k;
-      *(bf16x8*)(dst + (size_t)r * kPfDv + 8 * pc) = *(const bf16x8*)(o + r * kOutPitch + 16 * pc);
+    for (int bi = 0; bi < 8; ++bi) {
+      bf16x8 v;
+      if (pt == 0) {  // key step bi: token l32, columns 16 bi + 8 kg ..
+        v = *(const bf16x8*)(ot + l32 * kPitchK + 2 * (16 * bi + 8 * kg));
+      } else {        // value block (ks, cb) = (bi / 4, bi % 4): two transposed 4-row reads
+        const int ks = bi >> 2, cb = bi & 3;
+        const int tr = 16 * ks + 4 * kg + (li >> 2), col = 32 * cb + 16 * (G & 1) + 4 * (li & 3);
+        v = tr_pair(ot + tr * kPitchV + 2 * col, ot + (tr + 8) * kPitchV + 2 * col);
+      }
+      *(bf16x8*)(dst + 8 * (64 * bi + lane)) = v;
     }
     __syncthreads();
   }
 }
 
 // ----------------------------------------------------------------------------- attention
-// One workgroup (8 waves, two per SIMD) per (sequence b, head h, block of 256 query tokens);
-// wave w holds query tokens i0 + 32w .. +31 (MFMA N = rows).  Each key tile crosses into LDS
-// once for all 256 rows (with 128-row blocks the blocks of one head fetched every tile twice
-// as often, mostly from beyond L2).  Key tiles of 32 tokens stream through a
-// ring of four LDS buffers: the K rows (128 columns, from the workspace) with the cached
-// rotary keys (64 columns, already rotated at their own positions) in the 192-wide tile
-// layout of the one-branch decode, and the V rows (128 columns) after them.  Per tile and
-// wave: S^T = K . Q^T (12 K-steps), causal mask, online softmax with a lazy max (raised only
-// past kLazyTau log2 units), O^T += V^T P^T (8 MFMAs, the value operand read transposed).
+// One workgroup (8 waves, two per SIMD) per (sequence b, head h, pair of 256-token query
+// blocks); wave w holds query tokens i0 + 32w .. +31 (MFMA N = rows).  Each key tile of 32
+// tokens crosses into LDS once for all 256 rows, through a ring of six 20 KiB buffers: the
+// tile's 20 operand blocks exactly as the workspace stores them (8 key steps, 4 rotary
+// steps, 8 value blocks), so every load is 1 KiB of contiguous memory and every LDS read is a
+// lane-linear 16-byte read at one per-tile base address plus a constant.  Per tile and wave:
+// S^T = K . Q^T (12 MFMAs), causal mask on the diagonal tiles, online softmax with a lazy max
+// (raised only past kAtLazy log2 units), O^T += V^T P^T (8 MFMAs).
 constexpr int kAtWaves = 8;
 constexpr int kAtRows = 32 * kAtWaves;
-constexpr int kAtRing = 4;
+constexpr int kAtRing = 6;
 constexpr float kAtLazy = 8.0f;
-using GK = Geom<128>;                                  // K tile: 32 x 256 B + 32 x 128 B
-constexpr int kAtVOff = GK::kBufBytes;                 // V tile after it: 32 x 256 B
-constexpr int kAtBuf = GK::kBufBytes + kTT * 256;      // 20 KiB
-// loads per wave and tile: one of K rows, one of V rows, and for waves 0-3 one of rotary rows
+constexpr int kAtROff = kTileK;                 // rotary blocks after the 8 key blocks
+constexpr int kAtVOff = kTileK + kTileR;        // value blocks after them
+constexpr int kAtBuf = kTileK + kTileR + kTileV;  // 20 KiB
+// loads per wave and tile: key block w, value block w, and for waves 0-3 rotary block w
 constexpr int kAtIssuesLo = 3, kAtIssuesHi = 2;
+
+// wait until this wave has at most `younger` tiles' loads out beyond the one it needs
+template <int Younger>
+__device__ __forceinline__ void wait_tiles(int w) {
+  if (w < 4)
+    wait_vmcnt<Younger * kAtIssuesLo>();
+  else
+    wait_vmcnt<Younger * kAtIssuesHi>();
+}
 
 __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
-    const bf16* __restrict__ rope, int64_t rope_tok, int64_t rope_seq,
-    const int32_t* __restrict__ bt, int64_t bt_stride, int paged,
     const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ kbuf,
-    const bf16* __restrict__ vbuf, bf16* __restrict__ out, int B, int H, int sq, int L_pad,
-    float qscale, float out_scale, RopeFreq rf) {
+    const bf16* __restrict__ rbuf, const bf16* __restrict__ vbuf, bf16* __restrict__ out,
+    int B, int H, int sq, int L_pad, float qscale, float out_scale, RopeFreq rf) {
   struct Smem {
     char ring[kAtRing][kAtBuf];
   };
-  __shared__ __align__(16) Smem sm;  // 80 KiB
+  __shared__ __align__(1024) Smem sm;  // 120 KiB
   // Causal balance: a workgroup takes query blocks n_qb - 1 - j and j of one (b, h), the
   // heavy one first, so every workgroup scans about n_qb + 1 blocks' worth of key tiles
   // (a lone middle block when n_qb is odd).  XCD-aware order: blocks go round-robin over the
@@ -233,11 +281,13 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, kg = lane >> 5;
   const int L = min(max(seqlens[b], 0), max_seqlen);
-  const bf16* kb = kbuf + ((size_t)b * H + h) * L_pad * kPfDn;
-  const bf16* vb = vbuf + ((size_t)b * H + h) * L_pad * kPfDv;
-  const uint32_t rope_row_b = (uint32_t)(rope_tok * 2);
-  const int G = lane >> 4, li = lane & 15;
+  const char* kb = reinterpret_cast<const char*>(kbuf + ((size_t)b * H + h) * L_pad * kPfDn);
+  const char* vb = reinterpret_cast<const char*>(vbuf + ((size_t)b * H + h) * L_pad * kPfDv);
+  const char* rb = reinterpret_cast<const char*>(rbuf + (size_t)b * L_pad * kPfDr);
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  // a lane's operand in any block of ring buffer k: one register per tile, constants after
+  const uint32_t lane_b = lds_addr(sm.ring[0]) + 16 * lane;
+  auto slot = [&](int k) { return opaque(lane_b + (uint32_t)(k % kAtRing) * kAtBuf); };
 
   for (int pass = 0; pass < 2; ++pass) {
     const int qb = pass == 0 ? n_qb - 1 - jb : jb;
@@ -250,38 +300,17 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     const int pos_g = min(L - sq + i0 + kAtRows - 1, L - 1);  // the block's last position
     const int n_tiles = pos_g >= 0 ? pos_g / kTT + 1 : 0;
 
-    // tile k into its ring buffer; past n_tiles the loads go out with no valid row (zeros, no
-    // memory touched) so that every wave issues the same count and every wait is fixed
+    // tile k into its ring buffer: 1 KiB blocks, lane i's 16 bytes at 16 i.  Past n_tiles the
+    // loads go out with an empty range (zeros, no memory touched) so that every wave issues
+    // the same count and every wait is fixed.
     auto issue = [&](int k) {
       char* buf = sm.ring[k % kAtRing];
-      const int t0 = kTT * k;
-      const int valid = __builtin_amdgcn_readfirstlane(k < n_tiles ? max(0, min(kTT, L - t0)) : 0);
-      const bf16* rb;
-      if (paged) {
-        const int64_t pg = valid > 0 ? bt[(int64_t)b * bt_stride + t0 / kPage] : 0;
-        rb = rope + pg * rope_seq + (int64_t)(t0 % kPage) * rope_tok;
-      } else {
-        rb = rope + (int64_t)b * rope_seq + (int64_t)t0 * rope_tok;
-      }
-      // wave w: K rows 4w .. 4w + 3 and V rows 4w .. 4w + 3 (lane -> row 4w + lane / 16, physical
-      // chunk lane % 16, which fetches logical chunk (lane % 16) ^ swizzle(row)), and for w < 4
-      // the rotary rows 8w .. 8w + 7
-      const int r = 4 * w + (lane >> 4), c = lane & 15;
-      const uint32_t off = r * 256 + 16 * (c ^ lat_sw<Sw32>(r));
-      dma16(rsrc(kb + (size_t)t0 * kPfDn, valid * 256), buf + 4 * w * 256, off);
-      dma16(rsrc(vb + (size_t)t0 * kPfDv, valid * 256), buf + kAtVOff + 4 * w * 256, off);
-      if (w < 4) {
-        const int rt = 8 * w + (lane >> 3);
-        dma16(rsrc(rb, valid * rope_row_b), buf + GK::kRopeOff + w * 1024,
-              rt * rope_row_b + 16 * ((lane & 7) ^ rope_sw(rt)));
-      }
-    };
-    // tile k has landed for this wave: only the kAtRing - 2 younger tiles' loads may be out
-    auto wait_tile = [&]() {
+      const uint32_t n = k < n_tiles ? 1u : 0u;
+      const size_t t = (size_t)k;
+      dma16(rsrc(kb + t * kTileK, n * kTileK), buf + w * 1024, w * 1024 + 16 * lane);
+      dma16(rsrc(vb + t * kTileV, n * kTileV), buf + kAtVOff + w * 1024, w * 1024 + 16 * lane);
       if (w < 4)
-        wait_vmcnt<(kAtRing - 2) * kAtIssuesLo>();
-      else
-        wait_vmcnt<(kAtRing - 2) * kAtIssuesHi>();
+        dma16(rsrc(rb + t * kTileR, n * kTileR), buf + kAtROff + w * 1024, w * 1024 + 16 * lane);
     };
 
     // query as the B operand (K = 192 columns, N = 32 rows): lane (row l32, half kg), K-step j
@@ -318,39 +347,27 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     f32x16 O[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) O[cb] = f32x16{};
+    // tiles this wave needs (through its last position), and the limit of the causal mask:
+    // a tile starting at t0 needs the mask iff t0 + kTT - 1 > lim (the wave's first position)
+    const int n_w = pos_w >= 0 ? min(pos_w, L - 1) / kTT + 1 : 0;
+    const int lim = L - sq + iw;
 
+    // operand j of a tile: key steps 0-7, rotary steps 8-11
+    auto key_op = [&](uint32_t sb, int j) {
+      return lds_read16_at(sb + (j < 8 ? 1024 * j : kAtROff + 1024 * (j - 8)));
+    };
+    // causal mask: token t0 + 8 (i / 4) + 4 kg + i % 4 is seen by rows at positions >= it
+    auto mask = [&](f32x16& S, int t0) {
 #pragma unroll
-    for (int j = 0; j < kAtRing - 1; ++j) issue(j);
-    for (int k = 0; k < n_tiles; ++k) {
-      wait_tile();
-      lds_barrier();                            // ... for every wave; tile k - 1's buffer is free
-      issue(k + kAtRing - 1);
-      const int t0 = kTT * k;
-      if (t0 > pos_w) continue;  // every row of the wave is before this tile (uniform)
-      const char* buf = sm.ring[k % kAtRing];
-
-      // scores S^T[t][row] over 8 key steps and 4 rotary steps
-      f32x16 S = f32x16{};
-#pragma unroll
-      for (int j = 0; j < 12; ++j) {
-        const bf16x8 a = j < 8 ? lds_read16(buf + lat_chunk<Sw32, 128>(l32, 2 * j + kg))
-                               : lds_read16(buf + rope_chunk<128>(l32, 2 * (j - 8) + kg));
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb8[j], S, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const int t = t0 + 8 * (i >> 2) + 4 * kg + (i & 3);
+        S[i] = t <= pos ? S[i] : -INFINITY;
       }
-      // causal mask: token t0 + 8 (i / 4) + 4 kg + i % 4 is seen by rows at positions >= it;
-      // only tiles that reach past the wave's first position need it (a uniform branch)
-      if (t0 + kTT - 1 > L - sq + iw) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = t0 + 8 * (i >> 2) + 4 * kg + (i & 3);
-          S[i] = t <= pos ? S[i] : -INFINITY;
-        }
-      }
-      float mx = S[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[i]);
-      mx = max_xor32(mx);
-      // lazy raise of the running max; the first tile a row sees sets it
+    };
+    // a tile's row max into the running max (mx = -inf: the tile adds nothing); the max is
+    // raised lazily, only past kAtLazy log2 units, and the first tile a row sees sets it; O
+    // and l are rescaled when any row of the wave raised
+    auto take_max = [&](float mx) {
       const bool raise = mx > m_ref + kAtLazy || (m_ref == -INFINITY && mx != -INFINITY);
       float alpha = 1.0f;
       if (raise) {
@@ -363,35 +380,85 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
         for (int cb = 0; cb < 4; ++cb) O[cb] *= alpha;
         l_run *= alpha;
       }
-      // weights against m_ref (0 while the row has seen nothing): bf16 pairs in the value
-      // operand's token order, summed as the MFMA uses them
-      const float m_off = m_ref == -INFINITY ? 0.0f : m_ref;
-      uint32_t pw[2][4];
-      float psum = 0.0f;
+    };
+    auto row_max = [&](const f32x16& S) {
+      float mx = S[0];
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const bf16x2 p = __builtin_convertvector(
-            f32x2{__builtin_amdgcn_exp2f(S[i] - m_off), __builtin_amdgcn_exp2f(S[i + 1] - m_off)},
-            bf16x2);
-        pw[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, p);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[i]);
+      return max_xor32(mx);
+    };
+
+#pragma unroll
+    for (int j = 0; j < kAtRing - 1; ++j) issue(j);
+    wait_tiles<kAtRing - 2>(w);  // tile 0 has landed for this wave ...
+    lds_barrier();               // ... and for every wave
+    f32x16 S = f32x16{};
+    if (n_w > 0) {
+      const uint32_t s0 = slot(0);
+#pragma unroll
+      for (int j = 0; j < 12; ++j)
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(key_op(s0, j), qb8[j], S, 0, 0, 0);
+      if (kTT - 1 > lim) mask(S, 0);
+      take_max(row_max(S));
+    }
+    // Software pipeline, one tile deep: iteration k scores tile k + 1 while it turns tile k's
+    // scores (in S, their max already taken) into weights, then sums tile k's values.  The
+    // code below is in issue order, fenced in small groups: each score MFMA goes out with the
+    // key read two steps ahead and the arithmetic of one weight pair (or the value reads), so
+    // the matrix core and the vector ALU work side by side.
+    for (int k = 0; k < n_tiles; ++k) {
+      wait_tiles<kAtRing - 3>(w);  // tile k + 1 has landed for this wave ...
+      lds_barrier();  // ... and for every wave, which are all done with tile k - 1's buffer
+      issue(k + kAtRing - 1);
+      if (k >= n_w) continue;  // every row of the wave is before this tile (uniform)
+      const uint32_t bk = slot(k), bn = slot(k + 1);
+      const int tn = kTT * (k + 1);
+      const float m_off = m_ref == -INFINITY ? 0.0f : m_ref;  // 0 while nothing was seen
+      __builtin_amdgcn_sched_barrier(0);
+
+      f32x16 Sn = f32x16{};
+      bf16x8 kq[12], vop[8];
+      uint32_t pw[8];
+      float psum = 0.0f;
+      kq[0] = key_op(bn, 0);
+      kq[1] = key_op(bn, 1);
+#pragma unroll
+      for (int j = 0; j < 12; ++j) {
+        if (j + 2 < 12) kq[j + 2] = key_op(bn, j + 2);
+        Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[j], qb8[j], Sn, 0, 0, 0);
+        if (j < 8) {
+          // weights of tile k's tokens 2j, 2j + 1 of the lane: bf16 pairs in the value
+          // operand's token order, summed as the MFMA uses them
+          const bf16x2 p = __builtin_convertvector(
+              f32x2{__builtin_amdgcn_exp2f(S[2 * j] - m_off),
+                    __builtin_amdgcn_exp2f(S[2 * j + 1] - m_off)},
+              bf16x2);
+          pw[j] = __builtin_bit_cast(uint32_t, p);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(p, ones, psum, false);
+        } else {
+          vop[2 * (j - 8)] = lds_read16_at(bk + kAtVOff + 1024 * (2 * (j - 8)));
+          vop[2 * (j - 8) + 1] = lds_read16_at(bk + kAtVOff + 1024 * (2 * (j - 8) + 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       l_run += sum_xor32(psum);
-      // O^T[d][row] += V^T P^T: value operand rows (tokens) 4 kg + li / 4 (+ 8) of each
-      // 16-token step, columns 32 cb + 16 (G & 1) + 4 (li & 3)
+      // tile k + 1's causal mask, diagonal tiles only (a uniform branch)
+      if (tn + kTT - 1 > lim) mask(Sn, tn);
+      // O^T[d][row] += V^T P^T: value block 4 ks + cb holds columns 32 cb .. +31 of the
+      // 16-token step ks; the weights' token order matches its rows
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 pb =
-            __builtin_bit_cast(bf16x8, u32x4{pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]});
+            __builtin_bit_cast(bf16x8, u32x4{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2],
+                                             pw[4 * ks + 3]});
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const int col = 32 * cb + 16 * (G & 1) + 4 * (li & 3);
-          const int r = 16 * ks + 4 * kg + (li >> 2);
-          const bf16x8 va = tr_pair(buf + kAtVOff + lat_piece<Sw32, 128>(r, col),
-                                    buf + kAtVOff + lat_piece<Sw32, 128>(r + 8, col));
-          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, O[cb], 0, 0, 0);
-        }
+        for (int cb = 0; cb < 4; ++cb)
+          O[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[4 * ks + cb], pb, O[cb], 0, 0, 0);
       }
+      // past n_w the scores of tile k + 1 are not used
+      take_max(k + 1 < n_w ? row_max(Sn) : -INFINITY);
+      S = Sn;
     }
     // no tile load is still in flight when the block ends (the ring refills for the next one,
     // or the workgroup ends), and every wave is done reading the ring
@@ -424,9 +491,10 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_prefill_kv, dim3(p.L_pad / kKvTok, p.H, p.B), dim3(64 * kKvWaves), 0, s,
-                     (const bf16*)a.latent, a.lat_tok, a.lat_seq, a.block_table, a.bt_stride,
-                     p.paged, a.seqlens, p.max_seqlen, (const bf16*)a.w_uk, (const bf16*)a.w_uv,
-                     (bf16*)a.kbuf, (bf16*)a.vbuf, p.H, p.L_pad);
+                     (const bf16*)a.latent, a.lat_tok, a.lat_seq, (const bf16*)a.rope,
+                     a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
+                     p.max_seqlen, (const bf16*)a.w_uk, (const bf16*)a.w_uv, (bf16*)a.kbuf,
+                     (bf16*)a.rbuf, (bf16*)a.vbuf, p.H, p.L_pad);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;
@@ -434,11 +502,11 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   make_rope_freq(kPfDr, a.rope_theta, &rf);
   const int n_wg = ((p.sq + kAtRows - 1) / kAtRows + 1) / 2;  // workgroups per (b, h)
   const int64_t groups = ((int64_t)p.B * p.H + 7) / 8;  // pairs (b, h) in groups of eight
-  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_wg)), dim3(64 * kAtWaves), 0, s,
-                     (const bf16*)a.q_nope, (const bf16*)a.q_rope, (const bf16*)a.rope,
-                     a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
-                     p.max_seqlen, (const bf16*)a.kbuf, (const bf16*)a.vbuf, (bf16*)a.out, p.B,
-                     p.H, p.sq, p.L_pad, a.softmax_scale * kLog2e, a.out_scale, rf);
+  hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_wg)), dim3(64 * kAtWaves), 0,
+                     s, (const bf16*)a.q_nope, (const bf16*)a.q_rope, a.seqlens, p.max_seqlen,
+                     (const bf16*)a.kbuf, (const bf16*)a.rbuf, (const bf16*)a.vbuf,
+                     (bf16*)a.out, p.B, p.H, p.sq, p.L_pad, a.softmax_scale * kLog2e,
+                     a.out_scale, rf);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(2);
   return e;

@@ -440,10 +440,11 @@ def test_prefill_workspace_size_and_validation(lib):
     """mla_prefill's host checks: every call below fails validation before anything is
     launched (the pointers are never dereferenced)."""
     p = params_for("mla_bf16_b32_h128_l4096", num_queries=300, max_seqlen=300)
-    # keys and values, [B, H, L_pad, 128] bf16 each, L_pad = 300 rounded up to 512
-    assert B.prefill_workspace_size(p) == 2 * 2 * 128 * 512 * 128 * 2
+    # keys and values, B x H x L_pad x 128 bf16 each (L_pad = 300 rounded up to 512), and
+    # the rotary keys, B x L_pad x 64 bf16
+    assert B.prefill_workspace_size(p) == 2 * 2 * 128 * 512 * 128 * 2 + 2 * 512 * 64 * 2
     p1 = params_for("mla_bf16_b32_h128_l4096", num_queries=1, max_seqlen=1)
-    assert B.prefill_workspace_size(p1) == 2 * 2 * 128 * 256 * 128 * 2
+    assert B.prefill_workspace_size(p1) == 2 * 2 * 128 * 256 * 128 * 2 + 2 * 256 * 64 * 2
     ws = B.prefill_workspace_size(p)
     assert call(lib, p, fn="mla_prefill", ws_bytes=ws - 1) == 4        # MLA_ERR_WORKSPACE
     assert call(lib, p, fn="mla_prefill", q_nope=None) == 1            # MLA_ERR_NULL
