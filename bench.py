@@ -357,6 +357,19 @@ def cpu_baseline_prefill(inp, seconds: float):
             "seconds": round(el, 2), "cpu": _cpu_model()}
 
 
+def calibration_copy(args):
+    """A plain copy kernel of known size (torch.mul into a fresh tensor) for scaling the HBM
+    byte counters of a profiled run."""
+    import torch
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy kernel: {n} bytes read, {n} bytes written")
+
+
 def bench_prefill(args, ev, stream):
     """One prefill call per step on a prefill workload (every token of the sequence new),
     caches flushed before every step, outside the event pair (as for the decode)."""
@@ -406,6 +419,7 @@ def bench_prefill(args, ev, stream):
     at_ms = statistics.mean(ev.ms(e[1], e[2]) for e in st)
     for e in pf + pp + st:
         ev.destroy(e)
+    calibration_copy(args)
     ms = statistics.mean(total)
     value = (proj + attn) / (ms * 1e-3) / 1e12
     at_tf = attn / (at_ms * 1e-3) / 1e12
@@ -572,13 +586,7 @@ def main():
     probe_gbps = read_probe(ev, stream)
     log(f"[bench] read-stream probe: {probe_gbps:.1f} GB/s")
 
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy kernel: {n} bytes read, {n} bytes written")
+    calibration_copy(args)
 
     value = cache_bytes / (ms * 1e-3) / 1e12
     ent = None if args.variant != "none" else counters_entry(w.name, args.num_queries, bool(lf))
