@@ -8,18 +8,18 @@
 // 核心机制 step 3, and the compute-heavy regime the yololab MLA page names in
 // 繁榮背後的代價).  Two launches:
 //
-//  * k_prefill_kv: K and V of every (sequence, head, token) into the workspace,
-//    [B][H][L_pad][128] each, as one MFMA GEMM [tokens x 512] . [512 x 256] per head;
-//  * k_prefill_attn: per (sequence, head, block of 256 query tokens), a flash-attention
-//    pass over the key tokens up to the block's last position: scores over the 128 key
-//    columns plus the cached rotary key (64), online softmax, values summed in registers.
+//  * k_prefill_kv: K and V of every (sequence, head, token) into the workspace, B x H x
+//    L_pad x 128 each, as one MFMA GEMM [tokens x 512] . [512 x 256] per head, stored as the
+//    attention's MFMA operand blocks; it also copies the rotary keys into that form;
+//  * k_prefill_attn: per (sequence, head) and two blocks of 256 query tokens, a
+//    flash-attention pass over the key tokens up to each block's last position: scores over
+//    the 128 key columns plus the cached rotary key (64), online softmax, values summed in
+//    registers.
 //
 // Query token i of a sequence of L tokens sits at position L - s_q + i, its rotary query is
 // rotated there, and it sees the tokens up to and including itself; a token that sees none
 // writes zeros.  Layouts as the multi-token decode: q_nope [B, s_q, H, 128], q_rope
 // [B, s_q, H, 64], out [B, s_q, H, 128].
-#include <type_traits>
-
 #include "device_common.h"
 #include "launch.h"
 #include "tile_bf16.h"
