@@ -357,6 +357,50 @@ def cpu_baseline_prefill(inp, seconds: float):
             "seconds": round(el, 2), "cpu": _cpu_model()}
 
 
+def bench_probe(args, ev, stream):
+    """The issue probe (include/mla_probe.h): MFMA 32x32x16 bf16 chains and v_exp_f32 chains
+    alone and side by side on each SIMD, both accumulator forms; median of 5 runs each."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "mlra_latent_kv_amd", "libmla_probe.so"))
+    lib.mla_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    lib.mla_probe_issue_out_words.restype = ctypes.c_size_t
+    out = torch.empty(lib.mla_probe_issue_out_words(), dtype=torch.float32, device="cuda")
+    iters = 4096
+    names = ["8 waves matrix", "waves 0-3 matrix + 4-7 vector", "waves 0-3 matrix",
+             "waves 4-7 vector", "8 waves matrix+vector interleaved", "8 waves vector"]
+    e = ev.create(2)
+    res = {}
+    for agpr in (0, 1):
+        for mode in range(6):
+            ms = []
+            for i in range(6):
+                ev.record(e[0], stream)
+                if lib.mla_probe_issue(mode, agpr, iters, out.data_ptr(), stream) != 0:
+                    raise RuntimeError("mla_probe_issue failed")
+                ev.record(e[1], stream)
+                torch.cuda.synchronize()
+                if i:
+                    ms.append(ev.ms(e[0], e[1]))
+            res[(agpr, mode)] = 1e3 * statistics.median(ms)
+    ev.destroy(e)
+    # a 32x32x16 bf16 MFMA holds the matrix core 32 cycles (8 passes of 4): the matrix-only
+    # run with one wave per SIMD then gives the clock the SIMDs ran at
+    mfma_cycles = iters * 4 * 32
+    ghz = mfma_cycles / (res[(1, 2)] * 1e-6) / 1e9
+    exp_cyc = res[(1, 3)] * 1e-6 * ghz * 1e9 / (iters * 16)
+    taken = (res[(1, 1)] - res[(1, 3)]) * 1e-6 * ghz * 1e9 / (iters * 4)
+    return {
+        "metric": "issue_probe", "unit": "us", "iters": iters,
+        "us": {f"{'agpr' if a else 'vgpr'} acc, mode {m}: {names[m]}": round(t, 1)
+               for (a, m), t in sorted(res.items())},
+        "clock_ghz_from_matrix_only": round(ghz, 3),
+        "vector_cycles_per_mul_exp_pair": round(exp_cyc, 2),
+        "vector_issue_cycles_lost_per_mfma_beside_it": round(taken, 1),
+        "vgpr_over_agpr_accumulators_matrix_only": round(res[(0, 2)] / res[(1, 2)], 3),
+    }
+
+
 def calibration_copy(args):
     """A plain copy kernel of known size (torch.mul into a fresh tensor) for scaling the HBM
     byte counters of a profiled run."""
@@ -454,9 +498,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--op", choices=["decode", "append", "prefill"], default="decode",
+    ap.add_argument("--op", choices=["decode", "append", "prefill", "probe"], default="decode",
                     help="decode: the decode step (the metric); append: one step's cache write; "
-                         "prefill: the un-absorbed many-query step on a prefill workload")
+                         "prefill: the un-absorbed many-query step on a prefill workload; "
+                         "probe: the matrix-core / vector-ALU issue probe")
     ap.add_argument("--variant", default="none",
                     choices=["none", "gate", "query_latent", "output_latent",
                              "query_latent+output_latent"],
@@ -497,6 +542,10 @@ def main():
     B.load()
     if args.op == "append":
         print(json.dumps(bench_append(args, HipEvents(), torch.cuda.current_stream().cuda_stream)),
+              flush=True)
+        return
+    if args.op == "probe":
+        print(json.dumps(bench_probe(args, HipEvents(), torch.cuda.current_stream().cuda_stream)),
               flush=True)
         return
     if args.op == "prefill":

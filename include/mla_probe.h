@@ -1,5 +1,5 @@
 /*
- * mla_probe.h - read-stream probe (libmla_probe.so): measurement support for the decode
+ * mla_probe.h - read-stream and issue probes (libmla_probe.so): measurement support for the
  * benchmark, not part of the decode path.
  *
  * The decode step's main loop is bound by the HBM read stream of the latent cache (the
@@ -31,6 +31,24 @@ size_t mla_probe_out_words(void);
  * the launch fails.  Allocates nothing.
  */
 int mla_probe_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream);
+
+/* Number of floats mla_probe_issue writes to `out`. */
+size_t mla_probe_issue_out_words(void);
+
+/*
+ * Issue probe of one SIMD's matrix core and vector ALU (the rates behind the MFMA-bound
+ * kernels' design: how fast MFMA 32x32x16 bf16 chains and v_exp_f32 chains run, alone and
+ * side by side).  One workgroup of 8 waves per CU for 256 CUs; `iters` iterations of four
+ * independent MFMA chains (matrix waves) or sixteen independent exp2 chains (vector waves).
+ * mode: 0 all waves matrix; 1 waves 0-3 matrix and 4-7 vector (one of each per SIMD);
+ * 2 waves 0-3 matrix only; 3 waves 4-7 vector only; 4 all waves both, interleaved; 5 all
+ * waves vector.  agpr != 0 keeps the MFMA accumulators in the accumulation registers.
+ * `out` (device, caller-owned, mla_probe_issue_out_words() floats) receives meaningless
+ * per-lane sums.  Asynchronous on `stream`; time it with events.  Returns 0, 1 for a NULL
+ * pointer, a mode outside 0..5 or iters outside 1..2^20, or 6 when the launch fails.
+ * Allocates nothing.
+ */
+int mla_probe_issue(int mode, int agpr, int iters, float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

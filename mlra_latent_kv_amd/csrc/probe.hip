@@ -1,6 +1,7 @@
 // Read-stream probe: the HBM read rate a plain streaming kernel reaches on this device, the
-// practical ceiling next to the published peak.  Measurement support for the benchmark, not
-// part of the decode path (libmla_probe.so, declared in include/mla_probe.h).
+// practical ceiling next to the published peak; and an issue probe of the matrix core and the
+// vector ALU.  Measurement support for the benchmark, not part of the decode path
+// (libmla_probe.so, declared in include/mla_probe.h).
 //
 // Each of 512 workgroups (256 threads) streams one contiguous chunk of the buffer: per
 // iteration every lane issues eight 16-byte non-temporal loads (global_load_dwordx4 nt) of
@@ -46,9 +47,93 @@ __global__ __launch_bounds__(kThreads) void k_read_stream(const u32x4* __restric
   if ((threadIdx.x & 63) == 0) out[(size_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64] = acc;
 }
 
+// Issue probe: how the matrix core and the vector ALU share a SIMD.  One workgroup of 8
+// waves per CU (two per SIMD; wave w runs on SIMD w % 4, so waves 0-3 and 4-7 pair up).
+// Per iteration a matrix wave issues four independent MFMA 32x32x16 bf16 chains and a vector
+// wave sixteen independent exp2(0.999 x) chains (v_mul + v_exp_f32).  Modes:
+//   0  all 8 waves matrix            1  waves 0-3 matrix, waves 4-7 vector
+//   2  waves 0-3 matrix, 4-7 idle    3  waves 4-7 vector, 0-3 idle
+//   4  all 8 waves both, interleaved in one instruction stream
+//   5  all 8 waves vector
+// AGPR: accumulators in the accumulation registers (MFMA written as inline asm with an "a"
+// operand) instead of the architectural ones.  The per-lane results go to `out` so nothing
+// is removed; their values mean nothing.
+constexpr int kIssueBlocks = 256, kIssueThreads = 512;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int MODE, bool AGPR>
+__global__ __launch_bounds__(kIssueThreads, 1) void k_issue_probe(float* __restrict__ out, int iters,
+                                                                  float seed) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w >> 2;
+  bf16x8_t a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (threadIdx.x + i));
+    b[i] = (__bf16)(seed * i);
+  }
+  f32x16_t acc[4] = {};
+  float v[16];
+  for (int i = 0; i < 16; ++i) v[i] = seed * (threadIdx.x + i);
+  auto mfma4 = [&]() {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (AGPR)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[c]) : "v"(a), "v"(b));
+      else
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+  };
+  auto exp16 = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_exp2f(v[i] * 0.999f);
+  };
+  if (MODE == 4) {
+    for (int it = 0; it < iters; ++it) {
+      mfma4();
+      exp16();
+    }
+  } else {
+    const bool matrix = MODE == 0 || (MODE <= 2 && grp == 0);
+    const bool vector = MODE == 5 || (MODE == 1 && grp == 1) || (MODE == 3 && grp == 1);
+    if (matrix)
+      for (int it = 0; it < iters; ++it) mfma4();
+    if (vector)
+      for (int it = 0; it < iters; ++it) exp16();
+  }
+  float r = 0.0f;
+  for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < 16; ++i) r += acc[c][i];
+  for (int i = 0; i < 16; ++i) r += v[i];
+  out[(size_t)blockIdx.x * kIssueThreads + threadIdx.x] = r;
+}
+
+template <bool AGPR>
+hipError_t launch_issue(int mode, float* out, int iters, hipStream_t s) {
+  const dim3 g(kIssueBlocks), t(kIssueThreads);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((k_issue_probe<0, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
+    case 1: hipLaunchKernelGGL((k_issue_probe<1, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
+    case 2: hipLaunchKernelGGL((k_issue_probe<2, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
+    case 3: hipLaunchKernelGGL((k_issue_probe<3, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
+    case 4: hipLaunchKernelGGL((k_issue_probe<4, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
+    default: hipLaunchKernelGGL((k_issue_probe<5, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mla_probe_issue_out_words(void) { return (size_t)kIssueBlocks * kIssueThreads; }
+
+int mla_probe_issue(int mode, int agpr, int iters, float* out, hipStream_t stream) {
+  if (!out || mode < 0 || mode > 5 || iters < 1 || iters > (1 << 20)) return 1;
+  const hipError_t e = agpr ? launch_issue<true>(mode, out, iters, stream)
+                            : launch_issue<false>(mode, out, iters, stream);
+  return e == hipSuccess ? 0 : 6;
+}
 
 size_t mla_probe_out_words(void) { return (size_t)kBlocks * (kThreads / 64); }
 
