@@ -92,6 +92,25 @@ def test_prefill_agrees_with_absorbed_decode(sq):
     assert_close(pre, oracle_prefill(inp), "bf16", f"prefill vs oracle s_q={sq}")
 
 
+ODD = I.Workload("prefill_odd_b3_h5", batch=3, heads=5, branches=1, d_nope=128, d_v=128,
+                 d_cb=512, d_rope=64, dtype="bf16", paged=False, seqlen=600, out_scale=0.5, seed=31)
+ODD_PAGED = I.Workload("prefill_odd_paged_b2_h7", batch=2, heads=7, branches=1, d_nope=128,
+                       d_v=128, d_cb=512, d_rope=64, dtype="bf16", paged=True, seqlen=400, seed=32)
+
+
+@pytest.mark.parametrize("w,sq,lens", [(ODD, 300, [600, 257, 1]), (ODD_PAGED, 515, [400, 515])],
+                         ids=["b3_h5_contig", "b2_h7_paged"])
+def test_prefill_head_counts_off_the_grid_groups(w, sq, lens):
+    """Head counts and batches whose (sequence, head) pairs do not fill whole groups of eight
+    (15 and 14 pairs: the attention grid's padding workgroups return at once), an odd
+    out_scale, three query blocks (a lone middle block) and a sequence shorter than s_q."""
+    for sharp in (False, True):
+        inp = I.make_inputs(w, seed=7, seqlens=lens, num_queries=sq,
+                            q_gain=I.sharp_q_gain(w) if sharp else 1.0)
+        got, _ = gpu_prefill(inp)
+        assert_close(got, oracle_prefill(inp), "bf16", f"{w.name} sq={sq} sharp={sharp}")
+
+
 def test_prefill_empty_sequences_write_zeros():
     inp = I.make_inputs(H128, seed=3, seqlens=[0, 0], num_queries=40, max_seqlen=64)
     got, _ = gpu_prefill(inp)
