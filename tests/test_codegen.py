@@ -1,6 +1,6 @@
 """Guards on the generated gfx950 code of the kernels (host only: hipcc -S).
 
-* Both main loops prefetch tiles with direct-to-LDS loads that stay in flight while the
+* Both main loops and the two prefill kernels prefetch tiles with direct-to-LDS loads that stay in flight while the
   current tile is consumed.  The compiler's wait analysis can silently defeat that by
   inserting ``s_waitcnt vmcnt(0)`` (wait for every outstanding load) in front of an LDS read
   it cannot tell apart from the loads in flight, or by spilling to scratch (whose reloads need
@@ -35,10 +35,10 @@ def _asm(src: str, tmp_path) -> str:
     return out.read_text()
 
 
-def _kernels(asm: str):
-    """(name, body lines, metadata text) of each k_main kernel in the assembly."""
+def _kernels(asm: str, pattern: str = r"k_main_bf16\w*"):
+    """(name, body lines, metadata text) of each kernel whose name matches `pattern`."""
     out = []
-    for m in re.finditer(r"^(_ZN3mla\w*k_main_bf16\w*):.*$", asm, re.M):
+    for m in re.finditer(r"^(_ZN3mla\w*" + pattern + r"):.*$", asm, re.M):
         name = m.group(1)
         end = asm.index(".Lfunc_end", m.end())
         meta = asm[asm.index(f".amdhsa_kernel {name}"):]
@@ -127,10 +127,14 @@ def _drains_after_issue(blocks, head, members):
     return found
 
 
-@pytest.mark.parametrize("src", ["main_bf16.hip", "main_bf16_wide.hip"])
-def test_main_loop_keeps_tile_loads_in_flight(src, tmp_path):
-    kernels = _kernels(_asm(src, tmp_path))
-    assert kernels, "no main-loop kernel found"
+@pytest.mark.parametrize("src,pattern", [("main_bf16.hip", r"k_main_bf16\w*"),
+                                         ("main_bf16_wide.hip", r"k_main_bf16\w*"),
+                                         ("prefill.hip", r"k_prefill_(?:attn|kv)\w*")])
+def test_main_loop_keeps_tile_loads_in_flight(src, pattern, tmp_path):
+    """Also the prefill's two kernels: the attention's key-tile ring and the projection's
+    double-buffered latent and weight chunks."""
+    kernels = _kernels(_asm(src, tmp_path), pattern)
+    assert len(kernels) >= (2 if src == "prefill.hip" else 1), "no main-loop kernel found"
     for name, lines, _meta in kernels:
         loop = _main_loop(lines)
         assert loop is not None, (name, "main loop not found")
