@@ -1,7 +1,8 @@
 """Guards on the generated gfx950 code of the kernels (host only: hipcc -S).
 
-* Both main loops and the two prefill kernels prefetch tiles with direct-to-LDS loads that stay in flight while the
-  current tile is consumed.  The compiler's wait analysis can silently defeat that by
+* Both main loops and the two prefill kernels prefetch tiles with direct-to-LDS loads that
+  stay in flight while the current tile is consumed.  The compiler's wait analysis can
+  silently defeat that by
   inserting ``s_waitcnt vmcnt(0)`` (wait for every outstanding load) in front of an LDS read
   it cannot tell apart from the loads in flight, or by spilling to scratch (whose reloads need
   the same wait).  The kernels are compiled the way the library build does, and inside each
