@@ -2,11 +2,11 @@
 
 * Both main loops and the two prefill kernels prefetch tiles with direct-to-LDS loads that
   stay in flight while the current tile is consumed.  The compiler's wait analysis can
-  silently defeat that by
-  inserting ``s_waitcnt vmcnt(0)`` (wait for every outstanding load) in front of an LDS read
-  it cannot tell apart from the loads in flight, or by spilling to scratch (whose reloads need
-  the same wait).  The kernels are compiled the way the library build does, and inside each
-  main loop no such wait may follow the tile loads and nothing may spill.
+  silently defeat that by inserting ``s_waitcnt vmcnt(0)`` (wait for every outstanding load)
+  in front of an LDS read it cannot tell apart from the loads in flight, or by spilling to
+  scratch (whose reloads need the same wait).  The kernels are compiled the way the library
+  build does, and inside each main loop no such wait may follow the tile loads and nothing
+  may spill.
 * A matrix-core (MFMA) result may be read or overwritten by another instruction only after
   a number of wait states that the hardware does not enforce; the compiler pads straight-line
   code with ``s_nop``, but it once left a read one instruction behind the MFMA on the taken
