@@ -117,6 +117,40 @@ def read_probe(ev, stream, reps: int = 5, gib: int = 2):
     return n / (statistics.median(ms) * 1e-3) / 1e9
 
 
+def read_pages_probe(ev, stream, inp, case, flush_fn, reps: int = 5):
+    """Median rate (GB/s) of the page-gather probe over the workload's own paged pool: every
+    page a sequence uses, sequence by sequence in block-table order (the order the decode's
+    work items read them), caches flushed before each run.  Returns (GB/s, bytes read)."""
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "mlra_latent_kv_amd", "libmla_probe.so"))
+    lib.mla_probe_read_pages.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_probe_out_words.restype = ctypes.c_size_t
+    bt = np.asarray(inp["block_table"])
+    lens = np.asarray(inp["seqlens"], np.int64)
+    order = np.concatenate([bt[b, :(int(L) + 63) // 64] for b, L in enumerate(lens)])
+    assert order.min() >= 0 and order.max() < case.cache.shape[0]  # inside the pool
+    pages = torch.from_numpy(order.astype(np.int32)).to(case.cache.device)
+    page_bytes = case.cache[0].numel() * case.cache.element_size()
+    out = torch.empty(lib.mla_probe_out_words(), dtype=torch.int32, device=case.cache.device)
+    e = ev.create(2)
+    ms = []
+    for i in range(reps + 1):
+        flush_fn(i)
+        ev.record(e[0], stream)
+        if lib.mla_probe_read_pages(case.cache.data_ptr(), page_bytes, pages.data_ptr(),
+                                    len(order), out.data_ptr(), stream) != 0:
+            raise RuntimeError("mla_probe_read_pages failed")
+        ev.record(e[1], stream)
+        torch.cuda.synchronize()
+        if i:
+            ms.append(ev.ms(e[0], e[1]))
+    ev.destroy(e)
+    nbytes = len(order) * page_bytes
+    return nbytes / (statistics.median(ms) * 1e-3) / 1e9, nbytes
+
+
 def source_sha(kernel: str) -> str:
     """Hash of the sources the main-loop kernel is built from."""
     h = hashlib.sha256()
@@ -634,6 +668,10 @@ def main():
     main_ms = statistics.mean(stage["main"])
     probe_gbps = read_probe(ev, stream)
     log(f"[bench] read-stream probe: {probe_gbps:.1f} GB/s")
+    pages_gbps = pages_bytes = None
+    if inp["paged"] and not lf:
+        pages_gbps, pages_bytes = read_pages_probe(ev, stream, inp, case, do_flush)
+        log(f"[bench] page-gather probe over the workload's pool: {pages_gbps:.1f} GB/s")
 
     calibration_copy(args)
 
@@ -688,6 +726,10 @@ def main():
             "frac_trace": None if trace_us is None else round(
                 cache_bytes / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "frac_of_read_probe": round(achieved / probe_gbps, 4),
+            # paged workloads: the same pages streamed in the same order by a plain kernel
+            "page_probe_GBps": None if pages_gbps is None else round(pages_gbps, 1),
+            "page_probe_bytes": pages_bytes,
+            "frac_of_page_probe": None if pages_gbps is None else round(achieved / pages_gbps, 4),
             "empty_event_pair_us": round(pair_ms * 1e3, 2),
         },
         "cpu_baseline": None,

@@ -32,6 +32,18 @@ size_t mla_probe_out_words(void);
  */
 int mla_probe_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream);
 
+/*
+ * The same stream over a paged pool: read every byte of the pages pages[0 .. n_pages-1]
+ * (device int32 indices into `pool`, each page `page_bytes` long at pool + index *
+ * page_bytes, a multiple of 16) in list order, as a decode reads a shuffled paged cache;
+ * mla_probe_out_words() XOR folds go to `out`.  The caller keeps every index inside the
+ * pool.  Asynchronous on `stream`.  Returns 0, 1 for a NULL pointer, n_pages < 1 or a page
+ * size that is 0, not a multiple of 16 or over 16 MiB, or 6 when the launch fails.
+ * Allocates nothing.
+ */
+int mla_probe_read_pages(const void* pool, size_t page_bytes, const int32_t* pages,
+                         int n_pages, uint32_t* out, hipStream_t stream);
+
 /* Number of floats mla_probe_issue writes to `out`. */
 size_t mla_probe_issue_out_words(void);
 

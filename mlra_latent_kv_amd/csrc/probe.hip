@@ -47,6 +47,40 @@ __global__ __launch_bounds__(kThreads) void k_read_stream(const u32x4* __restric
   if ((threadIdx.x & 63) == 0) out[(size_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64] = acc;
 }
 
+// Page-gather probe: the same stream over a paged pool, page by page in a given order (the
+// order a decode reads a shuffled paged cache).  Workgroup g takes entries
+// [g n / kBlocks, (g + 1) n / kBlocks) of the page list; its four waves take every fourth
+// page of that range, each page's index read once (a uniform, scalar load), and stream it
+// with eight non-temporal 16-byte loads in flight per lane.
+__global__ __launch_bounds__(kThreads) void k_read_pages(const char* __restrict__ pool,
+                                                         uint32_t page_units,
+                                                         const int32_t* __restrict__ pages,
+                                                         int n_pages,
+                                                         uint32_t* __restrict__ out) {
+  const int first = (int)((int64_t)blockIdx.x * n_pages / kBlocks);
+  const int last = (int)((int64_t)(blockIdx.x + 1) * n_pages / kBlocks);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  constexpr uint32_t kStep = 64 * kUnroll;  // units per wave and iteration
+  uint32_t acc = 0;
+  for (int p = first + wave; p < last; p += kThreads / 64) {
+    const int pg = __builtin_amdgcn_readfirstlane(pages[p]);
+    const u32x4* q = reinterpret_cast<const u32x4*>(pool + (size_t)pg * ((size_t)page_units * 16));
+    for (uint32_t i = lane; i < page_units; i += kStep) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t x = i + 64 * u;
+        v[u] = x < page_units ? __builtin_nontemporal_load(q + x) : u32x4{};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
+  if (lane == 0) out[(size_t)blockIdx.x * (kThreads / 64) + wave] = acc;
+}
+
 // Issue probe: how the matrix core and the vector ALU share a SIMD.  One workgroup of 8
 // waves per CU (two per SIMD; wave w runs on SIMD w % 4, so waves 0-3 and 4-7 pair up).
 // Per iteration a matrix wave issues four independent MFMA 32x32x16 bf16 chains and a vector
@@ -125,6 +159,17 @@ hipError_t launch_issue(int mode, float* out, int iters, hipStream_t s) {
 }  // namespace
 
 extern "C" {
+
+int mla_probe_read_pages(const void* pool, size_t page_bytes, const int32_t* pages,
+                         int n_pages, uint32_t* out, hipStream_t stream) {
+  if (!pool || !pages || !out || n_pages < 1 || page_bytes == 0 || page_bytes % 16 ||
+      page_bytes / 16 > (1u << 20))
+    return 1;
+  hipLaunchKernelGGL(k_read_pages, dim3(kBlocks), dim3(kThreads), 0, stream,
+                     static_cast<const char*>(pool), (uint32_t)(page_bytes / 16), pages, n_pages,
+                     out);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
 
 size_t mla_probe_issue_out_words(void) { return (size_t)kIssueBlocks * kIssueThreads; }
 

@@ -41,8 +41,8 @@ def test_probe_library_exports_its_header(lib):
     """The probes (benchmark support) export what include/mla_probe.h declares."""
     from mlra_latent_kv_amd import build
     declared = B.header_functions(os.path.join(ROOT, "include", "mla_probe.h"))
-    assert set(declared) == {"mla_probe_out_words", "mla_probe_read", "mla_probe_issue_out_words",
-                             "mla_probe_issue"}
+    assert set(declared) == {"mla_probe_out_words", "mla_probe_read", "mla_probe_read_pages",
+                             "mla_probe_issue_out_words", "mla_probe_issue"}
     out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -54,6 +54,11 @@ def test_probe_library_exports_its_header(lib):
                                      ctypes.c_void_p]
     assert probe.mla_probe_read(None, 16, FAKE, None) == 1       # rejected before any launch
     assert probe.mla_probe_read(FAKE, 24, FAKE, None) == 1
+    probe.mla_probe_read_pages.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert probe.mla_probe_read_pages(FAKE, 73728, None, 4, FAKE, None) == 1
+    assert probe.mla_probe_read_pages(FAKE, 73720, FAKE, 4, FAKE, None) == 1
+    assert probe.mla_probe_read_pages(FAKE, 73728, FAKE, 0, FAKE, None) == 1
     probe.mla_probe_issue_out_words.restype = ctypes.c_size_t
     assert probe.mla_probe_issue_out_words() == 256 * 512
     probe.mla_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
