@@ -329,7 +329,7 @@ def mla_prefill(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, num_queries: int,
                 batches: Optional[Iterable[int]] = None,
                 heads: Optional[Iterable[int]] = None) -> np.ndarray:
     """Prefill: the s_q newest tokens of each sequence attend causally over its cache, computed
-    the un-absorbed way for all of a head's query tokens at once (MLA, one latent branch).
+    the un-absorbed way for all of a head's query tokens at once.
 
     The yololab page (section "繁榮背後的代價…") names the regime in which many query rows
     meet one cache read; the interview Q&A ("MLA … 是什么", 核心机制 step 3) gives the
@@ -338,12 +338,14 @@ def mla_prefill(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, num_queries: int,
     definition, inputs and layouts as ``mla_decode(num_queries=s_q)``: query rows
     [B, s_q * H, ...] with row i * H + h = head h of query token i, which sits at position
     L - s_q + i (rotary part rotated there) and sees tokens 0 .. L - s_q + i; a row that sees no
-    token is zero.  Returns [len(batches), len(rows), d_v]; ``heads`` selects query rows.
+    token is zero.  With NB latent branches (MLRA, "[ICLR 2025] MLRA…", sections 2.1 and 2.2)
+    branch b has its own keys K_b = c_b W_UK[b]^T and values V_b = c_b W_UV[b] from its slice
+    c_b of the latent, its own query q_nope[.., b, :] and its own softmax; every branch adds the
+    same rotary score, and the head's output is out_scale times the sum of the branch outputs.
+    Returns [len(batches), len(rows), d_v]; ``heads`` selects query rows.
     """
     W_UK, W_UV = to_f64(w_uk), to_f64(w_uv)
-    if W_UK.shape[0] != 1:
-        raise ValueError("the prefill covers one latent branch (MLA)")
-    _, Hw, d_nope, d_c = W_UK.shape
+    NB, Hw, d_nope, d_cb = W_UK.shape
     d_v = W_UV.shape[-1]
     qn, qr = to_f64(q_nope), to_f64(q_rope)
     B, R = qn.shape[0], qn.shape[1]
@@ -358,21 +360,23 @@ def mla_prefill(q_nope, q_rope, cache, seqlens, w_uk, w_uv, *, num_queries: int,
         rows = sequence_rows(cache, b, L, page_size, block_table, to_f64)   # [L, d_c + d_rope]
         if L == 0:
             continue
-        lat = rows[:, :d_c]
-        k_rot = rope(rows[:, d_c:d_c + d_rope], np.arange(L), theta)         # keys at position t
+        lat = rows[:, :NB * d_cb]
+        k_rot = rope(rows[:, NB * d_cb:NB * d_cb + d_rope], np.arange(L), theta)  # keys at t
         pos = L - sq + np.arange(sq)                                           # query positions
         mask = np.arange(L)[None, :] > pos[:, None]                            # [s_q, L] future
         seen = pos >= 0                                                        # sees >= 1 token
         for h in sorted({r % Hw for r in sel}):
-            K = lat @ W_UK[0, h].T                                             # [L, d_nope]
-            V = lat @ W_UV[0, h]                                               # [L, d_v]
-            q_n = qn[b, h::Hw, 0]                                              # [s_q, d_nope]
             q_r = rope(qr[b, h::Hw], pos, theta)                               # [s_q, d_rope]
-            S = scale * (q_n @ K.T + q_r @ k_rot.T)                            # [s_q, L]
-            S[mask] = -np.inf
             O = np.zeros((sq, d_v), dtype=F64)
-            if seen.any():
-                O[seen] = softmax(S[seen]) @ V
+            for br in range(NB):
+                c = lat[:, br * d_cb:(br + 1) * d_cb]                          # [L, d_cb]
+                K = c @ W_UK[br, h].T                                          # [L, d_nope]
+                V = c @ W_UV[br, h]                                            # [L, d_v]
+                q_n = qn[b, h::Hw, br]                                         # [s_q, d_nope]
+                S = scale * (q_n @ K.T + q_r @ k_rot.T)                        # [s_q, L]
+                S[mask] = -np.inf
+                if seen.any():
+                    O[seen] += softmax(S[seen]) @ V
             for j, r in enumerate(sel):
                 if r % Hw == h:
                     out[i, j] = out_scale * O[r // Hw]

@@ -1019,7 +1019,8 @@ def test_e4m3_round_trip_and_saturation():
 # head (the interview Q&A's 核心机制 step 3, in the many-query regime of the yololab page's
 # 繁榮背後的代價 section).  O.mla_prefill computes all query tokens of a head at once; it is
 # pinned against the scalar masked brute force, the per-row decode oracle (itself pinned
-# above), an exact first-token form and causality.
+# above, for MLA and for the four MLRA branches), an exact first-token form, causality and
+# the one-live-branch reduction.
 
 def _prefill_case(sq, L, Hw=2, dn=3, dc=4, dr=4, dv=5, seed=0):
     rng = np.random.default_rng(seed + 100 * sq + L)
@@ -1093,9 +1094,47 @@ def test_prefill_causality():
             assert not np.allclose(after[r], base[r])
 
 
+def _mlra_prefill_case(sq, L, Hw=2, NB=4, dn=3, dcb=4, dr=4, dv=5, seed=0):
+    rng = np.random.default_rng(seed + 1000 + 100 * sq + L)
+    qn = rng.standard_normal((1, sq * Hw, NB, dn))
+    qr = rng.standard_normal((1, sq * Hw, dr))
+    cache = rng.standard_normal((1, max(L, 1), NB * dcb + dr))
+    w_uk = rng.standard_normal((NB, Hw, dn, dcb))
+    w_uv = rng.standard_normal((NB, Hw, dcb, dv))
+    return qn, qr, cache, w_uk, w_uv
+
+
+@pytest.mark.parametrize("sq,L", [(3, 7), (4, 2), (1, 5)])
+def test_prefill_mlra_equals_per_row_decode(sq, L):
+    """Four branches (MLRA): equal to the per-row multi-query decode oracle, whose branch sum
+    is pinned above (hand-worked 163/120 example, one-live-branch and identical-branch
+    reductions), to fp64 rounding."""
+    qn, qr, cache, w_uk, w_uv = _mlra_prefill_case(sq, L)
+    kw = dict(num_queries=sq, d_rope=4, scale=0.4, out_scale=0.5, theta=1e4)
+    a = O.mla_prefill(qn, qr, cache, [L], w_uk, w_uv, **kw)
+    b = O.mla_decode(qn, qr, cache, [L], w_uk, w_uv, **kw)
+    assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(b).max())
+
+
+def test_prefill_mlra_one_live_branch_is_mla_on_it():
+    """Branches 0, 1 and 3 with zero W_UV contribute nothing: the result is the one-branch
+    prefill of branch 2 alone (its latent slice, its query, its weights) times out_scale."""
+    sq, L = 4, 6
+    qn, qr, cache, w_uk, w_uv = _mlra_prefill_case(sq, L)
+    w_uv = w_uv.copy()
+    w_uv[[0, 1, 3]] = 0.0
+    kw = dict(num_queries=sq, d_rope=4, scale=0.4, theta=1e4)
+    got = O.mla_prefill(qn, qr, cache, [L], w_uk, w_uv, out_scale=0.5, **kw)
+    one = np.concatenate([cache[:, :, 8:12], cache[:, :, 16:]], axis=-1)
+    ref = O.mla_prefill(qn[:, :, 2:3], qr, one, [L], w_uk[2:3], w_uv[2:3], out_scale=0.5, **kw)
+    assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
 def _prefill_pins_pass():
     checks = [lambda: test_prefill_brute_force(2, 7), lambda: test_prefill_brute_force(4, 2),
-              test_prefill_first_token_is_its_value, test_prefill_causality]
+              test_prefill_first_token_is_its_value, test_prefill_causality,
+              lambda: test_prefill_mlra_equals_per_row_decode(3, 7),
+              test_prefill_mlra_one_live_branch_is_mla_on_it]
     with np.errstate(all="ignore"):
         for c in checks:
             try:
@@ -1114,7 +1153,11 @@ def test_prefill_pins_pass_unplanted():
     ("mask_off_by_one", "np.arange(L)[None, :] > pos[:, None]", "np.arange(L)[None, :] >= pos[:, None]"),
     ("queries_at_last_position", "q_r = rope(qr[b, h::Hw], pos, theta)",
      "q_r = rope(qr[b, h::Hw], np.full(sq, L - 1), theta)"),
-    ("values_from_keys", "V = lat @ W_UV[0, h]", "V = (lat @ W_UK[0, h].T)[:, :1] * np.ones((1, d_v))"),
+    ("values_from_keys", "V = c @ W_UV[br, h]", "V = (c @ W_UK[br, h].T)[:, :1] * np.ones((1, d_v))"),
+    ("branch_query_of_branch_0", "q_n = qn[b, h::Hw, br]", "q_n = qn[b, h::Hw, 0]"),
+    ("latent_slice_of_branch_0", "c = lat[:, br * d_cb:(br + 1) * d_cb]", "c = lat[:, :d_cb]"),
+    ("keys_of_branch_0", "K = c @ W_UK[br, h].T", "K = c @ W_UK[0, h].T"),
+    ("branches_not_summed", "O[seen] += softmax(S[seen]) @ V", "O[seen] = softmax(S[seen]) @ V"),
 ])
 def test_prefill_planted_mistake_is_caught(monkeypatch, mistake, old, new):
     """Each mistake is planted in a copy of the oracle's prefill, on the CPU."""
