@@ -344,15 +344,16 @@ MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 def prefill_flops(w, lens, sq):
     """Algorithmic work of one prefill call: the up-projection of every cached latent to its
-    per-head key and value (2 * 512 * 256 per token and head) and the causal attention, 2 *
-    (192 + 128) per visible (query, key) pair and head."""
+    per-head key and value (2 * 512 * 256 per token and head, whether as one 512-wide branch
+    or four 128-wide ones) and the causal attention, 2 * (192 + 128) per visible (query, key)
+    pair, head and branch."""
     import numpy as np
     proj = 2.0 * float(np.sum(lens)) * w.d_c * (w.d_nope + w.d_v) * w.heads
     pairs = 0.0
     for L in lens:
         vis = np.clip(int(L) - sq + 1 + np.arange(sq), 0, int(L))
         pairs += float(vis.sum())
-    attn = 2.0 * pairs * (w.d_nope + w.d_rope + w.d_v) * w.heads
+    attn = 2.0 * pairs * (w.d_nope + w.d_rope + w.d_v) * w.heads * w.branches
     return proj, attn
 
 

@@ -403,18 +403,24 @@ mla_status mla_cache_append(const mla_append_params* p, const void* hidden, cons
  *   K_t    = W_UK[h] c_t                       (d_nope)   V_t = W_UV[h]^T c_t   (d_v)
  *   s_t    = softmax_scale * (q_nope[b,i,h] . K_t + RoPE(q_rope[b,i,h], P) . k_t),  t <= P
  *   out[b,i,h] = out_scale * sum_{t <= P} softmax(s)_t V_t    (zero when P < 0)
- *   q_nope [B, s_q, H, 1, 128], q_rope [B, s_q, H, 64], out [B, s_q, H, 128], caches, seqlens,
- *   block_table and weights exactly as mla_decode (w_uk [1, H, 128, 512], w_uv [1, H, 512, 128]).
- * Supported: MLA_BF16, num_branches 1, d_latent 512, d_rope 64, d_nope 128, d_v 128, any
- * H in [1, 4096], batch <= 65535, page_size 0 or 64, flags 0, latent_format 0 (otherwise
- * MLA_ERR_UNSUPPORTED).  num_splits is not used.  Pointers of q_nope, q_rope, latent, rope,
+ *   q_nope [B, s_q, H, NB, 128], q_rope [B, s_q, H, 64], out [B, s_q, H, 128], caches, seqlens,
+ *   block_table and weights exactly as mla_decode (w_uk [NB, H, 128, d_latent], w_uv
+ *   [NB, H, d_latent, 128]).
+ * MLRA-4 (num_branches 4, d_latent 128 per branch; "[ICLR 2025] MLRA…", sections 2.1 and
+ * 2.2) as in mlra_decode: branch br up-projects its own latent slice with W_UK[br] and
+ * W_UV[br], scores its own query q_nope[b,i,h,br] plus the shared rotary term, takes its own
+ * softmax, and out = out_scale * the sum of the branch outputs.
+ * Supported: MLA_BF16, num_branches 1 with d_latent 512 or num_branches 4 with d_latent 128,
+ * d_rope 64, d_nope 128, d_v 128, any H in [1, 4096], batch <= 65535, page_size 0 or 64,
+ * flags 0, latent_format 0 (otherwise MLA_ERR_UNSUPPORTED).  num_splits is not used.  Pointers of q_nope, q_rope, latent, rope,
  * w_uk, w_uv and out 16-byte aligned, cache strides multiples of 8 elements (MLA_ERR_ALIGN).
  * The workspace (>= mla_prefill_workspace_size bytes, 256-byte aligned, no initialisation)
- * receives the up-projected keys and values (B x H x L_pad x 128 bf16 each, L_pad =
+ * receives the up-projected keys and values (B x H x NB x L_pad x 128 bf16 each, L_pad =
  * max_seqlen rounded up to a multiple of 256) and a copy of the rotary keys (B x L_pad x 64
- * bf16), in an internal tiled order.  Two kernels run on `stream`: the up-projection (a GEMM
- * of the cached latents against W_UK and W_UV, which also copies the rotary keys) and a
- * causal flash-attention pass.
+ * bf16), in an internal tiled order, and with NB = 4 the branch outputs (B x s_q x H x 4 x
+ * 128 fp32).  Kernels on `stream`: the up-projection (a GEMM of the cached latents against
+ * W_UK and W_UV, which also copies the rotary keys), a causal flash-attention pass per
+ * (head, branch), and with NB = 4 the scaled branch sum.
  */
 mla_status mla_prefill_workspace_size(const mla_params* p, size_t* bytes);
 mla_status mla_prefill(const mla_params* p, const void* q_nope, const void* q_rope,
@@ -423,8 +429,8 @@ mla_status mla_prefill(const mla_params* p, const void* q_nope, const void* q_ro
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 /* Tracing variant of mla_prefill: also records three caller-created HIP events (hipEvent_t
  * values passed as void*) on `stream`: events[0] before the up-projection, events[1] between
- * it and the attention, events[2] after the attention.  A failed hipEventRecord returns
- * MLA_ERR_HIP. */
+ * it and the attention, events[2] after the attention (and, with NB = 4, the branch sum).
+ * A failed hipEventRecord returns MLA_ERR_HIP. */
 mla_status mla_prefill_timed(const mla_params* p, const void* q_nope, const void* q_rope,
                              const void* latent, const void* rope, const int32_t* seqlens,
                              const int32_t* block_table, const void* w_uk, const void* w_uv,

@@ -338,6 +338,7 @@ mla_status run_prefill(const mla_params* p, const void* q_nope, const void* q_ro
   a.kbuf = static_cast<char*>(workspace) + plan.off_k;
   a.rbuf = static_cast<char*>(workspace) + plan.off_r;
   a.vbuf = static_cast<char*>(workspace) + plan.off_v;
+  a.obuf = static_cast<char*>(workspace) + plan.off_o;
   return to_status(launch_prefill(plan, a, stream, events));
 }
 }  // namespace

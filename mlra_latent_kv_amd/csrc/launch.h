@@ -45,14 +45,17 @@ struct PrefillArgs {
   const void* rope;
   const int32_t* seqlens;
   const int32_t* block_table;
-  const void* w_uk;     // [H][128][512]
-  const void* w_uv;     // [H][512][128]
+  const void* w_uk;     // [NB][H][128][dcb]
+  const void* w_uv;     // [NB][H][dcb][128]
   void* out;            // [B][s_q][H][128]
   int64_t lat_tok, lat_seq, rope_tok, rope_seq, bt_stride;
   float softmax_scale, out_scale, rope_theta;
-  void* kbuf;           // workspace: up-projected keys, operand blocks [B][H][L_pad / 32][8 KiB]
-  void* rbuf;           // workspace: rotary keys, operand blocks [B][L_pad / 32][4 KiB]
-  void* vbuf;           // workspace: up-projected values, operand blocks [B][H][L_pad / 32][8 KiB]
+  // workspace: keys and values as operand blocks [B][H NB][L_pad / 32][8 KiB] each, the
+  // rotary keys [B][L_pad / 32][4 KiB], and (NB > 1) the branch outputs [B][s_q][H NB][128] fp32
+  void* kbuf;
+  void* rbuf;
+  void* vbuf;
+  void* obuf;
 };
 // events (tracing, else null): three hipEvent_t recorded before the projection, between the
 // two kernels and after the attention

@@ -208,9 +208,11 @@ mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
       !(p->rope_theta > 0.0f) || !std::isfinite(p->rope_theta))
     return MLA_ERR_SHAPE;
   if (p->page_size != 0 && p->page_size != kPage) return MLA_ERR_UNSUPPORTED;
-  // MLA with the bf16 decode dims; no folded or gated forms, no fp8 latent, no device checks
-  if (p->dtype != MLA_BF16 || p->num_branches != 1 || p->d_latent != 512 || p->d_rope != 64 ||
-      p->d_nope != 128 || p->d_v != 128 || p->flags != 0 || p->latent_format != 0)
+  // MLA (one 512-wide branch) or MLRA-4 (four 128-wide branches) with the bf16 decode dims;
+  // no folded or gated forms, no fp8 latent, no device checks
+  if (p->dtype != MLA_BF16 || (p->num_branches != 1 && p->num_branches != 4) ||
+      p->d_latent != 512 / p->num_branches || p->d_rope != 64 || p->d_nope != 128 ||
+      p->d_v != 128 || p->flags != 0 || p->latent_format != 0)
     return MLA_ERR_UNSUPPORTED;
   if (p->latent_stride_tok < 512 || p->rope_stride_tok < 64 || p->latent_stride_seq < 0 ||
       p->rope_stride_seq < 0)
@@ -224,18 +226,24 @@ mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
   q.B = p->batch;
   q.H = p->num_heads;
   q.sq = p->num_queries > 1 ? p->num_queries : 1;
+  q.NB = p->num_branches;
+  q.dcb = p->d_latent;
   q.paged = p->page_size == kPage;
   q.max_seqlen = p->max_seqlen;
   q.L_pad = (int)(ceil_div(std::max(p->max_seqlen, 1), 256) * 256);
-  // attention grid, one dimension: (sequence, head, pair of 256-token query blocks)
-  if ((ceil_div((int64_t)q.B * q.H, 8) * 8) * ceil_div(ceil_div(q.sq, 256), 2) > INT32_MAX)
+  // attention grid, one dimension: (sequence, head and branch, pair of 256-token query blocks)
+  if ((ceil_div((int64_t)q.B * q.H * q.NB, 8) * 8) * ceil_div(ceil_div(q.sq, 256), 2) > INT32_MAX)
     return MLA_ERR_SHAPE;
-  const size_t kv = (size_t)q.B * q.H * q.L_pad * 128 * 2;
+  // branch-sum grid: one thread per 8 output columns of each (sequence, token, head)
+  if (q.NB > 1 && ceil_div((int64_t)q.B * q.sq * q.H * 16, 256) > INT32_MAX) return MLA_ERR_SHAPE;
+  const size_t kv = (size_t)q.B * q.H * q.NB * q.L_pad * 128 * 2;
   const size_t r = (size_t)q.B * q.L_pad * 64 * 2;
+  const size_t o = q.NB > 1 ? (size_t)q.B * q.sq * q.H * q.NB * 128 * 4 : 0;
   q.off_k = 0;
   q.off_r = align_up(kv);
   q.off_v = q.off_r + align_up(r);
-  q.bytes = q.off_v + align_up(kv);
+  q.off_o = q.off_v + align_up(kv);
+  q.bytes = q.off_o + align_up(o);
   *plan = q;
   return MLA_OK;
 }

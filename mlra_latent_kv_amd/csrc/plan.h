@@ -99,14 +99,17 @@ mla_status check_append_call(const mla_append_params* p, const AppendPlan& plan,
                              size_t workspace_bytes);
 
 // Prefill (mla_prefill): the un-absorbed many-query step.  The workspace holds the keys and
-// values up-projected from the latent (B x H x L_pad x 128 bf16 each) and a copy of the rotary
-// keys (B x L_pad x 64 bf16), all as MFMA operand blocks of 32-token tiles.
+// values up-projected from the latent (B x H x NB x L_pad x 128 bf16 each) and a copy of the
+// rotary keys (B x L_pad x 64 bf16), all as MFMA operand blocks of 32-token tiles, and with
+// MLRA branches (NB = 4) each branch's normalised output (B x s_q x H x NB x 128 fp32) for the
+// branch sum.
 struct PrefillPlan {
   int B, H, sq;       // sequences, weight heads, query tokens per sequence (rows s_q x H)
+  int NB, dcb;        // latent branches (1 MLA, 4 MLRA) and latent columns per branch
   int paged, max_seqlen;
-  int L_pad;          // key rows per (sequence, head) in the workspace: max_seqlen rounded up
-                      // to the projection's 256-token blocks
-  size_t off_k, off_r, off_v, bytes;
+  int L_pad;          // key rows per (sequence, head, branch) in the workspace: max_seqlen
+                      // rounded up to the projection's 256-token blocks
+  size_t off_k, off_r, off_v, off_o, bytes;
 };
 
 // Validates *p for the prefill and fills *plan.  Touches no device.

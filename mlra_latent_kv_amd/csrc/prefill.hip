@@ -19,7 +19,10 @@
 // Query token i of a sequence of L tokens sits at position L - s_q + i, its rotary query is
 // rotated there, and it sees the tokens up to and including itself; a token that sees none
 // writes zeros.  Layouts as the multi-token decode: q_nope [B, s_q, H, 128], q_rope
-// [B, s_q, H, 64], out [B, s_q, H, 128].
+// [B, s_q, H, 64], out [B, s_q, H, 128].  MLRA-4 ("[ICLR 2025] MLRA…", sections 2.1 and
+// 2.2) runs the same two kernels per (head, branch) on each branch's 128-wide latent slice
+// and weights (q_nope [B, s_q, H, 4, 128]), and a third launch sums the four normalised
+// branch outputs times out_scale.
 #include "device_common.h"
 #include "launch.h"
 #include "tile_bf16.h"
@@ -41,14 +44,14 @@ constexpr int kPfDc = 512, kPfDn = 128, kPfDv = 128, kPfDr = 64;
 constexpr int kTileK = kTT * kPfDn * 2, kTileR = kTT * kPfDr * 2, kTileV = kTT * kPfDv * 2;
 
 // ----------------------------------------------------------------------------- K and V
-// One workgroup (8 waves, two per SIMD) per (sequence b, block of 256 tokens, head h).  Wave w
-// computes tokens 64 (w & 3) .. +63 (two 32-row M blocks) of part w >> 2 (0: K, 1: V), all
-// 128 output columns (four 32-column N blocks), MFMA 32x32x16 over the 512 latent columns in
-// eight chunks of 64.  Each chunk stages, by direct-to-LDS loads, the 256 latent rows (128
+// One workgroup (8 waves, two per SIMD) per (sequence b, block of 256 tokens, head h and
+// latent branch br).  Wave w computes tokens 64 (w & 3) .. +63 (two 32-row M blocks) of part
+// w >> 2 (0: K, 1: V), all 128 output columns (four 32-column N blocks), MFMA 32x32x16 over
+// the branch's latent columns (all 512 for MLA, 128 per MLRA branch) in chunks of 64.  Each chunk stages, by direct-to-LDS loads, the 256 latent rows (128
 // bytes of each), W_UK[h]'s 128 rows (their columns of the chunk) and W_UV[h]'s 64 rows of the
 // chunk (256 bytes each); double-buffered, so one chunk's 64 MFMAs per SIMD cover the next
 // one's loads.
-constexpr int kKvTok = 256, kKvChunk = 64, kKvChunks = kPfDc / kKvChunk, kKvWaves = 8;
+constexpr int kKvTok = 256, kKvChunk = 64, kKvWaves = 8;
 constexpr int kKvABytes = kKvTok * kKvChunk * 2;     // 32 KiB
 constexpr int kKvBkBytes = kPfDn * kKvChunk * 2;     // 16 KiB
 constexpr int kKvBvBytes = kKvChunk * kPfDv * 2;     // 16 KiB
@@ -62,6 +65,7 @@ __device__ __forceinline__ uint32_t row128(int r, int c) {
   return (uint32_t)(r * 128 + 16 * (c ^ ((r >> 1) & 7)));
 }
 
+template <int NB>
 __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     const bf16* __restrict__ latent, int64_t lat_tok, int64_t lat_seq,
     const bf16* __restrict__ rope, int64_t rope_tok, int64_t rope_seq,
@@ -73,15 +77,19 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     char st[2][kKvStage];
   };
   __shared__ __align__(16) Smem sm;  // 128 KiB, reused for the output tile
-  const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tb = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;  // hb = h NB + br
+  const int h = hb / NB, br = hb % NB;
+  constexpr int dcb = kPfDc / NB, n_chunks = dcb / kKvChunk;  // latent columns of the branch
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, kg = lane >> 5;
   const int L = min(max(seqlens[b], 0), max_seqlen);
   const int t0 = tb * kKvTok;
   const uint32_t lat_row_b = (uint32_t)(lat_tok * 2);
-  const char* wk = reinterpret_cast<const char*>(w_uk + (size_t)h * kPfDn * kPfDc);
-  const char* wv = reinterpret_cast<const char*>(w_uv + (size_t)h * kPfDc * kPfDv);
+  // W_UK [NB][H][128][dcb] and W_UV [NB][H][dcb][128]: the (branch, head) blocks
+  const char* wk = reinterpret_cast<const char*>(w_uk + ((size_t)br * H + h) * kPfDn * dcb);
+  const char* wv = reinterpret_cast<const char*>(w_uv + ((size_t)br * H + h) * dcb * kPfDv);
+  const uint32_t col0_b = (uint32_t)(br * dcb * 2);  // the branch's first latent byte in a row
 
   // wave w issues loads 8w .. 8w + 7 of a stage: 0..31 latent rows 8i.., 32..47 W_UK rows
   // 8(i - 32).., 48..63 W_UV rows 4(i - 48).. (one KiB each); rows past the sequence read as
@@ -105,14 +113,14 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
         const int vu = __builtin_amdgcn_readfirstlane(valid);
         const int r = lane >> 3, c = lane & 7;
         dma16(rsrc(base, vu * lat_row_b), s + r0 * 128,
-              r * lat_row_b + q * 128 + 16 * (c ^ (((r0 + r) >> 1) & 7)));
+              r * lat_row_b + col0_b + q * 128 + 16 * (c ^ (((r0 + r) >> 1) & 7)));
       } else if (i < 48) {
         const int r0 = 8 * (i - 32), r = r0 + (lane >> 3), c = lane & 7;
-        dma16(rsrc(wk, kPfDn * kPfDc * 2), s + kKvABytes + r0 * 128,
-              r * (kPfDc * 2) + q * 128 + 16 * (c ^ ((r >> 1) & 7)));
+        dma16(rsrc(wk, kPfDn * dcb * 2), s + kKvABytes + r0 * 128,
+              r * (dcb * 2) + q * 128 + 16 * (c ^ ((r >> 1) & 7)));
       } else {
         const int r0 = 4 * (i - 48), r = r0 + (lane >> 4), c = lane & 15;
-        dma16(rsrc(wv, kPfDc * kPfDv * 2), s + kKvABytes + kKvBkBytes + r0 * 256,
+        dma16(rsrc(wv, dcb * kPfDv * 2), s + kKvABytes + kKvBkBytes + r0 * 256,
               (q * kKvChunk + r) * (kPfDv * 2) + 16 * (c ^ lat_sw<Sw32>(r)));
       }
     }
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
   // the first head's workgroups also copy the block's rotary keys into the workspace as
   // operand blocks: thread tid, pieces tid + 512 u = (tile, step m, lane i) in order; zeros
   // past the sequence
-  if (h == 0) {
+  if (hb == 0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int pc = tid + 512 * u;
@@ -147,8 +155,8 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
   const int G = lane >> 4, li = lane & 15;
 
   issue(0);
-  for (int q = 0; q < kKvChunks; ++q) {
-    if (q + 1 < kKvChunks) {
+  for (int q = 0; q < n_chunks; ++q) {
+    if (q + 1 < n_chunks) {
       issue(q + 1);
       wait_vmcnt<kKvIssues>();  // chunk q has landed for this wave
     } else {
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
   constexpr int kPitchK = 2 * kPfDn + 16, kPitchV = 2 * kPfDv + 64;
   static_assert(kKvTok * kPitchV <= sizeof(Smem), "output tile exceeds the LDS");
   char* o = reinterpret_cast<char*>(&sm);
-  const size_t head_tok = ((size_t)b * H + h) * L_pad + t0;  // first token of the block
+  const size_t head_tok = ((size_t)b * H * NB + hb) * L_pad + t0;  // first token of the block
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
     const int pitch = pt == 0 ? kPitchK : kPitchV;
@@ -259,7 +267,8 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
     const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ kbuf,
     const bf16* __restrict__ rbuf, const bf16* __restrict__ vbuf, bf16* __restrict__ out,
-    int B, int H, int sq, int L_pad, float qscale, float out_scale, RopeFreq rf) {
+    float* __restrict__ obr, int B, int H, int NB, int sq, int L_pad, float qscale,
+    float out_scale, RopeFreq rf) {
   struct Smem {
     char ring[kAtRing][kAtBuf];
   };
@@ -273,16 +282,17 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
   const int n_qb = (sq + kAtRows - 1) / kAtRows;
   const int n_wg = (n_qb + 1) / 2;
   const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
+  const int HB = H * NB;                    // (head, branch) pairs: hb = h NB + br
   const int bh = (r / n_wg) * 8 + x;
-  if (bh >= B * H) return;  // padding of the grid to whole groups of eight pairs
+  if (bh >= B * HB) return;  // padding of the grid to whole groups of eight pairs
   const int jb = r % n_wg;
-  const int b = bh / H, h = bh % H;
+  const int b = bh / HB, hb = bh % HB, h = hb / NB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, kg = lane >> 5;
   const int L = min(max(seqlens[b], 0), max_seqlen);
-  const char* kb = reinterpret_cast<const char*>(kbuf + ((size_t)b * H + h) * L_pad * kPfDn);
-  const char* vb = reinterpret_cast<const char*>(vbuf + ((size_t)b * H + h) * L_pad * kPfDv);
+  const char* kb = reinterpret_cast<const char*>(kbuf + ((size_t)b * HB + hb) * L_pad * kPfDn);
+  const char* vb = reinterpret_cast<const char*>(vbuf + ((size_t)b * HB + hb) * L_pad * kPfDv);
   const char* rb = reinterpret_cast<const char*>(rbuf + (size_t)b * L_pad * kPfDr);
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
   // a lane's operand in any block of ring buffer k: one register per tile, constants after
@@ -318,10 +328,12 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     // scaled by softmax_scale * log2(e).  Rows past s_q load row s_q - 1 and are not stored.
     bf16x8 qb8[12];
     {
+      // q_nope [B][s_q][H][NB][128] holds the branch's query at (head, branch) row hb;
+      // q_rope [B][s_q][H][64] is shared by the branches of a head
       const int irc = min(ir, sq - 1);
-      const size_t row = ((size_t)b * sq + irc) * H + h;
-      const bf16* qn = q_nope + row * kPfDn + 8 * kg;
-      const bf16* qr = q_rope + row * kPfDr + 8 * kg;
+      const size_t tok = (size_t)b * sq + irc;
+      const bf16* qn = q_nope + (tok * HB + hb) * kPfDn + 8 * kg;
+      const bf16* qr = q_rope + (tok * H + h) * kPfDr + 8 * kg;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const bf16x8 v = *(const bf16x8*)(qn + 16 * j);
@@ -465,20 +477,58 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     wait_vmcnt<0>();
     lds_barrier();
 
-    // out[row][d] = out_scale * O / l; O^T item e of block cb: column 32 cb + 8 (e / 4) +
-    // 4 kg + e % 4 of row l32
+    // out[row][d] = out_scale * O / l (MLA), or the branch's O / l into the fp32 branch
+    // outputs (MLRA, summed and scaled by the next launch); O^T item e of block cb: column
+    // 32 cb + 8 (e / 4) + 4 kg + e % 4 of row l32
     if (ir < sq) {
-      const float inv = l_run > 0.0f ? out_scale / l_run : 0.0f;
-      bf16* orow = out + (((size_t)b * sq + ir) * H + h) * kPfDv;
+      const float inv = l_run > 0.0f ? (NB == 1 ? out_scale : 1.0f) / l_run : 0.0f;
+      if (NB == 1) {
+        bf16* orow = out + (((size_t)b * sq + ir) * H + h) * kPfDv;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *(bf16x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
-              bf16x4{(bf16)(O[cb][4 * q] * inv), (bf16)(O[cb][4 * q + 1] * inv),
-                     (bf16)(O[cb][4 * q + 2] * inv), (bf16)(O[cb][4 * q + 3] * inv)};
+          for (int q = 0; q < 4; ++q)
+            *(bf16x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
+                bf16x4{(bf16)(O[cb][4 * q] * inv), (bf16)(O[cb][4 * q + 1] * inv),
+                       (bf16)(O[cb][4 * q + 2] * inv), (bf16)(O[cb][4 * q + 3] * inv)};
+      } else {
+        float* orow = obr + (((size_t)b * sq + ir) * HB + hb) * kPfDv;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(f32x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
+                f32x4{O[cb][4 * q] * inv, O[cb][4 * q + 1] * inv, O[cb][4 * q + 2] * inv,
+                      O[cb][4 * q + 3] * inv};
+      }
     }
   }
+}
+
+// ----------------------------------------------------------------------------- branch sum
+// MLRA: out[b][i][h] = out_scale * sum over branches of the branch outputs (each already
+// normalised by its own softmax sum), fp32, rounded once to bf16.  One thread per 8 columns.
+__global__ __launch_bounds__(256) void k_prefill_branch_sum(const float* __restrict__ obr,
+                                                            bf16* __restrict__ out, int NB,
+                                                            int64_t rows, float out_scale) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, 8-column piece)
+  if (i >= rows * (kPfDv / 8)) return;
+  const int64_t row = i / (kPfDv / 8);
+  const int c = (int)(i % (kPfDv / 8)) * 8;
+  float acc[8] = {};
+  for (int br = 0; br < NB; ++br) {
+    const float* src = obr + (row * NB + br) * kPfDv + c;
+    const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += lo[e];
+      acc[4 + e] += hi[e];
+    }
+  }
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)(acc[e] * out_scale);
+  *(bf16x8*)(out + row * kPfDv + c) = v;
 }
 
 }  // namespace
@@ -490,7 +540,8 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_prefill_kv, dim3(p.L_pad / kKvTok, p.H, p.B), dim3(64 * kKvWaves), 0, s,
+  hipLaunchKernelGGL(p.NB == 1 ? k_prefill_kv<1> : k_prefill_kv<4>,
+                     dim3(p.L_pad / kKvTok, p.H * p.NB, p.B), dim3(64 * kKvWaves), 0, s,
                      (const bf16*)a.latent, a.lat_tok, a.lat_seq, (const bf16*)a.rope,
                      a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
                      p.max_seqlen, (const bf16*)a.w_uk, (const bf16*)a.w_uv, (bf16*)a.kbuf,
@@ -501,13 +552,20 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   RopeFreq rf;
   make_rope_freq(kPfDr, a.rope_theta, &rf);
   const int n_wg = ((p.sq + kAtRows - 1) / kAtRows + 1) / 2;  // workgroups per (b, h)
-  const int64_t groups = ((int64_t)p.B * p.H + 7) / 8;  // pairs (b, h) in groups of eight
+  const int64_t groups = ((int64_t)p.B * p.H * p.NB + 7) / 8;  // (b, h, branch) in eights
   hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_wg)), dim3(64 * kAtWaves), 0,
                      s, (const bf16*)a.q_nope, (const bf16*)a.q_rope, a.seqlens, p.max_seqlen,
                      (const bf16*)a.kbuf, (const bf16*)a.rbuf, (const bf16*)a.vbuf,
-                     (bf16*)a.out, p.B, p.H, p.sq, p.L_pad, a.softmax_scale * kLog2e,
-                     a.out_scale, rf);
+                     (bf16*)a.out, (float*)a.obuf, p.B, p.H, p.NB, p.sq, p.L_pad,
+                     a.softmax_scale * kLog2e, a.out_scale, rf);
   e = hipGetLastError();
+  if (e == hipSuccess && p.NB > 1) {
+    const int64_t rows = (int64_t)p.B * p.sq * p.H;
+    const int64_t pieces = rows * (kPfDv / 8);
+    hipLaunchKernelGGL(k_prefill_branch_sum, dim3((unsigned)((pieces + 255) / 256)), dim3(256),
+                       0, s, (const float*)a.obuf, (bf16*)a.out, p.NB, rows, a.out_scale);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess) e = mark(2);
   return e;
 }

@@ -106,6 +106,9 @@ PREFILL_WORKLOADS = {
                  d_v=128, d_cb=512, d_rope=64, dtype="bf16", paged=False, seqlen=4096, seed=1007),
         Workload("prefill_bf16_paged_b4_h32_l4096", batch=4, heads=32, branches=1, d_nope=128,
                  d_v=128, d_cb=512, d_rope=64, dtype="bf16", paged=True, seqlen=4096, seed=1008),
+        Workload("prefill_mlra4_bf16_b1_h32_l4096", batch=1, heads=32, branches=4, d_nope=128,
+                 d_v=128, d_cb=128, d_rope=64, dtype="bf16", paged=False, seqlen=4096,
+                 out_scale=0.5, seed=1009),
     ]
 }
 

@@ -450,14 +450,19 @@ def test_append_call_checks(lib):
 
 # ----------------------------------------------------------------------------- prefill
 def test_prefill_workspace_size_and_validation(lib):
-    """mla_prefill's host checks: every call below fails validation before anything is
-    launched (the pointers are never dereferenced)."""
+    """mla_prefill's workspace sizes (MLA and MLRA-4) and host checks: every call below fails
+    validation before anything is launched (the pointers are never dereferenced)."""
     p = params_for("mla_bf16_b32_h128_l4096", num_queries=300, max_seqlen=300)
     # keys and values, B x H x L_pad x 128 bf16 each (L_pad = 300 rounded up to 512), and
     # the rotary keys, B x L_pad x 64 bf16
     assert B.prefill_workspace_size(p) == 2 * 2 * 128 * 512 * 128 * 2 + 2 * 512 * 64 * 2
     p1 = params_for("mla_bf16_b32_h128_l4096", num_queries=1, max_seqlen=1)
     assert B.prefill_workspace_size(p1) == 2 * 2 * 128 * 256 * 128 * 2 + 2 * 256 * 64 * 2
+    # MLRA-4 (four 128-wide branches): keys and values per (head, branch), the rotary keys,
+    # and the fp32 branch outputs B x s_q x H x 4 x 128
+    p4 = params_for("mlra4_bf16_b32_h32_l8192", num_queries=300, max_seqlen=300)
+    assert B.prefill_workspace_size(p4) == (2 * 2 * 32 * 4 * 512 * 128 * 2 + 2 * 512 * 64 * 2
+                                            + 2 * 300 * 32 * 4 * 128 * 4)
     ws = B.prefill_workspace_size(p)
     assert call(lib, p, fn="mla_prefill", ws_bytes=ws - 1) == 4        # MLA_ERR_WORKSPACE
     assert call(lib, p, fn="mla_prefill", q_nope=None) == 1            # MLA_ERR_NULL
@@ -465,7 +470,8 @@ def test_prefill_workspace_size_and_validation(lib):
     assert call(lib, p, fn="mla_prefill", q_rope=FAKE + 8) == 7        # MLA_ERR_ALIGN
     assert call(lib, p, fn="mla_prefill", out=FAKE + 2) == 7
     assert call(lib, p, fn="mla_prefill", workspace=FAKE + 16) == 7
-    for over, status in [(dict(num_branches=4, d_latent=128), 3),     # MLA only
+    for over, status in [(dict(num_branches=4, d_latent=512), 3),     # MLRA-4 at 128 per branch
+                         (dict(num_branches=2, d_latent=256), 3),
                          (dict(d_latent=128), 3), (dict(d_nope=64), 3),
                          (dict(flags=B.MLA_FLAG_QUERY_LATENT), 3),
                          (dict(dtype=B.MLA_F32), 3), (dict(dtype=9), 5),

@@ -1,11 +1,11 @@
-"""GPU prefill (mla_prefill: many new tokens per sequence, un-absorbed) against the fp64
-oracle's prefill, which computes the same causal definition as the multi-token decode (token
-i at position L - s_q + i sees tokens 0 .. L - s_q + i).  Cases cover contiguous and paged
-caches, lengths that are not multiples of the 32-token key tiles, the 64-token pages or the
-256-token query and projection blocks, L < s_q (rows that see nothing are exactly zero), the
-default and the sharp query distributions, agreement with the absorbed decode path at small
-s_q, and the full-size prefill workload on sampled rows.  Bounds as for the decode (max-abs
-2e-2, rel-L2 1e-2, worst per-row rel-L2 5e-2).
+"""GPU prefill (mla_prefill: many new tokens per sequence, un-absorbed; MLA and MLRA-4)
+against the fp64 oracle's prefill, which computes the same causal definition as the
+multi-token decode (token i at position L - s_q + i sees tokens 0 .. L - s_q + i).  Cases
+cover contiguous and paged caches, lengths that are not multiples of the 32-token key tiles,
+the 64-token pages or the 256-token query and projection blocks, L < s_q (rows that see
+nothing are exactly zero), the default and the sharp query distributions, agreement with
+the absorbed decode path at small s_q, and the full-size prefill workloads on sampled rows.
+Bounds as for the decode (max-abs 2e-2, rel-L2 1e-2, worst per-row rel-L2 5e-2).
 """
 
 import numpy as np
@@ -111,6 +111,61 @@ def test_prefill_head_counts_off_the_grid_groups(w, sq, lens):
         assert_close(got, oracle_prefill(inp), "bf16", f"{w.name} sq={sq} sharp={sharp}")
 
 
+MLRA4 = I.WORKLOADS["mlra4_bf16_b32_h32_l8192"]
+MLRA4_PAGED = I.Workload("prefill_mlra4_paged_b3_h32", batch=3, heads=32, branches=4, d_nope=128,
+                         d_v=128, d_cb=128, d_rope=64, dtype="bf16", paged=True, seqlen=700,
+                         out_scale=0.5, seed=33)
+
+
+@pytest.mark.parametrize("w,sq,lens", [(MLRA4, 200, [300, 129]), (MLRA4, 33, [33, 95, 161]),
+                                       (MLRA4_PAGED, 257, [700, 257, 2])],
+                         ids=["mlra4_sq200", "mlra4_sq33_tails", "mlra4_paged_sq257"])
+def test_prefill_mlra_matches_oracle(w, sq, lens):
+    """MLRA-4: four 128-wide branches per head, each with its own up-projected keys and
+    values, query and softmax, the shared rotary score, and the scaled branch sum; distinct
+    per-branch queries (default and sharp)."""
+    for sharp in (False, True):
+        inp = I.make_inputs(w, seed=5, seqlens=lens, num_queries=sq,
+                            q_gain=I.sharp_q_gain(w) if sharp else 1.0)
+        got, _ = gpu_prefill(inp)
+        ref = oracle_prefill(inp)
+        assert got.shape == ref.shape == (len(lens), sq * w.heads, w.d_v)
+        for b, L in enumerate(lens):
+            dead = max(0, sq - L)
+            assert not got[b, : dead * w.heads].any(), "a token that sees nothing is not zero"
+        assert_close(got, ref, "bf16", f"{w.name} sq={sq} sharp={sharp}")
+
+
+@pytest.mark.parametrize("sq", [1, 4, 16])
+def test_prefill_mlra_agrees_with_absorbed_decode(sq):
+    """The un-absorbed MLRA-4 prefill and the absorbed multi-token mlra_decode compute one
+    definition."""
+    import torch
+    from mlra_latent_kv_amd import harness as H
+    inp = I.make_inputs(MLRA4, seed=12, seqlens=[640, 70, 17], num_queries=sq,
+                        q_gain=I.sharp_q_gain(MLRA4))
+    pre, _ = gpu_prefill(inp)
+    case = H.to_device(inp)
+    dec = case.run()
+    torch.cuda.synchronize()
+    dec = dec.float().cpu().numpy().astype(np.float64)
+    assert_close(pre, dec, "bf16", f"mlra4 prefill vs absorbed decode s_q={sq}")
+    assert_close(pre, oracle_prefill(inp), "bf16", f"mlra4 prefill vs oracle s_q={sq}")
+
+
+def test_prefill_mlra_full_size_sampled():
+    """The MLRA-4 prefill workload (one sequence of 4096 new tokens, 32 heads, four branches)
+    at full size, sharp queries, on sampled rows across the query blocks and heads."""
+    w = I.PREFILL_WORKLOADS["prefill_mlra4_bf16_b1_h32_l4096"]
+    inp = I.make_inputs(w, num_queries=w.seqlen, q_gain=I.sharp_q_gain(w))
+    got, _ = gpu_prefill(inp)
+    tokens = [0, 1, 31, 32, 255, 256, 2047, 2048, 4095]
+    heads = [0, 7, 16, 31]
+    rows = [i * w.heads + h for i in tokens for h in heads]
+    ref = oracle_prefill(inp, heads=rows)
+    assert_close(got[:, rows], ref, "bf16", "mlra4 prefill full size sampled")
+
+
 def test_prefill_empty_sequences_write_zeros():
     inp = I.make_inputs(H128, seed=3, seqlens=[0, 0], num_queries=40, max_seqlen=64)
     got, _ = gpu_prefill(inp)
@@ -156,9 +211,10 @@ def test_prefill_timed_matches_untimed():
 
 
 def test_prefill_rejects_unsupported():
+    """One MLRA branch on its own (128-wide latent, no branch sum) has no prefill."""
     from mlra_latent_kv_amd import binding as B
     from mlra_latent_kv_amd import harness as H
-    inp = I.make_inputs(I.WORKLOADS["mlra4_bf16_b32_h32_l8192"], seed=1, seqlens=[10],
+    inp = I.make_inputs(I.WORKLOADS["mlra_shard_bf16_b32_h32_l8192"], seed=1, seqlens=[10],
                         num_queries=4)
     p = H.make_params(inp)
     with pytest.raises(B.MlaError, match="UNSUPPORTED"):
