@@ -418,7 +418,7 @@ mla_status mla_cache_append(const mla_append_params* p, const void* hidden, cons
  * receives the up-projected keys and values (B x H x NB x L_pad x 128 bf16 each, L_pad =
  * max_seqlen rounded up to a multiple of 256) and a copy of the rotary keys (B x L_pad x 64
  * bf16), in an internal tiled order, and with NB = 4 the branch outputs (B x s_q x H x 4 x
- * 128 fp32).  Kernels on `stream`: the up-projection (a GEMM of the cached latents against
+ * 128 bf16).  Kernels on `stream`: the up-projection (a GEMM of the cached latents against
  * W_UK and W_UV, which also copies the rotary keys), a causal flash-attention pass per
  * (head, branch), and with NB = 4 the scaled branch sum.
  */

@@ -51,7 +51,7 @@ struct PrefillArgs {
   int64_t lat_tok, lat_seq, rope_tok, rope_seq, bt_stride;
   float softmax_scale, out_scale, rope_theta;
   // workspace: keys and values as operand blocks [B][H NB][L_pad / 32][8 KiB] each, the
-  // rotary keys [B][L_pad / 32][4 KiB], and (NB > 1) the branch outputs [B][s_q][H NB][128] fp32
+  // rotary keys [B][L_pad / 32][4 KiB], and (NB > 1) the branch outputs [B][s_q][H NB][128] bf16
   void* kbuf;
   void* rbuf;
   void* vbuf;

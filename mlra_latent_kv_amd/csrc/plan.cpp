@@ -238,7 +238,7 @@ mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
   if (q.NB > 1 && ceil_div((int64_t)q.B * q.sq * q.H * 16, 256) > INT32_MAX) return MLA_ERR_SHAPE;
   const size_t kv = (size_t)q.B * q.H * q.NB * q.L_pad * 128 * 2;
   const size_t r = (size_t)q.B * q.L_pad * 64 * 2;
-  const size_t o = q.NB > 1 ? (size_t)q.B * q.sq * q.H * q.NB * 128 * 4 : 0;
+  const size_t o = q.NB > 1 ? (size_t)q.B * q.sq * q.H * q.NB * 128 * 2 : 0;
   q.off_k = 0;
   q.off_r = align_up(kv);
   q.off_v = q.off_r + align_up(r);

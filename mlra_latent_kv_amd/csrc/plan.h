@@ -101,7 +101,7 @@ mla_status check_append_call(const mla_append_params* p, const AppendPlan& plan,
 // Prefill (mla_prefill): the un-absorbed many-query step.  The workspace holds the keys and
 // values up-projected from the latent (B x H x NB x L_pad x 128 bf16 each) and a copy of the
 // rotary keys (B x L_pad x 64 bf16), all as MFMA operand blocks of 32-token tiles, and with
-// MLRA branches (NB = 4) each branch's normalised output (B x s_q x H x NB x 128 fp32) for the
+// MLRA branches (NB = 4) each branch's normalised output (B x s_q x H x NB x 128 bf16) for the
 // branch sum.
 struct PrefillPlan {
   int B, H, sq;       // sequences, weight heads, query tokens per sequence (rows s_q x H)

@@ -267,7 +267,7 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
     const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ kbuf,
     const bf16* __restrict__ rbuf, const bf16* __restrict__ vbuf, bf16* __restrict__ out,
-    float* __restrict__ obr, int B, int H, int NB, int sq, int L_pad, float qscale,
+    bf16* __restrict__ obr, int B, int H, int NB, int sq, int L_pad, float qscale,
     float out_scale, RopeFreq rf) {
   struct Smem {
     char ring[kAtRing][kAtBuf];
@@ -477,38 +477,29 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
     wait_vmcnt<0>();
     lds_barrier();
 
-    // out[row][d] = out_scale * O / l (MLA), or the branch's O / l into the fp32 branch
-    // outputs (MLRA, summed and scaled by the next launch); O^T item e of block cb: column
-    // 32 cb + 8 (e / 4) + 4 kg + e % 4 of row l32
+    // out[row][d] = out_scale * O / l (MLA), or the branch's O / l into the branch outputs
+    // (MLRA, bf16, summed in fp32 and scaled by the next launch); O^T item e of block cb:
+    // column 32 cb + 8 (e / 4) + 4 kg + e % 4 of row l32
     if (ir < sq) {
       const float inv = l_run > 0.0f ? (NB == 1 ? out_scale : 1.0f) / l_run : 0.0f;
-      if (NB == 1) {
-        bf16* orow = out + (((size_t)b * sq + ir) * H + h) * kPfDv;
+      bf16* orow = NB == 1 ? out + (((size_t)b * sq + ir) * H + h) * kPfDv
+                           : obr + (((size_t)b * sq + ir) * HB + hb) * kPfDv;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *(bf16x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
-                bf16x4{(bf16)(O[cb][4 * q] * inv), (bf16)(O[cb][4 * q + 1] * inv),
-                       (bf16)(O[cb][4 * q + 2] * inv), (bf16)(O[cb][4 * q + 3] * inv)};
-      } else {
-        float* orow = obr + (((size_t)b * sq + ir) * HB + hb) * kPfDv;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *(f32x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
-                f32x4{O[cb][4 * q] * inv, O[cb][4 * q + 1] * inv, O[cb][4 * q + 2] * inv,
-                      O[cb][4 * q + 3] * inv};
-      }
+        for (int q = 0; q < 4; ++q)
+          *(bf16x4*)(orow + 32 * cb + 8 * q + 4 * kg) =
+              bf16x4{(bf16)(O[cb][4 * q] * inv), (bf16)(O[cb][4 * q + 1] * inv),
+                     (bf16)(O[cb][4 * q + 2] * inv), (bf16)(O[cb][4 * q + 3] * inv)};
     }
   }
 }
 
 // ----------------------------------------------------------------------------- branch sum
 // MLRA: out[b][i][h] = out_scale * sum over branches of the branch outputs (each already
-// normalised by its own softmax sum), fp32, rounded once to bf16.  One thread per 8 columns.
-__global__ __launch_bounds__(256) void k_prefill_branch_sum(const float* __restrict__ obr,
+// normalised by its own softmax sum), summed in fp32 and rounded once to bf16.  One thread
+// per 8 columns.
+__global__ __launch_bounds__(256) void k_prefill_branch_sum(const bf16* __restrict__ obr,
                                                             bf16* __restrict__ out, int NB,
                                                             int64_t rows, float out_scale) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, 8-column piece)
@@ -517,13 +508,9 @@ __global__ __launch_bounds__(256) void k_prefill_branch_sum(const float* __restr
   const int c = (int)(i % (kPfDv / 8)) * 8;
   float acc[8] = {};
   for (int br = 0; br < NB; ++br) {
-    const float* src = obr + (row * NB + br) * kPfDv + c;
-    const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
+    const bf16x8 v = *(const bf16x8*)(obr + (row * NB + br) * kPfDv + c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += lo[e];
-      acc[4 + e] += hi[e];
-    }
+    for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
   }
   bf16x8 v;
 #pragma unroll
@@ -556,14 +543,14 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   hipLaunchKernelGGL(k_prefill_attn, dim3((unsigned)(groups * 8 * n_wg)), dim3(64 * kAtWaves), 0,
                      s, (const bf16*)a.q_nope, (const bf16*)a.q_rope, a.seqlens, p.max_seqlen,
                      (const bf16*)a.kbuf, (const bf16*)a.rbuf, (const bf16*)a.vbuf,
-                     (bf16*)a.out, (float*)a.obuf, p.B, p.H, p.NB, p.sq, p.L_pad,
+                     (bf16*)a.out, (bf16*)a.obuf, p.B, p.H, p.NB, p.sq, p.L_pad,
                      a.softmax_scale * kLog2e, a.out_scale, rf);
   e = hipGetLastError();
   if (e == hipSuccess && p.NB > 1) {
     const int64_t rows = (int64_t)p.B * p.sq * p.H;
     const int64_t pieces = rows * (kPfDv / 8);
     hipLaunchKernelGGL(k_prefill_branch_sum, dim3((unsigned)((pieces + 255) / 256)), dim3(256),
-                       0, s, (const float*)a.obuf, (bf16*)a.out, p.NB, rows, a.out_scale);
+                       0, s, (const bf16*)a.obuf, (bf16*)a.out, p.NB, rows, a.out_scale);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark(2);

@@ -459,10 +459,10 @@ def test_prefill_workspace_size_and_validation(lib):
     p1 = params_for("mla_bf16_b32_h128_l4096", num_queries=1, max_seqlen=1)
     assert B.prefill_workspace_size(p1) == 2 * 2 * 128 * 256 * 128 * 2 + 2 * 256 * 64 * 2
     # MLRA-4 (four 128-wide branches): keys and values per (head, branch), the rotary keys,
-    # and the fp32 branch outputs B x s_q x H x 4 x 128
+    # and the bf16 branch outputs B x s_q x H x 4 x 128
     p4 = params_for("mlra4_bf16_b32_h32_l8192", num_queries=300, max_seqlen=300)
     assert B.prefill_workspace_size(p4) == (2 * 2 * 32 * 4 * 512 * 128 * 2 + 2 * 512 * 64 * 2
-                                            + 2 * 300 * 32 * 4 * 128 * 4)
+                                            + 2 * 300 * 32 * 4 * 128 * 2)
     ws = B.prefill_workspace_size(p)
     assert call(lib, p, fn="mla_prefill", ws_bytes=ws - 1) == 4        # MLA_ERR_WORKSPACE
     assert call(lib, p, fn="mla_prefill", q_nope=None) == 1            # MLA_ERR_NULL
