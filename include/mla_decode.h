@@ -410,9 +410,10 @@ mla_status mla_cache_append(const mla_append_params* p, const void* hidden, cons
  * 2.2) as in mlra_decode: branch br up-projects its own latent slice with W_UK[br] and
  * W_UV[br], scores its own query q_nope[b,i,h,br] plus the shared rotary term, takes its own
  * softmax, and out = out_scale * the sum of the branch outputs.
- * Supported: MLA_BF16, num_branches 1 with d_latent 512 or num_branches 4 with d_latent 128,
- * d_rope 64, d_nope 128, d_v 128, any H in [1, 4096], batch <= 65535, page_size 0 or 64,
- * flags 0, latent_format 0 (otherwise MLA_ERR_UNSUPPORTED).  num_splits is not used.  Pointers of q_nope, q_rope, latent, rope,
+ * Supported: MLA_BF16, num_branches 1 with d_latent 512 (MLA) or 128 (one MLRA branch cached
+ * on its own, the tensor-parallel shard) or num_branches 4 with d_latent 128, d_rope 64,
+ * d_nope 128, d_v 128, any H in [1, 4096], batch <= 65535, page_size 0 or 64, flags 0,
+ * latent_format 0 (otherwise MLA_ERR_UNSUPPORTED).  num_splits is not used.  Pointers of q_nope, q_rope, latent, rope,
  * w_uk, w_uv and out 16-byte aligned, cache strides multiples of 8 elements (MLA_ERR_ALIGN).
  * The workspace (>= mla_prefill_workspace_size bytes, 256-byte aligned, no initialisation)
  * receives the up-projected keys and values (B x H x NB x L_pad x 128 bf16 each, L_pad =

@@ -208,14 +208,16 @@ mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
       !(p->rope_theta > 0.0f) || !std::isfinite(p->rope_theta))
     return MLA_ERR_SHAPE;
   if (p->page_size != 0 && p->page_size != kPage) return MLA_ERR_UNSUPPORTED;
-  // MLA (one 512-wide branch) or MLRA-4 (four 128-wide branches) with the bf16 decode dims;
-  // no folded or gated forms, no fp8 latent, no device checks
-  if (p->dtype != MLA_BF16 || (p->num_branches != 1 && p->num_branches != 4) ||
-      p->d_latent != 512 / p->num_branches || p->d_rope != 64 || p->d_nope != 128 ||
+  // MLA (one 512-wide branch), MLRA-4 (four 128-wide branches) or one MLRA branch on its own
+  // (128 wide) with the bf16 decode dims; no folded or gated forms, no fp8 latent, no device
+  // checks
+  const bool shape_ok = (p->num_branches == 1 && (p->d_latent == 512 || p->d_latent == 128)) ||
+                        (p->num_branches == 4 && p->d_latent == 128);
+  if (p->dtype != MLA_BF16 || !shape_ok || p->d_rope != 64 || p->d_nope != 128 ||
       p->d_v != 128 || p->flags != 0 || p->latent_format != 0)
     return MLA_ERR_UNSUPPORTED;
-  if (p->latent_stride_tok < 512 || p->rope_stride_tok < 64 || p->latent_stride_seq < 0 ||
-      p->rope_stride_seq < 0)
+  if (p->latent_stride_tok < (int64_t)p->num_branches * p->d_latent || p->rope_stride_tok < 64 ||
+      p->latent_stride_seq < 0 || p->rope_stride_seq < 0)
     return MLA_ERR_SHAPE;
   if ((p->latent_stride_tok | p->latent_stride_seq | p->rope_stride_tok | p->rope_stride_seq) % 8)
     return MLA_ERR_ALIGN;

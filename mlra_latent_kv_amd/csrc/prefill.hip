@@ -47,7 +47,8 @@ constexpr int kTileK = kTT * kPfDn * 2, kTileR = kTT * kPfDr * 2, kTileV = kTT *
 // One workgroup (8 waves, two per SIMD) per (sequence b, block of 256 tokens, head h and
 // latent branch br).  Wave w computes tokens 64 (w & 3) .. +63 (two 32-row M blocks) of part
 // w >> 2 (0: K, 1: V), all 128 output columns (four 32-column N blocks), MFMA 32x32x16 over
-// the branch's latent columns (all 512 for MLA, 128 per MLRA branch) in chunks of 64.  Each chunk stages, by direct-to-LDS loads, the 256 latent rows (128
+// the branch's DCB latent columns (512 for MLA; 128 per MLRA branch, or for one MLRA branch
+// cached on its own) in chunks of 64.  Each chunk stages, by direct-to-LDS loads, the 256 latent rows (128
 // bytes of each), W_UK[h]'s 128 rows (their columns of the chunk) and W_UV[h]'s 64 rows of the
 // chunk (256 bytes each); double-buffered, so one chunk's 64 MFMAs per SIMD cover the next
 // one's loads.
@@ -65,21 +66,21 @@ __device__ __forceinline__ uint32_t row128(int r, int c) {
   return (uint32_t)(r * 128 + 16 * (c ^ ((r >> 1) & 7)));
 }
 
-template <int NB>
+template <int DCB>
 __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     const bf16* __restrict__ latent, int64_t lat_tok, int64_t lat_seq,
     const bf16* __restrict__ rope, int64_t rope_tok, int64_t rope_seq,
     const int32_t* __restrict__ bt, int64_t bt_stride, int paged,
     const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ w_uk,
     const bf16* __restrict__ w_uv, bf16* __restrict__ kout, bf16* __restrict__ rout,
-    bf16* __restrict__ vout, int H, int L_pad) {
+    bf16* __restrict__ vout, int H, int NB, int L_pad) {
   struct Smem {
     char st[2][kKvStage];
   };
   __shared__ __align__(16) Smem sm;  // 128 KiB, reused for the output tile
   const int tb = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;  // hb = h NB + br
   const int h = hb / NB, br = hb % NB;
-  constexpr int dcb = kPfDc / NB, n_chunks = dcb / kKvChunk;  // latent columns of the branch
+  constexpr int dcb = DCB, n_chunks = dcb / kKvChunk;  // latent columns of a branch
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, kg = lane >> 5;
@@ -527,12 +528,12 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(p.NB == 1 ? k_prefill_kv<1> : k_prefill_kv<4>,
+  hipLaunchKernelGGL(p.dcb == 512 ? k_prefill_kv<512> : k_prefill_kv<128>,
                      dim3(p.L_pad / kKvTok, p.H * p.NB, p.B), dim3(64 * kKvWaves), 0, s,
                      (const bf16*)a.latent, a.lat_tok, a.lat_seq, (const bf16*)a.rope,
                      a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
                      p.max_seqlen, (const bf16*)a.w_uk, (const bf16*)a.w_uv, (bf16*)a.kbuf,
-                     (bf16*)a.rbuf, (bf16*)a.vbuf, p.H, p.L_pad);
+                     (bf16*)a.rbuf, (bf16*)a.vbuf, p.H, p.NB, p.L_pad);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;

@@ -472,7 +472,7 @@ def test_prefill_workspace_size_and_validation(lib):
     assert call(lib, p, fn="mla_prefill", workspace=FAKE + 16) == 7
     for over, status in [(dict(num_branches=4, d_latent=512), 3),     # MLRA-4 at 128 per branch
                          (dict(num_branches=2, d_latent=256), 3),
-                         (dict(d_latent=128), 3), (dict(d_nope=64), 3),
+                         (dict(d_latent=256), 3), (dict(d_nope=64), 3),
                          (dict(flags=B.MLA_FLAG_QUERY_LATENT), 3),
                          (dict(dtype=B.MLA_F32), 3), (dict(dtype=9), 5),
                          (dict(page_size=16), 3), (dict(num_queries=-1), 2),

@@ -138,8 +138,8 @@ def test_main_loop_keeps_tile_loads_in_flight(src, pattern, tmp_path):
     assert len(kernels) >= (2 if src == "prefill.hip" else 1), "no main-loop kernel found"
     for name, lines, _meta in kernels:
         loop = _main_loop(lines)
-        if loop is None and "k_prefill_kvILi4E" in name:
-            continue  # MLRA's 128-wide branches: two chunks, fully unrolled, no loop
+        if loop is None and "k_prefill_kvILi128E" in name:
+            continue  # 128-wide MLRA branches: two chunks, fully unrolled, no loop
         assert loop is not None, (name, "main loop not found")
         blocks, head, members = loop
         waits = _drains_after_issue(blocks, head, members)

@@ -166,6 +166,51 @@ def test_prefill_mlra_full_size_sampled():
     assert_close(got[:, rows], ref, "bf16", "mlra4 prefill full size sampled")
 
 
+SHARD = I.WORKLOADS["mlra_shard_bf16_b32_h32_l8192"]
+
+
+@pytest.mark.parametrize("sq,lens", [(200, [300, 129]), (33, [33, 95, 161])],
+                         ids=["shard_sq200", "shard_sq33_tails"])
+def test_prefill_mlra_shard_matches_oracle(sq, lens):
+    """One MLRA branch cached on its own (rows [c_b (128) | k_rope (64)], the tensor-parallel
+    shard), default and sharp queries."""
+    for sharp in (False, True):
+        inp = I.make_inputs(SHARD, seed=5, seqlens=lens, num_queries=sq,
+                            q_gain=I.sharp_q_gain(SHARD) if sharp else 1.0)
+        got, _ = gpu_prefill(inp)
+        assert_close(got, oracle_prefill(inp), "bf16", f"shard sq={sq} sharp={sharp}")
+
+
+def test_prefill_mlra_shards_sum_to_mlra4():
+    """Tensor-parallel MLRA-4 prefill on one GPU: each branch's prefill on its own, reading its
+    [c_b | k_rope] columns out of the MLRA-4 rows (latent pointer offset by 128 b, rotary
+    pointer by 512, row stride 576) with its query, W_UK / W_UV blocks and out_scale 0.5, sums
+    to the one-call MLRA-4 prefill ("[ICLR 2025] MLRA…", sections 2.1 and 4)."""
+    import torch
+    from mlra_latent_kv_amd import binding as B
+    from mlra_latent_kv_amd import harness as Hn
+    from test_gpu_parity import rel_l2
+    inp = I.make_inputs(MLRA4, seed=14, seqlens=[300, 77], num_queries=150,
+                        q_gain=I.sharp_q_gain(MLRA4))
+    full, case = gpu_prefill(inp)
+    total = torch.zeros(case.out.shape, dtype=torch.float32, device=case.out.device)
+    esz = case.cache.element_size()
+    for br in range(4):
+        p = case.params.copy()
+        p.num_branches, p.d_latent = 1, 128
+        ws = torch.empty(B.prefill_workspace_size(p), dtype=torch.uint8, device=case.out.device)
+        out = torch.empty_like(case.out)
+        qn = case.q_nope[:, :, br:br + 1].contiguous()
+        B.mla_prefill(p, qn, case.q_rope, case.cache.data_ptr() + 128 * br * esz,
+                      case.cache.data_ptr() + 512 * esz, case.seqlens, None, case.w_uk[br],
+                      case.w_uv[br], out, ws)
+        torch.cuda.synchronize()
+        total += out.float()
+    got = total.cpu().numpy().astype(np.float64)
+    assert_close(got, oracle_prefill(inp), "bf16", "sum of 4 shard prefills vs oracle")
+    assert rel_l2(got, full) < 5e-3, rel_l2(got, full)
+
+
 def test_prefill_empty_sequences_write_zeros():
     inp = I.make_inputs(H128, seed=3, seqlens=[0, 0], num_queries=40, max_seqlen=64)
     got, _ = gpu_prefill(inp)
@@ -211,11 +256,10 @@ def test_prefill_timed_matches_untimed():
 
 
 def test_prefill_rejects_unsupported():
-    """One MLRA branch on its own (128-wide latent, no branch sum) has no prefill."""
+    """The folded-query form has no prefill (the prefill up-projects keys itself)."""
     from mlra_latent_kv_amd import binding as B
     from mlra_latent_kv_amd import harness as H
-    inp = I.make_inputs(I.WORKLOADS["mlra_shard_bf16_b32_h32_l8192"], seed=1, seqlens=[10],
-                        num_queries=4)
-    p = H.make_params(inp)
+    inp = I.make_inputs(MLRA4, seed=1, seqlens=[10], num_queries=4)
+    p = H.make_params(inp, flags=B.MLA_FLAG_QUERY_LATENT)
     with pytest.raises(B.MlaError, match="UNSUPPORTED"):
         B.prefill_workspace_size(p)
