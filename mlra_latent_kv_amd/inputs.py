@@ -109,6 +109,11 @@ PREFILL_WORKLOADS = {
         Workload("prefill_mlra4_bf16_b1_h32_l4096", batch=1, heads=32, branches=4, d_nope=128,
                  d_v=128, d_cb=128, d_rope=64, dtype="bf16", paged=False, seqlen=4096,
                  out_scale=0.5, seed=1009),
+        # one MLRA branch cached on its own (the 4-way tensor-parallel shard of the workload
+        # above, at four sequences): rows [c_b (128) | k_rope (64)], out_scale 0.5
+        Workload("prefill_mlra_shard_bf16_b4_h32_l4096", batch=4, heads=32, branches=1,
+                 d_nope=128, d_v=128, d_cb=128, d_rope=64, dtype="bf16", paged=False,
+                 seqlen=4096, out_scale=0.5, seed=1010),
     ]
 }
 
