@@ -317,6 +317,9 @@ mla_status run_prefill(const mla_params* p, const void* q_nope, const void* q_ro
   st = check_prefill_call(plan, q_nope, q_rope, latent, rope, seqlens, block_table, w_uk, w_uv,
                           out, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
+  int n_cu = 0;  // the device is asked only for a valid call
+  if (device_cu_count(&n_cu) != hipSuccess) return MLA_ERR_HIP;
+  if (n_cu > 0 && n_cu < plan.n_cu) plan.n_cu = n_cu;
   PrefillArgs a;
   a.q_nope = q_nope;
   a.q_rope = q_rope;

@@ -190,7 +190,7 @@ mla_status check_call(const mla_params* p, const Plan& plan, int want_branches,
   return MLA_OK;
 }
 
-mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
+mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan, int n_cu) {
   if (!p || !plan) return MLA_ERR_NULL;
   if (p->dtype != MLA_F32 && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (p->latent_format != 0 && p->latent_format != MLA_LATENT_FP8) return MLA_ERR_DTYPE;
@@ -233,6 +233,9 @@ mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan) {
   q.paged = p->page_size == kPage;
   q.max_seqlen = p->max_seqlen;
   q.L_pad = (int)(ceil_div(std::max(p->max_seqlen, 1), 256) * 256);
+  q.n_cu = (n_cu <= 0 || n_cu > kMaxCUs) ? kMaxCUs : n_cu;
+  // projection tiles (256 tokens of one sequence, head and branch) indexed in 32 bits
+  if ((int64_t)q.B * q.H * q.NB * (q.L_pad / 256) > INT32_MAX) return MLA_ERR_SHAPE;
   // attention grid, one dimension: (sequence, head and branch, pair of 256-token query blocks)
   if ((ceil_div((int64_t)q.B * q.H * q.NB, 8) * 8) * ceil_div(ceil_div(q.sq, 256), 2) > INT32_MAX)
     return MLA_ERR_SHAPE;

@@ -109,11 +109,14 @@ struct PrefillPlan {
   int paged, max_seqlen;
   int L_pad;          // key rows per (sequence, head, branch) in the workspace: max_seqlen
                       // rounded up to the projection's 256-token blocks
+  int n_cu;           // compute units: the projection runs one workgroup per CU
   size_t off_k, off_r, off_v, off_o, bytes;
 };
 
-// Validates *p for the prefill and fills *plan.  Touches no device.
-mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan);
+// Validates *p for the prefill and fills *plan for a device with n_cu compute units (n_cu <= 0
+// or > kMaxCUs: kMaxCUs; the caller may lower plan->n_cu to the device's count afterwards).
+// Touches no device.
+mla_status make_prefill_plan(const mla_params* p, PrefillPlan* plan, int n_cu = 0);
 
 // Per-call checks on top of make_prefill_plan: pointers, alignment, workspace size.
 mla_status check_prefill_call(const PrefillPlan& plan, const void* q_nope, const void* q_rope,

@@ -23,6 +23,8 @@
 // 2.2) runs the same two kernels per (head, branch) on each branch's 128-wide latent slice
 // and weights (q_nope [B, s_q, H, 4, 128]), and a third launch sums the four normalised
 // branch outputs times out_scale.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 #include "tile_bf16.h"
@@ -66,6 +68,21 @@ __device__ __forceinline__ uint32_t row128(int r, int c) {
   return (uint32_t)(r * 128 + 16 * (c ^ ((r >> 1) & 7)));
 }
 
+// Output tile of one part, staged for the operand-block stores: 256 rows at a 320-byte pitch
+// (values; keys use 272), from the start of stage 1 on, so stage 0 can take the next tile's
+// first chunk meanwhile.
+constexpr int kKvOutBytes = kKvTok * (2 * kPfDv + 64);
+
+// One bf16 into LDS through a restrict pointer: the access then carries alias-scope
+// information, so the compiler does not wait for the direct-to-LDS loads in flight into the
+// other stage before it.
+__device__ __forceinline__ void lds_write2(char* __restrict__ p, bf16 v) { *(bf16*)p = v; }
+
+// A workgroup's unit of work: 256 tokens of one (sequence, head and branch hb = h NB + br).
+struct KvTile {
+  int b, hb, t0, L;
+};
+
 template <int DCB>
 __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     const bf16* __restrict__ latent, int64_t lat_tok, int64_t lat_seq,
@@ -73,64 +90,89 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
     const int32_t* __restrict__ bt, int64_t bt_stride, int paged,
     const int32_t* __restrict__ seqlens, int max_seqlen, const bf16* __restrict__ w_uk,
     const bf16* __restrict__ w_uv, bf16* __restrict__ kout, bf16* __restrict__ rout,
-    bf16* __restrict__ vout, int H, int NB, int L_pad) {
+    bf16* __restrict__ vout, int B, int H, int NB, int L_pad) {
   struct Smem {
     char st[2][kKvStage];
+    char out_tail[kKvOutBytes - kKvStage];  // the output tile runs on from stage 1 into this
   };
-  __shared__ __align__(16) Smem sm;  // 128 KiB, reused for the output tile
-  const int tb = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;  // hb = h NB + br
-  const int h = hb / NB, br = hb % NB;
+  __shared__ __align__(16) Smem sm;  // 144 KiB
   constexpr int dcb = DCB, n_chunks = dcb / kKvChunk;  // latent columns of a branch
+  static_assert(n_chunks % 2 == 0, "every tile's first chunk goes to stage 0");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, kg = lane >> 5;
-  const int L = min(max(seqlens[b], 0), max_seqlen);
-  const int t0 = tb * kKvTok;
   const uint32_t lat_row_b = (uint32_t)(lat_tok * 2);
-  // W_UK [NB][H][128][dcb] and W_UV [NB][H][dcb][128]: the (branch, head) blocks
-  const char* wk = reinterpret_cast<const char*>(w_uk + ((size_t)br * H + h) * kPfDn * dcb);
-  const char* wv = reinterpret_cast<const char*>(w_uv + ((size_t)br * H + h) * dcb * kPfDv);
-  const uint32_t col0_b = (uint32_t)(br * dcb * 2);  // the branch's first latent byte in a row
+  // tiles in (sequence, head, branch, token block) order, token block fastest; workgroup g
+  // takes tiles g, g + G, g + 2G, ...: the workgroups of one XCD keep to the same few token
+  // blocks, whose latent rows stay in its L2 while the heads' weights stream past
+  const int n_tb = L_pad / kKvTok, HNB = H * NB;
+  const int n_tiles = B * HNB * n_tb;  // below 2^31 (the plan checks)
+  auto tile_at = [&](int n) {
+    KvTile t;
+    const int r = n / n_tb;
+    t.t0 = (n - r * n_tb) * kKvTok;
+    t.b = r / HNB;
+    t.hb = r - t.b * HNB;
+    t.L = min(max(seqlens[t.b], 0), max_seqlen);
+    return t;
+  };
 
-  // wave w issues loads 8w .. 8w + 7 of a stage: 0..31 latent rows 8i.., 32..47 W_UK rows
-  // 8(i - 32).., 48..63 W_UV rows 4(i - 48).. (one KiB each); rows past the sequence read as
-  // zeros (the descriptor ends at its last token)
-  auto issue = [&](int q) {
+  // chunk q of tile tl into stage q % 2, 64 loads of one KiB, 8 per wave: waves 0-3 the 256
+  // latent rows (8 rows a load), waves 4-5 W_UK's 128 rows (8 a load), waves 6-7 W_UV's 64
+  // rows (4 a load); rows past the sequence read as zeros (the descriptor ends at its last
+  // token)
+  auto issue = [&](const KvTile& tl, int q, bool live) {
     char* s = sm.st[q & 1];
+    const int h = tl.hb / NB, br = tl.hb - h * NB;
+    // W_UK [NB][H][128][dcb] and W_UV [NB][H][dcb][128]: the (branch, head) blocks
+    const bf16* wk = w_uk + ((size_t)br * H + h) * kPfDn * dcb;
+    const bf16* wv = w_uv + ((size_t)br * H + h) * dcb * kPfDv;
+    const uint32_t col0_b = (uint32_t)(br * dcb * 2);  // the branch's first latent byte in a row
+    const uint32_t on = live ? ~0u : 0u;  // a dead issue: empty descriptors, zeros, no reads
+    if (w < 4) {  // waves 0-3: latent rows
 #pragma unroll
-    for (int u = 0; u < kKvIssues; ++u) {
-      const int i = kKvIssues * w + u;  // uniform
-      if (i < 32) {
-        const int r0 = 8 * i, t = t0 + r0;  // 8 rows of one page
-        const int valid = max(0, min(8, L - t));
+      for (int u = 0; u < kKvIssues; ++u) {
+        const int r0 = 8 * (kKvIssues * w + u), t = tl.t0 + r0;  // 8 rows of one page
+        const int valid = max(0, min(8, tl.L - t));
         const bf16* base;
         if (paged) {
-          const int tt = min(t, max(L - 1, 0));
-          const int64_t pg = valid > 0 ? bt[(int64_t)b * bt_stride + tt / kPage] : 0;
+          const int tt = min(t, max(tl.L - 1, 0));
+          const int64_t pg = valid > 0 ? bt[(int64_t)tl.b * bt_stride + tt / kPage] : 0;
           base = latent + pg * lat_seq + (int64_t)(tt % kPage) * lat_tok;
         } else {
-          base = latent + (int64_t)b * lat_seq + (int64_t)t * lat_tok;
+          base = latent + (int64_t)tl.b * lat_seq + (int64_t)t * lat_tok;
         }
         const int vu = __builtin_amdgcn_readfirstlane(valid);
         const int r = lane >> 3, c = lane & 7;
-        dma16(rsrc(base, vu * lat_row_b), s + r0 * 128,
+        dma16(rsrc(base, (vu * lat_row_b) & on), s + r0 * 128,
               r * lat_row_b + col0_b + q * 128 + 16 * (c ^ (((r0 + r) >> 1) & 7)));
-      } else if (i < 48) {
-        const int r0 = 8 * (i - 32), r = r0 + (lane >> 3), c = lane & 7;
-        dma16(rsrc(wk, kPfDn * dcb * 2), s + kKvABytes + r0 * 128,
-              r * (dcb * 2) + q * 128 + 16 * (c ^ ((r >> 1) & 7)));
-      } else {
-        const int r0 = 4 * (i - 48), r = r0 + (lane >> 4), c = lane & 15;
-        dma16(rsrc(wv, dcb * kPfDv * 2), s + kKvABytes + kKvBkBytes + r0 * 256,
+      }
+    } else if (w < 6) {  // waves 4-5: W_UK rows
+      const auto rk = rsrc(wk, (kPfDn * dcb * 2) & on);
+#pragma unroll
+      for (int u = 0; u < kKvIssues; ++u) {
+        const int r0 = 8 * (kKvIssues * (w - 4) + u), r = r0 + (lane >> 3), c = lane & 7;
+        dma16(rk, s + kKvABytes + r0 * 128, r * (dcb * 2) + q * 128 + 16 * (c ^ ((r >> 1) & 7)));
+      }
+    } else {  // waves 6-7: W_UV rows
+      const auto rv = rsrc(wv, (dcb * kPfDv * 2) & on);
+#pragma unroll
+      for (int u = 0; u < kKvIssues; ++u) {
+        const int r0 = 4 * (kKvIssues * (w - 6) + u), r = r0 + (lane >> 4), c = lane & 15;
+        dma16(rv, s + kKvABytes + kKvBkBytes + r0 * 256,
               (q * kKvChunk + r) * (kPfDv * 2) + 16 * (c ^ lat_sw<Sw32>(r)));
       }
     }
   };
 
-  // the first head's workgroups also copy the block's rotary keys into the workspace as
-  // operand blocks: thread tid, pieces tid + 512 u = (tile, step m, lane i) in order; zeros
-  // past the sequence
-  if (hb == 0) {
+  const int g = blockIdx.x, G = gridDim.x;
+  if (g >= n_tiles) return;
+
+  // the rotary keys of every (sequence, 256-token block) go into the workspace as operand
+  // blocks first, workgroup g taking blocks g, g + G, ...: thread tid, pieces tid + 512 u =
+  // (tile, step m, lane i) in order; zeros past the sequence
+  for (int rb = g; rb < B * n_tb; rb += G) {
+    const int b = rb / n_tb, t0 = (rb - b * n_tb) * kKvTok;
+    const int L = min(max(seqlens[b], 0), max_seqlen);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int pc = tid + 512 * u;
@@ -148,92 +190,101 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
   }
 
   const int mq = w & 3, part = w >> 2;
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
-  const int G = lane >> 4, li = lane & 15;
+  const int l32 = lane & 31, kg = lane >> 5, G16 = lane >> 4, li = lane & 15;
+  issue(tile_at(g), 0, true);
+  for (int n = g; n < n_tiles; n += G) {
+    const KvTile cur = tile_at(n);
 
-  issue(0);
-  for (int q = 0; q < n_chunks; ++q) {
-    if (q + 1 < n_chunks) {
-      issue(q + 1);
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16{};
+    for (int q = 0; q < n_chunks; ++q) {
+      // chunk q + 1 of this tile, or the next tile's chunk 0 (stage 0, whose chunk is done),
+      // goes out before chunk q is waited for; after the last tile a dead issue keeps the
+      // count
+      {
+        const bool last = q + 1 == n_chunks;
+        const int nn = last ? n + G : n;
+        issue(nn == n ? cur : tile_at(min(nn, n_tiles - 1)), last ? 0 : q + 1, nn < n_tiles);
+      }
       wait_vmcnt<kKvIssues>();  // chunk q has landed for this wave
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // ... and for every wave
-    const char* s = sm.st[q & 1];
+      lds_barrier();  // ... and for every wave
+      const char* s = sm.st[q & 1];
 #pragma unroll
-    for (int j = 0; j < kKvChunk / 16; ++j) {
-      bf16x8 a[2], bo[4];
+      for (int j = 0; j < kKvChunk / 16; ++j) {
+        bf16x8 a[2], bo[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int r = 64 * mq + 32 * mb + l32;
-        a[mb] = lds_read16(s + row128(r, 2 * j + kg));
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        if (part == 0) {  // W_UK rows n: 8 consecutive latent columns of row n
-          bo[nb] = lds_read16(s + kKvABytes + row128(32 * nb + l32, 2 * j + kg));
-        } else {          // W_UV rows c: column v, 8 consecutive rows, two transposed reads
-          const int col = 32 * nb + 16 * (G & 1) + 4 * (li & 3);
-          const int r1 = 16 * j + 8 * (G >> 1) + (li >> 2);
-          const char* bv = s + kKvABytes + kKvBkBytes;
-          bo[nb] = tr_pair(bv + lat_piece<Sw32, 128>(r1, col), bv + lat_piece<Sw32, 128>(r1 + 4, col));
+        for (int mb = 0; mb < 2; ++mb) {
+          const int r = 64 * mq + 32 * mb + l32;
+          a[mb] = lds_read16(s + row128(r, 2 * j + kg));
         }
-      }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bo[nb], acc[mb][nb], 0, 0, 0);
-    }
-    lds_barrier();  // every wave is done with this stage before it is refilled
-  }
-
-  // ---- output: each part's 256 x 128 tile through LDS in turn, then whole operand blocks
-  // (1 KiB of contiguous workspace per wave and store).  D layout: lane (column l32 of N
-  // block nb, half kg), item i -> token 8 (i / 4) + 4 kg + i % 4 of the M block.  Row pitches:
-  // 272 bytes for the keys (16 rows at one 16-byte column hit 16 distinct bank slots), 320
-  // for the values (the transposed reads' 4 rows x 64 bytes per half-wave are distinct).
-  constexpr int kPitchK = 2 * kPfDn + 16, kPitchV = 2 * kPfDv + 64;
-  static_assert(kKvTok * kPitchV <= sizeof(Smem), "output tile exceeds the LDS");
-  char* o = reinterpret_cast<char*>(&sm);
-  const size_t head_tok = ((size_t)b * H * NB + hb) * L_pad + t0;  // first token of the block
-#pragma unroll
-  for (int pt = 0; pt < 2; ++pt) {
-    const int pitch = pt == 0 ? kPitchK : kPitchV;
-    if (part == pt) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int t = 64 * mq + 32 * mb + 8 * (i >> 2) + 4 * kg + (i & 3);
-            *(bf16*)(o + t * pitch + 2 * (32 * nb + l32)) = (bf16)acc[mb][nb][i];
+        for (int nb = 0; nb < 4; ++nb) {
+          if (part == 0) {  // W_UK rows n: 8 consecutive latent columns of row n
+            bo[nb] = lds_read16(s + kKvABytes + row128(32 * nb + l32, 2 * j + kg));
+          } else {          // W_UV rows c: column v, 8 consecutive rows, two transposed reads
+            const int col = 32 * nb + 16 * (G16 & 1) + 4 * (li & 3);
+            const int r1 = 16 * j + 8 * (G16 >> 1) + (li >> 2);
+            const char* bv = s + kKvABytes + kKvBkBytes;
+            bo[nb] = tr_pair(bv + lat_piece<Sw32, 128>(r1, col), bv + lat_piece<Sw32, 128>(r1 + 4, col));
           }
-    }
-    __syncthreads();
-    // 8 tiles x 8 blocks: wave w writes blocks 8 w .. 8 w + 7 (tile w), lane by lane
-    bf16* dst = (pt == 0 ? kout : vout) + head_tok * kPfDv + (size_t)w * (kTT * kPfDv);
-    const char* ot = o + kTT * w * pitch;  // the wave's tile
+        }
 #pragma unroll
-    for (int bi = 0; bi < 8; ++bi) {
-      bf16x8 v;
-      if (pt == 0) {  // key step bi: token l32, columns 16 bi + 8 kg ..
-        v = *(const bf16x8*)(ot + l32 * kPitchK + 2 * (16 * bi + 8 * kg));
-      } else {        // value block (ks, cb) = (bi / 4, bi % 4): two transposed 4-row reads
-        const int ks = bi >> 2, cb = bi & 3;
-        const int tr = 16 * ks + 4 * kg + (li >> 2), col = 32 * cb + 16 * (G & 1) + 4 * (li & 3);
-        v = tr_pair(ot + tr * kPitchV + 2 * col, ot + (tr + 8) * kPitchV + 2 * col);
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bo[nb], acc[mb][nb], 0, 0, 0);
       }
-      *(bf16x8*)(dst + 8 * (64 * bi + lane)) = v;
+      lds_barrier();  // every wave is done with this stage before it is refilled
     }
-    __syncthreads();
+
+    // ---- output: each part's 256 x 128 tile through LDS in turn (from stage 1 on), then
+    // whole operand blocks (1 KiB of contiguous workspace per wave and store), while the next
+    // tile's first chunk lands in stage 0 (LDS-only barriers, so its loads stay in flight).  D layout:
+    // lane (column l32 of N block nb, half kg), item i -> token 8 (i / 4) + 4 kg + i % 4 of the
+    // M block.  Row pitches: 272 bytes for the keys (16 rows at one 16-byte column hit 16
+    // distinct bank slots), 320 for the values (the transposed reads' 4 rows x 64 bytes per
+    // half-wave are distinct).
+    constexpr int kPitchK = 2 * kPfDn + 16, kPitchV = 2 * kPfDv + 64;
+    static_assert(kKvTok * kPitchV == kKvOutBytes, "output tile size");
+    char* o = sm.st[1];
+    const size_t head_tok = ((size_t)cur.b * HNB + cur.hb) * L_pad + cur.t0;  // block's first token
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const int pitch = pt == 0 ? kPitchK : kPitchV;
+      if (part == pt) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int t = 64 * mq + 32 * mb + 8 * (i >> 2) + 4 * kg + (i & 3);
+              lds_write2(o + t * pitch + 2 * (32 * nb + l32), (bf16)acc[mb][nb][i]);
+            }
+      }
+      lds_barrier();
+      // 8 tiles x 8 blocks: wave w writes blocks 8 w .. 8 w + 7 (tile w), lane by lane
+      bf16* dst = (pt == 0 ? kout : vout) + head_tok * kPfDv + (size_t)w * (kTT * kPfDv);
+      const char* ot = o + kTT * w * pitch;  // the wave's tile
+#pragma unroll
+      for (int bi = 0; bi < 8; ++bi) {
+        bf16x8 v;
+        if (pt == 0) {  // key step bi: token l32, columns 16 bi + 8 kg ..
+          v = lds_read16(ot + l32 * kPitchK + 2 * (16 * bi + 8 * kg));
+        } else {        // value block (ks, cb) = (bi / 4, bi % 4): two transposed 4-row reads
+          const int ks = bi >> 2, cb = bi & 3;
+          const int tr = 16 * ks + 4 * kg + (li >> 2), col = 32 * cb + 16 * (G16 & 1) + 4 * (li & 3);
+          v = tr_pair(ot + tr * kPitchV + 2 * col, ot + (tr + 8) * kPitchV + 2 * col);
+        }
+        *(bf16x8*)(dst + 8 * (64 * bi + lane)) = v;
+      }
+      lds_barrier();
+    }
   }
+  wait_vmcnt<0>();  // the dead issue's LDS writes, before the workgroup's LDS is released
 }
 
 // ----------------------------------------------------------------------------- attention
@@ -528,12 +579,14 @@ hipError_t launch_prefill(const PrefillPlan& p, const PrefillArgs& a, hipStream_
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(p.dcb == 512 ? k_prefill_kv<512> : k_prefill_kv<128>,
-                     dim3(p.L_pad / kKvTok, p.H * p.NB, p.B), dim3(64 * kKvWaves), 0, s,
+  const int64_t kv_tiles = (int64_t)p.B * p.H * p.NB * (p.L_pad / kKvTok);
+  const unsigned kv_wg = (unsigned)std::min<int64_t>(kv_tiles, p.n_cu);  // one per CU
+  hipLaunchKernelGGL(p.dcb == 512 ? k_prefill_kv<512> : k_prefill_kv<128>, dim3(kv_wg),
+                     dim3(64 * kKvWaves), 0, s,
                      (const bf16*)a.latent, a.lat_tok, a.lat_seq, (const bf16*)a.rope,
                      a.rope_tok, a.rope_seq, a.block_table, a.bt_stride, p.paged, a.seqlens,
                      p.max_seqlen, (const bf16*)a.w_uk, (const bf16*)a.w_uv, (bf16*)a.kbuf,
-                     (bf16*)a.rbuf, (bf16*)a.vbuf, p.H, p.NB, p.L_pad);
+                     (bf16*)a.rbuf, (bf16*)a.vbuf, p.B, p.H, p.NB, p.L_pad);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;
