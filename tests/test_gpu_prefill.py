@@ -123,7 +123,9 @@ MLRA4_PAGED = I.Workload("prefill_mlra4_paged_b3_h32", batch=3, heads=32, branch
 def test_prefill_mlra_matches_oracle(w, sq, lens):
     """MLRA-4: four 128-wide branches per head, each with its own up-projected keys and
     values, query and softmax, the shared rotary score, and the scaled branch sum; distinct
-    per-branch queries (default and sharp)."""
+    per-branch queries (default and sharp).  The projection's tile loop is uneven here: 384
+    and 1152 tiles of 256 tokens over one workgroup per CU (on 256 CUs, 1 or 2 and 4 or 5
+    tiles each)."""
     for sharp in (False, True):
         inp = I.make_inputs(w, seed=5, seqlens=lens, num_queries=sq,
                             q_gain=I.sharp_q_gain(w) if sharp else 1.0)
