@@ -403,11 +403,12 @@ def bench_probe(args, ev, stream):
     out = torch.empty(lib.mla_probe_issue_out_words(), dtype=torch.float32, device="cuda")
     iters = 4096
     names = ["8 waves matrix", "waves 0-3 matrix + 4-7 vector", "waves 0-3 matrix",
-             "waves 4-7 vector", "8 waves matrix+vector interleaved", "8 waves vector"]
+             "waves 4-7 vector", "8 waves matrix+vector interleaved", "8 waves vector",
+             "waves 0-3 matrix+vector interleaved (one wave per SIMD)"]
     e = ev.create(2)
     res = {}
     for agpr in (0, 1):
-        for mode in range(6):
+        for mode in range(7):
             ms = []
             for i in range(6):
                 ev.record(e[0], stream)
@@ -433,6 +434,10 @@ def bench_probe(args, ev, stream):
         "vector_cycles_per_mul_exp_pair": round(exp_cyc, 2),
         "vector_issue_cycles_lost_per_mfma_beside_it": round(taken, 1),
         "vgpr_over_agpr_accumulators_matrix_only": round(res[(0, 2)] / res[(1, 2)], 3),
+        # one wave per SIMD issuing both streams: the share of the shorter stream's time that
+        # is hidden behind the longer one (1: full overlap, 0: the two run one after the other)
+        "one_wave_overlap_of_shorter_stream": round(
+            (res[(1, 2)] + res[(1, 3)] - res[(1, 6)]) / min(res[(1, 2)], res[(1, 3)]), 3),
     }
 
 

@@ -54,10 +54,11 @@ size_t mla_probe_issue_out_words(void);
  * independent MFMA chains (matrix waves) or sixteen independent exp2 chains (vector waves).
  * mode: 0 all waves matrix; 1 waves 0-3 matrix and 4-7 vector (one of each per SIMD);
  * 2 waves 0-3 matrix only; 3 waves 4-7 vector only; 4 all waves both, interleaved; 5 all
- * waves vector.  agpr != 0 keeps the MFMA accumulators in the accumulation registers.
+ * waves vector; 6 waves 0-3 both, interleaved (one wave per SIMD), 4-7 idle.  agpr != 0 keeps
+ * the MFMA accumulators in the accumulation registers.
  * `out` (device, caller-owned, mla_probe_issue_out_words() floats) receives meaningless
  * per-lane sums.  Asynchronous on `stream`; time it with events.  Returns 0, 1 for a NULL
- * pointer, a mode outside 0..5 or iters outside 1..2^20, or 6 when the launch fails.
+ * pointer, a mode outside 0..6 or iters outside 1..2^20, or 6 when the launch fails.
  * Allocates nothing.
  */
 int mla_probe_issue(int mode, int agpr, int iters, float* out, hipStream_t stream);

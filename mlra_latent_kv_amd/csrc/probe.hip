@@ -88,7 +88,8 @@ __global__ __launch_bounds__(kThreads) void k_read_pages(const char* __restrict_
 //   0  all 8 waves matrix            1  waves 0-3 matrix, waves 4-7 vector
 //   2  waves 0-3 matrix, 4-7 idle    3  waves 4-7 vector, 0-3 idle
 //   4  all 8 waves both, interleaved in one instruction stream
-//   5  all 8 waves vector
+//   5  all 8 waves vector            6  waves 0-3 both, interleaved, 4-7 idle (one wave
+//                                       per SIMD feeding both units from one stream)
 // AGPR: accumulators in the accumulation registers (MFMA written as inline asm with an "a"
 // operand) instead of the architectural ones.  The per-lane results go to `out` so nothing
 // is removed; their values mean nothing.
@@ -122,12 +123,12 @@ __global__ __launch_bounds__(kIssueThreads, 1) void k_issue_probe(float* __restr
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_exp2f(v[i] * 0.999f);
   };
-  if (MODE == 4) {
+  if (MODE == 4 || (MODE == 6 && grp == 0)) {
     for (int it = 0; it < iters; ++it) {
       mfma4();
       exp16();
     }
-  } else {
+  } else if (MODE != 6) {
     const bool matrix = MODE == 0 || (MODE <= 2 && grp == 0);
     const bool vector = MODE == 5 || (MODE == 1 && grp == 1) || (MODE == 3 && grp == 1);
     if (matrix)
@@ -151,6 +152,7 @@ hipError_t launch_issue(int mode, float* out, int iters, hipStream_t s) {
     case 2: hipLaunchKernelGGL((k_issue_probe<2, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
     case 3: hipLaunchKernelGGL((k_issue_probe<3, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
     case 4: hipLaunchKernelGGL((k_issue_probe<4, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
+    case 6: hipLaunchKernelGGL((k_issue_probe<6, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
     default: hipLaunchKernelGGL((k_issue_probe<5, AGPR>), g, t, 0, s, out, iters, 1e-3f); break;
   }
   return hipGetLastError();
@@ -174,7 +176,7 @@ int mla_probe_read_pages(const void* pool, size_t page_bytes, const int32_t* pag
 size_t mla_probe_issue_out_words(void) { return (size_t)kIssueBlocks * kIssueThreads; }
 
 int mla_probe_issue(int mode, int agpr, int iters, float* out, hipStream_t stream) {
-  if (!out || mode < 0 || mode > 5 || iters < 1 || iters > (1 << 20)) return 1;
+  if (!out || mode < 0 || mode > 6 || iters < 1 || iters > (1 << 20)) return 1;
   const hipError_t e = agpr ? launch_issue<true>(mode, out, iters, stream)
                             : launch_issue<false>(mode, out, iters, stream);
   return e == hipSuccess ? 0 : 6;

@@ -64,7 +64,7 @@ def test_probe_library_exports_its_header(lib):
     probe.mla_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_void_p]
     assert probe.mla_probe_issue(0, 0, 16, None, None) == 1      # rejected before any launch
-    assert probe.mla_probe_issue(6, 0, 16, FAKE, None) == 1
+    assert probe.mla_probe_issue(7, 0, 16, FAKE, None) == 1
     assert probe.mla_probe_issue(1, 1, 0, FAKE, None) == 1
 
 
