@@ -46,14 +46,15 @@ constexpr int kPfDc = 512, kPfDn = 128, kPfDv = 128, kPfDr = 64;
 constexpr int kTileK = kTT * kPfDn * 2, kTileR = kTT * kPfDr * 2, kTileV = kTT * kPfDv * 2;
 
 // ----------------------------------------------------------------------------- K and V
-// One workgroup (8 waves, two per SIMD) per (sequence b, block of 256 tokens, head h and
-// latent branch br).  Wave w computes tokens 64 (w & 3) .. +63 (two 32-row M blocks) of part
-// w >> 2 (0: K, 1: V), all 128 output columns (four 32-column N blocks), MFMA 32x32x16 over
-// the branch's DCB latent columns (512 for MLA; 128 per MLRA branch, or for one MLRA branch
-// cached on its own) in chunks of 64.  Each chunk stages, by direct-to-LDS loads, the 256 latent rows (128
-// bytes of each), W_UK[h]'s 128 rows (their columns of the chunk) and W_UV[h]'s 64 rows of the
-// chunk (256 bytes each); double-buffered, so one chunk's 64 MFMAs per SIMD cover the next
-// one's loads.
+// A tile is (sequence b, block of 256 tokens, head h and latent branch br); one workgroup
+// (8 waves, two per SIMD) per CU walks its share of the tiles.  Wave w computes tokens
+// 64 (w & 3) .. +63 (two 32-row M blocks) of part w >> 2 (0: K, 1: V), all 128 output
+// columns (four 32-column N blocks), MFMA 32x32x16 over the branch's DCB latent columns (512
+// for MLA; 128 per MLRA branch, or for one MLRA branch cached on its own) in chunks of 64.
+// Each chunk stages, by direct-to-LDS loads, the 256 latent rows (128 bytes of each),
+// W_UK[h]'s 128 rows (their columns of the chunk) and W_UV[h]'s 64 rows of the chunk (256
+// bytes each); double-buffered, so one chunk's 64 MFMAs per SIMD cover the next one's loads,
+// and the next tile's first chunk loads during the current tile's output phase.
 constexpr int kKvTok = 256, kKvChunk = 64, kKvWaves = 8;
 constexpr int kKvABytes = kKvTok * kKvChunk * 2;     // 32 KiB
 constexpr int kKvBkBytes = kPfDn * kKvChunk * 2;     // 16 KiB
