@@ -421,7 +421,9 @@ mla_status mla_cache_append(const mla_append_params* p, const void* hidden, cons
  * bf16), in an internal tiled order, and with NB = 4 the branch outputs (B x s_q x H x 4 x
  * 128 bf16).  Kernels on `stream`: the up-projection (a GEMM of the cached latents against
  * W_UK and W_UV, which also copies the rotary keys), a causal flash-attention pass per
- * (head, branch), and with NB = 4 the scaled branch sum.
+ * (head, branch), and with NB = 4 the scaled branch sum.  The up-projection's 256-token tiles,
+ * B x H x NB x L_pad / 256, must number below 2^31 (MLA_ERR_SHAPE); it runs one workgroup per
+ * compute unit, the count asked of the current device once (MLA_ERR_HIP if that fails).
  */
 mla_status mla_prefill_workspace_size(const mla_params* p, size_t* bytes);
 mla_status mla_prefill(const mla_params* p, const void* q_nope, const void* q_rope,
