@@ -36,6 +36,15 @@ using namespace tile;
 
 constexpr int kPfDc = 512, kPfDn = 128, kPfDv = 128, kPfDr = 64;
 
+// Direct-to-LDS load with the default cache policy.  The decode streams every cached row once
+// and loads it non-temporally; the prefill re-reads what it loads (each latent chunk by every
+// head, each head's weight chunks by every token block, each key and value tile by the query
+// blocks of its head), so its loads stay in the caches: projection 205.7 -> 174.3 us at 128
+// heads x 4096 tokens, 93 -> 85 on MLRA-4, same-process A/B on MI355X, outputs bitwise equal.
+__device__ __forceinline__ void dma16_keep(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
 // Workspace layout: operand blocks.  Each 32-token tile of keys, values and rotary keys is
 // stored as the MFMA operands the attention feeds, 1 KiB per block, lane i's 8 bf16 at
 // 16 i, so the attention loads whole tiles as contiguous KiBs and reads them lane-linearly.
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
         }
         const int vu = __builtin_amdgcn_readfirstlane(valid);
         const int r = lane >> 3, c = lane & 7;
-        dma16(rsrc(base, (vu * lat_row_b) & on), s + r0 * 128,
+        dma16_keep(rsrc(base, (vu * lat_row_b) & on), s + r0 * 128,
               r * lat_row_b + col0_b + q * 128 + 16 * (c ^ (((r0 + r) >> 1) & 7)));
       }
     } else if (w < 6) {  // waves 4-5: W_UK rows
@@ -152,14 +161,14 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void k_prefill_kv(
 #pragma unroll
       for (int u = 0; u < kKvIssues; ++u) {
         const int r0 = 8 * (kKvIssues * (w - 4) + u), r = r0 + (lane >> 3), c = lane & 7;
-        dma16(rk, s + kKvABytes + r0 * 128, r * (dcb * 2) + q * 128 + 16 * (c ^ ((r >> 1) & 7)));
+        dma16_keep(rk, s + kKvABytes + r0 * 128, r * (dcb * 2) + q * 128 + 16 * (c ^ ((r >> 1) & 7)));
       }
     } else {  // waves 6-7: W_UV rows
       const auto rv = rsrc(wv, (dcb * kPfDv * 2) & on);
 #pragma unroll
       for (int u = 0; u < kKvIssues; ++u) {
         const int r0 = 4 * (kKvIssues * (w - 6) + u), r = r0 + (lane >> 4), c = lane & 15;
-        dma16(rv, s + kKvABytes + kKvBkBytes + r0 * 256,
+        dma16_keep(rv, s + kKvABytes + kKvBkBytes + r0 * 256,
               (q * kKvChunk + r) * (kPfDv * 2) + 16 * (c ^ lat_sw<Sw32>(r)));
       }
     }
@@ -370,10 +379,10 @@ __global__ __launch_bounds__(64 * kAtWaves, 1) void k_prefill_attn(
       char* buf = sm.ring[k % kAtRing];
       const uint32_t n = k < n_tiles ? 1u : 0u;
       const size_t t = (size_t)k;
-      dma16(rsrc(kb + t * kTileK, n * kTileK), buf + w * 1024, w * 1024 + 16 * lane);
-      dma16(rsrc(vb + t * kTileV, n * kTileV), buf + kAtVOff + w * 1024, w * 1024 + 16 * lane);
+      dma16_keep(rsrc(kb + t * kTileK, n * kTileK), buf + w * 1024, w * 1024 + 16 * lane);
+      dma16_keep(rsrc(vb + t * kTileV, n * kTileV), buf + kAtVOff + w * 1024, w * 1024 + 16 * lane);
       if (w < 4)
-        dma16(rsrc(rb + t * kTileR, n * kTileR), buf + kAtROff + w * 1024, w * 1024 + 16 * lane);
+        dma16_keep(rsrc(rb + t * kTileR, n * kTileR), buf + kAtROff + w * 1024, w * 1024 + 16 * lane);
     };
 
     // query as the B operand (K = 192 columns, N = 32 rows): lane (row l32, half kg), K-step j
